@@ -1,0 +1,174 @@
+/*
+ * convrot.h — C ABI of the MI355X (gfx950) rotated W8A8 linear layer over NVFP4 weights.
+ *
+ * What the layer computes (ComfyUI Turing Utils README on comfy.icu, section "Nodes",
+ * bullet "Load ConvRot DiT and Load ConvRot CLIP"; MiniMax H3 explainer on modelpad.app,
+ * "Foundations" and the MLP and "convrot" paragraphs):
+ *   y = x W^T for a linear layer whose weight W [N, K] is stored packed as NVFP4.
+ *   Both operands are zero-padded along K to K_pad = 256 * ceil(K / 256), rotated by the
+ *   same 256-wide block rotation R = H/16 (H the Sylvester-ordered Walsh-Hadamard matrix
+ *   of order 256, applied to each 256-column block), quantized per row to symmetric S8
+ *   with an FP32 scale, multiplied in an INT8 GEMM with int32 accumulation, and the
+ *   accumulator is dequantized by the two row scales.  Because R R^T = I the rotation
+ *   cancels in the product; it only spreads outlier channels before quantization.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers unless stated otherwise.  The caller owns every buffer;
+ *     outputs must not alias inputs.  Calls are asynchronous on `stream`; nothing is
+ *     synchronised and no device memory is allocated.
+ *   - Arguments are validated on the host before anything is enqueued; a non-CR_OK status
+ *     means nothing was launched.  Faults inside a launched kernel surface at the caller's
+ *     next synchronisation.  There is no fallback path: an unsupported device (anything
+ *     but gfx950) yields CR_ERR_NO_DEVICE.
+ *   - Strides (ld_*) are in elements of the pointed-to type.  Every base pointer must be
+ *     16-byte aligned and every row stride a multiple of 16 bytes, except the NVFP4 block
+ *     scales (any stride) and the output of the GEMM (element-aligned).  Violations return
+ *     CR_ERR_MISALIGNED.
+ *   - K_pad may not exceed CR_MAX_K_PAD, so that 127 * 127 * K_pad fits in an int32.
+ *   - Rows are independent.  A row whose maximum |value| after rotation is 0 gets scale 0
+ *     and all-zero codes.
+ *
+ * Arithmetic (binary32, round to nearest even; each step evaluated exactly as written):
+ *   NVFP4 element k of weight row n: code = nibble k of the row (low nibble of byte k/2
+ *     for even k, high nibble for odd k), block scale = E4M3 byte k/16 of the row,
+ *     value = fp32(E2M1(code) * E4M3(scale)) * g, g the FP32 global scale; columns
+ *     k >= K are 0 whatever bytes the row padding holds.
+ *   SwiGLU element (MiniMax H3 explainer, MLP paragraph): gate a = h[m, k], value
+ *     b = h[m, F + k]; sigma = 1 / (1 + E(-a)) with E a fixed exp built from IEEE basic
+ *     operations (Cody-Waite reduction, degree-7 Taylor polynomial, scaling by 2^k);
+ *     result (a * sigma) * b, kept in FP32.
+ *   Rotation: per 256-block, butterfly stages h = 1, 2, ..., 128 ((u, v) -> (u+v, u-v)
+ *     on the pair j, j+h), then * 0.0625.
+ *   Row quantization: a = max |y|; scale = a / 127; r = 127 / a; q = clamp(rint(y * r),
+ *     -127, 127).
+ *   Epilogue: out = ((float)acc * a_scale[m]) * b_scale[n], rounded once to the output type.
+ */
+#ifndef CONVROT_H
+#define CONVROT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CR_ABI_VERSION 1
+#define CR_MAX_K_PAD 133120       /* largest multiple of 256 with 127*127*K_pad < 2^31 */
+#define CR_TWO_PASS_K_PAD 16384   /* K_pad above this streams each row twice */
+#define CR_DEFAULT_MAX_TILE_BYTES ((size_t)128 << 20)
+
+typedef enum {
+    CR_OK = 0,
+    CR_ERR_INVALID_ARG = 1,       /* null pointer, size < 1, stride too small, bad flag */
+    CR_ERR_UNSUPPORTED_DTYPE = 2, /* dtype not accepted by this entry point */
+    CR_ERR_MISALIGNED = 3,        /* base pointer or row stride alignment violated */
+    CR_ERR_TOO_LARGE = 4,         /* K_pad > CR_MAX_K_PAD, or workspace too small */
+    CR_ERR_NO_DEVICE = 5,         /* no current HIP device, or it is not gfx950 */
+    CR_ERR_LAUNCH = 6             /* the HIP runtime rejected a launch or an event call */
+} cr_status;
+
+typedef enum { CR_BF16 = 0, CR_FP16 = 1, CR_FP32 = 2, CR_I32 = 3 } cr_dtype;
+
+enum {
+    CR_FLAG_NONE = 0,
+    CR_FLAG_FORCE_TWO_PASS = 1    /* stream rows twice even when K_pad <= CR_TWO_PASS_K_PAD */
+};
+
+/* ABI version of the loaded library (CR_ABI_VERSION when header and library match). */
+int cr_abi_version(void);
+
+/* Static, human-readable name of a status. */
+const char *cr_status_string(cr_status s);
+
+/* 256 * ceil(k / 256) for k >= 1; 0 for k < 1. */
+int64_t cr_padded_k(int64_t k);
+
+/*
+ * Weight preparation: NVFP4 decode, ConvRot256, row quantization (the three are fused;
+ * ComfyUI Turing Utils README, "Load ConvRot DiT ..." bullet: decode, FP32 rotation and
+ * S8 quantization of the weight are one step, and only a bounded call-local S8 tile is
+ * expanded while the packed NVFP4 bytes stay untouched).
+ *   w_fp4        [n_rows, ld_fp4] uint8, element k in byte k/2 (low nibble = even k);
+ *                ld_fp4 >= ceil(K/2), a multiple of 16.
+ *   w_sf         [n_rows, ld_sf] uint8 E4M3 block scales, ld_sf >= ceil(K/16), any stride.
+ *   global_scale device pointer to one float g.
+ *   n_rows, K    rows to prepare and the logical K (1 <= K, K_pad <= CR_MAX_K_PAD).
+ *   w_s8         [n_rows, ld_s8] int8 out, ld_s8 >= K_pad, a multiple of 16.
+ *   w_scale      [n_rows] float out.
+ *   flags        CR_FLAG_NONE or CR_FLAG_FORCE_TWO_PASS.
+ */
+cr_status cr_prep_weight_nvfp4(const uint8_t *w_fp4, int64_t ld_fp4,
+                               const uint8_t *w_sf, int64_t ld_sf,
+                               const float *global_scale, int64_t n_rows, int64_t K,
+                               int8_t *w_s8, int64_t ld_s8, float *w_scale,
+                               uint32_t flags, hipStream_t stream);
+
+/*
+ * Activation preparation: ConvRot256 and row quantization of X [M, K] (same bullet:
+ * the rotation is paired, identical for activations and weights).
+ *   x        [M, ld_x] of x_dtype (CR_BF16, CR_FP16 or CR_FP32); ld_x >= K.
+ *   x_s8     [M, ld_s8] int8 out, ld_s8 >= K_pad.   x_scale [M] float out.
+ */
+cr_status cr_quant_act(const void *x, cr_dtype x_dtype, int64_t ld_x, int64_t M, int64_t K,
+                       int8_t *x_s8, int64_t ld_s8, float *x_scale,
+                       uint32_t flags, hipStream_t stream);
+
+/*
+ * Fused SwiGLU + activation preparation (same bullet: SwiGLU runs before the rotation;
+ * MiniMax H3 explainer, MLP paragraph: the first half of fc1's output is the gate).
+ *   h        [M, ld_h] of h_dtype; gate = h[:, 0:F], value = h[:, F:2F]; ld_h >= 2F.
+ *   F        logical width of the SwiGLU output (the GEMM's K).
+ *   x_s8     [M, ld_s8] int8 out with ld_s8 >= 256 * ceil(F/256); x_scale [M] float out.
+ */
+cr_status cr_quant_act_swiglu(const void *h, cr_dtype h_dtype, int64_t ld_h, int64_t M, int64_t F,
+                              int8_t *x_s8, int64_t ld_s8, float *x_scale,
+                              uint32_t flags, hipStream_t stream);
+
+/*
+ * Row-scaled INT8 GEMM with the dequantizing epilogue fused (the int32 accumulator never
+ * reaches memory unless c_dtype is CR_I32; MiniMax H3 explainer, fused-kernel paragraph).
+ *   a_s8 [M, lda] int8 and b_s8 [N, ldb] int8, both K-contiguous; K_pad a multiple of 256.
+ *   a_scale [M], b_scale [N] float; may be NULL only when c_dtype == CR_I32.
+ *   c [M, ldc] of c_dtype (CR_BF16, CR_FP16, CR_FP32 or CR_I32 for the raw accumulator);
+ *   ldc >= N; columns n >= N of each output row are never written.
+ */
+cr_status cr_gemm_s8_rowscale(const int8_t *a_s8, int64_t lda, const float *a_scale,
+                              const int8_t *b_s8, int64_t ldb, const float *b_scale,
+                              int64_t M, int64_t N, int64_t K_pad,
+                              void *c, cr_dtype c_dtype, int64_t ldc, hipStream_t stream);
+
+/*
+ * The whole layer with bounded call-local staging (ComfyUI Turing Utils README, same
+ * bullet: weights stay packed, S8 weight tiles of bounded size are prepared per chunk of
+ * output columns, optionally on a second stream with producer/consumer events; serial and
+ * pipelined results are identical).
+ *   x          [M, ld_x] X (or H [M, ld_h] with 2K columns used when swiglu != 0).
+ *   K          logical K of the GEMM (F when swiglu != 0).
+ *   w_fp4, ld_fp4, w_sf, ld_sf, global_scale   the NVFP4 weight [N, K] as above.
+ *   out [M, ldc] of out_dtype (not CR_I32).
+ *   workspace  device buffer of at least cr_linear_nvfp4_workspace_bytes(...) bytes,
+ *              16-byte aligned; holds the S8 activation, its scales and two S8 weight tiles.
+ *   max_tile_bytes  bound of one S8 weight tile (0 selects CR_DEFAULT_MAX_TILE_BYTES);
+ *              tiles hold a multiple of 256 rows (at least 256).
+ *   s_main     stream of the activation preparation and the GEMMs.
+ *   s_aux      NULL: weight tiles are prepared on s_main (serial staging); otherwise
+ *              they are prepared on s_aux, ordered against s_main by events.  On return
+ *              all work is ordered before any later work on s_main.
+ */
+size_t cr_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes);
+
+cr_status cr_linear_nvfp4(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu,
+                          int64_t M, int64_t K,
+                          const uint8_t *w_fp4, int64_t ld_fp4,
+                          const uint8_t *w_sf, int64_t ld_sf, const float *global_scale,
+                          int64_t N, void *out, cr_dtype out_dtype, int64_t ldc,
+                          void *workspace, size_t ws_bytes, size_t max_tile_bytes,
+                          uint32_t flags, hipStream_t s_main, hipStream_t s_aux);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVROT_H */

@@ -1,0 +1,308 @@
+// C ABI of the rotated W8A8 NVFP4 linear layer: argument validation, device checks,
+// launch configuration and the bounded-staging layer orchestration.
+//
+// Layer orchestration (ComfyUI Turing Utils README, "Load ConvRot DiT ..." bullet):
+// the activation is prepared once; the weight is prepared in chunks of output rows into
+// call-local S8 tiles of bounded size (two tiles alternate), each chunk followed by the
+// GEMM that writes its column band of the output; with a second stream the preparation
+// of chunk c+1 overlaps the GEMM of chunk c, ordered by producer/consumer events.  The
+// chunking and the overlap change no value.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "../../include/convrot.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other (read-only cache)
+
+cr_status current_device_ok()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return CR_ERR_NO_DEVICE;
+    }
+    int s = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (s == 0) {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return CR_ERR_NO_DEVICE;
+        }
+        s = (std::strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_arch_ok[dev].store(s, std::memory_order_relaxed);
+    }
+    return s == 1 ? CR_OK : CR_ERR_NO_DEVICE;
+}
+
+inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+inline int64_t elem_size(cr_dtype d)
+{
+    switch (d) {
+    case CR_BF16: case CR_FP16: return 2;
+    case CR_FP32: case CR_I32: return 4;
+    default: return 0;
+    }
+}
+
+inline cr_status from_hip(hipError_t e) { return e == hipSuccess ? CR_OK : CR_ERR_LAUNCH; }
+
+constexpr int64_t kMaxRows = 0x7fffffff;
+
+inline int64_t pad256(int64_t k) { return ((k + 255) / 256) * 256; }
+
+cr_status check_flags(uint32_t flags)
+{
+    return (flags & ~(uint32_t)CR_FLAG_FORCE_TWO_PASS) ? CR_ERR_INVALID_ARG : CR_OK;
+}
+
+cr_status check_act(const void *x, cr_dtype dt, int64_t ld_x, int64_t M, int64_t K, int64_t cols,
+                    int8_t *x_s8, int64_t ld_s8, float *x_scale, uint32_t flags)
+{
+    if (!x || !x_s8 || !x_scale) return CR_ERR_INVALID_ARG;
+    if (dt != CR_BF16 && dt != CR_FP16 && dt != CR_FP32) return CR_ERR_UNSUPPORTED_DTYPE;
+    if (M < 1 || K < 1 || M > kMaxRows) return CR_ERR_INVALID_ARG;
+    if (check_flags(flags) != CR_OK) return CR_ERR_INVALID_ARG;
+    const int64_t kp = pad256(K);
+    if (kp > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
+    if (ld_x < cols || ld_s8 < kp) return CR_ERR_INVALID_ARG;
+    const int64_t es = elem_size(dt);
+    if (!aligned(x, 16) || (ld_x * es) % 16 != 0) return CR_ERR_MISALIGNED;
+    if (!aligned(x_s8, 16) || ld_s8 % 16 != 0 || !aligned(x_scale, 4)) return CR_ERR_MISALIGNED;
+    return CR_OK;
+}
+
+cr_status check_weight(const uint8_t *w_fp4, int64_t ld_fp4, const uint8_t *w_sf, int64_t ld_sf,
+                       const float *g, int64_t n_rows, int64_t K, int8_t *w_s8, int64_t ld_s8,
+                       float *w_scale, uint32_t flags)
+{
+    if (!w_fp4 || !w_sf || !g || !w_s8 || !w_scale) return CR_ERR_INVALID_ARG;
+    if (n_rows < 1 || K < 1 || n_rows > kMaxRows) return CR_ERR_INVALID_ARG;
+    if (check_flags(flags) != CR_OK) return CR_ERR_INVALID_ARG;
+    const int64_t kp = pad256(K);
+    if (kp > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
+    if (ld_fp4 < (K + 1) / 2 || ld_sf < (K + 15) / 16 || ld_s8 < kp) return CR_ERR_INVALID_ARG;
+    if (!aligned(w_fp4, 16) || ld_fp4 % 16 != 0) return CR_ERR_MISALIGNED;
+    if (!aligned(g, 4) || !aligned(w_scale, 4)) return CR_ERR_MISALIGNED;
+    if (!aligned(w_s8, 16) || ld_s8 % 16 != 0) return CR_ERR_MISALIGNED;
+    return CR_OK;
+}
+
+cr_status check_gemm(const int8_t *a, int64_t lda, const float *sa, const int8_t *b, int64_t ldb,
+                     const float *sb, int64_t M, int64_t N, int64_t K_pad, void *c, cr_dtype cdt,
+                     int64_t ldc)
+{
+    if (!a || !b || !c) return CR_ERR_INVALID_ARG;
+    if (cdt != CR_BF16 && cdt != CR_FP16 && cdt != CR_FP32 && cdt != CR_I32) return CR_ERR_UNSUPPORTED_DTYPE;
+    if (cdt != CR_I32 && (!sa || !sb)) return CR_ERR_INVALID_ARG;
+    if (M < 1 || N < 1 || K_pad < 1 || K_pad % 256 != 0) return CR_ERR_INVALID_ARG;
+    if (M > kMaxRows || N > kMaxRows) return CR_ERR_INVALID_ARG;
+    if (((M + 255) / 256) * ((N + 255) / 256) > kMaxRows) return CR_ERR_TOO_LARGE;
+    if (K_pad > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
+    if (lda < K_pad || ldb < K_pad || ldc < N) return CR_ERR_INVALID_ARG;
+    if (!aligned(a, 16) || !aligned(b, 16) || lda % 16 != 0 || ldb % 16 != 0) return CR_ERR_MISALIGNED;
+    if (!aligned(c, (size_t)elem_size(cdt))) return CR_ERR_MISALIGNED;
+    if ((sa && !aligned(sa, 4)) || (sb && !aligned(sb, 4))) return CR_ERR_MISALIGNED;
+    return CR_OK;
+}
+
+// Workspace layout of cr_linear_nvfp4 (every region 256-byte aligned):
+//   x_s8 [M, K_pad] | x_scale [M] | tile0 [R, K_pad] | tscale0 [R] | tile1 | tscale1
+struct LayerPlan {
+    int64_t K_pad, R, nchunks;
+    size_t off_xscale, off_tile[2], off_tscale[2], bytes;
+};
+
+inline size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+LayerPlan plan_layer(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes)
+{
+    LayerPlan p{};
+    if (max_tile_bytes == 0) max_tile_bytes = CR_DEFAULT_MAX_TILE_BYTES;
+    p.K_pad = pad256(K);
+    int64_t R = (int64_t)(max_tile_bytes / (size_t)p.K_pad) / 256 * 256;
+    if (R < 256) R = 256;
+    const int64_t Nr = ((N + 255) / 256) * 256;
+    if (R > Nr) R = Nr;
+    p.R = R;
+    p.nchunks = (N + R - 1) / R;
+    size_t off = up256((size_t)M * (size_t)p.K_pad);
+    p.off_xscale = off;
+    off = up256(off + (size_t)M * 4);
+    const int ntiles = p.nchunks > 1 ? 2 : 1;
+    for (int t = 0; t < 2; t++) {
+        p.off_tile[t] = off;
+        p.off_tscale[t] = up256(off + (size_t)R * (size_t)p.K_pad);
+        if (t < ntiles) off = up256(p.off_tscale[t] + (size_t)R * 4);
+    }
+    p.bytes = off;
+    return p;
+}
+
+struct EventSet {
+    hipEvent_t ev[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+    bool ok = true;
+    explicit EventSet(bool create)
+    {
+        if (!create) return;
+        for (auto &e : ev)
+            if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) { ok = false; e = nullptr; }
+    }
+    ~EventSet()
+    {
+        for (auto &e : ev)
+            if (e) (void)hipEventDestroy(e);
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+int cr_abi_version(void) { return CR_ABI_VERSION; }
+
+const char *cr_status_string(cr_status s)
+{
+    switch (s) {
+    case CR_OK: return "CR_OK";
+    case CR_ERR_INVALID_ARG: return "CR_ERR_INVALID_ARG";
+    case CR_ERR_UNSUPPORTED_DTYPE: return "CR_ERR_UNSUPPORTED_DTYPE";
+    case CR_ERR_MISALIGNED: return "CR_ERR_MISALIGNED";
+    case CR_ERR_TOO_LARGE: return "CR_ERR_TOO_LARGE";
+    case CR_ERR_NO_DEVICE: return "CR_ERR_NO_DEVICE";
+    case CR_ERR_LAUNCH: return "CR_ERR_LAUNCH";
+    default: return "CR_ERR_UNKNOWN";
+    }
+}
+
+int64_t cr_padded_k(int64_t k) { return k < 1 ? 0 : pad256(k); }
+
+cr_status cr_prep_weight_nvfp4(const uint8_t *w_fp4, int64_t ld_fp4, const uint8_t *w_sf, int64_t ld_sf,
+                               const float *global_scale, int64_t n_rows, int64_t K,
+                               int8_t *w_s8, int64_t ld_s8, float *w_scale,
+                               uint32_t flags, hipStream_t stream)
+{
+    cr_status s = check_weight(w_fp4, ld_fp4, w_sf, ld_sf, global_scale, n_rows, K, w_s8, ld_s8, w_scale, flags);
+    if (s != CR_OK) return s;
+    if ((s = current_device_ok()) != CR_OK) return s;
+    return from_hip(convrot::launch_prep_weight(w_fp4, ld_fp4, w_sf, ld_sf, global_scale, n_rows, K, w_s8,
+                                                ld_s8, w_scale, (flags & CR_FLAG_FORCE_TWO_PASS) != 0, stream));
+}
+
+cr_status cr_quant_act(const void *x, cr_dtype x_dtype, int64_t ld_x, int64_t M, int64_t K,
+                       int8_t *x_s8, int64_t ld_s8, float *x_scale, uint32_t flags, hipStream_t stream)
+{
+    cr_status s = check_act(x, x_dtype, ld_x, M, K, K, x_s8, ld_s8, x_scale, flags);
+    if (s != CR_OK) return s;
+    if ((s = current_device_ok()) != CR_OK) return s;
+    return from_hip(convrot::launch_quant_act(x, (int)x_dtype, ld_x, M, K, x_s8, ld_s8, x_scale,
+                                              (flags & CR_FLAG_FORCE_TWO_PASS) != 0, stream));
+}
+
+cr_status cr_quant_act_swiglu(const void *h, cr_dtype h_dtype, int64_t ld_h, int64_t M, int64_t F,
+                              int8_t *x_s8, int64_t ld_s8, float *x_scale, uint32_t flags, hipStream_t stream)
+{
+    if (F > (int64_t)1 << 40) return CR_ERR_TOO_LARGE;
+    cr_status s = check_act(h, h_dtype, ld_h, M, F, 2 * F, x_s8, ld_s8, x_scale, flags);
+    if (s != CR_OK) return s;
+    if ((s = current_device_ok()) != CR_OK) return s;
+    return from_hip(convrot::launch_quant_act_swiglu(h, (int)h_dtype, ld_h, M, F, x_s8, ld_s8, x_scale,
+                                                     (flags & CR_FLAG_FORCE_TWO_PASS) != 0, stream));
+}
+
+cr_status cr_gemm_s8_rowscale(const int8_t *a_s8, int64_t lda, const float *a_scale,
+                              const int8_t *b_s8, int64_t ldb, const float *b_scale,
+                              int64_t M, int64_t N, int64_t K_pad,
+                              void *c, cr_dtype c_dtype, int64_t ldc, hipStream_t stream)
+{
+    cr_status s = check_gemm(a_s8, lda, a_scale, b_s8, ldb, b_scale, M, N, K_pad, c, c_dtype, ldc);
+    if (s != CR_OK) return s;
+    if ((s = current_device_ok()) != CR_OK) return s;
+    return from_hip(convrot::launch_gemm_s8(a_s8, lda, a_scale, b_s8, ldb, b_scale, M, N, K_pad, c,
+                                            (int)c_dtype, ldc, stream));
+}
+
+size_t cr_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes)
+{
+    if (M < 1 || N < 1 || K < 1 || pad256(K) > CR_MAX_K_PAD) return 0;
+    return plan_layer(M, N, K, max_tile_bytes).bytes;
+}
+
+cr_status cr_linear_nvfp4(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu,
+                          int64_t M, int64_t K,
+                          const uint8_t *w_fp4, int64_t ld_fp4,
+                          const uint8_t *w_sf, int64_t ld_sf, const float *global_scale,
+                          int64_t N, void *out, cr_dtype out_dtype, int64_t ldc,
+                          void *workspace, size_t ws_bytes, size_t max_tile_bytes,
+                          uint32_t flags, hipStream_t s_main, hipStream_t s_aux)
+{
+    if (!workspace || !out) return CR_ERR_INVALID_ARG;
+    if (out_dtype == CR_I32) return CR_ERR_UNSUPPORTED_DTYPE;
+    if (M < 1 || N < 1 || K < 1) return CR_ERR_INVALID_ARG;
+    if (swiglu && K > (int64_t)1 << 40) return CR_ERR_TOO_LARGE;
+    if (pad256(K) > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
+    const LayerPlan p = plan_layer(M, N, K, max_tile_bytes);
+    if (!aligned(workspace, 256)) return CR_ERR_MISALIGNED;
+    if (ws_bytes < p.bytes) return CR_ERR_TOO_LARGE;
+    int8_t *ws = static_cast<int8_t *>(workspace);
+    int8_t *x_s8 = ws;
+    float *x_scale = reinterpret_cast<float *>(ws + p.off_xscale);
+    int8_t *tile[2] = {ws + p.off_tile[0], ws + p.off_tile[1]};
+    float *tscale[2] = {reinterpret_cast<float *>(ws + p.off_tscale[0]),
+                        reinterpret_cast<float *>(ws + p.off_tscale[1])};
+    // validate every call of the plan before enqueueing anything
+    cr_status s = check_act(x, x_dtype, ld_x, M, K, swiglu ? 2 * K : K, x_s8, p.K_pad, x_scale, flags);
+    if (s != CR_OK) return s;
+    s = check_weight(w_fp4, ld_fp4, w_sf, ld_sf, global_scale, p.R < N ? p.R : N, K, tile[0], p.K_pad,
+                     tscale[0], flags);
+    if (s != CR_OK) return s;
+    s = check_gemm(x_s8, p.K_pad, x_scale, tile[0], p.K_pad, tscale[0], M, p.R < N ? p.R : N, p.K_pad,
+                   out, out_dtype, ldc);
+    if (s != CR_OK) return s;
+    if ((s = current_device_ok()) != CR_OK) return s;
+
+    const bool tp = (flags & CR_FLAG_FORCE_TWO_PASS) != 0;
+    const int64_t es = elem_size(out_dtype);
+    const bool overlap = s_aux != nullptr && s_aux != s_main && p.nchunks > 1;
+    EventSet evs(overlap);
+    if (overlap && !evs.ok) return CR_ERR_LAUNCH;
+    hipEvent_t ev_start = evs.ev[0], ev_prep[2] = {evs.ev[1], evs.ev[2]}, ev_gemm[2] = {evs.ev[3], evs.ev[4]};
+
+    if (overlap) {
+        // the staging stream must not run ahead of work already queued on s_main
+        if (hipEventRecord(ev_start, s_main) != hipSuccess) return CR_ERR_LAUNCH;
+        if (hipStreamWaitEvent(s_aux, ev_start, 0) != hipSuccess) return CR_ERR_LAUNCH;
+    }
+    hipError_t e = swiglu
+        ? convrot::launch_quant_act_swiglu(x, (int)x_dtype, ld_x, M, K, x_s8, p.K_pad, x_scale, tp, s_main)
+        : convrot::launch_quant_act(x, (int)x_dtype, ld_x, M, K, x_s8, p.K_pad, x_scale, tp, s_main);
+    if (e != hipSuccess) return CR_ERR_LAUNCH;
+
+    for (int64_t c = 0; c < p.nchunks; c++) {
+        const int b = (int)(c & 1);
+        const int64_t n0 = c * p.R;
+        const int64_t rows = (N - n0) < p.R ? (N - n0) : p.R;
+        hipStream_t sp = overlap ? s_aux : s_main;
+        if (overlap && c >= 2 && hipStreamWaitEvent(s_aux, ev_gemm[b], 0) != hipSuccess) return CR_ERR_LAUNCH;
+        e = convrot::launch_prep_weight(w_fp4 + n0 * ld_fp4, ld_fp4, w_sf + n0 * ld_sf, ld_sf, global_scale,
+                                        rows, K, tile[b], p.K_pad, tscale[b], tp, sp);
+        if (e != hipSuccess) return CR_ERR_LAUNCH;
+        if (overlap) {
+            if (hipEventRecord(ev_prep[b], s_aux) != hipSuccess) return CR_ERR_LAUNCH;
+            if (hipStreamWaitEvent(s_main, ev_prep[b], 0) != hipSuccess) return CR_ERR_LAUNCH;
+        }
+        e = convrot::launch_gemm_s8(x_s8, p.K_pad, x_scale, tile[b], p.K_pad, tscale[b], M, rows, p.K_pad,
+                                    static_cast<int8_t *>(out) + n0 * es, (int)out_dtype, ldc, s_main);
+        if (e != hipSuccess) return CR_ERR_LAUNCH;
+        if (overlap && hipEventRecord(ev_gemm[b], s_main) != hipSuccess) return CR_ERR_LAUNCH;
+    }
+    return CR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// Weight preparation kernel: NVFP4 decode + ConvRot256 + per-row S8 quantization, fused.
+//
+// ComfyUI Turing Utils README, "Load ConvRot DiT ..." bullet: packed NVFP4 weights stay
+// unchanged in memory; for each call a bounded tile of rows is decoded, rotated in FP32
+// with the same block rotation as the activations, and quantized to S8 with an FP32 row
+// scale; logical K is zero-padded to a multiple of 256 and serialized padding is ignored.
+//
+// NVFP4 element k of a row: nibble k of the packed row (low nibble of byte k/2 for even
+// k), an E2M1 code (sign, 2 exponent bits with bias 1, 1 mantissa bit); its 16-element
+// block k/16 has an E4M3 scale byte (sign, 4 exponent bits with bias 7, 3 mantissa bits,
+// S.1111.111 = NaN); the tensor has one FP32 global scale g.
+// Decoded value = (E2M1 * E4M3, exact in binary32) * g, rounded once.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.hpp"
+#include "row_prep.hpp"
+
+namespace convrot {
+
+// E2M1 magnitude code m (0..7) -> binary32 bits: 0, 0.5, then (1 + m0/2) * 2^(e-1).
+__device__ __forceinline__ float e2m1_to_f32(uint32_t code)
+{
+    const uint32_t m = code & 7u;
+    uint32_t bits = (m >= 2u) ? ((m + 252u) << 22) : (m ? 0x3f000000u : 0u);
+    bits |= (code & 8u) << 28;
+    return __uint_as_float(bits);
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b)
+{
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    float mag;
+    if (e == 0u) mag = (float)m * 0x1.0p-9f;                       // subnormal: m/8 * 2^-6
+    else if (e == 15u && m == 7u) mag = __builtin_nanf("");
+    else mag = __uint_as_float(((e + 120u) << 23) | (m << 20));
+    return (b & 0x80u) ? -mag : mag;
+}
+
+struct NVFP4Loader {
+    const uint8_t *codes;
+    int64_t ld_codes;
+    const uint8_t *sf;
+    int64_t ld_sf;
+    const float *g;
+    int64_t K;
+    __device__ __forceinline__ void load16(int64_t row, int64_t seg, float (&v)[16]) const
+    {
+        const int64_t k0 = seg * 16;
+        if (k0 >= K) {                 // pure padding: no byte of the row is read
+#pragma unroll
+            for (int i = 0; i < 16; i++) v[i] = 0.0f;
+            return;
+        }
+        const float gs = *g;
+        const float sc = e4m3_to_f32(sf[row * ld_sf + seg]);
+        const uint8_t *p = codes + row * ld_codes + seg * 8;
+        if (k0 + 16 <= K) {
+            const uint2 q = *reinterpret_cast<const uint2 *>(p);
+            const uint32_t w[2] = {q.x, q.y};
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const uint32_t code = (w[i >> 3] >> (4 * (i & 7))) & 15u;
+                const float prod = e2m1_to_f32(code) * sc;
+                v[i] = prod * gs;
+            }
+            return;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            float val = 0.0f;
+            if (k0 + i < K) {
+                const uint32_t byte = p[i >> 1];
+                const uint32_t code = (i & 1) ? (byte >> 4) : (byte & 15u);
+                const float prod = e2m1_to_f32(code) * sc;
+                val = prod * gs;
+            }
+            v[i] = val;
+        }
+    }
+};
+
+__global__ void prep_weight_kernel(NVFP4Loader ld, int nb, int8_t *__restrict__ out, int64_t ld_out,
+                                   float *__restrict__ scale, int two_pass)
+{
+    row_prep(ld, (int64_t)blockIdx.x, nb, out, ld_out, scale, two_pass != 0);
+}
+
+hipError_t launch_prep_weight(const uint8_t *codes, int64_t ld_codes, const uint8_t *sf, int64_t ld_sf,
+                              const float *g, int64_t n_rows, int64_t K, int8_t *w_s8, int64_t ld_s8,
+                              float *w_scale, bool two_pass, hipStream_t st)
+{
+    const int64_t nb = (K + 255) / 256;
+    const int threads = row_prep_threads(nb);
+    const size_t lds = row_prep_lds_bytes(threads);
+    const bool tp = two_pass || nb > kMaxGroups;
+    NVFP4Loader L{codes, ld_codes, sf, ld_sf, g, K};
+    hipLaunchKernelGGL(prep_weight_kernel, dim3((unsigned)n_rows), dim3(threads), lds, st,
+                       L, (int)nb, w_s8, ld_s8, w_scale, tp ? 1 : 0);
+    return hipGetLastError();
+}
+
+}  // namespace convrot

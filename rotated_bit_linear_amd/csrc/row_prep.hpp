@@ -1,0 +1,218 @@
+// Row preparation engine shared by the activation and weight kernels (gfx950).
+//
+// One workgroup prepares one row: every 256-column block of the row is held by a group
+// of 16 lanes, 16 fp32 values per lane; a wave holds 4 blocks.  The block rotation
+// (ConvRot256: y = x * H/16, H the Sylvester Walsh-Hadamard matrix, paired on activations
+// and weights; ComfyUI Turing Utils README, "Load ConvRot DiT ..." bullet) is evaluated
+// with the butterfly stages in the fixed order h = 1, 2, ..., 128:
+//   phase A: lane t holds elements 16t..16t+15, stages h = 1..8 run inside the lane;
+//   transpose through LDS so lane t holds elements t, t+16, ..., t+240;
+//   phase B: stages h = 16..128 run inside the lane, then the 1/16 scaling;
+//   transpose back so lane t again holds 16 contiguous elements.
+// Every butterfly is the same IEEE add/sub as in the plain definition, so the result is
+// bit-identical to the sequential transform whatever the data layout.
+// Then the row maximum of |y| (exact, order-free), the FP32 scale a/127 and the rounded
+// reciprocal 127/a, and q = clamp(rint(y * r), -127, 127) stored as 16 contiguous bytes.
+//
+// Rows whose K_pad exceeds 64 blocks (16384 columns), or when forced, are streamed twice:
+// pass 1 rotates every block to find the row maximum, pass 2 reloads, rotates again and
+// quantizes (same operations, so the same bits).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace convrot {
+
+constexpr int kLanesPerBlock = 16;          // lanes sharing one 256-column block
+constexpr int kTileStrideF = 272;           // floats per 16x16 transpose tile (256 + 16 pad)
+constexpr int kMaxGroups = 64;              // 1024 threads
+
+// XOR swizzle of 16-byte chunks inside a 16x16 fp32 tile: conflict-free ds_read/ds_write
+// for both row-wise (b128) and column-wise (b32) access with 32 or 64 LDS banks.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+
+__device__ __forceinline__ int tile_index(int row, int col)
+{
+    return row * 16 + (((col >> 2) ^ swz(row)) << 2) + (col & 3);
+}
+
+// Orders LDS traffic between the lanes of one wave (LDS operations of a wave execute in
+// issue order; the fences stop the compiler from moving accesses across this point).
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// In-lane butterflies over the 4 index bits of a 16-element register array.
+__device__ __forceinline__ void butterflies16(float (&v)[16])
+{
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            if (j & h) continue;
+            float u = v[j], w = v[j + h];
+            v[j] = u + w;
+            v[j + h] = u - w;
+        }
+    }
+}
+
+// Full ConvRot256 of the block held by this lane's 16-lane group.  `tile` is the group's
+// private 16x16 LDS tile.  In: v[i] = x[16t + i].  Out: v[i] = y[16t + i].
+__device__ __forceinline__ void convrot256(float (&v)[16], float *tile, int t)
+{
+    butterflies16(v);                                   // stages h = 1, 2, 4, 8
+#pragma unroll
+    for (int c = 0; c < 4; c++) {                       // row t <- v
+        float4 q = make_float4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
+        *reinterpret_cast<float4 *>(tile + t * 16 + ((c ^ swz(t)) << 2)) = q;
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < 16; j++) v[j] = tile[tile_index(j, t)];   // v[j] = x'[16j + t]
+    butterflies16(v);                                   // stages h = 16, 32, 64, 128
+#pragma unroll
+    for (int j = 0; j < 16; j++) v[j] = v[j] * 0.0625f;
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < 16; j++) tile[tile_index(j, t)] = v[j];
+    wave_lds_sync();
+#pragma unroll
+    for (int c = 0; c < 4; c++) {                       // v <- row t
+        float4 q = *reinterpret_cast<const float4 *>(tile + t * 16 + ((c ^ swz(t)) << 2));
+        v[4 * c] = q.x; v[4 * c + 1] = q.y; v[4 * c + 2] = q.z; v[4 * c + 3] = q.w;
+    }
+    wave_lds_sync();
+}
+
+__device__ __forceinline__ float wave_max(float a)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+    return a;
+}
+
+// Workgroup maximum; every thread gets the result.  `red` holds one float per wave.
+__device__ __forceinline__ float block_max(float a, float *red)
+{
+    a = wave_max(a);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = a;
+    __syncthreads();
+    const int nw = blockDim.x >> 6;
+    float m = 0.0f;
+    for (int i = 0; i < nw; i++) m = fmaxf(m, red[i]);
+    return m;
+}
+
+__device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d)
+{
+    uint32_t r = (uint32_t)(uint8_t)(int8_t)(int)a;
+    r |= (uint32_t)(uint8_t)(int8_t)(int)b << 8;
+    r |= (uint32_t)(uint8_t)(int8_t)(int)c << 16;
+    r |= (uint32_t)(uint8_t)(int8_t)(int)d << 24;
+    return r;
+}
+
+__device__ __forceinline__ void quantize_store16(const float (&v)[16], float r, int8_t *dst)
+{
+    float q[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        float t = rintf(v[i] * r);
+        t = fminf(fmaxf(t, -127.0f), 127.0f);
+        q[i] = t;
+    }
+    uint4 o;
+    o.x = pack4(q[0], q[1], q[2], q[3]);
+    o.y = pack4(q[4], q[5], q[6], q[7]);
+    o.z = pack4(q[8], q[9], q[10], q[11]);
+    o.w = pack4(q[12], q[13], q[14], q[15]);
+    *reinterpret_cast<uint4 *>(dst) = o;
+}
+
+// Dynamic LDS of one workgroup: per-group transpose tiles followed by the reduction slots.
+__host__ __device__ constexpr size_t row_prep_lds_bytes(int threads)
+{
+    return (size_t)(threads / kLanesPerBlock) * kTileStrideF * sizeof(float) + 16 * sizeof(float);
+}
+
+// Loader concept: `__device__ void load16(int64_t row, int64_t seg, float (&v)[16]) const`
+// fills v with the fp32 elements 16*seg .. 16*seg+15 of the row (zero for k >= K).
+template <class Loader>
+__device__ __forceinline__ void row_prep(const Loader &ld, int64_t row, int nb,
+                                         int8_t *__restrict__ out, int64_t ld_out,
+                                         float *__restrict__ scale_out, bool two_pass)
+{
+    extern __shared__ float lds[];
+    const int tid = threadIdx.x;
+    const int grp = tid >> 4;
+    const int t = tid & 15;
+    const int G = blockDim.x >> 4;
+    float *tile = lds + grp * kTileStrideF;
+    float *red = lds + G * kTileStrideF;
+    int8_t *orow = out + row * ld_out;
+
+    float v[16];
+    float amax = 0.0f;
+    if (!two_pass) {
+        const int b = grp;
+        if (b < nb) {
+            ld.load16(row, (int64_t)b * 16 + t, v);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; i++) v[i] = 0.0f;
+        }
+        convrot256(v, tile, t);
+#pragma unroll
+        for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(v[i]));
+        const float a = block_max(amax, red);
+        if (b < nb) {
+            const float r = (a == 0.0f) ? 0.0f : 127.0f / a;
+            quantize_store16(v, r, orow + (int64_t)(b * 256 + t * 16));
+        }
+        if (tid == 0) scale_out[row] = (a == 0.0f) ? 0.0f : a / 127.0f;
+        return;
+    }
+    const int nslices = (nb + G - 1) / G;
+    for (int s = 0; s < nslices; s++) {
+        const int b = s * G + grp;
+        if (b < nb) {
+            ld.load16(row, (int64_t)b * 16 + t, v);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; i++) v[i] = 0.0f;
+        }
+        convrot256(v, tile, t);
+#pragma unroll
+        for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(v[i]));
+    }
+    const float a = block_max(amax, red);
+    const float r = (a == 0.0f) ? 0.0f : 127.0f / a;
+    for (int s = 0; s < nslices; s++) {
+        const int b = s * G + grp;
+        if (b < nb) {
+            ld.load16(row, (int64_t)b * 16 + t, v);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; i++) v[i] = 0.0f;
+        }
+        convrot256(v, tile, t);
+        if (b < nb) quantize_store16(v, r, orow + (int64_t)b * 256 + t * 16);
+    }
+    if (tid == 0) scale_out[row] = (a == 0.0f) ? 0.0f : a / 127.0f;
+}
+
+// Threads per workgroup for a row of nb blocks: 4 blocks per wave, all blocks resident
+// when nb <= 64 (one pass), otherwise 1024 threads streaming the row twice.
+inline int row_prep_threads(int64_t nb)
+{
+    int64_t g = nb < kMaxGroups ? nb : kMaxGroups;
+    return (int)(((g + 3) / 4) * 64);
+}
+
+}  // namespace convrot

@@ -1,0 +1,126 @@
+"""The C-ABI library loads, exports every function include/convrot.h declares, carries
+gfx950 code, and validates arguments on the host before anything is enqueued.
+
+No computation runs here: the validation cases use fake (never dereferenced) pointer
+values and return before any HIP call; the no-device case runs only where no GPU is
+visible.
+"""
+import ctypes as C
+
+import pytest
+import torch
+
+import rotated_bit_linear_amd as rbl
+
+OK, INV, DT, MIS, BIG, NODEV = 0, 1, 2, 3, 4, 5
+A16 = 0x10000          # 16-byte aligned fake device address
+ST = None              # default stream
+
+
+def test_library_exports_header_functions():
+    L = rbl.lib()
+    names = rbl.header_functions()
+    assert set(names) >= {"cr_prep_weight_nvfp4", "cr_quant_act", "cr_quant_act_swiglu",
+                          "cr_gemm_s8_rowscale", "cr_linear_nvfp4", "cr_linear_nvfp4_workspace_bytes",
+                          "cr_abi_version", "cr_status_string", "cr_padded_k"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_library_holds_gfx950_code():
+    blob = open(rbl.LIB_PATH, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+
+
+def test_version_and_helpers():
+    L = rbl.lib()
+    assert L.cr_abi_version() == rbl.CR_ABI_VERSION
+    assert [L.cr_padded_k(k) for k in (0, 1, 256, 257, 20000)] == [0, 256, 256, 512, 20224]
+    assert L.cr_status_string(4) == b"CR_ERR_TOO_LARGE"
+
+
+def qa(x=A16, dt=0, ld_x=512, M=4, K=512, q=A16, ld_q=512, s=A16, flags=0):
+    return rbl.lib().cr_quant_act(x, dt, ld_x, M, K, q, ld_q, s, flags, ST)
+
+
+def test_quant_act_validation():
+    assert qa(x=None) == INV
+    assert qa(M=0) == INV
+    assert qa(K=0) == INV
+    assert qa(dt=3) == DT
+    assert qa(ld_x=500) == INV            # ld_x < K
+    assert qa(ld_q=256) == INV            # ld_s8 < K_pad
+    assert qa(x=A16 + 2) == MIS
+    assert qa(ld_x=513, K=512) == MIS      # 1026-byte rows
+    assert qa(K=CR_BIG, ld_x=CR_BIG + 16, ld_q=CR_BIG + 256) == BIG
+    assert qa(flags=4) == INV
+    assert qa(q=A16 + 8) == MIS
+
+
+CR_BIG = rbl.CR_MAX_K_PAD + 1
+
+
+def test_swiglu_validation():
+    L = rbl.lib()
+    assert L.cr_quant_act_swiglu(A16, 0, 1000, 4, 512, A16, 512, A16, 0, ST) == INV   # ld_h < 2F
+    assert L.cr_quant_act_swiglu(A16, 0, 1024, 4, 512, A16, 256, A16, 0, ST) == INV   # ld_s8 < F_pad
+    assert L.cr_quant_act_swiglu(A16, 3, 1024, 4, 512, A16, 512, A16, 0, ST) == DT
+
+
+def pw(codes=A16, ld=256, sf=A16, ld_sf=32, g=A16, n=8, K=512, q=A16, ld_q=512, s=A16, flags=0):
+    return rbl.lib().cr_prep_weight_nvfp4(codes, ld, sf, ld_sf, g, n, K, q, ld_q, s, flags, ST)
+
+
+def test_prep_weight_validation():
+    assert pw(g=None) == INV
+    assert pw(n=0) == INV
+    assert pw(ld=200) == INV               # < ceil(K/2)
+    assert pw(ld_sf=31) == INV             # < ceil(K/16)
+    assert pw(ld=264) == MIS               # not a multiple of 16
+    assert pw(codes=A16 + 4) == MIS
+    assert pw(K=CR_BIG, ld=CR_BIG, ld_sf=CR_BIG, ld_q=CR_BIG + 256) == BIG
+    assert pw(flags=2) == INV
+
+
+def gm(a=A16, lda=512, sa=A16, b=A16, ldb=512, sb=A16, M=8, N=8, K=512, c=A16, dt=0, ldc=8):
+    return rbl.lib().cr_gemm_s8_rowscale(a, lda, sa, b, ldb, sb, M, N, K, c, dt, ldc, ST)
+
+
+def test_gemm_validation():
+    assert gm(K=500, lda=512, ldb=512) == INV      # K_pad not a multiple of 256
+    assert gm(sa=None) == INV
+    assert gm(ldc=7) == INV
+    assert gm(dt=7) == DT
+    assert gm(a=A16 + 1) == MIS
+    assert gm(lda=520) == MIS
+    assert gm(c=A16 + 1) == MIS
+    assert gm(K=rbl.CR_MAX_K_PAD + 256, lda=rbl.CR_MAX_K_PAD + 256, ldb=rbl.CR_MAX_K_PAD + 256) == BIG
+
+
+def test_layer_validation_and_workspace():
+    L = rbl.lib()
+    ws = L.cr_linear_nvfp4_workspace_bytes(64, 256, 512, 0)
+    assert ws >= 64 * 512 + 64 * 4 + 256 * 512 + 256 * 4
+    big = L.cr_linear_nvfp4_workspace_bytes(19989, 21504, 5376, 16 << 20)
+    one = L.cr_linear_nvfp4_workspace_bytes(19989, 21504, 5376, 0)
+    assert big < one                            # 16 MiB tiles: two 3072-row tiles
+    args = dict(x=A16, dt=0, ldx=512, sw=0, M=64, K=512, w=A16, ldw=256, sf=A16, ldsf=32, g=A16, N=256,
+                out=A16, odt=0, ldc=256, ws=0x100000, wsb=ws, mt=0, fl=0)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.cr_linear_nvfp4(a["x"], a["dt"], a["ldx"], a["sw"], a["M"], a["K"], a["w"], a["ldw"], a["sf"],
+                                 a["ldsf"], a["g"], a["N"], a["out"], a["odt"], a["ldc"], a["ws"], a["wsb"],
+                                 a["mt"], a["fl"], ST, None)
+    assert call(wsb=ws - 1) == BIG
+    assert call(ws=0x100010) == MIS                # workspace must be 256-byte aligned
+    assert call(odt=3) == DT
+    assert call(ldc=255) == INV
+    assert call(sw=1) == INV                       # SwiGLU needs ld_x >= 2K
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="valid arguments would launch on a real GPU")
+def test_valid_arguments_report_no_device_without_gpu():
+    assert qa() == NODEV
+    assert pw() == NODEV
+    assert gm() == NODEV
