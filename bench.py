@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Benchmark of the rotated W8A8 NVFP4 linear layer on one MI355X.
+
+One step = the QKV projection layer (qkv_proj [21504, 5376]) and the FFN-down layer with
+fused SwiGLU (fc2 [5376, 14336], H [19989, 28672]) at M = 19989 tokens, each layer being
+activation preparation (main stream) || NVFP4 weight preparation (second stream) -> INT8
+MFMA GEMM with the row-scale epilogue (main stream).  All calls go through the C ABI.
+Inputs are seeded synthetic data resident in HBM before timing starts.
+
+Prints one JSON line: ms/layer (mean over the two layers), per-layer and per-kernel
+timings from HIP events recorded on the launching streams, the GEMM roofline (INT8 MFMA
+peak), the preparation kernels' HBM rates, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms/layer and INT8 TOPS (fraction of peak), QKV and FFN-down at M=19989"
+PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 MFMA, TOP/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+GEMM_SOURCES = ["rotated_bit_linear_amd/csrc/gemm_s8.hip", "rotated_bit_linear_amd/csrc/kernels.hpp"]
+PMC_PROFILE = os.path.join(ROOT, "profiles", "gemm_s8_qkv_m19989_hbm_counters.md")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workloads", default="qkv,ffn_down")
+    ap.add_argument("--max-tile-bytes", type=int, default=0, help="0 = library default")
+    ap.add_argument("--serial", action="store_true", help="prepare weights on the main stream")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=1024)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this size (counter calibration) and exit")
+    ap.add_argument("--json-out", default="")
+    return ap.parse_args()
+
+
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, or None if
+    the GEMM source changed since the counters were taken."""
+    if not os.path.exists(PMC_PROFILE):
+        return None
+    txt = open(PMC_PROFILE).read()
+    m_hash = re.search(r"gemm_source_sha256_16:\s*([0-9a-f]+)", txt)
+    m_bytes = re.search(r"hbm_bytes_per_launch_calibrated:\s*([0-9.eE+]+)", txt)
+    if not (m_hash and m_bytes) or m_hash.group(1) != gemm_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+class Layer:
+    def __init__(self, name, torch, rbl, synth, dev):
+        w = synth.WORKLOADS[name]
+        self.name, self.w = name, w
+        t0 = time.perf_counter()
+        x = synth.make_activation(w)
+        p = synth.make_weight_nvfp4(w)
+        self.host_x, self.host_p = x, p
+        self.x = x.to(dev)
+        self.codes, self.sf = p.codes.to(dev), p.sf.to(dev)
+        self.g = torch.tensor([p.g], dtype=torch.float32, device=dev)
+        kp = w.K_pad
+        self.x_s8 = torch.empty(w.M, kp, dtype=torch.int8, device=dev)
+        self.x_scale = torch.empty(w.M, dtype=torch.float32, device=dev)
+        self.w_s8 = torch.empty(w.N, kp, dtype=torch.int8, device=dev)
+        self.w_scale = torch.empty(w.N, dtype=torch.float32, device=dev)
+        self.out = torch.empty(w.M, w.N, dtype=synth.TORCH_DTYPE[w.out_dtypes[0]], device=dev)
+        self.gen_s = time.perf_counter() - t0
+        es = self.x.element_size()
+        cols = 2 * w.K if w.swiglu else w.K
+        self.act_bytes = w.M * cols * es + w.M * kp + 4 * w.M
+        self.w_bytes = w.N * ((w.K + 1) // 2) + w.N * ((w.K + 15) // 16) + 4 + w.N * kp + 4 * w.N
+        self.gemm_ops = 2 * w.M * w.N * kp
+
+
+def run_layer(L, rbl, s_main, s_aux, ev):
+    """Activation prep || weight prep, then the GEMM; ev = 7 events (or None)."""
+    w = L.w
+    if s_aux is not None:
+        ev[0].record(s_main)
+        s_aux.wait_event(ev[0])
+    ev[1].record(s_main)
+    if w.swiglu:
+        rbl.cr_quant_act_swiglu(L.x, w.K, L.x_s8, L.x_scale, stream=s_main)
+    else:
+        rbl.cr_quant_act(L.x, w.K, L.x_s8, L.x_scale, stream=s_main)
+    ev[2].record(s_main)
+    sw = s_aux if s_aux is not None else s_main
+    ev[3].record(sw)
+    rbl.cr_prep_weight_nvfp4(L.codes, L.sf, L.g, w.K, L.w_s8, L.w_scale, stream=sw)
+    ev[4].record(sw)
+    if s_aux is not None:
+        s_main.wait_event(ev[4])
+    ev[5].record(s_main)
+    rbl.cr_gemm_s8_rowscale(L.x_s8, L.x_scale, L.w_s8, L.w_scale, L.out, stream=s_main)
+    ev[6].record(s_main)
+
+
+def cpu_baseline(layers, sample_rows):
+    """The CPU oracle, as it stands, on a bounded sample: the whole weight preparation
+    (a fixed per-layer cost) plus activation preparation, int32 GEMM and epilogue on the
+    first `sample_rows` rows, extrapolated linearly in M (rows are independent)."""
+    import numpy as np
+
+    import oracle
+    import synth
+    per_layer = []
+    detail = {}
+    t_all = time.perf_counter()
+    for L in layers:
+        w, p = L.w, L.host_p
+        m = min(sample_rows, w.M)
+        xs = L.host_x[:m]
+        xb = xs.contiguous().numpy() if w.x_dtype == synth.DT_FP32 else synth.bits_u16(xs)
+        t0 = time.perf_counter()
+        qw, sw = oracle.prep_weight_nvfp4(p.codes.numpy(), p.sf.numpy(), p.g, w.K)
+        t1 = time.perf_counter()
+        qx, sx = oracle.quant_act(xb, w.x_dtype, w.K, swiglu=w.swiglu)
+        acc = oracle.gemm_s8(qx, qw)
+        oracle.epilogue(acc, sx, sw, w.out_dtypes[0])
+        t2 = time.perf_counter()
+        est = (t1 - t0) + (t2 - t1) * (w.M / m)
+        per_layer.append(est)
+        detail[L.name] = {"weight_prep_s": round(t1 - t0, 3), "rows": m, "rows_s": round(t2 - t1, 3),
+                          "layer_s_extrapolated": round(est, 2)}
+        del qw, qx, acc
+    wall = time.perf_counter() - t_all
+    return {
+        "value": round(1000.0 * sum(per_layer) / len(per_layer), 1),
+        "unit": "ms/layer",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"whole weight preparation + first {sample_rows} rows of activation prep, int32 GEMM "
+                   f"and epilogue per layer, extrapolated linearly to M=19989; {wall:.1f} s of CPU work"),
+        "detail": detail,
+    }
+
+
+def copy_calibration(mib: int):
+    import torch
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (the layer is data-parallel over tokens "
+              "with no communication; multi-GPU sharding is not built). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return
+
+    import torch
+
+    import rotated_bit_linear_amd as rbl
+    import synth
+
+    dev = torch.device("cuda:0")
+    rbl.lib()
+    names = [n.strip() for n in args.workloads.split(",") if n.strip()]
+    layers = []
+    for n in names:
+        print(f"bench: generating {n} ...", file=sys.stderr, flush=True)
+        layers.append(Layer(n, torch, rbl, synth, dev))
+    torch.cuda.synchronize()
+
+    s_main = torch.cuda.current_stream()
+    s_aux = None if args.serial else torch.cuda.Stream()
+    K, W = args.steps, args.warmup
+    mk = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+    evs = [[[mk() for _ in range(7)] for _ in layers] for _ in range(K)]
+    scratch = [[mk() for _ in range(7)] for _ in layers]
+
+    print(f"bench: warmup {W} steps", file=sys.stderr, flush=True)
+    for _ in range(W):
+        for li, L in enumerate(layers):
+            run_layer(L, rbl, s_main, s_aux, scratch[li])
+    torch.cuda.synchronize()
+
+    print(f"bench: timing {K} steps", file=sys.stderr, flush=True)
+    start, end = mk(), mk()
+    t0 = time.perf_counter()
+    start.record(s_main)
+    for k in range(K):
+        for li, L in enumerate(layers):
+            run_layer(L, rbl, s_main, s_aux, evs[k][li])
+    end.record(s_main)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1000.0
+    ms_per_step = start.elapsed_time(end) / K
+
+    layer_info = {}
+    for li, L in enumerate(layers):
+        def mean(a, b):
+            return sum(evs[k][li][a].elapsed_time(evs[k][li][b]) for k in range(K)) / K
+        t_layer = mean(1, 6)
+        t_act, t_w, t_g = mean(1, 2), mean(3, 4), mean(5, 6)
+        layer_info[L.name] = {
+            "M": L.w.M, "N": L.w.N, "K": L.w.K, "K_pad": L.w.K_pad, "swiglu": L.w.swiglu,
+            "ms": round(t_layer, 4),
+            "gemm_ms": round(t_g, 4),
+            "gemm_tops": round(L.gemm_ops / (t_g * 1e-3) / 1e12, 1),
+            "gemm_frac_peak": round(L.gemm_ops / (t_g * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+            "layer_tops": round(L.gemm_ops / (t_layer * 1e-3) / 1e12, 1),
+            "act_prep_ms": round(t_act, 4),
+            "act_prep_gbs": round(L.act_bytes / (t_act * 1e-3) / 1e9, 1),
+            "weight_prep_ms": round(t_w, 4),
+            "weight_prep_gbs": round(L.w_bytes / (t_w * 1e-3) / 1e9, 1),
+        }
+
+    # the product entry point computes the same layer (one untimed call per layer)
+    for L in layers:
+        ref = L.out.clone()
+        got = rbl.linear_nvfp4(L.x, L.codes, L.sf, L.g, L.w.K, out_dtype=L.out.dtype, swiglu=L.w.swiglu,
+                               max_tile_bytes=args.max_tile_bytes, aux_stream=s_aux)
+        torch.cuda.synchronize()
+        if not torch.equal(ref, got):
+            raise SystemExit(f"bench: cr_linear_nvfp4 differs from the component calls on {L.name}")
+        del got
+
+    dom = layers[0]
+    dom_info = layer_info[dom.name]
+    achieved = dom.gemm_ops / (dom_info["gemm_ms"] * 1e-3) / 1e12
+    traffic = counter_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(sum(v["ms"] for v in layer_info.values()) / len(layer_info), 4),
+        "unit": "ms/layer",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": "+".join(L.w.note for L in layers),
+            "M": layers[0].w.M,
+            "layers": names,
+            "inputs": "bf16 activations ~N(0,1) (QKV: 1% channels x20), NVFP4 weights from 0.02*N(0,1)",
+            "weight_prep_stream": "serial" if args.serial else "second stream",
+            "max_tile_bytes": args.max_tile_bytes or rbl.DEFAULT_MAX_TILE_BYTES,
+        },
+        "roofline": {
+            "kernel": f"gemm_s8_rowscale ({dom.name}: M={dom.w.M} N={dom.w.N} K_pad={dom.w.K_pad})",
+            "bound": "mfma",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_INT8_TOPS,
+            "unit": "TOP/s",
+            "frac": round(achieved / PEAK_INT8_TOPS, 4),
+            "traffic": traffic,
+        },
+        "layers": layer_info,
+        "wall_ms_timed_region": round(wall_ms, 2),
+        "gemm_source_sha256_16": gemm_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(layers, args.cpu_sample_rows)
+    line = json.dumps(result)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

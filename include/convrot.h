@@ -127,6 +127,15 @@ cr_status cr_quant_act_swiglu(const void *h, cr_dtype h_dtype, int64_t ld_h, int
                               uint32_t flags, hipStream_t stream);
 
 /*
+ * Unfused SwiGLU to FP32 (the ComfyUI Turing Utils README compares the fused
+ * SwiGLU + rotation + A8 path against an unfused activation): out[m, k] =
+ * swish(h[m, k]) * h[m, F + k] with the same element arithmetic as cr_quant_act_swiglu.
+ *   h [M, ld_h] of h_dtype (element-aligned), ld_h >= 2F; out [M, ld_out] float, ld_out >= F.
+ */
+cr_status cr_swiglu(const void *h, cr_dtype h_dtype, int64_t ld_h, int64_t M, int64_t F,
+                    float *out, int64_t ld_out, hipStream_t stream);
+
+/*
  * Row-scaled INT8 GEMM with the dequantizing epilogue fused (the int32 accumulator never
  * reaches memory unless c_dtype is CR_I32; MiniMax H3 explainer, fused-kernel paragraph).
  *   a_s8 [M, lda] int8 and b_s8 [N, ldb] int8, both K-contiguous; K_pad a multiple of 256.

@@ -30,6 +30,7 @@ def lib():
         L = C.CDLL(_build.LIB)
         i64, f32, u8, vp = C.c_int64, C.c_float, C.c_uint8, C.c_void_p
         sig = {
+            "or_num_threads": (C.c_int, []),
             "or_padded_k": (i64, [i64]),
             "or_e2m1": (f32, [u8]),
             "or_e4m3": (f32, [u8]),
@@ -75,6 +76,10 @@ def _elem_dtype(dtype: int):
 
 def padded_k(k: int) -> int:
     return int(lib().or_padded_k(k))
+
+
+def num_threads() -> int:
+    return int(lib().or_num_threads())
 
 
 # ------------------------------------------------------------------ formats ----

@@ -47,6 +47,20 @@
 #include <stdlib.h>
 #include <math.h>
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the row loops below run on (OpenMP over independent rows only). */
+int or_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
 #define OR_DT_BF16 0
 #define OR_DT_FP16 1
 #define OR_DT_FP32 2

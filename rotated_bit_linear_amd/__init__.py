@@ -59,6 +59,7 @@ def lib() -> C.CDLL:
             "cr_prep_weight_nvfp4": (C.c_int, [vp, i64, vp, i64, vp, i64, i64, vp, i64, vp, u32, vp]),
             "cr_quant_act": (C.c_int, [vp, C.c_int, i64, i64, i64, vp, i64, vp, u32, vp]),
             "cr_quant_act_swiglu": (C.c_int, [vp, C.c_int, i64, i64, i64, vp, i64, vp, u32, vp]),
+            "cr_swiglu": (C.c_int, [vp, C.c_int, i64, i64, i64, vp, i64, vp]),
             "cr_gemm_s8_rowscale": (C.c_int, [vp, i64, vp, vp, i64, vp, i64, i64, i64, vp, C.c_int, i64, vp]),
             "cr_linear_nvfp4_workspace_bytes": (sz, [i64, i64, i64, sz]),
             "cr_linear_nvfp4": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, i64, vp, i64, vp, i64,
@@ -137,6 +138,13 @@ def cr_quant_act_swiglu(h, F, x_s8, x_scale, flags=0, stream=None):
     _check("cr_quant_act_swiglu", lib().cr_quant_act_swiglu(
         _ptr(h), _TORCH_TO_CR[h.dtype], ld_h, M, F, _ptr(x_s8), ld_s8, _ptr(x_scale), flags,
         _stream(stream)))
+
+
+def cr_swiglu(h, F, out, stream=None):
+    M, ld_h = _rows_ld(h)
+    _, ld_out = _rows_ld(out)
+    _check("cr_swiglu", lib().cr_swiglu(_ptr(h), _TORCH_TO_CR[h.dtype], ld_h, M, F, _ptr(out), ld_out,
+                                        _stream(stream)))
 
 
 def cr_gemm_s8_rowscale(a_s8, a_scale, b_s8, b_scale, c, stream=None, M=None, N=None):

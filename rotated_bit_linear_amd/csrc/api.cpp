@@ -216,6 +216,19 @@ cr_status cr_quant_act_swiglu(const void *h, cr_dtype h_dtype, int64_t ld_h, int
                                                      (flags & CR_FLAG_FORCE_TWO_PASS) != 0, stream));
 }
 
+cr_status cr_swiglu(const void *h, cr_dtype h_dtype, int64_t ld_h, int64_t M, int64_t F,
+                    float *out, int64_t ld_out, hipStream_t stream)
+{
+    if (!h || !out) return CR_ERR_INVALID_ARG;
+    if (h_dtype != CR_BF16 && h_dtype != CR_FP16 && h_dtype != CR_FP32) return CR_ERR_UNSUPPORTED_DTYPE;
+    if (M < 1 || F < 1 || F > ((int64_t)1 << 40) || M > ((int64_t)1 << 40) / F) return CR_ERR_INVALID_ARG;
+    if (ld_h < 2 * F || ld_out < F) return CR_ERR_INVALID_ARG;
+    if (!aligned(h, (size_t)elem_size(h_dtype)) || !aligned(out, 4)) return CR_ERR_MISALIGNED;
+    cr_status s = current_device_ok();
+    if (s != CR_OK) return s;
+    return from_hip(convrot::launch_swiglu(h, (int)h_dtype, ld_h, M, F, out, ld_out, stream));
+}
+
 cr_status cr_gemm_s8_rowscale(const int8_t *a_s8, int64_t lda, const float *a_scale,
                               const int8_t *b_s8, int64_t ldb, const float *b_scale,
                               int64_t M, int64_t N, int64_t K_pad,
@@ -269,7 +282,8 @@ cr_status cr_linear_nvfp4(const void *x, cr_dtype x_dtype, int64_t ld_x, int swi
 
     const bool tp = (flags & CR_FLAG_FORCE_TWO_PASS) != 0;
     const int64_t es = elem_size(out_dtype);
-    const bool overlap = s_aux != nullptr && s_aux != s_main && p.nchunks > 1;
+    // with a second stream the first weight tile is prepared while the activation is
+    const bool overlap = s_aux != nullptr && s_aux != s_main;
     EventSet evs(overlap);
     if (overlap && !evs.ok) return CR_ERR_LAUNCH;
     hipEvent_t ev_start = evs.ev[0], ev_prep[2] = {evs.ev[1], evs.ev[2]}, ev_gemm[2] = {evs.ev[3], evs.ev[4]};

@@ -15,6 +15,9 @@ hipError_t launch_quant_act_swiglu(const void *h, int dtype, int64_t ld_h, int64
                                    int8_t *x_s8, int64_t ld_s8, float *x_scale, bool two_pass,
                                    hipStream_t st);
 
+hipError_t launch_swiglu(const void *h, int dtype, int64_t ld_h, int64_t M, int64_t F, float *out,
+                         int64_t ld_out, hipStream_t st);
+
 hipError_t launch_prep_weight(const uint8_t *codes, int64_t ld_codes, const uint8_t *sf, int64_t ld_sf,
                               const float *g, int64_t n_rows, int64_t K, int8_t *w_s8, int64_t ld_s8,
                               float *w_scale, bool two_pass, hipStream_t st);

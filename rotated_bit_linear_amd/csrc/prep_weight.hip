@@ -80,10 +80,11 @@ struct NVFP4Loader {
     }
 };
 
+template <int RB>
 __global__ void prep_weight_kernel(NVFP4Loader ld, int nb, int8_t *__restrict__ out, int64_t ld_out,
                                    float *__restrict__ scale, int two_pass)
 {
-    row_prep(ld, (int64_t)blockIdx.x, nb, out, ld_out, scale, two_pass != 0);
+    row_prep<NVFP4Loader, RB>(ld, (int64_t)blockIdx.x, nb, out, ld_out, scale, two_pass != 0);
 }
 
 hipError_t launch_prep_weight(const uint8_t *codes, int64_t ld_codes, const uint8_t *sf, int64_t ld_sf,
@@ -91,12 +92,15 @@ hipError_t launch_prep_weight(const uint8_t *codes, int64_t ld_codes, const uint
                               float *w_scale, bool two_pass, hipStream_t st)
 {
     const int64_t nb = (K + 255) / 256;
-    const int threads = row_prep_threads(nb);
-    const size_t lds = row_prep_lds_bytes(threads);
-    const bool tp = two_pass || nb > kMaxGroups;
+    const RowPrepShape s = row_prep_shape(nb, two_pass);
+    const size_t lds = row_prep_lds_bytes(s.threads);
     NVFP4Loader L{codes, ld_codes, sf, ld_sf, g, K};
-    hipLaunchKernelGGL(prep_weight_kernel, dim3((unsigned)n_rows), dim3(threads), lds, st,
-                       L, (int)nb, w_s8, ld_s8, w_scale, tp ? 1 : 0);
+    if (s.rb == 2)
+        hipLaunchKernelGGL(prep_weight_kernel<2>, dim3((unsigned)n_rows), dim3(s.threads), lds, st,
+                           L, (int)nb, w_s8, ld_s8, w_scale, 0);
+    else
+        hipLaunchKernelGGL(prep_weight_kernel<1>, dim3((unsigned)n_rows), dim3(s.threads), lds, st,
+                           L, (int)nb, w_s8, ld_s8, w_scale, s.two_pass ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -149,45 +149,64 @@ struct SwigluLoader {
     }
 };
 
-template <class Loader>
+// Unfused SwiGLU: out[m, k] = swish(h[m, k]) * h[m, F + k] in FP32 (same element function
+// as the fused path).  One thread per element, grid-stride over rows.
+template <int DT>
+__global__ void swiglu_kernel(const typename Elem<DT>::T *__restrict__ h, int64_t ld_h, int64_t M, int64_t F,
+                              float *__restrict__ out, int64_t ld_out)
+{
+    const int64_t total = M * F;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t m = i / F, k = i - m * F;
+        const float a = Elem<DT>::cvt(h[m * ld_h + k]);
+        const float b = Elem<DT>::cvt(h[m * ld_h + F + k]);
+        out[m * ld_out + k] = swiglu_elem(a, b);
+    }
+}
+
+template <class Loader, int RB>
 __global__ void quant_act_kernel(Loader ld, int nb, int8_t *__restrict__ out, int64_t ld_out,
                                  float *__restrict__ scale, int two_pass)
 {
-    row_prep(ld, (int64_t)blockIdx.x, nb, out, ld_out, scale, two_pass != 0);
+    row_prep<Loader, RB>(ld, (int64_t)blockIdx.x, nb, out, ld_out, scale, two_pass != 0);
 }
 
 // --------------------------------------------------------------------- launchers ----
+
+template <class Loader>
+static hipError_t launch_rows(const Loader &L, int64_t rows, int64_t nb, int8_t *out, int64_t ld_out,
+                              float *scale, bool force_two_pass, hipStream_t st)
+{
+    const RowPrepShape s = row_prep_shape(nb, force_two_pass);
+    const size_t lds = row_prep_lds_bytes(s.threads);
+    if (s.rb == 2)
+        hipLaunchKernelGGL((quant_act_kernel<Loader, 2>), dim3((unsigned)rows), dim3(s.threads), lds, st,
+                           L, (int)nb, out, ld_out, scale, 0);
+    else
+        hipLaunchKernelGGL((quant_act_kernel<Loader, 1>), dim3((unsigned)rows), dim3(s.threads), lds, st,
+                           L, (int)nb, out, ld_out, scale, s.two_pass ? 1 : 0);
+    return hipGetLastError();
+}
 
 template <int DT>
 static hipError_t launch_act(const void *x, int64_t ld_x, int64_t M, int64_t K, int8_t *x_s8,
                              int64_t ld_s8, float *x_scale, bool two_pass, hipStream_t st)
 {
-    const int64_t nb = (K + 255) / 256;
-    const int threads = row_prep_threads(nb);
-    const size_t lds = row_prep_lds_bytes(threads);
-    const bool tp = two_pass || nb > kMaxGroups;
     ActLoader<DT> L{static_cast<const typename Elem<DT>::T *>(x), ld_x, K,
                     ((uintptr_t)x % 16 == 0) && ((ld_x * (int64_t)sizeof(typename Elem<DT>::T)) % 16 == 0)};
-    hipLaunchKernelGGL(quant_act_kernel<ActLoader<DT>>, dim3((unsigned)M), dim3(threads), lds, st,
-                       L, (int)nb, x_s8, ld_s8, x_scale, tp ? 1 : 0);
-    return hipGetLastError();
+    return launch_rows(L, M, (K + 255) / 256, x_s8, ld_s8, x_scale, two_pass, st);
 }
 
 template <int DT>
 static hipError_t launch_swiglu(const void *h, int64_t ld_h, int64_t M, int64_t F, int8_t *x_s8,
                                 int64_t ld_s8, float *x_scale, bool two_pass, hipStream_t st)
 {
-    const int64_t nb = (F + 255) / 256;
-    const int threads = row_prep_threads(nb);
-    const size_t lds = row_prep_lds_bytes(threads);
-    const bool tp = two_pass || nb > kMaxGroups;
     const int64_t es = (int64_t)sizeof(typename Elem<DT>::T);
     const bool row_ok = ((uintptr_t)h % 16 == 0) && ((ld_h * es) % 16 == 0);
     SwigluLoader<DT> L{static_cast<const typename Elem<DT>::T *>(h), ld_h, F, row_ok,
                        row_ok && ((F * es) % 16 == 0)};
-    hipLaunchKernelGGL(quant_act_kernel<SwigluLoader<DT>>, dim3((unsigned)M), dim3(threads), lds, st,
-                       L, (int)nb, x_s8, ld_s8, x_scale, tp ? 1 : 0);
-    return hipGetLastError();
+    return launch_rows(L, M, (F + 255) / 256, x_s8, ld_s8, x_scale, two_pass, st);
 }
 
 hipError_t launch_quant_act(const void *x, int dtype, int64_t ld_x, int64_t M, int64_t K,
@@ -200,6 +219,25 @@ hipError_t launch_quant_act(const void *x, int dtype, int64_t ld_x, int64_t M, i
     case 2: return launch_act<2>(x, ld_x, M, K, x_s8, ld_s8, x_scale, two_pass, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_swiglu(const void *h, int dtype, int64_t ld_h, int64_t M, int64_t F, float *out,
+                         int64_t ld_out, hipStream_t st)
+{
+    const int64_t total = M * F;
+    const int threads = 256;
+    const int64_t want = (total + threads - 1) / threads;
+    const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
+    switch (dtype) {
+    case 0: hipLaunchKernelGGL(swiglu_kernel<0>, dim3(blocks), dim3(threads), 0, st,
+                               static_cast<const uint16_t *>(h), ld_h, M, F, out, ld_out); break;
+    case 1: hipLaunchKernelGGL(swiglu_kernel<1>, dim3(blocks), dim3(threads), 0, st,
+                               static_cast<const uint16_t *>(h), ld_h, M, F, out, ld_out); break;
+    case 2: hipLaunchKernelGGL(swiglu_kernel<2>, dim3(blocks), dim3(threads), 0, st,
+                               static_cast<const float *>(h), ld_h, M, F, out, ld_out); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_quant_act_swiglu(const void *h, int dtype, int64_t ld_h, int64_t M, int64_t F,

@@ -26,7 +26,7 @@ namespace convrot {
 
 constexpr int kLanesPerBlock = 16;          // lanes sharing one 256-column block
 constexpr int kTileStrideF = 272;           // floats per 16x16 transpose tile (256 + 16 pad)
-constexpr int kMaxGroups = 64;              // 1024 threads
+constexpr int kMaxGroups = 32;              // 512 threads
 
 // XOR swizzle of 16-byte chunks inside a 16x16 fp32 tile: conflict-free ds_read/ds_write
 // for both row-wise (b128) and column-wise (b32) access with 32 or 64 LDS banks.
@@ -143,7 +143,11 @@ __host__ __device__ constexpr size_t row_prep_lds_bytes(int threads)
 
 // Loader concept: `__device__ void load16(int64_t row, int64_t seg, float (&v)[16]) const`
 // fills v with the fp32 elements 16*seg .. 16*seg+15 of the row (zero for k >= K).
-template <class Loader>
+//
+// One pass (two_pass == false): the G = blockDim/16 groups hold RB blocks each, block
+// grp + r*G in v[r]; requires nb <= RB*G.  Two passes: RB is 1 and the row is streamed in
+// slices of G blocks, once for the maximum and once for the codes.
+template <class Loader, int RB>
 __device__ __forceinline__ void row_prep(const Loader &ld, int64_t row, int nb,
                                          int8_t *__restrict__ out, int64_t ld_out,
                                          float *__restrict__ scale_out, bool two_pass)
@@ -157,27 +161,33 @@ __device__ __forceinline__ void row_prep(const Loader &ld, int64_t row, int nb,
     float *red = lds + G * kTileStrideF;
     int8_t *orow = out + row * ld_out;
 
-    float v[16];
     float amax = 0.0f;
     if (!two_pass) {
-        const int b = grp;
-        if (b < nb) {
-            ld.load16(row, (int64_t)b * 16 + t, v);
-        } else {
+        float v[RB][16];
 #pragma unroll
-            for (int i = 0; i < 16; i++) v[i] = 0.0f;
+        for (int r = 0; r < RB; r++) {
+            const int b = grp + r * G;
+            if (b < nb) {
+                ld.load16(row, (int64_t)b * 16 + t, v[r]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; i++) v[r][i] = 0.0f;
+            }
+            convrot256(v[r], tile, t);
+#pragma unroll
+            for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(v[r][i]));
         }
-        convrot256(v, tile, t);
-#pragma unroll
-        for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(v[i]));
         const float a = block_max(amax, red);
-        if (b < nb) {
-            const float r = (a == 0.0f) ? 0.0f : 127.0f / a;
-            quantize_store16(v, r, orow + (int64_t)(b * 256 + t * 16));
+        const float rcp = (a == 0.0f) ? 0.0f : 127.0f / a;
+#pragma unroll
+        for (int r = 0; r < RB; r++) {
+            const int b = grp + r * G;
+            if (b < nb) quantize_store16(v[r], rcp, orow + (int64_t)b * 256 + t * 16);
         }
         if (tid == 0) scale_out[row] = (a == 0.0f) ? 0.0f : a / 127.0f;
         return;
     }
+    float v[16];
     const int nslices = (nb + G - 1) / G;
     for (int s = 0; s < nslices; s++) {
         const int b = s * G + grp;
@@ -192,7 +202,7 @@ __device__ __forceinline__ void row_prep(const Loader &ld, int64_t row, int nb,
         for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(v[i]));
     }
     const float a = block_max(amax, red);
-    const float r = (a == 0.0f) ? 0.0f : 127.0f / a;
+    const float rcp = (a == 0.0f) ? 0.0f : 127.0f / a;
     for (int s = 0; s < nslices; s++) {
         const int b = s * G + grp;
         if (b < nb) {
@@ -202,17 +212,33 @@ __device__ __forceinline__ void row_prep(const Loader &ld, int64_t row, int nb,
             for (int i = 0; i < 16; i++) v[i] = 0.0f;
         }
         convrot256(v, tile, t);
-        if (b < nb) quantize_store16(v, r, orow + (int64_t)b * 256 + t * 16);
+        if (b < nb) quantize_store16(v, rcp, orow + (int64_t)b * 256 + t * 16);
     }
     if (tid == 0) scale_out[row] = (a == 0.0f) ? 0.0f : a / 127.0f;
 }
 
-// Threads per workgroup for a row of nb blocks: 4 blocks per wave, all blocks resident
-// when nb <= 64 (one pass), otherwise 1024 threads streaming the row twice.
-inline int row_prep_threads(int64_t nb)
+// Launch shape of a row of nb blocks: at most 512 threads (32 groups, 35 KB of LDS).
+struct RowPrepShape {
+    int threads;   // workgroup size, a multiple of 64
+    int rb;        // blocks held per 16-lane group in one-pass mode (1 or 2)
+    bool two_pass;
+};
+
+inline RowPrepShape row_prep_shape(int64_t nb, bool force_two_pass)
 {
-    int64_t g = nb < kMaxGroups ? nb : kMaxGroups;
-    return (int)(((g + 3) / 4) * 64);
+    RowPrepShape s{};
+    if (!force_two_pass && nb <= 2 * kMaxGroups) {
+        s.rb = nb <= kMaxGroups ? 1 : 2;
+        const int64_t groups = (nb + s.rb - 1) / s.rb;
+        s.threads = (int)(((groups + 3) / 4) * 64);
+        s.two_pass = false;
+    } else {
+        const int64_t groups = nb < kMaxGroups ? nb : kMaxGroups;
+        s.threads = (int)(((groups + 3) / 4) * 64);
+        s.rb = 1;
+        s.two_pass = true;
+    }
+    return s;
 }
 
 }  // namespace convrot

@@ -1,0 +1,70 @@
+"""GPU parity at the five workload sizes (tiny, QKV M=4096, QKV M=19989, FFN-down with
+SwiGLU M=19989, long-K fp16), in the launch configuration the benchmark times
+(cr_linear_nvfp4, default tile bound, weight preparation on a second stream).
+
+Full checks: every S8 code and row scale of the activation and of the weight, bit-exact.
+Sampled checks: the layer output on a seeded sample of rows that always holds the M tail
+and every zero/tiny row, against the oracle's int32 GEMM and epilogue on those rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rotated_bit_linear_amd as rbl
+import synth
+from helpers import TOL, assert_bits_equal, dev, out_f64, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE_ROWS = 512
+
+
+def host_bits(x: torch.Tensor, dt: int) -> np.ndarray:
+    return x.contiguous().numpy() if dt == synth.DT_FP32 else synth.bits_u16(x)
+
+
+@pytest.mark.parametrize("name", ["tiny", "qkv_m4096", "qkv", "ffn_down", "longk"])
+def test_workload_parity(name):
+    w = synth.WORKLOADS[name]
+    x = synth.make_activation(w)
+    p = synth.make_weight_nvfp4(w)
+    xb = host_bits(x, w.x_dtype)
+    gs = torch.tensor([p.g], dtype=torch.float32, device=dev())
+    xd, cd, sd = x.to(dev()), p.codes.to(dev()), p.sf.to(dev())
+    aux = torch.cuda.Stream()
+
+    say(f"{name}: cr_quant_act{'_swiglu' if w.swiglu else ''} M={w.M} K={w.K}")
+    qx, sx = rbl.quant_act(xd, w.K, swiglu=w.swiglu)
+    say(f"{name}: cr_prep_weight_nvfp4 N={w.N} K={w.K}")
+    qw, sw = rbl.prep_weight_nvfp4(cd, sd, gs, w.K)
+    outs = {}
+    for odt in w.out_dtypes:
+        say(f"{name}: cr_linear_nvfp4 M={w.M} N={w.N} K={w.K} out={odt} (default tiles, aux stream)")
+        outs[odt] = rbl.linear_nvfp4(xd, cd, sd, gs, w.K, out_dtype=synth.TORCH_DTYPE[odt], swiglu=w.swiglu,
+                                     aux_stream=aux)
+    torch.cuda.synchronize()
+
+    rqx, rsx = oracle.quant_act(xb, w.x_dtype, w.K, swiglu=w.swiglu)
+    assert_bits_equal(qx.cpu().numpy(), rqx, f"{name} x_s8")
+    assert_bits_equal(sx.cpu().numpy().view(np.uint32), rsx.view(np.uint32), f"{name} x_scale")
+    del qx
+    rqw, rsw = oracle.prep_weight_nvfp4(p.codes.numpy(), p.sf.numpy(), p.g, w.K)
+    assert_bits_equal(qw.cpu().numpy(), rqw, f"{name} w_s8")
+    assert_bits_equal(sw.cpu().numpy().view(np.uint32), rsw.view(np.uint32), f"{name} w_scale")
+    del qw
+
+    zero, tiny = synth.special_rows(w)
+    rows = synth.sample_rows(w.M, SAMPLE_ROWS, w.seed, torch.cat([zero, tiny]))
+    if w.M <= 64:
+        rows = torch.arange(w.M)
+    r = rows.numpy()
+    acc = oracle.gemm_s8(np.ascontiguousarray(rqx[r]), rqw)
+    for odt, out in outs.items():
+        ref = oracle.epilogue(acc, rsx[r], rsw, odt)
+        got = out[rows.to(dev())].cpu()
+        err = rel_l2(out_f64(got, odt), out_f64(ref, odt))
+        print(f"{name} out={odt}: rows checked={len(r)} rel_l2={err:.3e}")
+        assert err <= TOL[odt], err
+        if len(zero):
+            assert (out[zero.to(dev())] == 0).all()

@@ -1,0 +1,245 @@
+"""GPU parity of each entry point against the CPU oracle on small, ragged inputs.
+
+Bar: S8 codes, row scales and int32 accumulators bit-exact; dequantized outputs within
+relative L2 1e-3 (bf16/fp16) or 1e-5 (fp32) of the oracle's output in the same dtype.
+Every call goes through the C ABI (rotated_bit_linear_amd's ctypes binding).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rotated_bit_linear_amd as rbl
+import synth
+from helpers import TOL, assert_bits_equal, dev, out_f64, rel_l2, say, u16
+
+pytestmark = pytest.mark.gpu
+
+DT_T = {synth.DT_BF16: torch.bfloat16, synth.DT_FP16: torch.float16, synth.DT_FP32: torch.float32}
+
+
+def host_bits(x: torch.Tensor, dt: int) -> np.ndarray:
+    return x.contiguous().numpy() if dt == synth.DT_FP32 else synth.bits_u16(x)
+
+
+def make_x(M, cols, dt, seed, ld=None, special=False):
+    g = torch.Generator().manual_seed(seed)
+    ld = ld or cols
+    x = torch.randn(M, ld, generator=g) * 2
+    x[:, cols:] = torch.randn(M, ld - cols, generator=g) * 1e4          # garbage past K
+    if special and M >= 4:
+        x[1, :] = 0.0
+        x[2, :cols] *= 1e-4
+        x[3, : min(cols, 7)] *= 300.0
+    return x.to(DT_T[dt])
+
+
+# ------------------------------------------------------------------ SwiGLU bits ----
+
+@pytest.mark.parametrize("dt", [synth.DT_BF16, synth.DT_FP16])
+def test_swiglu_exhaustive_gate_values(dt):
+    F = 65536
+    gate = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    g = torch.Generator().manual_seed(5)
+    value = torch.randn(F, generator=g).to(DT_T[dt]).view(torch.int16)
+    h = torch.cat([gate, value]).view(DT_T[dt]).reshape(1, 2 * F)
+    out = torch.empty(1, F, dtype=torch.float32, device=dev())
+    say(f"cr_swiglu dtype={dt} F={F} all gate bit patterns")
+    rbl.cr_swiglu(h.to(dev()), F, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()[0]
+    hb = synth.bits_u16(h)[0]
+    conv = oracle.bf16_to_f32 if dt == synth.DT_BF16 else oracle.fp16_to_f32
+    ref = oracle.swiglu(conv(hb[:F]), conv(hb[F:]))
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert_bits_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32), "swiglu bits")
+
+
+def test_swiglu_fp32_random_and_edges():
+    g = torch.Generator().manual_seed(6)
+    F = 1 << 20
+    gate = torch.cat([torch.randn(F - 16, generator=g) * 8,
+                      torch.tensor([0.0, -0.0, 88.7, -88.7, 89.0, -89.0, 103.9, -103.9, 104.5, -104.5,
+                                    1e-30, -1e-30, 3e38, -3e38, 1e-45, -1e-45])])
+    value = torch.randn(F, generator=g)
+    h = torch.cat([gate, value]).reshape(1, 2 * F)
+    out = torch.empty(1, F, dtype=torch.float32, device=dev())
+    say("cr_swiglu fp32 random + edge gates")
+    rbl.cr_swiglu(h.to(dev()), F, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()[0]
+    ref = oracle.swiglu(gate.numpy(), value.numpy())
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert_bits_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32), "swiglu fp32 bits")
+
+
+# ------------------------------------------------------------ activation prep ----
+
+ACT_CASES = [
+    # dt, M, K, ld, special, forced two-pass
+    (synth.DT_BF16, 64, 512, 512, False, False),
+    (synth.DT_BF16, 37, 300, 304, True, False),
+    (synth.DT_FP16, 33, 1000, 1016, True, False),
+    (synth.DT_FP32, 17, 777, 780, True, False),
+    (synth.DT_BF16, 5, 16384, 16384, False, False),
+    (synth.DT_BF16, 5, 16385, 16392, True, False),    # 65 blocks: two-pass by size
+    (synth.DT_FP16, 3, 20000, 20000, True, False),
+    (synth.DT_BF16, 11, 5376, 5376, True, True),      # forced two-pass
+    (synth.DT_FP32, 1, 1, 4, False, False),           # one element
+]
+
+
+@pytest.mark.parametrize("dt,M,K,ld,special,forced", ACT_CASES,
+                         ids=[f"dt{c[0]}-M{c[1]}-K{c[2]}-ld{c[3]}{'-tp' if c[5] else ''}" for c in ACT_CASES])
+def test_quant_act_bit_exact(dt, M, K, ld, special, forced):
+    x = make_x(M, K, dt, seed=M * 7 + K, ld=ld, special=special)
+    say(f"cr_quant_act dt={dt} M={M} K={K} ld={ld} forced_two_pass={forced}")
+    q, s = rbl.quant_act(x.to(dev()), K, flags=rbl.CR_FLAG_FORCE_TWO_PASS if forced else 0)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant_act(host_bits(x, dt), dt, K)
+    assert_bits_equal(q.cpu().numpy(), rq, "x_s8")
+    assert_bits_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32), "x_scale")
+
+
+def test_two_pass_equals_one_pass_activation():
+    x = make_x(50, 4000, synth.DT_BF16, seed=3, special=True).to(dev())
+    say("cr_quant_act one-pass vs forced two-pass M=50 K=4000")
+    q1, s1 = rbl.quant_act(x, 4000)
+    q2, s2 = rbl.quant_act(x, 4000, flags=rbl.CR_FLAG_FORCE_TWO_PASS)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2) and torch.equal(s1, s2)
+
+
+SWI_CASES = [
+    (synth.DT_BF16, 32, 14336),
+    (synth.DT_BF16, 9, 300),        # value half not 16-byte aligned: element loads
+    (synth.DT_FP32, 7, 1000),
+    (synth.DT_FP16, 5, 640),
+    (synth.DT_BF16, 3, 8200),
+]
+
+
+@pytest.mark.parametrize("dt,M,F", SWI_CASES, ids=[f"dt{c[0]}-M{c[1]}-F{c[2]}" for c in SWI_CASES])
+def test_quant_act_swiglu_bit_exact(dt, M, F):
+    h = make_x(M, 2 * F, dt, seed=F + M, ld=2 * F + (8 if dt != synth.DT_FP32 else 4), special=True)
+    for forced in (False, True):
+        say(f"cr_quant_act_swiglu dt={dt} M={M} F={F} forced_two_pass={forced}")
+        q, s = rbl.quant_act(h.to(dev()), F, swiglu=True, flags=rbl.CR_FLAG_FORCE_TWO_PASS if forced else 0)
+        torch.cuda.synchronize()
+        rq, rs = oracle.quant_act(host_bits(h, dt), dt, F, swiglu=True)
+        assert_bits_equal(q.cpu().numpy(), rq, "x_s8 (swiglu)")
+        assert_bits_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32), "x_scale (swiglu)")
+
+
+# ---------------------------------------------------------------- weight prep ----
+
+W_CASES = [(256, 512, None, None), (300, 1000, 512, 80), (97, 20000, None, None), (64, 5376, None, None),
+           (1, 17, 16, 5)]
+
+
+@pytest.mark.parametrize("N,K,ldc,ldsf", W_CASES, ids=[f"N{c[0]}-K{c[1]}" for c in W_CASES])
+def test_prep_weight_bit_exact(N, K, ldc, ldsf):
+    g = torch.Generator().manual_seed(N + K)
+    w = 0.02 * torch.randn(N, K, generator=g)
+    p = synth.nvfp4_encode(w, ld_codes=ldc, ld_sf=ldsf, garbage_seed=N)
+    gs = torch.tensor([p.g], dtype=torch.float32, device=dev())
+    rq, rs = oracle.prep_weight_nvfp4(p.codes.numpy(), p.sf.numpy(), p.g, K)
+    for forced in (False, True):
+        say(f"cr_prep_weight_nvfp4 N={N} K={K} ld={p.ld_codes}/{p.ld_sf} forced_two_pass={forced}")
+        q, s = rbl.prep_weight_nvfp4(p.codes.to(dev()), p.sf.to(dev()), gs, K,
+                                     flags=rbl.CR_FLAG_FORCE_TWO_PASS if forced else 0)
+        torch.cuda.synchronize()
+        assert_bits_equal(q.cpu().numpy(), rq, "w_s8")
+        assert_bits_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32), "w_scale")
+
+
+# ----------------------------------------------------------------------- GEMM ----
+
+G_CASES = [(64, 256, 512), (300, 700, 768), (1, 1, 256), (513, 255, 1280), (257, 300, 5376), (600, 520, 256)]
+
+
+@pytest.mark.parametrize("M,N,Kp", G_CASES, ids=[f"M{c[0]}-N{c[1]}-K{c[2]}" for c in G_CASES])
+def test_gemm_int32_exact_and_epilogues(M, N, Kp):
+    g = torch.Generator().manual_seed(M * N + Kp)
+    a = torch.randint(-127, 128, (M, Kp), generator=g, dtype=torch.int32).to(torch.int8)
+    b = torch.randint(-127, 128, (N, Kp), generator=g, dtype=torch.int32).to(torch.int8)
+    sa = torch.rand(M, generator=g) * 1e-2
+    sb = torch.rand(N, generator=g) * 1e-3
+    sa[0] = 0.0
+    acc = oracle.gemm_s8(a.numpy(), b.numpy())
+    ad, bd, sad, sbd = a.to(dev()), b.to(dev()), sa.to(dev()), sb.to(dev())
+    ldc = N + 9
+    for odt in (synth.DT_I32, synth.DT_BF16, synth.DT_FP16, synth.DT_FP32):
+        tdt = synth.TORCH_DTYPE[odt]
+        full = torch.full((M, ldc), 7, dtype=tdt, device=dev())
+        c = full[:, :N]
+        say(f"cr_gemm_s8_rowscale M={M} N={N} K_pad={Kp} out={odt} ldc={ldc}")
+        rbl.cr_gemm_s8_rowscale(ad, sad, bd, sbd, c)
+        torch.cuda.synchronize()
+        fc = full.cpu()
+        assert (fc[:, N:] == 7).all(), "columns past N were written"
+        ref = oracle.epilogue(acc, sa.numpy(), sb.numpy(), odt)
+        if odt == synth.DT_I32:
+            assert_bits_equal(fc[:, :N].numpy(), acc, "int32 accumulator")
+        else:
+            got = out_f64(fc[:, :N], odt)
+            err = rel_l2(got, out_f64(ref, odt))
+            assert err <= TOL[odt], err
+
+
+# ---------------------------------------------------------------------- layer ----
+
+def _layer_inputs(M, N, K, dt, swiglu, seed):
+    w = synth.Workload("t", M, N, K, dt, (synth.DT_BF16,), seed, swiglu=swiglu, outlier_frac=0.01)
+    x = synth.make_activation(w)
+    p = synth.make_weight_nvfp4(w)
+    return w, x, p
+
+
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_layer_chunking_and_streams_identical(swiglu):
+    M, N, K = 300, 1000, 1000
+    w, x, p = _layer_inputs(M, N, K, synth.DT_BF16, swiglu, 11)
+    xd, cd, sd = x.to(dev()), p.codes.to(dev()), p.sf.to(dev())
+    gs = torch.tensor([p.g], dtype=torch.float32, device=dev())
+    aux = torch.cuda.Stream()
+    outs = []
+    for mt, use_aux in [(0, False), (256 * 1024, False), (256 * 1024, True), (512 * 1024, True), (0, True)]:
+        say(f"cr_linear_nvfp4 M={M} N={N} K={K} swiglu={swiglu} max_tile={mt} aux={use_aux}")
+        outs.append(rbl.linear_nvfp4(xd, cd, sd, gs, K, swiglu=swiglu, max_tile_bytes=mt,
+                                     aux_stream=aux if use_aux else None))
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    ref = oracle.linear_nvfp4(synth.bits_u16(x), synth.DT_BF16, K, swiglu, p.codes.numpy(), p.sf.numpy(),
+                              p.g, synth.DT_BF16)
+    err = rel_l2(out_f64(outs[0], synth.DT_BF16), out_f64(ref, synth.DT_BF16))
+    assert err <= TOL[synth.DT_BF16], err
+
+
+def test_layer_tiny_full():
+    w = synth.WORKLOADS["tiny"]
+    x = synth.make_activation(w)
+    p = synth.make_weight_nvfp4(w)
+    gs = torch.tensor([p.g], dtype=torch.float32, device=dev())
+    say("cr_linear_nvfp4 tiny 64x256x512 bf16 (and the three steps separately)")
+    out = rbl.linear_nvfp4(x.to(dev()), p.codes.to(dev()), p.sf.to(dev()), gs, w.K)
+    qx, sx = rbl.quant_act(x.to(dev()), w.K)
+    qw, sw = rbl.prep_weight_nvfp4(p.codes.to(dev()), p.sf.to(dev()), gs, w.K)
+    acc = torch.empty(w.M, w.N, dtype=torch.int32, device=dev())
+    rbl.cr_gemm_s8_rowscale(qx, sx, qw, sw, acc)
+    torch.cuda.synchronize()
+    xb = synth.bits_u16(x)
+    rqx, rsx = oracle.quant_act(xb, w.x_dtype, w.K)
+    rqw, rsw = oracle.prep_weight_nvfp4(p.codes.numpy(), p.sf.numpy(), p.g, w.K)
+    racc = oracle.gemm_s8(rqx, rqw)
+    assert_bits_equal(qx.cpu().numpy(), rqx, "x_s8")
+    assert_bits_equal(qw.cpu().numpy(), rqw, "w_s8")
+    assert_bits_equal(acc.cpu().numpy(), racc, "acc")
+    ref = oracle.epilogue(racc, rsx, rsw, synth.DT_BF16)
+    err = rel_l2(out_f64(out, synth.DT_BF16), out_f64(ref, synth.DT_BF16))
+    assert err <= TOL[synth.DT_BF16], err
+    exact = np.mean(u16(out) == ref)
+    print(f"tiny: rel_l2={err:.3e} bit-identical fraction={exact:.4f}")
