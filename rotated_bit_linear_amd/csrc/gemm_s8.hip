@@ -4,11 +4,20 @@
 // DiT ..." bullet: row-scaled INT8 GEMM over the rotated S8 operands; MiniMax H3
 // explainer, fused-kernel paragraph: rescaling inside the matmul).
 //
-// Tiling: a 256x256 output tile per workgroup of 4 waves (2x2), each wave 128x128 as a
-// 4x4 grid of v_mfma_i32_32x32x32_i8.  K advances 64 bytes per step through two LDS
-// stages (register-staged prefetch of the next step while the current one computes).
-// LDS rows are 64 bytes (4 chunks of 16 B); chunk c of row r lives at c ^ swz(r) so that
-// fragment reads (32 rows, one chunk) and the prefetch writes are bank-conflict free.
+// Tiling: a BM x BN output tile per workgroup, WAVES_M x WAVES_N waves, each wave a
+// (WT_M/32) x (WT_N/32) grid of v_mfma_i32_32x32x32_i8.  K advances BK bytes per step
+// through an LDS ring of STAGES stages filled by direct global->LDS loads
+// (global_load_lds_dwordx4: every lane moves 16 bytes, a wave fills 1 KB of LDS), so no
+// VGPR staging is needed and STAGES-1 steps are in flight while one is consumed.
+// LDS rows hold BK bytes (BK/16 chunks of 16 B); chunk c of row r lives at c ^ swz(r),
+// which keeps the 32-row fragment reads bank-conflict free with 32 or 64 banks; the
+// global side of each DMA lane picks the chunk that lands in its LDS slot, so every
+// group of BK/16 lanes still reads one contiguous BK-byte row segment.
+// Software pipeline of one step k (BK/32 slices of 32 along K, ks = 0 .. KS-1):
+//   read fragments (k, ks+1) || MFMAs on (k, ks)          for ks < KS-1
+//   wait for the own DMA of step k+1, barrier (every wave is past its reads of stage k),
+//   DMA of step k+STAGES into stage k, read fragments (k+1, 0) || MFMAs on (k, KS-1)
+// so LDS latency, the barrier and the DMA issue all overlap queued MFMA work.
 // Workgroups are renumbered so that each XCD (workgroup id mod 8 on this part) works on a
 // contiguous band of tiles, ordered in groups of 8 M-tiles, for L2 reuse of both operands.
 #include <hip/hip_runtime.h>
@@ -16,35 +25,88 @@
 #include <hip/hip_fp16.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels.hpp"
+
+#ifndef CONVROT_GEMM_WAVES_M
+#define CONVROT_GEMM_WAVES_M 4
+#endif
+#ifndef CONVROT_GEMM_WAVES_N
+#define CONVROT_GEMM_WAVES_N 2
+#endif
+#ifndef CONVROT_GEMM_WT_M
+#define CONVROT_GEMM_WT_M 64
+#endif
+#ifndef CONVROT_GEMM_WT_N
+#define CONVROT_GEMM_WT_N 128
+#endif
+#ifndef CONVROT_GEMM_BK
+#define CONVROT_GEMM_BK 64
+#endif
+#ifndef CONVROT_GEMM_STAGES
+#define CONVROT_GEMM_STAGES 4
+#endif
 
 namespace convrot {
 
 typedef int32_t v4i __attribute__((ext_vector_type(4)));
 typedef int32_t v16i __attribute__((ext_vector_type(16)));
 
-constexpr int GBM = 256, GBN = 256, GBK = 64;
-constexpr int GTHREADS = 256;
+constexpr int WAVES_M = CONVROT_GEMM_WAVES_M, WAVES_N = CONVROT_GEMM_WAVES_N;
+constexpr int WT_M = CONVROT_GEMM_WT_M, WT_N = CONVROT_GEMM_WT_N;
+constexpr int FM = WT_M / 32, FN = WT_N / 32;      // MFMA tiles per wave
+constexpr int GBM = WAVES_M * WT_M, GBN = WAVES_N * WT_N, GBK = CONVROT_GEMM_BK;
+constexpr int GWAVES = WAVES_M * WAVES_N;
+constexpr int GTHREADS = 64 * GWAVES;
+constexpr int GSTAGES = CONVROT_GEMM_STAGES;
+constexpr int KS = GBK / 32;                       // 32-deep MFMA slices per step
+constexpr int CPR = GBK / 16;                      // 16-byte chunks per LDS row
+constexpr int RPP = 1024 / GBK;                    // rows per 1 KB DMA piece
 constexpr int GROUP_M = 8;
 constexpr int NUM_XCD = 8;
+constexpr int STAGE_A = GBM * GBK, STAGE_B = GBN * GBK;
+constexpr int PIECES = (STAGE_A + STAGE_B) / 1024;  // 1 KB DMA pieces per stage
+constexpr int PPW = PIECES / GWAVES;                 // pieces per wave per stage
+static_assert(GBK == 64 || GBK == 128, "BK is 64 or 128");
+static_assert(256 % (GBK * GSTAGES) == 0, "a K_pad multiple of 256 must be whole groups of stages");
+static_assert(PIECES % GWAVES == 0 && (STAGE_A / 1024) % PPW == 0, "DMA pieces must split evenly");
+static_assert(GSTAGES * (STAGE_A + STAGE_B) <= 160 * 1024, "LDS ring exceeds 160 KB");
+static_assert(PPW * (GSTAGES - 1) <= 63, "vmcnt range");
+static_assert(KS % 2 == 0, "fragment register sets alternate per slice");
 
-__device__ __forceinline__ int gswz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+constexpr int EPI_STRIDE = 272;                    // bytes per LDS row of the epilogue tile
+constexpr int EPI_BYTES = 32 * EPI_STRIDE;         // one 32-row x 256-byte tile per wave
 
-template <int OUT>
-__device__ __forceinline__ void store_out(void *C, int64_t idx, int32_t acc, float sa, float sb)
+// s_waitcnt immediates (gfx9 encoding) waiting for vmcnt <= n only / lgkmcnt == 0 only.
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+constexpr int waitcnt_lgkm0() { return 15 | (7 << 4) | (0 << 8) | (3 << 14); }
+
+// chunk swizzle of an LDS row: for 4 chunks, rows 0..7 (and 0..15 in pairs) get distinct
+// bank groups; for 8 chunks, rows 0..7 and the even/odd rows of 0..15 do.
+// scheduling groups "1 MFMA, then 2 LDS reads", repeated until NFR reads are placed
+template <int T, int NFR>
+__device__ __forceinline__ void read_groups()
 {
-    if constexpr (OUT == 3) {
-        static_cast<int32_t *>(C)[idx] = acc;
-    } else {
-        const float v = ((float)acc * sa) * sb;
-        if constexpr (OUT == 2) {
-            static_cast<float *>(C)[idx] = v;
-        } else if constexpr (OUT == 0) {
-            static_cast<__hip_bfloat16 *>(C)[idx] = __float2bfloat16(v);
-        } else {
-            static_cast<__half *>(C)[idx] = __float2half(v);
-        }
+    if constexpr (2 * T < NFR) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, (2 * T + 1 < NFR) ? 2 : 1, 0); // DS read
+        read_groups<T + 1, NFR>();
     }
+}
+
+// orders LDS traffic between the lanes of one wave
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int gswz(int row)
+{
+    if constexpr (CPR == 4) return ((row >> 1) ^ (row >> 2)) & 3;
+    else return (row ^ (row >> 3)) & 7;
 }
 
 template <int OUT>
@@ -54,7 +116,21 @@ void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__re
                     int M, int N, int K_pad, void *__restrict__ C, int64_t ldc,
                     int tiles_m, int tiles_n)
 {
-    __shared__ __attribute__((aligned(16))) int8_t smem[2][(GBM + GBN) * GBK];
+    __shared__ __attribute__((aligned(1024))) int8_t lA0[STAGE_A];
+    __shared__ __attribute__((aligned(1024))) int8_t lA1[STAGE_A];
+    __shared__ __attribute__((aligned(1024))) int8_t lB0[STAGE_B];
+    __shared__ __attribute__((aligned(1024))) int8_t lB1[STAGE_B];
+#if CONVROT_GEMM_STAGES == 4
+    __shared__ __attribute__((aligned(1024))) int8_t lA2[STAGE_A];
+    __shared__ __attribute__((aligned(1024))) int8_t lA3[STAGE_A];
+    __shared__ __attribute__((aligned(1024))) int8_t lB2[STAGE_B];
+    __shared__ __attribute__((aligned(1024))) int8_t lB3[STAGE_B];
+    int8_t *const stA[GSTAGES] = {lA0, lA1, lA2, lA3};
+    int8_t *const stB[GSTAGES] = {lB0, lB1, lB2, lB3};
+#else
+    int8_t *const stA[GSTAGES] = {lA0, lA1};
+    int8_t *const stB[GSTAGES] = {lB0, lB1};
+#endif
 
     // ---- tile id: XCD-contiguous renumbering, then grouped ordering along M ----
     const int total = tiles_m * tiles_n;
@@ -70,102 +146,291 @@ void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__re
     const int tn = (lid % in_group) / gsize;
     const int m0 = tm * GBM, n0 = tn * GBN;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-    // ---- global -> register prefetch assignment: 4 chunks of A and 4 of B per thread ----
-    const int lrow = tid >> 2, lc = tid & 3;
-    const int8_t *pa[4];
-    const int8_t *pb[4];
+    // ---- DMA assignment: wave w moves pieces w*PPW .. w*PPW+PPW-1 of the stage (A pieces
+    //      first, then B), each piece RPP rows x BK bytes; lane p covers row p/CPR of a
+    //      piece and the LDS slot p%CPR, which holds logical chunk (p%CPR) ^ swz(row) ----
+    const int piece0 = wave * PPW;
+    const bool dma_a = piece0 < STAGE_A / 1024;
+    const int prow = lane / CPR;
+    const int8_t *gsrc[PPW];
 #pragma unroll
-    for (int p = 0; p < 4; p++) {
-        const int ra = min(m0 + lrow + 64 * p, M - 1);        // rows past M read row M-1
-        const int rb = min(n0 + lrow + 64 * p, N - 1);        // (results masked at the store)
-        pa[p] = A + (int64_t)ra * lda + lc * 16;
-        pb[p] = B + (int64_t)rb * ldb + lc * 16;
+    for (int j = 0; j < PPW; j++) {
+        if (dma_a) {
+            const int r = (piece0 + j) * RPP + prow;                          // row inside the tile
+            const int chunk = (lane % CPR) ^ gswz(r);
+            gsrc[j] = A + (int64_t)min(m0 + r, M - 1) * lda + chunk * 16;     // rows past M: row M-1
+        } else {
+            const int r = (piece0 - STAGE_A / 1024 + j) * RPP + prow;
+            const int chunk = (lane % CPR) ^ gswz(r);
+            gsrc[j] = B + (int64_t)min(n0 + r, N - 1) * ldb + chunk * 16;     // (masked at the store)
+        }
     }
-    const int st_off = lrow * GBK + ((lc ^ gswz(lrow)) << 4);   // + p * 64 rows * 64 B
+    const int dma_off = (dma_a ? piece0 : piece0 - STAGE_A / 1024) * 1024;
 
-    v16i acc[4][4];
+    auto issue = [&](int s, int kt) {
+        int8_t *dst = (dma_a ? stA[s] : stB[s]) + dma_off;
+        const int64_t ko = (int64_t)kt * GBK;
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+        for (int j = 0; j < PPW; j++)
+            __builtin_amdgcn_global_load_lds(gsrc[j] + ko, dst + j * 1024, 16, 0, 0);
+    };
+
+    // ---- fragment offsets: row = base + (lane & 31), chunk = 2 ks + (lane >> 5) ----
+    const int frow = lane & 31, fhalf = lane >> 5;
+    int offA[KS][FM], offB[KS][FN];
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+    for (int ks = 0; ks < KS; ks++) {
+        const int c = 2 * ks + fhalf;
+#pragma unroll
+        for (int i = 0; i < FM; i++) {
+            const int r = wm * WT_M + i * 32 + frow;
+            offA[ks][i] = r * GBK + ((c ^ gswz(r)) << 4);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; j++) {
+            const int r = wn * WT_N + j * 32 + frow;
+            offB[ks][j] = r * GBK + ((c ^ gswz(r)) << 4);
+        }
+    }
+
+    v16i acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0;
 
-    uint4 ra_[4], rb_[4];
-    auto gload = [&](int kt) {
-        const int64_t ko = (int64_t)kt * GBK;
+    v4i fa[2][FM], fb[2][FN];
+    auto read_frags = [&](int s, int ks, int slot) {
+        const int8_t *sA = stA[s];
+        const int8_t *sB = stB[s];
 #pragma unroll
-        for (int p = 0; p < 4; p++) {
-            ra_[p] = *reinterpret_cast<const uint4 *>(pa[p] + ko);
-            rb_[p] = *reinterpret_cast<const uint4 *>(pb[p] + ko);
+        for (int i = 0; i < FM; i++) fa[slot][i] = *reinterpret_cast<const v4i *>(sA + offA[ks][i]);
+#pragma unroll
+        for (int j = 0; j < FN; j++) fb[slot][j] = *reinterpret_cast<const v4i *>(sB + offB[ks][j]);
+    };
+    // MFMA roles: the weight fragment is the first operand and the activation fragment the
+    // second, so D = (W X^T) per 32x32 block and lane l of a block holds output row
+    // m = l%32 and the 4-column runs n = 8g + 4(l/32) + q (g, q = 0..3) in registers 4g+q.
+    auto mfmas = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[slot][j], fa[slot][i], acc[i][j], 0, 0, 0);
+    };
+    // MFMAs number t0 .. t1-1 of a slice (t = i*FN + j)
+    auto mfmas_range = [&](int slot, int t0, int t1) {
+#pragma unroll
+        for (int t = 0; t < FM * FN; t++) {
+            if (t < t0 || t >= t1) continue;
+            const int i = t / FN, j = t % FN;
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[slot][j], fa[slot][i], acc[i][j], 0, 0, 0);
         }
     };
-    auto lstore = [&](int buf) {
+    // scheduling hints: each slice opens with an MFMA (its operands were read during the
+    // previous slice), then the next slice's fragment reads go out two at a time between
+    // MFMAs, front-loaded so they land well before that slice starts; after a barrier the
+    // DMA issues are spread over the remaining MFMAs
+    constexpr int NFR = FM + FN, NMF = FM * FN;
+    constexpr int RD_GROUPS = (NFR + 1) / 2;
+    static_assert(RD_GROUPS + 1 < NMF, "need more MFMAs than read pairs per slice");
+    auto interleave_reads = [&](bool with_dma, int pre) {
+        read_groups<0, NFR>();
+        if (with_dma) {
+            constexpr int rest = NMF - 1 - RD_GROUPS;   // only used after the barrier (pre = 1)
 #pragma unroll
-        for (int p = 0; p < 4; p++) {
-            *reinterpret_cast<uint4 *>(&smem[buf][st_off + p * 64 * GBK]) = ra_[p];
-            *reinterpret_cast<uint4 *>(&smem[buf][GBM * GBK + st_off + p * 64 * GBK]) = rb_[p];
+            for (int t = 0; t < (PPW < rest ? PPW : rest); t++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                   // VMEM (DMA)
+            }
+            if constexpr (rest > PPW) __builtin_amdgcn_sched_group_barrier(0x008, rest - PPW, 0);
+            else if constexpr (PPW > rest) __builtin_amdgcn_sched_group_barrier(0x010, PPW - rest, 0);
+        } else if (pre == 0) {
+            __builtin_amdgcn_sched_group_barrier(0x008, NMF - RD_GROUPS, 0);
+        } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, NMF - 1 - RD_GROUPS, 0);
         }
     };
+    // wait until this wave's DMA of a step has landed while `younger` later steps, issued
+    // after it, may stay in flight (vmcnt counts this wave's outstanding DMAs)
+    auto wait_dma = [&](int younger) {
+        if (younger >= 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * PPW));
+        else if (younger == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * PPW));
+        else if (younger == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(PPW));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    };
+    auto barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
 
-    // fragment read offsets: row = base + (lane & 31), chunk = 2s + (lane >> 5)
-    const int frow = lane & 31, fhalf = lane >> 5;
+    // Prologue: every stage is free; steps 0..STAGES-1 are issued, step 0 awaited.
+    // In step k the DMAs issued so far cover steps 0..min(k+STAGES-1, nk-1), so before the
+    // barrier of step k+1 at most min(k+STAGES-1, nk-1) - (k+1) younger steps are in flight.
+    const int nk = K_pad / GBK;   // a multiple of STAGES, >= STAGES (K_pad % 256 == 0)
+#pragma unroll
+    for (int s = 0; s < GSTAGES; s++) issue(s, s);
+    wait_dma(GSTAGES - 1);
+    barrier();
+    read_frags(0, 0, 0);
 
-    const int nk = K_pad / GBK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt++) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
-        const int8_t *sA = smem[cur];
-        const int8_t *sB = smem[cur] + GBM * GBK;
+    // One step on stage S; the loop runs whole groups of STAGES steps (stage index known at
+    // compile time) and only the last group is peeled, which keeps every step free of
+    // branches around its LDS reads.  Inside the loop STAGES-2 younger steps are in flight
+    // at each barrier and the DMA of step k+STAGES always exists; in the last group
+    // (k = nk-STAGES+S) STAGES-2-S remain and nothing new is issued.  The barrier opens the
+    // last slice: its fragments were read during the previous slice.
+    auto step = [&](auto S_, int kt, int younger, bool do_issue, bool last) {
+        constexpr int S = decltype(S_)::value;
 #pragma unroll
-        for (int s = 0; s < 2; s++) {
-            const int c = 2 * s + fhalf;
-            v4i a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int r = wm * 128 + i * 32 + frow;
-                a[i] = *reinterpret_cast<const v4i *>(sA + r * GBK + ((c ^ gswz(r)) << 4));
+        for (int ks = 0; ks < KS; ks++) {
+            if (ks < KS - 1) {
+                read_frags(S, ks + 1, (ks + 1) & 1);
+                mfmas(ks & 1);
+                interleave_reads(false, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            } else if (!last) {
+                // the first MFMA consumes this slice's fragments, so every LDS read of
+                // stage S has completed before the barrier; it also keeps the matrix pipe
+                // busy while the barrier resolves
+                mfmas_range(ks & 1, 0, 1);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                wait_dma(younger);
+                barrier();
+                read_frags((S + 1) % GSTAGES, 0, 0);
+                mfmas_range(ks & 1, 1, NMF);
+                if (do_issue) issue(S, kt + S + GSTAGES);
+                interleave_reads(do_issue, 1);
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                mfmas(ks & 1);
             }
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const int r = wn * 128 + j * 32 + frow;
-                b[j] = *reinterpret_cast<const v4i *>(sB + r * GBK + ((c ^ gswz(r)) << 4));
-            }
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-                for (int j = 0; j < 4; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
         }
-        if (kt + 1 < nk) lstore(cur ^ 1);
-        __syncthreads();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    int kt = 0;
+    for (; kt < nk - GSTAGES; kt += GSTAGES) {
+        step(I0{}, kt, GSTAGES - 2, true, false);
+        step(I1{}, kt, GSTAGES - 2, true, false);
+        if constexpr (GSTAGES == 4) {
+            step(I2{}, kt, GSTAGES - 2, true, false);
+            step(I3{}, kt, GSTAGES - 2, true, false);
+        }
+    }
+    if constexpr (GSTAGES == 4) {
+        step(I0{}, kt, 2, false, false);
+        step(I1{}, kt, 1, false, false);
+        step(I2{}, kt, 0, false, false);
+        step(I3{}, kt, 0, false, true);
+    } else {
+        step(I0{}, kt, 0, false, false);
+        step(I1{}, kt, 0, false, true);
     }
 
-    // ---- epilogue: accumulator element r of lane l is row 8(r/4) + 4(l/32) + r%4, col l%32 ----
-    float sbv[4];
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int n = n0 + wn * 128 + j * 32 + frow;
-        sbv[j] = (OUT != 3 && n < N) ? sb[n] : 0.0f;
+    // ---- epilogue through LDS: every wave owns EPI_BYTES of the (now idle) stage ring.
+    //      Per 32-row block i and per 256-byte column chunk, lanes write their dequantized
+    //      4-column runs to rows of a padded LDS tile, then read it back in 16-byte pieces,
+    //      so each global store instruction covers 4 rows x 256 contiguous bytes. ----
+    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+    barrier();                                     // every wave is done with the ring
+    constexpr int ES = (OUT == 0 || OUT == 1) ? 2 : 4;
+    constexpr int NC = 256 / ES;                   // columns per chunk
+    constexpr int CHUNKS = WT_N / NC;
+    static_assert(WT_N % NC == 0, "wave tile width must be whole 256-byte chunks");
+    constexpr int WPA = (GWAVES + 2 * GSTAGES - 1) / (2 * GSTAGES);   // waves per region
+    static_assert(WPA * EPI_BYTES <= STAGE_A && WPA * EPI_BYTES <= STAGE_B, "epilogue tile fits the ring");
+    int8_t *etile;
+    switch (wave / WPA) {          // wave-uniform: a scalar branch
+    case 0: etile = lA0; break;
+    case 1: etile = lA1; break;
+#if CONVROT_GEMM_STAGES == 4
+    case 2: etile = lA2; break;
+    case 3: etile = lA3; break;
+    case 4: etile = lB0; break;
+    case 5: etile = lB1; break;
+    case 6: etile = lB2; break;
+    default: etile = lB3; break;
+#else
+    case 2: etile = lB0; break;
+    default: etile = lB1; break;
+#endif
     }
+    etile += (wave % WPA) * EPI_BYTES;
+    const bool vec_ok = (((uintptr_t)C) % 16 == 0) && ((ldc * ES) % 16 == 0);
+    const int nbase = n0 + wn * WT_N;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < FM; i++) {
+        const int m = m0 + wm * WT_M + i * 32 + frow;
+        const float sav = (OUT != 3 && m < M) ? sa[m] : 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fhalf + (r & 3);
-            if (m >= M) continue;
-            const float sav = (OUT != 3) ? sa[m] : 0.0f;
+        for (int c = 0; c < CHUNKS; c++) {
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const int n = n0 + wn * 128 + j * 32 + frow;
-                if (n < N) store_out<OUT>(C, (int64_t)m * ldc + n, acc[i][j][r], sav, sbv[j]);
+            for (int jj = 0; jj < NC / 32; jj++) {
+                const int j = c * (NC / 32) + jj;
+#pragma unroll
+                for (int g = 0; g < 4; g++) {
+                    const int nl = jj * 32 + 8 * g + 4 * fhalf;   // column inside the chunk
+                    int8_t *dst = etile + frow * EPI_STRIDE + nl * ES;
+                    const int32_t a0 = acc[i][j][4 * g], a1 = acc[i][j][4 * g + 1];
+                    const int32_t a2 = acc[i][j][4 * g + 2], a3 = acc[i][j][4 * g + 3];
+                    if constexpr (OUT == 3) {
+                        *reinterpret_cast<v4i *>(dst) = v4i{a0, a1, a2, a3};
+                    } else {
+                        const int n = nbase + c * NC + nl;
+                        float s4[4];
+#pragma unroll
+                        for (int q = 0; q < 4; q++) s4[q] = (n + q < N) ? sb[n + q] : 0.0f;
+                        const float v0 = ((float)a0 * sav) * s4[0], v1 = ((float)a1 * sav) * s4[1];
+                        const float v2 = ((float)a2 * sav) * s4[2], v3 = ((float)a3 * sav) * s4[3];
+                        if constexpr (OUT == 2) {
+                            *reinterpret_cast<float4 *>(dst) = make_float4(v0, v1, v2, v3);
+                        } else if constexpr (OUT == 0) {
+                            const __hip_bfloat16 h[4] = {__float2bfloat16(v0), __float2bfloat16(v1),
+                                                         __float2bfloat16(v2), __float2bfloat16(v3)};
+                            *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(h);
+                        } else {
+                            const __half h[4] = {__float2half(v0), __float2half(v1), __float2half(v2),
+                                                 __float2half(v3)};
+                            *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(h);
+                        }
+                    }
+                }
             }
+            wave_sync();
+            // 32 rows x 256 bytes = 512 pieces of 16 B, 8 per lane, 4 rows per instruction
+#pragma unroll
+            for (int t = 0; t < 8; t++) {
+                const int q = lane + 64 * t;
+                const int row = q >> 4, cc = q & 15;
+                const uint4 v = *reinterpret_cast<const uint4 *>(etile + row * EPI_STRIDE + cc * 16);
+                const int mg = m0 + wm * WT_M + i * 32 + row;
+                const int ng = nbase + c * NC + cc * (16 / ES);
+                if (mg < M) {
+                    int8_t *out = static_cast<int8_t *>(C) + ((int64_t)mg * ldc + ng) * ES;
+                    if (vec_ok && ng + 16 / ES <= N) {
+                        *reinterpret_cast<uint4 *>(out) = v;
+                    } else {
+                        const int8_t *vb = reinterpret_cast<const int8_t *>(&v);
+#pragma unroll
+                        for (int e = 0; e < 16 / ES; e++)
+                            if (ng + e < N) {
+                                if constexpr (ES == 2) reinterpret_cast<uint16_t *>(out)[e] = reinterpret_cast<const uint16_t *>(vb)[e];
+                                else reinterpret_cast<uint32_t *>(out)[e] = reinterpret_cast<const uint32_t *>(vb)[e];
+                            }
+                    }
+                }
+            }
+            wave_sync();
         }
     }
 }

@@ -170,23 +170,24 @@ def test_gemm_int32_exact_and_epilogues(M, N, Kp):
     sa[0] = 0.0
     acc = oracle.gemm_s8(a.numpy(), b.numpy())
     ad, bd, sad, sbd = a.to(dev()), b.to(dev()), sa.to(dev()), sb.to(dev())
-    ldc = N + 9
-    for odt in (synth.DT_I32, synth.DT_BF16, synth.DT_FP16, synth.DT_FP32):
-        tdt = synth.TORCH_DTYPE[odt]
-        full = torch.full((M, ldc), 7, dtype=tdt, device=dev())
-        c = full[:, :N]
-        say(f"cr_gemm_s8_rowscale M={M} N={N} K_pad={Kp} out={odt} ldc={ldc}")
-        rbl.cr_gemm_s8_rowscale(ad, sad, bd, sbd, c)
-        torch.cuda.synchronize()
-        fc = full.cpu()
-        assert (fc[:, N:] == 7).all(), "columns past N were written"
-        ref = oracle.epilogue(acc, sa.numpy(), sb.numpy(), odt)
-        if odt == synth.DT_I32:
-            assert_bits_equal(fc[:, :N].numpy(), acc, "int32 accumulator")
-        else:
-            got = out_f64(fc[:, :N], odt)
-            err = rel_l2(got, out_f64(ref, odt))
-            assert err <= TOL[odt], err
+    # an odd row stride (element stores) and a 16-byte multiple (vector stores, N tail)
+    for ldc in (N + 9, (N + 7) // 8 * 8 + 8):
+        for odt in (synth.DT_I32, synth.DT_BF16, synth.DT_FP16, synth.DT_FP32):
+            tdt = synth.TORCH_DTYPE[odt]
+            full = torch.full((M, ldc), 7, dtype=tdt, device=dev())
+            c = full[:, :N]
+            say(f"cr_gemm_s8_rowscale M={M} N={N} K_pad={Kp} out={odt} ldc={ldc}")
+            rbl.cr_gemm_s8_rowscale(ad, sad, bd, sbd, c)
+            torch.cuda.synchronize()
+            fc = full.cpu()
+            assert (fc[:, N:] == 7).all(), "columns past N were written"
+            ref = oracle.epilogue(acc, sa.numpy(), sb.numpy(), odt)
+            if odt == synth.DT_I32:
+                assert_bits_equal(fc[:, :N].numpy(), acc, "int32 accumulator")
+            else:
+                got = out_f64(fc[:, :N], odt)
+                err = rel_l2(got, out_f64(ref, odt))
+                assert err <= TOL[odt], err
 
 
 # ---------------------------------------------------------------------- layer ----
