@@ -42,16 +42,17 @@
 #define CONVROT_GEMM_WT_N 128
 #endif
 #ifndef CONVROT_GEMM_BK
-#define CONVROT_GEMM_BK 64
+#define CONVROT_GEMM_BK 128
 #endif
 #ifndef CONVROT_GEMM_STAGES
-#define CONVROT_GEMM_STAGES 4
+#define CONVROT_GEMM_STAGES 2
 #endif
 
 namespace convrot {
 
 typedef int32_t v4i __attribute__((ext_vector_type(4)));
 typedef int32_t v16i __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int WAVES_M = CONVROT_GEMM_WAVES_M, WAVES_N = CONVROT_GEMM_WAVES_N;
 constexpr int WT_M = CONVROT_GEMM_WT_M, WT_N = CONVROT_GEMM_WT_N;
@@ -341,6 +342,34 @@ void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__re
     //      Per 32-row block i and per 256-byte column chunk, lanes write their dequantized
     //      4-column runs to rows of a padded LDS tile, then read it back in 16-byte pieces,
     //      so each global store instruction covers 4 rows x 256 contiguous bytes. ----
+    // all row and column scales this lane needs are requested at once, before the barrier,
+    // so their latency overlaps the last MFMAs: sav[i] for its row of block i, sbv[j][g]
+    // for the 4-column run n = 8g + 4(l/32) .. +3 of block j (16-byte loads when aligned)
+    const int nbase = n0 + wn * WT_N;
+    float sav[FM];
+    float4 sbv[FN][4];
+    if constexpr (OUT != 3) {
+#pragma unroll
+        for (int i = 0; i < FM; i++) {
+            const int m = m0 + wm * WT_M + i * 32 + frow;
+            sav[i] = (m < M) ? sa[m] : 0.0f;
+        }
+        const bool sb16 = ((uintptr_t)sb % 16) == 0;
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const int n = nbase + j * 32 + 8 * g + 4 * fhalf;
+                if (sb16 && n + 4 <= N) {
+                    sbv[j][g] = *reinterpret_cast<const float4 *>(sb + n);
+                } else {
+                    sbv[j][g].x = (n < N) ? sb[n] : 0.0f;
+                    sbv[j][g].y = (n + 1 < N) ? sb[n + 1] : 0.0f;
+                    sbv[j][g].z = (n + 2 < N) ? sb[n + 2] : 0.0f;
+                    sbv[j][g].w = (n + 3 < N) ? sb[n + 3] : 0.0f;
+                }
+            }
+    }
     __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
     barrier();                                     // every wave is done with the ring
     constexpr int ES = (OUT == 0 || OUT == 1) ? 2 : 4;
@@ -367,11 +396,9 @@ void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__re
     }
     etile += (wave % WPA) * EPI_BYTES;
     const bool vec_ok = (((uintptr_t)C) % 16 == 0) && ((ldc * ES) % 16 == 0);
-    const int nbase = n0 + wn * WT_N;
+    const bool interior = vec_ok && m0 + GBM <= M && n0 + GBN <= N;   // uniform fast path
 #pragma unroll
     for (int i = 0; i < FM; i++) {
-        const int m = m0 + wm * WT_M + i * 32 + frow;
-        const float sav = (OUT != 3 && m < M) ? sa[m] : 0.0f;
 #pragma unroll
         for (int c = 0; c < CHUNKS; c++) {
 #pragma unroll
@@ -386,12 +413,9 @@ void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__re
                     if constexpr (OUT == 3) {
                         *reinterpret_cast<v4i *>(dst) = v4i{a0, a1, a2, a3};
                     } else {
-                        const int n = nbase + c * NC + nl;
-                        float s4[4];
-#pragma unroll
-                        for (int q = 0; q < 4; q++) s4[q] = (n + q < N) ? sb[n + q] : 0.0f;
-                        const float v0 = ((float)a0 * sav) * s4[0], v1 = ((float)a1 * sav) * s4[1];
-                        const float v2 = ((float)a2 * sav) * s4[2], v3 = ((float)a3 * sav) * s4[3];
+                        const float4 s4 = sbv[j][g];
+                        const float v0 = ((float)a0 * sav[i]) * s4.x, v1 = ((float)a1 * sav[i]) * s4.y;
+                        const float v2 = ((float)a2 * sav[i]) * s4.z, v3 = ((float)a3 * sav[i]) * s4.w;
                         if constexpr (OUT == 2) {
                             *reinterpret_cast<float4 *>(dst) = make_float4(v0, v1, v2, v3);
                         } else if constexpr (OUT == 0) {
@@ -415,10 +439,14 @@ void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__re
                 const uint4 v = *reinterpret_cast<const uint4 *>(etile + row * EPI_STRIDE + cc * 16);
                 const int mg = m0 + wm * WT_M + i * 32 + row;
                 const int ng = nbase + c * NC + cc * (16 / ES);
-                if (mg < M) {
-                    int8_t *out = static_cast<int8_t *>(C) + ((int64_t)mg * ldc + ng) * ES;
+                int8_t *out = static_cast<int8_t *>(C) + ((int64_t)mg * ldc + ng) * ES;
+                if (interior) {
+                    // streaming store: the output is written once and must not evict the
+                    // operand tiles other workgroups are still reading from L2
+                    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(out));
+                } else if (mg < M) {
                     if (vec_ok && ng + 16 / ES <= N) {
-                        *reinterpret_cast<uint4 *>(out) = v;
+                        __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(out));
                     } else {
                         const int8_t *vb = reinterpret_cast<const int8_t *>(&v);
 #pragma unroll
