@@ -44,47 +44,52 @@ struct NVFP4Loader {
     int64_t ld_sf;
     const float *g;
     int64_t K;
-    __device__ __forceinline__ void load16(int64_t row, int64_t seg, float (&v)[16]) const
+    // raw bytes of one 16-element segment: 8 code bytes and its block-scale byte
+    struct Raw {
+        uint32_t w0, w1, sc;
+    };
+    __device__ __forceinline__ void fetch(int64_t row, int64_t seg, Raw &r) const
     {
         const int64_t k0 = seg * 16;
-        if (k0 >= K) {                 // pure padding: no byte of the row is read
-#pragma unroll
-            for (int i = 0; i < 16; i++) v[i] = 0.0f;
-            return;
-        }
-        const float gs = *g;
-        const float sc = e4m3_to_f32(sf[row * ld_sf + seg]);
+        r.w0 = r.w1 = r.sc = 0u;
+        if (k0 >= K) return;           // pure padding: no byte of the row is read
+        r.sc = sf[row * ld_sf + seg];
         const uint8_t *p = codes + row * ld_codes + seg * 8;
         if (k0 + 16 <= K) {
             const uint2 q = *reinterpret_cast<const uint2 *>(p);
-            const uint32_t w[2] = {q.x, q.y};
-#pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const uint32_t code = (w[i >> 3] >> (4 * (i & 7))) & 15u;
-                const float prod = e2m1_to_f32(code) * sc;
-                v[i] = prod * gs;
-            }
+            r.w0 = q.x;
+            r.w1 = q.y;
             return;
         }
+        const int64_t nbytes = (K - k0 + 1) / 2;   // bytes holding elements k0 .. K-1
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            if (i < nbytes) {
+                const uint32_t byte = p[i];
+                if (i < 4) r.w0 |= byte << (8 * i);
+                else r.w1 |= byte << (8 * (i - 4));
+            }
+    }
+    __device__ __forceinline__ void decode(const Raw &r, int64_t seg, float (&v)[16]) const
+    {
+        const int64_t k0 = seg * 16;
+        const float gs = *g;
+        const float sc = e4m3_to_f32(r.sc);
 #pragma unroll
         for (int i = 0; i < 16; i++) {
-            float val = 0.0f;
-            if (k0 + i < K) {
-                const uint32_t byte = p[i >> 1];
-                const uint32_t code = (i & 1) ? (byte >> 4) : (byte & 15u);
-                const float prod = e2m1_to_f32(code) * sc;
-                val = prod * gs;
-            }
-            v[i] = val;
+            const uint32_t code = (((i < 8) ? r.w0 : r.w1) >> (4 * (i & 7))) & 15u;
+            const float prod = e2m1_to_f32(code) * sc;   // exact
+            const float val = prod * gs;
+            v[i] = (k0 + i < K) ? val : 0.0f;             // nibbles past K are padding
         }
     }
 };
 
 template <int RB>
-__global__ void prep_weight_kernel(NVFP4Loader ld, int nb, int8_t *__restrict__ out, int64_t ld_out,
-                                   float *__restrict__ scale, int two_pass)
+__global__ __launch_bounds__(512) void prep_weight_kernel(NVFP4Loader ld, int64_t n_rows, int nb, int8_t *__restrict__ out,
+                                   int64_t ld_out, float *__restrict__ scale, int two_pass)
 {
-    row_prep<NVFP4Loader, RB>(ld, (int64_t)blockIdx.x, nb, out, ld_out, scale, two_pass != 0);
+    row_prep_kernel_body<NVFP4Loader, RB>(ld, n_rows, nb, out, ld_out, scale, two_pass);
 }
 
 hipError_t launch_prep_weight(const uint8_t *codes, int64_t ld_codes, const uint8_t *sf, int64_t ld_sf,
@@ -94,13 +99,14 @@ hipError_t launch_prep_weight(const uint8_t *codes, int64_t ld_codes, const uint
     const int64_t nb = (K + 255) / 256;
     const RowPrepShape s = row_prep_shape(nb, two_pass);
     const size_t lds = row_prep_lds_bytes(s.threads);
+    const dim3 grid((unsigned)row_prep_grid(n_rows, s));
     NVFP4Loader L{codes, ld_codes, sf, ld_sf, g, K};
     if (s.rb == 2)
-        hipLaunchKernelGGL(prep_weight_kernel<2>, dim3((unsigned)n_rows), dim3(s.threads), lds, st,
-                           L, (int)nb, w_s8, ld_s8, w_scale, 0);
+        hipLaunchKernelGGL(prep_weight_kernel<2>, grid, dim3(s.threads), lds, st,
+                           L, n_rows, (int)nb, w_s8, ld_s8, w_scale, 0);
     else
-        hipLaunchKernelGGL(prep_weight_kernel<1>, dim3((unsigned)n_rows), dim3(s.threads), lds, st,
-                           L, (int)nb, w_s8, ld_s8, w_scale, s.two_pass ? 1 : 0);
+        hipLaunchKernelGGL(prep_weight_kernel<1>, grid, dim3(s.threads), lds, st,
+                           L, n_rows, (int)nb, w_s8, ld_s8, w_scale, s.two_pass ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -32,52 +32,55 @@ template <> struct Elem<2> {   // fp32
     static __device__ __forceinline__ float cvt(float f) { return f; }
 };
 
-// 16 consecutive elements starting at p (16-byte aligned) as fp32.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// The activation is read exactly once: non-temporal loads keep it from displacing the
-// GEMM operands in L2.
+// Raw bytes of 16 consecutive elements: 32 bytes for 16-bit types, 64 for fp32.
+template <int DT> struct RawSeg {
+    u32x4 w[DT == 2 ? 4 : 2];
+};
+
+// Fetch elements [k0, k0+16) of a row with logical length K: vector loads when the whole
+// segment lies below K and the row permits 16-byte loads (non-temporal: the activation is
+// read once), element loads for a segment straddling K, nothing at all past K.
 template <int DT>
-__device__ __forceinline__ void load16_vec(const typename Elem<DT>::T *p, float (&v)[16])
+__device__ __forceinline__ void fetch_seg(const typename Elem<DT>::T *row, int64_t k0, int64_t K, bool aligned,
+                                          RawSeg<DT> &r)
 {
+    constexpr int NW = DT == 2 ? 4 : 2;
+    if (aligned && k0 + 16 <= K) {
+#pragma unroll
+        for (int c = 0; c < NW; c++) r.w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row + k0) + c);
+        return;
+    }
+#pragma unroll
+    for (int c = 0; c < NW; c++) r.w[c] = u32x4{0u, 0u, 0u, 0u};
+    if (k0 >= K) return;
     if constexpr (DT == 2) {
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(row + k0);
 #pragma unroll
-        for (int c = 0; c < 4; c++) {
-            f32x4 q = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p) + c);
-            v[4 * c] = q.x; v[4 * c + 1] = q.y; v[4 * c + 2] = q.z; v[4 * c + 3] = q.w;
-        }
+        for (int i = 0; i < 16; i++)
+            if (k0 + i < K) r.w[i >> 2][i & 3] = p[i];
     } else {
+        const uint16_t *p = reinterpret_cast<const uint16_t *>(row + k0);
 #pragma unroll
-        for (int c = 0; c < 2; c++) {
-            u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p) + c);
-            uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                v[8 * c + 2 * i] = Elem<DT>::cvt((uint16_t)(w[i] & 0xffffu));
-                v[8 * c + 2 * i + 1] = Elem<DT>::cvt((uint16_t)(w[i] >> 16));
-            }
-        }
+        for (int i = 0; i < 16; i++)
+            if (k0 + i < K) r.w[i >> 3][(i >> 1) & 3] |= (uint32_t)p[i] << (16 * (i & 1));
     }
 }
 
-// Elements [k0, k0+16) of a row with logical length K (zero past K); `aligned` says the
-// row base permits 16-byte vector loads.
 template <int DT>
-__device__ __forceinline__ void load16_row(const typename Elem<DT>::T *row, int64_t k0, int64_t K,
-                                           bool aligned, float (&v)[16])
+__device__ __forceinline__ void decode_seg(const RawSeg<DT> &r, float (&v)[16])
 {
-    if (aligned && k0 + 16 <= K) {
-        load16_vec<DT>(row + k0, v);
-        return;
-    }
-    if (k0 >= K) {                     // pure padding: nothing is read
+    if constexpr (DT == 2) {
 #pragma unroll
-        for (int i = 0; i < 16; i++) v[i] = 0.0f;
-        return;
-    }
+        for (int i = 0; i < 16; i++) v[i] = __uint_as_float(r.w[i >> 2][i & 3]);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 16; i++) v[i] = (k0 + i < K) ? Elem<DT>::cvt(row[k0 + i]) : 0.0f;
+        for (int i = 0; i < 16; i++) {
+            const uint32_t w = r.w[i >> 3][(i >> 1) & 3];
+            v[i] = Elem<DT>::cvt((uint16_t)((i & 1) ? (w >> 16) : (w & 0xffffu)));
+        }
+    }
 }
 
 // ------------------------------------------------------ reproducible exponential ----
@@ -91,11 +94,11 @@ __device__ __forceinline__ float repro_exp(float x)
     const float kLog2e = 0x1.715476p+0f;
     const float kC1 = 0x1.62e4p-1f;
     const float kC2 = 0x1.7f7d1cp-20f;
-    if (x != x) return x;
-    if (x > 89.0f) return __builtin_inff();
-    if (x < -104.0f) return 0.0f;
-    const float kf = rintf(x * kLog2e);
-    float r = fmaf(-kf, kC1, x);
+    // evaluate on x clamped to [-104, 89] (unchanged inside that range), then select the
+    // out-of-range results: no divergent branches per element
+    const float xc = fminf(fmaxf(x, -104.0f), 89.0f);
+    const float kf = rintf(xc * kLog2e);
+    float r = fmaf(-kf, kC1, xc);
     r = fmaf(-kf, kC2, r);
     float p = 0x1.a01a02p-13f;             // 1/7!
     p = fmaf(p, r, 0x1.6c16c2p-10f);       // 1/6!
@@ -105,7 +108,10 @@ __device__ __forceinline__ float repro_exp(float x)
     p = fmaf(p, r, 0x1.0p-1f);             // 1/2!
     p = fmaf(p, r, 1.0f);
     p = fmaf(p, r, 1.0f);
-    return __builtin_amdgcn_ldexpf(p, (int)kf);
+    float e = __builtin_amdgcn_ldexpf(p, (int)kf);
+    e = (x > 89.0f) ? __builtin_inff() : e;
+    e = (x < -104.0f) ? 0.0f : e;
+    return (x != x) ? x : e;
 }
 
 // swish(gate) * value with swish(a) = a / (1 + E(-a)) evaluated as a * (1 / (1 + E(-a))).
@@ -125,10 +131,12 @@ struct ActLoader {
     int64_t ld;
     int64_t K;
     bool aligned;
-    __device__ __forceinline__ void load16(int64_t row, int64_t seg, float (&v)[16]) const
+    using Raw = RawSeg<DT>;
+    __device__ __forceinline__ void fetch(int64_t row, int64_t seg, Raw &r) const
     {
-        load16_row<DT>(x + row * ld, seg * 16, K, aligned, v);
+        fetch_seg<DT>(x + row * ld, seg * 16, K, aligned, r);
     }
+    __device__ __forceinline__ void decode(const Raw &r, int64_t, float (&v)[16]) const { decode_seg<DT>(r, v); }
 };
 
 template <int DT>
@@ -138,12 +146,20 @@ struct SwigluLoader {
     int64_t F;
     bool aligned_gate;
     bool aligned_value;
-    __device__ __forceinline__ void load16(int64_t row, int64_t seg, float (&v)[16]) const
+    struct Raw {
+        RawSeg<DT> gate, value;
+    };
+    __device__ __forceinline__ void fetch(int64_t row, int64_t seg, Raw &r) const
     {
-        const typename Elem<DT>::T *r = h + row * ld;
+        const typename Elem<DT>::T *p = h + row * ld;
+        fetch_seg<DT>(p, seg * 16, F, aligned_gate, r.gate);
+        fetch_seg<DT>(p + F, seg * 16, F, aligned_value, r.value);
+    }
+    __device__ __forceinline__ void decode(const Raw &r, int64_t, float (&v)[16]) const
+    {
         float b[16];
-        load16_row<DT>(r, seg * 16, F, aligned_gate, v);
-        load16_row<DT>(r + F, seg * 16, F, aligned_value, b);
+        decode_seg<DT>(r.gate, v);
+        decode_seg<DT>(r.value, b);
 #pragma unroll
         for (int i = 0; i < 16; i++) v[i] = swiglu_elem(v[i], b[i]);   // zero past F: 0 * sig * 0
     }
@@ -166,10 +182,10 @@ __global__ void swiglu_kernel(const typename Elem<DT>::T *__restrict__ h, int64_
 }
 
 template <class Loader, int RB>
-__global__ void quant_act_kernel(Loader ld, int nb, int8_t *__restrict__ out, int64_t ld_out,
+__global__ __launch_bounds__(512) void quant_act_kernel(Loader ld, int64_t n_rows, int nb, int8_t *__restrict__ out, int64_t ld_out,
                                  float *__restrict__ scale, int two_pass)
 {
-    row_prep<Loader, RB>(ld, (int64_t)blockIdx.x, nb, out, ld_out, scale, two_pass != 0);
+    row_prep_kernel_body<Loader, RB>(ld, n_rows, nb, out, ld_out, scale, two_pass);
 }
 
 // --------------------------------------------------------------------- launchers ----
@@ -180,12 +196,13 @@ static hipError_t launch_rows(const Loader &L, int64_t rows, int64_t nb, int8_t 
 {
     const RowPrepShape s = row_prep_shape(nb, force_two_pass);
     const size_t lds = row_prep_lds_bytes(s.threads);
+    const dim3 grid((unsigned)row_prep_grid(rows, s));
     if (s.rb == 2)
-        hipLaunchKernelGGL((quant_act_kernel<Loader, 2>), dim3((unsigned)rows), dim3(s.threads), lds, st,
-                           L, (int)nb, out, ld_out, scale, 0);
+        hipLaunchKernelGGL((quant_act_kernel<Loader, 2>), grid, dim3(s.threads), lds, st,
+                           L, rows, (int)nb, out, ld_out, scale, 0);
     else
-        hipLaunchKernelGGL((quant_act_kernel<Loader, 1>), dim3((unsigned)rows), dim3(s.threads), lds, st,
-                           L, (int)nb, out, ld_out, scale, s.two_pass ? 1 : 0);
+        hipLaunchKernelGGL((quant_act_kernel<Loader, 1>), grid, dim3(s.threads), lds, st,
+                           L, rows, (int)nb, out, ld_out, scale, s.two_pass ? 1 : 0);
     return hipGetLastError();
 }
 

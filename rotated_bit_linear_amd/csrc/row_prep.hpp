@@ -135,22 +135,89 @@ __device__ __forceinline__ void quantize_store16(const float (&v)[16], float r, 
     *reinterpret_cast<uint4 *>(dst) = o;
 }
 
-// Dynamic LDS of one workgroup: per-group transpose tiles followed by the reduction slots.
+// Dynamic LDS of one workgroup: per-group transpose tiles followed by two sets of
+// reduction slots (alternating between consecutive rows of the row loop).
 __host__ __device__ constexpr size_t row_prep_lds_bytes(int threads)
 {
-    return (size_t)(threads / kLanesPerBlock) * kTileStrideF * sizeof(float) + 16 * sizeof(float);
+    return (size_t)(threads / kLanesPerBlock) * kTileStrideF * sizeof(float) + 32 * sizeof(float);
 }
 
-// Loader concept: `__device__ void load16(int64_t row, int64_t seg, float (&v)[16]) const`
-// fills v with the fp32 elements 16*seg .. 16*seg+15 of the row (zero for k >= K).
-//
-// One pass (two_pass == false): the G = blockDim/16 groups hold RB blocks each, block
-// grp + r*G in v[r]; requires nb <= RB*G.  Two passes: RB is 1 and the row is streamed in
-// slices of G blocks, once for the maximum and once for the codes.
+// Loader concept:
+//   struct Raw;                                      raw bytes of one 16-element segment
+//   void fetch(int64_t row, int64_t seg, Raw &) const;    issue the loads (nothing past K)
+//   void decode(const Raw &, int64_t seg, float (&)[16]) const;   fp32 elements 16*seg..,
+//                                                                 zero for k >= K
+// Splitting the two lets a workgroup request the next row while it works on this one.
+
+// One pass, several rows per workgroup: the G = blockDim/16 groups hold RB blocks each
+// (block grp + r*G in v[r]; requires nb <= RB*G).  Rows blockIdx.x, +gridDim.x, ... are
+// processed in turn; the raw bytes of the next row are fetched before the current row is
+// decoded, so their latency overlaps the rotation, the reduction and the stores.
 template <class Loader, int RB>
-__device__ __forceinline__ void row_prep(const Loader &ld, int64_t row, int nb,
-                                         int8_t *__restrict__ out, int64_t ld_out,
-                                         float *__restrict__ scale_out, bool two_pass)
+__device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, int nb,
+                                              int8_t *__restrict__ out, int64_t ld_out,
+                                              float *__restrict__ scale_out)
+{
+    extern __shared__ float lds[];
+    const int tid = threadIdx.x;
+    const int grp = tid >> 4;
+    const int t = tid & 15;
+    const int G = blockDim.x >> 4;
+    float *tile = lds + grp * kTileStrideF;
+    float *red = lds + G * kTileStrideF;
+
+    typename Loader::Raw nxt[RB];
+    auto fetch_row = [&](int64_t r) {
+#pragma unroll
+        for (int q = 0; q < RB; q++) {
+            const int b = grp + q * G;
+            if (b < nb) ld.fetch(r, (int64_t)b * 16 + t, nxt[q]);
+        }
+    };
+    int64_t row = blockIdx.x;
+    fetch_row(row);
+    int parity = 0;
+    for (; row < n_rows; row += gridDim.x) {
+        typename Loader::Raw cur[RB];
+#pragma unroll
+        for (int q = 0; q < RB; q++) cur[q] = nxt[q];
+        const int64_t next = row + gridDim.x;
+        if (next < n_rows) fetch_row(next);
+
+        float v[RB][16];
+        float amax = 0.0f;
+#pragma unroll
+        for (int q = 0; q < RB; q++) {
+            const int b = grp + q * G;
+            if (b < nb) {
+                ld.decode(cur[q], (int64_t)b * 16 + t, v[q]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; i++) v[q][i] = 0.0f;
+            }
+            convrot256(v[q], tile, t);
+#pragma unroll
+            for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(v[q][i]));
+        }
+        const float a = block_max(amax, red + 16 * parity);
+        parity ^= 1;
+        const float rcp = (a == 0.0f) ? 0.0f : 127.0f / a;
+        int8_t *orow = out + row * ld_out;
+#pragma unroll
+        for (int q = 0; q < RB; q++) {
+            const int b = grp + q * G;
+            if (b < nb) quantize_store16(v[q], rcp, orow + (int64_t)b * 256 + t * 16);
+        }
+        if (tid == 0) scale_out[row] = (a == 0.0f) ? 0.0f : a / 127.0f;
+    }
+}
+
+// Two passes, one row per workgroup: the row is streamed in slices of G blocks, once for
+// the maximum and once for the codes (the same operations both times, so the same bits).
+template <class Loader>
+__device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row, int nb,
+                                                  int8_t *__restrict__ out, int64_t ld_out,
+                                                  float *__restrict__ scale_out)
 {
     extern __shared__ float lds[];
     const int tid = threadIdx.x;
@@ -161,42 +228,21 @@ __device__ __forceinline__ void row_prep(const Loader &ld, int64_t row, int nb,
     float *red = lds + G * kTileStrideF;
     int8_t *orow = out + row * ld_out;
 
-    float amax = 0.0f;
-    if (!two_pass) {
-        float v[RB][16];
-#pragma unroll
-        for (int r = 0; r < RB; r++) {
-            const int b = grp + r * G;
-            if (b < nb) {
-                ld.load16(row, (int64_t)b * 16 + t, v[r]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 16; i++) v[r][i] = 0.0f;
-            }
-            convrot256(v[r], tile, t);
-#pragma unroll
-            for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(v[r][i]));
-        }
-        const float a = block_max(amax, red);
-        const float rcp = (a == 0.0f) ? 0.0f : 127.0f / a;
-#pragma unroll
-        for (int r = 0; r < RB; r++) {
-            const int b = grp + r * G;
-            if (b < nb) quantize_store16(v[r], rcp, orow + (int64_t)b * 256 + t * 16);
-        }
-        if (tid == 0) scale_out[row] = (a == 0.0f) ? 0.0f : a / 127.0f;
-        return;
-    }
-    float v[16];
-    const int nslices = (nb + G - 1) / G;
-    for (int s = 0; s < nslices; s++) {
-        const int b = s * G + grp;
+    auto load = [&](int b, float (&v)[16]) {
         if (b < nb) {
-            ld.load16(row, (int64_t)b * 16 + t, v);
+            typename Loader::Raw raw;
+            ld.fetch(row, (int64_t)b * 16 + t, raw);
+            ld.decode(raw, (int64_t)b * 16 + t, v);
         } else {
 #pragma unroll
             for (int i = 0; i < 16; i++) v[i] = 0.0f;
         }
+    };
+    float v[16];
+    float amax = 0.0f;
+    const int nslices = (nb + G - 1) / G;
+    for (int s = 0; s < nslices; s++) {
+        load(s * G + grp, v);
         convrot256(v, tile, t);
 #pragma unroll
         for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(v[i]));
@@ -205,16 +251,21 @@ __device__ __forceinline__ void row_prep(const Loader &ld, int64_t row, int nb,
     const float rcp = (a == 0.0f) ? 0.0f : 127.0f / a;
     for (int s = 0; s < nslices; s++) {
         const int b = s * G + grp;
-        if (b < nb) {
-            ld.load16(row, (int64_t)b * 16 + t, v);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; i++) v[i] = 0.0f;
-        }
+        load(b, v);
         convrot256(v, tile, t);
         if (b < nb) quantize_store16(v, rcp, orow + (int64_t)b * 256 + t * 16);
     }
     if (tid == 0) scale_out[row] = (a == 0.0f) ? 0.0f : a / 127.0f;
+}
+
+// Kernel body shared by all loaders.
+template <class Loader, int RB>
+__device__ __forceinline__ void row_prep_kernel_body(const Loader &ld, int64_t n_rows, int nb,
+                                                     int8_t *__restrict__ out, int64_t ld_out,
+                                                     float *__restrict__ scale_out, int two_pass)
+{
+    if (two_pass) row_prep_two_pass(ld, (int64_t)blockIdx.x, nb, out, ld_out, scale_out);
+    else row_prep_rows<Loader, RB>(ld, n_rows, nb, out, ld_out, scale_out);
 }
 
 // Launch shape of a row of nb blocks: at most 512 threads (32 groups, 35 KB of LDS).
@@ -223,6 +274,23 @@ struct RowPrepShape {
     int rb;        // blocks held per 16-lane group in one-pass mode (1 or 2)
     bool two_pass;
 };
+
+// Workgroups of the one-pass row loop: enough resident rows per CU to hide latency,
+// never more workgroups than rows.  Two-pass launches one workgroup per row.
+inline int row_prep_grid(int64_t n_rows, const RowPrepShape &s)
+{
+    if (s.two_pass) return (int)n_rows;
+    static int cus_cache[64] = {0};
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+        cus = cus_cache[dev];
+        if (cus == 0 && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+            cus_cache[dev] = cus;
+    }
+    if (cus <= 0) cus = 256;
+    const int64_t want = (int64_t)cus * 8;
+    return (int)(n_rows < want ? n_rows : want);
+}
 
 inline RowPrepShape row_prep_shape(int64_t nb, bool force_two_pass)
 {
