@@ -55,21 +55,24 @@ def gemm_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic():
+def counter_traffic(launch_shape):
     """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, or None if
-    the GEMM source changed since the counters were taken."""
+    the GEMM source or the launch shape (M, N, K_pad) changed since the counters were taken."""
     if not os.path.exists(PMC_PROFILE):
         return None
     txt = open(PMC_PROFILE).read()
     m_hash = re.search(r"gemm_source_sha256_16:\s*([0-9a-f]+)", txt)
     m_bytes = re.search(r"hbm_bytes_per_launch_calibrated:\s*([0-9.eE+]+)", txt)
-    if not (m_hash and m_bytes) or m_hash.group(1) != gemm_source_hash():
+    m_shape = re.search(r"launch_shape_m_n_kpad:\s*(\d+)\s+(\d+)\s+(\d+)", txt)
+    if not (m_hash and m_bytes and m_shape) or m_hash.group(1) != gemm_source_hash():
+        return None
+    if tuple(int(v) for v in m_shape.groups()) != tuple(launch_shape):
         return None
     return float(m_bytes.group(1))
 
 
 class Layer:
-    def __init__(self, name, torch, rbl, synth, dev):
+    def __init__(self, name, torch, rbl, synth, dev, max_tile_bytes):
         w = synth.WORKLOADS[name]
         self.name, self.w = name, w
         t0 = time.perf_counter()
@@ -80,10 +83,14 @@ class Layer:
         self.codes, self.sf = p.codes.to(dev), p.sf.to(dev)
         self.g = torch.tensor([p.g], dtype=torch.float32, device=dev)
         kp = w.K_pad
+        # the chunking cr_linear_nvfp4 uses on this device, mirrored with component calls
+        self.R, self.nchunks = rbl.cr_linear_nvfp4_plan(w.M, w.N, w.K, max_tile_bytes)
+        self.chunks = [(n0, min(self.R, w.N - n0)) for n0 in range(0, w.N, self.R)]
+        ntiles = 2 if self.nchunks > 1 else 1
         self.x_s8 = torch.empty(w.M, kp, dtype=torch.int8, device=dev)
         self.x_scale = torch.empty(w.M, dtype=torch.float32, device=dev)
-        self.w_s8 = torch.empty(w.N, kp, dtype=torch.int8, device=dev)
-        self.w_scale = torch.empty(w.N, dtype=torch.float32, device=dev)
+        self.w_s8 = [torch.empty(self.R, kp, dtype=torch.int8, device=dev) for _ in range(ntiles)]
+        self.w_scale = [torch.empty(self.R, dtype=torch.float32, device=dev) for _ in range(ntiles)]
         self.out = torch.empty(w.M, w.N, dtype=synth.TORCH_DTYPE[w.out_dtypes[0]], device=dev)
         self.gen_s = time.perf_counter() - t0
         es = self.x.element_size()
@@ -91,29 +98,41 @@ class Layer:
         self.act_bytes = w.M * cols * es + w.M * kp + 4 * w.M
         self.w_bytes = w.N * ((w.K + 1) // 2) + w.N * ((w.K + 15) // 16) + 4 + w.N * kp + 4 * w.N
         self.gemm_ops = 2 * w.M * w.N * kp
+        self.n_events = 3 + 4 * self.nchunks
 
 
 def run_layer(L, rbl, s_main, s_aux, ev):
-    """Activation prep || weight prep, then the GEMM; ev = 7 events (or None)."""
+    """The layer as cr_linear_nvfp4 runs it: activation prep (main stream) while chunk 0 of
+    the weight is prepared (second stream); GEMM of chunk c on the main stream while chunk
+    c+1 is prepared; a weight tile is refilled only after the GEMM that read it.
+    ev: 3 + 4 * nchunks events: start, act begin/end, then per chunk prep begin/end and
+    GEMM begin/end."""
     w = L.w
+    sw = s_aux if s_aux is not None else s_main
+    ev[0].record(s_main)
     if s_aux is not None:
-        ev[0].record(s_main)
         s_aux.wait_event(ev[0])
-    ev[1].record(s_main)
     if w.swiglu:
         rbl.cr_quant_act_swiglu(L.x, w.K, L.x_s8, L.x_scale, stream=s_main)
     else:
         rbl.cr_quant_act(L.x, w.K, L.x_s8, L.x_scale, stream=s_main)
+    ev[1].record(s_main)
+    for c, (n0, r) in enumerate(L.chunks):
+        t = c % 2
+        e = 3 + 4 * c
+        if c >= 2 and s_aux is not None:
+            s_aux.wait_event(ev[e - 8 + 3])           # GEMM of chunk c-2 read this tile
+        ev[e].record(sw)
+        rbl.cr_prep_weight_nvfp4(L.codes[n0:n0 + r], L.sf[n0:n0 + r], L.g, w.K, L.w_s8[t][:r],
+                                 L.w_scale[t][:r], stream=sw)
+        ev[e + 1].record(sw)
+        if s_aux is not None:
+            s_main.wait_event(ev[e + 1])
+        ev[e + 2].record(s_main)
+        rbl.cr_gemm_s8_rowscale(L.x_s8, L.x_scale, L.w_s8[t][:r], L.w_scale[t][:r],
+                                L.out[:, n0:n0 + r], stream=s_main)
+        ev[e + 3].record(s_main)
     ev[2].record(s_main)
-    sw = s_aux if s_aux is not None else s_main
-    ev[3].record(sw)
-    rbl.cr_prep_weight_nvfp4(L.codes, L.sf, L.g, w.K, L.w_s8, L.w_scale, stream=sw)
-    ev[4].record(sw)
-    if s_aux is not None:
-        s_main.wait_event(ev[4])
-    ev[5].record(s_main)
-    rbl.cr_gemm_s8_rowscale(L.x_s8, L.x_scale, L.w_s8, L.w_scale, L.out, stream=s_main)
-    ev[6].record(s_main)
 
 
 def cpu_baseline(layers, sample_rows):
@@ -191,15 +210,15 @@ def main():
     layers = []
     for n in names:
         print(f"bench: generating {n} ...", file=sys.stderr, flush=True)
-        layers.append(Layer(n, torch, rbl, synth, dev))
+        layers.append(Layer(n, torch, rbl, synth, dev, args.max_tile_bytes))
     torch.cuda.synchronize()
 
     s_main = torch.cuda.current_stream()
     s_aux = None if args.serial else torch.cuda.Stream()
     K, W = args.steps, args.warmup
     mk = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
-    evs = [[[mk() for _ in range(7)] for _ in layers] for _ in range(K)]
-    scratch = [[mk() for _ in range(7)] for _ in layers]
+    evs = [[[mk() for _ in range(L.n_events)] for L in layers] for _ in range(K)]
+    scratch = [[mk() for _ in range(L.n_events)] for L in layers]
 
     print(f"bench: warmup {W} steps", file=sys.stderr, flush=True)
     for _ in range(W):
@@ -223,12 +242,18 @@ def main():
     for li, L in enumerate(layers):
         def mean(a, b):
             return sum(evs[k][li][a].elapsed_time(evs[k][li][b]) for k in range(K)) / K
-        t_layer = mean(1, 6)
-        t_act, t_w, t_g = mean(1, 2), mean(3, 4), mean(5, 6)
+        nc = L.nchunks
+        t_layer = mean(0, 2)
+        t_act = mean(0, 1)
+        t_w = sum(mean(3 + 4 * c, 4 + 4 * c) for c in range(nc))
+        g_launch = [mean(5 + 4 * c, 6 + 4 * c) for c in range(nc)]
+        t_g = sum(g_launch)
         layer_info[L.name] = {
             "M": L.w.M, "N": L.w.N, "K": L.w.K, "K_pad": L.w.K_pad, "swiglu": L.w.swiglu,
+            "weight_chunks": nc, "rows_per_chunk": L.R,
             "ms": round(t_layer, 4),
             "gemm_ms": round(t_g, 4),
+            "gemm_launch_ms": [round(v, 4) for v in g_launch],
             "gemm_tops": round(L.gemm_ops / (t_g * 1e-3) / 1e12, 1),
             "gemm_frac_peak": round(L.gemm_ops / (t_g * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
             "layer_tops": round(L.gemm_ops / (t_layer * 1e-3) / 1e12, 1),
@@ -236,6 +261,7 @@ def main():
             "act_prep_gbs": round(L.act_bytes / (t_act * 1e-3) / 1e9, 1),
             "weight_prep_ms": round(t_w, 4),
             "weight_prep_gbs": round(L.w_bytes / (t_w * 1e-3) / 1e9, 1),
+            "not_gemm_ms": round(t_layer - t_g, 4),
         }
 
     # the product entry point computes the same layer (one untimed call per layer)
@@ -250,8 +276,12 @@ def main():
 
     dom = layers[0]
     dom_info = layer_info[dom.name]
-    achieved = dom.gemm_ops / (dom_info["gemm_ms"] * 1e-3) / 1e12
-    traffic = counter_traffic()
+    # per launch: algorithmic ops of one chunk's GEMM over its mean launch duration
+    launch_ops = dom.gemm_ops / dom.nchunks
+    launch_ms = dom_info["gemm_ms"] / dom.nchunks
+    achieved = launch_ops / (launch_ms * 1e-3) / 1e12
+    launch_shape = (dom.w.M, dom.chunks[0][1], dom.w.K_pad)
+    traffic = counter_traffic(launch_shape)
     result = {
         "metric": METRIC,
         "value": round(sum(v["ms"] for v in layer_info.values()) / len(layer_info), 4),
@@ -274,7 +304,8 @@ def main():
             "max_tile_bytes": args.max_tile_bytes or rbl.DEFAULT_MAX_TILE_BYTES,
         },
         "roofline": {
-            "kernel": f"gemm_s8_rowscale ({dom.name}: M={dom.w.M} N={dom.w.N} K_pad={dom.w.K_pad})",
+            "kernel": (f"gemm_s8_rowscale ({dom.name}: {dom.nchunks} launch(es) of M={launch_shape[0]} "
+                       f"N={launch_shape[1]} K_pad={launch_shape[2]})"),
             "bound": "mfma",
             "achieved": round(achieved, 1),
             "peak": PEAK_INT8_TOPS,

@@ -168,6 +168,14 @@ cr_status cr_gemm_s8_rowscale(const int8_t *a_s8, int64_t lda, const float *a_sc
  */
 size_t cr_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes);
 
+/* The chunking cr_linear_nvfp4 uses on the current device: rows per weight chunk (a
+ * multiple of 256) and the number of chunks.  The bound max_tile_bytes caps a chunk; a
+ * weight that fits one chunk is still split in two when the two GEMMs need no more
+ * workgroup rounds over the device's compute units than one (the second chunk is then
+ * prepared while the first multiplies).  Host pointers; CR_OK or an argument status. */
+cr_status cr_linear_nvfp4_plan(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes,
+                               int64_t *rows_per_chunk, int64_t *nchunks);
+
 cr_status cr_linear_nvfp4(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu,
                           int64_t M, int64_t K,
                           const uint8_t *w_fp4, int64_t ld_fp4,

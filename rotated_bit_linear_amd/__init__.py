@@ -62,6 +62,7 @@ def lib() -> C.CDLL:
             "cr_swiglu": (C.c_int, [vp, C.c_int, i64, i64, i64, vp, i64, vp]),
             "cr_gemm_s8_rowscale": (C.c_int, [vp, i64, vp, vp, i64, vp, i64, i64, i64, vp, C.c_int, i64, vp]),
             "cr_linear_nvfp4_workspace_bytes": (sz, [i64, i64, i64, sz]),
+            "cr_linear_nvfp4_plan": (C.c_int, [i64, i64, i64, sz, C.POINTER(i64), C.POINTER(i64)]),
             "cr_linear_nvfp4": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, i64, vp, i64, vp, i64,
                                           vp, C.c_int, i64, vp, sz, sz, u32, vp, vp]),
         }
@@ -161,6 +162,14 @@ def cr_gemm_s8_rowscale(a_s8, a_scale, b_s8, b_scale, c, stream=None, M=None, N=
 
 def cr_linear_nvfp4_workspace_bytes(M, N, K, max_tile_bytes=0) -> int:
     return int(lib().cr_linear_nvfp4_workspace_bytes(M, N, K, max_tile_bytes))
+
+
+def cr_linear_nvfp4_plan(M, N, K, max_tile_bytes=0) -> tuple[int, int]:
+    """(rows per weight chunk, number of chunks) that cr_linear_nvfp4 uses on this device."""
+    r, n = C.c_int64(0), C.c_int64(0)
+    _check("cr_linear_nvfp4_plan", lib().cr_linear_nvfp4_plan(M, N, K, max_tile_bytes,
+                                                              C.byref(r), C.byref(n)))
+    return int(r.value), int(n.value)
 
 
 def cr_linear_nvfp4(x, K, swiglu, w_fp4, w_sf, global_scale, out, workspace, max_tile_bytes=0,

@@ -121,25 +121,52 @@ struct LayerPlan {
 
 inline size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+int current_cus()
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    return cus;
+}
+
+// Rows per weight chunk.  The tile bound gives the largest chunk (a multiple of the GEMM
+// tile height).  When the whole weight fits one chunk it is still split in two whenever
+// the two GEMMs together need no more rounds of workgroups over the CUs than one GEMM
+// would: then the second chunk's preparation can overlap the first chunk's GEMM and the
+// split costs nothing.
+int64_t plan_rows(int64_t M, int64_t N, int64_t K_pad, size_t max_tile_bytes, int cus)
+{
+    const int64_t T = convrot::kGemmTileRows;
+    int64_t R = (int64_t)(max_tile_bytes / (size_t)K_pad) / T * T;
+    if (R < T) R = T;
+    const int64_t tiles_n = (N + T - 1) / T;
+    if (R < tiles_n * T) return R;                      // chunked by the bound already
+    if (tiles_n < 2) return tiles_n * T;
+    const int64_t tiles_m = (M + convrot::kGemmTileCols - 1) / convrot::kGemmTileCols;
+    auto rounds = [&](int64_t tiles) { return (tiles + cus - 1) / cus; };
+    const int64_t t0 = (tiles_n + 1) / 2, t1 = tiles_n - t0;
+    if (rounds(tiles_m * t0) + rounds(tiles_m * t1) <= rounds(tiles_m * tiles_n)) return t0 * T;
+    return tiles_n * T;
+}
+
 LayerPlan plan_layer(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes)
 {
     LayerPlan p{};
     if (max_tile_bytes == 0) max_tile_bytes = CR_DEFAULT_MAX_TILE_BYTES;
     p.K_pad = pad256(K);
-    int64_t R = (int64_t)(max_tile_bytes / (size_t)p.K_pad) / 256 * 256;
-    if (R < 256) R = 256;
-    const int64_t Nr = ((N + 255) / 256) * 256;
-    if (R > Nr) R = Nr;
-    p.R = R;
-    p.nchunks = (N + R - 1) / R;
+    p.R = plan_rows(M, N, p.K_pad, max_tile_bytes, current_cus());
+    p.nchunks = (N + p.R - 1) / p.R;
     size_t off = up256((size_t)M * (size_t)p.K_pad);
     p.off_xscale = off;
     off = up256(off + (size_t)M * 4);
     const int ntiles = p.nchunks > 1 ? 2 : 1;
     for (int t = 0; t < 2; t++) {
         p.off_tile[t] = off;
-        p.off_tscale[t] = up256(off + (size_t)R * (size_t)p.K_pad);
-        if (t < ntiles) off = up256(p.off_tscale[t] + (size_t)R * 4);
+        p.off_tscale[t] = up256(off + (size_t)p.R * (size_t)p.K_pad);
+        if (t < ntiles) off = up256(p.off_tscale[t] + (size_t)p.R * 4);
     }
     p.bytes = off;
     return p;
@@ -239,6 +266,18 @@ cr_status cr_gemm_s8_rowscale(const int8_t *a_s8, int64_t lda, const float *a_sc
     if ((s = current_device_ok()) != CR_OK) return s;
     return from_hip(convrot::launch_gemm_s8(a_s8, lda, a_scale, b_s8, ldb, b_scale, M, N, K_pad, c,
                                             (int)c_dtype, ldc, stream));
+}
+
+cr_status cr_linear_nvfp4_plan(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes,
+                               int64_t *rows_per_chunk, int64_t *nchunks)
+{
+    if (!rows_per_chunk || !nchunks) return CR_ERR_INVALID_ARG;
+    if (M < 1 || N < 1 || K < 1) return CR_ERR_INVALID_ARG;
+    if (pad256(K) > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
+    const LayerPlan p = plan_layer(M, N, K, max_tile_bytes);
+    *rows_per_chunk = p.R;
+    *nchunks = p.nchunks;
+    return CR_OK;
 }
 
 size_t cr_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes)

@@ -6,6 +6,10 @@
 
 namespace convrot {
 
+// output tile of one GEMM workgroup (rows of A = activation rows, rows of B = weight rows)
+constexpr int64_t kGemmTileCols = 256;   // M direction
+constexpr int64_t kGemmTileRows = 256;   // N direction (weight rows)
+
 // dtype codes follow cr_dtype: 0 bf16, 1 fp16, 2 fp32, 3 int32 (GEMM output only)
 hipError_t launch_quant_act(const void *x, int dtype, int64_t ld_x, int64_t M, int64_t K,
                             int8_t *x_s8, int64_t ld_s8, float *x_scale, bool two_pass,

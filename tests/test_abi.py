@@ -22,6 +22,7 @@ def test_library_exports_header_functions():
     names = rbl.header_functions()
     assert set(names) >= {"cr_prep_weight_nvfp4", "cr_quant_act", "cr_quant_act_swiglu",
                           "cr_gemm_s8_rowscale", "cr_linear_nvfp4", "cr_linear_nvfp4_workspace_bytes",
+                          "cr_linear_nvfp4_plan",
                           "cr_abi_version", "cr_status_string", "cr_padded_k"}
     for n in names:
         assert hasattr(L, n), n
@@ -117,6 +118,29 @@ def test_layer_validation_and_workspace():
     assert call(odt=3) == DT
     assert call(ldc=255) == INV
     assert call(sw=1) == INV                       # SwiGLU needs ld_x >= 2K
+
+
+def test_layer_chunk_plan():
+    # Without a device the planner assumes 256 compute units, as on MI355X.
+    # QKV (M 19989, N 21504): 79 x 84 tiles take 26 rounds; two halves of 42 tile columns
+    # take 13 + 13, so the weight is split and its second half is prepared during the
+    # first GEMM.
+    assert rbl.cr_linear_nvfp4_plan(19989, 21504, 5376) == (10752, 2)
+    assert rbl.cr_linear_nvfp4_plan(4096, 21504, 5376) == (10752, 2)       # 6 rounds = 3 + 3
+    # FFN down (N 5376): 79 x 21 tiles take 7 rounds, halves 4 + 4: not split.
+    assert rbl.cr_linear_nvfp4_plan(19989, 5376, 14336) == (5376, 1)
+    # one tile row of workgroups: a split would double the rounds
+    assert rbl.cr_linear_nvfp4_plan(64, 512, 256) == (512, 1)
+    assert rbl.cr_linear_nvfp4_plan(8192, 5000, 20000) == (5120, 1)
+    # the tile bound chunks first: 16 MiB / 5376 B per row -> 3072 rows
+    assert rbl.cr_linear_nvfp4_plan(19989, 21504, 5376, 16 << 20) == (3072, 7)
+    assert rbl.cr_linear_nvfp4_plan(1, 1, 1) == (256, 1)
+    # a bound below one tile height still gives one 256-row chunk
+    assert rbl.cr_linear_nvfp4_plan(300, 1000, 5376, 1) == (256, 4)
+    with pytest.raises(rbl.CrError):
+        rbl.cr_linear_nvfp4_plan(0, 256, 256)
+    with pytest.raises(rbl.CrError):
+        rbl.cr_linear_nvfp4_plan(1, 256, rbl.CR_MAX_K_PAD + 1)
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="valid arguments would launch on a real GPU")
