@@ -18,13 +18,16 @@
 
 namespace convrot {
 
-// E2M1 magnitude code m (0..7) -> binary32 bits: 0, 0.5, then (1 + m0/2) * 2^(e-1).
-__device__ __forceinline__ float e2m1_to_f32(uint32_t code)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// E2M1 codes -> binary32 with the gfx950 conversion instruction: nibbles 2j and 2j+1 of
+// `word` (byte j) become .x and .y.  With a scale of 1.0 the result is the exact E2M1
+// value; no other scale is used here, since the instruction applies only the exponent of
+// its scale operand.
+template <int J>
+__device__ __forceinline__ f32x2 e2m1_pair(uint32_t word)
 {
-    const uint32_t m = code & 7u;
-    uint32_t bits = (m >= 2u) ? ((m + 252u) << 22) : (m ? 0x3f000000u : 0u);
-    bits |= (code & 8u) << 28;
-    return __uint_as_float(bits);
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, J);
 }
 
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b)
@@ -44,6 +47,7 @@ struct NVFP4Loader {
     int64_t ld_sf;
     const float *g;
     int64_t K;
+    float gs;      // *g, read once per workgroup
     // raw bytes of one 16-element segment: 8 code bytes and its block-scale byte
     struct Raw {
         uint32_t w0, w1, sc;
@@ -73,22 +77,30 @@ struct NVFP4Loader {
     __device__ __forceinline__ void decode(const Raw &r, int64_t seg, float (&v)[16]) const
     {
         const int64_t k0 = seg * 16;
-        const float gs = *g;
         const float sc = e4m3_to_f32(r.sc);
+        f32x2 e[8];
+        e[0] = e2m1_pair<0>(r.w0); e[1] = e2m1_pair<1>(r.w0);
+        e[2] = e2m1_pair<2>(r.w0); e[3] = e2m1_pair<3>(r.w0);
+        e[4] = e2m1_pair<0>(r.w1); e[5] = e2m1_pair<1>(r.w1);
+        e[6] = e2m1_pair<2>(r.w1); e[7] = e2m1_pair<3>(r.w1);
 #pragma unroll
         for (int i = 0; i < 16; i++) {
-            const uint32_t code = (((i < 8) ? r.w0 : r.w1) >> (4 * (i & 7))) & 15u;
-            const float prod = e2m1_to_f32(code) * sc;   // exact
-            const float val = prod * gs;
-            v[i] = (k0 + i < K) ? val : 0.0f;             // nibbles past K are padding
+            const float prod = ((i & 1) ? e[i >> 1].y : e[i >> 1].x) * sc;   // exact
+            v[i] = prod * gs;
+        }
+        if (k0 + 16 > K) {                                // nibbles past K are padding
+#pragma unroll
+            for (int i = 0; i < 16; i++)
+                if (k0 + i >= K) v[i] = 0.0f;
         }
     }
 };
 
 template <int RB>
-__global__ __launch_bounds__(512) void prep_weight_kernel(NVFP4Loader ld, int64_t n_rows, int nb, int8_t *__restrict__ out,
+__global__ __launch_bounds__(512, CONVROT_PREP_MIN_WAVES) void prep_weight_kernel(NVFP4Loader ld, int64_t n_rows, int nb, int8_t *__restrict__ out,
                                    int64_t ld_out, float *__restrict__ scale, int two_pass)
 {
+    ld.gs = *ld.g;
     row_prep_kernel_body<NVFP4Loader, RB>(ld, n_rows, nb, out, ld_out, scale, two_pass);
 }
 
@@ -100,7 +112,7 @@ hipError_t launch_prep_weight(const uint8_t *codes, int64_t ld_codes, const uint
     const RowPrepShape s = row_prep_shape(nb, two_pass);
     const size_t lds = row_prep_lds_bytes(s.threads);
     const dim3 grid((unsigned)row_prep_grid(n_rows, s));
-    NVFP4Loader L{codes, ld_codes, sf, ld_sf, g, K};
+    NVFP4Loader L{codes, ld_codes, sf, ld_sf, g, K, 0.0f};
     if (s.rb == 2)
         hipLaunchKernelGGL(prep_weight_kernel<2>, grid, dim3(s.threads), lds, st,
                            L, n_rows, (int)nb, w_s8, ld_s8, w_scale, 0);

@@ -68,19 +68,23 @@ __device__ __forceinline__ void fetch_seg(const typename Elem<DT>::T *row, int64
     }
 }
 
+// element i (0..15) of a fetched segment
+template <int DT>
+__device__ __forceinline__ float seg_elem(const RawSeg<DT> &r, int i)
+{
+    if constexpr (DT == 2) {
+        return __uint_as_float(r.w[i >> 2][i & 3]);
+    } else {
+        const uint32_t w = r.w[i >> 3][(i >> 1) & 3];
+        return Elem<DT>::cvt((uint16_t)((i & 1) ? (w >> 16) : (w & 0xffffu)));
+    }
+}
+
 template <int DT>
 __device__ __forceinline__ void decode_seg(const RawSeg<DT> &r, float (&v)[16])
 {
-    if constexpr (DT == 2) {
 #pragma unroll
-        for (int i = 0; i < 16; i++) v[i] = __uint_as_float(r.w[i >> 2][i & 3]);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const uint32_t w = r.w[i >> 3][(i >> 1) & 3];
-            v[i] = Elem<DT>::cvt((uint16_t)((i & 1) ? (w >> 16) : (w & 0xffffu)));
-        }
-    }
+    for (int i = 0; i < 16; i++) v[i] = seg_elem<DT>(r, i);
 }
 
 // ------------------------------------------------------ reproducible exponential ----
@@ -88,15 +92,20 @@ __device__ __forceinline__ void decode_seg(const RawSeg<DT> &r, float (&v)[16])
 // E(x) ~ exp(x) from IEEE basic operations only: Cody & Waite (1980) reduction
 // x = k ln2 + r, k = rint(x log2 e), ln2 = C1 + C2 with C1 holding 15 significant bits,
 // then the degree-7 Taylor polynomial of exp(r) in Horner form with fused multiply-adds,
-// then the exact scaling by 2^k.  Coefficients: RN(1/n!).
-__device__ __forceinline__ float repro_exp(float x)
+// then the exact scaling by 2^k.  Coefficients: RN(1/n!).  By definition E(x) = +inf for
+// x > 89 and E(x) = 0 for x < -104.
+//
+// The steps are evaluated on x clamped to [-200, 200] with no further selects: inside
+// [-104, 89] nothing changes; for x in (89, 200] the reduction gives k >= 128 with
+// p >= 1.32 (k = 128) or p >= 0.70 (k > 128), so p * 2^k overflows to +inf; for x in
+// [-200, -104) it gives p * 2^k < 2^-150, which rounds to 0.  A NaN argument is clamped
+// to a bound; the callers below only use E(-a) inside a product with a, which is NaN.
+__device__ __forceinline__ float repro_exp_nan_free(float x)
 {
     const float kLog2e = 0x1.715476p+0f;
     const float kC1 = 0x1.62e4p-1f;
     const float kC2 = 0x1.7f7d1cp-20f;
-    // evaluate on x clamped to [-104, 89] (unchanged inside that range), then select the
-    // out-of-range results: no divergent branches per element
-    const float xc = fminf(fmaxf(x, -104.0f), 89.0f);
+    const float xc = fminf(fmaxf(x, -200.0f), 200.0f);
     const float kf = rintf(xc * kLog2e);
     float r = fmaf(-kf, kC1, xc);
     r = fmaf(-kf, kC2, r);
@@ -108,19 +117,40 @@ __device__ __forceinline__ float repro_exp(float x)
     p = fmaf(p, r, 0x1.0p-1f);             // 1/2!
     p = fmaf(p, r, 1.0f);
     p = fmaf(p, r, 1.0f);
-    float e = __builtin_amdgcn_ldexpf(p, (int)kf);
-    e = (x > 89.0f) ? __builtin_inff() : e;
-    e = (x < -104.0f) ? 0.0f : e;
-    return (x != x) ? x : e;
+    return __builtin_amdgcn_ldexpf(p, (int)kf);
 }
 
-// swish(gate) * value with swish(a) = a / (1 + E(-a)) evaluated as a * (1 / (1 + E(-a))).
-__device__ __forceinline__ float swiglu_elem(float gate, float value)
+// 1 / d for 1 <= d < 2^126, correctly rounded: the hardware reciprocal estimate refined by
+// one Newton step in fused multiply-adds (Markstein's correction).  The tests check it
+// against IEEE division for every d that an fp32 gate can produce here.
+__device__ __forceinline__ float recip_refined(float d)
 {
-    const float t = repro_exp(-gate);
-    const float sig = 1.0f / (1.0f + t);
-    const float sw = gate * sig;
-    return sw * value;
+    const float y = __builtin_amdgcn_rcpf(d);
+    const float e = fmaf(-d, y, 1.0f);
+    return fmaf(e, y, y);
+}
+
+constexpr float kRecipLimit = 0x1p126f;   // d at or above: IEEE division (gate below about -87.3)
+
+// The SwiGLU element: swish(a) * b with swish(a) = a * sigma(a), sigma(a) = 1 / (1 + E(-a)),
+// every operation rounded once as written.
+__device__ __forceinline__ float swiglu_exact(float a, float b)
+{
+    const float d = 1.0f + repro_exp_nan_free(-a);
+    return (a * (1.0f / d)) * b;
+}
+
+// Same value; the refined reciprocal where it is exact, IEEE division for the lanes (a
+// wave-uniform branch, practically never taken) whose denominator is 2^126 or more.
+__device__ __forceinline__ float swiglu_elem(float a, float b)
+{
+    const float d = 1.0f + repro_exp_nan_free(-a);
+    float o = (a * recip_refined(d)) * b;
+    const bool far = !(d < kRecipLimit);
+    if (__builtin_amdgcn_ballot_w64(far) != 0) {
+        if (far) o = (a * (1.0f / d)) * b;
+    }
+    return o;
 }
 
 // --------------------------------------------------------------------- loaders ----
@@ -160,8 +190,21 @@ struct SwigluLoader {
         float b[16];
         decode_seg<DT>(r.gate, v);
         decode_seg<DT>(r.value, b);
+        bool far = false;
 #pragma unroll
-        for (int i = 0; i < 16; i++) v[i] = swiglu_elem(v[i], b[i]);   // zero past F: 0 * sig * 0
+        for (int i = 0; i < 16; i++) {                  // zero past F: 0 * sigma * 0
+            const float d = 1.0f + repro_exp_nan_free(-v[i]);
+            far |= !(d < kRecipLimit);
+            v[i] = (v[i] * recip_refined(d)) * b[i];
+        }
+        if (__builtin_amdgcn_ballot_w64(far) != 0) {   // some gate below about -87.3
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const float a = seg_elem<DT>(r.gate, i);
+                const float d = 1.0f + repro_exp_nan_free(-a);
+                if (!(d < kRecipLimit)) v[i] = swiglu_exact(a, seg_elem<DT>(r.value, i));
+            }
+        }
     }
 };
 
@@ -182,7 +225,7 @@ __global__ void swiglu_kernel(const typename Elem<DT>::T *__restrict__ h, int64_
 }
 
 template <class Loader, int RB>
-__global__ __launch_bounds__(512) void quant_act_kernel(Loader ld, int64_t n_rows, int nb, int8_t *__restrict__ out, int64_t ld_out,
+__global__ __launch_bounds__(512, CONVROT_PREP_MIN_WAVES) void quant_act_kernel(Loader ld, int64_t n_rows, int nb, int8_t *__restrict__ out, int64_t ld_out,
                                  float *__restrict__ scale, int two_pass)
 {
     row_prep_kernel_body<Loader, RB>(ld, n_rows, nb, out, ld_out, scale, two_pass);

@@ -7,12 +7,22 @@
 // with the butterfly stages in the fixed order h = 1, 2, ..., 128:
 //   phase A: lane t holds elements 16t..16t+15, stages h = 1..8 run inside the lane;
 //   transpose through LDS so lane t holds elements t, t+16, ..., t+240;
-//   phase B: stages h = 16..128 run inside the lane, then the 1/16 scaling;
+//   phase B: stages h = 16..128 run inside the lane;
 //   transpose back so lane t again holds 16 contiguous elements.
-// Every butterfly is the same IEEE add/sub as in the plain definition, so the result is
-// bit-identical to the sequential transform whatever the data layout.
-// Then the row maximum of |y| (exact, order-free), the FP32 scale a/127 and the rounded
-// reciprocal 127/a, and q = clamp(rint(y * r), -127, 127) stored as 16 contiguous bytes.
+// Every butterfly is the same IEEE add/sub as in the plain definition, so the butterfly
+// output z is bit-identical to the sequential transform whatever the data layout.
+//
+// The final 1/16 scaling y = z * 0.0625 is folded into the quantization.  With
+// a' = max |z| (exact, order-free): a = max |y| = a' * 0.0625 (rounding is monotone);
+// r = 127 / a; and when a' >= 2^-100, y * r = z * (r * 0.0625) exactly for every element
+// that can round to a nonzero code (scaling by 2^-4 is exact for normal numbers, and
+// elements so small that z * 0.0625 is subnormal give |y * r| < 2^-15 either way, hence
+// code 0).  Rows with 0 < a' < 2^-100 scale every element as written.  Either way the
+// codes and the scale a / 127 are those of the plain definition, bit for bit.
+//
+// Codes: q = clamp(rint(y * r), -127, 127); clamping first and then adding 1.5 * 2^23
+// rounds to the nearest integer, ties to even, and leaves q in two's complement in the
+// low byte of the sum (the sum lies in [2^23, 2^24), where the spacing is 1).
 //
 // Rows whose K_pad exceeds 64 blocks (16384 columns), or when forced, are streamed twice:
 // pass 1 rotates every block to find the row maximum, pass 2 reloads, rotates again and
@@ -23,6 +33,11 @@
 #include <stdint.h>
 
 namespace convrot {
+
+// Minimum waves per SIMD the preparation kernels are compiled for (caps their registers).
+#ifndef CONVROT_PREP_MIN_WAVES
+#define CONVROT_PREP_MIN_WAVES 2
+#endif
 
 constexpr int kLanesPerBlock = 16;          // lanes sharing one 256-column block
 constexpr int kTileStrideF = 272;           // floats per 16x16 transpose tile (256 + 16 pad)
@@ -61,9 +76,10 @@ __device__ __forceinline__ void butterflies16(float (&v)[16])
     }
 }
 
-// Full ConvRot256 of the block held by this lane's 16-lane group.  `tile` is the group's
-// private 16x16 LDS tile.  In: v[i] = x[16t + i].  Out: v[i] = y[16t + i].
-__device__ __forceinline__ void convrot256(float (&v)[16], float *tile, int t)
+// The eight butterfly stages of ConvRot256 on the block held by this lane's 16-lane group
+// (the 1/16 scaling is left to the quantization).  `tile` is the group's private 16x16
+// LDS tile.  In: v[i] = x[16t + i].  Out: v[i] = z[16t + i], y = z * 0.0625.
+__device__ __forceinline__ void hadamard256(float (&v)[16], float *tile, int t)
 {
     butterflies16(v);                                   // stages h = 1, 2, 4, 8
 #pragma unroll
@@ -75,8 +91,6 @@ __device__ __forceinline__ void convrot256(float (&v)[16], float *tile, int t)
 #pragma unroll
     for (int j = 0; j < 16; j++) v[j] = tile[tile_index(j, t)];   // v[j] = x'[16j + t]
     butterflies16(v);                                   // stages h = 16, 32, 64, 128
-#pragma unroll
-    for (int j = 0; j < 16; j++) v[j] = v[j] * 0.0625f;
     wave_lds_sync();
 #pragma unroll
     for (int j = 0; j < 16; j++) tile[tile_index(j, t)] = v[j];
@@ -109,30 +123,62 @@ __device__ __forceinline__ float block_max(float a, float *red)
     return m;
 }
 
-__device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d)
+// clamp(rint(t), -127, 127) in two's complement in the low byte of the result
+__device__ __forceinline__ uint32_t code_bits(float t)
 {
-    uint32_t r = (uint32_t)(uint8_t)(int8_t)(int)a;
-    r |= (uint32_t)(uint8_t)(int8_t)(int)b << 8;
-    r |= (uint32_t)(uint8_t)(int8_t)(int)c << 16;
-    r |= (uint32_t)(uint8_t)(int8_t)(int)d << 24;
-    return r;
+    t = fminf(fmaxf(t, -127.0f), 127.0f);
+    return __float_as_uint(t + 12582912.0f);
 }
 
-__device__ __forceinline__ void quantize_store16(const float (&v)[16], float r, int8_t *dst)
+// low bytes of a, b, c, d -> bytes 0..3
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
 {
-    float q[16];
+    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
+    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+
+// Codes of 16 butterfly outputs z, stored as 16 contiguous bytes: of z * m with
+// m = r * 0.0625 (folded), or of (z * 0.0625) * m with m = r (kScaleFirst).
+template <bool kScaleFirst>
+__device__ __forceinline__ void quantize_store16(const float (&z)[16], float m, int8_t *dst)
+{
+    uint32_t c[16];
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-        float t = rintf(v[i] * r);
-        t = fminf(fmaxf(t, -127.0f), 127.0f);
-        q[i] = t;
+        const float y = kScaleFirst ? z[i] * 0.0625f : z[i];
+        c[i] = code_bits(y * m);
     }
     uint4 o;
-    o.x = pack4(q[0], q[1], q[2], q[3]);
-    o.y = pack4(q[4], q[5], q[6], q[7]);
-    o.z = pack4(q[8], q[9], q[10], q[11]);
-    o.w = pack4(q[12], q[13], q[14], q[15]);
+    o.x = pack_low_bytes(c[0], c[1], c[2], c[3]);
+    o.y = pack_low_bytes(c[4], c[5], c[6], c[7]);
+    o.z = pack_low_bytes(c[8], c[9], c[10], c[11]);
+    o.w = pack_low_bytes(c[12], c[13], c[14], c[15]);
     *reinterpret_cast<uint4 *>(dst) = o;
+}
+
+// Row constants from a' = max |z|: the scale a / 127 and the code multiplier.
+struct RowQuant {
+    float scale;    // a / 127 (0 when a == 0)
+    float mult;     // r * 0.0625 (folded) or r (scale first)
+    bool folded;    // block-uniform
+};
+
+__device__ __forceinline__ RowQuant row_quant(float zmax)
+{
+    const float a = zmax * 0.0625f;
+    const float r = (a == 0.0f) ? 0.0f : 127.0f / a;
+    RowQuant q;
+    q.scale = (a == 0.0f) ? 0.0f : a / 127.0f;
+    q.folded = zmax >= 0x1p-100f;
+    q.mult = q.folded ? r * 0.0625f : r;
+    return q;
+}
+
+__device__ __forceinline__ void store_codes(const float (&z)[16], const RowQuant &q, int8_t *dst)
+{
+    if (q.folded) quantize_store16<false>(z, q.mult, dst);
+    else quantize_store16<true>(z, q.mult, dst);
 }
 
 // Dynamic LDS of one workgroup: per-group transpose tiles followed by two sets of
@@ -165,50 +211,68 @@ __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, 
     const int G = blockDim.x >> 4;
     float *tile = lds + grp * kTileStrideF;
     float *red = lds + G * kTileStrideF;
+    using Raw = typename Loader::Raw;
 
-    typename Loader::Raw nxt[RB];
-    auto fetch_row = [&](int64_t r) {
+    auto fetch_row = [&](int64_t r, Raw (&dst)[RB]) {
 #pragma unroll
         for (int q = 0; q < RB; q++) {
             const int b = grp + q * G;
-            if (b < nb) ld.fetch(r, (int64_t)b * 16 + t, nxt[q]);
+            if (b < nb) ld.fetch(r, (int64_t)b * 16 + t, dst[q]);
         }
     };
-    int64_t row = blockIdx.x;
-    fetch_row(row);
-    int parity = 0;
-    for (; row < n_rows; row += gridDim.x) {
-        typename Loader::Raw cur[RB];
-#pragma unroll
-        for (int q = 0; q < RB; q++) cur[q] = nxt[q];
-        const int64_t next = row + gridDim.x;
-        if (next < n_rows) fetch_row(next);
-
+    auto process = [&](const Raw (&cur)[RB], int64_t row, int parity) {
         float v[RB][16];
-        float amax = 0.0f;
+        float zmax = 0.0f;
 #pragma unroll
         for (int q = 0; q < RB; q++) {
             const int b = grp + q * G;
             if (b < nb) {
                 ld.decode(cur[q], (int64_t)b * 16 + t, v[q]);
-            } else {
+                hadamard256(v[q], tile, t);
 #pragma unroll
-                for (int i = 0; i < 16; i++) v[q][i] = 0.0f;
+                for (int i = 0; i < 16; i++) zmax = fmaxf(zmax, fabsf(v[q][i]));
             }
-            convrot256(v[q], tile, t);
-#pragma unroll
-            for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(v[q][i]));
         }
-        const float a = block_max(amax, red + 16 * parity);
-        parity ^= 1;
-        const float rcp = (a == 0.0f) ? 0.0f : 127.0f / a;
+        const RowQuant rq = row_quant(block_max(zmax, red + 16 * parity));
         int8_t *orow = out + row * ld_out;
 #pragma unroll
         for (int q = 0; q < RB; q++) {
             const int b = grp + q * G;
-            if (b < nb) quantize_store16(v[q], rcp, orow + (int64_t)b * 256 + t * 16);
+            if (b < nb) store_codes(v[q], rq, orow + (int64_t)b * 256 + t * 16);
         }
-        if (tid == 0) scale_out[row] = (a == 0.0f) ? 0.0f : a / 127.0f;
+        if (tid == 0) scale_out[row] = rq.scale;
+    };
+
+    int64_t row = blockIdx.x;
+    if constexpr (RB == 1) {
+        // two buffers in turn (the row loop unrolled by two): no register copies
+        Raw ra[RB], rb[RB];
+        if (row < n_rows) fetch_row(row, ra);
+        while (row < n_rows) {
+            int64_t next = row + gridDim.x;
+            if (next < n_rows) fetch_row(next, rb);
+            process(ra, row, 0);
+            row = next;
+            if (row >= n_rows) break;
+            next = row + gridDim.x;
+            if (next < n_rows) fetch_row(next, ra);
+            process(rb, row, 1);
+            row = next;
+        }
+    } else {
+        // one buffer copied forward: fewer live registers with two blocks per group
+        Raw nxt[RB];
+        if (row < n_rows) fetch_row(row, nxt);
+        int parity = 0;
+        for (; row < n_rows; row += gridDim.x) {
+            Raw cur[RB];
+#pragma unroll
+            for (int q = 0; q < RB; q++) cur[q] = nxt[q];
+            const int64_t next = row + gridDim.x;
+            if (next < n_rows) fetch_row(next, nxt);
+            process(cur, row, parity);
+            parity ^= 1;
+        }
     }
 }
 
@@ -239,23 +303,22 @@ __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row,
         }
     };
     float v[16];
-    float amax = 0.0f;
+    float zmax = 0.0f;
     const int nslices = (nb + G - 1) / G;
     for (int s = 0; s < nslices; s++) {
         load(s * G + grp, v);
-        convrot256(v, tile, t);
+        hadamard256(v, tile, t);
 #pragma unroll
-        for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(v[i]));
+        for (int i = 0; i < 16; i++) zmax = fmaxf(zmax, fabsf(v[i]));
     }
-    const float a = block_max(amax, red);
-    const float rcp = (a == 0.0f) ? 0.0f : 127.0f / a;
+    const RowQuant rq = row_quant(block_max(zmax, red));
     for (int s = 0; s < nslices; s++) {
         const int b = s * G + grp;
         load(b, v);
-        convrot256(v, tile, t);
-        if (b < nb) quantize_store16(v, rcp, orow + (int64_t)b * 256 + t * 16);
+        hadamard256(v, tile, t);
+        if (b < nb) store_codes(v, rq, orow + (int64_t)b * 256 + t * 16);
     }
-    if (tid == 0) scale_out[row] = (a == 0.0f) ? 0.0f : a / 127.0f;
+    if (tid == 0) scale_out[row] = rq.scale;
 }
 
 // Kernel body shared by all loaders.

@@ -75,6 +75,33 @@ def test_swiglu_fp32_random_and_edges():
     assert_bits_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32), "swiglu fp32 bits")
 
 
+def test_swiglu_fp32_every_gate_reaching_the_reciprocal():
+    """Every fp32 gate a with 2^-25 <= |a| < 2^7, value 1.0.  This range produces every
+    denominator 1 + E(-a) that the refined reciprocal handles (gates outside it give
+    d in {1, 2} or take the IEEE-division branch), so the refined reciprocal is checked
+    against the oracle's division for all of them.  16 chunks of 2^25 gates."""
+    F, M = 8192, 4096
+    n = F * M
+    h = torch.empty(M, 2 * F, dtype=torch.float32)
+    h[:, F:] = 1.0
+    hd = torch.empty(M, 2 * F, dtype=torch.float32, device=dev())
+    out = torch.empty(M, F, dtype=torch.float32, device=dev())
+    ones = np.ones(n, np.float32)
+    for c in range(16):
+        sign, e0 = c // 8, 102 + 4 * (c % 8)
+        start = (sign << 31) | (e0 << 23)
+        bits = np.arange(start, start + n, dtype=np.uint64).astype(np.uint32)
+        gate = bits.view(np.float32)
+        h[:, :F] = torch.from_numpy(gate.reshape(M, F))
+        say(f"cr_swiglu fp32 gates sign={sign} exponents {e0}..{e0 + 3}")
+        hd.copy_(h)
+        rbl.cr_swiglu(hd, F, out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().ravel()
+        ref = oracle.swiglu(gate, ones)
+        assert_bits_equal(got.view(np.uint32), ref.view(np.uint32), f"swiglu fp32 chunk {c}")
+
+
 # ------------------------------------------------------------ activation prep ----
 
 ACT_CASES = [
