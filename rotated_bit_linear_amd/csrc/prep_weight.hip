@@ -65,7 +65,7 @@ struct NVFP4Loader {
             r.w1 = q.y;
             return;
         }
-        const int64_t nbytes = (K - k0 + 1) / 2;   // bytes holding elements k0 .. K-1
+        const int nbytes = opaque((int)((K - k0 + 1) / 2));   // bytes holding elements k0 .. K-1
 #pragma unroll
         for (int i = 0; i < 8; i++)
             if (i < nbytes) {
@@ -89,15 +89,16 @@ struct NVFP4Loader {
             v[i] = prod * gs;
         }
         if (k0 + 16 > K) {                                // nibbles past K are padding
+            const int rem = opaque((int)(K > k0 ? K - k0 : 0));
 #pragma unroll
             for (int i = 0; i < 16; i++)
-                if (k0 + i >= K) v[i] = 0.0f;
+                if (i >= rem) v[i] = 0.0f;
         }
     }
 };
 
 template <int RB>
-__global__ __launch_bounds__(512, CONVROT_PREP_MIN_WAVES) void prep_weight_kernel(NVFP4Loader ld, int64_t n_rows, int nb, int8_t *__restrict__ out,
+__global__ __launch_bounds__(row_prep_max_threads<RB>()) void prep_weight_kernel(NVFP4Loader ld, int64_t n_rows, int nb, int8_t *__restrict__ out,
                                    int64_t ld_out, float *__restrict__ scale, int two_pass)
 {
     ld.gs = *ld.g;
@@ -111,14 +112,18 @@ hipError_t launch_prep_weight(const uint8_t *codes, int64_t ld_codes, const uint
     const int64_t nb = (K + 255) / 256;
     const RowPrepShape s = row_prep_shape(nb, two_pass);
     const size_t lds = row_prep_lds_bytes(s.threads);
-    const dim3 grid((unsigned)row_prep_grid(n_rows, s));
     NVFP4Loader L{codes, ld_codes, sf, ld_sf, g, K, 0.0f};
-    if (s.rb == 2)
+    if (s.rb == 2) {
+        const void *k = reinterpret_cast<const void *>(&prep_weight_kernel<2>);
+        const dim3 grid((unsigned)row_prep_grid(n_rows, s, k, lds));
         hipLaunchKernelGGL(prep_weight_kernel<2>, grid, dim3(s.threads), lds, st,
                            L, n_rows, (int)nb, w_s8, ld_s8, w_scale, 0);
-    else
+    } else {
+        const void *k = reinterpret_cast<const void *>(&prep_weight_kernel<1>);
+        const dim3 grid((unsigned)row_prep_grid(n_rows, s, k, lds));
         hipLaunchKernelGGL(prep_weight_kernel<1>, grid, dim3(s.threads), lds, st,
                            L, n_rows, (int)nb, w_s8, ld_s8, w_scale, s.two_pass ? 1 : 0);
+    }
     return hipGetLastError();
 }
 

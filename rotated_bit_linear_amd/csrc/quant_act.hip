@@ -55,16 +55,17 @@ __device__ __forceinline__ void fetch_seg(const typename Elem<DT>::T *row, int64
 #pragma unroll
     for (int c = 0; c < NW; c++) r.w[c] = u32x4{0u, 0u, 0u, 0u};
     if (k0 >= K) return;
+    const int rem = opaque((int)(K - k0 < 16 ? K - k0 : 16));   // elements below K
     if constexpr (DT == 2) {
         const uint32_t *p = reinterpret_cast<const uint32_t *>(row + k0);
 #pragma unroll
         for (int i = 0; i < 16; i++)
-            if (k0 + i < K) r.w[i >> 2][i & 3] = p[i];
+            if (i < rem) r.w[i >> 2][i & 3] = p[i];
     } else {
         const uint16_t *p = reinterpret_cast<const uint16_t *>(row + k0);
 #pragma unroll
         for (int i = 0; i < 16; i++)
-            if (k0 + i < K) r.w[i >> 3][(i >> 1) & 3] |= (uint32_t)p[i] << (16 * (i & 1));
+            if (i < rem) r.w[i >> 3][(i >> 1) & 3] |= (uint32_t)p[i] << (16 * (i & 1));
     }
 }
 
@@ -98,14 +99,15 @@ __device__ __forceinline__ void decode_seg(const RawSeg<DT> &r, float (&v)[16])
 // The steps are evaluated on x clamped to [-200, 200] with no further selects: inside
 // [-104, 89] nothing changes; for x in (89, 200] the reduction gives k >= 128 with
 // p >= 1.32 (k = 128) or p >= 0.70 (k > 128), so p * 2^k overflows to +inf; for x in
-// [-200, -104) it gives p * 2^k < 2^-150, which rounds to 0.  A NaN argument is clamped
-// to a bound; the callers below only use E(-a) inside a product with a, which is NaN.
+// [-200, -104) it gives p * 2^k < 2^-150, which rounds to 0.  A NaN argument gives NaN
+// or, if the clamp returns a bound, a finite value; the callers below only use E(-a)
+// inside a product with a, which is NaN either way.
 __device__ __forceinline__ float repro_exp_nan_free(float x)
 {
     const float kLog2e = 0x1.715476p+0f;
     const float kC1 = 0x1.62e4p-1f;
     const float kC2 = 0x1.7f7d1cp-20f;
-    const float xc = fminf(fmaxf(x, -200.0f), 200.0f);
+    const float xc = __builtin_amdgcn_fmed3f(x, -200.0f, 200.0f);
     const float kf = rintf(xc * kLog2e);
     float r = fmaf(-kf, kC1, xc);
     r = fmaf(-kf, kC2, r);
@@ -225,7 +227,7 @@ __global__ void swiglu_kernel(const typename Elem<DT>::T *__restrict__ h, int64_
 }
 
 template <class Loader, int RB>
-__global__ __launch_bounds__(512, CONVROT_PREP_MIN_WAVES) void quant_act_kernel(Loader ld, int64_t n_rows, int nb, int8_t *__restrict__ out, int64_t ld_out,
+__global__ __launch_bounds__(row_prep_max_threads<RB>()) void quant_act_kernel(Loader ld, int64_t n_rows, int nb, int8_t *__restrict__ out, int64_t ld_out,
                                  float *__restrict__ scale, int two_pass)
 {
     row_prep_kernel_body<Loader, RB>(ld, n_rows, nb, out, ld_out, scale, two_pass);
@@ -239,13 +241,17 @@ static hipError_t launch_rows(const Loader &L, int64_t rows, int64_t nb, int8_t 
 {
     const RowPrepShape s = row_prep_shape(nb, force_two_pass);
     const size_t lds = row_prep_lds_bytes(s.threads);
-    const dim3 grid((unsigned)row_prep_grid(rows, s));
-    if (s.rb == 2)
+    if (s.rb == 2) {
+        const void *k = reinterpret_cast<const void *>(&quant_act_kernel<Loader, 2>);
+        const dim3 grid((unsigned)row_prep_grid(rows, s, k, lds));
         hipLaunchKernelGGL((quant_act_kernel<Loader, 2>), grid, dim3(s.threads), lds, st,
                            L, rows, (int)nb, out, ld_out, scale, 0);
-    else
+    } else {
+        const void *k = reinterpret_cast<const void *>(&quant_act_kernel<Loader, 1>);
+        const dim3 grid((unsigned)row_prep_grid(rows, s, k, lds));
         hipLaunchKernelGGL((quant_act_kernel<Loader, 1>), grid, dim3(s.threads), lds, st,
                            L, rows, (int)nb, out, ld_out, scale, s.two_pass ? 1 : 0);
+    }
     return hipGetLastError();
 }
 

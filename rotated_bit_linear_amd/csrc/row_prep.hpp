@@ -32,16 +32,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace convrot {
+#include <mutex>
 
-// Minimum waves per SIMD the preparation kernels are compiled for (caps their registers).
-#ifndef CONVROT_PREP_MIN_WAVES
-#define CONVROT_PREP_MIN_WAVES 2
-#endif
+namespace convrot {
 
 constexpr int kLanesPerBlock = 16;          // lanes sharing one 256-column block
 constexpr int kTileStrideF = 272;           // floats per 16x16 transpose tile (256 + 16 pad)
-constexpr int kMaxGroups = 32;              // 512 threads
+constexpr int kMaxGroups1 = 60;             // one block per group: 960 threads, 65,408 B LDS
+constexpr int kMaxGroups2 = 32;             // two blocks per group: 512 threads
 
 // XOR swizzle of 16-byte chunks inside a 16x16 fp32 tile: conflict-free ds_read/ds_write
 // for both row-wise (b128) and column-wise (b32) access with 32 or 64 LDS banks.
@@ -101,6 +99,15 @@ __device__ __forceinline__ void hadamard256(float (&v)[16], float *tile, int t)
         v[4 * c] = q.x; v[4 * c + 1] = q.y; v[4 * c + 2] = q.z; v[4 * c + 3] = q.w;
     }
     wave_lds_sync();
+}
+
+// An opaque copy of a per-lane value.  Work that depends on it stays where it is written
+// (inside a rarely taken branch) instead of being hoisted out of the row loop, where its
+// per-element lane masks would occupy scalar registers for the whole loop.
+__device__ __forceinline__ int opaque(int v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
 }
 
 __device__ __forceinline__ float wave_max(float a)
@@ -331,45 +338,72 @@ __device__ __forceinline__ void row_prep_kernel_body(const Loader &ld, int64_t n
     else row_prep_rows<Loader, RB>(ld, n_rows, nb, out, ld_out, scale_out);
 }
 
-// Launch shape of a row of nb blocks: at most 512 threads (32 groups, 35 KB of LDS).
+// Launch shape of a row of nb blocks.  Up to 60 blocks, one block per 16-lane group
+// (up to 960 threads; the transpose tiles stay within 64 KiB of LDS); up to 64 blocks, two
+// per group (512 threads); beyond that, two passes with up to 60 groups.
 struct RowPrepShape {
     int threads;   // workgroup size, a multiple of 64
     int rb;        // blocks held per 16-lane group in one-pass mode (1 or 2)
     bool two_pass;
 };
 
-// Workgroups of the one-pass row loop: enough resident rows per CU to hide latency,
-// never more workgroups than rows.  Two-pass launches one workgroup per row.
-inline int row_prep_grid(int64_t n_rows, const RowPrepShape &s)
-{
-    if (s.two_pass) return (int)n_rows;
-    static int cus_cache[64] = {0};
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
-        cus = cus_cache[dev];
-        if (cus == 0 && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
-            cus_cache[dev] = cus;
-    }
-    if (cus <= 0) cus = 256;
-    const int64_t want = (int64_t)cus * 8;
-    return (int)(n_rows < want ? n_rows : want);
-}
+// Launch bound of the kernel instantiation that runs RB blocks per group.
+template <int RB>
+constexpr int row_prep_max_threads() { return RB == 1 ? 1024 : 512; }
 
 inline RowPrepShape row_prep_shape(int64_t nb, bool force_two_pass)
 {
     RowPrepShape s{};
-    if (!force_two_pass && nb <= 2 * kMaxGroups) {
-        s.rb = nb <= kMaxGroups ? 1 : 2;
-        const int64_t groups = (nb + s.rb - 1) / s.rb;
-        s.threads = (int)(((groups + 3) / 4) * 64);
-        s.two_pass = false;
+    int64_t groups;
+    if (!force_two_pass && nb <= kMaxGroups1) {
+        s.rb = 1;
+        groups = nb;
+    } else if (!force_two_pass && nb <= 2 * kMaxGroups2) {
+        s.rb = 2;
+        groups = (nb + 1) / 2;
     } else {
-        const int64_t groups = nb < kMaxGroups ? nb : kMaxGroups;
-        s.threads = (int)(((groups + 3) / 4) * 64);
         s.rb = 1;
         s.two_pass = true;
+        groups = nb < kMaxGroups1 ? nb : kMaxGroups1;
     }
+    s.threads = (int)(((groups + 3) / 4) * 64);
     return s;
+}
+
+// Workgroups of the one-pass row loop: as many as the device holds at once (each then
+// works through its rows with the next row always in flight), never more than rows.
+// Two-pass launches one workgroup per row.
+inline int row_prep_grid(int64_t n_rows, const RowPrepShape &s, const void *kernel, size_t lds)
+{
+    if (s.two_pass) return (int)n_rows;
+    struct Entry { int dev; const void *kernel; int threads; size_t lds; int64_t resident; };
+    static std::mutex mu;
+    static Entry cache[64];
+    static int n_cache = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) { (void)hipGetLastError(); dev = -1; }
+    int64_t resident = 0;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (int i = 0; i < n_cache; i++)
+            if (cache[i].dev == dev && cache[i].kernel == kernel && cache[i].threads == s.threads && cache[i].lds == lds)
+                resident = cache[i].resident;
+    }
+    if (resident == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+            (void)hipGetLastError();
+            cus = 256;
+        }
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, s.threads, lds) != hipSuccess || per_cu <= 0) {
+            (void)hipGetLastError();
+            per_cu = 1;
+        }
+        resident = (int64_t)cus * per_cu;
+        std::lock_guard<std::mutex> lock(mu);
+        if (n_cache < 64) cache[n_cache++] = Entry{dev, kernel, s.threads, lds, resident};
+    }
+    return (int)(n_rows < resident ? n_rows : resident);
 }
 
 }  // namespace convrot
