@@ -18,8 +18,9 @@
 //   wait for the own DMA of step k+1, barrier (every wave is past its reads of stage k),
 //   DMA of step k+STAGES into stage k, read fragments (k+1, 0) || MFMAs on (k, KS-1)
 // so LDS latency, the barrier and the DMA issue all overlap queued MFMA work.
-// Workgroups are renumbered so that each XCD (workgroup id mod 8 on this part) works on a
-// contiguous band of tiles, ordered in groups of 8 M-tiles, for L2 reuse of both operands.
+// Tiles are assigned so that all XCDs (workgroup id mod 8 on this part) work on one chip
+// block at a time, each on a compact sub-block: L2 reuse inside an XCD, and one MALL-resident
+// working set for the whole chip.
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
 #include <hip/hip_fp16.h>
@@ -133,18 +134,43 @@ void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__re
     int8_t *const stB[GSTAGES] = {lB0, lB1};
 #endif
 
-    // ---- tile id: XCD-contiguous renumbering, then grouped ordering along M ----
-    const int total = tiles_m * tiles_n;
+    // ---- tile id.  Workgroup pid runs on XCD pid % 8, as its idx-th workgroup there.
+    //      Chip blocks of (8 XA) x XB tiles: all XCDs work on the same block at the same
+    //      time (its operand bands are fetched once from HBM into the MALL and shared),
+    //      each on an XA x XB sub-block (L2 reuse inside the XCD); blocks advance along N
+    //      so consecutive blocks share their A bands.  Tiles outside whole blocks are split
+    //      XCD-contiguously afterwards, in groups of GROUP_M M-tiles. ----
     const int pid = blockIdx.x;
     const int xcd = pid % NUM_XCD, idx = pid / NUM_XCD;
-    const int per = total / NUM_XCD, rem = total % NUM_XCD;
-    const int lid = (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-    const int in_group = GROUP_M * tiles_n;
-    const int group = lid / in_group;
-    const int first_m = group * GROUP_M;
-    const int gsize = min(tiles_m - first_m, GROUP_M);
-    const int tm = first_m + (lid % in_group) % gsize;
-    const int tn = (lid % in_group) / gsize;
+    int xa = 8;                                      // largest power of two <= 8 with 8 xa <= tiles_m
+    while (xa > 1 && NUM_XCD * xa > tiles_m) xa >>= 1;
+    const int xb = 32 / xa;
+    const int nbm = tiles_m / (NUM_XCD * xa), nbn = tiles_n / xb;
+    const int main_per_xcd = nbm * nbn * xa * xb;
+    int tm, tn;
+    if (idx < main_per_xcd) {
+        const int blk = idx / (xa * xb), j = idx % (xa * xb);
+        const int bm = blk / nbn, bn = blk % nbn;
+        tm = bm * (NUM_XCD * xa) + xcd * xa + j % xa;
+        tn = bn * xb + j / xa;
+    } else {
+        const int trem = tiles_m * tiles_n - main_per_xcd * NUM_XCD;
+        const int rq = trem / NUM_XCD, rr = trem % NUM_XCD;
+        int r = ((xcd < rr) ? xcd * (rq + 1) : rr * (rq + 1) + (xcd - rr) * rq) + (idx - main_per_xcd);
+        const int mm = nbm * NUM_XCD * xa, nn = nbn * xb;
+        int h, w, bm0, bn0;
+        if (r < mm * (tiles_n - nn)) {              // right strip beside the blocks
+            h = mm; w = tiles_n - nn; bm0 = 0; bn0 = nn;
+        } else {                                    // bottom strip below them
+            r -= mm * (tiles_n - nn);
+            h = tiles_m - mm; w = tiles_n; bm0 = mm; bn0 = 0;
+        }
+        const int in_group = GROUP_M * w;
+        const int g = r / in_group;
+        const int gsize = min(h - g * GROUP_M, GROUP_M);
+        tm = bm0 + g * GROUP_M + (r % in_group) % gsize;
+        tn = bn0 + (r % in_group) / gsize;
+    }
     const int m0 = tm * GBM, n0 = tn * GBN;
 
     const int tid = threadIdx.x, lane = tid & 63;
