@@ -41,6 +41,7 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b)
 }
 
 struct NVFP4Loader {
+    static constexpr bool kFetchAfterDecode = false;   // little raw data, cheap decode
     const uint8_t *codes;
     int64_t ld_codes;
     const uint8_t *sf;

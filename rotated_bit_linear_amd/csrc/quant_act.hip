@@ -159,6 +159,7 @@ __device__ __forceinline__ float swiglu_elem(float a, float b)
 
 template <int DT>
 struct ActLoader {
+    static constexpr bool kFetchAfterDecode = true;
     const typename Elem<DT>::T *x;
     int64_t ld;
     int64_t K;
@@ -173,6 +174,7 @@ struct ActLoader {
 
 template <int DT>
 struct SwigluLoader {
+    static constexpr bool kFetchAfterDecode = true;
     const typename Elem<DT>::T *h;
     int64_t ld;
     int64_t F;

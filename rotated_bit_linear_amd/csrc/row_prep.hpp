@@ -38,8 +38,8 @@ namespace convrot {
 
 constexpr int kLanesPerBlock = 16;          // lanes sharing one 256-column block
 constexpr int kTileStrideF = 272;           // floats per 16x16 transpose tile (256 + 16 pad)
-constexpr int kMaxGroups1 = 60;             // one block per group: 960 threads, 65,408 B LDS
-constexpr int kMaxGroups2 = 32;             // two blocks per group: 512 threads
+constexpr int kMaxGroups1 = 60;             // two-pass rows: 960 threads
+constexpr int kMaxGroups2 = 32;             // one-pass rows: 512 threads
 
 // XOR swizzle of 16-byte chunks inside a 16x16 fp32 tile: conflict-free ds_read/ds_write
 // for both row-wise (b128) and column-wise (b32) access with 32 or 64 LDS banks.
@@ -196,6 +196,8 @@ __host__ __device__ constexpr size_t row_prep_lds_bytes(int threads)
 }
 
 // Loader concept:
+//   static constexpr bool kFetchAfterDecode;         request the next row after decoding
+//                                                    this one (else before: two buffers)
 //   struct Raw;                                      raw bytes of one 16-element segment
 //   void fetch(int64_t row, int64_t seg, Raw &) const;    issue the loads (nothing past K)
 //   void decode(const Raw &, int64_t seg, float (&)[16]) const;   fp32 elements 16*seg..,
@@ -227,14 +229,13 @@ __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, 
             if (b < nb) ld.fetch(r, (int64_t)b * 16 + t, dst[q]);
         }
     };
-    auto process = [&](const Raw (&cur)[RB], int64_t row, int parity) {
-        float v[RB][16];
+    // rotation, row maximum, codes and scale of one decoded row
+    auto finish = [&](float (&v)[RB][16], int64_t row, int parity) {
         float zmax = 0.0f;
 #pragma unroll
         for (int q = 0; q < RB; q++) {
             const int b = grp + q * G;
             if (b < nb) {
-                ld.decode(cur[q], (int64_t)b * 16 + t, v[q]);
                 hadamard256(v[q], tile, t);
 #pragma unroll
                 for (int i = 0; i < 16; i++) zmax = fmaxf(zmax, fabsf(v[q][i]));
@@ -249,10 +250,39 @@ __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, 
         }
         if (tid == 0) scale_out[row] = rq.scale;
     };
+    auto process = [&](const Raw (&cur)[RB], int64_t row, int parity) {
+        float v[RB][16];
+#pragma unroll
+        for (int q = 0; q < RB; q++) {
+            const int b = grp + q * G;
+            if (b < nb) ld.decode(cur[q], (int64_t)b * 16 + t, v[q]);
+        }
+        finish(v, row, parity);
+    };
 
     int64_t row = blockIdx.x;
-    if constexpr (RB == 1) {
-        // two buffers in turn (the row loop unrolled by two): no register copies
+    if constexpr (Loader::kFetchAfterDecode) {
+        // one buffer: the next row is requested as soon as this row's raw bytes are
+        // decoded (fewer live registers; the rotation, reduction and stores of this row
+        // cover the latency)
+        Raw raw[RB];
+        if (row < n_rows) fetch_row(row, raw);
+        int parity = 0;
+        for (; row < n_rows; row += gridDim.x) {
+            float v[RB][16];
+#pragma unroll
+            for (int q = 0; q < RB; q++) {
+                const int b = grp + q * G;
+                if (b < nb) ld.decode(raw[q], (int64_t)b * 16 + t, v[q]);
+            }
+            const int64_t next = row + gridDim.x;
+            if (next < n_rows) fetch_row(next, raw);
+            finish(v, row, parity);
+            parity ^= 1;
+        }
+    } else if constexpr (RB == 1) {
+        // two buffers in turn (the row loop unrolled by two): the next row is requested
+        // before this row is decoded, with no register copies
         Raw ra[RB], rb[RB];
         if (row < n_rows) fetch_row(row, ra);
         while (row < n_rows) {
@@ -267,7 +297,7 @@ __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, 
             row = next;
         }
     } else {
-        // one buffer copied forward: fewer live registers with two blocks per group
+        // one buffer copied forward
         Raw nxt[RB];
         if (row < n_rows) fetch_row(row, nxt);
         int parity = 0;
@@ -338,9 +368,9 @@ __device__ __forceinline__ void row_prep_kernel_body(const Loader &ld, int64_t n
     else row_prep_rows<Loader, RB>(ld, n_rows, nb, out, ld_out, scale_out);
 }
 
-// Launch shape of a row of nb blocks.  Up to 60 blocks, one block per 16-lane group
-// (up to 960 threads; the transpose tiles stay within 64 KiB of LDS); up to 64 blocks, two
-// per group (512 threads); beyond that, two passes with up to 60 groups.
+// Launch shape of a row of nb blocks.  Up to 32 blocks, one block per 16-lane group; up
+// to 64 blocks, two per group (at most 512 threads either way); beyond that, two passes
+// with up to 60 groups (960 threads).
 struct RowPrepShape {
     int threads;   // workgroup size, a multiple of 64
     int rb;        // blocks held per 16-lane group in one-pass mode (1 or 2)
@@ -355,7 +385,7 @@ inline RowPrepShape row_prep_shape(int64_t nb, bool force_two_pass)
 {
     RowPrepShape s{};
     int64_t groups;
-    if (!force_two_pass && nb <= kMaxGroups1) {
+    if (!force_two_pass && nb <= kMaxGroups2) {
         s.rb = 1;
         groups = nb;
     } else if (!force_two_pass && nb <= 2 * kMaxGroups2) {

@@ -162,8 +162,10 @@ def test_quant_act_swiglu_bit_exact(dt, M, F):
 
 # ---------------------------------------------------------------- weight prep ----
 
+# row shapes: one block per lane group (K <= 8192), two (8192 < K <= 16384: 14336 and a
+# 33-block row with a tail), two-pass (K > 16384), and tiny rows
 W_CASES = [(256, 512, None, None), (300, 1000, 512, 80), (97, 20000, None, None), (64, 5376, None, None),
-           (1, 17, 16, 5)]
+           (1, 17, 16, 5), (40, 14336, None, None), (21, 8200, 4112, 520)]
 
 
 @pytest.mark.parametrize("N,K,ldc,ldsf", W_CASES, ids=[f"N{c[0]}-K{c[1]}" for c in W_CASES])
