@@ -40,7 +40,7 @@ def parse_args():
     ap.add_argument("--max-tile-bytes", type=int, default=0, help="0 = library default")
     ap.add_argument("--serial", action="store_true", help="prepare weights on the main stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=1024)
+    ap.add_argument("--cpu-sample-rows", type=int, default=8192)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this size (counter calibration) and exit")
     ap.add_argument("--json-out", default="")
@@ -296,7 +296,7 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {
-            "workload": "+".join(L.w.note for L in layers),
+            "workload": "; ".join(L.w.note for L in layers),
             "M": layers[0].w.M,
             "layers": names,
             "inputs": "bf16 activations ~N(0,1) (QKV: 1% channels x20), NVFP4 weights from 0.02*N(0,1)",
