@@ -9,7 +9,9 @@ Inputs are seeded synthetic data resident in HBM before timing starts.
 
 Prints one JSON line: ms/layer (mean over the two layers), per-layer and per-kernel
 timings from HIP events recorded on the launching streams, the GEMM roofline (INT8 MFMA
-peak), the preparation kernels' HBM rates, and the CPU oracle timed on a bounded sample.
+peak), each kernel timed alone (preparation rates against the HBM peak and a measured
+device copy), the expanded-S8 control (weights prepared once, outside timing), and the CPU
+oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -37,6 +39,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workloads", default="qkv,ffn_down")
+    ap.add_argument("--next-shapes", default="out_proj,ffn_up",
+                    help="other linear shapes of the block, reported apart from value ('' = none)")
     ap.add_argument("--max-tile-bytes", type=int, default=0, help="0 = library default")
     ap.add_argument("--serial", action="store_true", help="prepare weights on the main stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -135,6 +139,62 @@ def run_layer(L, rbl, s_main, s_aux, ev):
     ev[2].record(s_main)
 
 
+def time_layers(torch, rbl, layers, K, W, s_main, s_aux):
+    """W untimed steps, then K timed steps over `layers`; per-step per-layer events,
+    ms per step (HIP events on the main stream) and the host wall time of the loop."""
+    mk = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+    evs = [[[mk() for _ in range(L.n_events)] for L in layers] for _ in range(K)]
+    scratch = [[mk() for _ in range(L.n_events)] for L in layers]
+    print(f"bench: warmup {W} steps of {[L.name for L in layers]}", file=sys.stderr, flush=True)
+    for _ in range(W):
+        for li, L in enumerate(layers):
+            run_layer(L, rbl, s_main, s_aux, scratch[li])
+    torch.cuda.synchronize()
+    print(f"bench: timing {K} steps", file=sys.stderr, flush=True)
+    start, end = mk(), mk()
+    t0 = time.perf_counter()
+    start.record(s_main)
+    for k in range(K):
+        for li, L in enumerate(layers):
+            run_layer(L, rbl, s_main, s_aux, evs[k][li])
+    end.record(s_main)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1000.0
+    return evs, start.elapsed_time(end) / K, wall_ms
+
+
+def layer_stats(L, ev_steps):
+    """Per-layer figures from the events of each timed step (see run_layer)."""
+    K = len(ev_steps)
+
+    def mean(a, b):
+        return sum(e[a].elapsed_time(e[b]) for e in ev_steps) / K
+    nc = L.nchunks
+    t_layer = mean(0, 2)
+    per_step = sorted(e[0].elapsed_time(e[2]) for e in ev_steps)
+    t_act = mean(0, 1)
+    t_w = sum(mean(3 + 4 * c, 4 + 4 * c) for c in range(nc))
+    g_launch = [mean(5 + 4 * c, 6 + 4 * c) for c in range(nc)]
+    t_g = sum(g_launch)
+    return {
+        "M": L.w.M, "N": L.w.N, "K": L.w.K, "K_pad": L.w.K_pad, "swiglu": L.w.swiglu,
+        "weight_chunks": nc, "rows_per_chunk": L.R,
+        "ms": round(t_layer, 4),
+        "ms_median": round(per_step[K // 2], 4),
+        "ms_min": round(per_step[0], 4),
+        "gemm_ms": round(t_g, 4),
+        "gemm_launch_ms": [round(v, 4) for v in g_launch],
+        "gemm_tops": round(L.gemm_ops / (t_g * 1e-3) / 1e12, 1),
+        "gemm_frac_peak": round(L.gemm_ops / (t_g * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+        "layer_tops": round(L.gemm_ops / (t_layer * 1e-3) / 1e12, 1),
+        "act_prep_ms": round(t_act, 4),
+        "act_prep_gbs": round(L.act_bytes / (t_act * 1e-3) / 1e9, 1),
+        "weight_prep_ms": round(t_w, 4),
+        "weight_prep_gbs": round(L.w_bytes / (t_w * 1e-3) / 1e9, 1),
+        "not_gemm_ms": round(t_layer - t_g, 4),
+    }
+
+
 def cpu_baseline(layers, sample_rows):
     """The CPU oracle, as it stands, on a bounded sample: the whole weight preparation
     (a fixed per-layer cost) plus activation preparation, int32 GEMM and epilogue on the
@@ -173,6 +233,31 @@ def cpu_baseline(layers, sample_rows):
                    f"and epilogue per layer, extrapolated linearly to M=19989; {wall:.1f} s of CPU work"),
         "detail": detail,
     }
+
+
+def time_loop(torch, fn, stream, n=10, warm=2):
+    """Mean ms of fn() over n back-to-back calls, HIP events on `stream`."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(n):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def copy_bandwidth(torch, stream) -> float:
+    """GB/s (bytes read + written) of a plain 1 GiB device-to-device copy."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    ms = time_loop(torch, lambda: dst.copy_(src), stream, n=5)
+    del src, dst
+    return 2 * n / (ms * 1e-3) / 1e9
 
 
 def copy_calibration(mib: int):
@@ -216,53 +301,39 @@ def main():
     s_main = torch.cuda.current_stream()
     s_aux = None if args.serial else torch.cuda.Stream()
     K, W = args.steps, args.warmup
-    mk = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
-    evs = [[[mk() for _ in range(L.n_events)] for L in layers] for _ in range(K)]
-    scratch = [[mk() for _ in range(L.n_events)] for L in layers]
+    evs, ms_per_step, wall_ms = time_layers(torch, rbl, layers, K, W, s_main, s_aux)
+    layer_info = {L.name: layer_stats(L, [evs[k][li] for k in range(K)]) for li, L in enumerate(layers)}
 
-    print(f"bench: warmup {W} steps", file=sys.stderr, flush=True)
-    for _ in range(W):
-        for li, L in enumerate(layers):
-            run_layer(L, rbl, s_main, s_aux, scratch[li])
-    torch.cuda.synchronize()
-
-    print(f"bench: timing {K} steps", file=sys.stderr, flush=True)
-    start, end = mk(), mk()
-    t0 = time.perf_counter()
-    start.record(s_main)
-    for k in range(K):
-        for li, L in enumerate(layers):
-            run_layer(L, rbl, s_main, s_aux, evs[k][li])
-    end.record(s_main)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1000.0
-    ms_per_step = start.elapsed_time(end) / K
-
-    layer_info = {}
-    for li, L in enumerate(layers):
-        def mean(a, b):
-            return sum(evs[k][li][a].elapsed_time(evs[k][li][b]) for k in range(K)) / K
-        nc = L.nchunks
-        t_layer = mean(0, 2)
-        t_act = mean(0, 1)
-        t_w = sum(mean(3 + 4 * c, 4 + 4 * c) for c in range(nc))
-        g_launch = [mean(5 + 4 * c, 6 + 4 * c) for c in range(nc)]
-        t_g = sum(g_launch)
-        layer_info[L.name] = {
-            "M": L.w.M, "N": L.w.N, "K": L.w.K, "K_pad": L.w.K_pad, "swiglu": L.w.swiglu,
-            "weight_chunks": nc, "rows_per_chunk": L.R,
-            "ms": round(t_layer, 4),
-            "gemm_ms": round(t_g, 4),
-            "gemm_launch_ms": [round(v, 4) for v in g_launch],
-            "gemm_tops": round(L.gemm_ops / (t_g * 1e-3) / 1e12, 1),
-            "gemm_frac_peak": round(L.gemm_ops / (t_g * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
-            "layer_tops": round(L.gemm_ops / (t_layer * 1e-3) / 1e12, 1),
-            "act_prep_ms": round(t_act, 4),
-            "act_prep_gbs": round(L.act_bytes / (t_act * 1e-3) / 1e9, 1),
+    # each kernel alone on the main stream, and the "expanded S8" control: the whole weight
+    # prepared once outside timing, then activation prep + one full-N GEMM per layer
+    print("bench: components alone and the expanded-S8 control", file=sys.stderr, flush=True)
+    copy_gbs = copy_bandwidth(torch, s_main)
+    for L in layers:
+        w = L.w
+        w_full = torch.empty(w.N, w.K_pad, dtype=torch.int8, device=dev)
+        ws_full = torch.empty(w.N, dtype=torch.float32, device=dev)
+        act = ((lambda: rbl.cr_quant_act_swiglu(L.x, w.K, L.x_s8, L.x_scale, stream=s_main)) if w.swiglu else
+               (lambda: rbl.cr_quant_act(L.x, w.K, L.x_s8, L.x_scale, stream=s_main)))
+        wprep = lambda: rbl.cr_prep_weight_nvfp4(L.codes, L.sf, L.g, w.K, w_full, ws_full, stream=s_main)  # noqa: E731
+        gemm = lambda: rbl.cr_gemm_s8_rowscale(L.x_s8, L.x_scale, w_full, ws_full, L.out, stream=s_main)  # noqa: E731
+        t_a = time_loop(torch, act, s_main)
+        t_w = time_loop(torch, wprep, s_main)
+        t_g = time_loop(torch, gemm, s_main)
+        t_x = time_loop(torch, lambda: (act(), gemm()), s_main)
+        layer_info[L.name]["alone"] = {
+            "act_prep_ms": round(t_a, 4),
+            "act_prep_gbs": round(L.act_bytes / (t_a * 1e-3) / 1e9, 1),
+            "act_prep_frac_hbm_peak": round(L.act_bytes / (t_a * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "act_prep_frac_copy": round(L.act_bytes / (t_a * 1e-3) / 1e9 / copy_gbs, 4),
             "weight_prep_ms": round(t_w, 4),
             "weight_prep_gbs": round(L.w_bytes / (t_w * 1e-3) / 1e9, 1),
-            "not_gemm_ms": round(t_layer - t_g, 4),
+            "weight_prep_frac_hbm_peak": round(L.w_bytes / (t_w * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "weight_prep_frac_copy": round(L.w_bytes / (t_w * 1e-3) / 1e9 / copy_gbs, 4),
+            "gemm_full_n_ms": round(t_g, 4),
+            "gemm_full_n_frac_peak": round(L.gemm_ops / (t_g * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+            "expanded_s8_control_ms": round(t_x, 4),
         }
+        del w_full, ws_full
 
     # the product entry point computes the same layer (one untimed call per layer)
     for L in layers:
@@ -273,6 +344,23 @@ def main():
         if not torch.equal(ref, got):
             raise SystemExit(f"bench: cr_linear_nvfp4 differs from the component calls on {L.name}")
         del got
+
+    # the block's other linear shapes (same kernels), timed the same way but apart from
+    # `value`; the MLP chain is fc1 followed by the FFN-down layer
+    next_info = None
+    nxt = [n.strip() for n in args.next_shapes.split(",") if n.strip()]
+    if nxt:
+        extra = []
+        for n in nxt:
+            print(f"bench: generating {n} ...", file=sys.stderr, flush=True)
+            extra.append(Layer(n, torch, rbl, synth, dev, args.max_tile_bytes))
+        torch.cuda.synchronize()
+        k2 = max(5, K // 2)
+        evs2, _, _ = time_layers(torch, rbl, extra, k2, W, s_main, s_aux)
+        next_info = {L.name: layer_stats(L, [evs2[k][li] for k in range(k2)]) for li, L in enumerate(extra)}
+        if "ffn_up" in next_info and "ffn_down" in layer_info:
+            next_info["mlp_chain_fc1_swiglu_fc2_ms"] = round(next_info["ffn_up"]["ms"] + layer_info["ffn_down"]["ms"], 4)
+        del extra
 
     dom = layers[0]
     dom_info = layer_info[dom.name]
@@ -314,7 +402,9 @@ def main():
             "traffic": traffic,
         },
         "layers": layer_info,
+        "next_shapes": next_info,
         "wall_ms_timed_region": round(wall_ms, 2),
+        "copy_gbs": round(copy_gbs, 1),
         "gemm_source_sha256_16": gemm_source_hash(),
     }
     if not args.no_cpu_baseline:

@@ -6,8 +6,8 @@ GEMM): it only draws random numbers and packs a synthetic NVFP4 checkpoint, the 
 model's weights would have been quantized before the layer ever sees them.
 
 Workloads (shapes from the modelpad.app MiniMax H3 explainer, parameter table of one
-block: qkv_proj [21504, 5376] and the SwiGLU MLP with fc1 [28672, 5376] / fc2
-[5376, 14336]; M = 19989 tokens and the K > 16384 streaming case from the "Load ConvRot
+block: qkv_proj [21504, 5376], out_proj [5376, 7168] and the SwiGLU MLP with fc1
+[28672, 5376] / fc2 [5376, 14336]; M = 19989 tokens and the K > 16384 streaming case from the "Load ConvRot
 DiT and Load ConvRot CLIP" bullet of the ComfyUI Turing Utils README).  The pages measure
 on real H3 NVFP4 weights with synthetic activations; real weights are not available, so
 W = 0.02 * N(0, 1) encoded to NVFP4 stands in for them.
@@ -70,7 +70,16 @@ WORKLOADS = {
     "longk": Workload("longk", 8192, 5000, 20000, DT_FP16, (DT_FP16, DT_FP32), 4,
                       zero_row_frac=0.02, tiny_row_frac=0.02,
                       note="K=20000 (padded 20224, two-pass), N=5000 tail, fp16 in"),
+    # the block's other linear layers (same kernels at new shapes)
+    "out_proj": Workload("out_proj", 19989, 5376, 7168, DT_BF16, (DT_BF16,), 5,
+                         note="out_proj [5376,7168] at M=19989"),
+    "ffn_up": Workload("ffn_up", 19989, 28672, 5376, DT_BF16, (DT_BF16,), 6,
+                       note="fc1 [28672,5376] at M=19989"),
 }
+
+# The MLP of one block as a chain: fc1 (ffn_up) writes H [M, 28672] in bf16, which the
+# FFN-down layer reads through its fused SwiGLU.
+MLP_CHAIN = ("ffn_up", "ffn_down")
 
 
 def _gen(seed: int) -> torch.Generator:
@@ -234,6 +243,6 @@ def sample_rows(M: int, n: int, seed: int, must: torch.Tensor | None = None) -> 
     return torch.unique(torch.cat(parts)).sort().values
 
 
-__all__ = ["Workload", "WORKLOADS", "make_activation", "make_weight_f32", "make_weight_nvfp4",
+__all__ = ["Workload", "WORKLOADS", "MLP_CHAIN", "make_activation", "make_weight_f32", "make_weight_nvfp4",
            "nvfp4_encode", "NVFP4Weight", "special_rows", "sample_rows", "bits_u16",
            "DT_BF16", "DT_FP16", "DT_FP32", "DT_I32", "TORCH_DTYPE", "DTYPE_NAME", "round_up"]

@@ -1,6 +1,7 @@
 """GPU parity at the five workload sizes (tiny, QKV M=4096, QKV M=19989, FFN-down with
-SwiGLU M=19989, long-K fp16), in the launch configuration the benchmark times
-(cr_linear_nvfp4, default tile bound, weight preparation on a second stream).
+SwiGLU M=19989, long-K fp16) and at the block's other linear shapes (out_proj, fc1), in the
+launch configuration the benchmark times (cr_linear_nvfp4, default tile bound, weight
+preparation on a second stream); and the block's MLP as a chain (fc1 -> SwiGLU -> fc2).
 
 Full checks: every S8 code and row scale of the activation and of the weight, bit-exact.
 Sampled checks: the layer output on a seeded sample of rows that always holds the M tail
@@ -24,7 +25,7 @@ def host_bits(x: torch.Tensor, dt: int) -> np.ndarray:
     return x.contiguous().numpy() if dt == synth.DT_FP32 else synth.bits_u16(x)
 
 
-@pytest.mark.parametrize("name", ["tiny", "qkv_m4096", "qkv", "ffn_down", "longk"])
+@pytest.mark.parametrize("name", ["tiny", "qkv_m4096", "qkv", "ffn_down", "longk", "out_proj", "ffn_up"])
 def test_workload_parity(name):
     w = synth.WORKLOADS[name]
     x = synth.make_activation(w)
@@ -68,3 +69,39 @@ def test_workload_parity(name):
         assert err <= TOL[odt], err
         if len(zero):
             assert (out[zero.to(dev())] == 0).all()
+
+
+def test_mlp_chain_fc1_swiglu_fc2():
+    """fc1 writes H [M, 28672] in bf16 through cr_linear_nvfp4; the FFN-down layer reads it
+    through its fused SwiGLU.  The oracle runs the same chain on a seeded sample of rows
+    (rows are independent): its own fc1 output rows, rounded to bf16, feed its FFN-down."""
+    up, down = (synth.WORKLOADS[n] for n in synth.MLP_CHAIN)
+    assert up.N == 2 * down.K and up.M == down.M
+    x = synth.make_activation(up)
+    pu, pd = synth.make_weight_nvfp4(up), synth.make_weight_nvfp4(down)
+    gu = torch.tensor([pu.g], dtype=torch.float32, device=dev())
+    gd = torch.tensor([pd.g], dtype=torch.float32, device=dev())
+    aux = torch.cuda.Stream()
+    say(f"chain: fc1 cr_linear_nvfp4 M={up.M} N={up.N} K={up.K}")
+    h = rbl.linear_nvfp4(x.to(dev()), pu.codes.to(dev()), pu.sf.to(dev()), gu, up.K,
+                         out_dtype=torch.bfloat16, aux_stream=aux)
+    say(f"chain: FFN-down cr_linear_nvfp4 swiglu M={down.M} N={down.N} F={down.K}")
+    y = rbl.linear_nvfp4(h, pd.codes.to(dev()), pd.sf.to(dev()), gd, down.K,
+                         out_dtype=torch.bfloat16, swiglu=True, aux_stream=aux)
+    torch.cuda.synchronize()
+
+    rows = synth.sample_rows(up.M, SAMPLE_ROWS, up.seed, torch.empty(0, dtype=torch.long))
+    r = rows.numpy()
+    rqwu, rswu = oracle.prep_weight_nvfp4(pu.codes.numpy(), pu.sf.numpy(), pu.g, up.K)
+    qx, sx = oracle.quant_act(synth.bits_u16(x[rows]), up.x_dtype, up.K)
+    h_ref = oracle.epilogue(oracle.gemm_s8(qx, rqwu), sx, rswu, synth.DT_BF16)   # bf16 bits
+    del rqwu
+    h_got = synth.bits_u16(h[rows.to(dev())].cpu())
+    h_same = float(np.mean(h_got == h_ref))
+    rqwd, rswd = oracle.prep_weight_nvfp4(pd.codes.numpy(), pd.sf.numpy(), pd.g, down.K)
+    qh, sh = oracle.quant_act(np.ascontiguousarray(h_ref), synth.DT_BF16, down.K, swiglu=True)
+    y_ref = oracle.epilogue(oracle.gemm_s8(qh, rqwd), sh, rswd, synth.DT_BF16)
+    got = y[rows.to(dev())].cpu()
+    err = rel_l2(out_f64(got, synth.DT_BF16), out_f64(y_ref, synth.DT_BF16))
+    print(f"chain: rows checked={len(r)} fc1 bf16 outputs identical={h_same:.6f} final rel_l2={err:.3e}")
+    assert err <= TOL[synth.DT_BF16], err
