@@ -44,11 +44,16 @@ def lib():
             "or_act_load": (None, [vp, C.c_int, i64, i64, i64, vp, i64]),
             "or_act_load_swiglu": (None, [vp, C.c_int, i64, i64, i64, vp, i64]),
             "or_quant_act": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, i64, vp]),
+            "or_quant_act_ex": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, vp, i64, vp]),
+            "or_act_prescale": (None, [vp, i64, i64, i64, vp]),
             "or_prep_weight_nvfp4": (C.c_int, [vp, i64, vp, i64, f32, i64, i64, vp, i64, vp]),
             "or_gemm_s8": (None, [vp, i64, vp, i64, i64, i64, i64, vp, i64]),
             "or_epilogue": (None, [vp, i64, vp, vp, i64, i64, C.c_int, vp, i64]),
+            "or_epilogue_ex": (None, [vp, i64, vp, vp, vp, i64, i64, C.c_int, vp, i64]),
             "or_linear_nvfp4": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, i64, vp, i64,
                                           f32, i64, vp, C.c_int, i64]),
+            "or_linear_nvfp4_ex": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, vp, i64, vp, i64,
+                                             f32, i64, vp, vp, C.c_int, i64]),
             "or_exp_array": (None, [vp, vp, i64]),
             "or_sigmoid_array": (None, [vp, vp, i64]),
             "or_swiglu_array": (None, [vp, vp, vp, i64]),
@@ -164,14 +169,33 @@ def act_load(x: np.ndarray, dtype: int, K: int, swiglu: bool = False) -> np.ndar
     return out
 
 
-def quant_act(x: np.ndarray, dtype: int, K: int, swiglu: bool = False):
-    """Activation preparation -> (x_s8 [M, K_pad] int8, x_scale [M] fp32)."""
+def _opt_f32(a, n: int):
+    """(array or None, pointer or None) for an optional float32 vector of length n."""
+    if a is None:
+        return None, None
+    a = np.ascontiguousarray(a, np.float32)
+    assert a.shape == (n,)
+    return a, _p(a)
+
+
+def act_prescale(buf: np.ndarray, K: int, c: np.ndarray) -> np.ndarray:
+    """The channel pre-scale step on loaded rows [M, K_pad] (a copy)."""
+    out = np.array(buf, np.float32, order="C")
+    c, cp = _opt_f32(c, K)
+    lib().or_act_prescale(_p(out), out.shape[0], K, out.shape[1], cp)
+    return out
+
+
+def quant_act(x: np.ndarray, dtype: int, K: int, swiglu: bool = False, pre_scale=None):
+    """Activation preparation -> (x_s8 [M, K_pad] int8, x_scale [M] fp32); pre_scale is an
+    optional [K] float32 channel pre-scale applied before the rotation."""
     x = np.ascontiguousarray(x, _elem_dtype(dtype))
     M = x.shape[0]
     kp = padded_k(K)
     q = np.empty((M, kp), np.int8)
     s = np.empty(M, np.float32)
-    rc = lib().or_quant_act(_p(x), dtype, x.shape[1], int(swiglu), M, K, _p(q), kp, _p(s))
+    c, cp = _opt_f32(pre_scale, K)
+    rc = lib().or_quant_act_ex(_p(x), dtype, x.shape[1], int(swiglu), M, K, cp, _p(q), kp, _p(s))
     assert rc == 0
     return q, s
 
@@ -202,21 +226,23 @@ def gemm_s8(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return acc
 
 
-def epilogue(acc: np.ndarray, s_x: np.ndarray, s_w: np.ndarray, out_dtype: int) -> np.ndarray:
-    """Row-scale dequantization; bf16/fp16 come back as uint16 bit patterns."""
+def epilogue(acc: np.ndarray, s_x: np.ndarray, s_w: np.ndarray, out_dtype: int, bias=None) -> np.ndarray:
+    """Row-scale dequantization (+ optional [N] float32 bias); bf16/fp16 come back as uint16
+    bit patterns."""
     acc = np.ascontiguousarray(acc, np.int32)
     s_x = np.ascontiguousarray(s_x, np.float32)
     s_w = np.ascontiguousarray(s_w, np.float32)
     M, N = acc.shape
+    b, bp = _opt_f32(bias, N)
     odt = {DT_BF16: np.uint16, DT_FP16: np.uint16, DT_FP32: np.float32, DT_I32: np.int32}[out_dtype]
     out = np.empty((M, N), odt)
-    lib().or_epilogue(_p(acc), N, _p(s_x), _p(s_w), M, N, out_dtype, _p(out), N)
+    lib().or_epilogue_ex(_p(acc), N, _p(s_x), _p(s_w), bp, M, N, out_dtype, _p(out), N)
     return out
 
 
 def linear_nvfp4(x: np.ndarray, x_dtype: int, K: int, swiglu: bool, codes: np.ndarray,
-                 sf: np.ndarray, g: float, out_dtype: int) -> np.ndarray:
-    """The whole layer on the rows of x."""
+                 sf: np.ndarray, g: float, out_dtype: int, pre_scale=None, bias=None) -> np.ndarray:
+    """The whole layer on the rows of x (optional channel pre-scale [K] and bias [N])."""
     x = np.ascontiguousarray(x, _elem_dtype(x_dtype))
     codes = np.ascontiguousarray(codes, np.uint8)
     sf = np.ascontiguousarray(sf, np.uint8)
@@ -224,7 +250,9 @@ def linear_nvfp4(x: np.ndarray, x_dtype: int, K: int, swiglu: bool, codes: np.nd
     N = codes.shape[0]
     odt = {DT_BF16: np.uint16, DT_FP16: np.uint16, DT_FP32: np.float32, DT_I32: np.int32}[out_dtype]
     out = np.empty((M, N), odt)
-    rc = lib().or_linear_nvfp4(_p(x), x_dtype, x.shape[1], int(swiglu), M, K, _p(codes),
-                               codes.shape[1], _p(sf), sf.shape[1], g, N, _p(out), out_dtype, N)
+    c, cp = _opt_f32(pre_scale, K)
+    b, bp = _opt_f32(bias, N)
+    rc = lib().or_linear_nvfp4_ex(_p(x), x_dtype, x.shape[1], int(swiglu), M, K, cp, _p(codes),
+                                  codes.shape[1], _p(sf), sf.shape[1], g, N, bp, _p(out), out_dtype, N)
     assert rc == 0
     return out

@@ -323,20 +323,40 @@ void or_act_load_swiglu(const void *h, int dtype, int64_t ld_h, int64_t M, int64
         }
 }
 
-/* Activation preparation: load (+SwiGLU), ConvRot256, row quantization.
- * x_s8 [M, K_pad] with stride ld_s8, x_scale [M].  Returns 0, or -1 on allocation failure. */
-int or_quant_act(const void *x, int dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
-                 int8_t *x_s8, int64_t ld_s8, float *x_scale)
+/* Channel pre-scale of the layer input (ComfyUI Turing Utils README, "Load ConvRot DiT
+ * ..." bullet: pre-scales and SwiGLU run before the rotation, and channel pre-scales keep
+ * the unfused order): buf[m, k] = buf[m, k] * c[k] for k < K, one FP32 rounding, applied
+ * to the loaded (or SwiGLU) value.  Padding columns stay 0. */
+void or_act_prescale(float *buf, int64_t M, int64_t K, int64_t ld, const float *c)
+{
+#pragma omp parallel for
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t k = 0; k < K; k++)
+            buf[m * ld + k] = buf[m * ld + k] * c[k];
+}
+
+/* Activation preparation: load (+SwiGLU), optional channel pre-scale (pre_scale [K] or
+ * NULL), ConvRot256, row quantization.  x_s8 [M, K_pad] with stride ld_s8, x_scale [M].
+ * Returns 0, or -1 on allocation failure. */
+int or_quant_act_ex(const void *x, int dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
+                    const float *pre_scale, int8_t *x_s8, int64_t ld_s8, float *x_scale)
 {
     int64_t kp = or_padded_k(K);
     float *buf = (float *)malloc(sizeof(float) * (size_t)(M > 0 ? M : 1) * (size_t)kp);
     if (!buf) return -1;
     if (swiglu) or_act_load_swiglu(x, dtype, ld_x, M, K, buf, kp);
     else or_act_load(x, dtype, ld_x, M, K, buf, kp);
+    if (pre_scale) or_act_prescale(buf, M, K, kp, pre_scale);
     or_convrot256(buf, M, kp, kp);
     or_row_quant(buf, M, kp, kp, x_s8, ld_s8, x_scale);
     free(buf);
     return 0;
+}
+
+int or_quant_act(const void *x, int dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
+                 int8_t *x_s8, int64_t ld_s8, float *x_scale)
+{
+    return or_quant_act_ex(x, dtype, ld_x, swiglu, M, K, NULL, x_s8, ld_s8, x_scale);
 }
 
 /* Weight preparation: NVFP4 decode, ConvRot256, row quantization. */
@@ -373,10 +393,12 @@ void or_gemm_s8(const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb,
 
 /* ------------------------------------------------------------- epilogue ---- */
 
-/* out[m, n] = ((float)acc[m, n] * s_x[m]) * s_w[n], rounded once to out_dtype;
- * OR_DT_I32 copies acc.  Only columns n < N of each row are written. */
-void or_epilogue(const int32_t *acc, int64_t ld_acc, const float *s_x, const float *s_w,
-                 int64_t M, int64_t N, int out_dtype, void *out, int64_t ldc)
+/* out[m, n] = ((float)acc[m, n] * s_x[m]) * s_w[n] (+ bias[n] when bias is not NULL:
+ * the linear layer's y = x W^T + b, MiniMax H3 explainer, "Foundations"; the bias is added
+ * in the epilogue, glossary entry "Epilogue"), each operation rounded in FP32, then one
+ * rounding to out_dtype.  OR_DT_I32 copies acc (no bias).  Only columns n < N are written. */
+void or_epilogue_ex(const int32_t *acc, int64_t ld_acc, const float *s_x, const float *s_w,
+                    const float *bias, int64_t M, int64_t N, int out_dtype, void *out, int64_t ldc)
 {
 #pragma omp parallel for
     for (int64_t m = 0; m < M; m++)
@@ -384,10 +406,17 @@ void or_epilogue(const int32_t *acc, int64_t ld_acc, const float *s_x, const flo
             int32_t a = acc[m * ld_acc + n];
             if (out_dtype == OR_DT_I32) { ((int32_t *)out)[m * ldc + n] = a; continue; }
             float v = ((float)a * s_x[m]) * s_w[n];
+            if (bias) v = v + bias[n];
             if (out_dtype == OR_DT_BF16) ((uint16_t *)out)[m * ldc + n] = or_f32_to_bf16(v);
             else if (out_dtype == OR_DT_FP16) ((uint16_t *)out)[m * ldc + n] = or_f32_to_fp16(v);
             else ((float *)out)[m * ldc + n] = v;
         }
+}
+
+void or_epilogue(const int32_t *acc, int64_t ld_acc, const float *s_x, const float *s_w,
+                 int64_t M, int64_t N, int out_dtype, void *out, int64_t ldc)
+{
+    or_epilogue_ex(acc, ld_acc, s_x, s_w, NULL, M, N, out_dtype, out, ldc);
 }
 
 /* -------------------------------------------------------------- layer ---- */
@@ -395,9 +424,10 @@ void or_epilogue(const int32_t *acc, int64_t ld_acc, const float *s_x, const flo
 /* The whole layer: activation preparation once, weight preparation, GEMM, epilogue.
  * (The pages' chunking over N and two-stream staging change no value, so the oracle
  * prepares the whole weight at once.)  Returns 0, or -1 on allocation failure. */
-int or_linear_nvfp4(const void *x, int x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
-                    const uint8_t *codes, int64_t ld_codes, const uint8_t *sf, int64_t ld_sf,
-                    float g, int64_t N, void *out, int out_dtype, int64_t ldc)
+int or_linear_nvfp4_ex(const void *x, int x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
+                       const float *pre_scale,
+                       const uint8_t *codes, int64_t ld_codes, const uint8_t *sf, int64_t ld_sf,
+                       float g, int64_t N, const float *bias, void *out, int out_dtype, int64_t ldc)
 {
     int64_t kp = or_padded_k(K);
     int8_t *xq = (int8_t *)malloc((size_t)(M > 0 ? M : 1) * (size_t)kp);
@@ -407,14 +437,22 @@ int or_linear_nvfp4(const void *x, int x_dtype, int64_t ld_x, int swiglu, int64_
     int32_t *acc = (int32_t *)malloc(sizeof(int32_t) * (size_t)(M > 0 ? M : 1) * (size_t)(N > 0 ? N : 1));
     int rc = -1;
     if (xq && xs && wq && ws && acc &&
-        or_quant_act(x, x_dtype, ld_x, swiglu, M, K, xq, kp, xs) == 0 &&
+        or_quant_act_ex(x, x_dtype, ld_x, swiglu, M, K, pre_scale, xq, kp, xs) == 0 &&
         or_prep_weight_nvfp4(codes, ld_codes, sf, ld_sf, g, N, K, wq, kp, ws) == 0) {
         or_gemm_s8(xq, kp, wq, kp, M, N, kp, acc, N);
-        or_epilogue(acc, N, xs, ws, M, N, out_dtype, out, ldc);
+        or_epilogue_ex(acc, N, xs, ws, bias, M, N, out_dtype, out, ldc);
         rc = 0;
     }
     free(xq); free(xs); free(wq); free(ws); free(acc);
     return rc;
+}
+
+int or_linear_nvfp4(const void *x, int x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
+                    const uint8_t *codes, int64_t ld_codes, const uint8_t *sf, int64_t ld_sf,
+                    float g, int64_t N, void *out, int out_dtype, int64_t ldc)
+{
+    return or_linear_nvfp4_ex(x, x_dtype, ld_x, swiglu, M, K, NULL, codes, ld_codes, sf, ld_sf,
+                              g, N, NULL, out, out_dtype, ldc);
 }
 
 /* ----------------------------------------------- elementwise array helpers ---- */
