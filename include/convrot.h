@@ -127,6 +127,21 @@ cr_status cr_quant_act_swiglu(const void *h, cr_dtype h_dtype, int64_t ld_h, int
                               uint32_t flags, hipStream_t stream);
 
 /*
+ * Activation preparation with an optional channel pre-scale (ComfyUI Turing Utils README,
+ * "Load ConvRot DiT ..." bullet: pre-scales and SwiGLU run before the rotation, and channel
+ * pre-scales keep the unfused order).  The loaded value of channel k (for swiglu != 0 the
+ * SwiGLU value) is multiplied by pre_scale[k] in FP32, then rotated and quantized as in
+ * cr_quant_act / cr_quant_act_swiglu.
+ *   x, x_dtype, ld_x   X [M, K], or H [M, 2K] when swiglu != 0 (K is then F).
+ *   pre_scale          [K] float, 4-byte aligned, or NULL (then identical to the calls
+ *                      above).  Channels k >= K are padding and stay 0.
+ *   x_s8, ld_s8, x_scale, flags as above.
+ */
+cr_status cr_quant_act_ex(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
+                          const float *pre_scale, int8_t *x_s8, int64_t ld_s8, float *x_scale,
+                          uint32_t flags, hipStream_t stream);
+
+/*
  * Unfused SwiGLU to FP32 (the ComfyUI Turing Utils README compares the fused
  * SwiGLU + rotation + A8 path against an unfused activation): out[m, k] =
  * swish(h[m, k]) * h[m, F + k] with the same element arithmetic as cr_quant_act_swiglu.
@@ -149,6 +164,20 @@ cr_status cr_gemm_s8_rowscale(const int8_t *a_s8, int64_t lda, const float *a_sc
                               void *c, cr_dtype c_dtype, int64_t ldc, hipStream_t stream);
 
 /*
+ * The same GEMM with a bias added in the epilogue (MiniMax H3 explainer, "Foundations":
+ * a linear layer is y = x W^T + b; glossary entry "Epilogue": scaling and bias fused onto
+ * the end of the GEMM):
+ *   out = (((float)acc * a_scale[m]) * b_scale[n]) + bias[n], each operation rounded in
+ *   FP32, then one rounding to c_dtype.
+ *   bias  [N] float, 4-byte aligned, or NULL (then identical to cr_gemm_s8_rowscale).
+ *         Not accepted with CR_I32 (CR_ERR_INVALID_ARG).
+ */
+cr_status cr_gemm_s8_rowscale_bias(const int8_t *a_s8, int64_t lda, const float *a_scale,
+                                   const int8_t *b_s8, int64_t ldb, const float *b_scale,
+                                   const float *bias, int64_t M, int64_t N, int64_t K_pad,
+                                   void *c, cr_dtype c_dtype, int64_t ldc, hipStream_t stream);
+
+/*
  * The whole layer with bounded call-local staging (ComfyUI Turing Utils README, same
  * bullet: weights stay packed, S8 weight tiles of bounded size are prepared per chunk of
  * output columns, optionally on a second stream with producer/consumer events; serial and
@@ -158,7 +187,8 @@ cr_status cr_gemm_s8_rowscale(const int8_t *a_s8, int64_t lda, const float *a_sc
  *   w_fp4, ld_fp4, w_sf, ld_sf, global_scale   the NVFP4 weight [N, K] as above.
  *   out [M, ldc] of out_dtype (not CR_I32).
  *   workspace  device buffer of at least cr_linear_nvfp4_workspace_bytes(...) bytes,
- *              16-byte aligned; holds the S8 activation, its scales and two S8 weight tiles.
+ *              256-byte aligned; holds the S8 activation, its scales and the S8 weight
+ *              tiles (two when the weight is chunked).
  *   max_tile_bytes  bound of one S8 weight tile (0 selects CR_DEFAULT_MAX_TILE_BYTES);
  *              tiles hold a multiple of 256 rows (at least 256).
  *   s_main     stream of the activation preparation and the GEMMs.
@@ -183,6 +213,17 @@ cr_status cr_linear_nvfp4(const void *x, cr_dtype x_dtype, int64_t ld_x, int swi
                           int64_t N, void *out, cr_dtype out_dtype, int64_t ldc,
                           void *workspace, size_t ws_bytes, size_t max_tile_bytes,
                           uint32_t flags, hipStream_t s_main, hipStream_t s_aux);
+
+/* The layer with an optional channel pre-scale of its input (pre_scale [K] or NULL, as in
+ * cr_quant_act_ex) and an optional bias (bias [N] or NULL, as in cr_gemm_s8_rowscale_bias);
+ * the other arguments as in cr_linear_nvfp4, which is this call with both NULL. */
+cr_status cr_linear_nvfp4_ex(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu,
+                             int64_t M, int64_t K, const float *pre_scale,
+                             const uint8_t *w_fp4, int64_t ld_fp4,
+                             const uint8_t *w_sf, int64_t ld_sf, const float *global_scale,
+                             int64_t N, const float *bias, void *out, cr_dtype out_dtype, int64_t ldc,
+                             void *workspace, size_t ws_bytes, size_t max_tile_bytes,
+                             uint32_t flags, hipStream_t s_main, hipStream_t s_aux);
 
 #ifdef __cplusplus
 }

@@ -61,10 +61,15 @@ def lib() -> C.CDLL:
             "cr_quant_act_swiglu": (C.c_int, [vp, C.c_int, i64, i64, i64, vp, i64, vp, u32, vp]),
             "cr_swiglu": (C.c_int, [vp, C.c_int, i64, i64, i64, vp, i64, vp]),
             "cr_gemm_s8_rowscale": (C.c_int, [vp, i64, vp, vp, i64, vp, i64, i64, i64, vp, C.c_int, i64, vp]),
+            "cr_gemm_s8_rowscale_bias": (C.c_int, [vp, i64, vp, vp, i64, vp, vp, i64, i64, i64, vp, C.c_int, i64,
+                                                   vp]),
+            "cr_quant_act_ex": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, vp, i64, vp, u32, vp]),
             "cr_linear_nvfp4_workspace_bytes": (sz, [i64, i64, i64, sz]),
             "cr_linear_nvfp4_plan": (C.c_int, [i64, i64, i64, sz, C.POINTER(i64), C.POINTER(i64)]),
             "cr_linear_nvfp4": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, i64, vp, i64, vp, i64,
                                           vp, C.c_int, i64, vp, sz, sz, u32, vp, vp]),
+            "cr_linear_nvfp4_ex": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, vp, i64, vp, i64, vp,
+                                             i64, vp, vp, C.c_int, i64, vp, sz, sz, u32, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -141,6 +146,14 @@ def cr_quant_act_swiglu(h, F, x_s8, x_scale, flags=0, stream=None):
         _stream(stream)))
 
 
+def cr_quant_act_ex(x, K, swiglu, pre_scale, x_s8, x_scale, flags=0, stream=None):
+    M, ld_x = _rows_ld(x)
+    _, ld_s8 = _rows_ld(x_s8)
+    _check("cr_quant_act_ex", lib().cr_quant_act_ex(
+        _ptr(x), _TORCH_TO_CR[x.dtype], ld_x, int(bool(swiglu)), M, K, _ptr(pre_scale), _ptr(x_s8), ld_s8,
+        _ptr(x_scale), flags, _stream(stream)))
+
+
 def cr_swiglu(h, F, out, stream=None):
     M, ld_h = _rows_ld(h)
     _, ld_out = _rows_ld(out)
@@ -164,6 +177,15 @@ def cr_linear_nvfp4_workspace_bytes(M, N, K, max_tile_bytes=0) -> int:
     return int(lib().cr_linear_nvfp4_workspace_bytes(M, N, K, max_tile_bytes))
 
 
+def cr_gemm_s8_rowscale_bias(a_s8, a_scale, b_s8, b_scale, bias, c, stream=None):
+    M, lda = _rows_ld(a_s8)
+    N, ldb = _rows_ld(b_s8)
+    _, ldc = _rows_ld(c)
+    _check("cr_gemm_s8_rowscale_bias", lib().cr_gemm_s8_rowscale_bias(
+        _ptr(a_s8), lda, _ptr(a_scale), _ptr(b_s8), ldb, _ptr(b_scale), _ptr(bias), M, N, a_s8.shape[1],
+        _ptr(c), _TORCH_TO_CR[c.dtype], ldc, _stream(stream)))
+
+
 def cr_linear_nvfp4_plan(M, N, K, max_tile_bytes=0) -> tuple[int, int]:
     """(rows per weight chunk, number of chunks) that cr_linear_nvfp4 uses on this device."""
     r, n = C.c_int64(0), C.c_int64(0)
@@ -173,29 +195,40 @@ def cr_linear_nvfp4_plan(M, N, K, max_tile_bytes=0) -> tuple[int, int]:
 
 
 def cr_linear_nvfp4(x, K, swiglu, w_fp4, w_sf, global_scale, out, workspace, max_tile_bytes=0,
-                    flags=0, stream=None, aux_stream=None):
+                    flags=0, stream=None, aux_stream=None, pre_scale=None, bias=None):
+    """cr_linear_nvfp4, or cr_linear_nvfp4_ex when a pre-scale or a bias is given."""
     M, ld_x = _rows_ld(x)
     N, ld_fp4 = _rows_ld(w_fp4)
     _, ld_sf = _rows_ld(w_sf)
     _, ldc = _rows_ld(out)
     aux = None if aux_stream is None else _stream(aux_stream)
-    _check("cr_linear_nvfp4", lib().cr_linear_nvfp4(
-        _ptr(x), _TORCH_TO_CR[x.dtype], ld_x, int(bool(swiglu)), M, K, _ptr(w_fp4), ld_fp4,
-        _ptr(w_sf), ld_sf, _ptr(global_scale), N, _ptr(out), _TORCH_TO_CR[out.dtype], ldc,
-        _ptr(workspace), workspace.numel() * workspace.element_size(), max_tile_bytes, flags,
-        _stream(stream), aux))
+    ws = (_ptr(workspace), workspace.numel() * workspace.element_size(), max_tile_bytes, flags,
+          _stream(stream), aux)
+    if pre_scale is None and bias is None:
+        _check("cr_linear_nvfp4", lib().cr_linear_nvfp4(
+            _ptr(x), _TORCH_TO_CR[x.dtype], ld_x, int(bool(swiglu)), M, K, _ptr(w_fp4), ld_fp4,
+            _ptr(w_sf), ld_sf, _ptr(global_scale), N, _ptr(out), _TORCH_TO_CR[out.dtype], ldc, *ws))
+    else:
+        _check("cr_linear_nvfp4_ex", lib().cr_linear_nvfp4_ex(
+            _ptr(x), _TORCH_TO_CR[x.dtype], ld_x, int(bool(swiglu)), M, K, _ptr(pre_scale), _ptr(w_fp4), ld_fp4,
+            _ptr(w_sf), ld_sf, _ptr(global_scale), N, _ptr(bias), _ptr(out), _TORCH_TO_CR[out.dtype], ldc, *ws))
 
 
 # ---------------------------------------------------------------- conveniences ----
 
-def quant_act(x: torch.Tensor, K: int | None = None, swiglu: bool = False, flags: int = 0):
-    """(x_s8 [M, K_pad] int8, x_scale [M] fp32) of X [M, K] or of SwiGLU(H [M, 2K])."""
+def quant_act(x: torch.Tensor, K: int | None = None, swiglu: bool = False, flags: int = 0,
+              pre_scale: torch.Tensor | None = None):
+    """(x_s8 [M, K_pad] int8, x_scale [M] fp32) of X [M, K] or of SwiGLU(H [M, 2K]), with an
+    optional [K] channel pre-scale."""
     if K is None:
         K = x.shape[1] // 2 if swiglu else x.shape[1]
     kp = padded_k(K)
     q = torch.empty(x.shape[0], kp, dtype=torch.int8, device=x.device)
     s = torch.empty(x.shape[0], dtype=torch.float32, device=x.device)
-    (cr_quant_act_swiglu if swiglu else cr_quant_act)(x, K, q, s, flags)
+    if pre_scale is not None:
+        cr_quant_act_ex(x, K, swiglu, pre_scale, q, s, flags)
+    else:
+        (cr_quant_act_swiglu if swiglu else cr_quant_act)(x, K, q, s, flags)
     return q, s
 
 
@@ -208,15 +241,19 @@ def prep_weight_nvfp4(w_fp4: torch.Tensor, w_sf: torch.Tensor, global_scale: tor
     return q, s
 
 
-def gemm_s8_rowscale(a_s8, a_scale, b_s8, b_scale, out_dtype=torch.bfloat16):
+def gemm_s8_rowscale(a_s8, a_scale, b_s8, b_scale, out_dtype=torch.bfloat16, bias=None):
     c = torch.empty(a_s8.shape[0], b_s8.shape[0], dtype=out_dtype, device=a_s8.device)
-    cr_gemm_s8_rowscale(a_s8, a_scale, b_s8, b_scale, c)
+    if bias is not None:
+        cr_gemm_s8_rowscale_bias(a_s8, a_scale, b_s8, b_scale, bias, c)
+    else:
+        cr_gemm_s8_rowscale(a_s8, a_scale, b_s8, b_scale, c)
     return c
 
 
 def linear_nvfp4(x, w_fp4, w_sf, global_scale, K, out_dtype=torch.bfloat16, swiglu=False, out=None,
-                 max_tile_bytes=0, flags=0, aux_stream=None, workspace=None):
-    """y = x W^T through the rotated S8 route (SwiGLU(x) W^T when swiglu)."""
+                 max_tile_bytes=0, flags=0, aux_stream=None, workspace=None, pre_scale=None, bias=None):
+    """y = x W^T (+ b) through the rotated S8 route (SwiGLU(x) W^T when swiglu); pre_scale
+    multiplies the input channels before the rotation."""
     M, N = x.shape[0], w_fp4.shape[0]
     if out is None:
         out = torch.empty(M, N, dtype=out_dtype, device=x.device)
@@ -224,5 +261,5 @@ def linear_nvfp4(x, w_fp4, w_sf, global_scale, K, out_dtype=torch.bfloat16, swig
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     cr_linear_nvfp4(x, K, swiglu, w_fp4, w_sf, global_scale, out, workspace, max_tile_bytes, flags,
-                    aux_stream=aux_stream)
+                    aux_stream=aux_stream, pre_scale=pre_scale, bias=bias)
     return out

@@ -222,25 +222,31 @@ cr_status cr_prep_weight_nvfp4(const uint8_t *w_fp4, int64_t ld_fp4, const uint8
                                                 ld_s8, w_scale, (flags & CR_FLAG_FORCE_TWO_PASS) != 0, stream));
 }
 
+cr_status cr_quant_act_ex(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
+                          const float *pre_scale, int8_t *x_s8, int64_t ld_s8, float *x_scale,
+                          uint32_t flags, hipStream_t stream)
+{
+    if (swiglu && K > (int64_t)1 << 40) return CR_ERR_TOO_LARGE;
+    cr_status s = check_act(x, x_dtype, ld_x, M, K, swiglu ? 2 * K : K, x_s8, ld_s8, x_scale, flags);
+    if (s != CR_OK) return s;
+    if (pre_scale && !aligned(pre_scale, 4)) return CR_ERR_MISALIGNED;
+    if ((s = current_device_ok()) != CR_OK) return s;
+    const bool tp = (flags & CR_FLAG_FORCE_TWO_PASS) != 0;
+    return from_hip(swiglu
+        ? convrot::launch_quant_act_swiglu(x, (int)x_dtype, ld_x, M, K, pre_scale, x_s8, ld_s8, x_scale, tp, stream)
+        : convrot::launch_quant_act(x, (int)x_dtype, ld_x, M, K, pre_scale, x_s8, ld_s8, x_scale, tp, stream));
+}
+
 cr_status cr_quant_act(const void *x, cr_dtype x_dtype, int64_t ld_x, int64_t M, int64_t K,
                        int8_t *x_s8, int64_t ld_s8, float *x_scale, uint32_t flags, hipStream_t stream)
 {
-    cr_status s = check_act(x, x_dtype, ld_x, M, K, K, x_s8, ld_s8, x_scale, flags);
-    if (s != CR_OK) return s;
-    if ((s = current_device_ok()) != CR_OK) return s;
-    return from_hip(convrot::launch_quant_act(x, (int)x_dtype, ld_x, M, K, x_s8, ld_s8, x_scale,
-                                              (flags & CR_FLAG_FORCE_TWO_PASS) != 0, stream));
+    return cr_quant_act_ex(x, x_dtype, ld_x, 0, M, K, nullptr, x_s8, ld_s8, x_scale, flags, stream);
 }
 
 cr_status cr_quant_act_swiglu(const void *h, cr_dtype h_dtype, int64_t ld_h, int64_t M, int64_t F,
                               int8_t *x_s8, int64_t ld_s8, float *x_scale, uint32_t flags, hipStream_t stream)
 {
-    if (F > (int64_t)1 << 40) return CR_ERR_TOO_LARGE;
-    cr_status s = check_act(h, h_dtype, ld_h, M, F, 2 * F, x_s8, ld_s8, x_scale, flags);
-    if (s != CR_OK) return s;
-    if ((s = current_device_ok()) != CR_OK) return s;
-    return from_hip(convrot::launch_quant_act_swiglu(h, (int)h_dtype, ld_h, M, F, x_s8, ld_s8, x_scale,
-                                                     (flags & CR_FLAG_FORCE_TWO_PASS) != 0, stream));
+    return cr_quant_act_ex(h, h_dtype, ld_h, 1, M, F, nullptr, x_s8, ld_s8, x_scale, flags, stream);
 }
 
 cr_status cr_swiglu(const void *h, cr_dtype h_dtype, int64_t ld_h, int64_t M, int64_t F,
@@ -256,16 +262,27 @@ cr_status cr_swiglu(const void *h, cr_dtype h_dtype, int64_t ld_h, int64_t M, in
     return from_hip(convrot::launch_swiglu(h, (int)h_dtype, ld_h, M, F, out, ld_out, stream));
 }
 
+cr_status cr_gemm_s8_rowscale_bias(const int8_t *a_s8, int64_t lda, const float *a_scale,
+                                   const int8_t *b_s8, int64_t ldb, const float *b_scale,
+                                   const float *bias, int64_t M, int64_t N, int64_t K_pad,
+                                   void *c, cr_dtype c_dtype, int64_t ldc, hipStream_t stream)
+{
+    cr_status s = check_gemm(a_s8, lda, a_scale, b_s8, ldb, b_scale, M, N, K_pad, c, c_dtype, ldc);
+    if (s != CR_OK) return s;
+    if (bias && c_dtype == CR_I32) return CR_ERR_INVALID_ARG;
+    if (bias && !aligned(bias, 4)) return CR_ERR_MISALIGNED;
+    if ((s = current_device_ok()) != CR_OK) return s;
+    return from_hip(convrot::launch_gemm_s8(a_s8, lda, a_scale, b_s8, ldb, b_scale, bias, M, N, K_pad, c,
+                                            (int)c_dtype, ldc, stream));
+}
+
 cr_status cr_gemm_s8_rowscale(const int8_t *a_s8, int64_t lda, const float *a_scale,
                               const int8_t *b_s8, int64_t ldb, const float *b_scale,
                               int64_t M, int64_t N, int64_t K_pad,
                               void *c, cr_dtype c_dtype, int64_t ldc, hipStream_t stream)
 {
-    cr_status s = check_gemm(a_s8, lda, a_scale, b_s8, ldb, b_scale, M, N, K_pad, c, c_dtype, ldc);
-    if (s != CR_OK) return s;
-    if ((s = current_device_ok()) != CR_OK) return s;
-    return from_hip(convrot::launch_gemm_s8(a_s8, lda, a_scale, b_s8, ldb, b_scale, M, N, K_pad, c,
-                                            (int)c_dtype, ldc, stream));
+    return cr_gemm_s8_rowscale_bias(a_s8, lda, a_scale, b_s8, ldb, b_scale, nullptr, M, N, K_pad, c,
+                                    c_dtype, ldc, stream);
 }
 
 cr_status cr_linear_nvfp4_plan(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes,
@@ -286,13 +303,13 @@ size_t cr_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t m
     return plan_layer(M, N, K, max_tile_bytes).bytes;
 }
 
-cr_status cr_linear_nvfp4(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu,
-                          int64_t M, int64_t K,
-                          const uint8_t *w_fp4, int64_t ld_fp4,
-                          const uint8_t *w_sf, int64_t ld_sf, const float *global_scale,
-                          int64_t N, void *out, cr_dtype out_dtype, int64_t ldc,
-                          void *workspace, size_t ws_bytes, size_t max_tile_bytes,
-                          uint32_t flags, hipStream_t s_main, hipStream_t s_aux)
+cr_status cr_linear_nvfp4_ex(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu,
+                             int64_t M, int64_t K, const float *pre_scale,
+                             const uint8_t *w_fp4, int64_t ld_fp4,
+                             const uint8_t *w_sf, int64_t ld_sf, const float *global_scale,
+                             int64_t N, const float *bias, void *out, cr_dtype out_dtype, int64_t ldc,
+                             void *workspace, size_t ws_bytes, size_t max_tile_bytes,
+                             uint32_t flags, hipStream_t s_main, hipStream_t s_aux)
 {
     if (!workspace || !out) return CR_ERR_INVALID_ARG;
     if (out_dtype == CR_I32) return CR_ERR_UNSUPPORTED_DTYPE;
@@ -317,6 +334,7 @@ cr_status cr_linear_nvfp4(const void *x, cr_dtype x_dtype, int64_t ld_x, int swi
     s = check_gemm(x_s8, p.K_pad, x_scale, tile[0], p.K_pad, tscale[0], M, p.R < N ? p.R : N, p.K_pad,
                    out, out_dtype, ldc);
     if (s != CR_OK) return s;
+    if ((pre_scale && !aligned(pre_scale, 4)) || (bias && !aligned(bias, 4))) return CR_ERR_MISALIGNED;
     if ((s = current_device_ok()) != CR_OK) return s;
 
     const bool tp = (flags & CR_FLAG_FORCE_TWO_PASS) != 0;
@@ -333,8 +351,8 @@ cr_status cr_linear_nvfp4(const void *x, cr_dtype x_dtype, int64_t ld_x, int swi
         if (hipStreamWaitEvent(s_aux, ev_start, 0) != hipSuccess) return CR_ERR_LAUNCH;
     }
     hipError_t e = swiglu
-        ? convrot::launch_quant_act_swiglu(x, (int)x_dtype, ld_x, M, K, x_s8, p.K_pad, x_scale, tp, s_main)
-        : convrot::launch_quant_act(x, (int)x_dtype, ld_x, M, K, x_s8, p.K_pad, x_scale, tp, s_main);
+        ? convrot::launch_quant_act_swiglu(x, (int)x_dtype, ld_x, M, K, pre_scale, x_s8, p.K_pad, x_scale, tp, s_main)
+        : convrot::launch_quant_act(x, (int)x_dtype, ld_x, M, K, pre_scale, x_s8, p.K_pad, x_scale, tp, s_main);
     if (e != hipSuccess) return CR_ERR_LAUNCH;
 
     for (int64_t c = 0; c < p.nchunks; c++) {
@@ -350,12 +368,26 @@ cr_status cr_linear_nvfp4(const void *x, cr_dtype x_dtype, int64_t ld_x, int swi
             if (hipEventRecord(ev_prep[b], s_aux) != hipSuccess) return CR_ERR_LAUNCH;
             if (hipStreamWaitEvent(s_main, ev_prep[b], 0) != hipSuccess) return CR_ERR_LAUNCH;
         }
-        e = convrot::launch_gemm_s8(x_s8, p.K_pad, x_scale, tile[b], p.K_pad, tscale[b], M, rows, p.K_pad,
+        e = convrot::launch_gemm_s8(x_s8, p.K_pad, x_scale, tile[b], p.K_pad, tscale[b],
+                                    bias ? bias + n0 : nullptr, M, rows, p.K_pad,
                                     static_cast<int8_t *>(out) + n0 * es, (int)out_dtype, ldc, s_main);
         if (e != hipSuccess) return CR_ERR_LAUNCH;
         if (overlap && hipEventRecord(ev_gemm[b], s_main) != hipSuccess) return CR_ERR_LAUNCH;
     }
     return CR_OK;
+}
+
+cr_status cr_linear_nvfp4(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu,
+                          int64_t M, int64_t K,
+                          const uint8_t *w_fp4, int64_t ld_fp4,
+                          const uint8_t *w_sf, int64_t ld_sf, const float *global_scale,
+                          int64_t N, void *out, cr_dtype out_dtype, int64_t ldc,
+                          void *workspace, size_t ws_bytes, size_t max_tile_bytes,
+                          uint32_t flags, hipStream_t s_main, hipStream_t s_aux)
+{
+    return cr_linear_nvfp4_ex(x, x_dtype, ld_x, swiglu, M, K, nullptr, w_fp4, ld_fp4, w_sf, ld_sf,
+                              global_scale, N, nullptr, out, out_dtype, ldc, workspace, ws_bytes,
+                              max_tile_bytes, flags, s_main, s_aux);
 }
 
 }  // extern "C"

@@ -111,12 +111,12 @@ __device__ __forceinline__ int gswz(int row)
     else return (row ^ (row >> 3)) & 7;
 }
 
-template <int OUT>
+template <int OUT, bool BIAS>
 __global__ __launch_bounds__(GTHREADS, 1)
 void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__restrict__ sa,
                     const int8_t *__restrict__ B, int64_t ldb, const float *__restrict__ sb,
-                    int M, int N, int K_pad, void *__restrict__ C, int64_t ldc,
-                    int tiles_m, int tiles_n)
+                    const float *__restrict__ bias, int M, int N, int K_pad, void *__restrict__ C,
+                    int64_t ldc, int tiles_m, int tiles_n)
 {
     __shared__ __attribute__((aligned(1024))) int8_t lA0[STAGE_A];
     __shared__ __attribute__((aligned(1024))) int8_t lA1[STAGE_A];
@@ -374,6 +374,19 @@ void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__re
     const int nbase = n0 + wn * WT_N;
     float sav[FM];
     float4 sbv[FN][4];
+    float4 bbv[BIAS ? FN : 1][4];                  // bias of the same columns (BIAS only)
+    auto load4 = [&](const float *v, bool v16, int n) {
+        float4 r;
+        if (v16 && n + 4 <= N) {
+            r = *reinterpret_cast<const float4 *>(v + n);
+        } else {
+            r.x = (n < N) ? v[n] : 0.0f;
+            r.y = (n + 1 < N) ? v[n + 1] : 0.0f;
+            r.z = (n + 2 < N) ? v[n + 2] : 0.0f;
+            r.w = (n + 3 < N) ? v[n + 3] : 0.0f;
+        }
+        return r;
+    };
     if constexpr (OUT != 3) {
 #pragma unroll
         for (int i = 0; i < FM; i++) {
@@ -381,19 +394,14 @@ void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__re
             sav[i] = (m < M) ? sa[m] : 0.0f;
         }
         const bool sb16 = ((uintptr_t)sb % 16) == 0;
+        const bool bi16 = ((uintptr_t)bias % 16) == 0;
 #pragma unroll
         for (int j = 0; j < FN; j++)
 #pragma unroll
             for (int g = 0; g < 4; g++) {
                 const int n = nbase + j * 32 + 8 * g + 4 * fhalf;
-                if (sb16 && n + 4 <= N) {
-                    sbv[j][g] = *reinterpret_cast<const float4 *>(sb + n);
-                } else {
-                    sbv[j][g].x = (n < N) ? sb[n] : 0.0f;
-                    sbv[j][g].y = (n + 1 < N) ? sb[n + 1] : 0.0f;
-                    sbv[j][g].z = (n + 2 < N) ? sb[n + 2] : 0.0f;
-                    sbv[j][g].w = (n + 3 < N) ? sb[n + 3] : 0.0f;
-                }
+                sbv[j][g] = load4(sb, sb16, n);
+                if constexpr (BIAS) bbv[j][g] = load4(bias, bi16, n);
             }
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
@@ -440,8 +448,12 @@ void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__re
                         *reinterpret_cast<v4i *>(dst) = v4i{a0, a1, a2, a3};
                     } else {
                         const float4 s4 = sbv[j][g];
-                        const float v0 = ((float)a0 * sav[i]) * s4.x, v1 = ((float)a1 * sav[i]) * s4.y;
-                        const float v2 = ((float)a2 * sav[i]) * s4.z, v3 = ((float)a3 * sav[i]) * s4.w;
+                        float v0 = ((float)a0 * sav[i]) * s4.x, v1 = ((float)a1 * sav[i]) * s4.y;
+                        float v2 = ((float)a2 * sav[i]) * s4.z, v3 = ((float)a3 * sav[i]) * s4.w;
+                        if constexpr (BIAS) {
+                            const float4 b4 = bbv[j][g];
+                            v0 = v0 + b4.x; v1 = v1 + b4.y; v2 = v2 + b4.z; v3 = v3 + b4.w;
+                        }
                         if constexpr (OUT == 2) {
                             *reinterpret_cast<float4 *>(dst) = make_float4(v0, v1, v2, v3);
                         } else if constexpr (OUT == 0) {
@@ -489,18 +501,31 @@ void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__re
     }
 }
 
+template <int OUT, bool BIAS>
+static void launch_one(const dim3 &grid, const dim3 &block, hipStream_t st, const int8_t *A, int64_t lda,
+                       const float *sa, const int8_t *B, int64_t ldb, const float *sb, const float *bias,
+                       int64_t M, int64_t N, int64_t K_pad, void *C, int64_t ldc, int tiles_m, int tiles_n)
+{
+    hipLaunchKernelGGL((gemm_s8_kernel<OUT, BIAS>), grid, block, 0, st, A, lda, sa, B, ldb, sb, bias,
+                       (int)M, (int)N, (int)K_pad, C, ldc, tiles_m, tiles_n);
+}
+
 hipError_t launch_gemm_s8(const int8_t *A, int64_t lda, const float *sa, const int8_t *B, int64_t ldb,
-                          const float *sb, int64_t M, int64_t N, int64_t K_pad, void *C, int out_dtype,
-                          int64_t ldc, hipStream_t st)
+                          const float *sb, const float *bias, int64_t M, int64_t N, int64_t K_pad, void *C,
+                          int out_dtype, int64_t ldc, hipStream_t st)
 {
     const int tiles_m = (int)((M + GBM - 1) / GBM);
     const int tiles_n = (int)((N + GBN - 1) / GBN);
     const dim3 grid((unsigned)(tiles_m * tiles_n)), block(GTHREADS);
+    const bool b = bias != nullptr;
     switch (out_dtype) {
-    case 0: hipLaunchKernelGGL(gemm_s8_kernel<0>, grid, block, 0, st, A, lda, sa, B, ldb, sb, (int)M, (int)N, (int)K_pad, C, ldc, tiles_m, tiles_n); break;
-    case 1: hipLaunchKernelGGL(gemm_s8_kernel<1>, grid, block, 0, st, A, lda, sa, B, ldb, sb, (int)M, (int)N, (int)K_pad, C, ldc, tiles_m, tiles_n); break;
-    case 2: hipLaunchKernelGGL(gemm_s8_kernel<2>, grid, block, 0, st, A, lda, sa, B, ldb, sb, (int)M, (int)N, (int)K_pad, C, ldc, tiles_m, tiles_n); break;
-    case 3: hipLaunchKernelGGL(gemm_s8_kernel<3>, grid, block, 0, st, A, lda, sa, B, ldb, sb, (int)M, (int)N, (int)K_pad, C, ldc, tiles_m, tiles_n); break;
+    case 0: (b ? launch_one<0, true> : launch_one<0, false>)(grid, block, st, A, lda, sa, B, ldb, sb, bias, M, N, K_pad, C, ldc, tiles_m, tiles_n); break;
+    case 1: (b ? launch_one<1, true> : launch_one<1, false>)(grid, block, st, A, lda, sa, B, ldb, sb, bias, M, N, K_pad, C, ldc, tiles_m, tiles_n); break;
+    case 2: (b ? launch_one<2, true> : launch_one<2, false>)(grid, block, st, A, lda, sa, B, ldb, sb, bias, M, N, K_pad, C, ldc, tiles_m, tiles_n); break;
+    case 3:
+        if (b) return hipErrorInvalidValue;   // the raw accumulator takes no bias
+        launch_one<3, false>(grid, block, st, A, lda, sa, B, ldb, sb, bias, M, N, K_pad, C, ldc, tiles_m, tiles_n);
+        break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -53,6 +53,8 @@ struct NVFP4Loader {
     struct Raw {
         uint32_t w0, w1, sc;
     };
+    using Lane = PreScaleLane<false>;   // no per-segment constants
+    __device__ __forceinline__ Lane lane(int64_t) const { return Lane{}; }
     __device__ __forceinline__ void fetch(int64_t row, int64_t seg, Raw &r) const
     {
         const int64_t k0 = seg * 16;
@@ -75,7 +77,7 @@ struct NVFP4Loader {
                 else r.w1 |= byte << (8 * (i - 4));
             }
     }
-    __device__ __forceinline__ void decode(const Raw &r, int64_t seg, float (&v)[16]) const
+    __device__ __forceinline__ void decode(const Raw &r, int64_t seg, const Lane &, float (&v)[16]) const
     {
         const int64_t k0 = seg * 16;
         const float sc = e4m3_to_f32(r.sc);

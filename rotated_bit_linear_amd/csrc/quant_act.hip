@@ -157,22 +157,35 @@ __device__ __forceinline__ float swiglu_elem(float a, float b)
 
 // --------------------------------------------------------------------- loaders ----
 
-template <int DT>
+// Activation loaders.  With kPre, the loaded (or SwiGLU) value of channel k is multiplied
+// by the channel pre-scale c[k] before the rotation (one FP32 rounding), the order of an
+// unfused pre-scale (ComfyUI Turing Utils README, "Load ConvRot DiT ..." bullet).
+template <int DT, bool kPre>
 struct ActLoader {
     static constexpr bool kFetchAfterDecode = true;
     const typename Elem<DT>::T *x;
     int64_t ld;
     int64_t K;
     bool aligned;
+    const float *pre;
     using Raw = RawSeg<DT>;
+    using Lane = PreScaleLane<kPre>;
+    __device__ __forceinline__ Lane lane(int64_t seg) const { return load_prescale<kPre>(pre, seg, K); }
     __device__ __forceinline__ void fetch(int64_t row, int64_t seg, Raw &r) const
     {
         fetch_seg<DT>(x + row * ld, seg * 16, K, aligned, r);
     }
-    __device__ __forceinline__ void decode(const Raw &r, int64_t, float (&v)[16]) const { decode_seg<DT>(r, v); }
+    __device__ __forceinline__ void decode(const Raw &r, int64_t, const Lane &ln, float (&v)[16]) const
+    {
+        decode_seg<DT>(r, v);
+        if constexpr (kPre) {
+#pragma unroll
+            for (int i = 0; i < 16; i++) v[i] = v[i] * ln.c[i];
+        }
+    }
 };
 
-template <int DT>
+template <int DT, bool kPre>
 struct SwigluLoader {
     static constexpr bool kFetchAfterDecode = true;
     const typename Elem<DT>::T *h;
@@ -180,16 +193,19 @@ struct SwigluLoader {
     int64_t F;
     bool aligned_gate;
     bool aligned_value;
+    const float *pre;
     struct Raw {
         RawSeg<DT> gate, value;
     };
+    using Lane = PreScaleLane<kPre>;
+    __device__ __forceinline__ Lane lane(int64_t seg) const { return load_prescale<kPre>(pre, seg, F); }
     __device__ __forceinline__ void fetch(int64_t row, int64_t seg, Raw &r) const
     {
         const typename Elem<DT>::T *p = h + row * ld;
         fetch_seg<DT>(p, seg * 16, F, aligned_gate, r.gate);
         fetch_seg<DT>(p + F, seg * 16, F, aligned_value, r.value);
     }
-    __device__ __forceinline__ void decode(const Raw &r, int64_t, float (&v)[16]) const
+    __device__ __forceinline__ void decode(const Raw &r, int64_t, const Lane &ln, float (&v)[16]) const
     {
         float b[16];
         decode_seg<DT>(r.gate, v);
@@ -208,6 +224,10 @@ struct SwigluLoader {
                 const float d = 1.0f + repro_exp_nan_free(-a);
                 if (!(d < kRecipLimit)) v[i] = swiglu_exact(a, seg_elem<DT>(r.value, i));
             }
+        }
+        if constexpr (kPre) {                           // after SwiGLU, as unfused
+#pragma unroll
+            for (int i = 0; i < 16; i++) v[i] = v[i] * ln.c[i];
         }
     }
 };
@@ -258,33 +278,37 @@ static hipError_t launch_rows(const Loader &L, int64_t rows, int64_t nb, int8_t 
 }
 
 template <int DT>
-static hipError_t launch_act(const void *x, int64_t ld_x, int64_t M, int64_t K, int8_t *x_s8,
-                             int64_t ld_s8, float *x_scale, bool two_pass, hipStream_t st)
+static hipError_t launch_act(const void *x, int64_t ld_x, int64_t M, int64_t K, const float *pre,
+                             int8_t *x_s8, int64_t ld_s8, float *x_scale, bool two_pass, hipStream_t st)
 {
-    ActLoader<DT> L{static_cast<const typename Elem<DT>::T *>(x), ld_x, K,
-                    ((uintptr_t)x % 16 == 0) && ((ld_x * (int64_t)sizeof(typename Elem<DT>::T)) % 16 == 0)};
-    return launch_rows(L, M, (K + 255) / 256, x_s8, ld_s8, x_scale, two_pass, st);
+    const auto *xp = static_cast<const typename Elem<DT>::T *>(x);
+    const bool aligned = ((uintptr_t)x % 16 == 0) && ((ld_x * (int64_t)sizeof(typename Elem<DT>::T)) % 16 == 0);
+    const int64_t nb = (K + 255) / 256;
+    if (pre) return launch_rows(ActLoader<DT, true>{xp, ld_x, K, aligned, pre}, M, nb, x_s8, ld_s8, x_scale, two_pass, st);
+    return launch_rows(ActLoader<DT, false>{xp, ld_x, K, aligned, nullptr}, M, nb, x_s8, ld_s8, x_scale, two_pass, st);
 }
 
 template <int DT>
-static hipError_t launch_swiglu(const void *h, int64_t ld_h, int64_t M, int64_t F, int8_t *x_s8,
-                                int64_t ld_s8, float *x_scale, bool two_pass, hipStream_t st)
+static hipError_t launch_swiglu(const void *h, int64_t ld_h, int64_t M, int64_t F, const float *pre,
+                                int8_t *x_s8, int64_t ld_s8, float *x_scale, bool two_pass, hipStream_t st)
 {
     const int64_t es = (int64_t)sizeof(typename Elem<DT>::T);
     const bool row_ok = ((uintptr_t)h % 16 == 0) && ((ld_h * es) % 16 == 0);
-    SwigluLoader<DT> L{static_cast<const typename Elem<DT>::T *>(h), ld_h, F, row_ok,
-                       row_ok && ((F * es) % 16 == 0)};
-    return launch_rows(L, M, (F + 255) / 256, x_s8, ld_s8, x_scale, two_pass, st);
+    const bool val_ok = row_ok && ((F * es) % 16 == 0);
+    const auto *hp = static_cast<const typename Elem<DT>::T *>(h);
+    const int64_t nb = (F + 255) / 256;
+    if (pre) return launch_rows(SwigluLoader<DT, true>{hp, ld_h, F, row_ok, val_ok, pre}, M, nb, x_s8, ld_s8, x_scale, two_pass, st);
+    return launch_rows(SwigluLoader<DT, false>{hp, ld_h, F, row_ok, val_ok, nullptr}, M, nb, x_s8, ld_s8, x_scale, two_pass, st);
 }
 
-hipError_t launch_quant_act(const void *x, int dtype, int64_t ld_x, int64_t M, int64_t K,
+hipError_t launch_quant_act(const void *x, int dtype, int64_t ld_x, int64_t M, int64_t K, const float *pre,
                             int8_t *x_s8, int64_t ld_s8, float *x_scale, bool two_pass,
                             hipStream_t st)
 {
     switch (dtype) {
-    case 0: return launch_act<0>(x, ld_x, M, K, x_s8, ld_s8, x_scale, two_pass, st);
-    case 1: return launch_act<1>(x, ld_x, M, K, x_s8, ld_s8, x_scale, two_pass, st);
-    case 2: return launch_act<2>(x, ld_x, M, K, x_s8, ld_s8, x_scale, two_pass, st);
+    case 0: return launch_act<0>(x, ld_x, M, K, pre, x_s8, ld_s8, x_scale, two_pass, st);
+    case 1: return launch_act<1>(x, ld_x, M, K, pre, x_s8, ld_s8, x_scale, two_pass, st);
+    case 2: return launch_act<2>(x, ld_x, M, K, pre, x_s8, ld_s8, x_scale, two_pass, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -309,13 +333,13 @@ hipError_t launch_swiglu(const void *h, int dtype, int64_t ld_h, int64_t M, int6
 }
 
 hipError_t launch_quant_act_swiglu(const void *h, int dtype, int64_t ld_h, int64_t M, int64_t F,
-                                   int8_t *x_s8, int64_t ld_s8, float *x_scale, bool two_pass,
-                                   hipStream_t st)
+                                   const float *pre, int8_t *x_s8, int64_t ld_s8, float *x_scale,
+                                   bool two_pass, hipStream_t st)
 {
     switch (dtype) {
-    case 0: return launch_swiglu<0>(h, ld_h, M, F, x_s8, ld_s8, x_scale, two_pass, st);
-    case 1: return launch_swiglu<1>(h, ld_h, M, F, x_s8, ld_s8, x_scale, two_pass, st);
-    case 2: return launch_swiglu<2>(h, ld_h, M, F, x_s8, ld_s8, x_scale, two_pass, st);
+    case 0: return launch_swiglu<0>(h, ld_h, M, F, pre, x_s8, ld_s8, x_scale, two_pass, st);
+    case 1: return launch_swiglu<1>(h, ld_h, M, F, pre, x_s8, ld_s8, x_scale, two_pass, st);
+    case 2: return launch_swiglu<2>(h, ld_h, M, F, pre, x_s8, ld_s8, x_scale, two_pass, st);
     default: return hipErrorInvalidValue;
     }
 }

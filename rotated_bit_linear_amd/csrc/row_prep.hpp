@@ -101,6 +101,23 @@ __device__ __forceinline__ void hadamard256(float (&v)[16], float *tile, int t)
     wave_lds_sync();
 }
 
+// Per-segment channel pre-scales of an activation loader: c[i] multiplies element 16 seg + i
+// (1.0 past K, where the element is 0 anyway); an empty struct when there are none.
+template <bool kPre> struct PreScaleLane { float c[16]; };
+template <> struct PreScaleLane<false> {};
+
+template <bool kPre>
+__device__ __forceinline__ PreScaleLane<kPre> load_prescale(const float *pre, int64_t seg, int64_t K)
+{
+    PreScaleLane<kPre> l;
+    if constexpr (kPre) {
+        const int64_t k0 = seg * 16;
+#pragma unroll
+        for (int i = 0; i < 16; i++) l.c[i] = (k0 + i < K) ? pre[k0 + i] : 1.0f;
+    }
+    return l;
+}
+
 // An opaque copy of a per-lane value.  Work that depends on it stays where it is written
 // (inside a rarely taken branch) instead of being hoisted out of the row loop, where its
 // per-element lane masks would occupy scalar registers for the whole loop.
@@ -199,9 +216,11 @@ __host__ __device__ constexpr size_t row_prep_lds_bytes(int threads)
 //   static constexpr bool kFetchAfterDecode;         request the next row after decoding
 //                                                    this one (else before: two buffers)
 //   struct Raw;                                      raw bytes of one 16-element segment
+//   struct Lane;                                     per-segment constants (same every row)
+//   Lane lane(int64_t seg) const;                    read them (once per workgroup)
 //   void fetch(int64_t row, int64_t seg, Raw &) const;    issue the loads (nothing past K)
-//   void decode(const Raw &, int64_t seg, float (&)[16]) const;   fp32 elements 16*seg..,
-//                                                                 zero for k >= K
+//   void decode(const Raw &, int64_t seg, const Lane &, float (&)[16]) const;
+//                                                    fp32 elements 16*seg.., zero for k >= K
 // Splitting the two lets a workgroup request the next row while it works on this one.
 
 // One pass, several rows per workgroup: the G = blockDim/16 groups hold RB blocks each
@@ -221,6 +240,12 @@ __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, 
     float *tile = lds + grp * kTileStrideF;
     float *red = lds + G * kTileStrideF;
     using Raw = typename Loader::Raw;
+    typename Loader::Lane lanes[RB];
+#pragma unroll
+    for (int q = 0; q < RB; q++) {
+        const int b = grp + q * G;
+        if (b < nb) lanes[q] = ld.lane((int64_t)b * 16 + t);
+    }
 
     auto fetch_row = [&](int64_t r, Raw (&dst)[RB]) {
 #pragma unroll
@@ -255,7 +280,7 @@ __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, 
 #pragma unroll
         for (int q = 0; q < RB; q++) {
             const int b = grp + q * G;
-            if (b < nb) ld.decode(cur[q], (int64_t)b * 16 + t, v[q]);
+            if (b < nb) ld.decode(cur[q], (int64_t)b * 16 + t, lanes[q], v[q]);
         }
         finish(v, row, parity);
     };
@@ -273,7 +298,7 @@ __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, 
 #pragma unroll
             for (int q = 0; q < RB; q++) {
                 const int b = grp + q * G;
-                if (b < nb) ld.decode(raw[q], (int64_t)b * 16 + t, v[q]);
+                if (b < nb) ld.decode(raw[q], (int64_t)b * 16 + t, lanes[q], v[q]);
             }
             const int64_t next = row + gridDim.x;
             if (next < n_rows) fetch_row(next, raw);
@@ -333,7 +358,8 @@ __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row,
         if (b < nb) {
             typename Loader::Raw raw;
             ld.fetch(row, (int64_t)b * 16 + t, raw);
-            ld.decode(raw, (int64_t)b * 16 + t, v);
+            const typename Loader::Lane ln = ld.lane((int64_t)b * 16 + t);
+            ld.decode(raw, (int64_t)b * 16 + t, ln, v);
         } else {
 #pragma unroll
             for (int i = 0; i < 16; i++) v[i] = 0.0f;

@@ -22,7 +22,8 @@ def test_library_exports_header_functions():
     names = rbl.header_functions()
     assert set(names) >= {"cr_prep_weight_nvfp4", "cr_quant_act", "cr_quant_act_swiglu",
                           "cr_gemm_s8_rowscale", "cr_linear_nvfp4", "cr_linear_nvfp4_workspace_bytes",
-                          "cr_linear_nvfp4_plan",
+                          "cr_linear_nvfp4_plan", "cr_quant_act_ex", "cr_gemm_s8_rowscale_bias",
+                          "cr_linear_nvfp4_ex",
                           "cr_abi_version", "cr_status_string", "cr_padded_k"}
     for n in names:
         assert hasattr(L, n), n
@@ -68,6 +69,18 @@ def test_swiglu_validation():
     assert L.cr_quant_act_swiglu(A16, 3, 1024, 4, 512, A16, 512, A16, 0, ST) == DT
 
 
+def qx(x=A16, dt=0, ld_x=512, sw=0, M=4, K=512, pre=A16, q=A16, ld_q=512, s=A16, flags=0):
+    return rbl.lib().cr_quant_act_ex(x, dt, ld_x, sw, M, K, pre, q, ld_q, s, flags, ST)
+
+
+def test_quant_act_ex_validation():
+    assert qx(pre=A16 + 2) == MIS           # pre-scale must be 4-byte aligned
+    assert qx(x=None) == INV
+    assert qx(sw=1) == INV                  # SwiGLU needs ld_x >= 2K
+    assert qx(sw=1, ld_x=1024, ld_q=256) == INV
+    assert qx(dt=3) == DT
+
+
 def pw(codes=A16, ld=256, sf=A16, ld_sf=32, g=A16, n=8, K=512, q=A16, ld_q=512, s=A16, flags=0):
     return rbl.lib().cr_prep_weight_nvfp4(codes, ld, sf, ld_sf, g, n, K, q, ld_q, s, flags, ST)
 
@@ -85,6 +98,16 @@ def test_prep_weight_validation():
 
 def gm(a=A16, lda=512, sa=A16, b=A16, ldb=512, sb=A16, M=8, N=8, K=512, c=A16, dt=0, ldc=8):
     return rbl.lib().cr_gemm_s8_rowscale(a, lda, sa, b, ldb, sb, M, N, K, c, dt, ldc, ST)
+
+
+def test_gemm_bias_validation():
+    L = rbl.lib()
+
+    def gb(bias=A16, dt=0, sa=A16):
+        return L.cr_gemm_s8_rowscale_bias(A16, 512, sa, A16, 512, A16, bias, 8, 8, 512, A16, dt, 8, ST)
+    assert gb(dt=3) == INV                 # no bias on the raw int32 accumulator
+    assert gb(bias=A16 + 2) == MIS
+    assert gb(sa=None) == INV
 
 
 def test_gemm_validation():

@@ -273,3 +273,87 @@ def test_layer_tiny_full():
     assert err <= TOL[synth.DT_BF16], err
     exact = np.mean(u16(out) == ref)
     print(f"tiny: rel_l2={err:.3e} bit-identical fraction={exact:.4f}")
+
+
+# ------------------------------------------------ channel pre-scale and bias ----
+
+PRE_CASES = [
+    # dt, M, K, swiglu, forced two-pass
+    (synth.DT_BF16, 37, 300, False, False),
+    (synth.DT_FP16, 9, 5376, False, False),
+    (synth.DT_FP32, 5, 16385, False, False),        # two-pass by size
+    (synth.DT_BF16, 7, 700, True, False),
+    (synth.DT_BF16, 4, 14336, True, False),         # two blocks per lane group
+    (synth.DT_BF16, 6, 1000, False, True),          # forced two-pass
+]
+
+
+@pytest.mark.parametrize("dt,M,K,swiglu,forced", PRE_CASES,
+                         ids=[f"dt{c[0]}-M{c[1]}-K{c[2]}{'-swiglu' if c[3] else ''}{'-tp' if c[4] else ''}"
+                              for c in PRE_CASES])
+def test_quant_act_prescale_bit_exact(dt, M, K, swiglu, forced):
+    cols = 2 * K if swiglu else K
+    mult = 4 if dt == synth.DT_FP32 else 8           # 16-byte row strides, garbage past the row
+    x = make_x(M, cols, dt, seed=M + K + 99, ld=(cols // mult + 1) * mult, special=True)
+    g = torch.Generator().manual_seed(K)
+    c = (torch.rand(K, generator=g) * 3.75 + 0.25).to(torch.float32)
+    say(f"cr_quant_act_ex dt={dt} M={M} K={K} swiglu={swiglu} pre_scale forced_two_pass={forced}")
+    q, s = rbl.quant_act(x.to(dev()), K, swiglu=swiglu, pre_scale=c.to(dev()),
+                         flags=rbl.CR_FLAG_FORCE_TWO_PASS if forced else 0)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant_act(host_bits(x, dt), dt, K, swiglu=swiglu, pre_scale=c.numpy())
+    assert_bits_equal(q.cpu().numpy(), rq, "x_s8 (pre-scaled)")
+    assert_bits_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32), "x_scale (pre-scaled)")
+
+
+@pytest.mark.parametrize("M,N,Kp", [(300, 700, 768), (257, 1030, 512)])
+def test_gemm_bias(M, N, Kp):
+    g = torch.Generator().manual_seed(M + N)
+    a = torch.randint(-127, 128, (M, Kp), generator=g, dtype=torch.int32).to(torch.int8)
+    b = torch.randint(-127, 128, (N, Kp), generator=g, dtype=torch.int32).to(torch.int8)
+    sa = torch.rand(M, generator=g) * 1e-2
+    sb = torch.rand(N, generator=g) * 1e-3
+    bias = torch.randn(N + 1, generator=g)
+    acc = oracle.gemm_s8(a.numpy(), b.numpy())
+    ad, bd, sad, sbd = a.to(dev()), b.to(dev()), sa.to(dev()), sb.to(dev())
+    biasd = bias.to(dev())
+    for off in (0, 1):                              # 16-byte aligned bias, and 4-byte aligned
+        bv = biasd[off:off + N]
+        for ldc in (N + 9, (N + 7) // 8 * 8 + 8):
+            for odt in (synth.DT_BF16, synth.DT_FP16, synth.DT_FP32):
+                tdt = synth.TORCH_DTYPE[odt]
+                full = torch.full((M, ldc), 7, dtype=tdt, device=dev())
+                c = full[:, :N]
+                say(f"cr_gemm_s8_rowscale_bias M={M} N={N} K_pad={Kp} out={odt} ldc={ldc} bias+{off}")
+                rbl.cr_gemm_s8_rowscale_bias(ad, sad, bd, sbd, bv, c)
+                torch.cuda.synchronize()
+                fc = full.cpu()
+                assert (fc[:, N:] == 7).all(), "columns past N were written"
+                ref = oracle.epilogue(acc, sa.numpy(), sb.numpy(), odt, bias=bias[off:off + N].numpy())
+                got = out_f64(fc[:, :N], odt)
+                err = rel_l2(got, out_f64(ref, odt))
+                assert err <= TOL[odt], err
+
+
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_layer_prescale_bias(swiglu):
+    M, N, K = 300, 1000, 1000
+    w, x, p = _layer_inputs(M, N, K, synth.DT_BF16, swiglu, 21)
+    g = torch.Generator().manual_seed(21)
+    c = (torch.rand(K, generator=g) + 0.5).to(torch.float32)
+    bias = torch.randn(N, generator=g)
+    xd, cd, sd = x.to(dev()), p.codes.to(dev()), p.sf.to(dev())
+    gs = torch.tensor([p.g], dtype=torch.float32, device=dev())
+    aux = torch.cuda.Stream()
+    outs = []
+    for mt, use_aux in [(0, False), (256 * 1024, True)]:
+        say(f"cr_linear_nvfp4_ex M={M} N={N} K={K} swiglu={swiglu} pre_scale bias max_tile={mt} aux={use_aux}")
+        outs.append(rbl.linear_nvfp4(xd, cd, sd, gs, K, out_dtype=torch.float32, swiglu=swiglu, max_tile_bytes=mt,
+                                     aux_stream=aux if use_aux else None, pre_scale=c.to(dev()),
+                                     bias=bias.to(dev())))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    ref = oracle.linear_nvfp4(synth.bits_u16(x), synth.DT_BF16, K, swiglu, p.codes.numpy(), p.sf.numpy(),
+                              p.g, synth.DT_FP32, pre_scale=c.numpy(), bias=bias.numpy())
+    err = rel_l2(out_f64(outs[0], synth.DT_FP32), out_f64(ref, synth.DT_FP32))
+    assert err <= TOL[synth.DT_FP32], err
