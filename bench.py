@@ -39,8 +39,9 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workloads", default="qkv,ffn_down")
-    ap.add_argument("--next-shapes", default="out_proj,ffn_up",
-                    help="other linear shapes of the block, reported apart from value ('' = none)")
+    ap.add_argument("--next-shapes", default="out_proj,ffn_up,qkv+pre_bias",
+                    help="other linear shapes of the block, reported apart from value ('' = none); "
+                         "name+pre_bias adds a channel pre-scale and a bias")
     ap.add_argument("--max-tile-bytes", type=int, default=0, help="0 = library default")
     ap.add_argument("--serial", action="store_true", help="prepare weights on the main stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -76,9 +77,10 @@ def counter_traffic(launch_shape):
 
 
 class Layer:
-    def __init__(self, name, torch, rbl, synth, dev, max_tile_bytes):
+    def __init__(self, name, torch, rbl, synth, dev, max_tile_bytes, pre_bias=False):
+        """pre_bias: also apply a channel pre-scale [K] and a bias [N] (seeded)."""
         w = synth.WORKLOADS[name]
-        self.name, self.w = name, w
+        self.name, self.w = (name + "_prescale_bias" if pre_bias else name), w
         t0 = time.perf_counter()
         x = synth.make_activation(w)
         p = synth.make_weight_nvfp4(w)
@@ -96,6 +98,11 @@ class Layer:
         self.w_s8 = [torch.empty(self.R, kp, dtype=torch.int8, device=dev) for _ in range(ntiles)]
         self.w_scale = [torch.empty(self.R, dtype=torch.float32, device=dev) for _ in range(ntiles)]
         self.out = torch.empty(w.M, w.N, dtype=synth.TORCH_DTYPE[w.out_dtypes[0]], device=dev)
+        self.pre = self.bias = None
+        if pre_bias:
+            g = torch.Generator().manual_seed(w.seed + 5000)
+            self.pre = (torch.rand(w.K, generator=g) * 1.5 + 0.5).to(dev)
+            self.bias = torch.randn(w.N, generator=g).to(dev)
         self.gen_s = time.perf_counter() - t0
         es = self.x.element_size()
         cols = 2 * w.K if w.swiglu else w.K
@@ -116,7 +123,9 @@ def run_layer(L, rbl, s_main, s_aux, ev):
     ev[0].record(s_main)
     if s_aux is not None:
         s_aux.wait_event(ev[0])
-    if w.swiglu:
+    if L.pre is not None:
+        rbl.cr_quant_act_ex(L.x, w.K, w.swiglu, L.pre, L.x_s8, L.x_scale, stream=s_main)
+    elif w.swiglu:
         rbl.cr_quant_act_swiglu(L.x, w.K, L.x_s8, L.x_scale, stream=s_main)
     else:
         rbl.cr_quant_act(L.x, w.K, L.x_s8, L.x_scale, stream=s_main)
@@ -133,8 +142,12 @@ def run_layer(L, rbl, s_main, s_aux, ev):
         if s_aux is not None:
             s_main.wait_event(ev[e + 1])
         ev[e + 2].record(s_main)
-        rbl.cr_gemm_s8_rowscale(L.x_s8, L.x_scale, L.w_s8[t][:r], L.w_scale[t][:r],
-                                L.out[:, n0:n0 + r], stream=s_main)
+        if L.bias is not None:
+            rbl.cr_gemm_s8_rowscale_bias(L.x_s8, L.x_scale, L.w_s8[t][:r], L.w_scale[t][:r], L.bias[n0:n0 + r],
+                                         L.out[:, n0:n0 + r], stream=s_main)
+        else:
+            rbl.cr_gemm_s8_rowscale(L.x_s8, L.x_scale, L.w_s8[t][:r], L.w_scale[t][:r],
+                                    L.out[:, n0:n0 + r], stream=s_main)
         ev[e + 3].record(s_main)
     ev[2].record(s_main)
 
@@ -353,7 +366,8 @@ def main():
         extra = []
         for n in nxt:
             print(f"bench: generating {n} ...", file=sys.stderr, flush=True)
-            extra.append(Layer(n, torch, rbl, synth, dev, args.max_tile_bytes))
+            base, _, opt = n.partition("+")
+            extra.append(Layer(base, torch, rbl, synth, dev, args.max_tile_bytes, pre_bias=(opt == "pre_bias")))
         torch.cuda.synchronize()
         k2 = max(5, K // 2)
         evs2, _, _ = time_layers(torch, rbl, extra, k2, W, s_main, s_aux)
