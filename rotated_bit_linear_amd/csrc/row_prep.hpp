@@ -396,7 +396,7 @@ __device__ __forceinline__ void row_prep_kernel_body(const Loader &ld, int64_t n
 
 // Launch shape of a row of nb blocks.  Up to 32 blocks, one block per 16-lane group; up
 // to 64 blocks, two per group (at most 512 threads either way); beyond that, two passes
-// with up to 60 groups (960 threads).
+// over slices of at most 60 groups (960 threads), the blocks spread evenly over the slices.
 struct RowPrepShape {
     int threads;   // workgroup size, a multiple of 64
     int rb;        // blocks held per 16-lane group in one-pass mode (1 or 2)
@@ -418,9 +418,11 @@ inline RowPrepShape row_prep_shape(int64_t nb, bool force_two_pass)
         s.rb = 2;
         groups = (nb + 1) / 2;
     } else {
+        // as few slices as 60 groups allow, with the blocks spread evenly over them
         s.rb = 1;
         s.two_pass = true;
-        groups = nb < kMaxGroups1 ? nb : kMaxGroups1;
+        const int64_t slices = (nb + kMaxGroups1 - 1) / kMaxGroups1;
+        groups = (nb + slices - 1) / slices;
     }
     s.threads = (int)(((groups + 3) / 4) * 64);
     return s;
