@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "ms/layer and INT8 TOPS (fraction of peak), QKV and FFN-down at M=19989"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 MFMA, TOP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+BT = 2                       # CR_FLAG_BLOCK_TRANSPOSED: the order cr_linear_nvfp4 uses inside
 GEMM_SOURCES = ["rotated_bit_linear_amd/csrc/gemm_s8.hip", "rotated_bit_linear_amd/csrc/kernels.hpp"]
 PMC_PROFILE = os.path.join(ROOT, "profiles", "gemm_s8_qkv_m19989_hbm_counters.md")
 
@@ -124,11 +125,11 @@ def run_layer(L, rbl, s_main, s_aux, ev):
     if s_aux is not None:
         s_aux.wait_event(ev[0])
     if L.pre is not None:
-        rbl.cr_quant_act_ex(L.x, w.K, w.swiglu, L.pre, L.x_s8, L.x_scale, stream=s_main)
+        rbl.cr_quant_act_ex(L.x, w.K, w.swiglu, L.pre, L.x_s8, L.x_scale, BT, stream=s_main)
     elif w.swiglu:
-        rbl.cr_quant_act_swiglu(L.x, w.K, L.x_s8, L.x_scale, stream=s_main)
+        rbl.cr_quant_act_swiglu(L.x, w.K, L.x_s8, L.x_scale, BT, stream=s_main)
     else:
-        rbl.cr_quant_act(L.x, w.K, L.x_s8, L.x_scale, stream=s_main)
+        rbl.cr_quant_act(L.x, w.K, L.x_s8, L.x_scale, BT, stream=s_main)
     ev[1].record(s_main)
     for c, (n0, r) in enumerate(L.chunks):
         t = c % 2
@@ -137,7 +138,7 @@ def run_layer(L, rbl, s_main, s_aux, ev):
             s_aux.wait_event(ev[e - 8 + 3])           # GEMM of chunk c-2 read this tile
         ev[e].record(sw)
         rbl.cr_prep_weight_nvfp4(L.codes[n0:n0 + r], L.sf[n0:n0 + r], L.g, w.K, L.w_s8[t][:r],
-                                 L.w_scale[t][:r], stream=sw)
+                                 L.w_scale[t][:r], BT, stream=sw)
         ev[e + 1].record(sw)
         if s_aux is not None:
             s_main.wait_event(ev[e + 1])
@@ -325,9 +326,9 @@ def main():
         w = L.w
         w_full = torch.empty(w.N, w.K_pad, dtype=torch.int8, device=dev)
         ws_full = torch.empty(w.N, dtype=torch.float32, device=dev)
-        act = ((lambda: rbl.cr_quant_act_swiglu(L.x, w.K, L.x_s8, L.x_scale, stream=s_main)) if w.swiglu else
-               (lambda: rbl.cr_quant_act(L.x, w.K, L.x_s8, L.x_scale, stream=s_main)))
-        wprep = lambda: rbl.cr_prep_weight_nvfp4(L.codes, L.sf, L.g, w.K, w_full, ws_full, stream=s_main)  # noqa: E731
+        act = ((lambda: rbl.cr_quant_act_swiglu(L.x, w.K, L.x_s8, L.x_scale, BT, stream=s_main)) if w.swiglu else
+               (lambda: rbl.cr_quant_act(L.x, w.K, L.x_s8, L.x_scale, BT, stream=s_main)))
+        wprep = lambda: rbl.cr_prep_weight_nvfp4(L.codes, L.sf, L.g, w.K, w_full, ws_full, BT, stream=s_main)  # noqa: E731
         gemm = lambda: rbl.cr_gemm_s8_rowscale(L.x_s8, L.x_scale, w_full, ws_full, L.out, stream=s_main)  # noqa: E731
         t_a = time_loop(torch, act, s_main)
         t_w = time_loop(torch, wprep, s_main)

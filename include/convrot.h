@@ -73,8 +73,17 @@ typedef enum { CR_BF16 = 0, CR_FP16 = 1, CR_FP32 = 2, CR_I32 = 3 } cr_dtype;
 
 enum {
     CR_FLAG_NONE = 0,
-    CR_FLAG_FORCE_TWO_PASS = 1    /* stream rows twice even when K_pad <= CR_TWO_PASS_K_PAD */
+    CR_FLAG_FORCE_TWO_PASS = 1,   /* stream rows twice even when K_pad <= CR_TWO_PASS_K_PAD */
+    CR_FLAG_BLOCK_TRANSPOSED = 2  /* S8 codes in block-transposed column order (below) */
 };
+
+/* Column order of the S8 outputs of the preparation calls.  Default (natural): column k
+ * holds the code of rotated element k.  With CR_FLAG_BLOCK_TRANSPOSED, inside every
+ * 256-column block, column 16 t + j holds the code of rotated element 16 j + t (t, j in
+ * 0..15): the same codes and row scales, in an order the kernels can write without their
+ * last LDS transposition.  The GEMM sums over K, so cr_gemm_s8_rowscale gives the same
+ * int32 sums when both of its operands use the same order; mixing orders is an error the
+ * library cannot detect.  cr_linear_nvfp4 uses the transposed order for its workspace. */
 
 /* ABI version of the loaded library (CR_ABI_VERSION when header and library match). */
 int cr_abi_version(void);
@@ -97,7 +106,7 @@ int64_t cr_padded_k(int64_t k);
  *   n_rows, K    rows to prepare and the logical K (1 <= K, K_pad <= CR_MAX_K_PAD).
  *   w_s8         [n_rows, ld_s8] int8 out, ld_s8 >= K_pad, a multiple of 16.
  *   w_scale      [n_rows] float out.
- *   flags        CR_FLAG_NONE or CR_FLAG_FORCE_TWO_PASS.
+ *   flags        CR_FLAG_NONE, CR_FLAG_FORCE_TWO_PASS and/or CR_FLAG_BLOCK_TRANSPOSED.
  */
 cr_status cr_prep_weight_nvfp4(const uint8_t *w_fp4, int64_t ld_fp4,
                                const uint8_t *w_sf, int64_t ld_sf,

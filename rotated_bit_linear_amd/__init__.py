@@ -21,7 +21,7 @@ from . import build as _build
 
 CR_ABI_VERSION = 1
 CR_BF16, CR_FP16, CR_FP32, CR_I32 = 0, 1, 2, 3
-CR_FLAG_NONE, CR_FLAG_FORCE_TWO_PASS = 0, 1
+CR_FLAG_NONE, CR_FLAG_FORCE_TWO_PASS, CR_FLAG_BLOCK_TRANSPOSED = 0, 1, 2
 CR_MAX_K_PAD = 133120
 DEFAULT_MAX_TILE_BYTES = 128 << 20
 STATUS = {0: "CR_OK", 1: "CR_ERR_INVALID_ARG", 2: "CR_ERR_UNSUPPORTED_DTYPE", 3: "CR_ERR_MISALIGNED",

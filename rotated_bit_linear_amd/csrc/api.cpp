@@ -59,7 +59,7 @@ inline int64_t pad256(int64_t k) { return ((k + 255) / 256) * 256; }
 
 cr_status check_flags(uint32_t flags)
 {
-    return (flags & ~(uint32_t)CR_FLAG_FORCE_TWO_PASS) ? CR_ERR_INVALID_ARG : CR_OK;
+    return (flags & ~(uint32_t)(CR_FLAG_FORCE_TWO_PASS | CR_FLAG_BLOCK_TRANSPOSED)) ? CR_ERR_INVALID_ARG : CR_OK;
 }
 
 cr_status check_act(const void *x, cr_dtype dt, int64_t ld_x, int64_t M, int64_t K, int64_t cols,
@@ -219,7 +219,8 @@ cr_status cr_prep_weight_nvfp4(const uint8_t *w_fp4, int64_t ld_fp4, const uint8
     if (s != CR_OK) return s;
     if ((s = current_device_ok()) != CR_OK) return s;
     return from_hip(convrot::launch_prep_weight(w_fp4, ld_fp4, w_sf, ld_sf, global_scale, n_rows, K, w_s8,
-                                                ld_s8, w_scale, (flags & CR_FLAG_FORCE_TWO_PASS) != 0, stream));
+                                                ld_s8, w_scale, (flags & CR_FLAG_FORCE_TWO_PASS) != 0,
+                                                (flags & CR_FLAG_BLOCK_TRANSPOSED) != 0, stream));
 }
 
 cr_status cr_quant_act_ex(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
@@ -232,9 +233,10 @@ cr_status cr_quant_act_ex(const void *x, cr_dtype x_dtype, int64_t ld_x, int swi
     if (pre_scale && !aligned(pre_scale, 4)) return CR_ERR_MISALIGNED;
     if ((s = current_device_ok()) != CR_OK) return s;
     const bool tp = (flags & CR_FLAG_FORCE_TWO_PASS) != 0;
+    const bool tr = (flags & CR_FLAG_BLOCK_TRANSPOSED) != 0;
     return from_hip(swiglu
-        ? convrot::launch_quant_act_swiglu(x, (int)x_dtype, ld_x, M, K, pre_scale, x_s8, ld_s8, x_scale, tp, stream)
-        : convrot::launch_quant_act(x, (int)x_dtype, ld_x, M, K, pre_scale, x_s8, ld_s8, x_scale, tp, stream));
+        ? convrot::launch_quant_act_swiglu(x, (int)x_dtype, ld_x, M, K, pre_scale, x_s8, ld_s8, x_scale, tp, tr, stream)
+        : convrot::launch_quant_act(x, (int)x_dtype, ld_x, M, K, pre_scale, x_s8, ld_s8, x_scale, tp, tr, stream));
 }
 
 cr_status cr_quant_act(const void *x, cr_dtype x_dtype, int64_t ld_x, int64_t M, int64_t K,
@@ -350,9 +352,11 @@ cr_status cr_linear_nvfp4_ex(const void *x, cr_dtype x_dtype, int64_t ld_x, int 
         if (hipEventRecord(ev_start, s_main) != hipSuccess) return CR_ERR_LAUNCH;
         if (hipStreamWaitEvent(s_aux, ev_start, 0) != hipSuccess) return CR_ERR_LAUNCH;
     }
+    // both S8 operands live only in the workspace: they use the block-transposed column
+    // order, which skips one LDS transposition per block and leaves every int32 sum as is
     hipError_t e = swiglu
-        ? convrot::launch_quant_act_swiglu(x, (int)x_dtype, ld_x, M, K, pre_scale, x_s8, p.K_pad, x_scale, tp, s_main)
-        : convrot::launch_quant_act(x, (int)x_dtype, ld_x, M, K, pre_scale, x_s8, p.K_pad, x_scale, tp, s_main);
+        ? convrot::launch_quant_act_swiglu(x, (int)x_dtype, ld_x, M, K, pre_scale, x_s8, p.K_pad, x_scale, tp, true, s_main)
+        : convrot::launch_quant_act(x, (int)x_dtype, ld_x, M, K, pre_scale, x_s8, p.K_pad, x_scale, tp, true, s_main);
     if (e != hipSuccess) return CR_ERR_LAUNCH;
 
     for (int64_t c = 0; c < p.nchunks; c++) {
@@ -362,7 +366,7 @@ cr_status cr_linear_nvfp4_ex(const void *x, cr_dtype x_dtype, int64_t ld_x, int 
         hipStream_t sp = overlap ? s_aux : s_main;
         if (overlap && c >= 2 && hipStreamWaitEvent(s_aux, ev_gemm[b], 0) != hipSuccess) return CR_ERR_LAUNCH;
         e = convrot::launch_prep_weight(w_fp4 + n0 * ld_fp4, ld_fp4, w_sf + n0 * ld_sf, ld_sf, global_scale,
-                                        rows, K, tile[b], p.K_pad, tscale[b], tp, sp);
+                                        rows, K, tile[b], p.K_pad, tscale[b], tp, true, sp);
         if (e != hipSuccess) return CR_ERR_LAUNCH;
         if (overlap) {
             if (hipEventRecord(ev_prep[b], s_aux) != hipSuccess) return CR_ERR_LAUNCH;

@@ -11,21 +11,22 @@ constexpr int64_t kGemmTileCols = 256;   // M direction
 constexpr int64_t kGemmTileRows = 256;   // N direction (weight rows)
 
 // dtype codes follow cr_dtype: 0 bf16, 1 fp16, 2 fp32, 3 int32 (GEMM output only)
-// pre: optional [K] (or [F]) channel pre-scale, nullptr for none
+// pre: optional [K] (or [F]) channel pre-scale, nullptr for none; transposed: codes in the
+// block-transposed column order (see row_prep.hpp)
 hipError_t launch_quant_act(const void *x, int dtype, int64_t ld_x, int64_t M, int64_t K, const float *pre,
-                            int8_t *x_s8, int64_t ld_s8, float *x_scale, bool two_pass,
+                            int8_t *x_s8, int64_t ld_s8, float *x_scale, bool two_pass, bool transposed,
                             hipStream_t st);
 
 hipError_t launch_quant_act_swiglu(const void *h, int dtype, int64_t ld_h, int64_t M, int64_t F,
                                    const float *pre, int8_t *x_s8, int64_t ld_s8, float *x_scale,
-                                   bool two_pass, hipStream_t st);
+                                   bool two_pass, bool transposed, hipStream_t st);
 
 hipError_t launch_swiglu(const void *h, int dtype, int64_t ld_h, int64_t M, int64_t F, float *out,
                          int64_t ld_out, hipStream_t st);
 
 hipError_t launch_prep_weight(const uint8_t *codes, int64_t ld_codes, const uint8_t *sf, int64_t ld_sf,
                               const float *g, int64_t n_rows, int64_t K, int8_t *w_s8, int64_t ld_s8,
-                              float *w_scale, bool two_pass, hipStream_t st);
+                              float *w_scale, bool two_pass, bool transposed, hipStream_t st);
 
 // bias: optional [N] FP32 bias added in the epilogue, nullptr for none (not with int32 out)
 hipError_t launch_gemm_s8(const int8_t *A, int64_t lda, const float *sa, const int8_t *B, int64_t ldb,

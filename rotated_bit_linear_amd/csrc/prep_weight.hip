@@ -102,30 +102,31 @@ struct NVFP4Loader {
 
 template <int RB>
 __global__ __launch_bounds__(row_prep_max_threads<RB>()) void prep_weight_kernel(NVFP4Loader ld, int64_t n_rows, int nb, int8_t *__restrict__ out,
-                                   int64_t ld_out, float *__restrict__ scale, int two_pass)
+                                   int64_t ld_out, float *__restrict__ scale, int mode)
 {
     ld.gs = *ld.g;
-    row_prep_kernel_body<NVFP4Loader, RB>(ld, n_rows, nb, out, ld_out, scale, two_pass);
+    row_prep_kernel_body<NVFP4Loader, RB>(ld, n_rows, nb, out, ld_out, scale, mode);
 }
 
 hipError_t launch_prep_weight(const uint8_t *codes, int64_t ld_codes, const uint8_t *sf, int64_t ld_sf,
                               const float *g, int64_t n_rows, int64_t K, int8_t *w_s8, int64_t ld_s8,
-                              float *w_scale, bool two_pass, hipStream_t st)
+                              float *w_scale, bool two_pass, bool transposed, hipStream_t st)
 {
     const int64_t nb = (K + 255) / 256;
     const RowPrepShape s = row_prep_shape(nb, two_pass);
     const size_t lds = row_prep_lds_bytes(s.threads);
+    const int mode = (s.two_pass ? 1 : 0) | (transposed ? 2 : 0);
     NVFP4Loader L{codes, ld_codes, sf, ld_sf, g, K, 0.0f};
     if (s.rb == 2) {
         const void *k = reinterpret_cast<const void *>(&prep_weight_kernel<2>);
         const dim3 grid((unsigned)row_prep_grid(n_rows, s, k, lds));
         hipLaunchKernelGGL(prep_weight_kernel<2>, grid, dim3(s.threads), lds, st,
-                           L, n_rows, (int)nb, w_s8, ld_s8, w_scale, 0);
+                           L, n_rows, (int)nb, w_s8, ld_s8, w_scale, mode);
     } else {
         const void *k = reinterpret_cast<const void *>(&prep_weight_kernel<1>);
         const dim3 grid((unsigned)row_prep_grid(n_rows, s, k, lds));
         hipLaunchKernelGGL(prep_weight_kernel<1>, grid, dim3(s.threads), lds, st,
-                           L, n_rows, (int)nb, w_s8, ld_s8, w_scale, s.two_pass ? 1 : 0);
+                           L, n_rows, (int)nb, w_s8, ld_s8, w_scale, mode);
     }
     return hipGetLastError();
 }

@@ -250,65 +250,68 @@ __global__ void swiglu_kernel(const typename Elem<DT>::T *__restrict__ h, int64_
 
 template <class Loader, int RB>
 __global__ __launch_bounds__(row_prep_max_threads<RB>()) void quant_act_kernel(Loader ld, int64_t n_rows, int nb, int8_t *__restrict__ out, int64_t ld_out,
-                                 float *__restrict__ scale, int two_pass)
+                                 float *__restrict__ scale, int mode)
 {
-    row_prep_kernel_body<Loader, RB>(ld, n_rows, nb, out, ld_out, scale, two_pass);
+    row_prep_kernel_body<Loader, RB>(ld, n_rows, nb, out, ld_out, scale, mode);
 }
 
 // --------------------------------------------------------------------- launchers ----
 
 template <class Loader>
 static hipError_t launch_rows(const Loader &L, int64_t rows, int64_t nb, int8_t *out, int64_t ld_out,
-                              float *scale, bool force_two_pass, hipStream_t st)
+                              float *scale, bool force_two_pass, bool transposed, hipStream_t st)
 {
     const RowPrepShape s = row_prep_shape(nb, force_two_pass);
     const size_t lds = row_prep_lds_bytes(s.threads);
+    const int mode = (s.two_pass ? 1 : 0) | (transposed ? 2 : 0);
     if (s.rb == 2) {
         const void *k = reinterpret_cast<const void *>(&quant_act_kernel<Loader, 2>);
         const dim3 grid((unsigned)row_prep_grid(rows, s, k, lds));
         hipLaunchKernelGGL((quant_act_kernel<Loader, 2>), grid, dim3(s.threads), lds, st,
-                           L, rows, (int)nb, out, ld_out, scale, 0);
+                           L, rows, (int)nb, out, ld_out, scale, mode);
     } else {
         const void *k = reinterpret_cast<const void *>(&quant_act_kernel<Loader, 1>);
         const dim3 grid((unsigned)row_prep_grid(rows, s, k, lds));
         hipLaunchKernelGGL((quant_act_kernel<Loader, 1>), grid, dim3(s.threads), lds, st,
-                           L, rows, (int)nb, out, ld_out, scale, s.two_pass ? 1 : 0);
+                           L, rows, (int)nb, out, ld_out, scale, mode);
     }
     return hipGetLastError();
 }
 
 template <int DT>
 static hipError_t launch_act(const void *x, int64_t ld_x, int64_t M, int64_t K, const float *pre,
-                             int8_t *x_s8, int64_t ld_s8, float *x_scale, bool two_pass, hipStream_t st)
+                             int8_t *x_s8, int64_t ld_s8, float *x_scale, bool two_pass, bool transposed,
+                             hipStream_t st)
 {
     const auto *xp = static_cast<const typename Elem<DT>::T *>(x);
     const bool aligned = ((uintptr_t)x % 16 == 0) && ((ld_x * (int64_t)sizeof(typename Elem<DT>::T)) % 16 == 0);
     const int64_t nb = (K + 255) / 256;
-    if (pre) return launch_rows(ActLoader<DT, true>{xp, ld_x, K, aligned, pre}, M, nb, x_s8, ld_s8, x_scale, two_pass, st);
-    return launch_rows(ActLoader<DT, false>{xp, ld_x, K, aligned, nullptr}, M, nb, x_s8, ld_s8, x_scale, two_pass, st);
+    if (pre) return launch_rows(ActLoader<DT, true>{xp, ld_x, K, aligned, pre}, M, nb, x_s8, ld_s8, x_scale, two_pass, transposed, st);
+    return launch_rows(ActLoader<DT, false>{xp, ld_x, K, aligned, nullptr}, M, nb, x_s8, ld_s8, x_scale, two_pass, transposed, st);
 }
 
 template <int DT>
 static hipError_t launch_swiglu(const void *h, int64_t ld_h, int64_t M, int64_t F, const float *pre,
-                                int8_t *x_s8, int64_t ld_s8, float *x_scale, bool two_pass, hipStream_t st)
+                                int8_t *x_s8, int64_t ld_s8, float *x_scale, bool two_pass, bool transposed,
+                                hipStream_t st)
 {
     const int64_t es = (int64_t)sizeof(typename Elem<DT>::T);
     const bool row_ok = ((uintptr_t)h % 16 == 0) && ((ld_h * es) % 16 == 0);
     const bool val_ok = row_ok && ((F * es) % 16 == 0);
     const auto *hp = static_cast<const typename Elem<DT>::T *>(h);
     const int64_t nb = (F + 255) / 256;
-    if (pre) return launch_rows(SwigluLoader<DT, true>{hp, ld_h, F, row_ok, val_ok, pre}, M, nb, x_s8, ld_s8, x_scale, two_pass, st);
-    return launch_rows(SwigluLoader<DT, false>{hp, ld_h, F, row_ok, val_ok, nullptr}, M, nb, x_s8, ld_s8, x_scale, two_pass, st);
+    if (pre) return launch_rows(SwigluLoader<DT, true>{hp, ld_h, F, row_ok, val_ok, pre}, M, nb, x_s8, ld_s8, x_scale, two_pass, transposed, st);
+    return launch_rows(SwigluLoader<DT, false>{hp, ld_h, F, row_ok, val_ok, nullptr}, M, nb, x_s8, ld_s8, x_scale, two_pass, transposed, st);
 }
 
 hipError_t launch_quant_act(const void *x, int dtype, int64_t ld_x, int64_t M, int64_t K, const float *pre,
-                            int8_t *x_s8, int64_t ld_s8, float *x_scale, bool two_pass,
+                            int8_t *x_s8, int64_t ld_s8, float *x_scale, bool two_pass, bool transposed,
                             hipStream_t st)
 {
     switch (dtype) {
-    case 0: return launch_act<0>(x, ld_x, M, K, pre, x_s8, ld_s8, x_scale, two_pass, st);
-    case 1: return launch_act<1>(x, ld_x, M, K, pre, x_s8, ld_s8, x_scale, two_pass, st);
-    case 2: return launch_act<2>(x, ld_x, M, K, pre, x_s8, ld_s8, x_scale, two_pass, st);
+    case 0: return launch_act<0>(x, ld_x, M, K, pre, x_s8, ld_s8, x_scale, two_pass, transposed, st);
+    case 1: return launch_act<1>(x, ld_x, M, K, pre, x_s8, ld_s8, x_scale, two_pass, transposed, st);
+    case 2: return launch_act<2>(x, ld_x, M, K, pre, x_s8, ld_s8, x_scale, two_pass, transposed, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -334,12 +337,12 @@ hipError_t launch_swiglu(const void *h, int dtype, int64_t ld_h, int64_t M, int6
 
 hipError_t launch_quant_act_swiglu(const void *h, int dtype, int64_t ld_h, int64_t M, int64_t F,
                                    const float *pre, int8_t *x_s8, int64_t ld_s8, float *x_scale,
-                                   bool two_pass, hipStream_t st)
+                                   bool two_pass, bool transposed, hipStream_t st)
 {
     switch (dtype) {
-    case 0: return launch_swiglu<0>(h, ld_h, M, F, pre, x_s8, ld_s8, x_scale, two_pass, st);
-    case 1: return launch_swiglu<1>(h, ld_h, M, F, pre, x_s8, ld_s8, x_scale, two_pass, st);
-    case 2: return launch_swiglu<2>(h, ld_h, M, F, pre, x_s8, ld_s8, x_scale, two_pass, st);
+    case 0: return launch_swiglu<0>(h, ld_h, M, F, pre, x_s8, ld_s8, x_scale, two_pass, transposed, st);
+    case 1: return launch_swiglu<1>(h, ld_h, M, F, pre, x_s8, ld_s8, x_scale, two_pass, transposed, st);
+    case 2: return launch_swiglu<2>(h, ld_h, M, F, pre, x_s8, ld_s8, x_scale, two_pass, transposed, st);
     default: return hipErrorInvalidValue;
     }
 }

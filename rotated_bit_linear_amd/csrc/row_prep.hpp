@@ -24,6 +24,12 @@
 // rounds to the nearest integer, ties to even, and leaves q in two's complement in the
 // low byte of the sum (the sum lies in [2^23, 2^24), where the spacing is 1).
 //
+// Code order.  Natural: the 16 codes a lane stores are elements 16t .. 16t+15 of its block.
+// Block-transposed: the transposition back is skipped and the lane stores the codes of
+// elements t, t+16, .., t+240 in that order, i.e. column 16t + j of every 256-column block
+// holds element 16j + t.  The same codes, in another column order; a GEMM over two
+// operands stored in the same order gives the same int32 sums.
+//
 // Rows whose K_pad exceeds 64 blocks (16384 columns), or when forced, are streamed twice:
 // pass 1 rotates every block to find the row maximum, pass 2 reloads, rotates again and
 // quantizes (same operations, so the same bits).
@@ -76,8 +82,9 @@ __device__ __forceinline__ void butterflies16(float (&v)[16])
 
 // The eight butterfly stages of ConvRot256 on the block held by this lane's 16-lane group
 // (the 1/16 scaling is left to the quantization).  `tile` is the group's private 16x16
-// LDS tile.  In: v[i] = x[16t + i].  Out: v[i] = z[16t + i], y = z * 0.0625.
-__device__ __forceinline__ void hadamard256(float (&v)[16], float *tile, int t)
+// LDS tile.  In: v[i] = x[16t + i].  Out: v[i] = z[16t + i] (natural), or v[j] =
+// z[16j + t] when !natural (the layout after phase B: the transposition back is skipped).
+__device__ __forceinline__ void hadamard256(float (&v)[16], float *tile, int t, bool natural)
 {
     butterflies16(v);                                   // stages h = 1, 2, 4, 8
 #pragma unroll
@@ -90,6 +97,7 @@ __device__ __forceinline__ void hadamard256(float (&v)[16], float *tile, int t)
     for (int j = 0; j < 16; j++) v[j] = tile[tile_index(j, t)];   // v[j] = x'[16j + t]
     butterflies16(v);                                   // stages h = 16, 32, 64, 128
     wave_lds_sync();
+    if (!natural) return;
 #pragma unroll
     for (int j = 0; j < 16; j++) tile[tile_index(j, t)] = v[j];
     wave_lds_sync();
@@ -230,7 +238,7 @@ __host__ __device__ constexpr size_t row_prep_lds_bytes(int threads)
 template <class Loader, int RB>
 __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, int nb,
                                               int8_t *__restrict__ out, int64_t ld_out,
-                                              float *__restrict__ scale_out)
+                                              float *__restrict__ scale_out, bool natural)
 {
     extern __shared__ float lds[];
     const int tid = threadIdx.x;
@@ -261,7 +269,7 @@ __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, 
         for (int q = 0; q < RB; q++) {
             const int b = grp + q * G;
             if (b < nb) {
-                hadamard256(v[q], tile, t);
+                hadamard256(v[q], tile, t, natural);
 #pragma unroll
                 for (int i = 0; i < 16; i++) zmax = fmaxf(zmax, fabsf(v[q][i]));
             }
@@ -343,7 +351,7 @@ __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, 
 template <class Loader>
 __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row, int nb,
                                                   int8_t *__restrict__ out, int64_t ld_out,
-                                                  float *__restrict__ scale_out)
+                                                  float *__restrict__ scale_out, bool natural)
 {
     extern __shared__ float lds[];
     const int tid = threadIdx.x;
@@ -370,7 +378,7 @@ __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row,
     const int nslices = (nb + G - 1) / G;
     for (int s = 0; s < nslices; s++) {
         load(s * G + grp, v);
-        hadamard256(v, tile, t);
+        hadamard256(v, tile, t, natural);
 #pragma unroll
         for (int i = 0; i < 16; i++) zmax = fmaxf(zmax, fabsf(v[i]));
     }
@@ -378,20 +386,22 @@ __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row,
     for (int s = 0; s < nslices; s++) {
         const int b = s * G + grp;
         load(b, v);
-        hadamard256(v, tile, t);
+        hadamard256(v, tile, t, natural);
         if (b < nb) store_codes(v, rq, orow + (int64_t)b * 256 + t * 16);
     }
     if (tid == 0) scale_out[row] = rq.scale;
 }
 
 // Kernel body shared by all loaders.
+// mode: bit 0 two-pass, bit 1 block-transposed code order
 template <class Loader, int RB>
 __device__ __forceinline__ void row_prep_kernel_body(const Loader &ld, int64_t n_rows, int nb,
                                                      int8_t *__restrict__ out, int64_t ld_out,
-                                                     float *__restrict__ scale_out, int two_pass)
+                                                     float *__restrict__ scale_out, int mode)
 {
-    if (two_pass) row_prep_two_pass(ld, (int64_t)blockIdx.x, nb, out, ld_out, scale_out);
-    else row_prep_rows<Loader, RB>(ld, n_rows, nb, out, ld_out, scale_out);
+    const bool natural = (mode & 2) == 0;
+    if (mode & 1) row_prep_two_pass(ld, (int64_t)blockIdx.x, nb, out, ld_out, scale_out, natural);
+    else row_prep_rows<Loader, RB>(ld, n_rows, nb, out, ld_out, scale_out, natural);
 }
 
 // Launch shape of a row of nb blocks.  Up to 32 blocks, one block per 16-lane group; up

@@ -93,7 +93,8 @@ def test_prep_weight_validation():
     assert pw(ld=264) == MIS               # not a multiple of 16
     assert pw(codes=A16 + 4) == MIS
     assert pw(K=CR_BIG, ld=CR_BIG, ld_sf=CR_BIG, ld_q=CR_BIG + 256) == BIG
-    assert pw(flags=2) == INV
+    assert pw(flags=4) == INV
+    assert pw(flags=2) != INV              # block-transposed order is a valid flag
 
 
 def gm(a=A16, lda=512, sa=A16, b=A16, ldb=512, sb=A16, M=8, N=8, K=512, c=A16, dt=0, ldc=8):

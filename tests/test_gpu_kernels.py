@@ -357,3 +357,52 @@ def test_layer_prescale_bias(swiglu):
                               p.g, synth.DT_FP32, pre_scale=c.numpy(), bias=bias.numpy())
     err = rel_l2(out_f64(outs[0], synth.DT_FP32), out_f64(ref, synth.DT_FP32))
     assert err <= TOL[synth.DT_FP32], err
+
+
+# ----------------------------------------------------- block-transposed order ----
+
+def _block_transposed(codes: np.ndarray) -> np.ndarray:
+    """Natural-order codes [rows, K_pad] -> block-transposed order: column 16t + j of each
+    256-column block holds element 16j + t."""
+    r, kp = codes.shape
+    return codes.reshape(r, kp // 256, 16, 16).transpose(0, 1, 3, 2).reshape(r, kp).copy()
+
+
+@pytest.mark.parametrize("dt,M,K,swiglu,forced", [(synth.DT_BF16, 37, 300, False, False),
+                                                  (synth.DT_BF16, 6, 700, True, False),
+                                                  (synth.DT_FP16, 3, 20000, False, False),
+                                                  (synth.DT_BF16, 5, 14336, True, True)])
+def test_block_transposed_activation(dt, M, K, swiglu, forced):
+    cols = 2 * K if swiglu else K
+    x = make_x(M, cols, dt, seed=K + 5, ld=(cols // 8 + 1) * 8, special=True)
+    flags = rbl.CR_FLAG_BLOCK_TRANSPOSED | (rbl.CR_FLAG_FORCE_TWO_PASS if forced else 0)
+    say(f"cr_quant_act block-transposed dt={dt} M={M} K={K} swiglu={swiglu} forced={forced}")
+    q, s = rbl.quant_act(x.to(dev()), K, swiglu=swiglu, flags=flags)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant_act(host_bits(x, dt), dt, K, swiglu=swiglu)
+    assert_bits_equal(q.cpu().numpy(), _block_transposed(rq), "x_s8 (block-transposed)")
+    assert_bits_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32), "x_scale (block-transposed)")
+
+
+@pytest.mark.parametrize("N,K", [(300, 1000), (40, 20000), (64, 14336)])
+def test_block_transposed_weight_and_gemm(N, K):
+    g = torch.Generator().manual_seed(N * 3 + K)
+    w = 0.02 * torch.randn(N, K, generator=g)
+    p = synth.nvfp4_encode(w, garbage_seed=N)
+    gs = torch.tensor([p.g], dtype=torch.float32, device=dev())
+    say(f"cr_prep_weight_nvfp4 block-transposed N={N} K={K}")
+    qt, st = rbl.prep_weight_nvfp4(p.codes.to(dev()), p.sf.to(dev()), gs, K, flags=rbl.CR_FLAG_BLOCK_TRANSPOSED)
+    qn, sn = rbl.prep_weight_nvfp4(p.codes.to(dev()), p.sf.to(dev()), gs, K)
+    x = make_x(65, K, synth.DT_BF16, seed=K)
+    xt, xst = rbl.quant_act(x.to(dev()), K, flags=rbl.CR_FLAG_BLOCK_TRANSPOSED)
+    xn, xsn = rbl.quant_act(x.to(dev()), K)
+    acc_t = torch.empty(65, N, dtype=torch.int32, device=dev())
+    acc_n = torch.empty(65, N, dtype=torch.int32, device=dev())
+    say(f"cr_gemm_s8_rowscale int32, both operands block-transposed vs natural, N={N} K={K}")
+    rbl.cr_gemm_s8_rowscale(xt, xst, qt, st, acc_t)
+    rbl.cr_gemm_s8_rowscale(xn, xsn, qn, sn, acc_n)
+    torch.cuda.synchronize()
+    rq, rs = oracle.prep_weight_nvfp4(p.codes.numpy(), p.sf.numpy(), p.g, K)
+    assert_bits_equal(qt.cpu().numpy(), _block_transposed(rq), "w_s8 (block-transposed)")
+    assert_bits_equal(st.cpu().numpy().view(np.uint32), rs.view(np.uint32), "w_scale (block-transposed)")
+    assert_bits_equal(acc_t.cpu().numpy(), acc_n.cpu().numpy(), "int32 sums, transposed vs natural order")
