@@ -47,6 +47,7 @@ def lib():
             "or_quant_act_ex": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, vp, i64, vp]),
             "or_act_prescale": (None, [vp, i64, i64, i64, vp]),
             "or_prep_weight_nvfp4": (C.c_int, [vp, i64, vp, i64, f32, i64, i64, vp, i64, vp]),
+            "or_weight_amax_nvfp4": (C.c_int, [vp, i64, vp, i64, f32, i64, i64, vp]),
             "or_gemm_s8": (None, [vp, i64, vp, i64, i64, i64, i64, vp, i64]),
             "or_epilogue": (None, [vp, i64, vp, vp, i64, i64, C.c_int, vp, i64]),
             "or_epilogue_ex": (None, [vp, i64, vp, vp, vp, i64, i64, C.c_int, vp, i64]),
@@ -213,6 +214,16 @@ def prep_weight_nvfp4(codes: np.ndarray, sf: np.ndarray, g: float, K: int):
     assert rc == 0
     return q, s
 
+
+def weight_amax_nvfp4(codes: np.ndarray, sf: np.ndarray, g: float, K: int) -> np.ndarray:
+    """Row maxima a[n] = max |ConvRot256(decode(W))[n, :]| -> [N] fp32."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    sf = np.ascontiguousarray(sf, np.uint8)
+    n = codes.shape[0]
+    a = np.empty(n, np.float32)
+    rc = lib().or_weight_amax_nvfp4(_p(codes), codes.shape[1], _p(sf), sf.shape[1], g, n, K, _p(a))
+    assert rc == 0
+    return a
 
 def gemm_s8(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     """int32 acc[M, N] = A[M, K_pad] . B[N, K_pad]^T."""

@@ -374,6 +374,33 @@ int or_prep_weight_nvfp4(const uint8_t *codes, int64_t ld_codes, const uint8_t *
     return 0;
 }
 
+/* Row maxima of the rotated weight: a[n] = max_k |y[n, k]| over all K_pad columns, where y
+ * is the NVFP4 decode followed by ConvRot256 (the quantity the row quantizer above starts
+ * from; s = a/127 and r = 127/a follow from it).  A GEMM that quantizes weight blocks on
+ * the fly needs a before it sees the whole row (ComfyUI Turing Utils README, "Load ConvRot
+ * DiT ..." bullet: the row scale covers the whole padded row, which is why long rows take
+ * two passes). */
+int or_weight_amax_nvfp4(const uint8_t *codes, int64_t ld_codes, const uint8_t *sf, int64_t ld_sf,
+                         float g, int64_t n_rows, int64_t K, float *amax)
+{
+    int64_t kp = or_padded_k(K);
+    float *buf = (float *)malloc(sizeof(float) * (size_t)(n_rows > 0 ? n_rows : 1) * (size_t)kp);
+    if (!buf) return -1;
+    or_nvfp4_decode(codes, ld_codes, sf, ld_sf, g, n_rows, K, buf, kp);
+    or_convrot256(buf, n_rows, kp, kp);
+#pragma omp parallel for
+    for (int64_t n = 0; n < n_rows; n++) {
+        float a = 0.0f;
+        for (int64_t k = 0; k < kp; k++) {
+            float m = fabsf(buf[n * kp + k]);
+            if (m > a) a = m;
+        }
+        amax[n] = a;
+    }
+    free(buf);
+    return 0;
+}
+
 /* ----------------------------------------------------------------- GEMM ---- */
 
 /* acc[m, n] = sum_k A[m, k] * B[n, k] (both operands K-contiguous, y = x W^T). */
