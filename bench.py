@@ -30,7 +30,13 @@ METRIC = "ms/layer and INT8 TOPS (fraction of peak), QKV and FFN-down at M=19989
 PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 MFMA, TOP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 BT = 2                       # CR_FLAG_BLOCK_TRANSPOSED: the order cr_linear_nvfp4 uses inside
-GEMM_SOURCES = ["rotated_bit_linear_amd/csrc/gemm_s8.hip", "rotated_bit_linear_amd/csrc/kernels.hpp"]
+# Decode-inside-GEMM: vector instructions per weight element at the minimum (decode: one
+# conversion per two elements and two multiplies; rotation: 8 butterfly adds; quantization:
+# multiply, clamp, rounding add and 3/4 of a byte permute) and the chip's vector issue peak
+# with one fp32 operation per lane per clock (256 CUs x 64 lanes x 2.4 GHz; no packed math).
+FUSED_VALU_PER_ELEM = 14.25
+PEAK_VALU_TOPS = 39.3
+GEMM_SOURCES = ["rotated_bit_linear_amd/csrc/gemm_s8.hip"]
 PMC_PROFILE = os.path.join(ROOT, "profiles", "gemm_s8_qkv_m19989_hbm_counters.md")
 
 
@@ -43,6 +49,8 @@ def parse_args():
     ap.add_argument("--next-shapes", default="out_proj,ffn_up,qkv+pre_bias",
                     help="other linear shapes of the block, reported apart from value ('' = none); "
                          "name+pre_bias adds a channel pre-scale and a bias")
+    ap.add_argument("--short-batches", default="1,16,64,128",
+                    help="activation rows of the short-batch (decode-inside-GEMM) lines; empty: none")
     ap.add_argument("--max-tile-bytes", type=int, default=0, help="0 = library default")
     ap.add_argument("--serial", action="store_true", help="prepare weights on the main stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -116,10 +124,13 @@ class Layer:
 def run_layer(L, rbl, s_main, s_aux, ev):
     """The layer as cr_linear_nvfp4 runs it: activation prep (main stream) while chunk 0 of
     the weight is prepared (second stream); GEMM of chunk c on the main stream while chunk
-    c+1 is prepared; a weight tile is refilled only after the GEMM that read it.
+    c+1 is prepared; a weight tile is refilled only after the GEMM that read it.  A weight
+    of one chunk is staged on the main stream.
     ev: 3 + 4 * nchunks events: start, act begin/end, then per chunk prep begin/end and
     GEMM begin/end."""
     w = L.w
+    if L.nchunks < 2:
+        s_aux = None                                  # a single chunk is staged on the main stream
     sw = s_aux if s_aux is not None else s_main
     ev[0].record(s_main)
     if s_aux is not None:
@@ -274,6 +285,74 @@ def copy_bandwidth(torch, stream) -> float:
     return 2 * n / (ms * 1e-3) / 1e9
 
 
+def short_batches(torch, rbl, synth, dev, s_main, rows_list, n=20):
+    """The QKV weight [21504, 5376] at short batches: the layer as cr_linear_nvfp4 runs it
+    (decode-inside-GEMM up to 64 rows, staged tiles above), the staged components one after
+    the other (activation prep, whole-weight prep, GEMM), and the fused GEMM with the weight's
+    row maxima computed once, as for a fixed weight.  Returns the per-batch times and the
+    fused kernel's vector-issue roofline at the smallest batch."""
+    w = synth.WORKLOADS["qkv_m128"]
+    p = synth.make_weight_nvfp4(w)
+    x_all = synth.make_activation(synth.Workload("short", max(rows_list), w.N, w.K, w.x_dtype, w.out_dtypes,
+                                                 w.seed, outlier_frac=w.outlier_frac)).to(dev)
+    cd, sfd = p.codes.to(dev), p.sf.to(dev)
+    gs = torch.tensor([p.g], dtype=torch.float32, device=dev)
+    amax = torch.empty(w.N, dtype=torch.float32, device=dev)
+    w_s8 = torch.empty(w.N, w.K_pad, dtype=torch.int8, device=dev)
+    w_sc = torch.empty(w.N, dtype=torch.float32, device=dev)
+    t_amax = time_loop(torch, lambda: rbl.cr_weight_amax_nvfp4(cd, sfd, gs, w.K, amax, stream=s_main), s_main, n=n)
+    aux = torch.cuda.Stream()
+    info = {"weight": "qkv_proj [21504, 5376] NVFP4", "weight_row_maxima_ms": round(t_amax, 4), "rows": {}}
+    t_gemm_small = None
+    for M in rows_list:
+        x = x_all[:M]
+        qx = torch.empty(M, w.K_pad, dtype=torch.int8, device=dev)
+        sx = torch.empty(M, dtype=torch.float32, device=dev)
+        y = torch.empty(M, w.N, dtype=torch.bfloat16, device=dev)
+        y2 = torch.empty_like(y)
+        ws = torch.empty(rbl.cr_linear_nvfp4_workspace_bytes(M, w.N, w.K), dtype=torch.uint8, device=dev)
+
+        def layer():
+            rbl.cr_linear_nvfp4(x, w.K, False, cd, sfd, gs, y, ws, stream=s_main, aux_stream=aux)
+
+        def staged():
+            rbl.cr_quant_act(x, w.K, qx, sx, BT, stream=s_main)
+            rbl.cr_prep_weight_nvfp4(cd, sfd, gs, w.K, w_s8, w_sc, BT, stream=s_main)
+            rbl.cr_gemm_s8_rowscale(qx, sx, w_s8, w_sc, y2, stream=s_main)
+
+        def fused_gemm():
+            rbl.cr_gemm_nvfp4_fused(qx, sx, cd, sfd, gs, amax, w.K, y2, flags=BT, stream=s_main)
+
+        def fused_cached():
+            rbl.cr_quant_act(x, w.K, qx, sx, BT, stream=s_main)
+            fused_gemm()
+
+        t_l, t_s = time_loop(torch, layer, s_main, n=n), time_loop(torch, staged, s_main, n=n)
+        same_staged = torch.equal(y, y2)
+        t_c, t_g = time_loop(torch, fused_cached, s_main, n=n), time_loop(torch, fused_gemm, s_main, n=n)
+        torch.cuda.synchronize()
+        same = same_staged and torch.equal(y, y2)
+        if t_gemm_small is None:
+            t_gemm_small = (M, t_g)
+        info["rows"][str(M)] = {
+            "path": "decode-inside-GEMM" if rbl.cr_linear_nvfp4_plan(M, w.N, w.K)[1] == 0 else "staged",
+            "layer_ms": round(t_l, 4),
+            "staged_components_ms": round(t_s, 4),
+            "fused_with_cached_row_maxima_ms": round(t_c, 4),
+            "fused_gemm_ms": round(t_g, 4),
+            "outputs_identical": bool(same),
+        }
+        del qx, sx, y, y2, ws
+    M0, tg = t_gemm_small
+    ops = FUSED_VALU_PER_ELEM * w.N * w.K_pad
+    achieved = ops / (tg * 1e-3) / 1e12
+    info["fused_roofline"] = {"kernel": f"gemm_nvfp4_fused (M={M0} N={w.N} K_pad={w.K_pad})", "bound": "alu",
+                              "achieved": round(achieved, 2), "peak": PEAK_VALU_TOPS, "unit": "Tops/s",
+                              "frac": round(achieved / PEAK_VALU_TOPS, 4),
+                              "per_element_ops": FUSED_VALU_PER_ELEM}
+    return info
+
+
 def copy_calibration(mib: int):
     import torch
     n = mib << 20
@@ -377,6 +456,12 @@ def main():
             next_info["mlp_chain_fc1_swiglu_fc2_ms"] = round(next_info["ffn_up"]["ms"] + layer_info["ffn_down"]["ms"], 4)
         del extra
 
+    short_info = None
+    rows_list = [int(v) for v in args.short_batches.split(",") if v.strip()]
+    if rows_list:
+        print(f"bench: short batches {rows_list} (decode-inside-GEMM)", file=sys.stderr, flush=True)
+        short_info = short_batches(torch, rbl, synth, dev, s_main, rows_list)
+
     dom = layers[0]
     dom_info = layer_info[dom.name]
     # per launch: algorithmic ops of one chunk's GEMM over its mean launch duration
@@ -418,6 +503,7 @@ def main():
         },
         "layers": layer_info,
         "next_shapes": next_info,
+        "short_batches": short_info,
         "wall_ms_timed_region": round(wall_ms, 2),
         "copy_gbs": round(copy_gbs, 1),
         "gemm_source_sha256_16": gemm_source_hash(),

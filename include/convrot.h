@@ -201,9 +201,15 @@ cr_status cr_gemm_s8_rowscale_bias(const int8_t *a_s8, int64_t lda, const float 
  *   max_tile_bytes  bound of one S8 weight tile (0 selects CR_DEFAULT_MAX_TILE_BYTES);
  *              tiles hold a multiple of 256 rows (at least 256).
  *   s_main     stream of the activation preparation and the GEMMs.
- *   s_aux      NULL: weight tiles are prepared on s_main (serial staging); otherwise
- *              they are prepared on s_aux, ordered against s_main by events.  On return
- *              all work is ordered before any later work on s_main.
+ *   s_aux      NULL: weight tiles are prepared on s_main (serial staging); otherwise,
+ *              when the weight takes more than one chunk, they are prepared on s_aux,
+ *              ordered against s_main by events (a single chunk is staged on s_main).
+ *              On return all work is ordered before any later work on s_main.
+ * Short batches (M <= 64) take the decode-inside-GEMM path instead: the weight's row
+ * maxima (cr_weight_amax_nvfp4), the activation preparation, then cr_gemm_nvfp4_fused,
+ * all on s_main (s_aux is not used); the workspace then holds the S8 activation, its
+ * scales and the [N] row maxima, and max_tile_bytes is not used.  Both paths give the
+ * same bits.
  */
 size_t cr_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes);
 
@@ -211,7 +217,8 @@ size_t cr_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t m
  * multiple of 256) and the number of chunks.  The bound max_tile_bytes caps a chunk; a
  * weight that fits one chunk is still split in two when the two GEMMs need no more
  * workgroup rounds over the device's compute units than one (the second chunk is then
- * prepared while the first multiplies).  Host pointers; CR_OK or an argument status. */
+ * prepared while the first multiplies).  Both are 0 for short batches (M <= 64), which
+ * decode the weight inside the GEMM.  Host pointers; CR_OK or an argument status. */
 cr_status cr_linear_nvfp4_plan(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes,
                                int64_t *rows_per_chunk, int64_t *nchunks);
 
@@ -233,6 +240,47 @@ cr_status cr_linear_nvfp4_ex(const void *x, cr_dtype x_dtype, int64_t ld_x, int 
                              int64_t N, const float *bias, void *out, cr_dtype out_dtype, int64_t ldc,
                              void *workspace, size_t ws_bytes, size_t max_tile_bytes,
                              uint32_t flags, hipStream_t s_main, hipStream_t s_aux);
+
+/*
+ * Row maxima of the rotated weight, without the codes: w_amax[n] = a = max_k |y[n, k]|,
+ * y the NVFP4 decode of row n followed by ConvRot256 (the a of the row quantization; the
+ * weight scale is a / 127).  It is what cr_gemm_nvfp4_fused needs before it can quantize a
+ * weight block on the fly (ComfyUI Turing Utils README, "Load ConvRot DiT ..." bullet: the
+ * row scale covers the whole padded row).  For a fixed weight it can be computed once and
+ * kept ([N] floats).
+ *   w_fp4, ld_fp4, w_sf, ld_sf, global_scale, n_rows, K   as in cr_prep_weight_nvfp4.
+ *   w_amax   [n_rows] float out, 4-byte aligned.
+ *   flags    CR_FLAG_NONE or CR_FLAG_FORCE_TWO_PASS (CR_FLAG_BLOCK_TRANSPOSED is accepted
+ *            and changes nothing).
+ */
+cr_status cr_weight_amax_nvfp4(const uint8_t *w_fp4, int64_t ld_fp4,
+                               const uint8_t *w_sf, int64_t ld_sf,
+                               const float *global_scale, int64_t n_rows, int64_t K,
+                               float *w_amax, uint32_t flags, hipStream_t stream);
+
+/*
+ * Decode-inside-GEMM (the weight's S8 codes and scales are never stored): the result of
+ * cr_gemm_s8_rowscale_bias on b_s8, b_scale = cr_prep_weight_nvfp4(W), bit for bit, computed
+ * by decoding, rotating and quantizing each 256-column block of the NVFP4 weight inside the
+ * GEMM (same bullet: the weight is decoded, rotated and quantized per call).  Every
+ * workgroup repeats the decode for its 32 weight rows once per 128 activation rows, so this
+ * is the path for short batches (M up to a few hundred); for long ones, prepare the weight
+ * once and use cr_gemm_s8_rowscale.
+ *   a_s8 [M, lda], a_scale [M]   the prepared activation (cr_quant_act and variants), in
+ *                natural column order, or block-transposed with CR_FLAG_BLOCK_TRANSPOSED.
+ *   w_fp4, ld_fp4, w_sf, ld_sf, global_scale, K   the NVFP4 weight [N, K] as above.
+ *   w_amax       [N] float from cr_weight_amax_nvfp4 on the same weight.
+ *   bias         [N] float or NULL, as in cr_gemm_s8_rowscale_bias.
+ *   c [M, ldc] of c_dtype (CR_I32: the raw accumulator, a_scale may be NULL, no bias).
+ *   flags        CR_FLAG_NONE or CR_FLAG_BLOCK_TRANSPOSED (the order of a_s8);
+ *                CR_FLAG_FORCE_TWO_PASS is accepted and changes nothing.
+ * M is at most 8388480 (65535 workgroup rows of 128).
+ */
+cr_status cr_gemm_nvfp4_fused(const int8_t *a_s8, int64_t lda, const float *a_scale,
+                              const uint8_t *w_fp4, int64_t ld_fp4,
+                              const uint8_t *w_sf, int64_t ld_sf, const float *global_scale,
+                              const float *w_amax, const float *bias, int64_t M, int64_t N, int64_t K,
+                              void *c, cr_dtype c_dtype, int64_t ldc, uint32_t flags, hipStream_t stream);
 
 #ifdef __cplusplus
 }

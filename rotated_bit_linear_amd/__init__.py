@@ -70,6 +70,9 @@ def lib() -> C.CDLL:
                                           vp, C.c_int, i64, vp, sz, sz, u32, vp, vp]),
             "cr_linear_nvfp4_ex": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, vp, i64, vp, i64, vp,
                                              i64, vp, vp, C.c_int, i64, vp, sz, sz, u32, vp, vp]),
+            "cr_weight_amax_nvfp4": (C.c_int, [vp, i64, vp, i64, vp, i64, i64, vp, u32, vp]),
+            "cr_gemm_nvfp4_fused": (C.c_int, [vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, i64, i64, i64, vp,
+                                              C.c_int, i64, u32, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -214,6 +217,24 @@ def cr_linear_nvfp4(x, K, swiglu, w_fp4, w_sf, global_scale, out, workspace, max
             _ptr(w_sf), ld_sf, _ptr(global_scale), N, _ptr(bias), _ptr(out), _TORCH_TO_CR[out.dtype], ldc, *ws))
 
 
+def cr_weight_amax_nvfp4(w_fp4, w_sf, global_scale, K, w_amax, flags=0, stream=None):
+    n, ld_fp4 = _rows_ld(w_fp4)
+    _, ld_sf = _rows_ld(w_sf)
+    _check("cr_weight_amax_nvfp4", lib().cr_weight_amax_nvfp4(
+        _ptr(w_fp4), ld_fp4, _ptr(w_sf), ld_sf, _ptr(global_scale), n, K, _ptr(w_amax), flags, _stream(stream)))
+
+
+def cr_gemm_nvfp4_fused(a_s8, a_scale, w_fp4, w_sf, global_scale, w_amax, K, c, bias=None, flags=0,
+                        stream=None):
+    M, lda = _rows_ld(a_s8)
+    N, ld_fp4 = _rows_ld(w_fp4)
+    _, ld_sf = _rows_ld(w_sf)
+    _, ldc = _rows_ld(c)
+    _check("cr_gemm_nvfp4_fused", lib().cr_gemm_nvfp4_fused(
+        _ptr(a_s8), lda, _ptr(a_scale), _ptr(w_fp4), ld_fp4, _ptr(w_sf), ld_sf, _ptr(global_scale),
+        _ptr(w_amax), _ptr(bias), M, N, K, _ptr(c), _TORCH_TO_CR[c.dtype], ldc, flags, _stream(stream)))
+
+
 # ---------------------------------------------------------------- conveniences ----
 
 def quant_act(x: torch.Tensor, K: int | None = None, swiglu: bool = False, flags: int = 0,
@@ -263,3 +284,18 @@ def linear_nvfp4(x, w_fp4, w_sf, global_scale, K, out_dtype=torch.bfloat16, swig
     cr_linear_nvfp4(x, K, swiglu, w_fp4, w_sf, global_scale, out, workspace, max_tile_bytes, flags,
                     aux_stream=aux_stream, pre_scale=pre_scale, bias=bias)
     return out
+
+
+def weight_amax_nvfp4(w_fp4: torch.Tensor, w_sf: torch.Tensor, global_scale: torch.Tensor, K: int,
+                      flags: int = 0) -> torch.Tensor:
+    """[N] fp32 row maxima of the rotated weight (input of gemm_nvfp4_fused)."""
+    a = torch.empty(w_fp4.shape[0], dtype=torch.float32, device=w_fp4.device)
+    cr_weight_amax_nvfp4(w_fp4, w_sf, global_scale, K, a, flags)
+    return a
+
+
+def gemm_nvfp4_fused(a_s8, a_scale, w_fp4, w_sf, global_scale, w_amax, K, out_dtype=torch.bfloat16,
+                     bias=None, flags=0):
+    c = torch.empty(a_s8.shape[0], w_fp4.shape[0], dtype=out_dtype, device=a_s8.device)
+    cr_gemm_nvfp4_fused(a_s8, a_scale, w_fp4, w_sf, global_scale, w_amax, K, c, bias, flags)
+    return c

@@ -112,11 +112,43 @@ cr_status check_gemm(const int8_t *a, int64_t lda, const float *sa, const int8_t
     return CR_OK;
 }
 
+cr_status check_fused(const int8_t *a_s8, int64_t lda, const float *a_scale, const uint8_t *w_fp4,
+                      int64_t ld_fp4, const uint8_t *w_sf, int64_t ld_sf, const float *g, const float *w_amax,
+                      const float *bias, int64_t M, int64_t N, int64_t K, void *c, cr_dtype c_dtype, int64_t ldc,
+                      uint32_t flags)
+{
+    if (!a_s8 || !w_fp4 || !w_sf || !g || !w_amax || !c) return CR_ERR_INVALID_ARG;
+    if (c_dtype != CR_BF16 && c_dtype != CR_FP16 && c_dtype != CR_FP32 && c_dtype != CR_I32)
+        return CR_ERR_UNSUPPORTED_DTYPE;
+    if (c_dtype != CR_I32 && !a_scale) return CR_ERR_INVALID_ARG;
+    if (bias && c_dtype == CR_I32) return CR_ERR_INVALID_ARG;
+    if (M < 1 || N < 1 || K < 1 || M > kMaxRows || N > kMaxRows) return CR_ERR_INVALID_ARG;
+    if (check_flags(flags) != CR_OK) return CR_ERR_INVALID_ARG;
+    const int64_t kp = pad256(K);
+    if (kp > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
+    if ((M + 127) / 128 > 65535) return CR_ERR_TOO_LARGE;
+    if (lda < kp || ld_fp4 < (K + 1) / 2 || ld_sf < (K + 15) / 16 || ldc < N) return CR_ERR_INVALID_ARG;
+    if (!aligned(a_s8, 16) || lda % 16 != 0) return CR_ERR_MISALIGNED;
+    if (!aligned(w_fp4, 16) || ld_fp4 % 16 != 0) return CR_ERR_MISALIGNED;
+    if (!aligned(g, 4) || !aligned(w_amax, 4)) return CR_ERR_MISALIGNED;
+    if ((a_scale && !aligned(a_scale, 4)) || (bias && !aligned(bias, 4))) return CR_ERR_MISALIGNED;
+    if (!aligned(c, (size_t)elem_size(c_dtype))) return CR_ERR_MISALIGNED;
+    return CR_OK;
+}
+
+// Batches of at most this many activation rows run the layer with the weight decoded
+// inside the GEMM (row-maximum pass, then cr_gemm_nvfp4_fused) instead of staging S8
+// weight tiles: with so few rows the decode dominates either way, and the staged path
+// adds the S8 write and read of the whole weight and a GEMM with few output tiles.
+constexpr int64_t kFusedMaxRows = 64;
+
 // Workspace layout of cr_linear_nvfp4 (every region 256-byte aligned):
-//   x_s8 [M, K_pad] | x_scale [M] | tile0 [R, K_pad] | tscale0 [R] | tile1 | tscale1
+//   staged: x_s8 [M, K_pad] | x_scale [M] | tile0 [R, K_pad] | tscale0 [R] | tile1 | tscale1
+//   fused:  x_s8 [M, K_pad] | x_scale [M] | w_amax [N]
 struct LayerPlan {
+    bool fused;
     int64_t K_pad, R, nchunks;
-    size_t off_xscale, off_tile[2], off_tscale[2], bytes;
+    size_t off_xscale, off_tile[2], off_tscale[2], off_amax, bytes;
 };
 
 inline size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -157,6 +189,13 @@ LayerPlan plan_layer(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes)
     LayerPlan p{};
     if (max_tile_bytes == 0) max_tile_bytes = CR_DEFAULT_MAX_TILE_BYTES;
     p.K_pad = pad256(K);
+    if (M <= kFusedMaxRows) {
+        p.fused = true;
+        p.off_xscale = up256((size_t)M * (size_t)p.K_pad);
+        p.off_amax = up256(p.off_xscale + (size_t)M * 4);
+        p.bytes = up256(p.off_amax + (size_t)N * 4);
+        return p;
+    }
     p.R = plan_rows(M, N, p.K_pad, max_tile_bytes, current_cus());
     p.nchunks = (N + p.R - 1) / p.R;
     size_t off = up256((size_t)M * (size_t)p.K_pad);
@@ -287,6 +326,39 @@ cr_status cr_gemm_s8_rowscale(const int8_t *a_s8, int64_t lda, const float *a_sc
                                     c_dtype, ldc, stream);
 }
 
+cr_status cr_weight_amax_nvfp4(const uint8_t *w_fp4, int64_t ld_fp4, const uint8_t *w_sf, int64_t ld_sf,
+                               const float *global_scale, int64_t n_rows, int64_t K, float *w_amax,
+                               uint32_t flags, hipStream_t stream)
+{
+    if (!w_fp4 || !w_sf || !global_scale || !w_amax) return CR_ERR_INVALID_ARG;
+    if (n_rows < 1 || K < 1 || n_rows > kMaxRows) return CR_ERR_INVALID_ARG;
+    if (check_flags(flags) != CR_OK) return CR_ERR_INVALID_ARG;
+    if (pad256(K) > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
+    if (ld_fp4 < (K + 1) / 2 || ld_sf < (K + 15) / 16) return CR_ERR_INVALID_ARG;
+    if (!aligned(w_fp4, 16) || ld_fp4 % 16 != 0) return CR_ERR_MISALIGNED;
+    if (!aligned(global_scale, 4) || !aligned(w_amax, 4)) return CR_ERR_MISALIGNED;
+    cr_status s = current_device_ok();
+    if (s != CR_OK) return s;
+    return from_hip(convrot::launch_weight_amax(w_fp4, ld_fp4, w_sf, ld_sf, global_scale, n_rows, K, w_amax,
+                                                (flags & CR_FLAG_FORCE_TWO_PASS) != 0, stream));
+}
+
+cr_status cr_gemm_nvfp4_fused(const int8_t *a_s8, int64_t lda, const float *a_scale,
+                              const uint8_t *w_fp4, int64_t ld_fp4, const uint8_t *w_sf, int64_t ld_sf,
+                              const float *global_scale, const float *w_amax, const float *bias,
+                              int64_t M, int64_t N, int64_t K, void *c, cr_dtype c_dtype, int64_t ldc,
+                              uint32_t flags, hipStream_t stream)
+{
+    cr_status s0 = check_fused(a_s8, lda, a_scale, w_fp4, ld_fp4, w_sf, ld_sf, global_scale, w_amax, bias, M, N, K,
+                               c, c_dtype, ldc, flags);
+    if (s0 != CR_OK) return s0;
+    cr_status s = current_device_ok();
+    if (s != CR_OK) return s;
+    return from_hip(convrot::launch_gemm_nvfp4_fused(a_s8, lda, a_scale, w_fp4, ld_fp4, w_sf, ld_sf, global_scale,
+                                                     w_amax, bias, M, N, K, c, (int)c_dtype, ldc,
+                                                     (flags & CR_FLAG_BLOCK_TRANSPOSED) != 0, stream));
+}
+
 cr_status cr_linear_nvfp4_plan(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes,
                                int64_t *rows_per_chunk, int64_t *nchunks)
 {
@@ -324,6 +396,29 @@ cr_status cr_linear_nvfp4_ex(const void *x, cr_dtype x_dtype, int64_t ld_x, int 
     int8_t *ws = static_cast<int8_t *>(workspace);
     int8_t *x_s8 = ws;
     float *x_scale = reinterpret_cast<float *>(ws + p.off_xscale);
+    if (p.fused) {
+        float *w_amax = reinterpret_cast<float *>(ws + p.off_amax);
+        cr_status s = check_act(x, x_dtype, ld_x, M, K, swiglu ? 2 * K : K, x_s8, p.K_pad, x_scale, flags);
+        if (s != CR_OK) return s;
+        s = check_fused(x_s8, p.K_pad, x_scale, w_fp4, ld_fp4, w_sf, ld_sf, global_scale, w_amax, bias, M, N, K,
+                        out, out_dtype, ldc, flags);
+        if (s != CR_OK) return s;
+        if (pre_scale && !aligned(pre_scale, 4)) return CR_ERR_MISALIGNED;
+        if ((s = current_device_ok()) != CR_OK) return s;
+        const bool tp = (flags & CR_FLAG_FORCE_TWO_PASS) != 0;
+        // all three launches on s_main: they are short, kernels running side by side on
+        // this chip take as long as one after the other, and the two cross-stream waits
+        // would cost more than the whole activation preparation
+        if (convrot::launch_weight_amax(w_fp4, ld_fp4, w_sf, ld_sf, global_scale, N, K, w_amax, tp, s_main) != hipSuccess)
+            return CR_ERR_LAUNCH;
+        hipError_t e = swiglu
+            ? convrot::launch_quant_act_swiglu(x, (int)x_dtype, ld_x, M, K, pre_scale, x_s8, p.K_pad, x_scale, tp, true, s_main)
+            : convrot::launch_quant_act(x, (int)x_dtype, ld_x, M, K, pre_scale, x_s8, p.K_pad, x_scale, tp, true, s_main);
+        if (e != hipSuccess) return CR_ERR_LAUNCH;
+        return from_hip(convrot::launch_gemm_nvfp4_fused(x_s8, p.K_pad, x_scale, w_fp4, ld_fp4, w_sf, ld_sf,
+                                                         global_scale, w_amax, bias, M, N, K, out, (int)out_dtype,
+                                                         ldc, true, s_main));
+    }
     int8_t *tile[2] = {ws + p.off_tile[0], ws + p.off_tile[1]};
     float *tscale[2] = {reinterpret_cast<float *>(ws + p.off_tscale[0]),
                         reinterpret_cast<float *>(ws + p.off_tscale[1])};
@@ -341,8 +436,11 @@ cr_status cr_linear_nvfp4_ex(const void *x, cr_dtype x_dtype, int64_t ld_x, int 
 
     const bool tp = (flags & CR_FLAG_FORCE_TWO_PASS) != 0;
     const int64_t es = elem_size(out_dtype);
-    // with a second stream the first weight tile is prepared while the activation is
-    const bool overlap = s_aux != nullptr && s_aux != s_main;
+    // with a second stream and several chunks, chunk c+1 is prepared while chunk c
+    // multiplies (and the first while the activation is prepared); a single chunk has only
+    // the activation preparation to run beside, which gains nothing on this chip, while the
+    // two cross-stream waits cost about as much as a small layer's activation preparation
+    const bool overlap = s_aux != nullptr && s_aux != s_main && p.nchunks > 1;
     EventSet evs(overlap);
     if (overlap && !evs.ok) return CR_ERR_LAUNCH;
     hipEvent_t ev_start = evs.ev[0], ev_prep[2] = {evs.ev[1], evs.ev[2]}, ev_gemm[2] = {evs.ev[3], evs.ev[4]};

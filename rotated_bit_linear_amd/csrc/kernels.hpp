@@ -33,4 +33,15 @@ hipError_t launch_gemm_s8(const int8_t *A, int64_t lda, const float *sa, const i
                           const float *sb, const float *bias, int64_t M, int64_t N, int64_t K_pad, void *C,
                           int out_dtype, int64_t ldc, hipStream_t st);
 
+// row maximum a = max |rotated row| of NVFP4 weight rows (no codes)
+hipError_t launch_weight_amax(const uint8_t *codes, int64_t ld_codes, const uint8_t *sf, int64_t ld_sf,
+                              const float *g, int64_t n_rows, int64_t K, float *amax, bool two_pass,
+                              hipStream_t st);
+
+// decode-inside-GEMM over NVFP4 weights with given row maxima (transposed: order of A)
+hipError_t launch_gemm_nvfp4_fused(const int8_t *A, int64_t lda, const float *sa, const uint8_t *codes,
+                                   int64_t ld_codes, const uint8_t *sf, int64_t ld_sf, const float *g,
+                                   const float *amax, const float *bias, int64_t M, int64_t N, int64_t K,
+                                   void *C, int out_dtype, int64_t ldc, bool transposed, hipStream_t st);
+
 }  // namespace convrot

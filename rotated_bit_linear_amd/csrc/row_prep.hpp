@@ -238,7 +238,7 @@ __host__ __device__ constexpr size_t row_prep_lds_bytes(int threads)
 template <class Loader, int RB>
 __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, int nb,
                                               int8_t *__restrict__ out, int64_t ld_out,
-                                              float *__restrict__ scale_out, bool natural)
+                                              float *__restrict__ scale_out, bool natural, bool amax_only)
 {
     extern __shared__ float lds[];
     const int tid = threadIdx.x;
@@ -274,7 +274,12 @@ __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, 
                 for (int i = 0; i < 16; i++) zmax = fmaxf(zmax, fabsf(v[q][i]));
             }
         }
-        const RowQuant rq = row_quant(block_max(zmax, red + 16 * parity));
+        const float zrow = block_max(zmax, red + 16 * parity);
+        if (amax_only) {                           // a = max |z * 0.0625|, no codes
+            if (tid == 0) scale_out[row] = zrow * 0.0625f;
+            return;
+        }
+        const RowQuant rq = row_quant(zrow);
         int8_t *orow = out + row * ld_out;
 #pragma unroll
         for (int q = 0; q < RB; q++) {
@@ -351,7 +356,8 @@ __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, 
 template <class Loader>
 __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row, int nb,
                                                   int8_t *__restrict__ out, int64_t ld_out,
-                                                  float *__restrict__ scale_out, bool natural)
+                                                  float *__restrict__ scale_out, bool natural,
+                                                  bool amax_only)
 {
     extern __shared__ float lds[];
     const int tid = threadIdx.x;
@@ -382,7 +388,12 @@ __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row,
 #pragma unroll
         for (int i = 0; i < 16; i++) zmax = fmaxf(zmax, fabsf(v[i]));
     }
-    const RowQuant rq = row_quant(block_max(zmax, red));
+    const float zrow = block_max(zmax, red);
+    if (amax_only) {
+        if (tid == 0) scale_out[row] = zrow * 0.0625f;
+        return;
+    }
+    const RowQuant rq = row_quant(zrow);
     for (int s = 0; s < nslices; s++) {
         const int b = s * G + grp;
         load(b, v);
@@ -393,15 +404,17 @@ __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row,
 }
 
 // Kernel body shared by all loaders.
-// mode: bit 0 two-pass, bit 1 block-transposed code order
+// mode: bit 0 two-pass, bit 1 block-transposed code order, bit 2 row maximum only (the
+// row's a = max |y| goes to scale_out; no codes are written and `out` is not used)
 template <class Loader, int RB>
 __device__ __forceinline__ void row_prep_kernel_body(const Loader &ld, int64_t n_rows, int nb,
                                                      int8_t *__restrict__ out, int64_t ld_out,
                                                      float *__restrict__ scale_out, int mode)
 {
     const bool natural = (mode & 2) == 0;
-    if (mode & 1) row_prep_two_pass(ld, (int64_t)blockIdx.x, nb, out, ld_out, scale_out, natural);
-    else row_prep_rows<Loader, RB>(ld, n_rows, nb, out, ld_out, scale_out, natural);
+    const bool amax_only = (mode & 4) != 0;
+    if (mode & 1) row_prep_two_pass(ld, (int64_t)blockIdx.x, nb, out, ld_out, scale_out, natural, amax_only);
+    else row_prep_rows<Loader, RB>(ld, n_rows, nb, out, ld_out, scale_out, natural, amax_only);
 }
 
 // Launch shape of a row of nb blocks.  Up to 32 blocks, one block per 16-lane group; up

@@ -75,6 +75,9 @@ WORKLOADS = {
                          note="out_proj [5376,7168] at M=19989"),
     "ffn_up": Workload("ffn_up", 19989, 28672, 5376, DT_BF16, (DT_BF16,), 6,
                        note="fc1 [28672,5376] at M=19989"),
+    # a short batch of the same QKV layer: the shape where the weight decode dominates
+    "qkv_m128": Workload("qkv_m128", 128, 21504, 5376, DT_BF16, (DT_BF16,), 7,
+                         outlier_frac=0.01, note="qkv_proj [21504,5376] at M=128"),
 }
 
 # The MLP of one block as a chain: fc1 (ffn_up) writes H [M, 28672] in bf16, which the

@@ -124,12 +124,12 @@ def test_gemm_validation():
 
 def test_layer_validation_and_workspace():
     L = rbl.lib()
-    ws = L.cr_linear_nvfp4_workspace_bytes(64, 256, 512, 0)
-    assert ws >= 64 * 512 + 64 * 4 + 256 * 512 + 256 * 4
+    ws = L.cr_linear_nvfp4_workspace_bytes(65, 256, 512, 0)
+    assert ws >= 65 * 512 + 65 * 4 + 256 * 512 + 256 * 4
     big = L.cr_linear_nvfp4_workspace_bytes(19989, 21504, 5376, 16 << 20)
     one = L.cr_linear_nvfp4_workspace_bytes(19989, 21504, 5376, 0)
     assert big < one                            # 16 MiB tiles: two 3072-row tiles
-    args = dict(x=A16, dt=0, ldx=512, sw=0, M=64, K=512, w=A16, ldw=256, sf=A16, ldsf=32, g=A16, N=256,
+    args = dict(x=A16, dt=0, ldx=512, sw=0, M=65, K=512, w=A16, ldw=256, sf=A16, ldsf=32, g=A16, N=256,
                 out=A16, odt=0, ldc=256, ws=0x100000, wsb=ws, mt=0, fl=0)
 
     def call(**kw):
@@ -142,6 +142,16 @@ def test_layer_validation_and_workspace():
     assert call(odt=3) == DT
     assert call(ldc=255) == INV
     assert call(sw=1) == INV                       # SwiGLU needs ld_x >= 2K
+    # the short-batch (decode-inside-GEMM) path validates the same way
+    wsf = L.cr_linear_nvfp4_workspace_bytes(64, 256, 512, 0)
+    assert wsf == 64 * 512 + 256 + 1024
+    assert call(M=64, wsb=wsf - 1) == BIG
+    assert call(M=64, wsb=wsf, ws=0x100010) == MIS
+    assert call(M=64, wsb=wsf, odt=3) == DT
+    assert call(M=64, wsb=wsf, ldc=255) == INV
+    assert call(M=64, wsb=wsf, sw=1) == INV
+    assert call(M=64, wsb=wsf, ldw=264) == MIS
+    assert call(M=64, wsb=wsf, fl=4) == INV
 
 
 def test_layer_chunk_plan():
@@ -154,11 +164,16 @@ def test_layer_chunk_plan():
     # FFN down (N 5376): 79 x 21 tiles take 7 rounds, halves 4 + 4: not split.
     assert rbl.cr_linear_nvfp4_plan(19989, 5376, 14336) == (5376, 1)
     # one tile row of workgroups: a split would double the rounds
-    assert rbl.cr_linear_nvfp4_plan(64, 512, 256) == (512, 1)
+    assert rbl.cr_linear_nvfp4_plan(65, 512, 256) == (512, 1)
     assert rbl.cr_linear_nvfp4_plan(8192, 5000, 20000) == (5120, 1)
+    # short batches decode the weight inside the GEMM: no chunks, a workspace of the S8
+    # activation, its scales and the [N] row maxima (256-byte aligned regions)
+    assert rbl.cr_linear_nvfp4_plan(64, 512, 256) == (0, 0)
+    assert rbl.cr_linear_nvfp4_plan(1, 21504, 5376) == (0, 0)
+    assert rbl.cr_linear_nvfp4_workspace_bytes(64, 512, 256) == 64 * 256 + 256 + 2048
+    assert rbl.cr_linear_nvfp4_workspace_bytes(1, 1, 1) == 256 + 256 + 256
     # the tile bound chunks first: 16 MiB / 5376 B per row -> 3072 rows
     assert rbl.cr_linear_nvfp4_plan(19989, 21504, 5376, 16 << 20) == (3072, 7)
-    assert rbl.cr_linear_nvfp4_plan(1, 1, 1) == (256, 1)
     # a bound below one tile height still gives one 256-row chunk
     assert rbl.cr_linear_nvfp4_plan(300, 1000, 5376, 1) == (256, 4)
     with pytest.raises(rbl.CrError):
@@ -167,8 +182,55 @@ def test_layer_chunk_plan():
         rbl.cr_linear_nvfp4_plan(1, 256, rbl.CR_MAX_K_PAD + 1)
 
 
+def wa(codes=A16, ld=256, sf=A16, ld_sf=32, g=A16, n=8, K=512, a=A16, flags=0):
+    return rbl.lib().cr_weight_amax_nvfp4(codes, ld, sf, ld_sf, g, n, K, a, flags, ST)
+
+
+def test_weight_amax_validation():
+    assert wa(a=None) == INV
+    assert wa(g=None) == INV
+    assert wa(n=0) == INV
+    assert wa(ld=200) == INV               # < ceil(K/2)
+    assert wa(ld_sf=31) == INV             # < ceil(K/16)
+    assert wa(ld=264) == MIS
+    assert wa(a=A16 + 2) == MIS
+    assert wa(K=CR_BIG, ld=CR_BIG, ld_sf=CR_BIG) == BIG
+    assert wa(flags=4) == INV
+
+
+def fz(a=A16, lda=512, sa=A16, codes=A16, ld=256, sf=A16, ld_sf=32, g=A16, am=A16, bias=None, M=8, N=40,
+       K=512, c=A16, dt=0, ldc=40, flags=0):
+    return rbl.lib().cr_gemm_nvfp4_fused(a, lda, sa, codes, ld, sf, ld_sf, g, am, bias, M, N, K, c, dt, ldc,
+                                         flags, ST)
+
+
+def test_gemm_fused_validation():
+    assert fz(am=None) == INV
+    assert fz(a=None) == INV
+    assert fz(sa=None) == INV              # scales needed unless int32 out
+    assert fz(dt=3, bias=A16) == INV       # no bias on the raw accumulator
+    assert fz(dt=7) == DT
+    assert fz(M=0) == INV
+    assert fz(lda=256) == INV              # < K_pad
+    assert fz(ld=200) == INV
+    assert fz(ldc=39) == INV
+    assert fz(lda=520) == MIS
+    assert fz(c=A16 + 1) == MIS
+    assert fz(bias=A16 + 2) == MIS
+    assert fz(K=CR_BIG, lda=CR_BIG + 256, ld=CR_BIG, ld_sf=CR_BIG) == BIG
+    assert fz(M=128 * 65535 + 1) == BIG    # workgroup rows of 128 activation rows
+    assert fz(flags=4) == INV
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="valid arguments would launch on a real GPU")
 def test_valid_arguments_report_no_device_without_gpu():
     assert qa() == NODEV
     assert pw() == NODEV
     assert gm() == NODEV
+    assert wa() == NODEV
+    assert fz() == NODEV
+    L = rbl.lib()
+    ws = L.cr_linear_nvfp4_workspace_bytes(64, 256, 512, 0)
+    assert L.cr_linear_nvfp4(A16, 0, 512, 0, 64, 512, A16, 256, A16, 32, A16, 256, A16, 0, 256, 0x100000, ws, 0, 0,
+                             ST, None) == NODEV
+    assert fz(dt=3, sa=None) == NODEV
