@@ -287,9 +287,10 @@ def copy_bandwidth(torch, stream) -> float:
 
 def short_batches(torch, rbl, synth, dev, s_main, rows_list, n=20):
     """The QKV weight [21504, 5376] at short batches: the layer as cr_linear_nvfp4 runs it
-    (decode-inside-GEMM up to 64 rows, staged tiles above), the staged components one after
-    the other (activation prep, whole-weight prep, GEMM), and the fused GEMM with the weight's
-    row maxima computed once, as for a fixed weight.  Returns the per-batch times and the
+    (decode-inside-GEMM up to 64 rows, staged tiles above), the same call captured into a HIP
+    graph and replayed, the staged components one after the other (activation prep,
+    whole-weight prep, GEMM), and the fused GEMM with the weight's row maxima computed once,
+    as for a fixed weight.  Returns the per-batch times and the
     fused kernel's vector-issue roofline at the smallest batch."""
     w = synth.WORKLOADS["qkv_m128"]
     p = synth.make_weight_nvfp4(w)
@@ -329,6 +330,14 @@ def short_batches(torch, rbl, synth, dev, s_main, rows_list, n=20):
 
         t_l, t_s = time_loop(torch, layer, s_main, n=n), time_loop(torch, staged, s_main, n=n)
         same_staged = torch.equal(y, y2)
+        # the same layer call captured once into a HIP graph and replayed
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            rbl.cr_linear_nvfp4(x, w.K, False, cd, sfd, gs, y, ws, aux_stream=aux)
+        t_gr = time_loop(torch, graph.replay, s_main, n=n)
+        torch.cuda.synchronize()
+        same_staged = same_staged and torch.equal(y, y2)
+        del graph
         t_c, t_g = time_loop(torch, fused_cached, s_main, n=n), time_loop(torch, fused_gemm, s_main, n=n)
         torch.cuda.synchronize()
         same = same_staged and torch.equal(y, y2)
@@ -337,6 +346,7 @@ def short_batches(torch, rbl, synth, dev, s_main, rows_list, n=20):
         info["rows"][str(M)] = {
             "path": "decode-inside-GEMM" if rbl.cr_linear_nvfp4_plan(M, w.N, w.K)[1] == 0 else "staged",
             "layer_ms": round(t_l, 4),
+            "layer_graph_replay_ms": round(t_gr, 4),
             "staged_components_ms": round(t_s, 4),
             "fused_with_cached_row_maxima_ms": round(t_c, 4),
             "fused_gemm_ms": round(t_g, 4),
