@@ -205,11 +205,11 @@ cr_status cr_gemm_s8_rowscale_bias(const int8_t *a_s8, int64_t lda, const float 
  *              when the weight takes more than one chunk, they are prepared on s_aux,
  *              ordered against s_main by events (a single chunk is staged on s_main).
  *              On return all work is ordered before any later work on s_main.
- * Short batches (M <= 64) take the decode-inside-GEMM path instead: the weight's row
- * maxima (cr_weight_amax_nvfp4), the activation preparation, then cr_gemm_nvfp4_fused,
- * all on s_main (s_aux is not used); the workspace then holds the S8 activation, its
- * scales and the [N] row maxima, and max_tile_bytes is not used.  Both paths give the
- * same bits.
+ * Short batches (M <= 64) take the decode-inside-GEMM path instead: the activation
+ * preparation, then cr_gemm_nvfp4_fused with w_amax NULL (the row maxima from its own
+ * first pass), both on s_main (s_aux is not used); the workspace then holds the S8
+ * activation and its scales, and max_tile_bytes is not used.  Both paths give the same
+ * bits.
  */
 size_t cr_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes);
 
@@ -269,7 +269,9 @@ cr_status cr_weight_amax_nvfp4(const uint8_t *w_fp4, int64_t ld_fp4,
  *   a_s8 [M, lda], a_scale [M]   the prepared activation (cr_quant_act and variants), in
  *                natural column order, or block-transposed with CR_FLAG_BLOCK_TRANSPOSED.
  *   w_fp4, ld_fp4, w_sf, ld_sf, global_scale, K   the NVFP4 weight [N, K] as above.
- *   w_amax       [N] float from cr_weight_amax_nvfp4 on the same weight.
+ *   w_amax       [N] float from cr_weight_amax_nvfp4 on the same weight, or NULL: then the
+ *                kernel finds the row maxima itself in a first pass over the weight (decode
+ *                and rotation only; every workgroup for its own 32 rows).
  *   bias         [N] float or NULL, as in cr_gemm_s8_rowscale_bias.
  *   c [M, ldc] of c_dtype (CR_I32: the raw accumulator, a_scale may be NULL, no bias).
  *   flags        CR_FLAG_NONE or CR_FLAG_BLOCK_TRANSPOSED (the order of a_s8);

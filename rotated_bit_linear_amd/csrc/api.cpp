@@ -117,7 +117,7 @@ cr_status check_fused(const int8_t *a_s8, int64_t lda, const float *a_scale, con
                       const float *bias, int64_t M, int64_t N, int64_t K, void *c, cr_dtype c_dtype, int64_t ldc,
                       uint32_t flags)
 {
-    if (!a_s8 || !w_fp4 || !w_sf || !g || !w_amax || !c) return CR_ERR_INVALID_ARG;
+    if (!a_s8 || !w_fp4 || !w_sf || !g || !c) return CR_ERR_INVALID_ARG;
     if (c_dtype != CR_BF16 && c_dtype != CR_FP16 && c_dtype != CR_FP32 && c_dtype != CR_I32)
         return CR_ERR_UNSUPPORTED_DTYPE;
     if (c_dtype != CR_I32 && !a_scale) return CR_ERR_INVALID_ARG;
@@ -130,25 +130,25 @@ cr_status check_fused(const int8_t *a_s8, int64_t lda, const float *a_scale, con
     if (lda < kp || ld_fp4 < (K + 1) / 2 || ld_sf < (K + 15) / 16 || ldc < N) return CR_ERR_INVALID_ARG;
     if (!aligned(a_s8, 16) || lda % 16 != 0) return CR_ERR_MISALIGNED;
     if (!aligned(w_fp4, 16) || ld_fp4 % 16 != 0) return CR_ERR_MISALIGNED;
-    if (!aligned(g, 4) || !aligned(w_amax, 4)) return CR_ERR_MISALIGNED;
+    if (!aligned(g, 4) || (w_amax && !aligned(w_amax, 4))) return CR_ERR_MISALIGNED;
     if ((a_scale && !aligned(a_scale, 4)) || (bias && !aligned(bias, 4))) return CR_ERR_MISALIGNED;
     if (!aligned(c, (size_t)elem_size(c_dtype))) return CR_ERR_MISALIGNED;
     return CR_OK;
 }
 
 // Batches of at most this many activation rows run the layer with the weight decoded
-// inside the GEMM (row-maximum pass, then cr_gemm_nvfp4_fused) instead of staging S8
-// weight tiles: with so few rows the decode dominates either way, and the staged path
-// adds the S8 write and read of the whole weight and a GEMM with few output tiles.
+// inside the GEMM (cr_gemm_nvfp4_fused, row maxima from its own first pass) instead of
+// staging S8 weight tiles: with so few rows the decode dominates either way, and the
+// staged path adds the S8 write and read of the whole weight and a GEMM with few tiles.
 constexpr int64_t kFusedMaxRows = 64;
 
 // Workspace layout of cr_linear_nvfp4 (every region 256-byte aligned):
 //   staged: x_s8 [M, K_pad] | x_scale [M] | tile0 [R, K_pad] | tscale0 [R] | tile1 | tscale1
-//   fused:  x_s8 [M, K_pad] | x_scale [M] | w_amax [N]
+//   fused:  x_s8 [M, K_pad] | x_scale [M]
 struct LayerPlan {
     bool fused;
     int64_t K_pad, R, nchunks;
-    size_t off_xscale, off_tile[2], off_tscale[2], off_amax, bytes;
+    size_t off_xscale, off_tile[2], off_tscale[2], bytes;
 };
 
 inline size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -192,8 +192,7 @@ LayerPlan plan_layer(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes)
     if (M <= kFusedMaxRows) {
         p.fused = true;
         p.off_xscale = up256((size_t)M * (size_t)p.K_pad);
-        p.off_amax = up256(p.off_xscale + (size_t)M * 4);
-        p.bytes = up256(p.off_amax + (size_t)N * 4);
+        p.bytes = up256(p.off_xscale + (size_t)M * 4);
         return p;
     }
     p.R = plan_rows(M, N, p.K_pad, max_tile_bytes, current_cus());
@@ -397,26 +396,23 @@ cr_status cr_linear_nvfp4_ex(const void *x, cr_dtype x_dtype, int64_t ld_x, int 
     int8_t *x_s8 = ws;
     float *x_scale = reinterpret_cast<float *>(ws + p.off_xscale);
     if (p.fused) {
-        float *w_amax = reinterpret_cast<float *>(ws + p.off_amax);
         cr_status s = check_act(x, x_dtype, ld_x, M, K, swiglu ? 2 * K : K, x_s8, p.K_pad, x_scale, flags);
         if (s != CR_OK) return s;
-        s = check_fused(x_s8, p.K_pad, x_scale, w_fp4, ld_fp4, w_sf, ld_sf, global_scale, w_amax, bias, M, N, K,
+        s = check_fused(x_s8, p.K_pad, x_scale, w_fp4, ld_fp4, w_sf, ld_sf, global_scale, nullptr, bias, M, N, K,
                         out, out_dtype, ldc, flags);
         if (s != CR_OK) return s;
         if (pre_scale && !aligned(pre_scale, 4)) return CR_ERR_MISALIGNED;
         if ((s = current_device_ok()) != CR_OK) return s;
         const bool tp = (flags & CR_FLAG_FORCE_TWO_PASS) != 0;
-        // all three launches on s_main: they are short, kernels running side by side on
-        // this chip take as long as one after the other, and the two cross-stream waits
-        // would cost more than the whole activation preparation
-        if (convrot::launch_weight_amax(w_fp4, ld_fp4, w_sf, ld_sf, global_scale, N, K, w_amax, tp, s_main) != hipSuccess)
-            return CR_ERR_LAUNCH;
+        // both launches on s_main: they are short, kernels running side by side on this
+        // chip take as long as one after the other, and cross-stream waits would cost more
+        // than the whole activation preparation
         hipError_t e = swiglu
             ? convrot::launch_quant_act_swiglu(x, (int)x_dtype, ld_x, M, K, pre_scale, x_s8, p.K_pad, x_scale, tp, true, s_main)
             : convrot::launch_quant_act(x, (int)x_dtype, ld_x, M, K, pre_scale, x_s8, p.K_pad, x_scale, tp, true, s_main);
         if (e != hipSuccess) return CR_ERR_LAUNCH;
         return from_hip(convrot::launch_gemm_nvfp4_fused(x_s8, p.K_pad, x_scale, w_fp4, ld_fp4, w_sf, ld_sf,
-                                                         global_scale, w_amax, bias, M, N, K, out, (int)out_dtype,
+                                                         global_scale, nullptr, bias, M, N, K, out, (int)out_dtype,
                                                          ldc, true, s_main));
     }
     int8_t *tile[2] = {ws + p.off_tile[0], ws + p.off_tile[1]};

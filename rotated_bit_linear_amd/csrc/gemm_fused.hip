@@ -7,9 +7,10 @@
 // ComfyUI Turing Utils README, "Load ConvRot DiT ..." bullet: weights stay packed NVFP4 in
 // memory and are decoded, rotated and quantized per call, then multiplied by the row-scaled
 // INT8 GEMM.  The row quantizer needs the row maximum a[n] = max |y[n, :]| over the whole
-// padded row before the first block can be quantized, so a is an input (from the row
-// maximum mode of the weight preparation kernel, and reusable across calls for a fixed
-// weight); the codes are then those of the plain definition, bit for bit: each block's
+// padded row before the first block can be quantized.  It is either an input (from the
+// row maximum mode of the weight preparation kernel, reusable across calls for a fixed
+// weight) or computed by a first pass of this kernel over the workgroup's band (decode and
+// rotation only).  The codes are those of the plain definition, bit for bit: each block's
 // butterflies are the same IEEE operations in the same order as in the two-step path, and
 // the code multiplier is derived from a exactly as there (a = max|z| / 16 is exact, so
 // max|z| = 16 a is recovered exactly for every row that takes the folded multiplier).
@@ -85,15 +86,9 @@ void gemm_nvfp4_fused_kernel(const int8_t *__restrict__ A, int64_t lda, const fl
 
     // ---- decode duties: band rows grp + 16 q; rows past N decode as zeros ----
     using Raw = NVFP4Loader::Raw;
-    RowQuant rq[FZ_RPG];
     bool live[FZ_RPG];
 #pragma unroll
-    for (int q = 0; q < FZ_RPG; q++) {
-        const int r = grp + FZ_GROUPS * q;
-        live[q] = n0 + r < N;
-        rq[q] = row_quant(live[q] ? amax[n0 + r] * 16.0f : 0.0f);
-        if (t == 0) sw_band[r] = rq[q].scale;
-    }
+    for (int q = 0; q < FZ_RPG; q++) live[q] = n0 + grp + FZ_GROUPS * q < N;
     auto fetch_block = [&](int b, Raw (&raw)[FZ_RPG]) {
 #pragma unroll
         for (int q = 0; q < FZ_RPG; q++) {
@@ -101,6 +96,44 @@ void gemm_nvfp4_fused_kernel(const int8_t *__restrict__ A, int64_t lda, const fl
             if (live[q]) W.fetch((int64_t)(n0 + grp + FZ_GROUPS * q), (int64_t)b * 16 + t, raw[q]);
         }
     };
+    RowQuant rq[FZ_RPG];
+    if (amax != nullptr) {
+#pragma unroll
+        for (int q = 0; q < FZ_RPG; q++) {
+            const int r = grp + FZ_GROUPS * q;
+            rq[q] = row_quant(live[q] ? amax[n0 + r] * 16.0f : 0.0f);
+        }
+    } else {
+        // pass 1: the band rows' maxima over the whole padded row.  Every block of a row
+        // is rotated by the same 16-lane group, so the maximum needs no workgroup barrier
+        // (the order of z does not matter for it: no transposition back)
+        float zm[FZ_RPG];
+        Raw raw[FZ_RPG];
+#pragma unroll
+        for (int q = 0; q < FZ_RPG; q++) zm[q] = 0.0f;
+        fetch_block(0, raw);
+        for (int b = 0; b < nb; b++) {
+            float v[FZ_RPG][16];
+#pragma unroll
+            for (int q = 0; q < FZ_RPG; q++) W.decode(raw[q], (int64_t)b * 16 + t, NVFP4Loader::Lane{}, v[q]);
+            if (b + 1 < nb) fetch_block(b + 1, raw);
+#pragma unroll
+            for (int q = 0; q < FZ_RPG; q++) {
+                hadamard256(v[q], tile, t, false);
+#pragma unroll
+                for (int i = 0; i < 16; i++) zm[q] = fmaxf(zm[q], fabsf(v[q][i]));
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < FZ_RPG; q++) {
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) zm[q] = fmaxf(zm[q], __shfl_xor(zm[q], off, 64));
+            rq[q] = row_quant(zm[q]);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < FZ_RPG; q++)
+        if (t == 0) sw_band[grp + FZ_GROUPS * q] = rq[q].scale;
     // decode (then request block b+1's bytes), rotate and quantize block b into `dst`
     auto make_block = [&](int b, Raw (&raw)[FZ_RPG], int8_t *dst) {
         float v[FZ_RPG][16];

@@ -144,7 +144,7 @@ def test_layer_validation_and_workspace():
     assert call(sw=1) == INV                       # SwiGLU needs ld_x >= 2K
     # the short-batch (decode-inside-GEMM) path validates the same way
     wsf = L.cr_linear_nvfp4_workspace_bytes(64, 256, 512, 0)
-    assert wsf == 64 * 512 + 256 + 1024
+    assert wsf == 64 * 512 + 256
     assert call(M=64, wsb=wsf - 1) == BIG
     assert call(M=64, wsb=wsf, ws=0x100010) == MIS
     assert call(M=64, wsb=wsf, odt=3) == DT
@@ -167,11 +167,11 @@ def test_layer_chunk_plan():
     assert rbl.cr_linear_nvfp4_plan(65, 512, 256) == (512, 1)
     assert rbl.cr_linear_nvfp4_plan(8192, 5000, 20000) == (5120, 1)
     # short batches decode the weight inside the GEMM: no chunks, a workspace of the S8
-    # activation, its scales and the [N] row maxima (256-byte aligned regions)
+    # activation and its scales (256-byte aligned regions)
     assert rbl.cr_linear_nvfp4_plan(64, 512, 256) == (0, 0)
     assert rbl.cr_linear_nvfp4_plan(1, 21504, 5376) == (0, 0)
-    assert rbl.cr_linear_nvfp4_workspace_bytes(64, 512, 256) == 64 * 256 + 256 + 2048
-    assert rbl.cr_linear_nvfp4_workspace_bytes(1, 1, 1) == 256 + 256 + 256
+    assert rbl.cr_linear_nvfp4_workspace_bytes(64, 512, 256) == 64 * 256 + 256
+    assert rbl.cr_linear_nvfp4_workspace_bytes(1, 1, 1) == 256 + 256
     # the tile bound chunks first: 16 MiB / 5376 B per row -> 3072 rows
     assert rbl.cr_linear_nvfp4_plan(19989, 21504, 5376, 16 << 20) == (3072, 7)
     # a bound below one tile height still gives one 256-row chunk
@@ -205,8 +205,9 @@ def fz(a=A16, lda=512, sa=A16, codes=A16, ld=256, sf=A16, ld_sf=32, g=A16, am=A1
 
 
 def test_gemm_fused_validation():
-    assert fz(am=None) == INV
     assert fz(a=None) == INV
+    assert fz(g=None) == INV
+    assert fz(am=A16 + 2) == MIS
     assert fz(sa=None) == INV              # scales needed unless int32 out
     assert fz(dt=3, bias=A16) == INV       # no bias on the raw accumulator
     assert fz(dt=7) == DT
@@ -229,6 +230,7 @@ def test_valid_arguments_report_no_device_without_gpu():
     assert gm() == NODEV
     assert wa() == NODEV
     assert fz() == NODEV
+    assert fz(am=None) == NODEV              # row maxima found by the kernel itself
     L = rbl.lib()
     ws = L.cr_linear_nvfp4_workspace_bytes(64, 256, 512, 0)
     assert L.cr_linear_nvfp4(A16, 0, 512, 0, 64, 512, A16, 256, A16, 32, A16, 256, A16, 0, 256, 0x100000, ws, 0, 0,

@@ -83,8 +83,11 @@ def test_gemm_fused_against_oracle(M, N, K):
                 tdt = synth.TORCH_DTYPE[odt]
                 full = torch.full((M, ldc), 7, dtype=tdt, device=dev())
                 c = full[:, :N]
-                say(f"cr_gemm_nvfp4_fused M={M} N={N} K={K} order={order} out={odt} bias={with_bias}")
-                rbl.cr_gemm_nvfp4_fused(qx, sx, cd, sfd, gs, amax, K, c, bias=bd if with_bias else None,
+                # row maxima given, or found by the kernel's own first pass (alternating)
+                am = amax if (odt + int(with_bias) + order) % 2 == 0 else None
+                say(f"cr_gemm_nvfp4_fused M={M} N={N} K={K} order={order} out={odt} bias={with_bias} "
+                    f"amax={'given' if am is not None else 'in-kernel'}")
+                rbl.cr_gemm_nvfp4_fused(qx, sx, cd, sfd, gs, am, K, c, bias=bd if with_bias else None,
                                         flags=order)
                 two = torch.empty(M, N, dtype=tdt, device=dev())
                 if with_bias:
@@ -117,9 +120,11 @@ def test_gemm_fused_qkv_shape_sampled(M):
     amax = rbl.weight_amax_nvfp4(cd, sfd, gs, w.K)
     qx, sx = rbl.quant_act(x.to(dev()), w.K, flags=bt)
     out = rbl.gemm_nvfp4_fused(qx, sx, cd, sfd, gs, amax, w.K, flags=bt)
+    out2 = rbl.gemm_nvfp4_fused(qx, sx, cd, sfd, gs, None, w.K, flags=bt)       # in-kernel row maxima
     acc = torch.empty(M, w.N, dtype=torch.int32, device=dev())
     rbl.cr_gemm_nvfp4_fused(qx, sx, cd, sfd, gs, amax, w.K, acc, flags=bt)
     torch.cuda.synchronize()
+    assert torch.equal(out, out2), "given and in-kernel row maxima give different outputs"
     rows = synth.sample_rows(w.N, 512, 77)
     ci, si = p.codes.numpy()[rows.numpy()], p.sf.numpy()[rows.numpy()]
     ra = oracle.weight_amax_nvfp4(ci, si, p.g, w.K)
