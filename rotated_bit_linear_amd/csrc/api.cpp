@@ -4,9 +4,11 @@
 // Layer orchestration (ComfyUI Turing Utils README, "Load ConvRot DiT ..." bullet):
 // the activation is prepared once; the weight is prepared in chunks of output rows into
 // call-local S8 tiles of bounded size (two tiles alternate), each chunk followed by the
-// GEMM that writes its column band of the output; with a second stream the preparation
-// of chunk c+1 overlaps the GEMM of chunk c, ordered by producer/consumer events.  The
-// chunking and the overlap change no value.
+// GEMM that writes its column band of the output; with a second stream and several
+// chunks, the preparation of chunk c+1 runs beside the GEMM of chunk c, ordered by
+// producer/consumer events.  Short batches skip the S8 weight altogether: the GEMM decodes
+// the weight blocks itself (decode-inside-GEMM).  Chunking, streams and the path taken
+// change no value.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
