@@ -374,7 +374,6 @@ void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__re
     const int nbase = n0 + wn * WT_N;
     float sav[FM];
     float4 sbv[FN][4];
-    float4 bbv[BIAS ? FN : 1][4];                  // bias of the same columns (BIAS only)
     auto load4 = [&](const float *v, bool v16, int n) {
         float4 r;
         if (v16 && n + 4 <= N) {
@@ -394,23 +393,30 @@ void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__re
             sav[i] = (m < M) ? sa[m] : 0.0f;
         }
         const bool sb16 = ((uintptr_t)sb % 16) == 0;
-        const bool bi16 = ((uintptr_t)bias % 16) == 0;
 #pragma unroll
         for (int j = 0; j < FN; j++)
 #pragma unroll
             for (int g = 0; g < 4; g++) {
                 const int n = nbase + j * 32 + 8 * g + 4 * fhalf;
                 sbv[j][g] = load4(sb, sb16, n);
-                if constexpr (BIAS) bbv[j][g] = load4(bias, bi16, n);
             }
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
     barrier();                                     // every wave is done with the ring
+    // the tile's GBN bias values go through LDS (past the last wave's epilogue tile) rather
+    // than 64 more registers per lane
+    constexpr int WPA = (GWAVES + 2 * GSTAGES - 1) / (2 * GSTAGES);   // waves per epilogue region
+    static_assert(WPA * EPI_BYTES + GBN * 4 <= STAGE_B, "bias area fits beside the epilogue tiles");
+    float *const bias_lds = reinterpret_cast<float *>(stB[GSTAGES - 1] + WPA * EPI_BYTES);
+    if constexpr (BIAS) {
+        const int tid_ = threadIdx.x;
+        if (tid_ < GBN) bias_lds[tid_] = (n0 + tid_ < N) ? bias[n0 + tid_] : 0.0f;
+        barrier();
+    }
     constexpr int ES = (OUT == 0 || OUT == 1) ? 2 : 4;
     constexpr int NC = 256 / ES;                   // columns per chunk
     constexpr int CHUNKS = WT_N / NC;
     static_assert(WT_N % NC == 0, "wave tile width must be whole 256-byte chunks");
-    constexpr int WPA = (GWAVES + 2 * GSTAGES - 1) / (2 * GSTAGES);   // waves per region
     static_assert(WPA * EPI_BYTES <= STAGE_A && WPA * EPI_BYTES <= STAGE_B, "epilogue tile fits the ring");
     int8_t *etile;
     switch (wave / WPA) {          // wave-uniform: a scalar branch
@@ -451,7 +457,8 @@ void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__re
                         float v0 = ((float)a0 * sav[i]) * s4.x, v1 = ((float)a1 * sav[i]) * s4.y;
                         float v2 = ((float)a2 * sav[i]) * s4.z, v3 = ((float)a3 * sav[i]) * s4.w;
                         if constexpr (BIAS) {
-                            const float4 b4 = bbv[j][g];
+                            const float4 b4 = *reinterpret_cast<const float4 *>(
+                                bias_lds + wn * WT_N + j * 32 + 8 * g + 4 * fhalf);
                             v0 = v0 + b4.x; v1 = v1 + b4.y; v2 = v2 + b4.z; v3 = v3 + b4.w;
                         }
                         if constexpr (OUT == 2) {
