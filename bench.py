@@ -363,6 +363,26 @@ def short_batches(torch, rbl, synth, dev, s_main, rows_list, n=20):
     return info
 
 
+def mfma_ceiling(torch, rbl, stream, iters=10000) -> dict:
+    """TOP/s of the register-only MFMA probe (cr_probe_mfma_i8) on random and on constant
+    int8 operands: what the power-limited matrix cores sustain with no memory traffic."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(512 * cus, dtype=torch.int32, device="cuda")
+    res = {}
+    for rnd in (True, False):
+        tops = 0.0
+        for _ in range(2):                         # the second launch is the one reported
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            ops = rbl.cr_probe_mfma_i8(rnd, iters, out, stream=stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            tops = ops / (a.elapsed_time(b) * 1e-3) / 1e12
+        res["random_int8" if rnd else "constant_int8"] = round(tops, 1)
+    del out
+    return res
+
+
 def copy_calibration(mib: int):
     import torch
     n = mib << 20
@@ -472,6 +492,9 @@ def main():
         print(f"bench: short batches {rows_list} (decode-inside-GEMM)", file=sys.stderr, flush=True)
         short_info = short_batches(torch, rbl, synth, dev, s_main, rows_list)
 
+    print("bench: register-only MFMA ceiling", file=sys.stderr, flush=True)
+    ceiling = mfma_ceiling(torch, rbl, s_main)
+
     dom = layers[0]
     dom_info = layer_info[dom.name]
     # per launch: algorithmic ops of one chunk's GEMM over its mean launch duration
@@ -510,6 +533,10 @@ def main():
             "unit": "TOP/s",
             "frac": round(achieved / PEAK_INT8_TOPS, 4),
             "traffic": traffic,
+            # what the matrix cores sustain with operands in registers (no memory traffic):
+            # random data toggles bits and meets the power limit; constant data does not
+            "measured_mfma_ceiling": ceiling,
+            "frac_of_random_data_ceiling": round(achieved / ceiling["random_int8"], 4),
         },
         "layers": layer_info,
         "next_shapes": next_info,

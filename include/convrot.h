@@ -284,6 +284,21 @@ cr_status cr_gemm_nvfp4_fused(const int8_t *a_s8, int64_t lda, const float *a_sc
                               const float *w_amax, const float *bias, int64_t M, int64_t N, int64_t K,
                               void *c, cr_dtype c_dtype, int64_t ldc, uint32_t flags, hipStream_t stream);
 
+/*
+ * Diagnostic, not part of the layer: the sustained rate of the INT8 matrix instruction the
+ * GEMM uses (v_mfma_i32_32x32x32_i8) with its operands already in registers, no memory
+ * traffic at all, on random (random_data != 0) or constant int8 data.  The matrix cores
+ * are power-limited, so toggling operand bits lower the sustained rate; this gives the
+ * ceiling a GEMM on real data can approach, beside the published dense peak.
+ *   iters      1 .. 1000000 loop iterations (16 MFMAs each, 8 waves per compute unit).
+ *   out        device buffer of at least out_elems ints, overwritten with meaningless sums;
+ *              out_elems must be >= 512 * (compute units of the current device).
+ *   ops        host pointer: the number of int8 operations (2 per multiply-add) the launch
+ *              performs; time the launch on `stream` to get the rate.
+ */
+cr_status cr_probe_mfma_i8(int random_data, int iters, int *out, size_t out_elems, double *ops,
+                           hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -71,6 +71,7 @@ def lib() -> C.CDLL:
             "cr_linear_nvfp4_ex": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, vp, i64, vp, i64, vp,
                                              i64, vp, vp, C.c_int, i64, vp, sz, sz, u32, vp, vp]),
             "cr_weight_amax_nvfp4": (C.c_int, [vp, i64, vp, i64, vp, i64, i64, vp, u32, vp]),
+            "cr_probe_mfma_i8": (C.c_int, [C.c_int, C.c_int, vp, sz, C.POINTER(C.c_double), vp]),
             "cr_gemm_nvfp4_fused": (C.c_int, [vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, i64, i64, i64, vp,
                                               C.c_int, i64, u32, vp]),
         }
@@ -233,6 +234,14 @@ def cr_gemm_nvfp4_fused(a_s8, a_scale, w_fp4, w_sf, global_scale, w_amax, K, c, 
     _check("cr_gemm_nvfp4_fused", lib().cr_gemm_nvfp4_fused(
         _ptr(a_s8), lda, _ptr(a_scale), _ptr(w_fp4), ld_fp4, _ptr(w_sf), ld_sf, _ptr(global_scale),
         _ptr(w_amax), _ptr(bias), M, N, K, _ptr(c), _TORCH_TO_CR[c.dtype], ldc, flags, _stream(stream)))
+
+
+def cr_probe_mfma_i8(random_data, iters, out, stream=None) -> float:
+    """Launch the register-only MFMA rate probe; returns the int8 operations it performs."""
+    ops = C.c_double(0.0)
+    _check("cr_probe_mfma_i8", lib().cr_probe_mfma_i8(int(bool(random_data)), iters, _ptr(out), out.numel(),
+                                                      C.byref(ops), _stream(stream)))
+    return float(ops.value)
 
 
 # ---------------------------------------------------------------- conveniences ----

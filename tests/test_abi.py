@@ -23,8 +23,8 @@ def test_library_exports_header_functions():
     assert set(names) >= {"cr_prep_weight_nvfp4", "cr_quant_act", "cr_quant_act_swiglu",
                           "cr_gemm_s8_rowscale", "cr_linear_nvfp4", "cr_linear_nvfp4_workspace_bytes",
                           "cr_linear_nvfp4_plan", "cr_quant_act_ex", "cr_gemm_s8_rowscale_bias",
-                          "cr_linear_nvfp4_ex",
-                          "cr_abi_version", "cr_status_string", "cr_padded_k"}
+                          "cr_linear_nvfp4_ex", "cr_weight_amax_nvfp4", "cr_gemm_nvfp4_fused",
+                          "cr_probe_mfma_i8", "cr_abi_version", "cr_status_string", "cr_padded_k"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -221,6 +221,15 @@ def test_gemm_fused_validation():
     assert fz(K=CR_BIG, lda=CR_BIG + 256, ld=CR_BIG, ld_sf=CR_BIG) == BIG
     assert fz(M=128 * 65535 + 1) == BIG    # workgroup rows of 128 activation rows
     assert fz(flags=4) == INV
+
+
+def test_probe_validation():
+    L = rbl.lib()
+    ops = C.c_double(0)
+    assert L.cr_probe_mfma_i8(1, 0, A16, 1 << 20, C.byref(ops), ST) == INV        # iters < 1
+    assert L.cr_probe_mfma_i8(1, 10, None, 1 << 20, C.byref(ops), ST) == INV
+    assert L.cr_probe_mfma_i8(1, 10, A16, 1 << 20, None, ST) == INV
+    assert L.cr_probe_mfma_i8(1, 10, A16 + 2, 1 << 20, C.byref(ops), ST) == MIS
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="valid arguments would launch on a real GPU")

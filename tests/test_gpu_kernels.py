@@ -406,3 +406,26 @@ def test_block_transposed_weight_and_gemm(N, K):
     assert_bits_equal(qt.cpu().numpy(), _block_transposed(rq), "w_s8 (block-transposed)")
     assert_bits_equal(st.cpu().numpy().view(np.uint32), rs.view(np.uint32), "w_scale (block-transposed)")
     assert_bits_equal(acc_t.cpu().numpy(), acc_n.cpu().numpy(), "int32 sums, transposed vs natural order")
+
+
+# ------------------------------------------------------------ diagnostic probe ----
+
+def test_probe_mfma_rates_are_plausible():
+    """The register-only MFMA probe runs and reports rates below the published peak, with
+    constant operands at least as fast as random ones (the power limit bites on toggling
+    bits)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(512 * cus, dtype=torch.int32, device=dev())
+    rates = {}
+    for rnd in (True, False):
+        for _ in range(2):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            say(f"cr_probe_mfma_i8 random={rnd}")
+            a.record()
+            ops = rbl.cr_probe_mfma_i8(rnd, 2000, out)
+            b.record()
+            torch.cuda.synchronize()
+            rates[rnd] = ops / (a.elapsed_time(b) * 1e-3) / 1e12
+    assert ops == 2.0 * 32768 * 16 * 2000 * 8 * cus
+    assert 100.0 < rates[True] <= 5000.0 * 1.05, rates
+    assert rates[False] >= 0.9 * rates[True], rates
