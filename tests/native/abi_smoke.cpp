@@ -1,0 +1,136 @@
+// Native consumer of the C ABI: no Python, no torch.  Device memory from hipMalloc, inputs
+// from a fixed-seed generator on the host.  Runs the layer through the component calls and
+// through cr_linear_nvfp4 (staged and short-batch paths, one and two streams) and checks
+// that every route gives the same bits; also checks argument errors come back as statuses.
+// Exit status 0 on success.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "convrot.h"
+
+#define HIP_OK(x)                                                                   \
+    do {                                                                            \
+        hipError_t e_ = (x);                                                        \
+        if (e_ != hipSuccess) {                                                     \
+            std::fprintf(stderr, "%s:%d %s: %s\n", __FILE__, __LINE__, #x, hipGetErrorString(e_)); \
+            return 1;                                                               \
+        }                                                                           \
+    } while (0)
+#define CR_OK_(x)                                                                   \
+    do {                                                                            \
+        cr_status s_ = (x);                                                         \
+        if (s_ != CR_OK) {                                                          \
+            std::fprintf(stderr, "%s:%d %s: %s\n", __FILE__, __LINE__, #x, cr_status_string(s_)); \
+            return 1;                                                               \
+        }                                                                           \
+    } while (0)
+
+namespace {
+
+uint32_t lcg(uint64_t &s)
+{
+    s = s * 6364136223846793005ull + 1442695040888963407ull;
+    return (uint32_t)(s >> 33);
+}
+
+uint16_t bf16_of(float f)      // truncation is fine for making inputs
+{
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
+}
+
+int run_case(int64_t M, int64_t N, int64_t K, hipStream_t s_main, hipStream_t s_aux)
+{
+    const int64_t kp = cr_padded_k(K), ld_fp4 = ((K + 1) / 2 + 15) / 16 * 16, ld_sf = (K + 15) / 16;
+    uint64_t seed = (uint64_t)(M * 1000003 + N * 1009 + K);
+    std::vector<uint16_t> hx((size_t)(M * kp));
+    for (auto &v : hx) v = bf16_of(((float)(lcg(seed) % 2001) - 1000.0f) / 400.0f);
+    std::vector<uint8_t> hc((size_t)(N * ld_fp4)), hs((size_t)(N * ld_sf));
+    for (auto &v : hc) v = (uint8_t)lcg(seed);
+    for (auto &v : hs) v = (uint8_t)(0x30 + lcg(seed) % 16);     // E4M3 scales 0.5 .. 1.875
+    const float g = 0.01f;
+
+    void *x, *out_a, *out_b, *ws;
+    uint8_t *codes, *sf;
+    int8_t *qx, *qw;
+    float *sx, *sw, *gd;
+    HIP_OK(hipMalloc(&x, hx.size() * 2));
+    HIP_OK(hipMalloc((void **)&codes, hc.size()));
+    HIP_OK(hipMalloc((void **)&sf, hs.size()));
+    HIP_OK(hipMalloc((void **)&gd, 4));
+    HIP_OK(hipMalloc((void **)&qx, (size_t)(M * kp)));
+    HIP_OK(hipMalloc((void **)&qw, (size_t)(N * kp)));
+    HIP_OK(hipMalloc((void **)&sx, (size_t)M * 4));
+    HIP_OK(hipMalloc((void **)&sw, (size_t)N * 4));
+    HIP_OK(hipMalloc(&out_a, (size_t)(M * N * 2)));
+    HIP_OK(hipMalloc(&out_b, (size_t)(M * N * 2)));
+    const size_t wsb = cr_linear_nvfp4_workspace_bytes(M, N, K, 0);
+    HIP_OK(hipMalloc(&ws, wsb));
+    HIP_OK(hipMemcpy(x, hx.data(), hx.size() * 2, hipMemcpyHostToDevice));
+    HIP_OK(hipMemcpy(codes, hc.data(), hc.size(), hipMemcpyHostToDevice));
+    HIP_OK(hipMemcpy(sf, hs.data(), hs.size(), hipMemcpyHostToDevice));
+    HIP_OK(hipMemcpy(gd, &g, 4, hipMemcpyHostToDevice));
+
+    // components: natural column order
+    CR_OK_(cr_quant_act(x, CR_BF16, kp, M, K, qx, kp, sx, CR_FLAG_NONE, s_main));
+    CR_OK_(cr_prep_weight_nvfp4(codes, ld_fp4, sf, ld_sf, gd, N, K, qw, kp, sw, CR_FLAG_NONE, s_main));
+    CR_OK_(cr_gemm_s8_rowscale(qx, kp, sx, qw, kp, sw, M, N, kp, out_a, CR_BF16, N, s_main));
+    HIP_OK(hipStreamSynchronize(s_main));
+    std::vector<uint16_t> ra((size_t)(M * N)), rb((size_t)(M * N));
+    HIP_OK(hipMemcpy(ra.data(), out_a, ra.size() * 2, hipMemcpyDeviceToHost));
+
+    for (int two = 0; two < 2; two++) {
+        HIP_OK(hipMemset(out_b, 0xFF, (size_t)(M * N * 2)));
+        CR_OK_(cr_linear_nvfp4(x, CR_BF16, kp, 0, M, K, codes, ld_fp4, sf, ld_sf, gd, N, out_b, CR_BF16, N, ws, wsb,
+                               0, CR_FLAG_NONE, s_main, two ? s_aux : nullptr));
+        HIP_OK(hipStreamSynchronize(s_main));
+        HIP_OK(hipMemcpy(rb.data(), out_b, rb.size() * 2, hipMemcpyDeviceToHost));
+        if (std::memcmp(ra.data(), rb.data(), ra.size() * 2) != 0) {
+            std::fprintf(stderr, "M=%lld N=%lld K=%lld: layer (streams=%d) differs from the components\n",
+                         (long long)M, (long long)N, (long long)K, 1 + two);
+            return 1;
+        }
+    }
+    int64_t rows = 0, chunks = 0;
+    CR_OK_(cr_linear_nvfp4_plan(M, N, K, 0, &rows, &chunks));
+    std::printf("M=%lld N=%lld K=%lld: components == layer (%s path), ok\n", (long long)M, (long long)N,
+                (long long)K, chunks == 0 ? "decode-inside-GEMM" : "staged");
+
+    // argument errors are statuses, nothing launched
+    if (cr_gemm_s8_rowscale(qx, kp, sx, qw, kp, sw, M, N, kp + 1, out_a, CR_BF16, N, s_main) != CR_ERR_INVALID_ARG ||
+        cr_quant_act(x, CR_BF16, kp, 0, K, qx, kp, sx, CR_FLAG_NONE, s_main) != CR_ERR_INVALID_ARG ||
+        cr_linear_nvfp4(x, CR_BF16, kp, 0, M, K, codes, ld_fp4, sf, ld_sf, gd, N, out_b, CR_BF16, N, ws, wsb - 1, 0,
+                        CR_FLAG_NONE, s_main, nullptr) != CR_ERR_TOO_LARGE) {
+        std::fprintf(stderr, "argument checks did not return the documented statuses\n");
+        return 1;
+    }
+    for (void *p : {(void *)x, (void *)codes, (void *)sf, (void *)gd, (void *)qx, (void *)qw, (void *)sx, (void *)sw,
+                    out_a, out_b, ws})
+        HIP_OK(hipFree(p));
+    return 0;
+}
+
+}  // namespace
+
+int main()
+{
+    if (cr_abi_version() != CR_ABI_VERSION) {
+        std::fprintf(stderr, "ABI version mismatch\n");
+        return 1;
+    }
+    hipStream_t s_main, s_aux;
+    HIP_OK(hipStreamCreate(&s_main));
+    HIP_OK(hipStreamCreate(&s_aux));
+    const int64_t cases[][3] = {{300, 520, 1000}, {8, 300, 5376}, {70, 1000, 20000}};
+    for (const auto &c : cases)
+        if (run_case(c[0], c[1], c[2], s_main, s_aux) != 0) return 1;
+    HIP_OK(hipStreamDestroy(s_main));
+    HIP_OK(hipStreamDestroy(s_aux));
+    std::printf("abi_smoke: all cases ok\n");
+    return 0;
+}
