@@ -2,16 +2,18 @@
 """Benchmark of the rotated W8A8 NVFP4 linear layer on one MI355X.
 
 One step = the QKV projection layer (qkv_proj [21504, 5376]) and the FFN-down layer with
-fused SwiGLU (fc2 [5376, 14336], H [19989, 28672]) at M = 19989 tokens, each layer being
-activation preparation (main stream) || NVFP4 weight preparation (second stream) -> INT8
-MFMA GEMM with the row-scale epilogue (main stream).  All calls go through the C ABI.
-Inputs are seeded synthetic data resident in HBM before timing starts.
+fused SwiGLU (fc2 [5376, 14336], H [19989, 28672]) at M = 19989 tokens, each layer run as
+cr_linear_nvfp4 runs it, through the component calls of the C ABI: activation preparation,
+NVFP4 weight preparation of each chunk (on a second stream when the weight takes several
+chunks), INT8 MFMA GEMM with the row-scale epilogue.  Inputs are seeded synthetic data
+resident in HBM before timing starts.
 
 Prints one JSON line: ms/layer (mean over the two layers), per-layer and per-kernel
 timings from HIP events recorded on the launching streams, the GEMM roofline (INT8 MFMA
-peak), each kernel timed alone (preparation rates against the HBM peak and a measured
-device copy), the expanded-S8 control (weights prepared once, outside timing), and the CPU
-oracle timed on a bounded sample.
+peak, with the register-only MFMA ceiling measured beside it), each kernel timed alone
+(preparation rates against the HBM peak and a measured device copy), the expanded-S8
+control (weights prepared once, outside timing), the block's other shapes, short batches
+(decode-inside-GEMM), and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -98,10 +100,15 @@ class Layer:
         self.codes, self.sf = p.codes.to(dev), p.sf.to(dev)
         self.g = torch.tensor([p.g], dtype=torch.float32, device=dev)
         kp = w.K_pad
-        # the chunking cr_linear_nvfp4 uses on this device, mirrored with component calls
+        # the chunking cr_linear_nvfp4 uses on this device, mirrored with component calls;
+        # no chunks means the short-batch path (the weight decoded inside the GEMM)
         self.R, self.nchunks = rbl.cr_linear_nvfp4_plan(w.M, w.N, w.K, max_tile_bytes)
+        self.fused = self.nchunks == 0
+        if self.fused:
+            self.R = w.N
+        self.n_launch = max(self.nchunks, 1)          # GEMM launches per layer
         self.chunks = [(n0, min(self.R, w.N - n0)) for n0 in range(0, w.N, self.R)]
-        ntiles = 2 if self.nchunks > 1 else 1
+        ntiles = 0 if self.fused else (2 if self.nchunks > 1 else 1)
         self.x_s8 = torch.empty(w.M, kp, dtype=torch.int8, device=dev)
         self.x_scale = torch.empty(w.M, dtype=torch.float32, device=dev)
         self.w_s8 = [torch.empty(self.R, kp, dtype=torch.int8, device=dev) for _ in range(ntiles)]
@@ -118,7 +125,7 @@ class Layer:
         self.act_bytes = w.M * cols * es + w.M * kp + 4 * w.M
         self.w_bytes = w.N * ((w.K + 1) // 2) + w.N * ((w.K + 15) // 16) + 4 + w.N * kp + 4 * w.N
         self.gemm_ops = 2 * w.M * w.N * kp
-        self.n_events = 3 + 4 * self.nchunks
+        self.n_events = 3 + 4 * self.n_launch
 
 
 def run_layer(L, rbl, s_main, s_aux, ev):
@@ -129,6 +136,23 @@ def run_layer(L, rbl, s_main, s_aux, ev):
     ev: 3 + 4 * nchunks events: start, act begin/end, then per chunk prep begin/end and
     GEMM begin/end."""
     w = L.w
+    if L.fused:                                       # short batch: the weight decoded in the GEMM
+        ev[0].record(s_main)
+        if L.pre is not None:
+            rbl.cr_quant_act_ex(L.x, w.K, w.swiglu, L.pre, L.x_s8, L.x_scale, BT, stream=s_main)
+        elif w.swiglu:
+            rbl.cr_quant_act_swiglu(L.x, w.K, L.x_s8, L.x_scale, BT, stream=s_main)
+        else:
+            rbl.cr_quant_act(L.x, w.K, L.x_s8, L.x_scale, BT, stream=s_main)
+        ev[1].record(s_main)
+        ev[3].record(s_main)                          # no separate weight preparation
+        ev[4].record(s_main)
+        ev[5].record(s_main)
+        rbl.cr_gemm_nvfp4_fused(L.x_s8, L.x_scale, L.codes, L.sf, L.g, None, w.K, L.out, bias=L.bias, flags=BT,
+                                stream=s_main)
+        ev[6].record(s_main)
+        ev[2].record(s_main)
+        return
     if L.nchunks < 2:
         s_aux = None                                  # a single chunk is staged on the main stream
     sw = s_aux if s_aux is not None else s_main
@@ -194,7 +218,7 @@ def layer_stats(L, ev_steps):
 
     def mean(a, b):
         return sum(e[a].elapsed_time(e[b]) for e in ev_steps) / K
-    nc = L.nchunks
+    nc = L.n_launch
     t_layer = mean(0, 2)
     per_step = sorted(e[0].elapsed_time(e[2]) for e in ev_steps)
     t_act = mean(0, 1)
@@ -203,7 +227,8 @@ def layer_stats(L, ev_steps):
     t_g = sum(g_launch)
     return {
         "M": L.w.M, "N": L.w.N, "K": L.w.K, "K_pad": L.w.K_pad, "swiglu": L.w.swiglu,
-        "weight_chunks": nc, "rows_per_chunk": L.R,
+        "weight_chunks": L.nchunks, "rows_per_chunk": L.R,
+        "path": "decode-inside-GEMM" if L.fused else "staged",
         "ms": round(t_layer, 4),
         "ms_median": round(per_step[K // 2], 4),
         "ms_min": round(per_step[0], 4),
@@ -215,7 +240,7 @@ def layer_stats(L, ev_steps):
         "act_prep_ms": round(t_act, 4),
         "act_prep_gbs": round(L.act_bytes / (t_act * 1e-3) / 1e9, 1),
         "weight_prep_ms": round(t_w, 4),
-        "weight_prep_gbs": round(L.w_bytes / (t_w * 1e-3) / 1e9, 1),
+        "weight_prep_gbs": round(L.w_bytes / (t_w * 1e-3) / 1e9, 1) if t_w > 0 else None,
         "not_gemm_ms": round(t_layer - t_g, 4),
     }
 
@@ -497,12 +522,35 @@ def main():
 
     dom = layers[0]
     dom_info = layer_info[dom.name]
-    # per launch: algorithmic ops of one chunk's GEMM over its mean launch duration
-    launch_ops = dom.gemm_ops / dom.nchunks
-    launch_ms = dom_info["gemm_ms"] / dom.nchunks
-    achieved = launch_ops / (launch_ms * 1e-3) / 1e12
-    launch_shape = (dom.w.M, dom.chunks[0][1], dom.w.K_pad)
-    traffic = counter_traffic(launch_shape)
+    if dom.fused:
+        # a short batch: the decode-inside-GEMM kernel, bound by vector issue
+        achieved = FUSED_VALU_PER_ELEM * dom.w.N * dom.w.K_pad / (dom_info["gemm_ms"] * 1e-3) / 1e12
+        roofline = {
+            "kernel": f"gemm_nvfp4_fused ({dom.name}: M={dom.w.M} N={dom.w.N} K_pad={dom.w.K_pad})",
+            "bound": "alu", "achieved": round(achieved, 2), "peak": PEAK_VALU_TOPS, "unit": "Tops/s",
+            "frac": round(achieved / PEAK_VALU_TOPS, 4), "traffic": None,
+            "per_element_ops": FUSED_VALU_PER_ELEM,
+        }
+    else:
+        # per launch: algorithmic ops of one chunk's GEMM over its mean launch duration
+        launch_ops = dom.gemm_ops / dom.nchunks
+        launch_ms = dom_info["gemm_ms"] / dom.nchunks
+        achieved = launch_ops / (launch_ms * 1e-3) / 1e12
+        launch_shape = (dom.w.M, dom.chunks[0][1], dom.w.K_pad)
+        roofline = {
+            "kernel": (f"gemm_s8_rowscale ({dom.name}: {dom.nchunks} launch(es) of M={launch_shape[0]} "
+                       f"N={launch_shape[1]} K_pad={launch_shape[2]})"),
+            "bound": "mfma",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_INT8_TOPS,
+            "unit": "TOP/s",
+            "frac": round(achieved / PEAK_INT8_TOPS, 4),
+            "traffic": counter_traffic(launch_shape),
+            # what the matrix cores sustain with operands in registers (no memory traffic):
+            # random data toggles bits and meets the power limit; constant data does not
+            "measured_mfma_ceiling": ceiling,
+            "frac_of_random_data_ceiling": round(achieved / ceiling["random_int8"], 4),
+        }
     result = {
         "metric": METRIC,
         "value": round(sum(v["ms"] for v in layer_info.values()) / len(layer_info), 4),
@@ -524,20 +572,7 @@ def main():
             "weight_prep_stream": "serial" if args.serial else "second stream",
             "max_tile_bytes": args.max_tile_bytes or rbl.DEFAULT_MAX_TILE_BYTES,
         },
-        "roofline": {
-            "kernel": (f"gemm_s8_rowscale ({dom.name}: {dom.nchunks} launch(es) of M={launch_shape[0]} "
-                       f"N={launch_shape[1]} K_pad={launch_shape[2]})"),
-            "bound": "mfma",
-            "achieved": round(achieved, 1),
-            "peak": PEAK_INT8_TOPS,
-            "unit": "TOP/s",
-            "frac": round(achieved / PEAK_INT8_TOPS, 4),
-            "traffic": traffic,
-            # what the matrix cores sustain with operands in registers (no memory traffic):
-            # random data toggles bits and meets the power limit; constant data does not
-            "measured_mfma_ceiling": ceiling,
-            "frac_of_random_data_ceiling": round(achieved / ceiling["random_int8"], 4),
-        },
+        "roofline": roofline,
         "layers": layer_info,
         "next_shapes": next_info,
         "short_batches": short_info,
