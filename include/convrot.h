@@ -25,6 +25,9 @@
  *     scales (any stride) and the output of the GEMM (element-aligned).  Violations return
  *     CR_ERR_MISALIGNED.
  *   - K_pad may not exceed CR_MAX_K_PAD, so that 127 * 127 * K_pad fits in an int32.
+ *   - A GEMM may have at most 8388607 output tiles of 256 x 256 (ceil(M/256) * ceil(N/256)),
+ *     and cr_gemm_nvfp4_fused at most 536870880 weight rows: a dispatch counts its work-items
+ *     in 32 bits.  Larger shapes return CR_ERR_TOO_LARGE; split them along M or N.
  *   - Rows are independent.  A row whose maximum |value| after rotation is 0 gets scale 0
  *     and all-zero codes.
  *

@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdint>
 #include <cstring>
 
 #include "../../include/convrot.h"
@@ -105,7 +106,8 @@ cr_status check_gemm(const int8_t *a, int64_t lda, const float *sa, const int8_t
     if (cdt != CR_I32 && (!sa || !sb)) return CR_ERR_INVALID_ARG;
     if (M < 1 || N < 1 || K_pad < 1 || K_pad % 256 != 0) return CR_ERR_INVALID_ARG;
     if (M > kMaxRows || N > kMaxRows) return CR_ERR_INVALID_ARG;
-    if (((M + 255) / 256) * ((N + 255) / 256) > kMaxRows) return CR_ERR_TOO_LARGE;
+    // one workgroup of 512 threads per 256 x 256 tile; a dispatch counts work-items in 32 bits
+    if (((M + 255) / 256) * ((N + 255) / 256) > (int64_t)(UINT32_MAX / 512)) return CR_ERR_TOO_LARGE;
     if (K_pad > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
     if (lda < K_pad || ldb < K_pad || ldc < N) return CR_ERR_INVALID_ARG;
     if (!aligned(a, 16) || !aligned(b, 16) || lda % 16 != 0 || ldb % 16 != 0) return CR_ERR_MISALIGNED;
@@ -129,6 +131,7 @@ cr_status check_fused(const int8_t *a_s8, int64_t lda, const float *a_scale, con
     const int64_t kp = pad256(K);
     if (kp > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
     if ((M + 127) / 128 > 65535) return CR_ERR_TOO_LARGE;
+    if ((N + 31) / 32 > (int64_t)(UINT32_MAX / 256)) return CR_ERR_TOO_LARGE;   // 32-bit work-item count
     if (lda < kp || ld_fp4 < (K + 1) / 2 || ld_sf < (K + 15) / 16 || ldc < N) return CR_ERR_INVALID_ARG;
     if (!aligned(a_s8, 16) || lda % 16 != 0) return CR_ERR_MISALIGNED;
     if (!aligned(w_fp4, 16) || ld_fp4 % 16 != 0) return CR_ERR_MISALIGNED;

@@ -46,6 +46,7 @@ constexpr int kLanesPerBlock = 16;          // lanes sharing one 256-column bloc
 constexpr int kTileStrideF = 272;           // floats per 16x16 transpose tile (256 + 16 pad)
 constexpr int kMaxGroups1 = 60;             // two-pass rows: 960 threads
 constexpr int kMaxGroups2 = 32;             // one-pass rows: 512 threads
+constexpr int64_t kTwoPassMaxGrid = 65536;  // workgroups of a two-pass launch (they loop)
 
 // XOR swizzle of 16-byte chunks inside a 16x16 fp32 tile: conflict-free ds_read/ds_write
 // for both row-wise (b128) and column-wise (b32) access with 32 or 64 LDS banks.
@@ -351,13 +352,15 @@ __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, 
     }
 }
 
-// Two passes, one row per workgroup: the row is streamed in slices of G blocks, once for
-// the maximum and once for the codes (the same operations both times, so the same bits).
+// Two passes, one row at a time per workgroup: the row is streamed in slices of G blocks,
+// once for the maximum and once for the codes (the same operations both times, so the
+// same bits).  `parity` selects the reduction slot set (alternating between consecutive
+// rows of a workgroup, so one barrier per row suffices).
 template <class Loader>
 __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row, int nb,
                                                   int8_t *__restrict__ out, int64_t ld_out,
                                                   float *__restrict__ scale_out, bool natural,
-                                                  bool amax_only)
+                                                  bool amax_only, int parity)
 {
     extern __shared__ float lds[];
     const int tid = threadIdx.x;
@@ -388,7 +391,7 @@ __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row,
 #pragma unroll
         for (int i = 0; i < 16; i++) zmax = fmaxf(zmax, fabsf(v[i]));
     }
-    const float zrow = block_max(zmax, red);
+    const float zrow = block_max(zmax, red + 16 * parity);
     if (amax_only) {
         if (tid == 0) scale_out[row] = zrow * 0.0625f;
         return;
@@ -413,8 +416,15 @@ __device__ __forceinline__ void row_prep_kernel_body(const Loader &ld, int64_t n
 {
     const bool natural = (mode & 2) == 0;
     const bool amax_only = (mode & 4) != 0;
-    if (mode & 1) row_prep_two_pass(ld, (int64_t)blockIdx.x, nb, out, ld_out, scale_out, natural, amax_only);
-    else row_prep_rows<Loader, RB>(ld, n_rows, nb, out, ld_out, scale_out, natural, amax_only);
+    if (mode & 1) {
+        int parity = 0;
+        for (int64_t row = blockIdx.x; row < n_rows; row += gridDim.x) {
+            row_prep_two_pass(ld, row, nb, out, ld_out, scale_out, natural, amax_only, parity);
+            parity ^= 1;
+        }
+    } else {
+        row_prep_rows<Loader, RB>(ld, n_rows, nb, out, ld_out, scale_out, natural, amax_only);
+    }
 }
 
 // Launch shape of a row of nb blocks.  Up to 32 blocks, one block per 16-lane group; up
@@ -456,7 +466,9 @@ inline RowPrepShape row_prep_shape(int64_t nb, bool force_two_pass)
 // Two-pass launches one workgroup per row.
 inline int row_prep_grid(int64_t n_rows, const RowPrepShape &s, const void *kernel, size_t lds)
 {
-    if (s.two_pass) return (int)n_rows;
+    // two-pass rows: one workgroup per row up to a cap that keeps the dispatch's 32-bit
+    // work-item count far from overflow (960 threads x 65536); beyond it workgroups loop
+    if (s.two_pass) return (int)(n_rows < kTwoPassMaxGrid ? n_rows : kTwoPassMaxGrid);
     struct Entry { int dev; const void *kernel; int threads; size_t lds; int64_t resident; };
     static std::mutex mu;
     static Entry cache[64];

@@ -120,6 +120,10 @@ def test_gemm_validation():
     assert gm(lda=520) == MIS
     assert gm(c=A16 + 1) == MIS
     assert gm(K=rbl.CR_MAX_K_PAD + 256, lda=rbl.CR_MAX_K_PAD + 256, ldb=rbl.CR_MAX_K_PAD + 256) == BIG
+    # more 256 x 256 tiles than a dispatch's 32-bit work-item count allows (512 threads each)
+    big = 1 << 21
+    assert gm(M=big, N=big, ldc=big) == BIG
+    assert gm(M=big, N=(1 << 21) // 256 * 2, ldc=big) != BIG   # 8192 x 16 tiles: fine
 
 
 def test_layer_validation_and_workspace():
@@ -220,6 +224,8 @@ def test_gemm_fused_validation():
     assert fz(bias=A16 + 2) == MIS
     assert fz(K=CR_BIG, lda=CR_BIG + 256, ld=CR_BIG, ld_sf=CR_BIG) == BIG
     assert fz(M=128 * 65535 + 1) == BIG    # workgroup rows of 128 activation rows
+    n_big = 32 * (0xFFFFFFFF // 256) + 32  # one 32-row band more than 2^32 work-items allow
+    assert fz(N=n_big, ldc=n_big) == BIG
     assert fz(flags=4) == INV
 
 

@@ -72,3 +72,26 @@ def test_preparation_and_layer_at_max_k():
         ref = oracle.epilogue(acc[:M], rs[:M], rsw, synth.DT_FP32)
         err = rel_l2(out_f64(y.cpu(), synth.DT_FP32), out_f64(ref, synth.DT_FP32))
         assert err <= TOL[synth.DT_FP32], (M, err)
+
+
+def test_two_pass_rows_beyond_the_grid_cap():
+    """Forced two-pass preparation of 70000 rows: more rows than two-pass workgroups
+    (65536), so workgroups loop over rows; every row bit-exact."""
+    M, K = 70000, 300
+    g = torch.Generator().manual_seed(8)
+    x = (torch.randn(M, 304, generator=g) * 2).to(torch.bfloat16)     # 16-byte row stride
+    x[:, K:] = 1e4
+    x[7] = 0.0
+    say(f"cr_quant_act forced two-pass M={M} K={K}")
+    q, s = rbl.quant_act(x.to(dev()), K, flags=rbl.CR_FLAG_FORCE_TWO_PASS)
+    w = 0.02 * torch.randn(M, 256, generator=g)
+    p = synth.nvfp4_encode(w, garbage_seed=8)
+    gs = torch.tensor([p.g], dtype=torch.float32, device=dev())
+    say(f"cr_weight_amax_nvfp4 forced two-pass N={M} K=256")
+    am = rbl.weight_amax_nvfp4(p.codes.to(dev()), p.sf.to(dev()), gs, 256, flags=rbl.CR_FLAG_FORCE_TWO_PASS)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant_act(synth.bits_u16(x), synth.DT_BF16, K)
+    assert_bits_equal(q.cpu().numpy(), rq, "x_s8")
+    assert_bits_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32), "x_scale")
+    ra = oracle.weight_amax_nvfp4(p.codes.numpy(), p.sf.numpy(), p.g, 256)
+    assert_bits_equal(am.cpu().numpy().view(np.uint32), ra.view(np.uint32), "w_amax")
