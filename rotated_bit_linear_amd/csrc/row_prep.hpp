@@ -38,6 +38,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdint>
 #include <mutex>
 
 namespace convrot {
@@ -404,6 +405,111 @@ __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row,
         if (b < nb) store_codes(v, rq, orow + (int64_t)b * 256 + t * 16);
     }
     if (tid == 0) scale_out[row] = rq.scale;
+}
+
+// Several short rows per workgroup (nb <= 32 blocks): `rpw` rows of nb blocks are held by
+// rpw * nb lane groups at once (group g: row slot g / nb, block g % nb), so that a
+// workgroup of up to 64 groups leaves few lanes idle whatever nb is (one row of 21 blocks
+// alone would leave 3 of 24 groups idle).  Row maximum: each group reduces its 16 lanes,
+// one lane per group writes it to LDS, one barrier, then every lane takes the maximum over
+// its row's nb entries; two alternating slot sets make one barrier per set of rows enough.
+// The raw bytes of the next set of rows are requested before this set is decoded.
+template <class Loader>
+__device__ __forceinline__ void row_prep_multi(const Loader &ld, int64_t n_rows, int nb, int rpw,
+                                               int8_t *__restrict__ out, int64_t ld_out,
+                                               float *__restrict__ scale_out, bool natural, bool amax_only)
+{
+    extern __shared__ float lds[];
+    const int tid = threadIdx.x;
+    const int grp = tid >> 4;
+    const int t = tid & 15;
+    const int G = blockDim.x >> 4;
+    float *tile = lds + grp * kTileStrideF;
+    float *red = lds + G * kTileStrideF;               // two sets of G floats
+    const int slot = grp / nb, b = grp - slot * nb;
+    const bool active = slot < rpw;
+    const int64_t seg = (int64_t)b * 16 + t;
+    using Raw = typename Loader::Raw;
+    typename Loader::Lane lane_c{};
+    if (active) lane_c = ld.lane(seg);
+    const int64_t step = (int64_t)gridDim.x * rpw;
+
+    auto fetch = [&](int64_t base, Raw &r) {
+        const int64_t row = base + slot;
+        if (active && row < n_rows) ld.fetch(row, seg, r);
+    };
+    auto process = [&](const Raw &r, int64_t base, int parity) {
+        const int64_t row = base + slot;
+        const bool live = active && row < n_rows;
+        float v[16];
+        if (live) {
+            ld.decode(r, seg, lane_c, v);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; i++) v[i] = 0.0f;
+        }
+        hadamard256(v, tile, t, natural);
+        float zm = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; i++) zm = fmaxf(zm, fabsf(v[i]));
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) zm = fmaxf(zm, __shfl_xor(zm, off, 64));
+        float *set = red + parity * G;
+        if (t == 0) set[grp] = zm;
+        __syncthreads();
+        float zrow = 0.0f;
+        if (active)
+            for (int i = 0; i < nb; i++) zrow = fmaxf(zrow, set[slot * nb + i]);
+        if (amax_only) {                               // a = max |z * 0.0625|, no codes
+            if (live && b == 0 && t == 0) scale_out[row] = zrow * 0.0625f;
+            return;
+        }
+        const RowQuant rq = row_quant(zrow);
+        if (live) store_codes(v, rq, out + row * ld_out + (int64_t)b * 256 + t * 16);
+        if (live && b == 0 && t == 0) scale_out[row] = rq.scale;
+    };
+
+    int64_t base = (int64_t)blockIdx.x * rpw;
+    Raw ra{}, rb{};
+    if (base < n_rows) fetch(base, ra);
+    int parity = 0;
+    while (base < n_rows) {                            // unrolled by two: the buffers alternate
+        int64_t next = base + step;
+        if (next < n_rows) fetch(next, rb);
+        process(ra, base, parity);
+        parity ^= 1;
+        base = next;
+        if (base >= n_rows) break;
+        next = base + step;
+        if (next < n_rows) fetch(next, ra);
+        process(rb, base, parity);
+        parity ^= 1;
+        base = next;
+    }
+}
+
+// Rows per workgroup for the multi-row form: the count (at most 64 lane groups in all)
+// that leaves the fewest idle lanes in the workgroup's last wave, the smallest on ties.
+inline int row_prep_multi_rows(int64_t nb)
+{
+    int best = 1;
+    int64_t best_idle = INT64_MAX;
+    for (int r = 1; r * nb <= 64; r++) {
+        const int64_t groups = r * nb, alloc = (groups + 3) / 4 * 4;
+        const int64_t idle_frac_x1000 = (alloc - groups) * 1000 / alloc;
+        if (idle_frac_x1000 < best_idle) {
+            best_idle = idle_frac_x1000;
+            best = r;
+        }
+    }
+    return best;
+}
+
+// Dynamic LDS of a multi-row workgroup: per-group transpose tiles and two sets of one
+// float per group.
+__host__ __device__ constexpr size_t row_prep_multi_lds_bytes(int threads)
+{
+    return (size_t)(threads / kLanesPerBlock) * (kTileStrideF + 2) * sizeof(float);
 }
 
 // Kernel body shared by all loaders.
