@@ -255,6 +255,15 @@ __global__ __launch_bounds__(row_prep_max_threads<RB>()) void quant_act_kernel(L
     row_prep_kernel_body<Loader, RB>(ld, n_rows, nb, out, ld_out, scale, mode);
 }
 
+// Several short rows per workgroup (see row_prep_multi).
+template <class Loader>
+__global__ __launch_bounds__(1024) void quant_act_multi_kernel(Loader ld, int64_t n_rows, int nb, int rpw,
+                                                             int8_t *__restrict__ out, int64_t ld_out,
+                                                             float *__restrict__ scale, int mode)
+{
+    row_prep_multi(ld, n_rows, nb, rpw, out, ld_out, scale, (mode & 2) == 0, false);
+}
+
 // --------------------------------------------------------------------- launchers ----
 
 template <class Loader>
@@ -264,6 +273,18 @@ static hipError_t launch_rows(const Loader &L, int64_t rows, int64_t nb, int8_t 
     const RowPrepShape s = row_prep_shape(nb, force_two_pass);
     const size_t lds = row_prep_lds_bytes(s.threads);
     const int mode = (s.two_pass ? 1 : 0) | (transposed ? 2 : 0);
+    const int rpw = (!s.two_pass && nb <= 32) ? row_prep_multi_rows(nb) : 1;
+    if (rpw >= 2) {
+        // rows whose lane groups would leave the last wave partly idle: several per workgroup
+        const int threads = (int)((rpw * nb + 3) / 4 * 64);
+        const size_t mlds = row_prep_multi_lds_bytes(threads);
+        const RowPrepShape ms{threads, 1, false};
+        const void *k = reinterpret_cast<const void *>(&quant_act_multi_kernel<Loader>);
+        const dim3 grid((unsigned)row_prep_grid((rows + rpw - 1) / rpw, ms, k, mlds));
+        hipLaunchKernelGGL((quant_act_multi_kernel<Loader>), grid, dim3(threads), mlds, st, L, rows, (int)nb, rpw,
+                           out, ld_out, scale, mode);
+        return hipGetLastError();
+    }
     if (s.rb == 2) {
         const void *k = reinterpret_cast<const void *>(&quant_act_kernel<Loader, 2>);
         const dim3 grid((unsigned)row_prep_grid(rows, s, k, lds));

@@ -413,7 +413,8 @@ __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row,
 // alone would leave 3 of 24 groups idle).  Row maximum: each group reduces its 16 lanes,
 // one lane per group writes it to LDS, one barrier, then every lane takes the maximum over
 // its row's nb entries; two alternating slot sets make one barrier per set of rows enough.
-// The raw bytes of the next set of rows are requested before this set is decoded.
+// The raw bytes of the next set of rows are requested before this set is decoded, or right
+// after it is decoded for loaders that prefer one buffer (Loader::kFetchAfterDecode).
 template <class Loader>
 __device__ __forceinline__ void row_prep_multi(const Loader &ld, int64_t n_rows, int nb, int rpw,
                                                int8_t *__restrict__ out, int64_t ld_out,
@@ -438,16 +439,17 @@ __device__ __forceinline__ void row_prep_multi(const Loader &ld, int64_t n_rows,
         const int64_t row = base + slot;
         if (active && row < n_rows) ld.fetch(row, seg, r);
     };
-    auto process = [&](const Raw &r, int64_t base, int parity) {
-        const int64_t row = base + slot;
-        const bool live = active && row < n_rows;
-        float v[16];
-        if (live) {
+    auto decode = [&](const Raw &r, int64_t base, float (&v)[16]) {
+        if (active && base + slot < n_rows) {
             ld.decode(r, seg, lane_c, v);
         } else {
 #pragma unroll
             for (int i = 0; i < 16; i++) v[i] = 0.0f;
         }
+    };
+    auto finish = [&](float (&v)[16], int64_t base, int parity) {
+        const int64_t row = base + slot;
+        const bool live = active && row < n_rows;
         hadamard256(v, tile, t, natural);
         float zm = 0.0f;
 #pragma unroll
@@ -470,21 +472,43 @@ __device__ __forceinline__ void row_prep_multi(const Loader &ld, int64_t n_rows,
     };
 
     int64_t base = (int64_t)blockIdx.x * rpw;
-    Raw ra{}, rb{};
-    if (base < n_rows) fetch(base, ra);
     int parity = 0;
-    while (base < n_rows) {                            // unrolled by two: the buffers alternate
-        int64_t next = base + step;
-        if (next < n_rows) fetch(next, rb);
-        process(ra, base, parity);
-        parity ^= 1;
-        base = next;
-        if (base >= n_rows) break;
-        next = base + step;
-        if (next < n_rows) fetch(next, ra);
-        process(rb, base, parity);
-        parity ^= 1;
-        base = next;
+    if constexpr (Loader::kFetchAfterDecode) {
+        // one buffer: the next set of rows is requested as soon as this set is decoded
+        Raw raw{};
+        if (base < n_rows) fetch(base, raw);
+        for (; base < n_rows; base += step) {
+            float v[16];
+            decode(raw, base, v);
+            if (base + step < n_rows) fetch(base + step, raw);
+            finish(v, base, parity);
+            parity ^= 1;
+        }
+    } else {
+        // two buffers in turn (unrolled by two): the next set is requested before decoding
+        Raw ra{}, rb{};
+        if (base < n_rows) fetch(base, ra);
+        while (base < n_rows) {
+            int64_t next = base + step;
+            if (next < n_rows) fetch(next, rb);
+            {
+                float v[16];
+                decode(ra, base, v);
+                finish(v, base, parity);
+            }
+            parity ^= 1;
+            base = next;
+            if (base >= n_rows) break;
+            next = base + step;
+            if (next < n_rows) fetch(next, ra);
+            {
+                float v[16];
+                decode(rb, base, v);
+                finish(v, base, parity);
+            }
+            parity ^= 1;
+            base = next;
+        }
     }
 }
 
