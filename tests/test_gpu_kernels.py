@@ -429,3 +429,42 @@ def test_probe_mfma_rates_are_plausible():
     assert ops == 2.0 * 32768 * 16 * 2000 * 8 * cus
     assert 100.0 < rates[True] <= 5000.0 * 1.05, rates
     assert rates[False] >= 0.9 * rates[True], rates
+
+
+# ------------------------------------------------------ rows per workgroup sweep ----
+
+@pytest.mark.parametrize("nb", list(range(1, 33)))
+def test_every_short_row_shape_bit_exact(nb):
+    """Rows of 1..32 blocks (ragged K = 256 nb - 7), where several rows share a workgroup:
+    activation, SwiGLU, weight and row-maximum preparation, bit-exact against the oracle,
+    with a row count that leaves the last set of rows of a workgroup incomplete."""
+    K = 256 * nb - 7
+    M = 37
+    ld = (2 * K + 7) // 8 * 8 + 8
+    g = torch.Generator().manual_seed(nb)
+    h = (torch.randn(M, ld, generator=g) * 2).to(torch.bfloat16)
+    h[3] = 0.0
+    hb = synth.bits_u16(h)
+    say(f"short rows nb={nb}: quant_act / swiglu")
+    q, s = rbl.quant_act(h.to(dev()), K, flags=rbl.CR_FLAG_BLOCK_TRANSPOSED if nb % 2 else 0)
+    qs, ss = rbl.quant_act(h.to(dev()), K, swiglu=True)
+    w = 0.02 * torch.randn(M + 4, K, generator=g)
+    p = synth.nvfp4_encode(w, garbage_seed=nb)
+    gs = torch.tensor([p.g], dtype=torch.float32, device=dev())
+    say(f"short rows nb={nb}: prep_weight / weight_amax")
+    qw, sw = rbl.prep_weight_nvfp4(p.codes.to(dev()), p.sf.to(dev()), gs, K)
+    am = rbl.weight_amax_nvfp4(p.codes.to(dev()), p.sf.to(dev()), gs, K)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant_act(hb, synth.DT_BF16, K)
+    if nb % 2:
+        rq = rq.reshape(M, nb, 16, 16).transpose(0, 1, 3, 2).reshape(M, 256 * nb)
+    assert_bits_equal(q.cpu().numpy(), rq, "x_s8")
+    assert_bits_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32), "x_scale")
+    rqs, rss = oracle.quant_act(hb, synth.DT_BF16, K, swiglu=True)
+    assert_bits_equal(qs.cpu().numpy(), rqs, "swiglu x_s8")
+    assert_bits_equal(ss.cpu().numpy().view(np.uint32), rss.view(np.uint32), "swiglu x_scale")
+    rqw, rsw = oracle.prep_weight_nvfp4(p.codes.numpy(), p.sf.numpy(), p.g, K)
+    assert_bits_equal(qw.cpu().numpy(), rqw, "w_s8")
+    assert_bits_equal(sw.cpu().numpy().view(np.uint32), rsw.view(np.uint32), "w_scale")
+    ra = oracle.weight_amax_nvfp4(p.codes.numpy(), p.sf.numpy(), p.g, K)
+    assert_bits_equal(am.cpu().numpy().view(np.uint32), ra.view(np.uint32), "w_amax")
