@@ -425,8 +425,8 @@ def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only (the layer is data-parallel over tokens "
-              "with no communication; multi-GPU sharding is not built). Use --gpus 1.", file=sys.stderr)
+        print("bench.py: runs on one GPU only (the layer is data-parallel over tokens with no "
+              "communication; multi-GPU sharding is not implemented). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
