@@ -388,22 +388,24 @@ def short_batches(torch, rbl, synth, dev, s_main, rows_list, n=20):
     return info
 
 
-def mfma_ceiling(torch, rbl, stream, iters=10000) -> dict:
-    """TOP/s of the register-only MFMA probe (cr_probe_mfma_i8) on random and on constant
-    int8 operands: what the power-limited matrix cores sustain with no memory traffic."""
+def mfma_ceiling(torch, rbl, stream, iters=20000) -> dict:
+    """TOP/s of the register-only MFMA probe (cr_probe_mfma_i8) on uniformly random bytes, on
+    bell-shaped bytes with the spread of the layer's S8 operands, and on constant bytes: what
+    the power-limited matrix cores sustain with no memory traffic."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     out = torch.empty(512 * cus, dtype=torch.int32, device="cuda")
     res = {}
-    for rnd in (True, False):
+    for kind, key in ((rbl.CR_PROBE_UNIFORM, "random_int8"), (rbl.CR_PROBE_BELL, "layer_like_int8"),
+                      (rbl.CR_PROBE_CONSTANT, "constant_int8")):
         tops = 0.0
         for _ in range(2):                         # the second launch is the one reported
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            ops = rbl.cr_probe_mfma_i8(rnd, iters, out, stream=stream)
+            ops = rbl.cr_probe_mfma_i8(kind, iters, out, stream=stream)
             b.record(stream)
             torch.cuda.synchronize()
             tops = ops / (a.elapsed_time(b) * 1e-3) / 1e12
-        res["random_int8" if rnd else "constant_int8"] = round(tops, 1)
+        res[key] = round(tops, 1)
     del out
     return res
 
@@ -550,6 +552,7 @@ def main():
             # random data toggles bits and meets the power limit; constant data does not
             "measured_mfma_ceiling": ceiling,
             "frac_of_random_data_ceiling": round(achieved / ceiling["random_int8"], 4),
+            "frac_of_layer_like_data_ceiling": round(achieved / ceiling["layer_like_int8"], 4),
         }
     result = {
         "metric": METRIC,

@@ -290,16 +290,23 @@ cr_status cr_gemm_nvfp4_fused(const int8_t *a_s8, int64_t lda, const float *a_sc
 /*
  * Diagnostic, not part of the layer: the sustained rate of the INT8 matrix instruction the
  * GEMM uses (v_mfma_i32_32x32x32_i8) with its operands already in registers, no memory
- * traffic at all, on random (random_data != 0) or constant int8 data.  The matrix cores
- * are power-limited, so toggling operand bits lower the sustained rate; this gives the
- * ceiling a GEMM on real data can approach, beside the published dense peak.
+ * traffic at all.  The matrix cores are power-limited, so toggling operand bits lower the
+ * sustained rate; this gives the ceiling a GEMM on real data can approach, beside the
+ * published dense peak.
+ *   data_kind  CR_PROBE_CONSTANT (every byte 1), CR_PROBE_UNIFORM (uniformly random bytes)
+ *              or CR_PROBE_BELL (bell-shaped bytes: the centred sum of four uniform bytes
+ *              times 7/32, standard deviation about 32, the spread of the layer's rotated
+ *              S8 operands); anything else is CR_ERR_INVALID_ARG.
  *   iters      1 .. 1000000 loop iterations (16 MFMAs each, 8 waves per compute unit).
  *   out        device buffer of at least out_elems ints, overwritten with meaningless sums;
  *              out_elems must be >= 512 * (compute units of the current device).
  *   ops        host pointer: the number of int8 operations (2 per multiply-add) the launch
  *              performs; time the launch on `stream` to get the rate.
  */
-cr_status cr_probe_mfma_i8(int random_data, int iters, int *out, size_t out_elems, double *ops,
+#define CR_PROBE_CONSTANT 0
+#define CR_PROBE_UNIFORM 1
+#define CR_PROBE_BELL 2
+cr_status cr_probe_mfma_i8(int data_kind, int iters, int *out, size_t out_elems, double *ops,
                            hipStream_t stream);
 
 #ifdef __cplusplus

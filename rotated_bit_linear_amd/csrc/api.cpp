@@ -493,17 +493,18 @@ cr_status cr_linear_nvfp4(const void *x, cr_dtype x_dtype, int64_t ld_x, int swi
                               max_tile_bytes, flags, s_main, s_aux);
 }
 
-cr_status cr_probe_mfma_i8(int random_data, int iters, int *out, size_t out_elems, double *ops,
+cr_status cr_probe_mfma_i8(int data_kind, int iters, int *out, size_t out_elems, double *ops,
                            hipStream_t stream)
 {
     if (!out || !ops || iters < 1 || iters > 1000000) return CR_ERR_INVALID_ARG;
+    if (data_kind < CR_PROBE_CONSTANT || data_kind > CR_PROBE_BELL) return CR_ERR_INVALID_ARG;
     if (!aligned(out, 4)) return CR_ERR_MISALIGNED;
     cr_status s = current_device_ok();
     if (s != CR_OK) return s;
     const int cus = current_cus();
     if (out_elems < (size_t)512 * (size_t)cus) return CR_ERR_INVALID_ARG;
     *ops = 2.0 * 32768.0 * 16.0 * (double)iters * (double)(8 * cus);
-    return from_hip(convrot::launch_probe_mfma(cus, iters, random_data != 0, out, stream));
+    return from_hip(convrot::launch_probe_mfma(cus, iters, data_kind, out, stream));
 }
 
 }  // extern "C"

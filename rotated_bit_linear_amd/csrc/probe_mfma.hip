@@ -5,7 +5,10 @@
 // the next the clock drops well below its peak, so the dense INT8 figure of the data sheet
 // is reachable only with constant operands.  The probe measures that ceiling on the device
 // at hand, so the GEMM's roofline fraction can be read against what the matrix cores
-// sustain on real data as well as against the published peak.
+// sustain on real data as well as against the published peak.  The bell-shaped kind is the
+// sum of four uniform bytes (Irwin-Hall), centred and scaled by 7/32: mean 0, standard
+// deviation about 32, range -112 .. 111 -- the rotated, row-quantized activations and
+// weights of the block's linear layers have standard deviations of 30 to 33.
 //
 // Shape: 2 workgroups of 4 waves per CU (8 waves, as in the GEMM), each wave cycling
 // through 4 A and 4 B fragments (16 bytes per lane each) into 4 independent accumulator
@@ -30,7 +33,22 @@ __device__ __forceinline__ uint32_t pm_hash(uint32_t x)
     return x;
 }
 
-__global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, int random_data, int *__restrict__ out)
+// four bytes of one operand register; kind 0 constant, 1 uniform, 2 bell-shaped
+__device__ __forceinline__ int pm_word(uint32_t seed, int kind)
+{
+    if (kind == 0) return 0x01010101;
+    if (kind == 1) return (int)pm_hash(seed);
+    uint32_t w = 0;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const uint32_t h = pm_hash(seed * 4u + q);
+        const int sum = (int)(h & 0xff) + (int)((h >> 8) & 0xff) + (int)((h >> 16) & 0xff) + (int)(h >> 24);
+        w |= (uint32_t)(uint8_t)(((sum - 510) * 7) >> 5) << (8 * q);
+    }
+    return (int)w;
+}
+
+__global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, int kind, int *__restrict__ out)
 {
     const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
     pm_v4i a[4], b[4];
@@ -38,8 +56,8 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, int random_d
     for (int f = 0; f < 4; f++)
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            a[f][e] = random_data ? (int)pm_hash(gid * 131u + f * 17u + e) : 0x01010101;
-            b[f][e] = random_data ? (int)pm_hash(gid * 977u + f * 29u + e + 7u) : 0x01010101;
+            a[f][e] = pm_word(gid * 131u + f * 17u + e, kind);
+            b[f][e] = pm_word(gid * 977u + f * 29u + e + 7u, kind);
         }
     pm_v16i acc[4];
 #pragma unroll
@@ -61,10 +79,9 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, int random_d
     out[gid] = total;                              // keeps the chains live
 }
 
-hipError_t launch_probe_mfma(int cus, int iters, bool random_data, int *out, hipStream_t st)
+hipError_t launch_probe_mfma(int cus, int iters, int kind, int *out, hipStream_t st)
 {
-    hipLaunchKernelGGL(probe_mfma_kernel, dim3((unsigned)(2 * cus)), dim3(256), 0, st, iters,
-                       random_data ? 1 : 0, out);
+    hipLaunchKernelGGL(probe_mfma_kernel, dim3((unsigned)(2 * cus)), dim3(256), 0, st, iters, kind, out);
     return hipGetLastError();
 }
 

@@ -236,6 +236,8 @@ def test_probe_validation():
     assert L.cr_probe_mfma_i8(1, 10, None, 1 << 20, C.byref(ops), ST) == INV
     assert L.cr_probe_mfma_i8(1, 10, A16, 1 << 20, None, ST) == INV
     assert L.cr_probe_mfma_i8(1, 10, A16 + 2, 1 << 20, C.byref(ops), ST) == MIS
+    assert L.cr_probe_mfma_i8(-1, 10, A16, 1 << 20, C.byref(ops), ST) == INV        # data kind
+    assert L.cr_probe_mfma_i8(3, 10, A16, 1 << 20, C.byref(ops), ST) == INV
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="valid arguments would launch on a real GPU")

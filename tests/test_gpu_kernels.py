@@ -411,24 +411,26 @@ def test_block_transposed_weight_and_gemm(N, K):
 # ------------------------------------------------------------ diagnostic probe ----
 
 def test_probe_mfma_rates_are_plausible():
-    """The register-only MFMA probe runs and reports rates below the published peak, with
-    constant operands at least as fast as random ones (the power limit bites on toggling
-    bits)."""
+    """The register-only MFMA probe runs for every data kind and reports rates below the
+    published peak, with constant operands at least as fast as random ones (the power limit
+    bites on toggling bits) and bell-shaped operands close to uniform ones."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     out = torch.empty(512 * cus, dtype=torch.int32, device=dev())
     rates = {}
-    for rnd in (True, False):
+    for kind in (rbl.CR_PROBE_UNIFORM, rbl.CR_PROBE_BELL, rbl.CR_PROBE_CONSTANT):
         for _ in range(2):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            say(f"cr_probe_mfma_i8 random={rnd}")
+            say(f"cr_probe_mfma_i8 kind={kind}")
             a.record()
-            ops = rbl.cr_probe_mfma_i8(rnd, 2000, out)
+            ops = rbl.cr_probe_mfma_i8(kind, 10000, out)
             b.record()
             torch.cuda.synchronize()
-            rates[rnd] = ops / (a.elapsed_time(b) * 1e-3) / 1e12
-    assert ops == 2.0 * 32768 * 16 * 2000 * 8 * cus
-    assert 100.0 < rates[True] <= 5000.0 * 1.05, rates
-    assert rates[False] >= 0.9 * rates[True], rates
+            rates[kind] = ops / (a.elapsed_time(b) * 1e-3) / 1e12
+        assert ops == 2.0 * 32768 * 16 * 10000 * 8 * cus
+    for r in rates.values():
+        assert 100.0 < r <= 5000.0 * 1.05, rates
+    assert rates[rbl.CR_PROBE_CONSTANT] >= 0.9 * rates[rbl.CR_PROBE_UNIFORM], rates
+    assert rates[rbl.CR_PROBE_BELL] >= 0.9 * rates[rbl.CR_PROBE_UNIFORM], rates
 
 
 # ------------------------------------------------------ rows per workgroup sweep ----

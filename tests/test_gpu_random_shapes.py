@@ -31,7 +31,7 @@ def _case(i):
     return M, N, K, xdt, odt, swiglu, order, extra
 
 
-CASES = [_case(i) for i in range(40)]
+CASES = [_case(i) for i in range(120)]
 
 
 def _ids(c):
