@@ -20,7 +20,8 @@
 // so LDS latency, the barrier and the DMA issue all overlap queued MFMA work.
 // Tiles are assigned so that all XCDs (workgroup id mod 8 on this part) work on one chip
 // block at a time, each on a compact sub-block: L2 reuse inside an XCD, and one MALL-resident
-// working set for the whole chip.
+// working set for the whole chip (the XCDs form a 2 x 4 grid over a square chip block, so a
+// round of workgroups touches as few distinct operand bands as possible).
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
 #include <hip/hip_fp16.h>
@@ -67,6 +68,8 @@ constexpr int CPR = GBK / 16;                      // 16-byte chunks per LDS row
 constexpr int RPP = 1024 / GBK;                    // rows per 1 KB DMA piece
 constexpr int GROUP_M = 8;
 constexpr int NUM_XCD = 8;
+constexpr int XCD_M = 2, XCD_N = 4;              // the XCDs' grid over a chip block
+static_assert(XCD_M * XCD_N == NUM_XCD, "XCD grid");
 constexpr int STAGE_A = GBM * GBK, STAGE_B = GBN * GBK;
 constexpr int PIECES = (STAGE_A + STAGE_B) / 1024;  // 1 KB DMA pieces per stage
 constexpr int PPW = PIECES / GWAVES;                 // pieces per wave per stage
@@ -135,29 +138,33 @@ void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__re
 #endif
 
     // ---- tile id.  Workgroup pid runs on XCD pid % 8, as its idx-th workgroup there.
-    //      Chip blocks of (8 XA) x XB tiles: all XCDs work on the same block at the same
-    //      time (its operand bands are fetched once from HBM into the MALL and shared),
-    //      each on an XA x XB sub-block (L2 reuse inside the XCD); blocks advance along N
-    //      so consecutive blocks share their A bands.  Tiles outside whole blocks are split
-    //      XCD-contiguously afterwards, in groups of GROUP_M M-tiles. ----
+    //      Chip blocks of (XCD_M XA) x (XCD_N XB) tiles: all XCDs work on the same block at
+    //      the same time (its operand bands are fetched once from HBM into the MALL and
+    //      shared), XCD x on the XA x XB sub-block at row x / XCD_N, column x % XCD_N of the
+    //      block (L2 reuse inside the XCD); blocks advance along N so consecutive blocks
+    //      share their A bands.  With 256 x 256 tiles the square 16 x 16 block reads 32
+    //      operand bands per round of 256 workgroups where a 64 x 4 block reads 68: with
+    //      K_pad = 14336 that is 117 MB instead of 250 MB, which the MALL can hold.  Tiles
+    //      outside whole blocks are split XCD-contiguously afterwards, in groups of GROUP_M
+    //      M-tiles. ----
     const int pid = blockIdx.x;
     const int xcd = pid % NUM_XCD, idx = pid / NUM_XCD;
-    int xa = 8;                                      // largest power of two <= 8 with 8 xa <= tiles_m
-    while (xa > 1 && NUM_XCD * xa > tiles_m) xa >>= 1;
+    int xa = 8;                                      // largest power of two <= 8 with XCD_M xa <= tiles_m
+    while (xa > 1 && XCD_M * xa > tiles_m) xa >>= 1;
     const int xb = 32 / xa;
-    const int nbm = tiles_m / (NUM_XCD * xa), nbn = tiles_n / xb;
+    const int nbm = tiles_m / (XCD_M * xa), nbn = tiles_n / (XCD_N * xb);
     const int main_per_xcd = nbm * nbn * xa * xb;
     int tm, tn;
     if (idx < main_per_xcd) {
         const int blk = idx / (xa * xb), j = idx % (xa * xb);
         const int bm = blk / nbn, bn = blk % nbn;
-        tm = bm * (NUM_XCD * xa) + xcd * xa + j % xa;
-        tn = bn * xb + j / xa;
+        tm = bm * (XCD_M * xa) + (xcd / XCD_N) * xa + j % xa;
+        tn = bn * (XCD_N * xb) + (xcd % XCD_N) * xb + j / xa;
     } else {
         const int trem = tiles_m * tiles_n - main_per_xcd * NUM_XCD;
         const int rq = trem / NUM_XCD, rr = trem % NUM_XCD;
         int r = ((xcd < rr) ? xcd * (rq + 1) : rr * (rq + 1) + (xcd - rr) * rq) + (idx - main_per_xcd);
-        const int mm = nbm * NUM_XCD * xa, nn = nbn * xb;
+        const int mm = nbm * XCD_M * xa, nn = nbn * XCD_N * xb;
         int h, w, bm0, bn0;
         if (r < mm * (tiles_n - nn)) {              // right strip beside the blocks
             h = mm; w = tiles_n - nn; bm0 = 0; bn0 = nn;
