@@ -268,9 +268,10 @@ __global__ __launch_bounds__(1024) void quant_act_multi_kernel(Loader ld, int64_
 
 template <class Loader>
 static hipError_t launch_rows(const Loader &L, int64_t rows, int64_t nb, int8_t *out, int64_t ld_out,
-                              float *scale, bool force_two_pass, bool transposed, hipStream_t st)
+                              float *scale, bool force_two_pass, bool transposed, hipStream_t st,
+                              int one_pass_groups = kMaxGroups2)
 {
-    const RowPrepShape s = row_prep_shape(nb, force_two_pass);
+    const RowPrepShape s = row_prep_shape(nb, force_two_pass, one_pass_groups);
     const size_t lds = row_prep_lds_bytes(s.threads);
     const int mode = (s.two_pass ? 1 : 0) | (transposed ? 2 : 0);
     const int rpw = (!s.two_pass && nb <= 32) ? row_prep_multi_rows(nb) : 1;
@@ -321,8 +322,11 @@ static hipError_t launch_swiglu(const void *h, int64_t ld_h, int64_t M, int64_t 
     const bool val_ok = row_ok && ((F * es) % 16 == 0);
     const auto *hp = static_cast<const typename Elem<DT>::T *>(h);
     const int64_t nb = (F + 255) / 256;
-    if (pre) return launch_rows(SwigluLoader<DT, true>{hp, ld_h, F, row_ok, val_ok, pre}, M, nb, x_s8, ld_s8, x_scale, two_pass, transposed, st);
-    return launch_rows(SwigluLoader<DT, false>{hp, ld_h, F, row_ok, val_ok, nullptr}, M, nb, x_s8, ld_s8, x_scale, two_pass, transposed, st);
+    if (pre)
+        return launch_rows(SwigluLoader<DT, true>{hp, ld_h, F, row_ok, val_ok, pre}, M, nb, x_s8, ld_s8, x_scale,
+                           two_pass, transposed, st, kMaxGroupsWide);
+    return launch_rows(SwigluLoader<DT, false>{hp, ld_h, F, row_ok, val_ok, nullptr}, M, nb, x_s8, ld_s8, x_scale,
+                       two_pass, transposed, st, kMaxGroupsWide);
 }
 
 hipError_t launch_quant_act(const void *x, int dtype, int64_t ld_x, int64_t M, int64_t K, const float *pre,

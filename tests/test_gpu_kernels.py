@@ -435,10 +435,12 @@ def test_probe_mfma_rates_are_plausible():
 
 # ------------------------------------------------------ rows per workgroup sweep ----
 
-@pytest.mark.parametrize("nb", list(range(1, 33)))
+@pytest.mark.parametrize("nb", list(range(1, 65)))
 def test_every_short_row_shape_bit_exact(nb):
-    """Rows of 1..32 blocks (ragged K = 256 nb - 7), where several rows share a workgroup:
-    activation, SwiGLU, weight and row-maximum preparation, bit-exact against the oracle,
+    """Rows of 1..64 blocks (ragged K = 256 nb - 7): up to 32 blocks several rows share a
+    workgroup; SwiGLU rows of 33..64 blocks hold one block per lane group, plain activation
+    and weight rows two.
+    Activation, SwiGLU, weight and row-maximum preparation, bit-exact against the oracle,
     with a row count that leaves the last set of rows of a workgroup incomplete."""
     K = 256 * nb - 7
     M = 37
