@@ -30,6 +30,9 @@
  *     in 32 bits.  Larger shapes return CR_ERR_TOO_LARGE; split them along M or N.
  *   - Rows are independent.  A row whose maximum |value| after rotation is 0 gets scale 0
  *     and all-zero codes.
+ *   - Inputs are assumed finite.  A NaN or an infinity in an activation row, or a NaN E4M3
+ *     block scale in a weight row, leaves that row's codes, scale and outputs unspecified;
+ *     every other row is unaffected (bit for bit), and the call still completes.
  *
  * Arithmetic (binary32, round to nearest even; each step evaluated exactly as written):
  *   NVFP4 element k of weight row n: code = nibble k of the row (low nibble of byte k/2

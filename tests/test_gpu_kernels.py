@@ -275,6 +275,56 @@ def test_layer_tiny_full():
     print(f"tiny: rel_l2={err:.3e} bit-identical fraction={exact:.4f}")
 
 
+# ------------------------------------------------ non-finite inputs stay local ----
+
+NF_CASES = [
+    # K, swiglu, forced two-pass: several rows per workgroup, one and two blocks per lane
+    # group, SwiGLU one block per group, forced and size-driven two-pass
+    (1000, False, False), (10000, False, False), (14336, True, False), (1000, True, True),
+    (17000, False, False),
+]
+
+
+@pytest.mark.parametrize("K,swiglu,forced", NF_CASES, ids=[f"K{c[0]}-sw{int(c[1])}-tp{int(c[2])}" for c in NF_CASES])
+def test_non_finite_rows_leave_other_rows_exact(K, swiglu, forced):
+    """Inputs are assumed finite; a NaN or an infinity leaves its own row's codes, scale and
+    outputs unspecified, but every other row stays bit-exact (rows are prepared independently,
+    also where several share a workgroup), for activations, SwiGLU, NVFP4 weights (a NaN E4M3
+    block scale) and the whole layer."""
+    M, N = 70, 300                                       # 70 rows: the layer stages S8 weight tiles
+    cols = 2 * K if swiglu else K
+    x = make_x(M, cols, synth.DT_BF16, seed=K + 7)
+    x[5, 17] = float("nan")
+    x[9, cols - 1] = float("inf")
+    x[12, cols // 2] = float("-inf")
+    x[66, 0] = float("nan")
+    bad = [5, 9, 12, 66]
+    good = [i for i in range(M) if i not in bad]
+    flags = rbl.CR_FLAG_FORCE_TWO_PASS if forced else 0
+    say(f"non-finite rows K={K} swiglu={swiglu} forced={forced}: quant_act")
+    q, s = rbl.quant_act(x.to(dev()), K, swiglu=swiglu, flags=flags)
+    p = synth.nvfp4_encode(0.02 * torch.randn(N, K, generator=torch.Generator().manual_seed(K)))
+    sf_bad = p.sf.clone()
+    sf_bad[7, 2] = 0x7F                                  # E4M3 NaN
+    gs = torch.tensor([p.g], dtype=torch.float32, device=dev())
+    say(f"non-finite rows K={K}: prep_weight with a NaN block scale, layer")
+    qw, sw = rbl.prep_weight_nvfp4(p.codes.to(dev()), sf_bad.to(dev()), gs, K, flags=flags)
+    out = rbl.linear_nvfp4(x.to(dev()), p.codes.to(dev()), p.sf.to(dev()), gs, K, swiglu=swiglu, flags=flags)
+    torch.cuda.synchronize()
+    xb = synth.bits_u16(x)[good]
+    rq, rs = oracle.quant_act(xb, synth.DT_BF16, K, swiglu=swiglu)
+    assert_bits_equal(q.cpu().numpy()[good], rq, "x_s8 of the finite rows")
+    assert_bits_equal(s.cpu().numpy()[good].view(np.uint32), rs.view(np.uint32), "x_scale of the finite rows")
+    wgood = [i for i in range(N) if i != 7]
+    rqw, rsw = oracle.prep_weight_nvfp4(p.codes.numpy()[wgood], p.sf.numpy()[wgood], p.g, K)
+    assert_bits_equal(qw.cpu().numpy()[wgood], rqw, "w_s8 of the finite rows")
+    assert_bits_equal(sw.cpu().numpy()[wgood].view(np.uint32), rsw.view(np.uint32), "w_scale of the finite rows")
+    ref = oracle.linear_nvfp4(xb, synth.DT_BF16, K, swiglu, p.codes.numpy(), p.sf.numpy(), p.g, synth.DT_BF16)
+    got = out.cpu()[good]
+    err = rel_l2(out_f64(got, synth.DT_BF16), out_f64(ref, synth.DT_BF16))
+    assert err <= TOL[synth.DT_BF16], err
+
+
 # ------------------------------------------------ channel pre-scale and bias ----
 
 PRE_CASES = [
@@ -283,7 +333,8 @@ PRE_CASES = [
     (synth.DT_FP16, 9, 5376, False, False),
     (synth.DT_FP32, 5, 16385, False, False),        # two-pass by size
     (synth.DT_BF16, 7, 700, True, False),
-    (synth.DT_BF16, 4, 14336, True, False),         # two blocks per lane group
+    (synth.DT_BF16, 4, 14336, True, False),         # 56-block SwiGLU rows: one block per lane group
+    (synth.DT_BF16, 4, 14336, False, False),        # 56-block plain rows: two blocks per lane group
     (synth.DT_BF16, 6, 1000, False, True),          # forced two-pass
 ]
 
