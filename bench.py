@@ -34,9 +34,9 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 BT = 2                       # CR_FLAG_BLOCK_TRANSPOSED: the order cr_linear_nvfp4 uses inside
 # Decode-inside-GEMM: vector instructions per weight element at the minimum (decode: one
 # conversion per two elements and two multiplies; rotation: 8 butterfly adds; quantization:
-# multiply, clamp, rounding add and 3/4 of a byte permute) and the chip's vector issue peak
-# with one fp32 operation per lane per clock (256 CUs x 64 lanes x 2.4 GHz; no packed math).
-FUSED_VALU_PER_ELEM = 14.25
+# multiply, rounding add and 3/4 of a byte permute) and the chip's vector issue peak with one
+# fp32 operation per lane per clock (256 CUs x 64 lanes x 2.4 GHz; no packed math).
+FUSED_VALU_PER_ELEM = 13.25
 PEAK_VALU_TOPS = 39.3
 GEMM_SOURCES = ["rotated_bit_linear_amd/csrc/gemm_s8.hip"]
 PMC_PROFILE = os.path.join(ROOT, "profiles", "gemm_s8_qkv_m19989_hbm_counters.md")

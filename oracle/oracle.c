@@ -31,7 +31,8 @@
  *                    h = 1, 2, ..., 128 and butterflies (u+v, u-v), then *0.0625;
  *   quantizer        a = max|y|; s = a/127; r = 127/a, itself rounded to FP32 and reused
  *                    for the whole row; q = clamp(rint(y*r), -127, 127); a zero row
- *                    gives s = 0 and q = 0;
+ *                    gives s = 0 and q = 0; a row whose 127/a overflows (a < ~3.7e-37)
+ *                    is quantized as its exact copy scaled by 2^64;
  *   NVFP4 layout     element k of row n is the nibble of byte n*ld + k/2 (low nibble for
  *                    even k); block scale of k is the E4M3 byte n*ld_sf + k/16; decoded
  *                    value = fp32(E2M1 * E4M3) * g (the first product is exact);
@@ -257,7 +258,12 @@ void or_convrot256(float *y, int64_t n_rows, int64_t K_pad, int64_t ld)
 
 /* Symmetric per-row INT8 quantization with an FP32 scale:
  * a = max_k |y_k| over all K_pad columns; a == 0 -> s = 0, every q = 0;
- * else s = a/127, r = 127/a (one FP32 reciprocal per row), q = clamp(rint(y*r), -127, 127). */
+ * else s = a/127, r = 127/a (one FP32 reciprocal per row), q = clamp(rint(y*r), -127, 127).
+ * For a below about 3.7e-37, 127/a overflows FP32 and y*r would be +-inf or NaN (0*inf);
+ * wherever r is finite the codes do not change when the whole row is multiplied by a power
+ * of two (every product involved scales exactly), so such a row is quantized as its copy
+ * multiplied by 2^64, which is exact and brings r back into range.  s stays a/127 of the row
+ * as given. */
 void or_row_quant(const float *y, int64_t n_rows, int64_t K_pad, int64_t ld_y,
                   int8_t *q, int64_t ld_q, float *s)
 {
@@ -275,9 +281,10 @@ void or_row_quant(const float *y, int64_t n_rows, int64_t K_pad, int64_t ld_y,
             continue;
         }
         s[n] = a / 127.0f;
-        float r = 127.0f / a;
+        const float up = isinf(127.0f / a) ? 0x1p64f : 1.0f;
+        float r = 127.0f / (a * up);
         for (int64_t k = 0; k < K_pad; k++) {
-            float t = rintf(row[k] * r);
+            float t = rintf((row[k] * up) * r);
             if (t > 127.0f) t = 127.0f;
             if (t < -127.0f) t = -127.0f;
             q[n * ld_q + k] = (int8_t)t;

@@ -17,10 +17,16 @@
 // r = 127 / a; and when a' >= 2^-100, y * r = z * (r * 0.0625) exactly for every element
 // that can round to a nonzero code (scaling by 2^-4 is exact for normal numbers, and
 // elements so small that z * 0.0625 is subnormal give |y * r| < 2^-15 either way, hence
-// code 0).  Rows with 0 < a' < 2^-100 scale every element as written.  Either way the
-// codes and the scale a / 127 are those of the plain definition, bit for bit.
+// code 0).  Rows with 0 < a' < 2^-100 scale every element as written and then multiply
+// it by 2^64 (exact), with r = 127 / (a * 2^64): where 127 / a is a finite FP32 value
+// (a >= ~3.7e-37) r is that value times 2^-64 exactly (both lie in the normal range), so
+// the products and codes are unchanged, and where it overflows this is the definition of
+// the quantizer for such rows (the row's exact copy scaled by 2^64).  Either way the codes
+// and the scale a / 127 are those of the definition, bit for bit.
 //
-// Codes: q = clamp(rint(y * r), -127, 127); clamping first and then adding 1.5 * 2^23
+// Codes: q = clamp(rint(y * r), -127, 127).  With |y| <= a and r = RN(127 / a),
+// |y * r| <= 127 (1 + 2^-24), whose FP32 rounding is at most 127 + 2^-17: rint never
+// leaves [-127, 127] for a finite row, so no clamp is evaluated.  Adding 1.5 * 2^23
 // rounds to the nearest integer, ties to even, and leaves q in two's complement in the
 // low byte of the sum (the sum lies in [2^23, 2^24), where the spacing is 1).
 //
@@ -158,10 +164,10 @@ __device__ __forceinline__ float block_max(float a, float *red)
     return m;
 }
 
-// clamp(rint(t), -127, 127) in two's complement in the low byte of the result
+// rint(t) in two's complement in the low byte of the result, for |t| < 128 (the
+// quantizer's products satisfy |t| <= 127 + 2^-17, so clamping to +-127 is a no-op)
 __device__ __forceinline__ uint32_t code_bits(float t)
 {
-    t = fminf(fmaxf(t, -127.0f), 127.0f);
     return __float_as_uint(t + 12582912.0f);
 }
 
@@ -174,14 +180,15 @@ __device__ __forceinline__ uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint3
 }
 
 // Codes of 16 butterfly outputs z, stored as 16 contiguous bytes: of z * m with
-// m = r * 0.0625 (folded), or of (z * 0.0625) * m with m = r (kScaleFirst).
+// m = r * 0.0625 (folded), or of ((z * 0.0625) * 2^64) * m with m = 127 / (a * 2^64)
+// (kScaleFirst, rows with a' < 2^-100).
 template <bool kScaleFirst>
 __device__ __forceinline__ void quantize_store16(const float (&z)[16], float m, int8_t *dst)
 {
     uint32_t c[16];
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-        const float y = kScaleFirst ? z[i] * 0.0625f : z[i];
+        const float y = kScaleFirst ? (z[i] * 0.0625f) * 0x1p64f : z[i];
         c[i] = code_bits(y * m);
     }
     uint4 o;
@@ -195,7 +202,7 @@ __device__ __forceinline__ void quantize_store16(const float (&z)[16], float m, 
 // Row constants from a' = max |z|: the scale a / 127 and the code multiplier.
 struct RowQuant {
     float scale;    // a / 127 (0 when a == 0)
-    float mult;     // r * 0.0625 (folded) or r (scale first)
+    float mult;     // r * 0.0625 (folded) or 127 / (a * 2^64) (scale first)
     bool folded;    // block-uniform
 };
 
@@ -206,7 +213,7 @@ __device__ __forceinline__ RowQuant row_quant(float zmax)
     RowQuant q;
     q.scale = (a == 0.0f) ? 0.0f : a / 127.0f;
     q.folded = zmax >= 0x1p-100f;
-    q.mult = q.folded ? r * 0.0625f : r;
+    q.mult = q.folded ? r * 0.0625f : 127.0f / (a * 0x1p64f);
     return q;
 }
 

@@ -109,3 +109,30 @@ def test_quant_uses_row_reciprocal_not_division(orc):
     q, _ = orc.row_quant(y[rows])
     assert np.array_equal(q.astype(np.float32), np.clip(via_r[rows], -127, 127))
     assert not np.array_equal(q.astype(np.float32), np.clip(via_s[rows], -127, 127))
+
+
+def test_quant_rows_whose_reciprocal_overflows(orc):
+    """Rows with max |y| below 127/FLT_MAX (~3.7e-37), where 127/a is not a finite FP32
+    value.  Pinned without the oracle's formula: (1) the codes equal those of the same row
+    at normal magnitude (the rows are exact power-of-two copies: multiples of 2^-11 stay
+    exact down to 2^-147), (2) the fp64 error bound |127*y/a - q| <= 1/2 holds (a sign-only
+    quantization, what an infinite r gives, fails it), (3) zero elements give code 0."""
+    rng = np.random.default_rng(7)
+    y = (rng.integers(-2047, 2048, (24, 512)) * 2.0 ** -11).astype(np.float32)
+    y[:, ::7] = 0.0
+    y[3, :] = 0.0
+    y[3, 100] = 1.5                                  # one nonzero element
+    for shift in (-124, -130, -136):           # normal, partly and mostly subnormal rows
+        yt = (y.astype(np.float64) * 2.0 ** shift).astype(np.float32)
+        assert np.array_equal(yt.astype(np.float64) * 2.0 ** -shift, y.astype(np.float64))   # exact copies
+        a = np.abs(yt).max(axis=1)
+        with np.errstate(over="ignore", divide="ignore"):
+            assert np.isinf(np.float32(127) / a).all()          # the reciprocal overflows
+        q, s = orc.row_quant(yt)
+        q0, _ = orc.row_quant(y)
+        assert np.array_equal(q, q0)
+        t = 127.0 * yt.astype(np.float64) / a[:, None].astype(np.float64)
+        assert (np.abs(t - q) <= 0.5 * (1 + 2 ** -20)).all()
+        assert (q[yt == 0] == 0).all()
+        assert (np.abs(q).max(axis=1) == 127).all()
+        assert np.array_equal(s, (a / np.float32(127)).astype(np.float32))
