@@ -28,6 +28,11 @@
  *   - A GEMM may have at most 8388607 output tiles of 256 x 256 (ceil(M/256) * ceil(N/256)),
  *     and cr_gemm_nvfp4_fused at most 536870880 weight rows: a dispatch counts its work-items
  *     in 32 bits.  Larger shapes return CR_ERR_TOO_LARGE; split them along M or N.
+ *   - Empty extents: a row count M (or n_rows) or an output width N of 0 is a valid call
+ *     that enqueues nothing and returns CR_OK once the other arguments pass the checks
+ *     that do not depend on the empty extent (dtypes, flags, K >= 1, strides); buffers of
+ *     zero size may be NULL.  K (or F) must be at least 1: the layer has at least one
+ *     input column.  Negative sizes are CR_ERR_INVALID_ARG.
  *   - Rows are independent.  A row whose maximum |value| after rotation is 0 gets scale 0
  *     and all-zero codes.
  *   - Inputs are assumed finite.  A NaN or an infinity in an activation row, or a NaN E4M3
@@ -46,7 +51,9 @@
  *   Rotation: per 256-block, butterfly stages h = 1, 2, ..., 128 ((u, v) -> (u+v, u-v)
  *     on the pair j, j+h), then * 0.0625.
  *   Row quantization: a = max |y|; scale = a / 127; r = 127 / a; q = clamp(rint(y * r),
- *     -127, 127).
+ *     -127, 127).  A row whose 127 / a overflows FP32 (a below about 3.7e-37) is quantized
+ *     as its exact copy multiplied by 2^64 (the codes of a row do not change under exact
+ *     power-of-two scaling wherever r is finite); its scale is still a / 127.
  *   Epilogue: out = ((float)acc * a_scale[m]) * b_scale[n], rounded once to the output type.
  */
 #ifndef CONVROT_H
@@ -67,7 +74,7 @@ extern "C" {
 
 typedef enum {
     CR_OK = 0,
-    CR_ERR_INVALID_ARG = 1,       /* null pointer, size < 1, stride too small, bad flag */
+    CR_ERR_INVALID_ARG = 1,       /* null pointer, negative size, K < 1, stride too small, bad flag */
     CR_ERR_UNSUPPORTED_DTYPE = 2, /* dtype not accepted by this entry point */
     CR_ERR_MISALIGNED = 3,        /* base pointer or row stride alignment violated */
     CR_ERR_TOO_LARGE = 4,         /* K_pad > CR_MAX_K_PAD, or workspace too small */
@@ -203,7 +210,8 @@ cr_status cr_gemm_s8_rowscale_bias(const int8_t *a_s8, int64_t lda, const float 
  *   out [M, ldc] of out_dtype (not CR_I32).
  *   workspace  device buffer of at least cr_linear_nvfp4_workspace_bytes(...) bytes,
  *              256-byte aligned; holds the S8 activation, its scales and the S8 weight
- *              tiles (two when the weight is chunked).
+ *              tiles (two when the weight is chunked).  An empty layer (M or N = 0)
+ *              needs none: the size is 0 and workspace, x and out may be NULL.
  *   max_tile_bytes  bound of one S8 weight tile (0 selects CR_DEFAULT_MAX_TILE_BYTES);
  *              tiles hold a multiple of 256 rows (at least 256).
  *   s_main     stream of the activation preparation and the GEMMs.
@@ -224,7 +232,8 @@ size_t cr_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t m
  * weight that fits one chunk is still split in two when the two GEMMs need no more
  * workgroup rounds over the device's compute units than one (the second chunk is then
  * prepared while the first multiplies).  Both are 0 for short batches (M <= 64), which
- * decode the weight inside the GEMM.  Host pointers; CR_OK or an argument status. */
+ * decode the weight inside the GEMM, and for an empty layer (M or N = 0, which needs no
+ * workspace and launches nothing).  Host pointers; CR_OK or an argument status. */
 cr_status cr_linear_nvfp4_plan(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes,
                                int64_t *rows_per_chunk, int64_t *nchunks);
 

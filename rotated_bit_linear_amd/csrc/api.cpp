@@ -68,9 +68,9 @@ cr_status check_flags(uint32_t flags)
 cr_status check_act(const void *x, cr_dtype dt, int64_t ld_x, int64_t M, int64_t K, int64_t cols,
                     int8_t *x_s8, int64_t ld_s8, float *x_scale, uint32_t flags)
 {
-    if (!x || !x_s8 || !x_scale) return CR_ERR_INVALID_ARG;
+    if (M > 0 && (!x || !x_s8 || !x_scale)) return CR_ERR_INVALID_ARG;   // M = 0: nothing is read or written
     if (dt != CR_BF16 && dt != CR_FP16 && dt != CR_FP32) return CR_ERR_UNSUPPORTED_DTYPE;
-    if (M < 1 || K < 1 || M > kMaxRows) return CR_ERR_INVALID_ARG;
+    if (M < 0 || K < 1 || M > kMaxRows) return CR_ERR_INVALID_ARG;
     if (check_flags(flags) != CR_OK) return CR_ERR_INVALID_ARG;
     const int64_t kp = pad256(K);
     if (kp > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
@@ -85,8 +85,8 @@ cr_status check_weight(const uint8_t *w_fp4, int64_t ld_fp4, const uint8_t *w_sf
                        const float *g, int64_t n_rows, int64_t K, int8_t *w_s8, int64_t ld_s8,
                        float *w_scale, uint32_t flags)
 {
-    if (!w_fp4 || !w_sf || !g || !w_s8 || !w_scale) return CR_ERR_INVALID_ARG;
-    if (n_rows < 1 || K < 1 || n_rows > kMaxRows) return CR_ERR_INVALID_ARG;
+    if (n_rows > 0 && (!w_fp4 || !w_sf || !g || !w_s8 || !w_scale)) return CR_ERR_INVALID_ARG;
+    if (n_rows < 0 || K < 1 || n_rows > kMaxRows) return CR_ERR_INVALID_ARG;
     if (check_flags(flags) != CR_OK) return CR_ERR_INVALID_ARG;
     const int64_t kp = pad256(K);
     if (kp > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
@@ -101,10 +101,10 @@ cr_status check_gemm(const int8_t *a, int64_t lda, const float *sa, const int8_t
                      const float *sb, int64_t M, int64_t N, int64_t K_pad, void *c, cr_dtype cdt,
                      int64_t ldc)
 {
-    if (!a || !b || !c) return CR_ERR_INVALID_ARG;
+    if ((M > 0 && !a) || (N > 0 && !b) || (M > 0 && N > 0 && !c)) return CR_ERR_INVALID_ARG;
     if (cdt != CR_BF16 && cdt != CR_FP16 && cdt != CR_FP32 && cdt != CR_I32) return CR_ERR_UNSUPPORTED_DTYPE;
-    if (cdt != CR_I32 && (!sa || !sb)) return CR_ERR_INVALID_ARG;
-    if (M < 1 || N < 1 || K_pad < 1 || K_pad % 256 != 0) return CR_ERR_INVALID_ARG;
+    if (cdt != CR_I32 && ((M > 0 && !sa) || (N > 0 && !sb))) return CR_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K_pad < 1 || K_pad % 256 != 0) return CR_ERR_INVALID_ARG;
     if (M > kMaxRows || N > kMaxRows) return CR_ERR_INVALID_ARG;
     // one workgroup of 512 threads per 256 x 256 tile; a dispatch counts work-items in 32 bits
     if (((M + 255) / 256) * ((N + 255) / 256) > (int64_t)(UINT32_MAX / 512)) return CR_ERR_TOO_LARGE;
@@ -121,12 +121,12 @@ cr_status check_fused(const int8_t *a_s8, int64_t lda, const float *a_scale, con
                       const float *bias, int64_t M, int64_t N, int64_t K, void *c, cr_dtype c_dtype, int64_t ldc,
                       uint32_t flags)
 {
-    if (!a_s8 || !w_fp4 || !w_sf || !g || !c) return CR_ERR_INVALID_ARG;
+    if ((M > 0 && !a_s8) || (N > 0 && (!w_fp4 || !w_sf || !g)) || (M > 0 && N > 0 && !c)) return CR_ERR_INVALID_ARG;
     if (c_dtype != CR_BF16 && c_dtype != CR_FP16 && c_dtype != CR_FP32 && c_dtype != CR_I32)
         return CR_ERR_UNSUPPORTED_DTYPE;
-    if (c_dtype != CR_I32 && !a_scale) return CR_ERR_INVALID_ARG;
+    if (c_dtype != CR_I32 && M > 0 && !a_scale) return CR_ERR_INVALID_ARG;
     if (bias && c_dtype == CR_I32) return CR_ERR_INVALID_ARG;
-    if (M < 1 || N < 1 || K < 1 || M > kMaxRows || N > kMaxRows) return CR_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 1 || M > kMaxRows || N > kMaxRows) return CR_ERR_INVALID_ARG;
     if (check_flags(flags) != CR_OK) return CR_ERR_INVALID_ARG;
     const int64_t kp = pad256(K);
     if (kp > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
@@ -194,6 +194,7 @@ LayerPlan plan_layer(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes)
     LayerPlan p{};
     if (max_tile_bytes == 0) max_tile_bytes = CR_DEFAULT_MAX_TILE_BYTES;
     p.K_pad = pad256(K);
+    if (M == 0 || N == 0) return p;                  // empty: no chunks, no workspace
     if (M <= kFusedMaxRows) {
         p.fused = true;
         p.off_xscale = up256((size_t)M * (size_t)p.K_pad);
@@ -259,7 +260,7 @@ cr_status cr_prep_weight_nvfp4(const uint8_t *w_fp4, int64_t ld_fp4, const uint8
                                uint32_t flags, hipStream_t stream)
 {
     cr_status s = check_weight(w_fp4, ld_fp4, w_sf, ld_sf, global_scale, n_rows, K, w_s8, ld_s8, w_scale, flags);
-    if (s != CR_OK) return s;
+    if (s != CR_OK || n_rows == 0) return s;
     if ((s = current_device_ok()) != CR_OK) return s;
     return from_hip(convrot::launch_prep_weight(w_fp4, ld_fp4, w_sf, ld_sf, global_scale, n_rows, K, w_s8,
                                                 ld_s8, w_scale, (flags & CR_FLAG_FORCE_TWO_PASS) != 0,
@@ -274,6 +275,7 @@ cr_status cr_quant_act_ex(const void *x, cr_dtype x_dtype, int64_t ld_x, int swi
     cr_status s = check_act(x, x_dtype, ld_x, M, K, swiglu ? 2 * K : K, x_s8, ld_s8, x_scale, flags);
     if (s != CR_OK) return s;
     if (pre_scale && !aligned(pre_scale, 4)) return CR_ERR_MISALIGNED;
+    if (M == 0) return CR_OK;
     if ((s = current_device_ok()) != CR_OK) return s;
     const bool tp = (flags & CR_FLAG_FORCE_TWO_PASS) != 0;
     const bool tr = (flags & CR_FLAG_BLOCK_TRANSPOSED) != 0;
@@ -297,11 +299,12 @@ cr_status cr_quant_act_swiglu(const void *h, cr_dtype h_dtype, int64_t ld_h, int
 cr_status cr_swiglu(const void *h, cr_dtype h_dtype, int64_t ld_h, int64_t M, int64_t F,
                     float *out, int64_t ld_out, hipStream_t stream)
 {
-    if (!h || !out) return CR_ERR_INVALID_ARG;
+    if (M > 0 && (!h || !out)) return CR_ERR_INVALID_ARG;
     if (h_dtype != CR_BF16 && h_dtype != CR_FP16 && h_dtype != CR_FP32) return CR_ERR_UNSUPPORTED_DTYPE;
-    if (M < 1 || F < 1 || F > ((int64_t)1 << 40) || M > ((int64_t)1 << 40) / F) return CR_ERR_INVALID_ARG;
+    if (M < 0 || F < 1 || F > ((int64_t)1 << 40) || M > ((int64_t)1 << 40) / F) return CR_ERR_INVALID_ARG;
     if (ld_h < 2 * F || ld_out < F) return CR_ERR_INVALID_ARG;
     if (!aligned(h, (size_t)elem_size(h_dtype)) || !aligned(out, 4)) return CR_ERR_MISALIGNED;
+    if (M == 0) return CR_OK;
     cr_status s = current_device_ok();
     if (s != CR_OK) return s;
     return from_hip(convrot::launch_swiglu(h, (int)h_dtype, ld_h, M, F, out, ld_out, stream));
@@ -316,6 +319,7 @@ cr_status cr_gemm_s8_rowscale_bias(const int8_t *a_s8, int64_t lda, const float 
     if (s != CR_OK) return s;
     if (bias && c_dtype == CR_I32) return CR_ERR_INVALID_ARG;
     if (bias && !aligned(bias, 4)) return CR_ERR_MISALIGNED;
+    if (M == 0 || N == 0) return CR_OK;
     if ((s = current_device_ok()) != CR_OK) return s;
     return from_hip(convrot::launch_gemm_s8(a_s8, lda, a_scale, b_s8, ldb, b_scale, bias, M, N, K_pad, c,
                                             (int)c_dtype, ldc, stream));
@@ -334,13 +338,14 @@ cr_status cr_weight_amax_nvfp4(const uint8_t *w_fp4, int64_t ld_fp4, const uint8
                                const float *global_scale, int64_t n_rows, int64_t K, float *w_amax,
                                uint32_t flags, hipStream_t stream)
 {
-    if (!w_fp4 || !w_sf || !global_scale || !w_amax) return CR_ERR_INVALID_ARG;
-    if (n_rows < 1 || K < 1 || n_rows > kMaxRows) return CR_ERR_INVALID_ARG;
+    if (n_rows > 0 && (!w_fp4 || !w_sf || !global_scale || !w_amax)) return CR_ERR_INVALID_ARG;
+    if (n_rows < 0 || K < 1 || n_rows > kMaxRows) return CR_ERR_INVALID_ARG;
     if (check_flags(flags) != CR_OK) return CR_ERR_INVALID_ARG;
     if (pad256(K) > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
     if (ld_fp4 < (K + 1) / 2 || ld_sf < (K + 15) / 16) return CR_ERR_INVALID_ARG;
     if (!aligned(w_fp4, 16) || ld_fp4 % 16 != 0) return CR_ERR_MISALIGNED;
     if (!aligned(global_scale, 4) || !aligned(w_amax, 4)) return CR_ERR_MISALIGNED;
+    if (n_rows == 0) return CR_OK;
     cr_status s = current_device_ok();
     if (s != CR_OK) return s;
     return from_hip(convrot::launch_weight_amax(w_fp4, ld_fp4, w_sf, ld_sf, global_scale, n_rows, K, w_amax,
@@ -355,7 +360,7 @@ cr_status cr_gemm_nvfp4_fused(const int8_t *a_s8, int64_t lda, const float *a_sc
 {
     cr_status s0 = check_fused(a_s8, lda, a_scale, w_fp4, ld_fp4, w_sf, ld_sf, global_scale, w_amax, bias, M, N, K,
                                c, c_dtype, ldc, flags);
-    if (s0 != CR_OK) return s0;
+    if (s0 != CR_OK || M == 0 || N == 0) return s0;
     cr_status s = current_device_ok();
     if (s != CR_OK) return s;
     return from_hip(convrot::launch_gemm_nvfp4_fused(a_s8, lda, a_scale, w_fp4, ld_fp4, w_sf, ld_sf, global_scale,
@@ -367,7 +372,7 @@ cr_status cr_linear_nvfp4_plan(int64_t M, int64_t N, int64_t K, size_t max_tile_
                                int64_t *rows_per_chunk, int64_t *nchunks)
 {
     if (!rows_per_chunk || !nchunks) return CR_ERR_INVALID_ARG;
-    if (M < 1 || N < 1 || K < 1) return CR_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 1) return CR_ERR_INVALID_ARG;
     if (pad256(K) > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
     const LayerPlan p = plan_layer(M, N, K, max_tile_bytes);
     *rows_per_chunk = p.R;
@@ -377,7 +382,7 @@ cr_status cr_linear_nvfp4_plan(int64_t M, int64_t N, int64_t K, size_t max_tile_
 
 size_t cr_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes)
 {
-    if (M < 1 || N < 1 || K < 1 || pad256(K) > CR_MAX_K_PAD) return 0;
+    if (M < 1 || N < 1 || K < 1 || pad256(K) > CR_MAX_K_PAD) return 0;   // an empty layer needs none
     return plan_layer(M, N, K, max_tile_bytes).bytes;
 }
 
@@ -389,11 +394,21 @@ cr_status cr_linear_nvfp4_ex(const void *x, cr_dtype x_dtype, int64_t ld_x, int 
                              void *workspace, size_t ws_bytes, size_t max_tile_bytes,
                              uint32_t flags, hipStream_t s_main, hipStream_t s_aux)
 {
-    if (!workspace || !out) return CR_ERR_INVALID_ARG;
     if (out_dtype == CR_I32) return CR_ERR_UNSUPPORTED_DTYPE;
-    if (M < 1 || N < 1 || K < 1) return CR_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 1) return CR_ERR_INVALID_ARG;
     if (swiglu && K > (int64_t)1 << 40) return CR_ERR_TOO_LARGE;
     if (pad256(K) > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
+    if (M == 0 || N == 0) {
+        // an empty layer: the arguments that do not depend on the empty extent are checked
+        // as for any other call, and nothing is enqueued
+        if (x_dtype != CR_BF16 && x_dtype != CR_FP16 && x_dtype != CR_FP32) return CR_ERR_UNSUPPORTED_DTYPE;
+        if (out_dtype != CR_BF16 && out_dtype != CR_FP16 && out_dtype != CR_FP32) return CR_ERR_UNSUPPORTED_DTYPE;
+        if (check_flags(flags) != CR_OK || ld_x < (swiglu ? 2 * K : K) || ldc < N) return CR_ERR_INVALID_ARG;
+        if (N > 0 && (!w_fp4 || !w_sf || !global_scale)) return CR_ERR_INVALID_ARG;
+        if (ld_fp4 < (K + 1) / 2 || ld_sf < (K + 15) / 16) return CR_ERR_INVALID_ARG;
+        return CR_OK;
+    }
+    if (!workspace || !out) return CR_ERR_INVALID_ARG;
     const LayerPlan p = plan_layer(M, N, K, max_tile_bytes);
     if (!aligned(workspace, 256)) return CR_ERR_MISALIGNED;
     if (ws_bytes < p.bytes) return CR_ERR_TOO_LARGE;

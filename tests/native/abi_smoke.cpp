@@ -101,9 +101,12 @@ int run_case(int64_t M, int64_t N, int64_t K, hipStream_t s_main, hipStream_t s_
     std::printf("M=%lld N=%lld K=%lld: components == layer (%s path), ok\n", (long long)M, (long long)N,
                 (long long)K, chunks == 0 ? "decode-inside-GEMM" : "staged");
 
-    // argument errors are statuses, nothing launched
+    // argument errors are statuses, nothing launched; empty extents are valid no-ops
     if (cr_gemm_s8_rowscale(qx, kp, sx, qw, kp, sw, M, N, kp + 1, out_a, CR_BF16, N, s_main) != CR_ERR_INVALID_ARG ||
-        cr_quant_act(x, CR_BF16, kp, 0, K, qx, kp, sx, CR_FLAG_NONE, s_main) != CR_ERR_INVALID_ARG ||
+        cr_quant_act(x, CR_BF16, kp, -1, K, qx, kp, sx, CR_FLAG_NONE, s_main) != CR_ERR_INVALID_ARG ||
+        cr_quant_act(nullptr, CR_BF16, kp, 0, K, nullptr, kp, nullptr, CR_FLAG_NONE, s_main) != CR_OK ||
+        cr_linear_nvfp4(nullptr, CR_BF16, kp, 0, 0, K, codes, ld_fp4, sf, ld_sf, gd, N, nullptr, CR_BF16, N,
+                        nullptr, 0, 0, CR_FLAG_NONE, s_main, nullptr) != CR_OK ||
         cr_linear_nvfp4(x, CR_BF16, kp, 0, M, K, codes, ld_fp4, sf, ld_sf, gd, N, out_b, CR_BF16, N, ws, wsb - 1, 0,
                         CR_FLAG_NONE, s_main, nullptr) != CR_ERR_TOO_LARGE) {
         std::fprintf(stderr, "argument checks did not return the documented statuses\n");

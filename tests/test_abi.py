@@ -47,7 +47,7 @@ def qa(x=A16, dt=0, ld_x=512, M=4, K=512, q=A16, ld_q=512, s=A16, flags=0):
 
 def test_quant_act_validation():
     assert qa(x=None) == INV
-    assert qa(M=0) == INV
+    assert qa(M=-1) == INV
     assert qa(K=0) == INV
     assert qa(dt=3) == DT
     assert qa(ld_x=500) == INV            # ld_x < K
@@ -87,7 +87,7 @@ def pw(codes=A16, ld=256, sf=A16, ld_sf=32, g=A16, n=8, K=512, q=A16, ld_q=512, 
 
 def test_prep_weight_validation():
     assert pw(g=None) == INV
-    assert pw(n=0) == INV
+    assert pw(n=-1) == INV
     assert pw(ld=200) == INV               # < ceil(K/2)
     assert pw(ld_sf=31) == INV             # < ceil(K/16)
     assert pw(ld=264) == MIS               # not a multiple of 16
@@ -180,8 +180,15 @@ def test_layer_chunk_plan():
     assert rbl.cr_linear_nvfp4_plan(19989, 21504, 5376, 16 << 20) == (3072, 7)
     # a bound below one tile height still gives one 256-row chunk
     assert rbl.cr_linear_nvfp4_plan(300, 1000, 5376, 1) == (256, 4)
+    # an empty layer: no chunks, no workspace
+    assert rbl.cr_linear_nvfp4_plan(0, 256, 256) == (0, 0)
+    assert rbl.cr_linear_nvfp4_plan(19989, 0, 5376) == (0, 0)
+    assert rbl.cr_linear_nvfp4_workspace_bytes(0, 256, 256) == 0
+    assert rbl.cr_linear_nvfp4_workspace_bytes(300, 0, 256) == 0
     with pytest.raises(rbl.CrError):
-        rbl.cr_linear_nvfp4_plan(0, 256, 256)
+        rbl.cr_linear_nvfp4_plan(-1, 256, 256)
+    with pytest.raises(rbl.CrError):
+        rbl.cr_linear_nvfp4_plan(1, 256, 0)
     with pytest.raises(rbl.CrError):
         rbl.cr_linear_nvfp4_plan(1, 256, rbl.CR_MAX_K_PAD + 1)
 
@@ -193,7 +200,7 @@ def wa(codes=A16, ld=256, sf=A16, ld_sf=32, g=A16, n=8, K=512, a=A16, flags=0):
 def test_weight_amax_validation():
     assert wa(a=None) == INV
     assert wa(g=None) == INV
-    assert wa(n=0) == INV
+    assert wa(n=-1) == INV
     assert wa(ld=200) == INV               # < ceil(K/2)
     assert wa(ld_sf=31) == INV             # < ceil(K/16)
     assert wa(ld=264) == MIS
@@ -215,7 +222,8 @@ def test_gemm_fused_validation():
     assert fz(sa=None) == INV              # scales needed unless int32 out
     assert fz(dt=3, bias=A16) == INV       # no bias on the raw accumulator
     assert fz(dt=7) == DT
-    assert fz(M=0) == INV
+    assert fz(M=-1) == INV
+    assert fz(N=-1) == INV
     assert fz(lda=256) == INV              # < K_pad
     assert fz(ld=200) == INV
     assert fz(ldc=39) == INV
@@ -253,3 +261,44 @@ def test_valid_arguments_report_no_device_without_gpu():
     assert L.cr_linear_nvfp4(A16, 0, 512, 0, 64, 512, A16, 256, A16, 32, A16, 256, A16, 0, 256, 0x100000, ws, 0, 0,
                              ST, None) == NODEV
     assert fz(dt=3, sa=None) == NODEV
+
+
+def test_empty_extents_are_no_ops():
+    """M (or n_rows) = 0 or N = 0: CR_OK with nothing enqueued, buffers of zero size may be
+    NULL; the arguments that do not depend on the empty extent are still checked, and K = 0
+    or a negative size is still an error.  (Returns before any HIP call: safe without a GPU.)"""
+    L = rbl.lib()
+    N0 = None
+    # activation preparation (plain, SwiGLU, pre-scaled) and the unfused SwiGLU
+    assert qa(x=N0, M=0, q=N0, s=N0) == OK
+    assert qa(x=N0, M=0, q=N0, s=N0, K=0) == INV
+    assert qa(x=N0, M=0, q=N0, s=N0, dt=3) == DT
+    assert qa(x=N0, M=0, q=N0, s=N0, flags=4) == INV
+    assert qa(x=N0, M=0, q=N0, s=N0, ld_q=256) == INV
+    assert L.cr_quant_act_swiglu(N0, 0, 1024, 0, 512, N0, 512, N0, 0, ST) == OK
+    assert qx(x=N0, M=0, q=N0, s=N0, pre=N0) == OK
+    assert L.cr_swiglu(N0, 0, 1024, 0, 512, N0, 512, ST) == OK
+    # weight preparation and row maxima
+    assert pw(codes=N0, sf=N0, g=N0, n=0, q=N0, s=N0) == OK
+    assert pw(codes=N0, sf=N0, g=N0, n=0, q=N0, s=N0, ld=200) == INV
+    assert wa(codes=N0, sf=N0, g=N0, n=0, a=N0) == OK
+    # GEMMs: no rows, or no columns
+    assert gm(a=N0, sa=N0, M=0, c=N0) == OK
+    assert gm(b=N0, sb=N0, N=0, c=N0, ldc=0) == OK
+    assert gm(a=N0, sa=N0, M=0, c=N0, dt=7) == DT
+    assert gm(a=N0, sa=N0, M=0, c=N0, K=500, lda=512, ldb=512) == INV
+    assert gm(M=-1) == INV
+    assert fz(a=N0, sa=N0, M=0, c=N0) == OK
+    assert fz(codes=N0, sf=N0, g=N0, am=N0, N=0, c=N0, ldc=0) == OK
+    # the layer: empty batch or empty output, no workspace
+    def layer(x=N0, M=0, N=256, out=N0, ws=N0, wsb=0, odt=0, dt=0, K=512, w=A16, sf=A16, g=A16):
+        return L.cr_linear_nvfp4(x, dt, 512, 0, M, K, w, 256, sf, 32, g, N, out, odt, 256, ws, wsb, 0, 0, ST, None)
+    assert layer() == OK
+    assert layer(M=300, x=A16, N=0, w=N0, sf=N0, g=N0) == OK
+    assert layer(odt=3) == DT
+    assert layer(dt=5) == DT
+    assert layer(K=0) == INV
+    assert layer(M=-1) == INV
+    assert layer(g=N0) == INV                       # N > 0: the weight is still required
+    assert L.cr_linear_nvfp4_ex(N0, 0, 512, 0, 0, 512, N0, A16, 256, A16, 32, A16, 256, N0, N0, 0, 256,
+                                N0, 0, 0, 0, ST, None) == OK

@@ -523,3 +523,38 @@ def test_every_short_row_shape_bit_exact(nb):
     assert_bits_equal(sw.cpu().numpy().view(np.uint32), rsw.view(np.uint32), "w_scale")
     ra = oracle.weight_amax_nvfp4(p.codes.numpy(), p.sf.numpy(), p.g, K)
     assert_bits_equal(am.cpu().numpy().view(np.uint32), ra.view(np.uint32), "w_amax")
+
+
+# ---------------------------------------------------------------- empty extents ----
+
+def test_empty_batches_and_empty_outputs():
+    """M = 0 (an empty batch) and N = 0 (no output columns) through the binding: empty
+    results, nothing launched, and the next ordinary call on the stream is unaffected."""
+    K, N, M = 700, 300, 40
+    g = torch.Generator().manual_seed(9)
+    p = synth.nvfp4_encode(0.02 * torch.randn(N, K, generator=g), garbage_seed=9)
+    gs = torch.tensor([p.g], dtype=torch.float32, device=dev())
+    cd, sfd = p.codes.to(dev()), p.sf.to(dev())
+    x = make_x(M, K, synth.DT_BF16, seed=10, ld=704).to(dev())
+    say("empty extents: quant_act / prep_weight / gemm / fused / linear with M = 0 or N = 0")
+    q0, s0 = rbl.quant_act(x[:0], K)
+    h0, hs0 = rbl.quant_act(torch.empty(0, 2 * K, dtype=torch.bfloat16, device=dev()), K, swiglu=True)
+    qw0, sw0 = rbl.prep_weight_nvfp4(cd[:0], sfd[:0], gs, K)
+    am0 = rbl.weight_amax_nvfp4(cd[:0], sfd[:0], gs, K)
+    assert q0.shape == (0, 768) and s0.shape == (0,) and h0.shape == (0, 768) and hs0.shape == (0,)
+    assert qw0.shape == (0, 768) and sw0.shape == (0,) and am0.shape == (0,)
+    qx, sx = rbl.quant_act(x, K)
+    qw, sw = rbl.prep_weight_nvfp4(cd, sfd, gs, K)
+    assert rbl.gemm_s8_rowscale(qx[:0], sx[:0], qw, sw).shape == (0, N)
+    assert rbl.gemm_s8_rowscale(qx, sx, qw[:0], sw[:0]).shape == (M, 0)
+    assert rbl.gemm_nvfp4_fused(qx[:0], sx[:0], cd, sfd, gs, None, K).shape == (0, N)
+    assert rbl.gemm_nvfp4_fused(qx, sx, cd[:0], sfd[:0], gs, None, K).shape == (M, 0)
+    for rows in (0, 100):                            # empty batch on both paths' sides of 64
+        xe = torch.empty(0, 704, dtype=torch.bfloat16, device=dev())[:, :K] if rows == 0 else x
+        y = rbl.linear_nvfp4(xe, cd if rows == 0 else cd[:0], sfd if rows == 0 else sfd[:0], gs, K)
+        assert y.shape == ((0, N) if rows == 0 else (M, 0))
+    y = rbl.linear_nvfp4(x, cd, sfd, gs, K, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.linear_nvfp4(synth.bits_u16(x.cpu()), synth.DT_BF16, K, False, p.codes.numpy(), p.sf.numpy(),
+                              p.g, synth.DT_FP32)
+    assert rel_l2(out_f64(y, synth.DT_FP32), out_f64(ref, synth.DT_FP32)) <= TOL[synth.DT_FP32]
