@@ -155,6 +155,54 @@ __device__ __forceinline__ float swiglu_elem(float a, float b)
     return o;
 }
 
+// ------------------------------------------------------------- bf16 sigma table ----
+
+// A bf16 gate has 65536 possible values, so sigma(a) = 1 / (1 + E(-a)) can be tabulated
+// once per workgroup in LDS by the definition itself (E and an IEEE division) and looked up
+// per element: the product (a * sigma) * b is then evaluated exactly as defined, with the
+// same sigma bits.  Outside magnitudes [2^-25, 2^7] sigma does not depend on |a|:
+//   |a| <= 2^-25: E(-a) is exactly 1 (k = 0, and every Horner step rounds 1 + r back to 1
+//                 for |r| <= 2^-25, ties to even at 2^-25), so sigma = 1/2;
+//   a >= 128:     E(-a) = 0 (the steps underflow below -104), so sigma = 1;
+//   a <= -128:    E(-a) = +inf (the steps overflow above 89), so sigma = 0;
+// so the magnitude is clamped to that range, whose two ends already hold those values.
+// Entry 2 (m - kSigLo) + s holds sigma of the bf16 pattern with magnitude bits m and sign s.
+constexpr uint32_t kSigLo = 0x3300;      // bf16 magnitude bits of 2^-25
+constexpr uint32_t kSigHi = 0x4300;      // bf16 magnitude bits of 2^7
+constexpr int kSigEntries = 2 * (int)(kSigHi - kSigLo + 1);
+constexpr size_t kSigTableBytes = (size_t)kSigEntries * sizeof(float);
+
+__device__ __forceinline__ void build_sigma_table(float *tab)
+{
+    for (int e = threadIdx.x; e < kSigEntries; e += blockDim.x) {
+        const uint32_t pattern = (kSigLo + (uint32_t)(e >> 1)) | ((uint32_t)(e & 1) << 15);
+        const float a = __uint_as_float(pattern << 16);
+        tab[e] = 1.0f / (1.0f + repro_exp_nan_free(-a));
+    }
+    __syncthreads();
+}
+
+// Table position inside the dynamic LDS (in floats), past `engine_bytes` used by the row
+// engine, at a 16-byte boundary.
+__device__ __forceinline__ uint32_t sigma_table_offset(size_t engine_bytes)
+{
+    return (uint32_t)((engine_bytes + 15) / 16 * 4);
+}
+
+__device__ __forceinline__ float *sigma_table_at(uint32_t off)
+{
+    extern __shared__ float lds_base[];
+    return lds_base + off;
+}
+
+// sigma of the bf16 gate with 16-bit pattern p, from the table at `off`
+__device__ __forceinline__ float sigma_lookup(uint32_t off, uint32_t p)
+{
+    extern __shared__ float lds_base[];
+    const uint32_t m = min(max(p & 0x7fffu, kSigLo), kSigHi);
+    return lds_base[off + (((m - kSigLo) << 1) | (p >> 15))];
+}
+
 // --------------------------------------------------------------------- loaders ----
 
 // Activation loaders.  With kPre, the loaded (or SwiGLU) value of channel k is multiplied
@@ -163,6 +211,7 @@ __device__ __forceinline__ float swiglu_elem(float a, float b)
 template <int DT, bool kPre>
 struct ActLoader {
     static constexpr bool kFetchAfterDecode = true;
+    static constexpr bool kSigTable = false;
     const typename Elem<DT>::T *x;
     int64_t ld;
     int64_t K;
@@ -188,12 +237,14 @@ struct ActLoader {
 template <int DT, bool kPre>
 struct SwigluLoader {
     static constexpr bool kFetchAfterDecode = true;
+    static constexpr bool kSigTable = DT == 0;     // bf16 gates: sigma from the LDS table
     const typename Elem<DT>::T *h;
     int64_t ld;
     int64_t F;
     bool aligned_gate;
     bool aligned_value;
     const float *pre;
+    uint32_t sig_off = 0;                          // the table's LDS position (set inside the kernel)
     struct Raw {
         RawSeg<DT> gate, value;
     };
@@ -208,8 +259,21 @@ struct SwigluLoader {
     __device__ __forceinline__ void decode(const Raw &r, int64_t, const Lane &ln, float (&v)[16]) const
     {
         float b[16];
-        decode_seg<DT>(r.gate, v);
         decode_seg<DT>(r.value, b);
+        if constexpr (kSigTable) {                      // zero past F: (0 * 1/2) * 0
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const uint32_t w = r.gate.w[i >> 3][(i >> 1) & 3];
+                const uint32_t p = (i & 1) ? (w >> 16) : (w & 0xffffu);
+                v[i] = (__uint_as_float(p << 16) * sigma_lookup(sig_off, p)) * b[i];
+            }
+            if constexpr (kPre) {
+#pragma unroll
+                for (int i = 0; i < 16; i++) v[i] = v[i] * ln.c[i];
+            }
+            return;
+        }
+        decode_seg<DT>(r.gate, v);
         bool far = false;
 #pragma unroll
         for (int i = 0; i < 16; i++) {                  // zero past F: 0 * sigma * 0
@@ -233,18 +297,25 @@ struct SwigluLoader {
 };
 
 // Unfused SwiGLU: out[m, k] = swish(h[m, k]) * h[m, F + k] in FP32 (same element function
-// as the fused path).  One thread per element, grid-stride over rows.
+// as the fused path: the sigma table for bf16).  One thread per element, grid-stride.
 template <int DT>
 __global__ void swiglu_kernel(const typename Elem<DT>::T *__restrict__ h, int64_t ld_h, int64_t M, int64_t F,
                               float *__restrict__ out, int64_t ld_out)
 {
+    if constexpr (DT == 0) build_sigma_table(sigma_table_at(0));
     const int64_t total = M * F;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t m = i / F, k = i - m * F;
-        const float a = Elem<DT>::cvt(h[m * ld_h + k]);
-        const float b = Elem<DT>::cvt(h[m * ld_h + F + k]);
-        out[m * ld_out + k] = swiglu_elem(a, b);
+        if constexpr (DT == 0) {
+            const uint32_t p = h[m * ld_h + k];
+            const float b = Elem<DT>::cvt(h[m * ld_h + F + k]);
+            out[m * ld_out + k] = (__uint_as_float(p << 16) * sigma_lookup(0, p)) * b;
+        } else {
+            const float a = Elem<DT>::cvt(h[m * ld_h + k]);
+            const float b = Elem<DT>::cvt(h[m * ld_h + F + k]);
+            out[m * ld_out + k] = swiglu_elem(a, b);
+        }
     }
 }
 
@@ -252,6 +323,10 @@ template <class Loader, int RB>
 __global__ __launch_bounds__(row_prep_max_threads<RB>()) void quant_act_kernel(Loader ld, int64_t n_rows, int nb, int8_t *__restrict__ out, int64_t ld_out,
                                  float *__restrict__ scale, int mode)
 {
+    if constexpr (Loader::kSigTable) {
+        ld.sig_off = sigma_table_offset(row_prep_lds_bytes(blockDim.x));
+        build_sigma_table(sigma_table_at(ld.sig_off));
+    }
     row_prep_kernel_body<Loader, RB>(ld, n_rows, nb, out, ld_out, scale, mode);
 }
 
@@ -261,6 +336,10 @@ __global__ __launch_bounds__(1024) void quant_act_multi_kernel(Loader ld, int64_
                                                              int8_t *__restrict__ out, int64_t ld_out,
                                                              float *__restrict__ scale, int mode)
 {
+    if constexpr (Loader::kSigTable) {
+        ld.sig_off = sigma_table_offset(row_prep_multi_lds_bytes(blockDim.x));
+        build_sigma_table(sigma_table_at(ld.sig_off));
+    }
     row_prep_multi(ld, n_rows, nb, rpw, out, ld_out, scale, (mode & 2) == 0, false);
 }
 
@@ -272,13 +351,19 @@ static hipError_t launch_rows(const Loader &L, int64_t rows, int64_t nb, int8_t 
                               int one_pass_groups = kMaxGroups2)
 {
     const RowPrepShape s = row_prep_shape(nb, force_two_pass, one_pass_groups);
-    const size_t lds = row_prep_lds_bytes(s.threads);
+    // the sigma table sits past the engine's LDS, at a 16-byte boundary
+    constexpr size_t extra = Loader::kSigTable ? kSigTableBytes + 16 : 0;
+    const size_t lds = row_prep_lds_bytes(s.threads) + extra;
     const int mode = (s.two_pass ? 1 : 0) | (transposed ? 2 : 0);
+    // a workgroup that builds the table works through many rows: two-pass rows then loop
+    // over the resident workgroups instead of one workgroup per row
+    RowPrepShape gs = s;
+    if (Loader::kSigTable) gs.two_pass = false;
     const int rpw = (!s.two_pass && nb <= 32) ? row_prep_multi_rows(nb) : 1;
     if (rpw >= 2) {
         // rows whose lane groups would leave the last wave partly idle: several per workgroup
         const int threads = (int)((rpw * nb + 3) / 4 * 64);
-        const size_t mlds = row_prep_multi_lds_bytes(threads);
+        const size_t mlds = row_prep_multi_lds_bytes(threads) + extra;
         const RowPrepShape ms{threads, 1, false};
         const void *k = reinterpret_cast<const void *>(&quant_act_multi_kernel<Loader>);
         const dim3 grid((unsigned)row_prep_grid((rows + rpw - 1) / rpw, ms, k, mlds));
@@ -293,7 +378,7 @@ static hipError_t launch_rows(const Loader &L, int64_t rows, int64_t nb, int8_t 
                            L, rows, (int)nb, out, ld_out, scale, mode);
     } else {
         const void *k = reinterpret_cast<const void *>(&quant_act_kernel<Loader, 1>);
-        const dim3 grid((unsigned)row_prep_grid(rows, s, k, lds));
+        const dim3 grid((unsigned)row_prep_grid(rows, gs, k, lds));
         hipLaunchKernelGGL((quant_act_kernel<Loader, 1>), grid, dim3(s.threads), lds, st,
                            L, rows, (int)nb, out, ld_out, scale, mode);
     }
@@ -349,8 +434,13 @@ hipError_t launch_swiglu(const void *h, int dtype, int64_t ld_h, int64_t M, int6
     const int64_t want = (total + threads - 1) / threads;
     const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
     switch (dtype) {
-    case 0: hipLaunchKernelGGL(swiglu_kernel<0>, dim3(blocks), dim3(threads), 0, st,
-                               static_cast<const uint16_t *>(h), ld_h, M, F, out, ld_out); break;
+    case 0: {
+        // every workgroup tabulates sigma first: larger workgroups, fewer of them
+        const int64_t want16 = (total + 1023) / 1024;
+        hipLaunchKernelGGL(swiglu_kernel<0>, dim3((unsigned)(want16 < 2048 ? want16 : 2048)), dim3(1024),
+                           kSigTableBytes, st, static_cast<const uint16_t *>(h), ld_h, M, F, out, ld_out);
+        break;
+    }
     case 1: hipLaunchKernelGGL(swiglu_kernel<1>, dim3(blocks), dim3(threads), 0, st,
                                static_cast<const uint16_t *>(h), ld_h, M, F, out, ld_out); break;
     case 2: hipLaunchKernelGGL(swiglu_kernel<2>, dim3(blocks), dim3(threads), 0, st,

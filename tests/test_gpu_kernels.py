@@ -558,3 +558,31 @@ def test_empty_batches_and_empty_outputs():
     ref = oracle.linear_nvfp4(synth.bits_u16(x.cpu()), synth.DT_BF16, K, False, p.codes.numpy(), p.sf.numpy(),
                               p.g, synth.DT_FP32)
     assert rel_l2(out_f64(y, synth.DT_FP32), out_f64(ref, synth.DT_FP32)) <= TOL[synth.DT_FP32]
+
+
+@pytest.mark.parametrize("F,flags", [(256, 0), (16384, 0), (16384, rbl.CR_FLAG_BLOCK_TRANSPOSED),
+                                     (512, rbl.CR_FLAG_FORCE_TWO_PASS)])
+def test_quant_act_swiglu_every_bf16_gate(F, flags):
+    """Every finite bf16 gate pattern through the fused SwiGLU preparation (whose bf16 sigma
+    comes from a table built in LDS): S8 codes and scales bit-exact against the oracle.  The
+    value of each element is 2^-e for the gate's exponent e (clamped to +-100), so every
+    product stays near 1 and no row overflows in the rotation; inf/NaN patterns are 0."""
+    pat = np.arange(65536, dtype=np.uint32)
+    gate = (pat << 16).view(np.float32).copy()
+    gate[~np.isfinite(gate)] = 0.0
+    e = np.clip(((pat >> 7) & 0xFF).astype(np.int64) - 127, -100, 100)
+    value = np.ldexp(np.ones(65536), -e).astype(np.float32)
+    M = 65536 // F
+    h = torch.cat([torch.from_numpy(gate.reshape(M, F)), torch.from_numpy(value.reshape(M, F))], dim=1)
+    h = h.to(torch.bfloat16)                        # both exact in bf16
+    assert np.array_equal((synth.bits_u16(h)[:, :F].astype(np.uint32) << 16).view(np.float32), gate.reshape(M, F))
+    say(f"cr_quant_act_swiglu all bf16 gate patterns F={F} flags={flags}")
+    q, s = rbl.quant_act(h.to(dev()), F, swiglu=True, flags=flags)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant_act(synth.bits_u16(h), synth.DT_BF16, F, swiglu=True)
+    if flags & rbl.CR_FLAG_BLOCK_TRANSPOSED:
+        perm = np.arange(rq.shape[1]).reshape(-1, 16, 16).transpose(0, 2, 1).reshape(-1)
+        rq = rq[:, perm]
+    assert np.isfinite(rs).all()
+    assert_bits_equal(q.cpu().numpy(), rq, "x_s8 (all bf16 gates)")
+    assert_bits_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32), "x_scale (all bf16 gates)")
