@@ -126,9 +126,7 @@ void gemm_nvfp4_fused_kernel(const int8_t *__restrict__ A, int64_t lda, const fl
         }
 #pragma unroll
         for (int q = 0; q < FZ_RPG; q++) {
-#pragma unroll
-            for (int off = 8; off >= 1; off >>= 1) zm[q] = fmaxf(zm[q], __shfl_xor(zm[q], off, 64));
-            rq[q] = row_quant(zm[q]);
+            rq[q] = row_quant(group16_max(zm[q]));
         }
     }
 #pragma unroll

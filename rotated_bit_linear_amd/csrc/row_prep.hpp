@@ -144,24 +144,48 @@ __device__ __forceinline__ int opaque(int v)
     return v;
 }
 
-__device__ __forceinline__ float wave_max(float a)
+// Maxima of non-negative floats (|z| values) taken on their bit patterns: for x, y >= 0 the
+// unsigned order of the patterns is the order of the values (+inf included), so an integer
+// maximum gives the float maximum exactly, with no NaN canonicalisation.
+// Maximum over each row of 16 lanes, in every lane of the row: DPP exchanges within quads
+// (lane ^ 1, lane ^ 2), then the half-row mirror (lane i <-> 7 - i) and the row mirror
+// (lane i <-> 15 - i), each folded in by v_max_u32.
+__device__ __forceinline__ uint32_t group16_umax(uint32_t x)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
-    return a;
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, true));  // row_half_mirror
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, true));  // row_mirror
+    return x;
 }
 
-// Workgroup maximum; every thread gets the result.  `red` holds one float per wave.
+__device__ __forceinline__ float group16_max(float a)
+{
+    return __uint_as_float(group16_umax(__float_as_uint(a)));
+}
+
+// Maximum over the wave (every lane active), as a wave-uniform value.
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x)
+{
+    x = group16_umax(x);
+    const uint32_t r0 = __builtin_amdgcn_readlane(x, 0), r1 = __builtin_amdgcn_readlane(x, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(x, 32), r3 = __builtin_amdgcn_readlane(x, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
+// Workgroup maximum of non-negative values; every thread gets the result.  `red` holds one
+// slot per wave.
 __device__ __forceinline__ float block_max(float a, float *red)
 {
-    a = wave_max(a);
+    const uint32_t m = wave_umax(__float_as_uint(a));
     const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[w] = a;
+    uint32_t *slots = reinterpret_cast<uint32_t *>(red);
+    if ((threadIdx.x & 63) == 0) slots[w] = m;
     __syncthreads();
     const int nw = blockDim.x >> 6;
-    float m = 0.0f;
-    for (int i = 0; i < nw; i++) m = fmaxf(m, red[i]);
-    return m;
+    uint32_t r = 0;
+    for (int i = 0; i < nw; i++) r = max(r, slots[i]);
+    return __uint_as_float(r);
 }
 
 // rint(t) in two's complement in the low byte of the result, for |t| < 128 (the
@@ -462,14 +486,14 @@ __device__ __forceinline__ void row_prep_multi(const Loader &ld, int64_t n_rows,
         float zm = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; i++) zm = fmaxf(zm, fabsf(v[i]));
-#pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) zm = fmaxf(zm, __shfl_xor(zm, off, 64));
-        float *set = red + parity * G;
-        if (t == 0) set[grp] = zm;
+        zm = group16_max(zm);
+        uint32_t *set = reinterpret_cast<uint32_t *>(red + parity * G);
+        if (t == 0) set[grp] = __float_as_uint(zm);
         __syncthreads();
-        float zrow = 0.0f;
+        uint32_t zbits = 0;
         if (active)
-            for (int i = 0; i < nb; i++) zrow = fmaxf(zrow, set[slot * nb + i]);
+            for (int i = 0; i < nb; i++) zbits = max(zbits, set[slot * nb + i]);
+        const float zrow = __uint_as_float(zbits);
         if (amax_only) {                               // a = max |z * 0.0625|, no codes
             if (live && b == 0 && t == 0) scale_out[row] = zrow * 0.0625f;
             return;
