@@ -174,7 +174,8 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t x)
 }
 
 // Workgroup maximum of non-negative values; every thread gets the result.  `red` holds one
-// slot per wave.
+// slot per wave (at most 16 waves): lane i of each 16-lane row reads slot i, and the row
+// reduces them.
 __device__ __forceinline__ float block_max(float a, float *red)
 {
     const uint32_t m = wave_umax(__float_as_uint(a));
@@ -182,10 +183,8 @@ __device__ __forceinline__ float block_max(float a, float *red)
     uint32_t *slots = reinterpret_cast<uint32_t *>(red);
     if ((threadIdx.x & 63) == 0) slots[w] = m;
     __syncthreads();
-    const int nw = blockDim.x >> 6;
-    uint32_t r = 0;
-    for (int i = 0; i < nw; i++) r = max(r, slots[i]);
-    return __uint_as_float(r);
+    const int i = threadIdx.x & 15;
+    return __uint_as_float(group16_umax(i < (int)(blockDim.x >> 6) ? slots[i] : 0u));
 }
 
 // rint(t) in two's complement in the low byte of the result, for |t| < 128 (the
@@ -471,14 +470,10 @@ __device__ __forceinline__ void row_prep_multi(const Loader &ld, int64_t n_rows,
         const int64_t row = base + slot;
         if (active && row < n_rows) ld.fetch(row, seg, r);
     };
-    auto decode = [&](const Raw &r, int64_t base, float (&v)[16]) {
-        if (active && base + slot < n_rows) {
-            ld.decode(r, seg, lane_c, v);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; i++) v[i] = 0.0f;
-        }
-    };
+    // every lane decodes: the raw bytes of a lane outside the workgroup's rows were never
+    // fetched (zero, so the values are 0), and those of a lane past the last row are the
+    // previous row's; neither lane stores anything
+    auto decode = [&](const Raw &r, int64_t, float (&v)[16]) { ld.decode(r, seg, lane_c, v); };
     auto finish = [&](float (&v)[16], int64_t base, int parity) {
         const int64_t row = base + slot;
         const bool live = active && row < n_rows;
@@ -490,10 +485,16 @@ __device__ __forceinline__ void row_prep_multi(const Loader &ld, int64_t n_rows,
         uint32_t *set = reinterpret_cast<uint32_t *>(red + parity * G);
         if (t == 0) set[grp] = __float_as_uint(zm);
         __syncthreads();
+        // lane t of a group reads slots t and t + 16 of its row (nb <= 32), and the group
+        // reduces them (every lane of a group shares its activity, so the DPP steps stay
+        // inside active rows)
         uint32_t zbits = 0;
-        if (active)
-            for (int i = 0; i < nb; i++) zbits = max(zbits, set[slot * nb + i]);
-        const float zrow = __uint_as_float(zbits);
+        if (active) {
+            const uint32_t *rs = set + slot * nb;
+            if (t < nb) zbits = rs[t];
+            if (t + 16 < nb) zbits = max(zbits, rs[t + 16]);
+        }
+        const float zrow = __uint_as_float(group16_umax(zbits));
         if (amax_only) {                               // a = max |z * 0.0625|, no codes
             if (live && b == 0 && t == 0) scale_out[row] = zrow * 0.0625f;
             return;
