@@ -38,6 +38,10 @@ BT = 2                       # CR_FLAG_BLOCK_TRANSPOSED: the order cr_linear_nvf
 # fp32 operation per lane per clock (256 CUs x 64 lanes x 2.4 GHz; no packed math).
 FUSED_VALU_PER_ELEM = 13.25
 PEAK_VALU_TOPS = 39.3
+# NVFP4 weight preparation, vector instructions per weight element at the minimum: decode 2.5,
+# rotation 8, row maximum 0.5 (v_max3), quantization 2.75; rows streamed twice (K_pad > 16384)
+# decode and rotate again (11 + 13.25).
+WEIGHT_VALU_PER_ELEM = {False: 13.75, True: 24.25}
 GEMM_SOURCES = ["rotated_bit_linear_amd/csrc/gemm_s8.hip"]
 PMC_PROFILE = os.path.join(ROOT, "profiles", "gemm_s8_qkv_m19989_hbm_counters.md")
 
@@ -479,6 +483,11 @@ def main():
             "weight_prep_gbs": round(L.w_bytes / (t_w * 1e-3) / 1e9, 1),
             "weight_prep_frac_hbm_peak": round(L.w_bytes / (t_w * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "weight_prep_frac_copy": round(L.w_bytes / (t_w * 1e-3) / 1e9 / copy_gbs, 4),
+            # the weight preparation is bound by vector issue, not bytes: its own roofline
+            "weight_prep_valu_tops": round(w.N * w.K_pad * WEIGHT_VALU_PER_ELEM[w.K_pad > 16384]
+                                           / (t_w * 1e-3) / 1e12, 2),
+            "weight_prep_frac_valu_peak": round(w.N * w.K_pad * WEIGHT_VALU_PER_ELEM[w.K_pad > 16384]
+                                                / (t_w * 1e-3) / 1e12 / PEAK_VALU_TOPS, 4),
             "gemm_full_n_ms": round(t_g, 4),
             "gemm_full_n_frac_peak": round(L.gemm_ops / (t_g * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
             "expanded_s8_control_ms": round(t_x, 4),
