@@ -40,6 +40,9 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b)
 
 struct NVFP4Loader {
     static constexpr bool kFetchAfterDecode = false;   // little raw data, cheap decode
+    // two-pass rows: loads then decode in place (prefetching the next slice measured 6 %
+    // slower on long-K weights: 12 bytes a lane are little to hide)
+    static constexpr bool kTwoPassPrefetch = false;
     const uint8_t *codes;
     int64_t ld_codes;
     const uint8_t *sf;
@@ -53,6 +56,7 @@ struct NVFP4Loader {
     };
     using Lane = PreScaleLane<false>;   // no per-segment constants
     __device__ __forceinline__ Lane lane(int64_t) const { return Lane{}; }
+    template <bool kKeep = false>                      // ordinary loads either way
     __device__ __forceinline__ void fetch(int64_t row, int64_t seg, Raw &r) const
     {
         const int64_t k0 = seg * 16;

@@ -41,15 +41,20 @@ template <int DT> struct RawSeg {
 
 // Fetch elements [k0, k0+16) of a row with logical length K: vector loads when the whole
 // segment lies below K and the row permits 16-byte loads (non-temporal: the activation is
-// read once), element loads for a segment straddling K, nothing at all past K.
-template <int DT>
+// read once; ordinary with kKeep, for the first pass over a row that is read twice),
+// element loads for a segment straddling K, nothing at all past K.
+template <int DT, bool kKeep = false>
 __device__ __forceinline__ void fetch_seg(const typename Elem<DT>::T *row, int64_t k0, int64_t K, bool aligned,
                                           RawSeg<DT> &r)
 {
     constexpr int NW = DT == 2 ? 4 : 2;
     if (aligned && k0 + 16 <= K) {
 #pragma unroll
-        for (int c = 0; c < NW; c++) r.w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row + k0) + c);
+        for (int c = 0; c < NW; c++) {
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(row + k0) + c;
+            if constexpr (kKeep) r.w[c] = *src;
+            else r.w[c] = __builtin_nontemporal_load(src);
+        }
         return;
     }
 #pragma unroll
@@ -211,6 +216,7 @@ __device__ __forceinline__ float sigma_lookup(uint32_t off, uint32_t p)
 template <int DT, bool kPre>
 struct ActLoader {
     static constexpr bool kFetchAfterDecode = true;
+    static constexpr bool kTwoPassPrefetch = true;
     static constexpr bool kSigTable = false;
     const typename Elem<DT>::T *x;
     int64_t ld;
@@ -220,9 +226,10 @@ struct ActLoader {
     using Raw = RawSeg<DT>;
     using Lane = PreScaleLane<kPre>;
     __device__ __forceinline__ Lane lane(int64_t seg) const { return load_prescale<kPre>(pre, seg, K); }
+    template <bool kKeep = false>
     __device__ __forceinline__ void fetch(int64_t row, int64_t seg, Raw &r) const
     {
-        fetch_seg<DT>(x + row * ld, seg * 16, K, aligned, r);
+        fetch_seg<DT, kKeep>(x + row * ld, seg * 16, K, aligned, r);
     }
     __device__ __forceinline__ void decode(const Raw &r, int64_t, const Lane &ln, float (&v)[16]) const
     {
@@ -237,6 +244,8 @@ struct ActLoader {
 template <int DT, bool kPre>
 struct SwigluLoader {
     static constexpr bool kFetchAfterDecode = true;
+    // fp32 segments (128 bytes a lane) leave no registers for a second buffer
+    static constexpr bool kTwoPassPrefetch = DT != 2;
     static constexpr bool kSigTable = DT == 0;     // bf16 gates: sigma from the LDS table
     const typename Elem<DT>::T *h;
     int64_t ld;
@@ -250,11 +259,12 @@ struct SwigluLoader {
     };
     using Lane = PreScaleLane<kPre>;
     __device__ __forceinline__ Lane lane(int64_t seg) const { return load_prescale<kPre>(pre, seg, F); }
+    template <bool kKeep = false>
     __device__ __forceinline__ void fetch(int64_t row, int64_t seg, Raw &r) const
     {
         const typename Elem<DT>::T *p = h + row * ld;
-        fetch_seg<DT>(p, seg * 16, F, aligned_gate, r.gate);
-        fetch_seg<DT>(p + F, seg * 16, F, aligned_value, r.value);
+        fetch_seg<DT, kKeep>(p, seg * 16, F, aligned_gate, r.gate);
+        fetch_seg<DT, kKeep>(p + F, seg * 16, F, aligned_value, r.value);
     }
     __device__ __forceinline__ void decode(const Raw &r, int64_t, const Lane &ln, float (&v)[16]) const
     {

@@ -256,10 +256,14 @@ __host__ __device__ constexpr size_t row_prep_lds_bytes(int threads)
 // Loader concept:
 //   static constexpr bool kFetchAfterDecode;         request the next row after decoding
 //                                                    this one (else before: two buffers)
+//   static constexpr bool kTwoPassPrefetch;          two-pass rows: request the next slice
+//                                                    before decoding this one
 //   struct Raw;                                      raw bytes of one 16-element segment
 //   struct Lane;                                     per-segment constants (same every row)
 //   Lane lane(int64_t seg) const;                    read them (once per workgroup)
-//   void fetch(int64_t row, int64_t seg, Raw &) const;    issue the loads (nothing past K)
+//   template <bool kKeep> void fetch(int64_t row, int64_t seg, Raw &) const;
+//                                                    issue the loads (nothing past K); kKeep:
+//                                                    the bytes will be read again soon
 //   void decode(const Raw &, int64_t seg, const Lane &, float (&)[16]) const;
 //                                                    fp32 elements 16*seg.., zero for k >= K
 // Splitting the two lets a workgroup request the next row while it works on this one.
@@ -403,22 +407,44 @@ __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row,
     float *red = lds + G * kTileStrideF;
     int8_t *orow = out + row * ld_out;
 
-    auto load = [&](int b, float (&v)[16]) {
+    // Slices are visited twice, pass 1 then pass 2 (once with amax_only); the raw bytes of
+    // the next visit are requested before this one is decoded, so their latency overlaps
+    // the rotation.  Pass 1 loads keep the row in the cache for pass 2.
+    using Raw = typename Loader::Raw;
+    const int nslices = (nb + G - 1) / G;
+    auto fetch_slice = [&](int s, bool first_pass, Raw &r) {
+        const int b = s * G + grp;
         if (b < nb) {
-            typename Loader::Raw raw;
-            ld.fetch(row, (int64_t)b * 16 + t, raw);
+            if (first_pass) ld.template fetch<true>(row, (int64_t)b * 16 + t, r);
+            else ld.fetch(row, (int64_t)b * 16 + t, r);
+        }
+    };
+    auto decode_slice = [&](int s, const Raw &r, float (&v)[16]) {
+        const int b = s * G + grp;
+        if (b < nb) {
             const typename Loader::Lane ln = ld.lane((int64_t)b * 16 + t);
-            ld.decode(raw, (int64_t)b * 16 + t, ln, v);
+            ld.decode(r, (int64_t)b * 16 + t, ln, v);
         } else {
 #pragma unroll
             for (int i = 0; i < 16; i++) v[i] = 0.0f;
         }
     };
+    // a second raw buffer for the loaders that gain from it (Loader::kTwoPassPrefetch)
+    constexpr bool kPrefetch = Loader::kTwoPassPrefetch;
     float v[16];
     float zmax = 0.0f;
-    const int nslices = (nb + G - 1) / G;
+    Raw cur{}, nxt{};
+    if constexpr (kPrefetch) fetch_slice(0, true, cur);
     for (int s = 0; s < nslices; s++) {
-        load(s * G + grp, v);
+        if constexpr (kPrefetch) {
+            if (s + 1 < nslices) fetch_slice(s + 1, true, nxt);
+            else if (!amax_only) fetch_slice(0, false, nxt);    // pass 2 starts over
+            decode_slice(s, cur, v);
+            cur = nxt;
+        } else {
+            fetch_slice(s, true, cur);
+            decode_slice(s, cur, v);
+        }
         hadamard256(v, tile, t, natural);
 #pragma unroll
         for (int i = 0; i < 16; i++) zmax = fmaxf(zmax, fabsf(v[i]));
@@ -431,7 +457,14 @@ __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row,
     const RowQuant rq = row_quant(zrow);
     for (int s = 0; s < nslices; s++) {
         const int b = s * G + grp;
-        load(b, v);
+        if constexpr (kPrefetch) {
+            if (s + 1 < nslices) fetch_slice(s + 1, false, nxt);
+            decode_slice(s, cur, v);
+            cur = nxt;
+        } else {
+            fetch_slice(s, false, cur);
+            decode_slice(s, cur, v);
+        }
         hadamard256(v, tile, t, natural);
         if (b < nb) store_codes(v, rq, orow + (int64_t)b * 256 + t * 16);
     }
