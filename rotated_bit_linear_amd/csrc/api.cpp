@@ -404,8 +404,10 @@ cr_status cr_linear_nvfp4_ex(const void *x, cr_dtype x_dtype, int64_t ld_x, int 
         if (x_dtype != CR_BF16 && x_dtype != CR_FP16 && x_dtype != CR_FP32) return CR_ERR_UNSUPPORTED_DTYPE;
         if (out_dtype != CR_BF16 && out_dtype != CR_FP16 && out_dtype != CR_FP32) return CR_ERR_UNSUPPORTED_DTYPE;
         if (check_flags(flags) != CR_OK || ld_x < (swiglu ? 2 * K : K) || ldc < N) return CR_ERR_INVALID_ARG;
-        if (N > 0 && (!w_fp4 || !w_sf || !global_scale)) return CR_ERR_INVALID_ARG;
+        if ((M > 0 && !x) || (N > 0 && (!w_fp4 || !w_sf || !global_scale))) return CR_ERR_INVALID_ARG;
         if (ld_fp4 < (K + 1) / 2 || ld_sf < (K + 15) / 16) return CR_ERR_INVALID_ARG;
+        if (!aligned(x, 16) || (ld_x * elem_size(x_dtype)) % 16 != 0) return CR_ERR_MISALIGNED;
+        if (!aligned(w_fp4, 16) || ld_fp4 % 16 != 0) return CR_ERR_MISALIGNED;
         return CR_OK;
     }
     if (!workspace || !out) return CR_ERR_INVALID_ARG;

@@ -300,5 +300,9 @@ def test_empty_extents_are_no_ops():
     assert layer(K=0) == INV
     assert layer(M=-1) == INV
     assert layer(g=N0) == INV                       # N > 0: the weight is still required
+    assert layer(M=300, N=0, w=N0, sf=N0, g=N0) == INV          # M > 0: x is not an empty buffer
+    assert layer(x=A16 + 2) == MIS                  # strides and alignment are still checked
+    assert L.cr_linear_nvfp4(N0, 0, 513, 0, 0, 512, A16, 256, A16, 32, A16, 256, N0, 0, 256, N0, 0, 0, 0, ST,
+                             None) == MIS            # 1026-byte rows
     assert L.cr_linear_nvfp4_ex(N0, 0, 512, 0, 0, 512, N0, A16, 256, A16, 32, A16, 256, N0, N0, 0, 256,
                                 N0, 0, 0, 0, ST, None) == OK
