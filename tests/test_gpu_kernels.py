@@ -586,3 +586,18 @@ def test_quant_act_swiglu_every_bf16_gate(F, flags):
     assert np.isfinite(rs).all()
     assert_bits_equal(q.cpu().numpy(), rq, "x_s8 (all bf16 gates)")
     assert_bits_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32), "x_scale (all bf16 gates)")
+
+
+@pytest.mark.parametrize("dt", [synth.DT_BF16, synth.DT_FP16])
+def test_quant_act_swiglu_two_pass_many_rows(dt):
+    """SwiGLU rows past 16384 columns (two passes) in more rows than the device holds
+    workgroups at once: with bf16 gates each workgroup builds the sigma table once and loops
+    over rows (alternating reduction slots), with fp16 one workgroup per row."""
+    M, F = 700, 17000
+    h = make_x(M, 2 * F, dt, seed=71, ld=2 * F + 8, special=True)
+    say(f"cr_quant_act_swiglu two-pass dt={dt} M={M} F={F}")
+    q, s = rbl.quant_act(h.to(dev()), F, swiglu=True)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant_act(host_bits(h, dt), dt, F, swiglu=True)
+    assert_bits_equal(q.cpu().numpy(), rq, "x_s8 (swiglu, two-pass, many rows)")
+    assert_bits_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32), "x_scale (swiglu, two-pass, many rows)")
