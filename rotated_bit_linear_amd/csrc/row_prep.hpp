@@ -407,9 +407,10 @@ __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row,
     float *red = lds + G * kTileStrideF;
     int8_t *orow = out + row * ld_out;
 
-    // Slices are visited twice, pass 1 then pass 2 (once with amax_only); the raw bytes of
-    // the next visit are requested before this one is decoded, so their latency overlaps
-    // the rotation.  Pass 1 loads keep the row in the cache for pass 2.
+    // Slices are visited twice, pass 1 then pass 2 (once with amax_only).  With
+    // Loader::kTwoPassPrefetch the raw bytes of the next visit are requested before this one
+    // is decoded, so their latency overlaps the rotation.  Pass 1 loads keep the row in the
+    // cache for pass 2.
     using Raw = typename Loader::Raw;
     const int nslices = (nb + G - 1) / G;
     auto fetch_slice = [&](int s, bool first_pass, Raw &r) {
@@ -475,8 +476,9 @@ __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row,
 // rpw * nb lane groups at once (group g: row slot g / nb, block g % nb), so that a
 // workgroup of up to 64 groups leaves few lanes idle whatever nb is (one row of 21 blocks
 // alone would leave 3 of 24 groups idle).  Row maximum: each group reduces its 16 lanes,
-// one lane per group writes it to LDS, one barrier, then every lane takes the maximum over
-// its row's nb entries; two alternating slot sets make one barrier per set of rows enough.
+// one lane per group writes it to LDS, one barrier, then lane t of each group reads entries
+// t and t + 16 of its row and the group reduces them; two alternating slot sets make one
+// barrier per set of rows enough.
 // The raw bytes of the next set of rows are requested before this set is decoded, or right
 // after it is decoded for loaders that prefer one buffer (Loader::kFetchAfterDecode).
 template <class Loader>
