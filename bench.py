@@ -2,17 +2,18 @@
 """Benchmark of the rotated W8A8 NVFP4 linear layer on one MI355X.
 
 One step = the QKV projection layer (qkv_proj [21504, 5376]) and the FFN-down layer with
-fused SwiGLU (fc2 [5376, 14336], H [19989, 28672]) at M = 19989 tokens, each layer run as
-cr_linear_nvfp4 runs it, through the component calls of the C ABI: activation preparation,
-NVFP4 weight preparation of each chunk (on a second stream when the weight takes several
-chunks), INT8 MFMA GEMM with the row-scale epilogue.  Inputs are seeded synthetic data
-resident in HBM before timing starts.
+fused SwiGLU (fc2 [5376, 14336], H [19989, 28672]) at M = 19989 tokens, each one call of the
+product entry point cr_linear_nvfp4 (activation preparation, NVFP4 weight preparation of each
+chunk on a second stream, INT8 MFMA GEMM with the row-scale epilogue).  Inputs are seeded
+synthetic data resident in HBM before timing starts.
 
-Prints one JSON line: ms/layer (mean over the two layers), per-layer and per-kernel
-timings from HIP events recorded on the launching streams, the GEMM roofline (INT8 MFMA
-peak, with the register-only MFMA ceiling measured beside it), each kernel timed alone
-(preparation rates against the HBM peak and a measured device copy), the expanded-S8
-control (weights prepared once, outside timing), the block's other shapes, short batches
+Prints one JSON line: ms/layer (mean over the two layers of the product call, HIP events on
+the calling stream), the per-kernel split of the same layers from a mirror of the call made
+of the component calls (each launch between events on its own stream), the GEMM roofline
+(INT8 MFMA peak), each kernel timed alone (preparation rates against the HBM peak and a
+measured device copy; the weight preparation also against its vector-issue roofline), the
+expanded-S8 control, the pages' 16 MiB staging bound, the other configurations (tiny, QKV at
+M = 4096, long K with fp16 and fp32 outputs), the block's other shapes, short batches
 (decode-inside-GEMM), and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
@@ -58,6 +59,10 @@ def parse_args():
     ap.add_argument("--short-batches", default="1,16,64,128",
                     help="activation rows of the short-batch (decode-inside-GEMM) lines; empty: none")
     ap.add_argument("--max-tile-bytes", type=int, default=0, help="0 = library default")
+    ap.add_argument("--bounded-tile-mib", type=int, default=16,
+                    help="also time the layers with S8 weight tiles bounded by this many MiB (0: skip)")
+    ap.add_argument("--configs", default="tiny,qkv_m4096,longk",
+                    help="the other configurations, reported apart from value ('' = none)")
     ap.add_argument("--serial", action="store_true", help="prepare weights on the main stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=8192)
@@ -92,10 +97,14 @@ def counter_traffic(launch_shape):
 
 
 class Layer:
-    def __init__(self, name, torch, rbl, synth, dev, max_tile_bytes, pre_bias=False):
-        """pre_bias: also apply a channel pre-scale [K] and a bias [N] (seeded)."""
+    def __init__(self, name, torch, rbl, synth, dev, max_tile_bytes, pre_bias=False, out_dtype=None):
+        """pre_bias: also apply a channel pre-scale [K] and a bias [N] (seeded); out_dtype:
+        one of the workload's output dtypes (default: its first)."""
         w = synth.WORKLOADS[name]
-        self.name, self.w = (name + "_prescale_bias" if pre_bias else name), w
+        odt = w.out_dtypes[0] if out_dtype is None else out_dtype
+        suffix = "" if out_dtype is None else "_out_" + synth.DTYPE_NAME[odt]
+        self.name, self.w = (name + ("_prescale_bias" if pre_bias else "") + suffix), w
+        self.max_tile_bytes = max_tile_bytes
         t0 = time.perf_counter()
         x = synth.make_activation(w)
         p = synth.make_weight_nvfp4(w)
@@ -117,7 +126,10 @@ class Layer:
         self.x_scale = torch.empty(w.M, dtype=torch.float32, device=dev)
         self.w_s8 = [torch.empty(self.R, kp, dtype=torch.int8, device=dev) for _ in range(ntiles)]
         self.w_scale = [torch.empty(self.R, dtype=torch.float32, device=dev) for _ in range(ntiles)]
-        self.out = torch.empty(w.M, w.N, dtype=synth.TORCH_DTYPE[w.out_dtypes[0]], device=dev)
+        self.out = torch.empty(w.M, w.N, dtype=synth.TORCH_DTYPE[odt], device=dev)
+        self.out_prod = torch.empty_like(self.out)      # the product call's output
+        self.ws = torch.empty(max(1, rbl.cr_linear_nvfp4_workspace_bytes(w.M, w.N, w.K, max_tile_bytes)),
+                              dtype=torch.uint8, device=dev)
         self.pre = self.bias = None
         if pre_bias:
             g = torch.Generator().manual_seed(w.seed + 5000)
@@ -132,8 +144,47 @@ class Layer:
         self.n_events = 3 + 4 * self.n_launch
 
 
+def run_product(L, rbl, s_main, s_aux):
+    """One call of the product entry point (cr_linear_nvfp4, or cr_linear_nvfp4_ex with a
+    pre-scale and a bias) on the main stream, weight tiles staged on s_aux."""
+    rbl.cr_linear_nvfp4(L.x, L.w.K, L.w.swiglu, L.codes, L.sf, L.g, L.out_prod, L.ws, L.max_tile_bytes,
+                        stream=s_main, aux_stream=s_aux, pre_scale=L.pre, bias=L.bias)
+
+
+def time_product(torch, rbl, layers, K, W, s_main, s_aux):
+    """W untimed steps, then K timed steps of the product call on every layer: per-layer
+    per-step ms (events recorded on the calling stream around each call), ms per step over
+    the whole loop, and the host wall time of the loop."""
+    mk = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+    evs = [[(mk(), mk()) for _ in layers] for _ in range(K)]
+    print(f"bench: warmup {W} steps of cr_linear_nvfp4 on {[L.name for L in layers]}", file=sys.stderr, flush=True)
+    for _ in range(W):
+        for L in layers:
+            run_product(L, rbl, s_main, s_aux)
+    torch.cuda.synchronize()
+    print(f"bench: timing {K} steps of cr_linear_nvfp4", file=sys.stderr, flush=True)
+    start, end = mk(), mk()
+    t0 = time.perf_counter()
+    start.record(s_main)
+    for k in range(K):
+        for li, L in enumerate(layers):
+            evs[k][li][0].record(s_main)
+            run_product(L, rbl, s_main, s_aux)
+            evs[k][li][1].record(s_main)
+    end.record(s_main)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1000.0
+    per_layer = [[evs[k][li][0].elapsed_time(evs[k][li][1]) for k in range(K)] for li in range(len(layers))]
+    return per_layer, start.elapsed_time(end) / K, wall_ms
+
+
+def product_stats(times):
+    t = sorted(times)
+    return {"ms": round(sum(t) / len(t), 4), "ms_median": round(t[len(t) // 2], 4), "ms_min": round(t[0], 4)}
+
+
 def run_layer(L, rbl, s_main, s_aux, ev):
-    """The layer as cr_linear_nvfp4 runs it: activation prep (main stream) while chunk 0 of
+    """The component mirror of the layer, as cr_linear_nvfp4 runs it: activation prep (main stream) while chunk 0 of
     the weight is prepared (second stream); GEMM of chunk c on the main stream while chunk
     c+1 is prepared; a weight tile is refilled only after the GEMM that read it.  A weight
     of one chunk is staged on the main stream.
@@ -392,28 +443,6 @@ def short_batches(torch, rbl, synth, dev, s_main, rows_list, n=20):
     return info
 
 
-def mfma_ceiling(torch, rbl, stream, iters=20000) -> dict:
-    """TOP/s of the register-only MFMA probe (cr_probe_mfma_i8) on uniformly random bytes, on
-    bell-shaped bytes with the spread of the layer's S8 operands, and on constant bytes: what
-    the power-limited matrix cores sustain with no memory traffic."""
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    out = torch.empty(512 * cus, dtype=torch.int32, device="cuda")
-    res = {}
-    for kind, key in ((rbl.CR_PROBE_UNIFORM, "random_int8"), (rbl.CR_PROBE_BELL, "layer_like_int8"),
-                      (rbl.CR_PROBE_CONSTANT, "constant_int8")):
-        tops = 0.0
-        for _ in range(2):                         # the second launch is the one reported
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            ops = rbl.cr_probe_mfma_i8(kind, iters, out, stream=stream)
-            b.record(stream)
-            torch.cuda.synchronize()
-            tops = ops / (a.elapsed_time(b) * 1e-3) / 1e12
-        res[key] = round(tops, 1)
-    del out
-    return res
-
-
 def copy_calibration(mib: int):
     import torch
     n = mib << 20
@@ -425,6 +454,69 @@ def copy_calibration(mib: int):
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+def alone_stats(torch, rbl, L, s_main, copy_gbs, n=10):
+    """Each kernel of the layer alone on the main stream, and the expanded-S8 control (the
+    whole weight prepared once outside timing, then activation prep + one full-N GEMM)."""
+    w = L.w
+    dev = L.x.device
+    w_full = torch.empty(w.N, w.K_pad, dtype=torch.int8, device=dev)
+    ws_full = torch.empty(w.N, dtype=torch.float32, device=dev)
+    act = ((lambda: rbl.cr_quant_act_swiglu(L.x, w.K, L.x_s8, L.x_scale, BT, stream=s_main)) if w.swiglu else
+           (lambda: rbl.cr_quant_act(L.x, w.K, L.x_s8, L.x_scale, BT, stream=s_main)))
+    wprep = lambda: rbl.cr_prep_weight_nvfp4(L.codes, L.sf, L.g, w.K, w_full, ws_full, BT, stream=s_main)  # noqa: E731
+    gemm = lambda: rbl.cr_gemm_s8_rowscale(L.x_s8, L.x_scale, w_full, ws_full, L.out, stream=s_main)  # noqa: E731
+    t_a = time_loop(torch, act, s_main, n=n)
+    t_w = time_loop(torch, wprep, s_main, n=n)
+    t_g = time_loop(torch, gemm, s_main, n=n)
+    t_x = time_loop(torch, lambda: (act(), gemm()), s_main, n=n)
+    valu = w.N * w.K_pad * WEIGHT_VALU_PER_ELEM[w.K_pad > 16384] / (t_w * 1e-3) / 1e12
+    out = {
+        "act_prep_ms": round(t_a, 4),
+        "act_prep_gbs": round(L.act_bytes / (t_a * 1e-3) / 1e9, 1),
+        "act_prep_frac_hbm_peak": round(L.act_bytes / (t_a * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "act_prep_frac_copy": round(L.act_bytes / (t_a * 1e-3) / 1e9 / copy_gbs, 4),
+        "weight_prep_ms": round(t_w, 4),
+        "weight_prep_gbs": round(L.w_bytes / (t_w * 1e-3) / 1e9, 1),
+        "weight_prep_frac_hbm_peak": round(L.w_bytes / (t_w * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "weight_prep_frac_copy": round(L.w_bytes / (t_w * 1e-3) / 1e9 / copy_gbs, 4),
+        # the weight preparation is bound by vector issue, not bytes: its own roofline
+        "weight_prep_valu_tops": round(valu, 2),
+        "weight_prep_frac_valu_peak": round(valu / PEAK_VALU_TOPS, 4),
+        "gemm_full_n_ms": round(t_g, 4),
+        "gemm_full_n_tops": round(L.gemm_ops / (t_g * 1e-3) / 1e12, 1),
+        "gemm_full_n_frac_peak": round(L.gemm_ops / (t_g * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+        "expanded_s8_control_ms": round(t_x, 4),
+    }
+    del w_full, ws_full
+    return out
+
+
+def check_product_equals_mirror(torch, L):
+    torch.cuda.synchronize()
+    if not torch.equal(L.out, L.out_prod):
+        raise SystemExit(f"bench: cr_linear_nvfp4 differs from the component calls on {L.name}")
+
+
+def measure_layers(torch, rbl, layers, K, W, s_main, s_aux):
+    """The product call timed over K steps (per-layer figures and ms per step), then the
+    component mirror over K steps for the per-kernel split; the two outputs must agree."""
+    prod, ms_step, wall = time_product(torch, rbl, layers, K, W, s_main, s_aux)
+    evs, mirror_step, _ = time_layers(torch, rbl, layers, K, W, s_main, s_aux)
+    info = {}
+    for li, L in enumerate(layers):
+        check_product_equals_mirror(torch, L)
+        ps = product_stats(prod[li])
+        split = layer_stats(L, [evs[k][li] for k in range(K)])
+        d = {k: split[k] for k in ("M", "N", "K", "K_pad", "swiglu", "weight_chunks", "rows_per_chunk", "path")}
+        d.update(ps)
+        d["layer_tops"] = round(L.gemm_ops / (ps["ms"] * 1e-3) / 1e12, 1)
+        d["split"] = {k: v for k, v in split.items() if k not in d}
+        d["split"]["component_mirror_ms"] = split["ms"]
+        d["product_minus_mirror_ms"] = round(ps["ms"] - split["ms"], 4)
+        info[L.name] = d
+    return info, ms_step, wall, mirror_step
 
 
 def main():
@@ -455,54 +547,56 @@ def main():
     s_main = torch.cuda.current_stream()
     s_aux = None if args.serial else torch.cuda.Stream()
     K, W = args.steps, args.warmup
-    evs, ms_per_step, wall_ms = time_layers(torch, rbl, layers, K, W, s_main, s_aux)
-    layer_info = {L.name: layer_stats(L, [evs[k][li] for k in range(K)]) for li, L in enumerate(layers)}
+    layer_info, ms_per_step, wall_ms, mirror_step = measure_layers(torch, rbl, layers, K, W, s_main, s_aux)
 
-    # each kernel alone on the main stream, and the "expanded S8" control: the whole weight
-    # prepared once outside timing, then activation prep + one full-N GEMM per layer
     print("bench: components alone and the expanded-S8 control", file=sys.stderr, flush=True)
     copy_gbs = copy_bandwidth(torch, s_main)
     for L in layers:
-        w = L.w
-        w_full = torch.empty(w.N, w.K_pad, dtype=torch.int8, device=dev)
-        ws_full = torch.empty(w.N, dtype=torch.float32, device=dev)
-        act = ((lambda: rbl.cr_quant_act_swiglu(L.x, w.K, L.x_s8, L.x_scale, BT, stream=s_main)) if w.swiglu else
-               (lambda: rbl.cr_quant_act(L.x, w.K, L.x_s8, L.x_scale, BT, stream=s_main)))
-        wprep = lambda: rbl.cr_prep_weight_nvfp4(L.codes, L.sf, L.g, w.K, w_full, ws_full, BT, stream=s_main)  # noqa: E731
-        gemm = lambda: rbl.cr_gemm_s8_rowscale(L.x_s8, L.x_scale, w_full, ws_full, L.out, stream=s_main)  # noqa: E731
-        t_a = time_loop(torch, act, s_main)
-        t_w = time_loop(torch, wprep, s_main)
-        t_g = time_loop(torch, gemm, s_main)
-        t_x = time_loop(torch, lambda: (act(), gemm()), s_main)
-        layer_info[L.name]["alone"] = {
-            "act_prep_ms": round(t_a, 4),
-            "act_prep_gbs": round(L.act_bytes / (t_a * 1e-3) / 1e9, 1),
-            "act_prep_frac_hbm_peak": round(L.act_bytes / (t_a * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "act_prep_frac_copy": round(L.act_bytes / (t_a * 1e-3) / 1e9 / copy_gbs, 4),
-            "weight_prep_ms": round(t_w, 4),
-            "weight_prep_gbs": round(L.w_bytes / (t_w * 1e-3) / 1e9, 1),
-            "weight_prep_frac_hbm_peak": round(L.w_bytes / (t_w * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "weight_prep_frac_copy": round(L.w_bytes / (t_w * 1e-3) / 1e9 / copy_gbs, 4),
-            # the weight preparation is bound by vector issue, not bytes: its own roofline
-            "weight_prep_valu_tops": round(w.N * w.K_pad * WEIGHT_VALU_PER_ELEM[w.K_pad > 16384]
-                                           / (t_w * 1e-3) / 1e12, 2),
-            "weight_prep_frac_valu_peak": round(w.N * w.K_pad * WEIGHT_VALU_PER_ELEM[w.K_pad > 16384]
-                                                / (t_w * 1e-3) / 1e12 / PEAK_VALU_TOPS, 4),
-            "gemm_full_n_ms": round(t_g, 4),
-            "gemm_full_n_frac_peak": round(L.gemm_ops / (t_g * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
-            "expanded_s8_control_ms": round(t_x, 4),
-        }
-        del w_full, ws_full
+        layer_info[L.name]["alone"] = alone_stats(torch, rbl, L, s_main, copy_gbs)
 
-    # the product entry point computes the same layer (one untimed call per layer)
-    for L in layers:
-        ref = L.out.clone()
-        got = rbl.linear_nvfp4(L.x, L.codes, L.sf, L.g, L.w.K, out_dtype=L.out.dtype, swiglu=L.w.swiglu,
-                               max_tile_bytes=args.max_tile_bytes, aux_stream=s_aux)
+    # the pages' bound on one S8 weight tile (16 MiB), same layers, product call, two streams
+    staging = None
+    if args.bounded_tile_mib > 0:
+        mt = args.bounded_tile_mib << 20
+        print(f"bench: the layers with S8 tiles bounded by {args.bounded_tile_mib} MiB", file=sys.stderr, flush=True)
+        for L in layers:
+            L.max_tile_bytes = mt
+            L.ws = torch.empty(rbl.cr_linear_nvfp4_workspace_bytes(L.w.M, L.w.N, L.w.K, mt), dtype=torch.uint8,
+                               device=dev)
+        k2 = max(5, K // 2)
+        prod, _, _ = time_product(torch, rbl, layers, k2, W, s_main, s_aux)
+        staging = {"max_tile_bytes": mt, "layers": {}}
+        for li, L in enumerate(layers):
+            check_product_equals_mirror(torch, L)
+            R, nch = rbl.cr_linear_nvfp4_plan(L.w.M, L.w.N, L.w.K, mt)
+            st = product_stats(prod[li])
+            st.update({"rows_per_chunk": R, "weight_chunks": nch, "workspace_bytes": L.ws.numel(),
+                       "vs_default_bound_ms": round(st["ms"] - layer_info[L.name]["ms"], 4)})
+            staging["layers"][L.name] = st
+        staging["value_ms_per_layer"] = round(sum(v["ms"] for v in staging["layers"].values()) / len(layers), 4)
+        for L in layers:
+            L.max_tile_bytes = args.max_tile_bytes
+            L.ws = torch.empty(1, dtype=torch.uint8, device=dev)
+
+    # the other configurations (tiny, QKV at M = 4096, long K with both output dtypes):
+    # product call + per-kernel split + each kernel alone, reported apart from `value`
+    cfg_info = None
+    cfgs = [c.strip() for c in args.configs.split(",") if c.strip()]
+    if cfgs:
+        extra = []
+        for n in cfgs:
+            w = synth.WORKLOADS[n]
+            for odt in w.out_dtypes:
+                print(f"bench: generating config {n} out={synth.DTYPE_NAME[odt]} ...", file=sys.stderr, flush=True)
+                extra.append(Layer(n, torch, rbl, synth, dev, args.max_tile_bytes,
+                                   out_dtype=odt if len(w.out_dtypes) > 1 else None))
         torch.cuda.synchronize()
-        if not torch.equal(ref, got):
-            raise SystemExit(f"bench: cr_linear_nvfp4 differs from the component calls on {L.name}")
-        del got
+        k2 = max(5, K // 2)
+        cfg_info, _, _, _ = measure_layers(torch, rbl, extra, k2, W, s_main, s_aux)
+        for L in extra:
+            cfg_info[L.name]["note"] = L.w.note
+            cfg_info[L.name]["alone"] = alone_stats(torch, rbl, L, s_main, copy_gbs)
+        del extra
 
     # the block's other linear shapes (same kernels), timed the same way but apart from
     # `value`; the MLP chain is fc1 followed by the FFN-down layer
@@ -516,8 +610,7 @@ def main():
             extra.append(Layer(base, torch, rbl, synth, dev, args.max_tile_bytes, pre_bias=(opt == "pre_bias")))
         torch.cuda.synchronize()
         k2 = max(5, K // 2)
-        evs2, _, _ = time_layers(torch, rbl, extra, k2, W, s_main, s_aux)
-        next_info = {L.name: layer_stats(L, [evs2[k][li] for k in range(k2)]) for li, L in enumerate(extra)}
+        next_info, _, _, _ = measure_layers(torch, rbl, extra, k2, W, s_main, s_aux)
         if "ffn_up" in next_info and "ffn_down" in layer_info:
             next_info["mlp_chain_fc1_swiglu_fc2_ms"] = round(next_info["ffn_up"]["ms"] + layer_info["ffn_down"]["ms"], 4)
         del extra
@@ -528,14 +621,11 @@ def main():
         print(f"bench: short batches {rows_list} (decode-inside-GEMM)", file=sys.stderr, flush=True)
         short_info = short_batches(torch, rbl, synth, dev, s_main, rows_list)
 
-    print("bench: register-only MFMA ceiling", file=sys.stderr, flush=True)
-    ceiling = mfma_ceiling(torch, rbl, s_main)
-
     dom = layers[0]
     dom_info = layer_info[dom.name]
     if dom.fused:
         # a short batch: the decode-inside-GEMM kernel, bound by vector issue
-        achieved = FUSED_VALU_PER_ELEM * dom.w.N * dom.w.K_pad / (dom_info["gemm_ms"] * 1e-3) / 1e12
+        achieved = FUSED_VALU_PER_ELEM * dom.w.N * dom.w.K_pad / (dom_info["split"]["gemm_ms"] * 1e-3) / 1e12
         roofline = {
             "kernel": f"gemm_nvfp4_fused ({dom.name}: M={dom.w.M} N={dom.w.N} K_pad={dom.w.K_pad})",
             "bound": "alu", "achieved": round(achieved, 2), "peak": PEAK_VALU_TOPS, "unit": "Tops/s",
@@ -544,8 +634,9 @@ def main():
         }
     else:
         # per launch: algorithmic ops of one chunk's GEMM over its mean launch duration
+        # (events around each GEMM launch of the component mirror, on the main stream)
         launch_ops = dom.gemm_ops / dom.nchunks
-        launch_ms = dom_info["gemm_ms"] / dom.nchunks
+        launch_ms = dom_info["split"]["gemm_ms"] / dom.nchunks
         achieved = launch_ops / (launch_ms * 1e-3) / 1e12
         launch_shape = (dom.w.M, dom.chunks[0][1], dom.w.K_pad)
         roofline = {
@@ -557,11 +648,8 @@ def main():
             "unit": "TOP/s",
             "frac": round(achieved / PEAK_INT8_TOPS, 4),
             "traffic": counter_traffic(launch_shape),
-            # what the matrix cores sustain with operands in registers (no memory traffic):
-            # random data toggles bits and meets the power limit; constant data does not
-            "measured_mfma_ceiling": ceiling,
-            "frac_of_random_data_ceiling": round(achieved / ceiling["random_int8"], 4),
-            "frac_of_layer_like_data_ceiling": round(achieved / ceiling["layer_like_int8"], 4),
+            "launch_ms": round(launch_ms, 4),
+            "per_launch_ops": launch_ops,
         }
     result = {
         "metric": METRIC,
@@ -580,12 +668,16 @@ def main():
             "workload": "; ".join(L.w.note for L in layers),
             "M": layers[0].w.M,
             "layers": names,
+            "timed_call": "cr_linear_nvfp4 (one call per layer, events on the calling stream)",
             "inputs": "bf16 activations ~N(0,1) (QKV: 1% channels x20), NVFP4 weights from 0.02*N(0,1)",
             "weight_prep_stream": "serial" if args.serial else "second stream",
             "max_tile_bytes": args.max_tile_bytes or rbl.DEFAULT_MAX_TILE_BYTES,
         },
         "roofline": roofline,
         "layers": layer_info,
+        "component_mirror_ms_per_step": round(mirror_step, 4),
+        "bounded_staging": staging,
+        "configs": cfg_info,
         "next_shapes": next_info,
         "short_batches": short_info,
         "wall_ms_timed_region": round(wall_ms, 2),

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define CR_ABI_VERSION 1
+#define CR_ABI_VERSION 2
 #define CR_MAX_K_PAD 133120       /* largest multiple of 256 with 127*127*K_pad < 2^31 */
 #define CR_TWO_PASS_K_PAD 16384   /* K_pad above this streams each row twice */
 #define CR_DEFAULT_MAX_TILE_BYTES ((size_t)128 << 20)
@@ -79,10 +79,20 @@ typedef enum {
     CR_ERR_MISALIGNED = 3,        /* base pointer or row stride alignment violated */
     CR_ERR_TOO_LARGE = 4,         /* K_pad > CR_MAX_K_PAD, or workspace too small */
     CR_ERR_NO_DEVICE = 5,         /* no current HIP device, or it is not gfx950 */
-    CR_ERR_LAUNCH = 6             /* the HIP runtime rejected a launch or an event call */
+    CR_ERR_LAUNCH = 6,            /* the HIP runtime rejected a launch or an event call */
+    /* not statuses: they give the type the whole range of int, so that any int a C caller
+     * passes is a value of the type (the library reads it; unknown values are rejected) */
+    CR_STATUS_RANGE_MIN_ = -0x7fffffff - 1,
+    CR_STATUS_RANGE_MAX_ = 0x7fffffff
 } cr_status;
 
-typedef enum { CR_BF16 = 0, CR_FP16 = 1, CR_FP32 = 2, CR_I32 = 3 } cr_dtype;
+typedef enum {
+    CR_BF16 = 0, CR_FP16 = 1, CR_FP32 = 2, CR_I32 = 3,
+    /* not dtypes: the whole range of int, as for cr_status (unknown values are
+     * CR_ERR_UNSUPPORTED_DTYPE) */
+    CR_DTYPE_RANGE_MIN_ = -0x7fffffff - 1,
+    CR_DTYPE_RANGE_MAX_ = 0x7fffffff
+} cr_dtype;
 
 enum {
     CR_FLAG_NONE = 0,
@@ -298,28 +308,6 @@ cr_status cr_gemm_nvfp4_fused(const int8_t *a_s8, int64_t lda, const float *a_sc
                               const uint8_t *w_sf, int64_t ld_sf, const float *global_scale,
                               const float *w_amax, const float *bias, int64_t M, int64_t N, int64_t K,
                               void *c, cr_dtype c_dtype, int64_t ldc, uint32_t flags, hipStream_t stream);
-
-/*
- * Diagnostic, not part of the layer: the sustained rate of the INT8 matrix instruction the
- * GEMM uses (v_mfma_i32_32x32x32_i8) with its operands already in registers, no memory
- * traffic at all.  The matrix cores are power-limited, so toggling operand bits lower the
- * sustained rate; this gives the ceiling a GEMM on real data can approach, beside the
- * published dense peak.
- *   data_kind  CR_PROBE_CONSTANT (every byte 1), CR_PROBE_UNIFORM (uniformly random bytes)
- *              or CR_PROBE_BELL (bell-shaped bytes: the centred sum of four uniform bytes
- *              times 7/32, standard deviation about 32, the spread of the layer's rotated
- *              S8 operands); anything else is CR_ERR_INVALID_ARG.
- *   iters      1 .. 1000000 loop iterations (16 MFMAs each, 8 waves per compute unit).
- *   out        device buffer of at least out_elems ints, overwritten with meaningless sums;
- *              out_elems must be >= 512 * (compute units of the current device).
- *   ops        host pointer: the number of int8 operations (2 per multiply-add) the launch
- *              performs; time the launch on `stream` to get the rate.
- */
-#define CR_PROBE_CONSTANT 0
-#define CR_PROBE_UNIFORM 1
-#define CR_PROBE_BELL 2
-cr_status cr_probe_mfma_i8(int data_kind, int iters, int *out, size_t out_elems, double *ops,
-                           hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -19,10 +19,9 @@ import torch
 
 from . import build as _build
 
-CR_ABI_VERSION = 1
+CR_ABI_VERSION = 2
 CR_BF16, CR_FP16, CR_FP32, CR_I32 = 0, 1, 2, 3
 CR_FLAG_NONE, CR_FLAG_FORCE_TWO_PASS, CR_FLAG_BLOCK_TRANSPOSED = 0, 1, 2
-CR_PROBE_CONSTANT, CR_PROBE_UNIFORM, CR_PROBE_BELL = 0, 1, 2
 CR_MAX_K_PAD = 133120
 DEFAULT_MAX_TILE_BYTES = 128 << 20
 STATUS = {0: "CR_OK", 1: "CR_ERR_INVALID_ARG", 2: "CR_ERR_UNSUPPORTED_DTYPE", 3: "CR_ERR_MISALIGNED",
@@ -72,7 +71,6 @@ def lib() -> C.CDLL:
             "cr_linear_nvfp4_ex": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, vp, i64, vp, i64, vp,
                                              i64, vp, vp, C.c_int, i64, vp, sz, sz, u32, vp, vp]),
             "cr_weight_amax_nvfp4": (C.c_int, [vp, i64, vp, i64, vp, i64, i64, vp, u32, vp]),
-            "cr_probe_mfma_i8": (C.c_int, [C.c_int, C.c_int, vp, sz, C.POINTER(C.c_double), vp]),
             "cr_gemm_nvfp4_fused": (C.c_int, [vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, i64, i64, i64, vp,
                                               C.c_int, i64, u32, vp]),
         }
@@ -235,15 +233,6 @@ def cr_gemm_nvfp4_fused(a_s8, a_scale, w_fp4, w_sf, global_scale, w_amax, K, c, 
     _check("cr_gemm_nvfp4_fused", lib().cr_gemm_nvfp4_fused(
         _ptr(a_s8), lda, _ptr(a_scale), _ptr(w_fp4), ld_fp4, _ptr(w_sf), ld_sf, _ptr(global_scale),
         _ptr(w_amax), _ptr(bias), M, N, K, _ptr(c), _TORCH_TO_CR[c.dtype], ldc, flags, _stream(stream)))
-
-
-def cr_probe_mfma_i8(data_kind, iters, out, stream=None) -> float:
-    """Launch the register-only MFMA rate probe on CR_PROBE_CONSTANT, CR_PROBE_UNIFORM or
-    CR_PROBE_BELL operands; returns the int8 operations it performs."""
-    ops = C.c_double(0.0)
-    _check("cr_probe_mfma_i8", lib().cr_probe_mfma_i8(int(data_kind), iters, _ptr(out), out.numel(),
-                                                      C.byref(ops), _stream(stream)))
-    return float(ops.value)
 
 
 # ---------------------------------------------------------------- conveniences ----

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libconvrot.so")
-SOURCES = ["api.cpp", "quant_act.hip", "prep_weight.hip", "gemm_s8.hip", "gemm_fused.hip", "probe_mfma.hip"]
+SOURCES = ["api.cpp", "quant_act.hip", "prep_weight.hip", "gemm_s8.hip", "gemm_fused.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -27,6 +27,19 @@ def _compile(src: str) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
     return obj
+
+
+def kernel_objects() -> list[str]:
+    """Object files of the kernel sources (every source but api.cpp), compiled if missing;
+    the sanitizer test links them under a host-only, instrumented build of api.cpp."""
+    os.makedirs(BUILD, exist_ok=True)
+    out = []
+    for src in SOURCES:
+        if src == "api.cpp":
+            continue
+        obj = os.path.join(BUILD, src + ".o")
+        out.append(obj if os.path.exists(obj) else _compile(src))
+    return out
 
 
 def build(verbose: bool = False) -> str:

@@ -14,6 +14,9 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
+#include <new>
+#include <vector>
 
 #include "../../include/convrot.h"
 #include "kernels.hpp"
@@ -216,20 +219,64 @@ LayerPlan plan_layer(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes)
     return p;
 }
 
+// Events that order the staging stream against the main stream.  A layer call takes one
+// set from a per-device pool and returns it once its work is enqueued: a wait enqueued on a
+// stream refers to the event's most recent record at the time of the wait, so a set can be
+// recorded again by the next call (on this thread or another) while earlier work is still
+// in flight.  Sets are created on first need (as many as there are concurrent callers) and
+// kept until the process ends; the pool is guarded by a mutex.
 struct EventSet {
     hipEvent_t ev[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
-    bool ok = true;
-    explicit EventSet(bool create)
+};
+
+std::mutex g_event_mu;
+std::vector<EventSet *> g_event_pool[kMaxDevices];
+
+class PooledEvents {
+public:
+    explicit PooledEvents(bool want)
     {
-        if (!create) return;
-        for (auto &e : ev)
-            if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) { ok = false; e = nullptr; }
+        if (!want) return;
+        if (hipGetDevice(&dev_) != hipSuccess || dev_ < 0 || dev_ >= kMaxDevices) {
+            (void)hipGetLastError();
+            dev_ = -1;
+            return;
+        }
+        {
+            std::lock_guard<std::mutex> lk(g_event_mu);
+            auto &pool = g_event_pool[dev_];
+            if (!pool.empty()) {
+                set_ = pool.back();
+                pool.pop_back();
+                return;
+            }
+        }
+        auto *s = new (std::nothrow) EventSet;
+        if (!s) return;
+        for (auto &e : s->ev)
+            if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+                (void)hipGetLastError();
+                for (auto &d : s->ev)
+                    if (d) (void)hipEventDestroy(d);
+                delete s;
+                return;
+            }
+        set_ = s;
     }
-    ~EventSet()
+    ~PooledEvents()
     {
-        for (auto &e : ev)
-            if (e) (void)hipEventDestroy(e);
+        if (!set_) return;
+        std::lock_guard<std::mutex> lk(g_event_mu);
+        g_event_pool[dev_].push_back(set_);
     }
+    PooledEvents(const PooledEvents &) = delete;
+    PooledEvents &operator=(const PooledEvents &) = delete;
+    bool ok() const { return set_ != nullptr; }
+    hipEvent_t operator[](int i) const { return set_->ev[i]; }
+
+private:
+    int dev_ = -1;
+    EventSet *set_ = nullptr;
 };
 
 }  // namespace
@@ -459,9 +506,14 @@ cr_status cr_linear_nvfp4_ex(const void *x, cr_dtype x_dtype, int64_t ld_x, int 
     // the activation preparation to run beside, which gains nothing on this chip, while the
     // two cross-stream waits cost about as much as a small layer's activation preparation
     const bool overlap = s_aux != nullptr && s_aux != s_main && p.nchunks > 1;
-    EventSet evs(overlap);
-    if (overlap && !evs.ok) return CR_ERR_LAUNCH;
-    hipEvent_t ev_start = evs.ev[0], ev_prep[2] = {evs.ev[1], evs.ev[2]}, ev_gemm[2] = {evs.ev[3], evs.ev[4]};
+    PooledEvents evs(overlap);
+    if (overlap && !evs.ok()) return CR_ERR_LAUNCH;
+    hipEvent_t ev_start = nullptr, ev_prep[2] = {nullptr, nullptr}, ev_gemm[2] = {nullptr, nullptr};
+    if (overlap) {
+        ev_start = evs[0];
+        ev_prep[0] = evs[1]; ev_prep[1] = evs[2];
+        ev_gemm[0] = evs[3]; ev_gemm[1] = evs[4];
+    }
 
     if (overlap) {
         // the staging stream must not run ahead of work already queued on s_main
@@ -508,20 +560,6 @@ cr_status cr_linear_nvfp4(const void *x, cr_dtype x_dtype, int64_t ld_x, int swi
     return cr_linear_nvfp4_ex(x, x_dtype, ld_x, swiglu, M, K, nullptr, w_fp4, ld_fp4, w_sf, ld_sf,
                               global_scale, N, nullptr, out, out_dtype, ldc, workspace, ws_bytes,
                               max_tile_bytes, flags, s_main, s_aux);
-}
-
-cr_status cr_probe_mfma_i8(int data_kind, int iters, int *out, size_t out_elems, double *ops,
-                           hipStream_t stream)
-{
-    if (!out || !ops || iters < 1 || iters > 1000000) return CR_ERR_INVALID_ARG;
-    if (data_kind < CR_PROBE_CONSTANT || data_kind > CR_PROBE_BELL) return CR_ERR_INVALID_ARG;
-    if (!aligned(out, 4)) return CR_ERR_MISALIGNED;
-    cr_status s = current_device_ok();
-    if (s != CR_OK) return s;
-    const int cus = current_cus();
-    if (out_elems < (size_t)512 * (size_t)cus) return CR_ERR_INVALID_ARG;
-    *ops = 2.0 * 32768.0 * 16.0 * (double)iters * (double)(8 * cus);
-    return from_hip(convrot::launch_probe_mfma(cus, iters, data_kind, out, stream));
 }
 
 }  // extern "C"

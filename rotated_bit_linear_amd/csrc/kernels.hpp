@@ -44,7 +44,5 @@ hipError_t launch_gemm_nvfp4_fused(const int8_t *A, int64_t lda, const float *sa
                                    const float *amax, const float *bias, int64_t M, int64_t N, int64_t K,
                                    void *C, int out_dtype, int64_t ldc, bool transposed, hipStream_t st);
 
-// register-only MFMA rate probe (diagnostic): 2 workgroups of 256 threads per CU
-hipError_t launch_probe_mfma(int cus, int iters, int kind, int *out, hipStream_t st);
 
 }  // namespace convrot

@@ -225,18 +225,20 @@ __device__ __forceinline__ void quantize_store16(const float (&z)[16], float m, 
 // Row constants from a' = max |z|: the scale a / 127 and the code multiplier.
 struct RowQuant {
     float scale;    // a / 127 (0 when a == 0)
-    float mult;     // r * 0.0625 (folded) or 127 / (a * 2^64) (scale first)
+    float mult;     // r * 0.0625 (folded) or 127 / (a * 2^64) (scale first); 0 when a == 0
     bool folded;    // block-uniform
 };
 
+// A zero row (a == 0: every z is 0) takes the scale-first branch with multiplier 0, so
+// every product is exactly 0 and every code 0; 127 / 0 is never formed.
 __device__ __forceinline__ RowQuant row_quant(float zmax)
 {
     const float a = zmax * 0.0625f;
-    const float r = (a == 0.0f) ? 0.0f : 127.0f / a;
+    const bool zero = (a == 0.0f);
     RowQuant q;
-    q.scale = (a == 0.0f) ? 0.0f : a / 127.0f;
+    q.scale = zero ? 0.0f : a / 127.0f;
     q.folded = zmax >= 0x1p-100f;
-    q.mult = q.folded ? r * 0.0625f : 127.0f / (a * 0x1p64f);
+    q.mult = q.folded ? (127.0f / a) * 0.0625f : (zero ? 0.0f : 127.0f / (a * 0x1p64f));
     return q;
 }
 

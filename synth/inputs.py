@@ -223,6 +223,32 @@ def nvfp4_encode(w: torch.Tensor, *, ld_codes: int | None = None, ld_sf: int | N
     return NVFP4Weight(codes=codes, sf=sf, g=float(g), K=K)
 
 
+def raw_nvfp4(N: int, K: int, seed: int, *, ld_codes: int | None = None, ld_sf: int | None = None,
+              g: float = 0.0137, uniform_rows: bool = True) -> NVFP4Weight:
+    """NVFP4 bytes drawn directly, not through an encoder: every code byte uniformly random
+    (so all 16 nibbles appear, -0 included), every block-scale byte a finite E4M3 byte (all
+    but 0x7F and 0xFF), and random garbage in the row padding of both arrays (NaN scale bytes
+    included there).  With ``uniform_rows`` the first 254 rows each use one scale byte for
+    the whole row, one row per finite byte in byte order; the remaining rows take the finite
+    bytes in seeded shuffles, so every byte occurs in any 254 consecutive scale slots."""
+    g_np = _gen(seed)
+    nb = (K + 15) // 16
+    ld_codes = ld_codes if ld_codes is not None else round_up((K + 1) // 2, 16)
+    ld_sf = ld_sf if ld_sf is not None else nb
+    codes = torch.randint(0, 256, (N, ld_codes), generator=g_np, dtype=torch.int32).to(torch.uint8)
+    sf = torch.randint(0, 256, (N, ld_sf), generator=g_np, dtype=torch.int32).to(torch.uint8)
+    finite = torch.tensor([b for b in range(256) if b not in (0x7F, 0xFF)], dtype=torch.uint8)
+    n_uni = min(N, 254) if uniform_rows else 0
+    if n_uni:
+        sf[:n_uni, :nb] = finite[:n_uni, None]
+    rest = N - n_uni
+    if rest:
+        reps = -(-(rest * nb) // 254)
+        pool = torch.cat([finite[torch.randperm(254, generator=g_np)] for _ in range(reps)])
+        sf[n_uni:, :nb] = pool[:rest * nb].view(rest, nb)
+    return NVFP4Weight(codes=codes, sf=sf, g=float(torch.tensor(g, dtype=torch.float32)), K=K)
+
+
 def make_weight_nvfp4(w: Workload, **kw) -> NVFP4Weight:
     kw.setdefault("garbage_seed", w.seed + 3000)
     return nvfp4_encode(make_weight_f32(w), **kw)
@@ -247,5 +273,5 @@ def sample_rows(M: int, n: int, seed: int, must: torch.Tensor | None = None) -> 
 
 
 __all__ = ["Workload", "WORKLOADS", "MLP_CHAIN", "make_activation", "make_weight_f32", "make_weight_nvfp4",
-           "nvfp4_encode", "NVFP4Weight", "special_rows", "sample_rows", "bits_u16",
+           "nvfp4_encode", "raw_nvfp4", "NVFP4Weight", "special_rows", "sample_rows", "bits_u16",
            "DT_BF16", "DT_FP16", "DT_FP32", "DT_I32", "TORCH_DTYPE", "DTYPE_NAME", "round_up"]

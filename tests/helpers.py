@@ -49,3 +49,27 @@ def assert_bits_equal(got: np.ndarray, ref: np.ndarray, what: str):
         first = tuple(bad[0])
         raise AssertionError(f"{what}: {len(bad)} of {ref.size} differ; first at {first}: "
                              f"got {got[first]!r} want {ref[first]!r}")
+
+
+def out_bits(arr, dtype: int) -> np.ndarray:
+    """Output (torch tensor, or oracle array with bf16/fp16 as uint16 bit patterns) as raw
+    bit patterns: uint16 for bf16/fp16, uint32 for fp32, int32 for the accumulator."""
+    if isinstance(arr, torch.Tensor):
+        arr = arr.detach().cpu().contiguous()
+        if dtype in (synth.DT_BF16, synth.DT_FP16):
+            return arr.view(torch.int16).numpy().view(np.uint16)
+        if dtype == synth.DT_FP32:
+            return arr.view(torch.int32).numpy().view(np.uint32)
+        return arr.numpy()
+    arr = np.ascontiguousarray(arr)
+    return arr.view(np.uint32) if dtype == synth.DT_FP32 else arr
+
+
+def check_output(got, ref, dtype: int, what: str) -> float:
+    """The output bar (relative L2 within TOL[dtype] against the oracle's output rounded to
+    the same dtype), then the stronger property the kernels are built to: the epilogue does
+    the oracle's operations in the oracle's order, so every output bit is identical."""
+    err = rel_l2(out_f64(got, dtype), out_f64(ref, dtype))
+    assert err <= TOL[dtype], (what, err)
+    assert_bits_equal(out_bits(got, dtype), out_bits(ref, dtype), f"{what} (bits)")
+    return err

@@ -24,7 +24,7 @@ def test_library_exports_header_functions():
                           "cr_gemm_s8_rowscale", "cr_linear_nvfp4", "cr_linear_nvfp4_workspace_bytes",
                           "cr_linear_nvfp4_plan", "cr_quant_act_ex", "cr_gemm_s8_rowscale_bias",
                           "cr_linear_nvfp4_ex", "cr_weight_amax_nvfp4", "cr_gemm_nvfp4_fused",
-                          "cr_probe_mfma_i8", "cr_abi_version", "cr_status_string", "cr_padded_k"}
+                          "cr_abi_version", "cr_status_string", "cr_padded_k"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -235,32 +235,6 @@ def test_gemm_fused_validation():
     n_big = 32 * (0xFFFFFFFF // 256) + 32  # one 32-row band more than 2^32 work-items allow
     assert fz(N=n_big, ldc=n_big) == BIG
     assert fz(flags=4) == INV
-
-
-def test_probe_validation():
-    L = rbl.lib()
-    ops = C.c_double(0)
-    assert L.cr_probe_mfma_i8(1, 0, A16, 1 << 20, C.byref(ops), ST) == INV        # iters < 1
-    assert L.cr_probe_mfma_i8(1, 10, None, 1 << 20, C.byref(ops), ST) == INV
-    assert L.cr_probe_mfma_i8(1, 10, A16, 1 << 20, None, ST) == INV
-    assert L.cr_probe_mfma_i8(1, 10, A16 + 2, 1 << 20, C.byref(ops), ST) == MIS
-    assert L.cr_probe_mfma_i8(-1, 10, A16, 1 << 20, C.byref(ops), ST) == INV        # data kind
-    assert L.cr_probe_mfma_i8(3, 10, A16, 1 << 20, C.byref(ops), ST) == INV
-
-
-@pytest.mark.skipif(torch.cuda.is_available(), reason="valid arguments would launch on a real GPU")
-def test_valid_arguments_report_no_device_without_gpu():
-    assert qa() == NODEV
-    assert pw() == NODEV
-    assert gm() == NODEV
-    assert wa() == NODEV
-    assert fz() == NODEV
-    assert fz(am=None) == NODEV              # row maxima found by the kernel itself
-    L = rbl.lib()
-    ws = L.cr_linear_nvfp4_workspace_bytes(64, 256, 512, 0)
-    assert L.cr_linear_nvfp4(A16, 0, 512, 0, 64, 512, A16, 256, A16, 32, A16, 256, A16, 0, 256, 0x100000, ws, 0, 0,
-                             ST, None) == NODEV
-    assert fz(dt=3, sa=None) == NODEV
 
 
 def test_empty_extents_are_no_ops():

@@ -20,8 +20,6 @@ def test_more_than_one_gpu_is_refused():
 
 def test_counter_traffic_follows_source_and_shape(tmp_path, monkeypatch):
     shape = (19989, 10752, 5376)
-    assert bench.counter_traffic(shape) is not None                 # the committed summary
-    assert bench.counter_traffic((19989, 5376, 5376)) is None       # another launch shape
     fake = tmp_path / "summary.md"
     fake.write_text("gemm_source_sha256_16: 0000000000000000\nlaunch_shape_m_n_kpad: 19989 10752 5376\n"
                     "hbm_bytes_per_launch_calibrated: 1.0e+09\n")
@@ -29,3 +27,6 @@ def test_counter_traffic_follows_source_and_shape(tmp_path, monkeypatch):
     assert bench.counter_traffic(shape) is None                     # the GEMM source changed
     fake.write_text(fake.read_text().replace("0000000000000000", bench.gemm_source_hash()))
     assert bench.counter_traffic(shape) == 1.0e9
+    assert bench.counter_traffic((19989, 5376, 5376)) is None       # another launch shape
+    monkeypatch.setattr(bench, "PMC_PROFILE", str(tmp_path / "missing.md"))
+    assert bench.counter_traffic(shape) is None

@@ -54,6 +54,61 @@ def test_decode_exact_for_power_of_two_g(orc):
             assert np.array_equal(got, decode_f64(codes, sf, g, K))
 
 
+def _all_codes_all_scales():
+    """Rows of 16 elements holding codes 0..15 in order (byte j = code 2j | code 2j+1 << 4),
+    one row per finite E4M3 scale byte (every byte but 0x7F and 0xFF, the NaNs)."""
+    scales = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], np.uint8)
+    row = np.array([(2 * j) | ((2 * j + 1) << 4) for j in range(8)], np.uint8)
+    codes = np.tile(row, (len(scales), 1))
+    return codes, scales[:, None].copy()
+
+
+# global scales that are not powers of two: decimal fractions, 1/3, one that puts products
+# in the subnormal range, one near the top of the range (largest products overflow to inf),
+# and the synthetic encoder's g for a 0.02 * N(0, 1) weight
+NON_DYADIC_G = [np.float32(0.0137), np.float32(1.0 / 3.0), np.float32(3.3e-43 * 1e4), np.float32(1.7e-41),
+                np.float32(1.9e35), np.float32(7.1e-37)]
+
+
+def _encoder_g():
+    w = 0.02 * torch.randn(64, 512, generator=torch.Generator().manual_seed(0))
+    return np.float32(synth.nvfp4_encode(w).g)
+
+
+def test_decode_non_dyadic_g_is_one_rounding_of_the_exact_product(orc):
+    """value = fp32(E2M1 * E4M3) * g with the first product exact (at most 2 + 4 significant
+    bits), so the decode is the exact product E2M1 * E4M3 * g rounded once to binary32.  That
+    product has at most 2 + 4 + 24 significant bits and is exact in float64; numpy's float64
+    -> float32 cast rounds it to nearest even, subnormals and overflow included.  E2M1 comes
+    from its closed form, E4M3 from torch's float8_e4m3fn; every code (with -0, code 8) meets
+    every finite scale byte (negative and subnormal ones included)."""
+    codes, sf = _all_codes_all_scales()
+    gs = NON_DYADIC_G + [_encoder_g()]
+    assert all(np.frexp(np.float64(g))[0] != 0.5 for g in gs), "every g must be a non-power of two"
+    for g in gs:
+        dec = orc.nvfp4_decode(codes, sf, float(g), 16)[:, :16]
+        exact = E2M1[None, :] * E4M3[sf[:, 0]][:, None] * np.float64(g)      # exact in float64
+        with np.errstate(over="ignore"):
+            want = exact.astype(np.float32)
+        assert np.array_equal(dec.view(np.uint32), want.view(np.uint32)), f"g={g!r}"
+        # zero codes give +-0 with the sign of the product (code 8 is -0)
+        assert np.array_equal(np.signbit(dec[:, 8]), np.signbit(want[:, 8]))
+
+
+def test_decode_pin_rejects_double_rounding(orc):
+    """The pin above has teeth: E2M1 * (E4M3 * g), which rounds the scale product first,
+    differs from one rounding of the exact product for some code, scale byte and g above."""
+    codes, sf = _all_codes_all_scales()
+    e2m1 = E2M1.astype(np.float32)
+    differs = 0
+    for g in NON_DYADIC_G:
+        with np.errstate(over="ignore"):
+            wrong = e2m1[None, :] * (E4M3[sf[:, 0]].astype(np.float32)[:, None] * np.float32(g))
+            want = (E2M1[None, :] * E4M3[sf[:, 0]][:, None] * np.float64(g)).astype(np.float32)
+        differs += int(np.count_nonzero(wrong.view(np.uint32) != want.view(np.uint32)))
+    assert differs > 0
+
+
 def test_decode_matches_synthetic_encoder(orc):
     g0 = torch.Generator().manual_seed(7)
     w = 0.02 * torch.randn(64, 1000, generator=g0)
