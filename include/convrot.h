@@ -267,6 +267,32 @@ cr_status cr_linear_nvfp4_ex(const void *x, cr_dtype x_dtype, int64_t ld_x, int 
                              uint32_t flags, hipStream_t s_main, hipStream_t s_aux);
 
 /*
+ * The layer for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): cr_linear_nvfp4_ex with serial
+ * staging on `stream` and, as its workspace, a device array of CR_NOALLOC_SCRATCH_BYTES
+ * inside the library (one per GPU, created when the library's code is loaded on that GPU
+ * and kept until the process ends).  Nothing is allocated: no hipMalloc, no hipFree, no
+ * event creation.  The results are those of cr_linear_nvfp4_ex, bit for bit.
+ *   x ... ldc        as in cr_linear_nvfp4_ex (the caller still owns inputs and outputs).
+ *   max_tile_bytes   bound of one S8 weight tile; 0 selects the largest bound for which
+ *                    the S8 activation, its scales and two weight tiles fit the array.
+ *   stream           every launch goes to this stream.
+ * Returns CR_ERR_TOO_LARGE, with nothing enqueued, when the layer's workspace (see
+ * cr_linear_nvfp4_workspace_bytes) would exceed CR_NOALLOC_SCRATCH_BYTES: the S8 activation
+ * alone takes M * K_pad bytes, so M * K_pad must stay well below 64 MiB (for example
+ * M <= 11000 at K = 5376).  All calls on one GPU share its array, and nothing in it needs
+ * to start at zero: calls that overlap in time on one GPU (two streams, or two host
+ * threads) race on it and must be ordered by the caller.
+ */
+#define CR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+cr_status cr_linear_nvfp4_noalloc(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu,
+                                  int64_t M, int64_t K, const float *pre_scale,
+                                  const uint8_t *w_fp4, int64_t ld_fp4,
+                                  const uint8_t *w_sf, int64_t ld_sf, const float *global_scale,
+                                  int64_t N, const float *bias, void *out, cr_dtype out_dtype, int64_t ldc,
+                                  size_t max_tile_bytes, uint32_t flags, hipStream_t stream);
+
+/*
  * Row maxima of the rotated weight, without the codes: w_amax[n] = a = max_k |y[n, k]|,
  * y the NVFP4 decode of row n followed by ConvRot256 (the a of the row quantization; the
  * weight scale is a / 127).  It is what cr_gemm_nvfp4_fused needs before it can quantize a

@@ -23,6 +23,7 @@ CR_ABI_VERSION = 2
 CR_BF16, CR_FP16, CR_FP32, CR_I32 = 0, 1, 2, 3
 CR_FLAG_NONE, CR_FLAG_FORCE_TWO_PASS, CR_FLAG_BLOCK_TRANSPOSED = 0, 1, 2
 CR_MAX_K_PAD = 133120
+NOALLOC_SCRATCH_BYTES = 64 << 20
 DEFAULT_MAX_TILE_BYTES = 128 << 20
 STATUS = {0: "CR_OK", 1: "CR_ERR_INVALID_ARG", 2: "CR_ERR_UNSUPPORTED_DTYPE", 3: "CR_ERR_MISALIGNED",
           4: "CR_ERR_TOO_LARGE", 5: "CR_ERR_NO_DEVICE", 6: "CR_ERR_LAUNCH"}
@@ -70,6 +71,8 @@ def lib() -> C.CDLL:
                                           vp, C.c_int, i64, vp, sz, sz, u32, vp, vp]),
             "cr_linear_nvfp4_ex": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, vp, i64, vp, i64, vp,
                                              i64, vp, vp, C.c_int, i64, vp, sz, sz, u32, vp, vp]),
+            "cr_linear_nvfp4_noalloc": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, vp, i64, vp, i64, vp,
+                                                  i64, vp, vp, C.c_int, i64, sz, u32, vp]),
             "cr_weight_amax_nvfp4": (C.c_int, [vp, i64, vp, i64, vp, i64, i64, vp, u32, vp]),
             "cr_gemm_nvfp4_fused": (C.c_int, [vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, i64, i64, i64, vp,
                                               C.c_int, i64, u32, vp]),
@@ -215,6 +218,19 @@ def cr_linear_nvfp4(x, K, swiglu, w_fp4, w_sf, global_scale, out, workspace, max
         _check("cr_linear_nvfp4_ex", lib().cr_linear_nvfp4_ex(
             _ptr(x), _TORCH_TO_CR[x.dtype], ld_x, int(bool(swiglu)), M, K, _ptr(pre_scale), _ptr(w_fp4), ld_fp4,
             _ptr(w_sf), ld_sf, _ptr(global_scale), N, _ptr(bias), _ptr(out), _TORCH_TO_CR[out.dtype], ldc, *ws))
+
+
+def cr_linear_nvfp4_noalloc(x, K, swiglu, w_fp4, w_sf, global_scale, out, max_tile_bytes=0, flags=0,
+                            stream=None, pre_scale=None, bias=None):
+    """The layer with the library's own device scratch as its workspace (nothing allocated)."""
+    M, ld_x = _rows_ld(x)
+    N, ld_fp4 = _rows_ld(w_fp4)
+    _, ld_sf = _rows_ld(w_sf)
+    _, ldc = _rows_ld(out)
+    _check("cr_linear_nvfp4_noalloc", lib().cr_linear_nvfp4_noalloc(
+        _ptr(x), _TORCH_TO_CR[x.dtype], ld_x, int(bool(swiglu)), M, K, _ptr(pre_scale), _ptr(w_fp4), ld_fp4,
+        _ptr(w_sf), ld_sf, _ptr(global_scale), N, _ptr(bias), _ptr(out), _TORCH_TO_CR[out.dtype], ldc,
+        max_tile_bytes, flags, _stream(stream)))
 
 
 def cr_weight_amax_nvfp4(w_fp4, w_sf, global_scale, K, w_amax, flags=0, stream=None):

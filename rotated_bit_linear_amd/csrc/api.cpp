@@ -279,6 +279,51 @@ private:
     EventSet *set_ = nullptr;
 };
 
+// Device scratch of cr_linear_nvfp4_noalloc: the layer's workspace for callers that cannot
+// allocate.  One copy per GPU, created with the code object and held until the process
+// ends.  In host code `scratch` names a host-side stand-in, not device memory: only the
+// address that hipGetSymbolAddress returns for the current device may reach a kernel.
+static __device__ __align__(256) int8_t scratch[CR_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device (guarded)
+
+// The current device's copy of `scratch`, resolved on the first call on that device (with
+// that device current) and kept.
+cr_status scratch_for_current_device(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return CR_ERR_NO_DEVICE;
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return CR_ERR_LAUNCH;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return CR_OK;
+}
+
+// The tile bound cr_linear_nvfp4_noalloc uses when the caller passes 0: the largest one for
+// which the activation and two S8 weight tiles (with their scales) fit the scratch; 0 when
+// not even the activation and two 256-row tiles fit.
+size_t noalloc_tile_bound(int64_t M, int64_t K)
+{
+    const int64_t kp = pad256(K);
+    const size_t act = up256((size_t)M * (size_t)kp) + up256((size_t)M * 4);
+    if (act + 512 >= CR_NOALLOC_SCRATCH_BYTES) return 0;
+    const size_t rem = CR_NOALLOC_SCRATCH_BYTES - act - 512;
+    const int64_t T = convrot::kGemmTileRows;
+    const int64_t rows = (int64_t)(rem / (2 * ((size_t)kp + 4))) / T * T;
+    return rows < T ? 0 : (size_t)rows * (size_t)kp;
+}
+
 }  // namespace
 
 extern "C" {
@@ -560,6 +605,35 @@ cr_status cr_linear_nvfp4(const void *x, cr_dtype x_dtype, int64_t ld_x, int swi
     return cr_linear_nvfp4_ex(x, x_dtype, ld_x, swiglu, M, K, nullptr, w_fp4, ld_fp4, w_sf, ld_sf,
                               global_scale, N, nullptr, out, out_dtype, ldc, workspace, ws_bytes,
                               max_tile_bytes, flags, s_main, s_aux);
+}
+
+cr_status cr_linear_nvfp4_noalloc(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu,
+                                  int64_t M, int64_t K, const float *pre_scale,
+                                  const uint8_t *w_fp4, int64_t ld_fp4,
+                                  const uint8_t *w_sf, int64_t ld_sf, const float *global_scale,
+                                  int64_t N, const float *bias, void *out, cr_dtype out_dtype, int64_t ldc,
+                                  size_t max_tile_bytes, uint32_t flags, hipStream_t stream)
+{
+    if (M < 0 || N < 0 || K < 1) return CR_ERR_INVALID_ARG;
+    if (pad256(K) > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
+    if (M == 0 || N == 0)    // an empty layer: argument checks only, as in cr_linear_nvfp4_ex
+        return cr_linear_nvfp4_ex(x, x_dtype, ld_x, swiglu, M, K, pre_scale, w_fp4, ld_fp4, w_sf, ld_sf,
+                                  global_scale, N, bias, out, out_dtype, ldc, nullptr, 0, max_tile_bytes, flags,
+                                  stream, nullptr);
+    size_t bound = max_tile_bytes;
+    if (bound == 0 && M > kFusedMaxRows) {
+        bound = noalloc_tile_bound(M, K);
+        if (bound == 0) return CR_ERR_TOO_LARGE;
+    }
+    if (plan_layer(M, N, K, bound).bytes > CR_NOALLOC_SCRATCH_BYTES) return CR_ERR_TOO_LARGE;
+    cr_status s = current_device_ok();
+    if (s != CR_OK) return s;
+    void *ws = nullptr;
+    if ((s = scratch_for_current_device(&ws)) != CR_OK) return s;
+    // serial staging on `stream`: no second stream, so no events are needed
+    return cr_linear_nvfp4_ex(x, x_dtype, ld_x, swiglu, M, K, pre_scale, w_fp4, ld_fp4, w_sf, ld_sf, global_scale,
+                              N, bias, out, out_dtype, ldc, ws, CR_NOALLOC_SCRATCH_BYTES, bound, flags, stream,
+                              nullptr);
 }
 
 }  // extern "C"

@@ -1,11 +1,11 @@
 // Sanitizer driver for the host side of the C ABI (argument validation, the chunk planner,
-// workspace sizes).  The test suite builds the library's sources host-only (no device
-// code) with AddressSanitizer and UndefinedBehaviorSanitizer and links this program against
-// them; it runs on the CPU.  Every call below either fails validation or has an empty
-// extent, so no kernel is ever launched: the pointers are aligned host addresses that no
-// call may dereference.  Calls with fully valid arguments are made only when no GPU is
-// visible, where they must return CR_ERR_NO_DEVICE.  Exit status 1 names the first
-// unexpected status.
+// workspace sizes, the allocation-free entry point's refusals).  The test suite builds
+// api.cpp with AddressSanitizer and UndefinedBehaviorSanitizer on its host side, links it
+// with the library's kernel objects and this program, and runs it on the CPU.  Every call
+// below either fails validation or has an empty extent, so no kernel is ever launched: the
+// pointers are aligned host addresses that no call may dereference.  Calls with fully valid
+// arguments are made only when no GPU is visible, where they must return CR_ERR_NO_DEVICE.
+// Exit status 1 names the first unexpected status.
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -135,7 +135,16 @@ int main()
     expect("layer null workspace", lin(300, 1000, 5376, CR_BF16, need, nullptr), CR_ERR_INVALID_ARG);
     expect("layer empty", lin(0, 1000, 5376, CR_BF16, 0, nullptr), CR_OK);
     expect("layer K too large", lin(300, 1000, BIG, CR_BF16, need, P()), CR_ERR_TOO_LARGE);
+    auto na = [&](int64_t M, int64_t N, int64_t K, size_t mt) {
+        return cr_linear_nvfp4_noalloc(P(), CR_BF16, 5376, 0, M, K, nullptr, Q<uint8_t>(), 2688, Q<uint8_t>(), 336,
+                                       Q<float>(), N, nullptr, P(), CR_BF16, 21504, mt, 0, nullptr);
+    };
+    expect("noalloc activation beyond the scratch", na(19989, 21504, 5376, 0), CR_ERR_TOO_LARGE);
+    expect("noalloc tiles beyond the scratch", na(4096, 21504, 5376, (size_t)64 << 20), CR_ERR_TOO_LARGE);
+    expect("noalloc empty", na(0, 21504, 5376, 0), CR_OK);
+    expect("noalloc negative", na(-1, 21504, 5376, 0), CR_ERR_INVALID_ARG);
     if (ndev == 0) {
+        expect("noalloc without a device", na(4096, 21504, 5376, 0), CR_ERR_NO_DEVICE);
         expect("layer without a device", lin(300, 1000, 5376, CR_BF16, need, P()), CR_ERR_NO_DEVICE);
         expect("qa without a device", qa(P(), 0, 512, 4, 512, P(), 512, P(), 0), CR_ERR_NO_DEVICE);
     }

@@ -4,7 +4,7 @@
    UndefinedBehaviorSanitizer (plus float-cast-overflow and float-divide-by-zero) and driven
    through every entry point on exactly-sized buffers (tests/native/oracle_sanitize.c).
 2. The host side of the C ABI (rotated_bit_linear_amd/csrc/api.cpp: validation, planner,
-   workspace sizes, the event pool) compiled host-only by hipcc with the same sanitizers,
+   workspace sizes, the event pool) compiled by hipcc with the same sanitizers on its host side,
    linked against the library's kernel objects, and driven with rejected arguments and
    empty extents (tests/native/abi_sanitize.cpp); no kernel is launched.
 """
@@ -42,12 +42,14 @@ def test_c_abi_host_side_under_asan_ubsan(tmp_path):
     from rotated_bit_linear_amd import build as hip_build
     kernel_objs = hip_build.kernel_objects()
     inc = os.path.join(ROOT, "include")
-    # host-only compiles: no device code, every -fsanitize= applies to the host side only
-    host = ["-x", "hip", "--offload-host-only", "-O1", "-g", "-std=c++17", "-fPIC",
-            "-Xarch_host", f"-fsanitize={SAN}", "-Xarch_host", "-fno-sanitize-recover=all", "-I", inc]
+    # every -fsanitize= applies to the host side only (-Xarch_host); api.cpp keeps its device
+    # part (the allocation-free entry point's scratch array), the driver has none
+    san = ["-O1", "-g", "-std=c++17", "-fPIC", "-Xarch_host", f"-fsanitize={SAN}", "-Xarch_host",
+           "-fno-sanitize-recover=all", "-I", inc]
     api_o, drv_o, exe = (str(tmp_path / n) for n in ("api.o", "drv.o", "abi_sanitize"))
-    _run([HIPCC, *host, "-c", os.path.join(ROOT, "rotated_bit_linear_amd", "csrc", "api.cpp"), "-o", api_o])
-    _run([HIPCC, *host, "-c", os.path.join(NATIVE, "abi_sanitize.cpp"), "-o", drv_o])
+    _run([HIPCC, "-x", "hip", "--offload-arch=gfx950", *san, "-c",
+          os.path.join(ROOT, "rotated_bit_linear_amd", "csrc", "api.cpp"), "-o", api_o])
+    _run([HIPCC, "-x", "hip", "--offload-host-only", *san, "-c", os.path.join(NATIVE, "abi_sanitize.cpp"), "-o", drv_o])
     _run([CLANGXX, f"-fsanitize={SAN}", drv_o, api_o, *kernel_objs, "-L/opt/rocm/lib", "-lamdhip64",
           "-Wl,-rpath,/opt/rocm/lib", "-o", exe])
     r = _run([exe], env=ENV, timeout=300)
