@@ -34,6 +34,14 @@ def _block_transposed(codes: np.ndarray) -> np.ndarray:
 CASES = [(300, 999, 0.0137), (264, 20000, 1.0 / 3.0), (270, 4111, 7.1e-37)]
 
 
+def _x(M, K, seed, scale):
+    """bf16 X [M, ld] with a 16-byte row stride ld and garbage in the columns past K."""
+    ld = (K + 7) // 8 * 8 + 8
+    full = torch.randn(M, ld, generator=torch.Generator().manual_seed(seed)) * scale
+    full[:, K:] = 3e4
+    return full.to(torch.bfloat16)
+
+
 def _weight(N, K, g):
     nb = (K + 15) // 16
     return synth.raw_nvfp4(N, K, seed=N + K, ld_codes=(K + 1) // 2 // 16 * 16 + 48, ld_sf=nb + 7, g=g)
@@ -70,12 +78,12 @@ def test_raw_bytes_fused_gemm_int32(N, K, g):
     cd, sfd = p.codes.to(dev()), p.sf.to(dev())
     gs = torch.tensor([p.g], dtype=torch.float32, device=dev())
     M = 37
-    x = (torch.randn(M, K, generator=torch.Generator().manual_seed(K)) * 3).to(torch.bfloat16)
-    rq, rs = oracle.quant_act(synth.bits_u16(x), synth.DT_BF16, K)
+    xf = _x(M, K, K, 3.0)
+    rq, rs = oracle.quant_act(synth.bits_u16(xf), synth.DT_BF16, K)
     rqw, _ = oracle.prep_weight_nvfp4(p.codes.numpy(), p.sf.numpy(), p.g, K)
     racc = oracle.gemm_s8(rq, rqw)
     bt = rbl.CR_FLAG_BLOCK_TRANSPOSED
-    qx, sx = rbl.quant_act(x.to(dev()), K, flags=bt)
+    qx, sx = rbl.quant_act(xf.to(dev())[:, :K], K, flags=bt)
     amax = rbl.weight_amax_nvfp4(cd, sfd, gs, K)
     for am in (amax, None):
         say(f"raw NVFP4 bytes: cr_gemm_nvfp4_fused int32 M={M} N={N} K={K} "
@@ -94,13 +102,13 @@ def test_raw_bytes_layer_both_paths(M):
     p = _weight(N, K, g)
     cd, sfd = p.codes.to(dev()), p.sf.to(dev())
     gs = torch.tensor([p.g], dtype=torch.float32, device=dev())
-    x = (torch.randn(M, K, generator=torch.Generator().manual_seed(M)) * 2).to(torch.bfloat16)
-    x[3] = 0.0
-    xd = x.to(dev())
+    xf = _x(M, K, M, 2.0)
+    xf[3, :K] = 0.0
+    xd = xf.to(dev())[:, :K]
     aux = torch.cuda.Stream()
     assert (rbl.cr_linear_nvfp4_plan(M, N, K)[1] == 0) == (M <= 64)   # no chunks: decode inside the GEMM
     for odt in (synth.DT_FP32, synth.DT_BF16):
-        ref = oracle.linear_nvfp4(synth.bits_u16(x), synth.DT_BF16, K, False, p.codes.numpy(), p.sf.numpy(),
+        ref = oracle.linear_nvfp4(synth.bits_u16(xf), synth.DT_BF16, K, False, p.codes.numpy(), p.sf.numpy(),
                                   p.g, odt)
         runs = [(0, None), (256 * 1024, None), (256 * 1024, aux)] if M > 64 else [(0, None), (0, aux)]
         for mt, st in runs:
