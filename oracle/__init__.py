@@ -55,6 +55,13 @@ def lib():
                                           f32, i64, vp, C.c_int, i64]),
             "or_linear_nvfp4_ex": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, vp, i64, vp, i64,
                                              f32, i64, vp, vp, C.c_int, i64]),
+            "or_row_quant_s4": (None, [vp, i64, i64, i64, vp, i64, vp]),
+            "or_pack_s4": (None, [vp, i64, i64, i64, vp, i64]),
+            "or_unpack_s4": (None, [vp, i64, i64, i64, vp, i64]),
+            "or_quant_weight_w4": (C.c_int, [vp, C.c_int, i64, i64, i64, vp, i64, vp]),
+            "or_gemm_s8s4": (C.c_int, [vp, i64, vp, i64, i64, i64, i64, vp, i64]),
+            "or_linear_w4a8": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, i64, vp, i64, vp, vp,
+                                         C.c_int, i64]),
             "or_exp_array": (None, [vp, vp, i64]),
             "or_sigmoid_array": (None, [vp, vp, i64]),
             "or_swiglu_array": (None, [vp, vp, vp, i64]),
@@ -265,5 +272,75 @@ def linear_nvfp4(x: np.ndarray, x_dtype: int, K: int, swiglu: bool, codes: np.nd
     b, bp = _opt_f32(bias, N)
     rc = lib().or_linear_nvfp4_ex(_p(x), x_dtype, x.shape[1], int(swiglu), M, K, cp, _p(codes),
                                   codes.shape[1], _p(sf), sf.shape[1], g, N, bp, _p(out), out_dtype, N)
+    assert rc == 0
+    return out
+
+
+# ------------------------------------------------------------ W4A8 variant ----
+
+def row_quant_s4(y: np.ndarray):
+    """4-bit row quantization -> (codes [n, K_pad] int8 in -7..7, scales [n] fp32)."""
+    y = np.ascontiguousarray(y, np.float32)
+    n, kp = y.shape
+    q = np.empty((n, kp), np.int8)
+    s = np.empty(n, np.float32)
+    lib().or_row_quant_s4(_p(y), n, kp, kp, _p(q), kp, _p(s))
+    return q, s
+
+
+def pack_s4(q: np.ndarray) -> np.ndarray:
+    """codes [n, K_pad] (values -8..7) -> packed [n, K_pad / 2] bytes."""
+    q = np.ascontiguousarray(q, np.int8)
+    n, kp = q.shape
+    assert kp % 16 == 0
+    p = np.empty((n, kp // 2), np.uint8)
+    lib().or_pack_s4(_p(q), n, kp, kp, _p(p), kp // 2)
+    return p
+
+
+def unpack_s4(p: np.ndarray, K_pad: int) -> np.ndarray:
+    p = np.ascontiguousarray(p, np.uint8)
+    n = p.shape[0]
+    q = np.empty((n, K_pad), np.int8)
+    lib().or_unpack_s4(_p(p), n, K_pad, p.shape[1], _p(q), K_pad)
+    return q
+
+
+def quant_weight_w4(w: np.ndarray, dtype: int, K: int):
+    """Dense W [N, >=K] -> (packed 4-bit codes [N, K_pad / 2] uint8, scales [N] fp32)."""
+    w = np.ascontiguousarray(w, _elem_dtype(dtype))
+    n = w.shape[0]
+    kp = padded_k(K)
+    p = np.empty((n, kp // 2), np.uint8)
+    s = np.empty(n, np.float32)
+    rc = lib().or_quant_weight_w4(_p(w), dtype, w.shape[1], n, K, _p(p), kp // 2, _p(s))
+    assert rc == 0
+    return p, s
+
+
+def gemm_s8s4(a: np.ndarray, b_s4: np.ndarray) -> np.ndarray:
+    """int32 acc[M, N] = A[M, K_pad] . unpack(B)[N, K_pad]^T."""
+    a = np.ascontiguousarray(a, np.int8)
+    b_s4 = np.ascontiguousarray(b_s4, np.uint8)
+    M, kp = a.shape
+    N = b_s4.shape[0]
+    acc = np.empty((M, N), np.int32)
+    rc = lib().or_gemm_s8s4(_p(a), kp, _p(b_s4), b_s4.shape[1], M, N, kp, _p(acc), N)
+    assert rc == 0
+    return acc
+
+
+def linear_w4a8(x: np.ndarray, x_dtype: int, K: int, swiglu: bool, w_s4: np.ndarray, w_scale: np.ndarray,
+                out_dtype: int, bias=None) -> np.ndarray:
+    """The W4A8 layer on the rows of x against a prepared 4-bit weight."""
+    x = np.ascontiguousarray(x, _elem_dtype(x_dtype))
+    w_s4 = np.ascontiguousarray(w_s4, np.uint8)
+    w_scale = np.ascontiguousarray(w_scale, np.float32)
+    M, N = x.shape[0], w_s4.shape[0]
+    odt = {DT_BF16: np.uint16, DT_FP16: np.uint16, DT_FP32: np.float32, DT_I32: np.int32}[out_dtype]
+    out = np.empty((M, N), odt)
+    b, bp = _opt_f32(bias, N)
+    rc = lib().or_linear_w4a8(_p(x), x_dtype, x.shape[1], int(swiglu), M, K, _p(w_s4), w_s4.shape[1],
+                              _p(w_scale), N, bp, _p(out), out_dtype, N)
     assert rc == 0
     return out

@@ -489,6 +489,140 @@ int or_linear_nvfp4(const void *x, int x_dtype, int64_t ld_x, int swiglu, int64_
                               g, N, NULL, out, out_dtype, ldc);
 }
 
+/* ------------------------------------------------ W4A8 variant (4-bit weights) ---- */
+
+/* ComfyUI Turing Utils README: the ConvRot path supports W8A8, W4A8 and W4A4 dispatch and
+ * ships a packed W4A8 kernel (opening paragraph; section "Nodes", bullet "Load ConvRot
+ * DiT"; section "Turing behavior").  The pages name these formats but do not describe
+ * them.  Reading taken: the W8A8 method with 4-bit weights.  The weight is rotated by the
+ * same ConvRot256 and each row is quantized symmetrically to the 15 levels -7..7 with one
+ * FP32 scale (a = max|y|, s = a/7, r = 7/a rounded to FP32, q = clamp(rint(y*r), -7, 7));
+ * activations are prepared exactly as for W8A8; the GEMM accumulates int8 x int4 products
+ * in int32; the epilogue is the W8A8 one. */
+
+/* 4-bit row quantization: the rule of or_row_quant with 7 levels.  A row whose 7/a
+ * overflows FP32 (a below about 2e-38) is quantized as its copy multiplied by 2^64, as
+ * for the 8-bit codes. */
+void or_row_quant_s4(const float *y, int64_t n_rows, int64_t K_pad, int64_t ld_y,
+                     int8_t *q, int64_t ld_q, float *s)
+{
+#pragma omp parallel for
+    for (int64_t n = 0; n < n_rows; n++) {
+        const float *row = y + n * ld_y;
+        float a = 0.0f;
+        for (int64_t k = 0; k < K_pad; k++) {
+            float m = fabsf(row[k]);
+            if (m > a) a = m;
+        }
+        if (a == 0.0f) {
+            s[n] = 0.0f;
+            for (int64_t k = 0; k < K_pad; k++) q[n * ld_q + k] = 0;
+            continue;
+        }
+        s[n] = a / 7.0f;
+        const float up = isinf(7.0f / a) ? 0x1p64f : 1.0f;
+        float r = 7.0f / (a * up);
+        for (int64_t k = 0; k < K_pad; k++) {
+            float t = rintf((row[k] * up) * r);
+            if (t > 7.0f) t = 7.0f;
+            if (t < -7.0f) t = -7.0f;
+            q[n * ld_q + k] = (int8_t)t;
+        }
+    }
+}
+
+/* The packed int4 format (this library's own; the pages print none): two's complement
+ * nibbles, 8 bytes per group of 16 consecutive codes c[0..15] of a row.  Byte j (j = 0..3)
+ * holds c[j] in its low nibble and c[4 + j] in its high nibble; byte 4 + j holds c[8 + j]
+ * and c[12 + j].  Row n starts at byte n * ld_p; a row of K_pad codes takes K_pad / 2
+ * bytes. */
+void or_pack_s4(const int8_t *q, int64_t n_rows, int64_t K_pad, int64_t ld_q, uint8_t *p, int64_t ld_p)
+{
+    for (int64_t n = 0; n < n_rows; n++)
+        for (int64_t g = 0; g < K_pad / 16; g++) {
+            const int8_t *c = q + n * ld_q + 16 * g;
+            uint8_t *b = p + n * ld_p + 8 * g;
+            for (int j = 0; j < 4; j++) {
+                b[j] = (uint8_t)((c[j] & 15) | ((c[4 + j] & 15) << 4));
+                b[4 + j] = (uint8_t)((c[8 + j] & 15) | ((c[12 + j] & 15) << 4));
+            }
+        }
+}
+
+static int8_t nibble_value(uint8_t u) { return (int8_t)(u < 8 ? u : (int)u - 16); }
+
+/* The inverse of or_pack_s4: codes -8..7 from the nibbles. */
+void or_unpack_s4(const uint8_t *p, int64_t n_rows, int64_t K_pad, int64_t ld_p, int8_t *q, int64_t ld_q)
+{
+    for (int64_t n = 0; n < n_rows; n++)
+        for (int64_t g = 0; g < K_pad / 16; g++) {
+            const uint8_t *b = p + n * ld_p + 8 * g;
+            int8_t *c = q + n * ld_q + 16 * g;
+            for (int j = 0; j < 4; j++) {
+                c[j] = nibble_value(b[j] & 15);
+                c[4 + j] = nibble_value(b[j] >> 4);
+                c[8 + j] = nibble_value(b[4 + j] & 15);
+                c[12 + j] = nibble_value(b[4 + j] >> 4);
+            }
+        }
+}
+
+/* W4A8 weight preparation from a dense weight W [N, K] (bf16/fp16/fp32, row stride ld_w):
+ * zero padding to K_pad, ConvRot256, 4-bit row quantization, packing.  Out: w_s4
+ * [N, ld_s4 bytes] (ld_s4 >= K_pad / 2), w_scale [N].  Returns 0, or -1 on allocation
+ * failure. */
+int or_quant_weight_w4(const void *w, int dtype, int64_t ld_w, int64_t N, int64_t K,
+                       uint8_t *w_s4, int64_t ld_s4, float *w_scale)
+{
+    int64_t kp = or_padded_k(K);
+    float *buf = (float *)malloc(sizeof(float) * (size_t)(N > 0 ? N : 1) * (size_t)kp);
+    int8_t *q = (int8_t *)malloc((size_t)(N > 0 ? N : 1) * (size_t)kp);
+    int rc = -1;
+    if (buf && q) {
+        or_act_load(w, dtype, ld_w, N, K, buf, kp);
+        or_convrot256(buf, N, kp, kp);
+        or_row_quant_s4(buf, N, kp, kp, q, kp, w_scale);
+        or_pack_s4(q, N, kp, kp, w_s4, ld_s4);
+        rc = 0;
+    }
+    free(buf);
+    free(q);
+    return rc;
+}
+
+/* acc[m, n] = sum_k A[m, k] * Wq[n, k], Wq the unpacked 4-bit codes of B [N, ldb bytes]. */
+int or_gemm_s8s4(const int8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                 int64_t M, int64_t N, int64_t K_pad, int32_t *acc, int64_t ldc)
+{
+    int8_t *bq = (int8_t *)malloc((size_t)(N > 0 ? N : 1) * (size_t)K_pad);
+    if (!bq) return -1;
+    or_unpack_s4(B, N, K_pad, ldb, bq, K_pad);
+    or_gemm_s8(A, lda, bq, K_pad, M, N, K_pad, acc, ldc);
+    free(bq);
+    return 0;
+}
+
+/* The W4A8 layer: activation preparation (as for W8A8, optional SwiGLU), the int8 x int4
+ * GEMM against the prepared weight, the row-scale epilogue (+ optional bias [N]).
+ * Returns 0, or -1 on allocation failure. */
+int or_linear_w4a8(const void *x, int x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
+                   const uint8_t *w_s4, int64_t ld_s4, const float *w_scale, int64_t N,
+                   const float *bias, void *out, int out_dtype, int64_t ldc)
+{
+    int64_t kp = or_padded_k(K);
+    int8_t *xq = (int8_t *)malloc((size_t)(M > 0 ? M : 1) * (size_t)kp);
+    float *xs = (float *)malloc(sizeof(float) * (size_t)(M > 0 ? M : 1));
+    int32_t *acc = (int32_t *)malloc(sizeof(int32_t) * (size_t)(M > 0 ? M : 1) * (size_t)(N > 0 ? N : 1));
+    int rc = -1;
+    if (xq && xs && acc && or_quant_act_ex(x, x_dtype, ld_x, swiglu, M, K, NULL, xq, kp, xs) == 0 &&
+        or_gemm_s8s4(xq, kp, w_s4, ld_s4, M, N, kp, acc, N) == 0) {
+        or_epilogue_ex(acc, N, xs, w_scale, bias, M, N, out_dtype, out, ldc);
+        rc = 0;
+    }
+    free(xq); free(xs); free(acc);
+    return rc;
+}
+
 /* ----------------------------------------------- elementwise array helpers ---- */
 /* Thin loops so the tests can sweep whole code spaces without one foreign call per value. */
 
