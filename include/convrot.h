@@ -267,6 +267,58 @@ cr_status cr_linear_nvfp4_ex(const void *x, cr_dtype x_dtype, int64_t ld_x, int 
                              uint32_t flags, hipStream_t s_main, hipStream_t s_aux);
 
 /*
+ * W4A8 variant: 4-bit weights, 8-bit activations (ComfyUI Turing Utils README, opening
+ * paragraph and section "Nodes", bullet "Load ConvRot DiT": the ConvRot path dispatches
+ * W8A8, W4A8 and W4A4 layers; section "Turing behavior": a packed W4A8 kernel).  The pages
+ * name the format but do not describe it; this library reads it as the W8A8 method with
+ * 4-bit weight rows: ConvRot256 as above, then per weight row a = max |y|, scale = a / 7,
+ * r = 7 / a (rounded to FP32), q = clamp(rint(y * r), -7, 7), the 2^64 extension for rows
+ * whose 7 / a overflows; activations as for W8A8; int32 accumulation; the same epilogue.
+ *
+ * Packed 4-bit codes (this library's format): a row of K_pad codes takes K_pad / 2 bytes
+ * in units of 32 bytes per 64 codes.  A unit's groups of 16 codes G0 (codes 0..15), G1,
+ * G2, G3 are stored in the order G0, G2, G1, G3, 8 bytes each; a group's codes c[0..15]
+ * are two's complement nibbles, byte j (j = 0..3) holding c[j] (low nibble) and c[4 + j]
+ * (high nibble), byte 4 + j holding c[8 + j] and c[12 + j].  The codes follow the column
+ * order of the flags (natural, or block-transposed with CR_FLAG_BLOCK_TRANSPOSED).
+ *
+ * Weight preparation (done once, offline: the packed codes and scales are what a W4A8
+ * checkpoint stores):
+ *   w          [N, ld_w] of w_dtype (CR_BF16, CR_FP16 or CR_FP32), the dense weight;
+ *              ld_w >= K, rows of 16-byte multiples, 16-byte aligned.
+ *   w_s4       [N, ld_s4] bytes out, ld_s4 >= K_pad / 2, a multiple of 16.
+ *   w_scale    [N] float out (a / 7).
+ *   flags      CR_FLAG_NONE, CR_FLAG_FORCE_TWO_PASS and/or CR_FLAG_BLOCK_TRANSPOSED.
+ */
+cr_status cr_quant_weight_w4(const void *w, cr_dtype w_dtype, int64_t ld_w, int64_t N, int64_t K,
+                             uint8_t *w_s4, int64_t ld_s4, float *w_scale, uint32_t flags, hipStream_t stream);
+
+/*
+ * W4A8 GEMM: out = ((float)sum_k a_s8[m, k] q[n, k] * a_scale[m]) * b_scale[n] (+ bias[n]),
+ * q the codes of the packed weight b_s4 [N, ldb bytes] (ldb >= K_pad / 2, a multiple of
+ * 16).  The other arguments, the limits and CR_I32 as in cr_gemm_s8_rowscale_bias; both
+ * operands must use the same column order.
+ */
+cr_status cr_gemm_s8s4_rowscale(const int8_t *a_s8, int64_t lda, const float *a_scale,
+                                const uint8_t *b_s4, int64_t ldb, const float *b_scale, const float *bias,
+                                int64_t M, int64_t N, int64_t K_pad, void *c, cr_dtype c_dtype, int64_t ldc,
+                                hipStream_t stream);
+
+/*
+ * The W4A8 layer: activation preparation of X [M, K] (or of SwiGLU(H [M, 2K]) when swiglu
+ * != 0) into the workspace, then cr_gemm_s8s4_rowscale against the prepared weight, both on
+ * `stream`.  flags: CR_FLAG_BLOCK_TRANSPOSED when the weight's codes are in that order (the
+ * activation is then prepared in the same order), CR_FLAG_FORCE_TWO_PASS.  workspace:
+ * cr_linear_w4a8_workspace_bytes(M, K) bytes, 256-byte aligned (S8 activation and its
+ * scales); an empty layer (M or N = 0) needs none.  out [M, ldc] of out_dtype (not CR_I32).
+ */
+size_t cr_linear_w4a8_workspace_bytes(int64_t M, int64_t K);
+cr_status cr_linear_w4a8(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
+                         const uint8_t *w_s4, int64_t ld_s4, const float *w_scale, int64_t N, const float *bias,
+                         void *out, cr_dtype out_dtype, int64_t ldc, void *workspace, size_t ws_bytes,
+                         uint32_t flags, hipStream_t stream);
+
+/*
  * The layer for callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): cr_linear_nvfp4_ex with serial
  * staging on `stream` and, as its workspace, a device array of CR_NOALLOC_SCRATCH_BYTES

@@ -74,6 +74,11 @@ def lib() -> C.CDLL:
             "cr_linear_nvfp4_noalloc": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, vp, i64, vp, i64, vp,
                                                   i64, vp, vp, C.c_int, i64, sz, u32, vp]),
             "cr_weight_amax_nvfp4": (C.c_int, [vp, i64, vp, i64, vp, i64, i64, vp, u32, vp]),
+            "cr_quant_weight_w4": (C.c_int, [vp, C.c_int, i64, i64, i64, vp, i64, vp, u32, vp]),
+            "cr_gemm_s8s4_rowscale": (C.c_int, [vp, i64, vp, vp, i64, vp, vp, i64, i64, i64, vp, C.c_int, i64, vp]),
+            "cr_linear_w4a8_workspace_bytes": (sz, [i64, i64]),
+            "cr_linear_w4a8": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, i64, vp, i64, vp, vp, C.c_int,
+                                         i64, vp, sz, u32, vp]),
             "cr_gemm_nvfp4_fused": (C.c_int, [vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, i64, i64, i64, vp,
                                               C.c_int, i64, u32, vp]),
         }
@@ -251,6 +256,36 @@ def cr_gemm_nvfp4_fused(a_s8, a_scale, w_fp4, w_sf, global_scale, w_amax, K, c, 
         _ptr(w_amax), _ptr(bias), M, N, K, _ptr(c), _TORCH_TO_CR[c.dtype], ldc, flags, _stream(stream)))
 
 
+def cr_quant_weight_w4(w, K, w_s4, w_scale, flags=0, stream=None):
+    N, ld_w = _rows_ld(w)
+    _, ld_s4 = _rows_ld(w_s4)
+    _check("cr_quant_weight_w4", lib().cr_quant_weight_w4(
+        _ptr(w), _TORCH_TO_CR[w.dtype], ld_w, N, K, _ptr(w_s4), ld_s4, _ptr(w_scale), flags, _stream(stream)))
+
+
+def cr_gemm_s8s4_rowscale(a_s8, a_scale, b_s4, b_scale, c, bias=None, stream=None):
+    M, lda = _rows_ld(a_s8)
+    N, ldb = _rows_ld(b_s4)
+    _, ldc = _rows_ld(c)
+    _check("cr_gemm_s8s4_rowscale", lib().cr_gemm_s8s4_rowscale(
+        _ptr(a_s8), lda, _ptr(a_scale), _ptr(b_s4), ldb, _ptr(b_scale), _ptr(bias), M, N, a_s8.shape[1],
+        _ptr(c), _TORCH_TO_CR[c.dtype], ldc, _stream(stream)))
+
+
+def cr_linear_w4a8_workspace_bytes(M, K) -> int:
+    return int(lib().cr_linear_w4a8_workspace_bytes(M, K))
+
+
+def cr_linear_w4a8(x, K, swiglu, w_s4, w_scale, out, workspace, bias=None, flags=0, stream=None):
+    M, ld_x = _rows_ld(x)
+    N, ld_s4 = _rows_ld(w_s4)
+    _, ldc = _rows_ld(out)
+    _check("cr_linear_w4a8", lib().cr_linear_w4a8(
+        _ptr(x), _TORCH_TO_CR[x.dtype], ld_x, int(bool(swiglu)), M, K, _ptr(w_s4), ld_s4, _ptr(w_scale), N,
+        _ptr(bias), _ptr(out), _TORCH_TO_CR[out.dtype], ldc, _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), flags, _stream(stream)))
+
+
 # ---------------------------------------------------------------- conveniences ----
 
 def quant_act(x: torch.Tensor, K: int | None = None, swiglu: bool = False, flags: int = 0,
@@ -315,3 +350,24 @@ def gemm_nvfp4_fused(a_s8, a_scale, w_fp4, w_sf, global_scale, w_amax, K, out_dt
     c = torch.empty(a_s8.shape[0], w_fp4.shape[0], dtype=out_dtype, device=a_s8.device)
     cr_gemm_nvfp4_fused(a_s8, a_scale, w_fp4, w_sf, global_scale, w_amax, K, c, bias, flags)
     return c
+
+
+def quant_weight_w4(w: torch.Tensor, K: int | None = None, flags: int = 0):
+    """(packed 4-bit codes [N, K_pad / 2] uint8, scales [N] fp32) of a dense weight [N, K]."""
+    if K is None:
+        K = w.shape[1]
+    kp = padded_k(K)
+    q = torch.empty(w.shape[0], kp // 2, dtype=torch.uint8, device=w.device)
+    s = torch.empty(w.shape[0], dtype=torch.float32, device=w.device)
+    cr_quant_weight_w4(w, K, q, s, flags)
+    return q, s
+
+
+def linear_w4a8(x, w_s4, w_scale, K, out_dtype=torch.bfloat16, swiglu=False, bias=None, flags=0, out=None):
+    """y = x W^T (+ b) through the W4A8 route against a prepared 4-bit weight."""
+    M, N = x.shape[0], w_s4.shape[0]
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype, device=x.device)
+    ws = torch.empty(max(1, cr_linear_w4a8_workspace_bytes(M, K)), dtype=torch.uint8, device=x.device)
+    cr_linear_w4a8(x, K, swiglu, w_s4, w_scale, out, ws, bias=bias, flags=flags)
+    return out

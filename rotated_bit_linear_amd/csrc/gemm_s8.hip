@@ -23,12 +23,11 @@
 // working set for the whole chip (the XCDs form a 2 x 4 grid over a square chip block, so a
 // round of workgroups touches as few distinct operand bands as possible).
 #include <hip/hip_runtime.h>
-#include <hip/hip_bf16.h>
-#include <hip/hip_fp16.h>
 #include <stdint.h>
 
 #include <type_traits>
 
+#include "gemm_common.hpp"
 #include "kernels.hpp"
 
 #ifndef CONVROT_GEMM_WAVES_M
@@ -52,9 +51,12 @@
 
 namespace convrot {
 
-typedef int32_t v4i __attribute__((ext_vector_type(4)));
-typedef int32_t v16i __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+using gemm::v4i;
+using gemm::v16i;
+using gemm::waitcnt_vm;
+using gemm::waitcnt_lgkm0;
+using gemm::read_groups;
+using gemm::EPI_BYTES;
 
 constexpr int WAVES_M = CONVROT_GEMM_WAVES_M, WAVES_N = CONVROT_GEMM_WAVES_N;
 constexpr int WT_M = CONVROT_GEMM_WT_M, WT_N = CONVROT_GEMM_WT_N;
@@ -66,10 +68,6 @@ constexpr int GSTAGES = CONVROT_GEMM_STAGES;
 constexpr int KS = GBK / 32;                       // 32-deep MFMA slices per step
 constexpr int CPR = GBK / 16;                      // 16-byte chunks per LDS row
 constexpr int RPP = 1024 / GBK;                    // rows per 1 KB DMA piece
-constexpr int GROUP_M = 8;
-constexpr int NUM_XCD = 8;
-constexpr int XCD_M = 2, XCD_N = 4;              // the XCDs' grid over a chip block
-static_assert(XCD_M * XCD_N == NUM_XCD, "XCD grid");
 constexpr int STAGE_A = GBM * GBK, STAGE_B = GBN * GBK;
 constexpr int PIECES = (STAGE_A + STAGE_B) / 1024;  // 1 KB DMA pieces per stage
 constexpr int PPW = PIECES / GWAVES;                 // pieces per wave per stage
@@ -80,34 +78,8 @@ static_assert(GSTAGES * (STAGE_A + STAGE_B) <= 160 * 1024, "LDS ring exceeds 160
 static_assert(PPW * (GSTAGES - 1) <= 63, "vmcnt range");
 static_assert(KS % 2 == 0, "fragment register sets alternate per slice");
 
-constexpr int EPI_STRIDE = 272;                    // bytes per LDS row of the epilogue tile
-constexpr int EPI_BYTES = 32 * EPI_STRIDE;         // one 32-row x 256-byte tile per wave
-
-// s_waitcnt immediates (gfx9 encoding) waiting for vmcnt <= n only / lgkmcnt == 0 only.
-constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
-constexpr int waitcnt_lgkm0() { return 15 | (7 << 4) | (0 << 8) | (3 << 14); }
-
 // chunk swizzle of an LDS row: for 4 chunks, rows 0..7 (and 0..15 in pairs) get distinct
 // bank groups; for 8 chunks, rows 0..7 and the even/odd rows of 0..15 do.
-// scheduling groups "1 MFMA, then 2 LDS reads", repeated until NFR reads are placed
-template <int T, int NFR>
-__device__ __forceinline__ void read_groups()
-{
-    if constexpr (2 * T < NFR) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, (2 * T + 1 < NFR) ? 2 : 1, 0); // DS read
-        read_groups<T + 1, NFR>();
-    }
-}
-
-// orders LDS traffic between the lanes of one wave
-__device__ __forceinline__ void wave_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 __device__ __forceinline__ int gswz(int row)
 {
     if constexpr (CPR == 4) return ((row >> 1) ^ (row >> 2)) & 3;
@@ -137,47 +109,9 @@ void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__re
     int8_t *const stB[GSTAGES] = {lB0, lB1};
 #endif
 
-    // ---- tile id.  Workgroup pid runs on XCD pid % 8, as its idx-th workgroup there.
-    //      Chip blocks of (XCD_M XA) x (XCD_N XB) tiles: all XCDs work on the same block at
-    //      the same time (its operand bands are fetched once from HBM into the MALL and
-    //      shared), XCD x on the XA x XB sub-block at row x / XCD_N, column x % XCD_N of the
-    //      block (L2 reuse inside the XCD); blocks advance along N so consecutive blocks
-    //      share their A bands.  With 256 x 256 tiles the square 16 x 16 block reads 32
-    //      operand bands per round of 256 workgroups where a 64 x 4 block reads 68: with
-    //      K_pad = 14336 that is 117 MB instead of 250 MB, which the MALL can hold.  Tiles
-    //      outside whole blocks are split XCD-contiguously afterwards, in groups of GROUP_M
-    //      M-tiles. ----
-    const int pid = blockIdx.x;
-    const int xcd = pid % NUM_XCD, idx = pid / NUM_XCD;
-    int xa = 8;                                      // largest power of two <= 8 with XCD_M xa <= tiles_m
-    while (xa > 1 && XCD_M * xa > tiles_m) xa >>= 1;
-    const int xb = 32 / xa;
-    const int nbm = tiles_m / (XCD_M * xa), nbn = tiles_n / (XCD_N * xb);
-    const int main_per_xcd = nbm * nbn * xa * xb;
+    // ---- tile id: XCD-aware order (gemm::tile_of) ----
     int tm, tn;
-    if (idx < main_per_xcd) {
-        const int blk = idx / (xa * xb), j = idx % (xa * xb);
-        const int bm = blk / nbn, bn = blk % nbn;
-        tm = bm * (XCD_M * xa) + (xcd / XCD_N) * xa + j % xa;
-        tn = bn * (XCD_N * xb) + (xcd % XCD_N) * xb + j / xa;
-    } else {
-        const int trem = tiles_m * tiles_n - main_per_xcd * NUM_XCD;
-        const int rq = trem / NUM_XCD, rr = trem % NUM_XCD;
-        int r = ((xcd < rr) ? xcd * (rq + 1) : rr * (rq + 1) + (xcd - rr) * rq) + (idx - main_per_xcd);
-        const int mm = nbm * XCD_M * xa, nn = nbn * XCD_N * xb;
-        int h, w, bm0, bn0;
-        if (r < mm * (tiles_n - nn)) {              // right strip beside the blocks
-            h = mm; w = tiles_n - nn; bm0 = 0; bn0 = nn;
-        } else {                                    // bottom strip below them
-            r -= mm * (tiles_n - nn);
-            h = tiles_m - mm; w = tiles_n; bm0 = mm; bn0 = 0;
-        }
-        const int in_group = GROUP_M * w;
-        const int g = r / in_group;
-        const int gsize = min(h - g * GROUP_M, GROUP_M);
-        tm = bm0 + g * GROUP_M + (r % in_group) % gsize;
-        tn = bn0 + (r % in_group) / gsize;
-    }
+    gemm::tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * GBM, n0 = tn * GBN;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -299,11 +233,7 @@ void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__re
         else if (younger == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(PPW));
         else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     };
-    auto barrier = [&]() {
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-    };
+    auto barrier = [&]() { gemm::barrier(); };
 
     // Prologue: every stage is free; steps 0..STAGES-1 are issued, step 0 awaited.
     // In step k the DMAs issued so far cover steps 0..min(k+STAGES-1, nk-1), so before the
@@ -371,43 +301,12 @@ void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__re
         step(I1{}, kt, 0, false, true);
     }
 
-    // ---- epilogue through LDS: every wave owns EPI_BYTES of the (now idle) stage ring.
-    //      Per 32-row block i and per 256-byte column chunk, lanes write their dequantized
-    //      4-column runs to rows of a padded LDS tile, then read it back in 16-byte pieces,
-    //      so each global store instruction covers 4 rows x 256 contiguous bytes. ----
-    // all row and column scales this lane needs are requested at once, before the barrier,
-    // so their latency overlaps the last MFMAs: sav[i] for its row of block i, sbv[j][g]
-    // for the 4-column run n = 8g + 4(l/32) .. +3 of block j (16-byte loads when aligned)
+    // ---- epilogue through LDS: every wave owns EPI_BYTES of the (now idle) stage ring
+    //      (gemm::store_tile); the scales are requested before the barrier so their latency
+    //      overlaps the last MFMAs ----
     const int nbase = n0 + wn * WT_N;
-    float sav[FM];
-    float4 sbv[FN][4];
-    auto load4 = [&](const float *v, bool v16, int n) {
-        float4 r;
-        if (v16 && n + 4 <= N) {
-            r = *reinterpret_cast<const float4 *>(v + n);
-        } else {
-            r.x = (n < N) ? v[n] : 0.0f;
-            r.y = (n + 1 < N) ? v[n + 1] : 0.0f;
-            r.z = (n + 2 < N) ? v[n + 2] : 0.0f;
-            r.w = (n + 3 < N) ? v[n + 3] : 0.0f;
-        }
-        return r;
-    };
-    if constexpr (OUT != 3) {
-#pragma unroll
-        for (int i = 0; i < FM; i++) {
-            const int m = m0 + wm * WT_M + i * 32 + frow;
-            sav[i] = (m < M) ? sa[m] : 0.0f;
-        }
-        const bool sb16 = ((uintptr_t)sb % 16) == 0;
-#pragma unroll
-        for (int j = 0; j < FN; j++)
-#pragma unroll
-            for (int g = 0; g < 4; g++) {
-                const int n = nbase + j * 32 + 8 * g + 4 * fhalf;
-                sbv[j][g] = load4(sb, sb16, n);
-            }
-    }
+    gemm::EpiScales<FM, FN> esc;
+    gemm::load_scales<OUT, FM, FN>(esc, sa, sb, m0 + wm * WT_M, nbase, frow, fhalf, M, N);
     __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
     barrier();                                     // every wave is done with the ring
     // the tile's GBN bias values go through LDS (past the last wave's epilogue tile) rather
@@ -420,10 +319,6 @@ void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__re
         if (tid_ < GBN) bias_lds[tid_] = (n0 + tid_ < N) ? bias[n0 + tid_] : 0.0f;
         barrier();
     }
-    constexpr int ES = (OUT == 0 || OUT == 1) ? 2 : 4;
-    constexpr int NC = 256 / ES;                   // columns per chunk
-    constexpr int CHUNKS = WT_N / NC;
-    static_assert(WT_N % NC == 0, "wave tile width must be whole 256-byte chunks");
     static_assert(WPA * EPI_BYTES <= STAGE_A && WPA * EPI_BYTES <= STAGE_B, "epilogue tile fits the ring");
     int8_t *etile;
     switch (wave / WPA) {          // wave-uniform: a scalar branch
@@ -442,77 +337,11 @@ void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__re
 #endif
     }
     etile += (wave % WPA) * EPI_BYTES;
+    constexpr int ES = (OUT == 0 || OUT == 1) ? 2 : 4;
     const bool vec_ok = (((uintptr_t)C) % 16 == 0) && ((ldc * ES) % 16 == 0);
     const bool interior = vec_ok && m0 + GBM <= M && n0 + GBN <= N;   // uniform fast path
-#pragma unroll
-    for (int i = 0; i < FM; i++) {
-#pragma unroll
-        for (int c = 0; c < CHUNKS; c++) {
-#pragma unroll
-            for (int jj = 0; jj < NC / 32; jj++) {
-                const int j = c * (NC / 32) + jj;
-#pragma unroll
-                for (int g = 0; g < 4; g++) {
-                    const int nl = jj * 32 + 8 * g + 4 * fhalf;   // column inside the chunk
-                    int8_t *dst = etile + frow * EPI_STRIDE + nl * ES;
-                    const int32_t a0 = acc[i][j][4 * g], a1 = acc[i][j][4 * g + 1];
-                    const int32_t a2 = acc[i][j][4 * g + 2], a3 = acc[i][j][4 * g + 3];
-                    if constexpr (OUT == 3) {
-                        *reinterpret_cast<v4i *>(dst) = v4i{a0, a1, a2, a3};
-                    } else {
-                        const float4 s4 = sbv[j][g];
-                        float v0 = ((float)a0 * sav[i]) * s4.x, v1 = ((float)a1 * sav[i]) * s4.y;
-                        float v2 = ((float)a2 * sav[i]) * s4.z, v3 = ((float)a3 * sav[i]) * s4.w;
-                        if constexpr (BIAS) {
-                            const float4 b4 = *reinterpret_cast<const float4 *>(
-                                bias_lds + wn * WT_N + j * 32 + 8 * g + 4 * fhalf);
-                            v0 = v0 + b4.x; v1 = v1 + b4.y; v2 = v2 + b4.z; v3 = v3 + b4.w;
-                        }
-                        if constexpr (OUT == 2) {
-                            *reinterpret_cast<float4 *>(dst) = make_float4(v0, v1, v2, v3);
-                        } else if constexpr (OUT == 0) {
-                            const __hip_bfloat16 h[4] = {__float2bfloat16(v0), __float2bfloat16(v1),
-                                                         __float2bfloat16(v2), __float2bfloat16(v3)};
-                            *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(h);
-                        } else {
-                            const __half h[4] = {__float2half(v0), __float2half(v1), __float2half(v2),
-                                                 __float2half(v3)};
-                            *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(h);
-                        }
-                    }
-                }
-            }
-            wave_sync();
-            // 32 rows x 256 bytes = 512 pieces of 16 B, 8 per lane, 4 rows per instruction
-#pragma unroll
-            for (int t = 0; t < 8; t++) {
-                const int q = lane + 64 * t;
-                const int row = q >> 4, cc = q & 15;
-                const uint4 v = *reinterpret_cast<const uint4 *>(etile + row * EPI_STRIDE + cc * 16);
-                const int mg = m0 + wm * WT_M + i * 32 + row;
-                const int ng = nbase + c * NC + cc * (16 / ES);
-                int8_t *out = static_cast<int8_t *>(C) + ((int64_t)mg * ldc + ng) * ES;
-                if (interior) {
-                    // streaming store: the output is written once and must not evict the
-                    // operand tiles other workgroups are still reading from L2
-                    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(out));
-                } else if (mg < M) {
-                    if (vec_ok && ng + 16 / ES <= N) {
-                        __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(out));
-                    } else {
-                        const int8_t *vb = reinterpret_cast<const int8_t *>(&v);
-#pragma unroll
-                        for (int e = 0; e < 16 / ES; e++)
-                            if (ng + e < N) {
-                                if constexpr (ES == 2) reinterpret_cast<uint16_t *>(out)[e] = reinterpret_cast<const uint16_t *>(vb)[e];
-                                else reinterpret_cast<uint32_t *>(out)[e] = reinterpret_cast<const uint32_t *>(vb)[e];
-                            }
-                    }
-                }
-            }
-            wave_sync();
-        }
-    }
+    gemm::store_tile<OUT, BIAS, FM, FN, WT_N>(acc, esc, etile, bias_lds + wn * WT_N, C, ldc, m0 + wm * WT_M,
+                                              nbase, M, N, interior, vec_ok, lane);
 }
 
 template <int OUT, bool BIAS>

@@ -329,7 +329,8 @@ __global__ void swiglu_kernel(const typename Elem<DT>::T *__restrict__ h, int64_
     }
 }
 
-template <class Loader, int RB>
+// kBits: 8-bit codes, or packed 4-bit codes (the W4A8 weight rows)
+template <class Loader, int RB, int kBits = 8>
 __global__ __launch_bounds__(row_prep_max_threads<RB>()) void quant_act_kernel(Loader ld, int64_t n_rows, int nb, int8_t *__restrict__ out, int64_t ld_out,
                                  float *__restrict__ scale, int mode)
 {
@@ -337,11 +338,11 @@ __global__ __launch_bounds__(row_prep_max_threads<RB>()) void quant_act_kernel(L
         ld.sig_off = sigma_table_offset(row_prep_lds_bytes(blockDim.x));
         build_sigma_table(sigma_table_at(ld.sig_off));
     }
-    row_prep_kernel_body<Loader, RB>(ld, n_rows, nb, out, ld_out, scale, mode);
+    row_prep_kernel_body<Loader, RB, kBits>(ld, n_rows, nb, out, ld_out, scale, mode);
 }
 
 // Several short rows per workgroup (see row_prep_multi).
-template <class Loader>
+template <class Loader, int kBits = 8>
 __global__ __launch_bounds__(1024) void quant_act_multi_kernel(Loader ld, int64_t n_rows, int nb, int rpw,
                                                              int8_t *__restrict__ out, int64_t ld_out,
                                                              float *__restrict__ scale, int mode)
@@ -350,12 +351,12 @@ __global__ __launch_bounds__(1024) void quant_act_multi_kernel(Loader ld, int64_
         ld.sig_off = sigma_table_offset(row_prep_multi_lds_bytes(blockDim.x));
         build_sigma_table(sigma_table_at(ld.sig_off));
     }
-    row_prep_multi(ld, n_rows, nb, rpw, out, ld_out, scale, (mode & 2) == 0, false);
+    row_prep_multi<Loader, kBits>(ld, n_rows, nb, rpw, out, ld_out, scale, (mode & 2) == 0, false);
 }
 
 // --------------------------------------------------------------------- launchers ----
 
-template <class Loader>
+template <class Loader, int kBits = 8>
 static hipError_t launch_rows(const Loader &L, int64_t rows, int64_t nb, int8_t *out, int64_t ld_out,
                               float *scale, bool force_two_pass, bool transposed, hipStream_t st,
                               int one_pass_groups = kMaxGroups2)
@@ -375,21 +376,21 @@ static hipError_t launch_rows(const Loader &L, int64_t rows, int64_t nb, int8_t 
         const int threads = (int)((rpw * nb + 3) / 4 * 64);
         const size_t mlds = row_prep_multi_lds_bytes(threads) + extra;
         const RowPrepShape ms{threads, 1, false};
-        const void *k = reinterpret_cast<const void *>(&quant_act_multi_kernel<Loader>);
+        const void *k = reinterpret_cast<const void *>(&quant_act_multi_kernel<Loader, kBits>);
         const dim3 grid((unsigned)row_prep_grid((rows + rpw - 1) / rpw, ms, k, mlds));
-        hipLaunchKernelGGL((quant_act_multi_kernel<Loader>), grid, dim3(threads), mlds, st, L, rows, (int)nb, rpw,
-                           out, ld_out, scale, mode);
+        hipLaunchKernelGGL((quant_act_multi_kernel<Loader, kBits>), grid, dim3(threads), mlds, st, L, rows, (int)nb,
+                           rpw, out, ld_out, scale, mode);
         return hipGetLastError();
     }
     if (s.rb == 2) {
-        const void *k = reinterpret_cast<const void *>(&quant_act_kernel<Loader, 2>);
+        const void *k = reinterpret_cast<const void *>(&quant_act_kernel<Loader, 2, kBits>);
         const dim3 grid((unsigned)row_prep_grid(rows, s, k, lds));
-        hipLaunchKernelGGL((quant_act_kernel<Loader, 2>), grid, dim3(s.threads), lds, st,
+        hipLaunchKernelGGL((quant_act_kernel<Loader, 2, kBits>), grid, dim3(s.threads), lds, st,
                            L, rows, (int)nb, out, ld_out, scale, mode);
     } else {
-        const void *k = reinterpret_cast<const void *>(&quant_act_kernel<Loader, 1>);
+        const void *k = reinterpret_cast<const void *>(&quant_act_kernel<Loader, 1, kBits>);
         const dim3 grid((unsigned)row_prep_grid(rows, gs, k, lds));
-        hipLaunchKernelGGL((quant_act_kernel<Loader, 1>), grid, dim3(s.threads), lds, st,
+        hipLaunchKernelGGL((quant_act_kernel<Loader, 1, kBits>), grid, dim3(s.threads), lds, st,
                            L, rows, (int)nb, out, ld_out, scale, mode);
     }
     return hipGetLastError();
@@ -432,6 +433,32 @@ hipError_t launch_quant_act(const void *x, int dtype, int64_t ld_x, int64_t M, i
     case 0: return launch_act<0>(x, ld_x, M, K, pre, x_s8, ld_s8, x_scale, two_pass, transposed, st);
     case 1: return launch_act<1>(x, ld_x, M, K, pre, x_s8, ld_s8, x_scale, two_pass, transposed, st);
     case 2: return launch_act<2>(x, ld_x, M, K, pre, x_s8, ld_s8, x_scale, two_pass, transposed, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// W4A8 weight preparation from dense rows (the activation loader, no pre-scale): ConvRot256,
+// 4-bit row quantization, packed codes (ComfyUI Turing Utils README: W4A8 dispatch; the
+// packed format is this library's, the pages describe none)
+template <int DT>
+static hipError_t launch_w4(const void *w, int64_t ld_w, int64_t N, int64_t K, uint8_t *w_s4, int64_t ld_s4,
+                            float *w_scale, bool two_pass, bool transposed, hipStream_t st)
+{
+    const auto *wp = static_cast<const typename Elem<DT>::T *>(w);
+    const bool aligned = ((uintptr_t)w % 16 == 0) && ((ld_w * (int64_t)sizeof(typename Elem<DT>::T)) % 16 == 0);
+    const int64_t nb = (K + 255) / 256;
+    return launch_rows<ActLoader<DT, false>, 4>(ActLoader<DT, false>{wp, ld_w, K, aligned, nullptr}, N, nb,
+                                                reinterpret_cast<int8_t *>(w_s4), ld_s4, w_scale, two_pass,
+                                                transposed, st);
+}
+
+hipError_t launch_quant_weight_w4(const void *w, int dtype, int64_t ld_w, int64_t N, int64_t K, uint8_t *w_s4,
+                                  int64_t ld_s4, float *w_scale, bool two_pass, bool transposed, hipStream_t st)
+{
+    switch (dtype) {
+    case 0: return launch_w4<0>(w, ld_w, N, K, w_s4, ld_s4, w_scale, two_pass, transposed, st);
+    case 1: return launch_w4<1>(w, ld_w, N, K, w_s4, ld_s4, w_scale, two_pass, transposed, st);
+    case 2: return launch_w4<2>(w, ld_w, N, K, w_s4, ld_s4, w_scale, two_pass, transposed, st);
     default: return hipErrorInvalidValue;
     }
 }

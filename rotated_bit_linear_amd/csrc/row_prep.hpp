@@ -36,6 +36,11 @@
 // holds element 16j + t.  The same codes, in another column order; a GEMM over two
 // operands stored in the same order gives the same int32 sums.
 //
+// 4-bit codes (the W4A8 weight rows) follow the same rule with L = 7 levels in place of
+// 127 (s = a / 7, r = 7 / a, no clamp evaluated: |y * r| <= 7 (1 + 2^-24)); everything said
+// above holds with 127 replaced by 7.  They are packed two per byte (quantize_store16_s4,
+// code_offset).
+//
 // Rows whose K_pad exceeds 64 blocks (16384 columns), or when forced, are streamed twice:
 // pass 1 rotates every block to find the row maximum, pass 2 reloads, rotates again and
 // quantizes (same operations, so the same bits).
@@ -222,30 +227,73 @@ __device__ __forceinline__ void quantize_store16(const float (&z)[16], float m, 
     *reinterpret_cast<uint4 *>(dst) = o;
 }
 
-// Row constants from a' = max |z|: the scale a / 127 and the code multiplier.
+// The same for 4-bit codes (levels -7..7): the 16 codes packed into 8 bytes, byte j
+// (j = 0..3) holding codes j and 4 + j and byte 4 + j codes 8 + j and 12 + j, low nibble
+// first, two's complement.  With |y| <= a and r = RN(7 / a), |y * r| <= 7 (1 + 2^-24), so
+// here too rint stays in range and no clamp is evaluated.
+template <bool kScaleFirst>
+__device__ __forceinline__ void quantize_store16_s4(const float (&z)[16], float m, int8_t *dst)
+{
+    uint32_t c[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const float y = kScaleFirst ? (z[i] * 0.0625f) * 0x1p64f : z[i];
+        c[i] = code_bits(y * m);
+    }
+    const uint32_t p0 = pack_low_bytes(c[0], c[1], c[2], c[3]);
+    const uint32_t p1 = pack_low_bytes(c[4], c[5], c[6], c[7]);
+    const uint32_t p2 = pack_low_bytes(c[8], c[9], c[10], c[11]);
+    const uint32_t p3 = pack_low_bytes(c[12], c[13], c[14], c[15]);
+    uint2 o;
+    o.x = (p0 & 0x0F0F0F0Fu) | ((p1 & 0x0F0F0F0Fu) << 4);
+    o.y = (p2 & 0x0F0F0F0Fu) | ((p3 & 0x0F0F0F0Fu) << 4);
+    *reinterpret_cast<uint2 *>(dst) = o;
+}
+
+// Row constants from a' = max |z|: the scale a / L and the code multiplier, for codes of
+// L = 127 (8-bit) or L = 7 (4-bit) levels on each side of zero.
 struct RowQuant {
-    float scale;    // a / 127 (0 when a == 0)
-    float mult;     // r * 0.0625 (folded) or 127 / (a * 2^64) (scale first); 0 when a == 0
+    float scale;    // a / L (0 when a == 0)
+    float mult;     // r * 0.0625 (folded) or L / (a * 2^64) (scale first); 0 when a == 0
     bool folded;    // block-uniform
 };
 
 // A zero row (a == 0: every z is 0) takes the scale-first branch with multiplier 0, so
-// every product is exactly 0 and every code 0; 127 / 0 is never formed.
+// every product is exactly 0 and every code 0; L / 0 is never formed.
+template <int kBits = 8>
 __device__ __forceinline__ RowQuant row_quant(float zmax)
 {
+    constexpr float L = kBits == 8 ? 127.0f : 7.0f;
     const float a = zmax * 0.0625f;
     const bool zero = (a == 0.0f);
     RowQuant q;
-    q.scale = zero ? 0.0f : a / 127.0f;
+    q.scale = zero ? 0.0f : a / L;
     q.folded = zmax >= 0x1p-100f;
-    q.mult = q.folded ? (127.0f / a) * 0.0625f : (zero ? 0.0f : 127.0f / (a * 0x1p64f));
+    q.mult = q.folded ? (L / a) * 0.0625f : (zero ? 0.0f : L / (a * 0x1p64f));
     return q;
 }
 
+// Byte offset of the codes of 16-lane group member t in block b of a row: 16 bytes per
+// lane for 8-bit codes; for packed 4-bit codes, 8 bytes per lane, the four groups of 16
+// codes of each 64-code unit stored in the order G0, G2, G1, G3 (so that a 16-byte read
+// holds one lane's codes for two consecutive 32-deep MFMA slices).
+template <int kBits>
+__device__ __forceinline__ int64_t code_offset(int64_t b, int t)
+{
+    if constexpr (kBits == 8) return b * 256 + t * 16;
+    else return b * 128 + (t >> 2) * 32 + ((((t & 1) << 1) | ((t >> 1) & 1)) << 3);
+}
+
+template <int kBits = 8>
 __device__ __forceinline__ void store_codes(const float (&z)[16], const RowQuant &q, int8_t *dst)
 {
-    if (q.folded) quantize_store16<false>(z, q.mult, dst);
-    else quantize_store16<true>(z, q.mult, dst);
+    if constexpr (kBits == 8) {
+        if (q.folded) quantize_store16<false>(z, q.mult, dst);
+        else quantize_store16<true>(z, q.mult, dst);
+    } else {
+        if (q.folded) quantize_store16_s4<false>(z, q.mult, dst);
+        else quantize_store16_s4<true>(z, q.mult, dst);
+    }
 }
 
 // Dynamic LDS of one workgroup: per-group transpose tiles followed by two sets of
@@ -274,7 +322,7 @@ __host__ __device__ constexpr size_t row_prep_lds_bytes(int threads)
 // (block grp + r*G in v[r]; requires nb <= RB*G).  Rows blockIdx.x, +gridDim.x, ... are
 // processed in turn; the raw bytes of the next row are fetched before the current row is
 // decoded, so their latency overlaps the rotation, the reduction and the stores.
-template <class Loader, int RB>
+template <class Loader, int RB, int kBits = 8>
 __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, int nb,
                                               int8_t *__restrict__ out, int64_t ld_out,
                                               float *__restrict__ scale_out, bool natural, bool amax_only)
@@ -318,12 +366,12 @@ __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, 
             if (tid == 0) scale_out[row] = zrow * 0.0625f;
             return;
         }
-        const RowQuant rq = row_quant(zrow);
+        const RowQuant rq = row_quant<kBits>(zrow);
         int8_t *orow = out + row * ld_out;
 #pragma unroll
         for (int q = 0; q < RB; q++) {
             const int b = grp + q * G;
-            if (b < nb) store_codes(v[q], rq, orow + (int64_t)b * 256 + t * 16);
+            if (b < nb) store_codes<kBits>(v[q], rq, orow + code_offset<kBits>(b, t));
         }
         if (tid == 0) scale_out[row] = rq.scale;
     };
@@ -394,7 +442,7 @@ __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, 
 // once for the maximum and once for the codes (the same operations both times, so the
 // same bits).  `parity` selects the reduction slot set (alternating between consecutive
 // rows of a workgroup, so one barrier per row suffices).
-template <class Loader>
+template <class Loader, int kBits = 8>
 __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row, int nb,
                                                   int8_t *__restrict__ out, int64_t ld_out,
                                                   float *__restrict__ scale_out, bool natural,
@@ -457,7 +505,7 @@ __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row,
         if (tid == 0) scale_out[row] = zrow * 0.0625f;
         return;
     }
-    const RowQuant rq = row_quant(zrow);
+    const RowQuant rq = row_quant<kBits>(zrow);
     for (int s = 0; s < nslices; s++) {
         const int b = s * G + grp;
         if constexpr (kPrefetch) {
@@ -469,7 +517,7 @@ __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row,
             decode_slice(s, cur, v);
         }
         hadamard256(v, tile, t, natural);
-        if (b < nb) store_codes(v, rq, orow + (int64_t)b * 256 + t * 16);
+        if (b < nb) store_codes<kBits>(v, rq, orow + code_offset<kBits>(b, t));
     }
     if (tid == 0) scale_out[row] = rq.scale;
 }
@@ -483,7 +531,7 @@ __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row,
 // barrier per set of rows enough.
 // The raw bytes of the next set of rows are requested before this set is decoded, or right
 // after it is decoded for loaders that prefer one buffer (Loader::kFetchAfterDecode).
-template <class Loader>
+template <class Loader, int kBits = 8>
 __device__ __forceinline__ void row_prep_multi(const Loader &ld, int64_t n_rows, int nb, int rpw,
                                                int8_t *__restrict__ out, int64_t ld_out,
                                                float *__restrict__ scale_out, bool natural, bool amax_only)
@@ -536,8 +584,8 @@ __device__ __forceinline__ void row_prep_multi(const Loader &ld, int64_t n_rows,
             if (live && b == 0 && t == 0) scale_out[row] = zrow * 0.0625f;
             return;
         }
-        const RowQuant rq = row_quant(zrow);
-        if (live) store_codes(v, rq, out + row * ld_out + (int64_t)b * 256 + t * 16);
+        const RowQuant rq = row_quant<kBits>(zrow);
+        if (live) store_codes<kBits>(v, rq, out + row * ld_out + code_offset<kBits>(b, t));
         if (live && b == 0 && t == 0) scale_out[row] = rq.scale;
     };
 
@@ -606,10 +654,10 @@ __host__ __device__ constexpr size_t row_prep_multi_lds_bytes(int threads)
     return (size_t)(threads / kLanesPerBlock) * (kTileStrideF + 2) * sizeof(float);
 }
 
-// Kernel body shared by all loaders.
+// Kernel body shared by all loaders (kBits: 8-bit codes, or packed 4-bit codes).
 // mode: bit 0 two-pass, bit 1 block-transposed code order, bit 2 row maximum only (the
 // row's a = max |y| goes to scale_out; no codes are written and `out` is not used)
-template <class Loader, int RB>
+template <class Loader, int RB, int kBits = 8>
 __device__ __forceinline__ void row_prep_kernel_body(const Loader &ld, int64_t n_rows, int nb,
                                                      int8_t *__restrict__ out, int64_t ld_out,
                                                      float *__restrict__ scale_out, int mode)
@@ -619,11 +667,11 @@ __device__ __forceinline__ void row_prep_kernel_body(const Loader &ld, int64_t n
     if (mode & 1) {
         int parity = 0;
         for (int64_t row = blockIdx.x; row < n_rows; row += gridDim.x) {
-            row_prep_two_pass(ld, row, nb, out, ld_out, scale_out, natural, amax_only, parity);
+            row_prep_two_pass<Loader, kBits>(ld, row, nb, out, ld_out, scale_out, natural, amax_only, parity);
             parity ^= 1;
         }
     } else {
-        row_prep_rows<Loader, RB>(ld, n_rows, nb, out, ld_out, scale_out, natural, amax_only);
+        row_prep_rows<Loader, RB, kBits>(ld, n_rows, nb, out, ld_out, scale_out, natural, amax_only);
     }
 }
 

@@ -6,7 +6,7 @@ takes the W8A8 method with 4-bit weight rows (levels -7..7, scale a/7).  Parity 
 pages' own W4A8 implementation is therefore unpinned; what is pinned here is that the
 oracle computes that reading:
 
-* packing: a hand-worked group of 16 codes, and the round trip over all nibble values;
+* packing: a hand-worked unit of 64 codes, and the round trip over all nibble values;
 * quantizer: a closed-form row (reciprocal 1, ties to even), the error bound
   |y - q s| <= s/2, full use of +-7, zero rows, invariance under power-of-two scaling
   (tiny rows included: the 2^64 extension), and the reciprocal (not division) reading on
@@ -27,19 +27,29 @@ H256 = scipy.linalg.hadamard(256).astype(np.float64)
 
 
 def unpack_by_hand(p: np.ndarray, K_pad: int) -> np.ndarray:
-    """The format, written from its definition: byte j (0..3) of a 16-code group holds codes
-    j and 4 + j, byte 4 + j codes 8 + j and 12 + j, low nibble first; nibbles are two's
-    complement."""
+    """The format, written from its definition: 32-byte units of 64 codes holding the groups
+    of 16 codes G0, G2, G1, G3 in that order; in a group, byte j (0..3) holds codes j and
+    4 + j, byte 4 + j codes 8 + j and 12 + j, low nibble first; two's complement nibbles."""
     n = p.shape[0]
-    g = p[:, :K_pad // 2].reshape(n, K_pad // 16, 8).astype(np.int16)
-    lo, hi = g & 15, g >> 4
-    nib = np.concatenate([lo[:, :, 0:4], hi[:, :, 0:4], lo[:, :, 4:8], hi[:, :, 4:8]], axis=2)
+    u = p[:, :K_pad // 2].reshape(n, K_pad // 64, 4, 8).astype(np.int16)
+    u = u[:, :, [0, 2, 1, 3], :]                     # stored slot -> group: G0 G2 G1 G3
+    lo, hi = u & 15, u >> 4
+    nib = np.concatenate([lo[..., 0:4], hi[..., 0:4], lo[..., 4:8], hi[..., 4:8]], axis=3)
     return np.where(nib >= 8, nib - 16, nib).reshape(n, K_pad).astype(np.int8)
 
 
-def test_pack_hand_worked_group(orc):
-    q = np.array([[1, 2, 3, 4, -1, -2, -3, -4, 7, -7, 0, 5, 6, -6, -5, 3]], np.int8)
-    assert orc.pack_s4(q).tolist() == [[0xF1, 0xE2, 0xD3, 0xC4, 0x67, 0xA9, 0xB0, 0x35]]
+def test_pack_hand_worked_unit(orc):
+    # one unit of 64 codes: G0 below, G1 all 1, G2 all -2, G3 all 3 (the rest of the row 0)
+    g0 = [1, 2, 3, 4, -1, -2, -3, -4, 7, -7, 0, 5, 6, -6, -5, 3]
+    q = np.zeros((1, 256), np.int8)
+    q[0, :64] = g0 + [1] * 16 + [-2] * 16 + [3] * 16
+    p = orc.pack_s4(q)
+    assert p.shape == (1, 128)
+    assert p[0, :32].tolist() == ([0xF1, 0xE2, 0xD3, 0xC4, 0x67, 0xA9, 0xB0, 0x35]   # G0
+                                  + [0xEE] * 8                                       # G2: -2 = 0xE
+                                  + [0x11] * 8                                       # G1
+                                  + [0x33] * 8)                                      # G3
+    assert (p[0, 32:] == 0).all()
 
 
 def test_pack_round_trip(orc):
