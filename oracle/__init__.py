@@ -292,7 +292,7 @@ def pack_s4(q: np.ndarray) -> np.ndarray:
     """codes [n, K_pad] (values -8..7) -> packed [n, K_pad / 2] bytes."""
     q = np.ascontiguousarray(q, np.int8)
     n, kp = q.shape
-    assert kp % 16 == 0
+    assert kp % 64 == 0
     p = np.empty((n, kp // 2), np.uint8)
     lib().or_pack_s4(_p(q), n, kp, kp, _p(p), kp // 2)
     return p

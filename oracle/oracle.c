@@ -532,16 +532,23 @@ void or_row_quant_s4(const float *y, int64_t n_rows, int64_t K_pad, int64_t ld_y
 }
 
 /* The packed int4 format (this library's own; the pages print none): two's complement
- * nibbles, 8 bytes per group of 16 consecutive codes c[0..15] of a row.  Byte j (j = 0..3)
- * holds c[j] in its low nibble and c[4 + j] in its high nibble; byte 4 + j holds c[8 + j]
- * and c[12 + j].  Row n starts at byte n * ld_p; a row of K_pad codes takes K_pad / 2
- * bytes. */
+ * nibbles, 32 bytes per unit of 64 consecutive codes of a row.  The unit's four groups of
+ * 16 codes, G0 (codes 0..15), G1, G2, G3, are stored in the order G0, G2, G1, G3, 8 bytes
+ * each.  A group of codes c[0..15] takes 8 bytes: byte j (j = 0..3) holds c[j] in its low
+ * nibble and c[4 + j] in its high nibble; byte 4 + j holds c[8 + j] and c[12 + j].  Row n
+ * starts at byte n * ld_p; a row of K_pad codes (a multiple of 64) takes K_pad / 2 bytes. */
+static int64_t s4_group_offset(int64_t g)     /* byte offset of group g (16 codes) in a row */
+{
+    static const int slot[4] = {0, 2, 1, 3};
+    return 32 * (g / 4) + 8 * slot[g % 4];
+}
+
 void or_pack_s4(const int8_t *q, int64_t n_rows, int64_t K_pad, int64_t ld_q, uint8_t *p, int64_t ld_p)
 {
     for (int64_t n = 0; n < n_rows; n++)
         for (int64_t g = 0; g < K_pad / 16; g++) {
             const int8_t *c = q + n * ld_q + 16 * g;
-            uint8_t *b = p + n * ld_p + 8 * g;
+            uint8_t *b = p + n * ld_p + s4_group_offset(g);
             for (int j = 0; j < 4; j++) {
                 b[j] = (uint8_t)((c[j] & 15) | ((c[4 + j] & 15) << 4));
                 b[4 + j] = (uint8_t)((c[8 + j] & 15) | ((c[12 + j] & 15) << 4));
@@ -556,7 +563,7 @@ void or_unpack_s4(const uint8_t *p, int64_t n_rows, int64_t K_pad, int64_t ld_p,
 {
     for (int64_t n = 0; n < n_rows; n++)
         for (int64_t g = 0; g < K_pad / 16; g++) {
-            const uint8_t *b = p + n * ld_p + 8 * g;
+            const uint8_t *b = p + n * ld_p + s4_group_offset(g);
             int8_t *c = q + n * ld_q + 16 * g;
             for (int j = 0; j < 4; j++) {
                 c[j] = nibble_value(b[j] & 15);
