@@ -135,6 +135,27 @@ int main()
     expect("layer null workspace", lin(300, 1000, 5376, CR_BF16, need, nullptr), CR_ERR_INVALID_ARG);
     expect("layer empty", lin(0, 1000, 5376, CR_BF16, 0, nullptr), CR_OK);
     expect("layer K too large", lin(300, 1000, BIG, CR_BF16, need, P()), CR_ERR_TOO_LARGE);
+    // W4A8
+    expect("w4 ld_s4 < K_pad/2", cr_quant_weight_w4(P(), CR_FP32, 512, 8, 512, Q<uint8_t>(), 255, Q<float>(), 0,
+                                                    nullptr), CR_ERR_INVALID_ARG);
+    expect("w4 dtype", cr_quant_weight_w4(P(), CR_I32, 512, 8, 512, Q<uint8_t>(), 256, Q<float>(), 0, nullptr),
+           CR_ERR_UNSUPPORTED_DTYPE);
+    expect("w4 empty", cr_quant_weight_w4(nullptr, CR_FP32, 512, 0, 512, nullptr, 256, nullptr, 0, nullptr), CR_OK);
+    expect("s8s4 ldb < K_pad/2", cr_gemm_s8s4_rowscale(Q<int8_t>(), 512, Q<float>(), Q<uint8_t>(), 240, Q<float>(),
+                                                       nullptr, 8, 8, 512, P(), CR_BF16, 8, nullptr),
+           CR_ERR_INVALID_ARG);
+    expect("s8s4 bias on i32", cr_gemm_s8s4_rowscale(Q<int8_t>(), 512, Q<float>(), Q<uint8_t>(), 256, Q<float>(),
+                                                     Q<float>(), 8, 8, 512, P(), CR_I32, 8, nullptr),
+           CR_ERR_INVALID_ARG);
+    expect("s8s4 empty", cr_gemm_s8s4_rowscale(Q<int8_t>(), 512, Q<float>(), Q<uint8_t>(), 256, Q<float>(), nullptr,
+                                               0, 8, 512, P(), CR_BF16, 8, nullptr), CR_OK);
+    expect("w4a8 small workspace", cr_linear_w4a8(P(), CR_BF16, 512, 0, 300, 512, Q<uint8_t>(), 256, Q<float>(), 8,
+                                                  nullptr, P(), CR_BF16, 8, P(), cr_linear_w4a8_workspace_bytes(300, 512) - 1,
+                                                  0, nullptr), CR_ERR_TOO_LARGE);
+    expect("w4a8 i32 out", cr_linear_w4a8(P(), CR_BF16, 512, 0, 300, 512, Q<uint8_t>(), 256, Q<float>(), 8, nullptr,
+                                          P(), CR_I32, 8, P(), 1 << 20, 0, nullptr), CR_ERR_UNSUPPORTED_DTYPE);
+    expect("w4a8 empty", cr_linear_w4a8(nullptr, CR_BF16, 512, 0, 0, 512, Q<uint8_t>(), 256, Q<float>(), 8, nullptr,
+                                        nullptr, CR_BF16, 8, nullptr, 0, 0, nullptr), CR_OK);
     auto na = [&](int64_t M, int64_t N, int64_t K, size_t mt) {
         return cr_linear_nvfp4_noalloc(P(), CR_BF16, 5376, 0, M, K, nullptr, Q<uint8_t>(), 2688, Q<uint8_t>(), 336,
                                        Q<float>(), N, nullptr, P(), CR_BF16, 21504, mt, 0, nullptr);
@@ -145,6 +166,9 @@ int main()
     expect("noalloc negative", na(-1, 21504, 5376, 0), CR_ERR_INVALID_ARG);
     if (ndev == 0) {
         expect("noalloc without a device", na(4096, 21504, 5376, 0), CR_ERR_NO_DEVICE);
+        expect("w4a8 without a device", cr_linear_w4a8(P(), CR_BF16, 512, 0, 300, 512, Q<uint8_t>(), 256, Q<float>(),
+                                                       8, nullptr, P(), CR_BF16, 8, P(), 1 << 20, 0, nullptr),
+               CR_ERR_NO_DEVICE);
         expect("layer without a device", lin(300, 1000, 5376, CR_BF16, need, P()), CR_ERR_NO_DEVICE);
         expect("qa without a device", qa(P(), 0, 512, 4, 512, P(), 512, P(), 0), CR_ERR_NO_DEVICE);
     }

@@ -43,6 +43,16 @@ void or_epilogue_ex(const int32_t *acc, int64_t ld_acc, const float *s_x, const 
 int or_linear_nvfp4_ex(const void *x, int x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
                        const float *pre_scale, const uint8_t *codes, int64_t ld_codes, const uint8_t *sf,
                        int64_t ld_sf, float g, int64_t N, const float *bias, void *out, int out_dtype, int64_t ldc);
+void or_row_quant_s4(const float *y, int64_t n_rows, int64_t K_pad, int64_t ld_y, int8_t *q, int64_t ld_q, float *s);
+void or_pack_s4(const int8_t *q, int64_t n_rows, int64_t K_pad, int64_t ld_q, uint8_t *p, int64_t ld_p);
+void or_unpack_s4(const uint8_t *p, int64_t n_rows, int64_t K_pad, int64_t ld_p, int8_t *q, int64_t ld_q);
+int or_quant_weight_w4(const void *w, int dtype, int64_t ld_w, int64_t N, int64_t K, uint8_t *w_s4, int64_t ld_s4,
+                       float *w_scale);
+int or_gemm_s8s4(const int8_t *A, int64_t lda, const uint8_t *B, int64_t ldb, int64_t M, int64_t N, int64_t K_pad,
+                 int32_t *acc, int64_t ldc);
+int or_linear_w4a8(const void *x, int x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K, const uint8_t *w_s4,
+                   int64_t ld_s4, const float *w_scale, int64_t N, const float *bias, void *out, int out_dtype,
+                   int64_t ldc);
 
 static uint64_t rng = 0x9e3779b97f4a7c15ull;
 static uint32_t next_u32(void)
@@ -216,6 +226,42 @@ static void gemm_epilogue_layer(void)
     free(codes); free(sf); free(x); free(pre); free(y);
 }
 
+/* the W4A8 functions on exactly-sized buffers: packed rows of K_pad / 2 bytes */
+static void w4a8_case(int64_t M, int64_t N, int64_t K)
+{
+    const int64_t kp = or_padded_k(K), lp = kp / 2;
+    float *w = xmalloc(sizeof(float) * (size_t)(N * K));
+    for (int64_t i = 0; i < N * K; i++) w[i] = next_normal() * 0.02f;
+    for (int64_t k = 0; k < K && N > 1; k++) w[K + k] = 0.0f;          /* row 1: a zero row */
+    uint8_t *p = xmalloc((size_t)(N * lp));
+    float *s = xmalloc(sizeof(float) * (size_t)N);
+    CHECK(or_quant_weight_w4(w, 2, K, N, K, p, lp, s) == 0, "quant_weight_w4");
+    int8_t *q = xmalloc((size_t)(N * kp));
+    or_unpack_s4(p, N, kp, lp, q, kp);
+    uint8_t *p2 = xmalloc((size_t)(N * lp));
+    or_pack_s4(q, N, kp, kp, p2, lp);
+    CHECK(memcmp(p, p2, (size_t)(N * lp)) == 0, "pack(unpack(p)) == p");
+    for (int64_t n = 0; n < N; n++) {
+        int mx = 0;
+        for (int64_t k = 0; k < kp; k++) mx = abs(q[n * kp + k]) > mx ? abs(q[n * kp + k]) : mx;
+        CHECK((s[n] == 0.0f && mx == 0) || mx == 7, "every nonzero 4-bit row reaches 7");
+    }
+    uint16_t *x = xmalloc(2 * (size_t)(M * K));
+    for (int64_t i = 0; i < M * K; i++) { float v = next_normal(); or_f32_to_bf16_array(&v, x + i, 1); }
+    int8_t *a = xmalloc((size_t)(M * kp));
+    for (int64_t i = 0; i < M * kp; i++) a[i] = (int8_t)((int)(next_u32() % 255) - 127);
+    int32_t *acc = xmalloc(sizeof(int32_t) * (size_t)(M * N));
+    CHECK(or_gemm_s8s4(a, kp, p, lp, M, N, kp, acc, N) == 0, "gemm_s8s4");
+    void *y = xmalloc(4 * (size_t)(M * N));
+    for (int dt = 0; dt < 3; dt++) CHECK(or_linear_w4a8(x, 0, K, 0, M, K, p, lp, s, N, NULL, y, dt, N) == 0, "w4a8");
+    float y4[256];
+    for (int i = 0; i < 256; i++) y4[i] = (float)(int)(next_u32() % 15) - 7.0f;
+    int8_t q4[256];
+    float s4;
+    or_row_quant_s4(y4, 1, 256, 256, q4, 256, &s4);
+    free(w); free(p); free(s); free(q); free(p2); free(x); free(a); free(acc); free(y);
+}
+
 int main(void)
 {
     formats();
@@ -233,6 +279,9 @@ int main(void)
     nvfp4_case(2, 16385, 0.25f);          /* a row past the two-pass width */
     act_case(1, 0, 2, 20000, 1);
     gemm_epilogue_layer();
+    w4a8_case(3, 5, 300);
+    w4a8_case(2, 3, 17);
+    w4a8_case(1, 2, 16385);
     printf("oracle sanitizer driver: ok\n");
     return 0;
 }
