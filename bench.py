@@ -40,7 +40,7 @@ BT = 2                       # CR_FLAG_BLOCK_TRANSPOSED: the order cr_linear_nvf
 FUSED_VALU_PER_ELEM = 13.25
 PEAK_VALU_TOPS = 39.3
 # NVFP4 weight preparation, vector instructions per weight element at the minimum: decode 2.5,
-# rotation 8, row maximum 0.5 (v_max3), quantization 2.75; rows streamed twice (K_pad > 16384)
+# rotation 8, row maximum 0.5 (v_max3), quantization 2.75; weight rows streamed twice (K_pad > 32768)
 # decode and rotate again (11 + 13.25).
 WEIGHT_VALU_PER_ELEM = {False: 13.75, True: 24.25}
 GEMM_SOURCES = ["rotated_bit_linear_amd/csrc/gemm_s8.hip"]
@@ -516,7 +516,7 @@ def alone_stats(torch, rbl, L, s_main, copy_gbs, n=10):
     t_w = time_loop(torch, wprep, s_main, n=n)
     t_g = time_loop(torch, gemm, s_main, n=n)
     t_x = time_loop(torch, lambda: (act(), gemm()), s_main, n=n)
-    valu = w.N * w.K_pad * WEIGHT_VALU_PER_ELEM[w.K_pad > 16384] / (t_w * 1e-3) / 1e12
+    valu = w.N * w.K_pad * WEIGHT_VALU_PER_ELEM[w.K_pad > 32768] / (t_w * 1e-3) / 1e12
     out = {
         "act_prep_ms": round(t_a, 4),
         "act_prep_gbs": round(L.act_bytes / (t_a * 1e-3) / 1e9, 1),

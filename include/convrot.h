@@ -69,7 +69,8 @@ extern "C" {
 
 #define CR_ABI_VERSION 2
 #define CR_MAX_K_PAD 133120       /* largest multiple of 256 with 127*127*K_pad < 2^31 */
-#define CR_TWO_PASS_K_PAD 16384   /* K_pad above this streams each row twice */
+#define CR_TWO_PASS_K_PAD 16384   /* activation rows with K_pad above this stream twice */
+#define CR_W_TWO_PASS_K_PAD 32768 /* NVFP4 weight rows with K_pad above this stream twice */
 #define CR_DEFAULT_MAX_TILE_BYTES ((size_t)128 << 20)
 
 typedef enum {
@@ -96,7 +97,7 @@ typedef enum {
 
 enum {
     CR_FLAG_NONE = 0,
-    CR_FLAG_FORCE_TWO_PASS = 1,   /* stream rows twice even when K_pad <= CR_TWO_PASS_K_PAD */
+    CR_FLAG_FORCE_TWO_PASS = 1,   /* stream rows twice whatever their length */
     CR_FLAG_BLOCK_TRANSPOSED = 2  /* S8 codes in block-transposed column order (below) */
 };
 

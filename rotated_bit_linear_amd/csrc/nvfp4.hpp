@@ -39,6 +39,7 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b)
 }
 
 struct NVFP4Loader {
+    static constexpr bool kFourBlocks = true;
     static constexpr bool kFetchAfterDecode = false;   // little raw data, cheap decode
     // two-pass rows: loads then decode in place (prefetching the next slice measured 6 %
     // slower on long-K weights: 12 bytes a lane are little to hide)

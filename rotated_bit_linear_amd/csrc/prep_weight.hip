@@ -60,7 +60,12 @@ hipError_t launch_prep_weight(const uint8_t *codes, int64_t ld_codes, const uint
     const int mode = (s.two_pass ? 1 : 0) | (transposed ? 2 : 0);
     NVFP4Loader L{codes, ld_codes, sf, ld_sf, g, K, 0.0f};
     if (launch_multi(L, n_rows, nb, s.two_pass, w_s8, ld_s8, w_scale, mode, st)) return hipGetLastError();
-    if (s.rb == 2) {
+    if (s.rb == 4) {
+        const void *k = reinterpret_cast<const void *>(&prep_weight_kernel<4>);
+        const dim3 grid((unsigned)row_prep_grid(n_rows, s, k, lds));
+        hipLaunchKernelGGL(prep_weight_kernel<4>, grid, dim3(s.threads), lds, st,
+                           L, n_rows, (int)nb, w_s8, ld_s8, w_scale, mode);
+    } else if (s.rb == 2) {
         const void *k = reinterpret_cast<const void *>(&prep_weight_kernel<2>);
         const dim3 grid((unsigned)row_prep_grid(n_rows, s, k, lds));
         hipLaunchKernelGGL(prep_weight_kernel<2>, grid, dim3(s.threads), lds, st,
@@ -84,7 +89,12 @@ hipError_t launch_weight_amax(const uint8_t *codes, int64_t ld_codes, const uint
     const int mode = (s.two_pass ? 1 : 0) | 2 | 4;     // the order of z does not matter for the maximum
     NVFP4Loader L{codes, ld_codes, sf, ld_sf, g, K, 0.0f};
     if (launch_multi(L, n_rows, nb, s.two_pass, nullptr, 0, amax, mode, st)) return hipGetLastError();
-    if (s.rb == 2) {
+    if (s.rb == 4) {
+        const void *k = reinterpret_cast<const void *>(&prep_weight_kernel<4>);
+        const dim3 grid((unsigned)row_prep_grid(n_rows, s, k, lds));
+        hipLaunchKernelGGL(prep_weight_kernel<4>, grid, dim3(s.threads), lds, st,
+                           L, n_rows, (int)nb, nullptr, (int64_t)0, amax, mode);
+    } else if (s.rb == 2) {
         const void *k = reinterpret_cast<const void *>(&prep_weight_kernel<2>);
         const dim3 grid((unsigned)row_prep_grid(n_rows, s, k, lds));
         hipLaunchKernelGGL(prep_weight_kernel<2>, grid, dim3(s.threads), lds, st,

@@ -215,6 +215,9 @@ __device__ __forceinline__ float sigma_lookup(uint32_t off, uint32_t p)
 // unfused pre-scale (ComfyUI Turing Utils README, "Load ConvRot DiT ..." bullet).
 template <int DT, bool kPre>
 struct ActLoader {
+    // rows of 65-128 blocks stream twice: measured faster than four blocks per group here
+    // (the second read is served from the cache, and a slice workgroup has 960 threads)
+    static constexpr bool kFourBlocks = false;
     static constexpr bool kFetchAfterDecode = true;
     static constexpr bool kTwoPassPrefetch = true;
     static constexpr bool kSigTable = false;
@@ -243,6 +246,8 @@ struct ActLoader {
 
 template <int DT, bool kPre>
 struct SwigluLoader {
+    // as for ActLoader (and fp16/fp32 gates with a pre-scale would spill at four blocks)
+    static constexpr bool kFourBlocks = false;
     static constexpr bool kFetchAfterDecode = true;
     // fp32 segments (128 bytes a lane) leave no registers for a second buffer
     static constexpr bool kTwoPassPrefetch = DT != 2;
@@ -361,7 +366,7 @@ static hipError_t launch_rows(const Loader &L, int64_t rows, int64_t nb, int8_t 
                               float *scale, bool force_two_pass, bool transposed, hipStream_t st,
                               int one_pass_groups = kMaxGroups2)
 {
-    const RowPrepShape s = row_prep_shape(nb, force_two_pass, one_pass_groups);
+    const RowPrepShape s = row_prep_shape(nb, force_two_pass, one_pass_groups, Loader::kFourBlocks);
     // the sigma table sits past the engine's LDS, at a 16-byte boundary
     constexpr size_t extra = Loader::kSigTable ? kSigTableBytes + 16 : 0;
     const size_t lds = row_prep_lds_bytes(s.threads) + extra;
@@ -381,6 +386,15 @@ static hipError_t launch_rows(const Loader &L, int64_t rows, int64_t nb, int8_t 
         hipLaunchKernelGGL((quant_act_multi_kernel<Loader, kBits>), grid, dim3(threads), mlds, st, L, rows, (int)nb,
                            rpw, out, ld_out, scale, mode);
         return hipGetLastError();
+    }
+    if constexpr (Loader::kFourBlocks) {
+        if (s.rb == 4) {
+            const void *k = reinterpret_cast<const void *>(&quant_act_kernel<Loader, 4, kBits>);
+            const dim3 grid((unsigned)row_prep_grid(rows, s, k, lds));
+            hipLaunchKernelGGL((quant_act_kernel<Loader, 4, kBits>), grid, dim3(s.threads), lds, st,
+                               L, rows, (int)nb, out, ld_out, scale, mode);
+            return hipGetLastError();
+        }
     }
     if (s.rb == 2) {
         const void *k = reinterpret_cast<const void *>(&quant_act_kernel<Loader, 2, kBits>);

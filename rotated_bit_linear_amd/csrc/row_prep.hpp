@@ -41,7 +41,8 @@
 // above holds with 127 replaced by 7.  They are packed two per byte (quantize_store16_s4,
 // code_offset).
 //
-// Rows whose K_pad exceeds 64 blocks (16384 columns), or when forced, are streamed twice:
+// Rows whose K_pad exceeds 128 blocks (32768 columns; 64 blocks for the activation loaders,
+// whose two-pass form measured faster), or when forced, are streamed twice:
 // pass 1 rotates every block to find the row maximum, pass 2 reloads, rotates again and
 // quantizes (same operations, so the same bits).
 #pragma once
@@ -57,7 +58,7 @@ namespace convrot {
 constexpr int kLanesPerBlock = 16;          // lanes sharing one 256-column block
 constexpr int kTileStrideF = 272;           // floats per 16x16 transpose tile (256 + 16 pad)
 constexpr int kMaxGroups1 = 60;             // two-pass rows: 960 threads
-constexpr int kMaxGroups2 = 32;             // one-pass rows: 512 threads
+constexpr int kMaxGroups2 = 32;             // one-pass rows: 512 threads (two or four blocks per group)
 constexpr int kMaxGroupsWide = 64;          // one-pass SwiGLU rows, one block per group
 constexpr int64_t kTwoPassMaxGrid = 65536;  // workgroups of a two-pass launch (they loop)
 
@@ -304,6 +305,8 @@ __host__ __device__ constexpr size_t row_prep_lds_bytes(int threads)
 }
 
 // Loader concept:
+//   static constexpr bool kFourBlocks;               rows of 65-128 blocks are held in one
+//                                                    pass, four blocks per lane group
 //   static constexpr bool kFetchAfterDecode;         request the next row after decoding
 //                                                    this one (else before: two buffers)
 //   static constexpr bool kTwoPassPrefetch;          two-pass rows: request the next slice
@@ -676,15 +679,17 @@ __device__ __forceinline__ void row_prep_kernel_body(const Loader &ld, int64_t n
 }
 
 // Launch shape of a row of nb blocks.  Up to one_pass_groups blocks (32, or 64 for the
-// SwiGLU activation kernel), one block per 16-lane group; up to 64 blocks, two per group (at
-// most 512 threads); beyond that, two passes over slices of at most 60 groups (960 threads),
-// the blocks spread evenly over the slices.  One block per group keeps fewer values per
+// SwiGLU activation kernel), one block per 16-lane group; up to 64 blocks, two per group,
+// and, for loaders that opt in, up to 128 blocks four per group (at most 512 threads: the
+// whole row stays in registers, so it is loaded, decoded and rotated once); beyond that, two
+// passes over slices of at most 60 groups (960 threads), the blocks spread evenly over the
+// slices.  One block per group keeps fewer values per
 // lane, so a SwiGLU row of 56 blocks runs 14 waves of at most 128 registers instead of 7
 // waves of 144 (1-3 % faster); rows with a short decode (plain activations, NVFP4 weights)
 // are 2-3 % faster at two blocks per group.
 struct RowPrepShape {
     int threads;   // workgroup size, a multiple of 64
-    int rb;        // blocks held per 16-lane group in one-pass mode (1 or 2)
+    int rb;        // blocks held per 16-lane group in one-pass mode (1, 2 or 4)
     bool two_pass;
 };
 
@@ -692,7 +697,13 @@ struct RowPrepShape {
 template <int RB>
 constexpr int row_prep_max_threads() { return RB == 1 ? 1024 : 512; }
 
-inline RowPrepShape row_prep_shape(int64_t nb, bool force_two_pass, int one_pass_groups = kMaxGroups2)
+// Longest row (in 256-column blocks) prepared in one pass: four blocks per group.
+constexpr int64_t kOnePassMaxBlocks = 4 * kMaxGroups2;
+
+// four_per_group: the loader takes rows of 65-128 blocks in one pass, four blocks per group
+// (the NVFP4 weight loader: it then decodes and rotates each block once instead of twice)
+inline RowPrepShape row_prep_shape(int64_t nb, bool force_two_pass, int one_pass_groups = kMaxGroups2,
+                                   bool four_per_group = true)
 {
     RowPrepShape s{};
     int64_t groups;
@@ -702,6 +713,9 @@ inline RowPrepShape row_prep_shape(int64_t nb, bool force_two_pass, int one_pass
     } else if (!force_two_pass && nb <= 2 * kMaxGroups2) {
         s.rb = 2;
         groups = (nb + 1) / 2;
+    } else if (!force_two_pass && four_per_group && nb <= kOnePassMaxBlocks) {
+        s.rb = 4;
+        groups = (nb + 3) / 4;
     } else {
         // as few slices as 60 groups allow, with the blocks spread evenly over them
         s.rb = 1;

@@ -113,6 +113,8 @@ ACT_CASES = [
     (synth.DT_BF16, 5, 16384, 16384, False, False),
     (synth.DT_BF16, 5, 16385, 16392, True, False),    # 65 blocks: two-pass by size
     (synth.DT_FP16, 3, 20000, 20000, True, False),
+    (synth.DT_FP32, 4, 32768, 32768, True, False),
+    (synth.DT_BF16, 4, 32769, 32776, True, False),
     (synth.DT_BF16, 11, 5376, 5376, True, True),      # forced two-pass
     (synth.DT_FP32, 1, 1, 4, False, False),           # one element
 ]
@@ -141,6 +143,9 @@ def test_two_pass_equals_one_pass_activation():
 
 SWI_CASES = [
     (synth.DT_BF16, 32, 14336),
+    (synth.DT_BF16, 6, 20000),      # 79 blocks: two-pass by size
+    (synth.DT_FP16, 4, 17000),      # 67 blocks, sigma computed
+    (synth.DT_BF16, 3, 33000),
     (synth.DT_BF16, 9, 300),        # value half not 16-byte aligned: element loads
     (synth.DT_FP32, 7, 1000),
     (synth.DT_FP16, 5, 640),
@@ -163,9 +168,11 @@ def test_quant_act_swiglu_bit_exact(dt, M, F):
 # ---------------------------------------------------------------- weight prep ----
 
 # row shapes: one block per lane group (K <= 8192), two (8192 < K <= 16384: 14336 and a
-# 33-block row with a tail), two-pass (K > 16384), and tiny rows
+# 33-block row with a tail), four (16384 < K <= 32768: 20000, 32768), two-pass (K > 32768:
+# 40000), and tiny rows
 W_CASES = [(256, 512, None, None), (300, 1000, 512, 80), (97, 20000, None, None), (64, 5376, None, None),
-           (1, 17, 16, 5), (40, 14336, None, None), (21, 8200, 4112, 520)]
+           (1, 17, 16, 5), (40, 14336, None, None), (21, 8200, 4112, 520), (33, 32768, None, None),
+           (19, 40000, None, None)]
 
 
 @pytest.mark.parametrize("N,K,ldc,ldsf", W_CASES, ids=[f"N{c[0]}-K{c[1]}" for c in W_CASES])
@@ -325,6 +332,8 @@ PRE_CASES = [
     (synth.DT_BF16, 37, 300, False, False),
     (synth.DT_FP16, 9, 5376, False, False),
     (synth.DT_FP32, 5, 16385, False, False),        # two-pass by size
+    (synth.DT_FP16, 3, 20000, True, False),         # SwiGLU fp16 + pre-scale, 79 blocks
+    (synth.DT_FP32, 3, 40000, False, False),
     (synth.DT_BF16, 7, 700, True, False),
     (synth.DT_BF16, 4, 14336, True, False),         # 56-block SwiGLU rows: one block per lane group
     (synth.DT_BF16, 4, 14336, False, False),        # 56-block plain rows: two blocks per lane group
@@ -555,14 +564,15 @@ def test_quant_act_swiglu_every_bf16_gate(F, flags):
 
 @pytest.mark.parametrize("dt", [synth.DT_BF16, synth.DT_FP16])
 def test_quant_act_swiglu_two_pass_many_rows(dt):
-    """SwiGLU rows past 16384 columns (two passes) in more rows than the device holds
-    workgroups at once: with bf16 gates each workgroup builds the sigma table once and loops
-    over rows (alternating reduction slots), with fp16 one workgroup per row."""
+    """SwiGLU rows of 67 blocks (two passes by size, and forced) in more rows than the device
+    holds workgroups at once: with bf16 gates each workgroup builds the sigma table once and
+    loops over rows (alternating reduction slots), with fp16 gates sigma is computed."""
     M, F = 700, 17000
     h = make_x(M, 2 * F, dt, seed=71, ld=2 * F + 8, special=True)
-    say(f"cr_quant_act_swiglu two-pass dt={dt} M={M} F={F}")
-    q, s = rbl.quant_act(h.to(dev()), F, swiglu=True)
-    torch.cuda.synchronize()
     rq, rs = oracle.quant_act(host_bits(h, dt), dt, F, swiglu=True)
-    assert_bits_equal(q.cpu().numpy(), rq, "x_s8 (swiglu, two-pass, many rows)")
-    assert_bits_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32), "x_scale (swiglu, two-pass, many rows)")
+    for flags in (0, rbl.CR_FLAG_FORCE_TWO_PASS):
+        say(f"cr_quant_act_swiglu many rows dt={dt} M={M} F={F} flags={flags}")
+        q, s = rbl.quant_act(h.to(dev()), F, swiglu=True, flags=flags)
+        torch.cuda.synchronize()
+        assert_bits_equal(q.cpu().numpy(), rq, f"x_s8 (swiglu, many rows, flags={flags})")
+        assert_bits_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32), f"x_scale (swiglu, flags={flags})")
