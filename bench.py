@@ -43,7 +43,7 @@ PEAK_VALU_TOPS = 39.3
 # rotation 8, row maximum 0.5 (v_max3), quantization 2.75; weight rows streamed twice (K_pad > 32768)
 # decode and rotate again (11 + 13.25).
 WEIGHT_VALU_PER_ELEM = {False: 13.75, True: 24.25}
-GEMM_SOURCES = ["rotated_bit_linear_amd/csrc/gemm_s8.hip"]
+GEMM_SOURCES = ["rotated_bit_linear_amd/csrc/gemm_s8.hip", "rotated_bit_linear_amd/csrc/gemm_common.hpp"]
 PMC_PROFILE = os.path.join(ROOT, "profiles", "gemm_s8_qkv_m19989_hbm_counters.md")
 
 

@@ -105,3 +105,64 @@ def test_mlp_chain_fc1_swiglu_fc2():
     assert_bits_equal(h_got, h_ref, "fc1 output (bf16 bits)")
     err = check_output(got, y_ref, synth.DT_BF16, "chain output")
     print(f"chain: final rel_l2={err:.3e}, bit-identical")
+
+
+def _block_transposed(codes: np.ndarray) -> np.ndarray:
+    r, kp = codes.shape
+    return codes.reshape(r, kp // 256, 16, 16).transpose(0, 1, 3, 2).reshape(r, kp).copy()
+
+
+def test_qkv_at_the_pages_16mib_tile_bound():
+    """QKV at M = 19989 with S8 weight tiles bounded by 16 MiB (the pages' bound: 7 chunks of
+    3072 rows, two tiles alternating, preparation on a second stream).  The call's own
+    workspace is read back afterwards: its S8 activation (block-transposed order) and row
+    scales bit-exact in full, its last weight tile (chunk 6, rows 18432..21503) bit-exact;
+    the output equals the default bound's bit for bit and the oracle's on sampled rows."""
+    w = synth.WORKLOADS["qkv"]
+    bound = 16 << 20
+    R, nch = rbl.cr_linear_nvfp4_plan(w.M, w.N, w.K, bound)
+    assert (R, nch) == (3072, 7)
+    x = synth.make_activation(w)
+    p = synth.make_weight_nvfp4(w)
+    gs = torch.tensor([p.g], dtype=torch.float32, device=dev())
+    xd, cd, sd = x.to(dev()), p.codes.to(dev()), p.sf.to(dev())
+    aux = torch.cuda.Stream()
+    ws = torch.empty(rbl.cr_linear_nvfp4_workspace_bytes(w.M, w.N, w.K, bound), dtype=torch.uint8, device=dev())
+    out = torch.empty(w.M, w.N, dtype=torch.bfloat16, device=dev())
+    say(f"qkv: cr_linear_nvfp4 M={w.M} N={w.N} K={w.K} max_tile_bytes=16 MiB, aux stream")
+    rbl.cr_linear_nvfp4(xd, w.K, False, cd, sd, gs, out, ws, bound, aux_stream=aux)
+    say("qkv: cr_linear_nvfp4 default tile bound")
+    ref_default = rbl.linear_nvfp4(xd, cd, sd, gs, w.K, aux_stream=aux)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_default), "16 MiB and default tile bounds differ"
+
+    kp = w.K_pad
+    up = lambda v: (v + 255) // 256 * 256   # noqa: E731  (the workspace's 256-byte regions)
+    host = ws.cpu().numpy()
+    x_s8 = host[:w.M * kp].view(np.int8).reshape(w.M, kp)
+    off = up(w.M * kp)
+    x_scale = host[off:off + 4 * w.M].view(np.float32)
+    off = up(off + 4 * w.M)
+    tiles = []
+    for _ in range(2):
+        t = host[off:off + R * kp].view(np.int8).reshape(R, kp)
+        off = up(off + R * kp)
+        s = host[off:off + 4 * R].view(np.float32)
+        off = up(off + 4 * R)
+        tiles.append((t, s))
+    rqx, rsx = oracle.quant_act(synth.bits_u16(x), w.x_dtype, w.K)
+    assert_bits_equal(x_s8, _block_transposed(rqx), "x_s8 in the workspace (block-transposed)")
+    assert_bits_equal(x_scale.view(np.uint32), rsx.view(np.uint32), "x_scale in the workspace")
+    last = nch - 1                            # chunk 6 went to tile 6 % 2 = 0
+    n0, rows = last * R, w.N - last * R
+    rqw, rsw = oracle.prep_weight_nvfp4(p.codes.numpy()[n0:], p.sf.numpy()[n0:], p.g, w.K)
+    t, s = tiles[last % 2]
+    assert_bits_equal(t[:rows], _block_transposed(rqw), "last S8 weight tile")
+    assert_bits_equal(s[:rows].view(np.uint32), rsw.view(np.uint32), "last weight tile scales")
+
+    rows_m = synth.sample_rows(w.M, SAMPLE_ROWS, w.seed, torch.empty(0, dtype=torch.long)).numpy()
+    rqw_all, rsw_all = oracle.prep_weight_nvfp4(p.codes.numpy(), p.sf.numpy(), p.g, w.K)
+    acc = oracle.gemm_s8(np.ascontiguousarray(rqx[rows_m]), rqw_all)
+    ref = oracle.epilogue(acc, rsx[rows_m], rsw_all, synth.DT_BF16)
+    err = check_output(out[torch.from_numpy(rows_m).to(dev())].cpu(), ref, synth.DT_BF16, "qkv at 16 MiB")
+    print(f"qkv at the 16 MiB bound: rows checked={len(rows_m)} rel_l2={err:.3e}, bit-identical")
