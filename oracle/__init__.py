@@ -62,6 +62,10 @@ def lib():
             "or_gemm_s8s4": (C.c_int, [vp, i64, vp, i64, i64, i64, i64, vp, i64]),
             "or_linear_w4a8": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, i64, vp, i64, vp, vp,
                                          C.c_int, i64]),
+            "or_quant_act_w4": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, i64, vp]),
+            "or_gemm_s4s4": (C.c_int, [vp, i64, vp, i64, i64, i64, i64, vp, i64]),
+            "or_linear_w4a4": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, i64, vp, i64, vp, vp,
+                                         C.c_int, i64]),
             "or_exp_array": (None, [vp, vp, i64]),
             "or_sigmoid_array": (None, [vp, vp, i64]),
             "or_swiglu_array": (None, [vp, vp, vp, i64]),
@@ -341,6 +345,47 @@ def linear_w4a8(x: np.ndarray, x_dtype: int, K: int, swiglu: bool, w_s4: np.ndar
     out = np.empty((M, N), odt)
     b, bp = _opt_f32(bias, N)
     rc = lib().or_linear_w4a8(_p(x), x_dtype, x.shape[1], int(swiglu), M, K, _p(w_s4), w_s4.shape[1],
+                              _p(w_scale), N, bp, _p(out), out_dtype, N)
+    assert rc == 0
+    return out
+
+
+# ------------------------------------------------------------ W4A4 variant ----
+
+def quant_act_w4(x: np.ndarray, dtype: int, K: int, swiglu: bool = False):
+    """X [M, >=K] (or H [M, >=2F]) -> (packed 4-bit codes [M, K_pad / 2] uint8, scales [M] fp32)."""
+    x = np.ascontiguousarray(x, _elem_dtype(dtype))
+    M = x.shape[0]
+    kp = padded_k(K)
+    p = np.empty((M, kp // 2), np.uint8)
+    s = np.empty(M, np.float32)
+    rc = lib().or_quant_act_w4(_p(x), dtype, x.shape[1], int(swiglu), M, K, _p(p), kp // 2, _p(s))
+    assert rc == 0
+    return p, s
+
+
+def gemm_s4s4(a_s4: np.ndarray, b_s4: np.ndarray, K_pad: int) -> np.ndarray:
+    """int32 acc[M, N] = unpack(A)[M, K_pad] . unpack(B)[N, K_pad]^T."""
+    a_s4 = np.ascontiguousarray(a_s4, np.uint8)
+    b_s4 = np.ascontiguousarray(b_s4, np.uint8)
+    M, N = a_s4.shape[0], b_s4.shape[0]
+    acc = np.empty((M, N), np.int32)
+    rc = lib().or_gemm_s4s4(_p(a_s4), a_s4.shape[1], _p(b_s4), b_s4.shape[1], M, N, K_pad, _p(acc), N)
+    assert rc == 0
+    return acc
+
+
+def linear_w4a4(x: np.ndarray, x_dtype: int, K: int, swiglu: bool, w_s4: np.ndarray, w_scale: np.ndarray,
+                out_dtype: int, bias=None) -> np.ndarray:
+    """The W4A4 layer on the rows of x against a prepared 4-bit weight."""
+    x = np.ascontiguousarray(x, _elem_dtype(x_dtype))
+    w_s4 = np.ascontiguousarray(w_s4, np.uint8)
+    w_scale = np.ascontiguousarray(w_scale, np.float32)
+    M, N = x.shape[0], w_s4.shape[0]
+    odt = {DT_BF16: np.uint16, DT_FP16: np.uint16, DT_FP32: np.float32, DT_I32: np.int32}[out_dtype]
+    out = np.empty((M, N), odt)
+    b, bp = _opt_f32(bias, N)
+    rc = lib().or_linear_w4a4(_p(x), x_dtype, x.shape[1], int(swiglu), M, K, _p(w_s4), w_s4.shape[1],
                               _p(w_scale), N, bp, _p(out), out_dtype, N)
     assert rc == 0
     return out

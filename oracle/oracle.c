@@ -630,6 +630,72 @@ int or_linear_w4a8(const void *x, int x_dtype, int64_t ld_x, int swiglu, int64_t
     return rc;
 }
 
+/* ------------------------------------------------ W4A4 variant (4-bit both sides) ---- */
+
+/* ComfyUI Turing Utils README: W4A4 is the third ConvRot format it dispatches (opening
+ * paragraph; section "Nodes", bullet "Load ConvRot DiT"), again without a description.
+ * Reading taken, as for W4A8: the W8A8 method with 4-bit rows on both sides; the
+ * activation row (after SwiGLU when fused) is rotated and quantized by the 4-bit rule
+ * above and packed like the weight; int32 accumulation of the 4-bit products; the W8A8
+ * epilogue. */
+
+/* Activation preparation to packed 4-bit rows: load (+SwiGLU), ConvRot256, 4-bit row
+ * quantization, packing.  x_s4 [M, ld_s4 bytes] (ld_s4 >= K_pad / 2), x_scale [M].
+ * Returns 0, or -1 on allocation failure. */
+int or_quant_act_w4(const void *x, int dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
+                    uint8_t *x_s4, int64_t ld_s4, float *x_scale)
+{
+    int64_t kp = or_padded_k(K);
+    float *buf = (float *)malloc(sizeof(float) * (size_t)(M > 0 ? M : 1) * (size_t)kp);
+    int8_t *q = (int8_t *)malloc((size_t)(M > 0 ? M : 1) * (size_t)kp);
+    int rc = -1;
+    if (buf && q) {
+        if (swiglu) or_act_load_swiglu(x, dtype, ld_x, M, K, buf, kp);
+        else or_act_load(x, dtype, ld_x, M, K, buf, kp);
+        or_convrot256(buf, M, kp, kp);
+        or_row_quant_s4(buf, M, kp, kp, q, kp, x_scale);
+        or_pack_s4(q, M, kp, kp, x_s4, ld_s4);
+        rc = 0;
+    }
+    free(buf);
+    free(q);
+    return rc;
+}
+
+/* acc[m, n] = sum_k Aq[m, k] * Wq[n, k], both the unpacked 4-bit codes of packed rows. */
+int or_gemm_s4s4(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                 int64_t M, int64_t N, int64_t K_pad, int32_t *acc, int64_t ldc)
+{
+    int8_t *aq = (int8_t *)malloc((size_t)(M > 0 ? M : 1) * (size_t)K_pad);
+    int rc = -1;
+    if (aq) {
+        or_unpack_s4(A, M, K_pad, lda, aq, K_pad);
+        rc = or_gemm_s8s4(aq, K_pad, B, ldb, M, N, K_pad, acc, ldc);
+    }
+    free(aq);
+    return rc;
+}
+
+/* The W4A4 layer: 4-bit activation preparation, the 4-bit x 4-bit GEMM against the
+ * prepared weight, the row-scale epilogue (+ optional bias [N]).  Returns 0 or -1. */
+int or_linear_w4a4(const void *x, int x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
+                   const uint8_t *w_s4, int64_t ld_s4, const float *w_scale, int64_t N,
+                   const float *bias, void *out, int out_dtype, int64_t ldc)
+{
+    int64_t kp = or_padded_k(K);
+    uint8_t *xq = (uint8_t *)malloc((size_t)(M > 0 ? M : 1) * (size_t)(kp / 2));
+    float *xs = (float *)malloc(sizeof(float) * (size_t)(M > 0 ? M : 1));
+    int32_t *acc = (int32_t *)malloc(sizeof(int32_t) * (size_t)(M > 0 ? M : 1) * (size_t)(N > 0 ? N : 1));
+    int rc = -1;
+    if (xq && xs && acc && or_quant_act_w4(x, x_dtype, ld_x, swiglu, M, K, xq, kp / 2, xs) == 0 &&
+        or_gemm_s4s4(xq, kp / 2, w_s4, ld_s4, M, N, kp, acc, N) == 0) {
+        or_epilogue_ex(acc, N, xs, w_scale, bias, M, N, out_dtype, out, ldc);
+        rc = 0;
+    }
+    free(xq); free(xs); free(acc);
+    return rc;
+}
+
 /* ----------------------------------------------- elementwise array helpers ---- */
 /* Thin loops so the tests can sweep whole code spaces without one foreign call per value. */
 

@@ -53,6 +53,13 @@ int or_gemm_s8s4(const int8_t *A, int64_t lda, const uint8_t *B, int64_t ldb, in
 int or_linear_w4a8(const void *x, int x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K, const uint8_t *w_s4,
                    int64_t ld_s4, const float *w_scale, int64_t N, const float *bias, void *out, int out_dtype,
                    int64_t ldc);
+int or_quant_act_w4(const void *x, int dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K, uint8_t *x_s4,
+                    int64_t ld_s4, float *x_scale);
+int or_gemm_s4s4(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb, int64_t M, int64_t N, int64_t K_pad,
+                 int32_t *acc, int64_t ldc);
+int or_linear_w4a4(const void *x, int x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K, const uint8_t *w_s4,
+                   int64_t ld_s4, const float *w_scale, int64_t N, const float *bias, void *out, int out_dtype,
+                   int64_t ldc);
 
 static uint64_t rng = 0x9e3779b97f4a7c15ull;
 static uint32_t next_u32(void)
@@ -254,6 +261,19 @@ static void w4a8_case(int64_t M, int64_t N, int64_t K)
     CHECK(or_gemm_s8s4(a, kp, p, lp, M, N, kp, acc, N) == 0, "gemm_s8s4");
     void *y = xmalloc(4 * (size_t)(M * N));
     for (int dt = 0; dt < 3; dt++) CHECK(or_linear_w4a8(x, 0, K, 0, M, K, p, lp, s, N, NULL, y, dt, N) == 0, "w4a8");
+    /* W4A4: 4-bit activation rows (plain and SwiGLU over the first K/2 pairs), the 4x4 GEMM */
+    uint8_t *xp = xmalloc((size_t)(M * lp));
+    float *xs = xmalloc(sizeof(float) * (size_t)M);
+    CHECK(or_quant_act_w4(x, 0, K, 0, M, K, xp, lp, xs) == 0, "quant_act_w4");
+    CHECK(or_gemm_s4s4(xp, lp, p, lp, M, N, kp, acc, N) == 0, "gemm_s4s4");
+    if (K >= 2) {
+        const int64_t kh = K / 2, lph = or_padded_k(kh) / 2;
+        uint8_t *hp = xmalloc((size_t)(M * lph));
+        CHECK(or_quant_act_w4(x, 0, K, 1, M, kh, hp, lph, xs) == 0, "quant_act_w4 swiglu");
+        free(hp);
+    }
+    for (int dt = 0; dt < 3; dt++) CHECK(or_linear_w4a4(x, 0, K, 0, M, K, p, lp, s, N, s, y, dt, N) == 0, "w4a4");
+    free(xp); free(xs);
     float y4[256];
     for (int i = 0; i < 256; i++) y4[i] = (float)(int)(next_u32() % 15) - 7.0f;
     int8_t q4[256];

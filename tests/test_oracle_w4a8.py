@@ -194,3 +194,65 @@ def test_layer_composition_and_error_band(orc):
     q8, s8 = row_quant(convrot256(act_load(w.numpy(), synth.DT_FP32, K)))
     y8 = orc.epilogue(orc.gemm_s8(qx, q8), sx, s8, synth.DT_FP32)
     assert np.linalg.norm(y8 - ref) / np.linalg.norm(ref) < rel / 5
+
+
+# ------------------------------------------------------------------ W4A4 ----
+# The README's third ConvRot format, W4A4, read the same way: 4-bit rows on both sides.
+
+def test_w4a4_activation_path_recovers_exact_codes(orc):
+    """Activations built as Q s R come back as exactly Q and s (the weight pin above, through
+    the activation loader, bf16 input: the values below are exact in bf16)."""
+    Q, s, X = _exact_weight(24, 512, 9, s_exp=-3)
+    xb = torch.from_numpy(X).to(torch.bfloat16)
+    assert np.array_equal(xb.float().numpy(), X)
+    p, sc = orc.quant_act_w4(synth.bits_u16(xb), synth.DT_BF16, 512)
+    assert np.array_equal(unpack_by_hand(p, 512), Q)
+    assert (sc == s).all()
+
+
+def test_w4a4_swiglu_is_swiglu_then_4bit_rows(orc):
+    rng = np.random.default_rng(10)
+    h = rng.standard_normal((6, 600)).astype(np.float32)
+    p, s = orc.quant_act_w4(h, synth.DT_FP32, 300, swiglu=True)
+    y = orc.convrot256(orc.act_load(h, synth.DT_FP32, 300, swiglu=True))
+    q, s2 = orc.row_quant_s4(y)
+    assert np.array_equal(unpack_by_hand(p, 512), q) and np.array_equal(s, s2)
+
+
+def test_gemm_s4s4_int64_brute_force(orc):
+    rng = np.random.default_rng(11)
+    for (M, N, K_pad) in [(1, 1, 256), (9, 17, 768)]:
+        qa = rng.integers(-7, 8, (M, K_pad), dtype=np.int8)
+        qb = rng.integers(-7, 8, (N, K_pad), dtype=np.int8)
+        ref = qa.astype(np.int64) @ qb.astype(np.int64).T
+        assert np.array_equal(orc.gemm_s4s4(orc.pack_s4(qa), orc.pack_s4(qb), K_pad).astype(np.int64), ref)
+
+
+def test_w4a4_layer_composition_and_error_band(orc):
+    """The layer equals its steps; its error against the float64 product is that of 4-bit
+    rows on both sides (above the W4A8 band), and the rotation still helps when the
+    activations carry outlier channels."""
+    g = torch.Generator().manual_seed(12)
+    M, N, K = 96, 320, 1024
+    x = torch.randn(M, K, generator=g)
+    x[:, torch.randperm(K, generator=g)[:10]] *= 20.0            # outlier channels
+    x = x.to(torch.bfloat16)
+    w = (0.02 * torch.randn(N, K, generator=g)).float()
+    xb = synth.bits_u16(x)
+    p, sw = orc.quant_weight_w4(w.numpy(), synth.DT_FP32, K)
+    y = orc.linear_w4a4(xb, synth.DT_BF16, K, False, p, sw, synth.DT_FP32)
+    px, sx = orc.quant_act_w4(xb, synth.DT_BF16, K)
+    assert np.array_equal(y, orc.epilogue(orc.gemm_s4s4(px, p, K), sx, sw, synth.DT_FP32))
+    ref = x.double().numpy() @ w.double().numpy().T
+    rel = np.linalg.norm(y - ref) / np.linalg.norm(ref)
+    y48 = orc.linear_w4a8(xb, synth.DT_BF16, K, False, p, sw, synth.DT_FP32)
+    rel48 = np.linalg.norm(y48 - ref) / np.linalg.norm(ref)
+    assert rel48 < rel < 0.5, (rel48, rel)
+    # the same 4-bit rows without the rotation (plain per-row absmax/7 on both operands)
+    def plain(v):
+        a = np.abs(v).max(axis=1, keepdims=True)
+        return np.clip(np.rint(v / a * 7), -7, 7), a / 7
+    qa, sa = plain(x.double().numpy())
+    qw, sww = plain(w.double().numpy())
+    rel_plain = np.linalg.norm((qa @ qw.T) * sa * sww.T - ref) / np.linalg.norm(ref)
+    assert rel < rel_plain / 1.5, (rel, rel_plain)
