@@ -63,6 +63,8 @@ def parse_args():
                     help="also time the layers with S8 weight tiles bounded by this many MiB (0: skip)")
     ap.add_argument("--w4a8", default="qkv,ffn_down",
                     help="layers timed through the W4A8 variant, apart from value ('' = none)")
+    ap.add_argument("--w4a4", default="qkv,ffn_down",
+                    help="layers timed through the W4A4 variant, apart from value ('' = none)")
     ap.add_argument("--configs", default="tiny,qkv_m4096,longk",
                     help="the other configurations, reported apart from value ('' = none)")
     ap.add_argument("--serial", action="store_true", help="prepare weights on the main stream")
@@ -488,6 +490,50 @@ def w4a8_layers(torch, rbl, synth, dev, names, s_main, n=20):
     return info
 
 
+def w4a4_layers(torch, rbl, synth, dev, names, s_main, n=20):
+    """The W4A4 variant at the metric's shapes: the weight prepared as for W4A8, then the layer
+    call cr_linear_w4a4, its activation preparation and its GEMM alone; outputs of the layer
+    and of activation prep + GEMM must agree."""
+    info = {}
+    for name in names:
+        w = synth.WORKLOADS[name]
+        x = synth.make_activation(w).to(dev)
+        wf = synth.make_weight_f32(w).to(dev)
+        p = torch.empty(w.N, w.K_pad // 2, dtype=torch.uint8, device=dev)
+        sw = torch.empty(w.N, dtype=torch.float32, device=dev)
+        rbl.cr_quant_weight_w4(wf, w.K, p, sw, BT, stream=s_main)
+        torch.cuda.synchronize()
+        del wf
+        out = torch.empty(w.M, w.N, dtype=torch.bfloat16, device=dev)
+        out2 = torch.empty_like(out)
+        ws = torch.empty(rbl.cr_linear_w4a4_workspace_bytes(w.M, w.K), dtype=torch.uint8, device=dev)
+        qx = torch.empty(w.M, w.K_pad // 2, dtype=torch.uint8, device=dev)
+        sx = torch.empty(w.M, dtype=torch.float32, device=dev)
+        act = lambda: rbl.cr_quant_act_w4(x, w.K, w.swiglu, qx, sx, BT, stream=s_main)  # noqa: E731
+        layer = lambda: rbl.cr_linear_w4a4(x, w.K, w.swiglu, p, sw, out, ws, flags=BT, stream=s_main)  # noqa: E731
+        gemm = lambda: rbl.cr_gemm_s4s4_rowscale(qx, sx, p, sw, out2, stream=s_main)  # noqa: E731
+        t_layer = time_loop(torch, layer, s_main, n=n)
+        t_act = time_loop(torch, act, s_main, n=n)
+        t_gemm = time_loop(torch, gemm, s_main, n=n)
+        torch.cuda.synchronize()
+        if not torch.equal(out, out2):
+            raise SystemExit(f"bench: cr_linear_w4a4 differs from activation prep + W4A4 GEMM on {name}")
+        ops = 2 * w.M * w.N * w.K_pad
+        in_cols = 2 * w.K if w.swiglu else w.K
+        act_bytes = w.M * (in_cols * x.element_size() + w.K_pad // 2 + 4)
+        info[name] = {
+            "M": w.M, "N": w.N, "K": w.K, "K_pad": w.K_pad, "swiglu": w.swiglu,
+            "layer_ms": round(t_layer, 4),
+            "act_prep_ms": round(t_act, 4),
+            "act_prep_gbs": round(act_bytes / (t_act * 1e-3) / 1e9, 1),
+            "gemm_ms": round(t_gemm, 4),
+            "gemm_tops": round(ops / (t_gemm * 1e-3) / 1e12, 1),
+            "gemm_frac_peak": round(ops / (t_gemm * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+        }
+        del x, p, sw, out, out2, ws, qx, sx
+    return info
+
+
 def copy_calibration(mib: int):
     import torch
     n = mib << 20
@@ -667,6 +713,13 @@ def main():
         w4_info = w4a8_layers(torch, rbl, synth, dev, w4_names, s_main, n=max(5, K // 2))
         w4_info["value_ms_per_layer"] = round(sum(v["layer_ms"] for v in w4_info.values()) / len(w4_names), 4)
 
+    w44_info = None
+    w44_names = [n.strip() for n in args.w4a4.split(",") if n.strip()]
+    if w44_names:
+        print(f"bench: W4A4 variant on {w44_names}", file=sys.stderr, flush=True)
+        w44_info = w4a4_layers(torch, rbl, synth, dev, w44_names, s_main, n=max(5, K // 2))
+        w44_info["value_ms_per_layer"] = round(sum(v["layer_ms"] for v in w44_info.values()) / len(w44_names), 4)
+
     short_info = None
     rows_list = [int(v) for v in args.short_batches.split(",") if v.strip()]
     if rows_list:
@@ -733,6 +786,7 @@ def main():
         "next_shapes": next_info,
         "short_batches": short_info,
         "w4a8": w4_info,
+        "w4a4": w44_info,
         "wall_ms_timed_region": round(wall_ms, 2),
         "copy_gbs": round(copy_gbs, 1),
         "gemm_source_sha256_16": gemm_source_hash(),

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define CR_ABI_VERSION 2
+#define CR_ABI_VERSION 3
 #define CR_MAX_K_PAD 133120       /* largest multiple of 256 with 127*127*K_pad < 2^31 */
 #define CR_TWO_PASS_K_PAD 16384   /* activation rows with K_pad above this stream twice */
 #define CR_W_TWO_PASS_K_PAD 32768 /* NVFP4 weight rows with K_pad above this stream twice */
@@ -315,6 +315,46 @@ cr_status cr_gemm_s8s4_rowscale(const int8_t *a_s8, int64_t lda, const float *a_
  */
 size_t cr_linear_w4a8_workspace_bytes(int64_t M, int64_t K);
 cr_status cr_linear_w4a8(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
+                         const uint8_t *w_s4, int64_t ld_s4, const float *w_scale, int64_t N, const float *bias,
+                         void *out, cr_dtype out_dtype, int64_t ldc, void *workspace, size_t ws_bytes,
+                         uint32_t flags, hipStream_t stream);
+
+/*
+ * W4A4 variant: 4-bit weights and 4-bit activations (ComfyUI Turing Utils README, opening
+ * paragraph and section "Nodes", bullet "Load ConvRot DiT": W4A4 dispatch; the packed
+ * layout is named there, not described).  This library reads it as the W4A8 reading on
+ * both operands: the activation row (SwiGLU first when swiglu != 0) goes through ConvRot256
+ * and the 4-bit per-row rule above (a = max |y|, scale a / 7, codes -7..7) and is packed in
+ * the format above; the weight is the one cr_quant_weight_w4 prepares; int32 sums of the
+ * 4-bit products; the same epilogue.
+ *
+ * Activation preparation: X [M, ld_x] (ld_x >= K; swiglu: H [M, ld_x], ld_x >= 2K, gate
+ * H[:, :K], value H[:, K:2K]) of x_dtype (CR_BF16, CR_FP16, CR_FP32), rows of 16-byte
+ * multiples, 16-byte aligned -> x_s4 [M, ld_s4] bytes (ld_s4 >= K_pad / 2, a multiple of
+ * 16) and x_scale [M] float.  flags as for cr_quant_weight_w4.
+ */
+cr_status cr_quant_act_w4(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
+                          uint8_t *x_s4, int64_t ld_s4, float *x_scale, uint32_t flags, hipStream_t stream);
+
+/*
+ * W4A4 GEMM: out = ((float)sum_k p[m, k] q[n, k] * a_scale[m]) * b_scale[n] (+ bias[n]), p and
+ * q the codes of the packed rows a_s4 [M, lda bytes] and b_s4 [N, ldb bytes] (lda, ldb >=
+ * K_pad / 2, multiples of 16).  The other arguments, the limits and CR_I32 as in
+ * cr_gemm_s8_rowscale_bias; both operands must use the same column order.
+ */
+cr_status cr_gemm_s4s4_rowscale(const uint8_t *a_s4, int64_t lda, const float *a_scale,
+                                const uint8_t *b_s4, int64_t ldb, const float *b_scale, const float *bias,
+                                int64_t M, int64_t N, int64_t K_pad, void *c, cr_dtype c_dtype, int64_t ldc,
+                                hipStream_t stream);
+
+/*
+ * The W4A4 layer: cr_quant_act_w4 into the workspace, then cr_gemm_s4s4_rowscale against the
+ * prepared weight, both on `stream`.  Arguments, flags and errors as for cr_linear_w4a8;
+ * workspace: cr_linear_w4a4_workspace_bytes(M, K) bytes, 256-byte aligned (the packed
+ * activation and its scales); an empty layer (M or N = 0) needs none.
+ */
+size_t cr_linear_w4a4_workspace_bytes(int64_t M, int64_t K);
+cr_status cr_linear_w4a4(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
                          const uint8_t *w_s4, int64_t ld_s4, const float *w_scale, int64_t N, const float *bias,
                          void *out, cr_dtype out_dtype, int64_t ldc, void *workspace, size_t ws_bytes,
                          uint32_t flags, hipStream_t stream);

@@ -19,7 +19,7 @@ import torch
 
 from . import build as _build
 
-CR_ABI_VERSION = 2
+CR_ABI_VERSION = 3
 CR_BF16, CR_FP16, CR_FP32, CR_I32 = 0, 1, 2, 3
 CR_FLAG_NONE, CR_FLAG_FORCE_TWO_PASS, CR_FLAG_BLOCK_TRANSPOSED = 0, 1, 2
 CR_MAX_K_PAD = 133120
@@ -78,6 +78,11 @@ def lib() -> C.CDLL:
             "cr_gemm_s8s4_rowscale": (C.c_int, [vp, i64, vp, vp, i64, vp, vp, i64, i64, i64, vp, C.c_int, i64, vp]),
             "cr_linear_w4a8_workspace_bytes": (sz, [i64, i64]),
             "cr_linear_w4a8": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, i64, vp, i64, vp, vp, C.c_int,
+                                         i64, vp, sz, u32, vp]),
+            "cr_quant_act_w4": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, i64, vp, u32, vp]),
+            "cr_gemm_s4s4_rowscale": (C.c_int, [vp, i64, vp, vp, i64, vp, vp, i64, i64, i64, vp, C.c_int, i64, vp]),
+            "cr_linear_w4a4_workspace_bytes": (sz, [i64, i64]),
+            "cr_linear_w4a4": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, i64, vp, i64, vp, vp, C.c_int,
                                          i64, vp, sz, u32, vp]),
             "cr_gemm_nvfp4_fused": (C.c_int, [vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, i64, i64, i64, vp,
                                               C.c_int, i64, u32, vp]),
@@ -286,6 +291,38 @@ def cr_linear_w4a8(x, K, swiglu, w_s4, w_scale, out, workspace, bias=None, flags
         0 if workspace is None else workspace.numel() * workspace.element_size(), flags, _stream(stream)))
 
 
+def cr_quant_act_w4(x, K, swiglu, x_s4, x_scale, flags=0, stream=None):
+    M, ld_x = _rows_ld(x)
+    _, ld_s4 = _rows_ld(x_s4)
+    _check("cr_quant_act_w4", lib().cr_quant_act_w4(
+        _ptr(x), _TORCH_TO_CR[x.dtype], ld_x, int(bool(swiglu)), M, K, _ptr(x_s4), ld_s4, _ptr(x_scale), flags,
+        _stream(stream)))
+
+
+def cr_gemm_s4s4_rowscale(a_s4, a_scale, b_s4, b_scale, c, bias=None, K_pad=None, stream=None):
+    M, lda = _rows_ld(a_s4)
+    N, ldb = _rows_ld(b_s4)
+    _, ldc = _rows_ld(c)
+    kp = 2 * a_s4.shape[1] if K_pad is None else K_pad
+    _check("cr_gemm_s4s4_rowscale", lib().cr_gemm_s4s4_rowscale(
+        _ptr(a_s4), lda, _ptr(a_scale), _ptr(b_s4), ldb, _ptr(b_scale), _ptr(bias), M, N, kp,
+        _ptr(c), _TORCH_TO_CR[c.dtype], ldc, _stream(stream)))
+
+
+def cr_linear_w4a4_workspace_bytes(M, K) -> int:
+    return int(lib().cr_linear_w4a4_workspace_bytes(M, K))
+
+
+def cr_linear_w4a4(x, K, swiglu, w_s4, w_scale, out, workspace, bias=None, flags=0, stream=None):
+    M, ld_x = _rows_ld(x)
+    N, ld_s4 = _rows_ld(w_s4)
+    _, ldc = _rows_ld(out)
+    _check("cr_linear_w4a4", lib().cr_linear_w4a4(
+        _ptr(x), _TORCH_TO_CR[x.dtype], ld_x, int(bool(swiglu)), M, K, _ptr(w_s4), ld_s4, _ptr(w_scale), N,
+        _ptr(bias), _ptr(out), _TORCH_TO_CR[out.dtype], ldc, _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), flags, _stream(stream)))
+
+
 # ---------------------------------------------------------------- conveniences ----
 
 def quant_act(x: torch.Tensor, K: int | None = None, swiglu: bool = False, flags: int = 0,
@@ -370,4 +407,26 @@ def linear_w4a8(x, w_s4, w_scale, K, out_dtype=torch.bfloat16, swiglu=False, bia
         out = torch.empty(M, N, dtype=out_dtype, device=x.device)
     ws = torch.empty(max(1, cr_linear_w4a8_workspace_bytes(M, K)), dtype=torch.uint8, device=x.device)
     cr_linear_w4a8(x, K, swiglu, w_s4, w_scale, out, ws, bias=bias, flags=flags)
+    return out
+
+
+def quant_act_w4(x: torch.Tensor, K: int | None = None, swiglu: bool = False, flags: int = 0):
+    """(packed 4-bit codes [M, K_pad / 2] uint8, scales [M] fp32) of X [M, K] or of
+    SwiGLU(H [M, 2K])."""
+    if K is None:
+        K = x.shape[1] // 2 if swiglu else x.shape[1]
+    kp = padded_k(K)
+    q = torch.empty(x.shape[0], kp // 2, dtype=torch.uint8, device=x.device)
+    s = torch.empty(x.shape[0], dtype=torch.float32, device=x.device)
+    cr_quant_act_w4(x, K, swiglu, q, s, flags)
+    return q, s
+
+
+def linear_w4a4(x, w_s4, w_scale, K, out_dtype=torch.bfloat16, swiglu=False, bias=None, flags=0, out=None):
+    """y = x W^T (+ b) through the W4A4 route against a prepared 4-bit weight."""
+    M, N = x.shape[0], w_s4.shape[0]
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype, device=x.device)
+    ws = torch.empty(max(1, cr_linear_w4a4_workspace_bytes(M, K)), dtype=torch.uint8, device=x.device)
+    cr_linear_w4a4(x, K, swiglu, w_s4, w_scale, out, ws, bias=bias, flags=flags)
     return out

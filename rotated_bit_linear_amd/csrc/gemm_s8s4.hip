@@ -19,6 +19,11 @@
 // G0 G2 | G1 G3 order puts one k-half of both slices side by side), so each slice reads
 // 2 KB of activation and 2 KB of weight fragments per wave instead of 2 KB + 4 KB.
 // Tile order, waits and the epilogue are those of the S8 x S8 GEMM (gemm_common.hpp).
+//
+// The W4A4 form (A4 = true) takes the activation codes packed the same way: both operands
+// are widened (products 256 qa qb; |256 * 7 * 7 * K_pad| < 2^31 for every accepted K_pad),
+// the epilogue shifts by 8 bits, a stage is 16 KB + 16 KB, and the activation fragments of
+// a slice pair are one 16-byte read like the weight's.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,21 +46,31 @@ constexpr int BM = W_M * T_M, BN = W_N * T_N;   // 256 x 256 workgroup tile
 constexpr int BK = 128;                         // K per step
 constexpr int NSTAGE = 3;
 constexpr int NWAVE = W_M * W_N, NTHREAD = 64 * NWAVE;
-constexpr int ROW_A = BK, ROW_B = BK / 2;       // LDS bytes per row of a stage
-constexpr int SA = BM * ROW_A, SB = BN * ROW_B, SSTAGE = SA + SB;
-// LDS: the activation stages A0 A1 A2 (32 KB each), then the weight stages B0 B1 B2
-// (16 KB each).  A DS instruction adds at most 65535 to its address register, so the
-// fragment reads use three address sets: activation rows (+0 for A0, +32768 for A1),
-// activation rows + 64 KB (A2), and weight rows + 96 KB (+16384 per stage).
-constexpr int A_BASE = 0, B_BASE = NSTAGE * SA;
-constexpr int PIECES_A = SA / 1024, PIECES_B = SB / 1024;    // 1 KB DMA pieces per stage
-constexpr int PPW = (PIECES_A + PIECES_B) / NWAVE;           // pieces per wave per stage
-constexpr int KS = BK / 32;                     // 32-deep slices per step (two per weight read)
-static_assert((PIECES_A + PIECES_B) % NWAVE == 0, "DMA pieces split evenly over the waves");
-static_assert(NSTAGE * SSTAGE <= 160 * 1024, "LDS ring exceeds 160 KB");
-static_assert(NWAVE * EPI_BYTES + BN * 4 <= NSTAGE * SSTAGE, "epilogue tiles and bias fit the ring");
-static_assert(PPW * (NSTAGE - 1) <= 63, "vmcnt range");
-static_assert(KS == 4, "the step below reads weight fragments for slices (0, 1) and (2, 3)");
+constexpr int ROW_B = BK / 2;                   // LDS bytes per weight row of a stage
+constexpr int SB = BN * ROW_B;
+constexpr int KS = BK / 32;                     // 32-deep slices per step (two per packed read)
+static_assert(KS == 4, "the step below reads packed fragments for slices (0, 1) and (2, 3)");
+
+// LDS of one form.  W4A8: the activation stages A0 A1 A2 (32 KB each), then the weight
+// stages B0 B1 B2 (16 KB each); a DS instruction adds at most 65535 to its address
+// register, so the fragment reads use three address sets: activation rows (+0 for A0,
+// +32768 for A1), activation rows + 64 KB (A2), and weight rows + 96 KB (+16384 per
+// stage).  W4A4: A0 A1 A2 of 16 KB, then B0 B1 B2, two address sets.
+template <bool A4>
+struct Ring {
+    static constexpr int ROW_A = A4 ? BK / 2 : BK;
+    static constexpr int SA = BM * ROW_A, SSTAGE = SA + SB;
+    static constexpr int A_BASE = 0, B_BASE = NSTAGE * SA;
+    static constexpr int PIECES_A = SA / 1024, PIECES_B = SB / 1024;    // 1 KB DMA pieces per stage
+    static constexpr int PPW = (PIECES_A + PIECES_B) / NWAVE;           // pieces per wave per stage
+    static constexpr int POOL = NSTAGE * SSTAGE > NWAVE * EPI_BYTES + BN * 4 ? NSTAGE * SSTAGE
+                                                                             : NWAVE * EPI_BYTES + BN * 4;
+    static_assert((PIECES_A + PIECES_B) % NWAVE == 0, "DMA pieces split evenly over the waves");
+    static_assert(POOL <= 160 * 1024, "LDS exceeds 160 KB");
+    static_assert(PPW * (NSTAGE - 1) <= 63, "vmcnt range");
+};
+constexpr int POOL_BYTES = Ring<false>::POOL > Ring<true>::POOL ? Ring<false>::POOL : Ring<true>::POOL;
+constexpr int MAX_PPW = Ring<false>::PPW > Ring<true>::PPW ? Ring<false>::PPW : Ring<true>::PPW;
 
 // 16-byte chunk swizzles: activation rows have 8 chunks, weight rows 4 (chunk 2p + h is
 // k-half h of slice pair p); both keep 32-row fragment reads free of bank conflicts
@@ -70,14 +85,19 @@ __device__ __forceinline__ v4i widen(uint32_t d0, uint32_t d1)
     return v4i{(int32_t)((d0 << 4) & hi), (int32_t)(d0 & hi), (int32_t)((d1 << 4) & hi), (int32_t)(d1 & hi)};
 }
 
-template <int OUT, bool BIAS>
+template <int OUT, bool BIAS, bool A4>
 __global__ __launch_bounds__(NTHREAD, 1)
 void gemm_s8s4_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__restrict__ sa,
                       const uint8_t *__restrict__ B, int64_t ldb, const float *__restrict__ sb,
                       const float *__restrict__ bias, int M, int N, int K_pad, void *__restrict__ C,
                       int64_t ldc, int tiles_m, int tiles_n)
 {
-    __shared__ __attribute__((aligned(1024))) int8_t pool[NSTAGE * SSTAGE];
+    // The pool and the DMA source arrays have types that do not depend on the template
+    // parameters: with a dependent operand type the host compilation drops the kernel's
+    // launch stub without a diagnostic (the DMA builtin is checked against the host target
+    // at instantiation).  One workgroup runs per CU either way.
+    using R = Ring<A4>;
+    __shared__ __attribute__((aligned(1024))) int8_t pool[POOL_BYTES];
 
     int tm, tn;
     gemm::tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -87,34 +107,41 @@ void gemm_s8s4_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__
     const int wm = wave / W_N, wn = wave % W_N;
 
     // ---- DMA assignment: wave w moves pieces w*PPW .. w*PPW+PPW-1 of a stage.  Piece
-    //      p < PIECES_A: activation rows 8p .. 8p+7 (lane: row lane/8, LDS slot lane%8);
+    //      p < PIECES_A: activation rows 8p .. 8p+7 (lane: row lane/8, LDS slot lane%8),
+    //      packed activation rows 16p .. 16p+15 in the W4A4 form (as the weight's);
     //      otherwise weight rows 16q .. 16q+15, q = p - PIECES_A (lane: row lane/4, slot
     //      lane%4).  Slot s of row r holds logical chunk s ^ swz(r); rows past M or N read
     //      the last row (their results are never stored). ----
-    const int8_t *gsrc[PPW];
-    int ldst[PPW], kstep[PPW];
+    const int8_t *gsrc[MAX_PPW];        // non-dependent types: see the pool above
+    int ldst[MAX_PPW], kstep[MAX_PPW];
 #pragma unroll
-    for (int j = 0; j < PPW; j++) {
-        const int p = wave * PPW + j;
-        if (p < PIECES_A) {
+    for (int j = 0; j < R::PPW; j++) {
+        const int p = wave * R::PPW + j;
+        if (A4 && p < R::PIECES_A) {
+            const int r = 16 * p + (lane >> 2);
+            const int chunk = (lane & 3) ^ swz_b(r);
+            gsrc[j] = A + (int64_t)min(m0 + r, M - 1) * lda + chunk * 16;
+            ldst[j] = R::A_BASE + p * 1024;
+            kstep[j] = BK / 2;
+        } else if (p < R::PIECES_A) {
             const int r = 8 * p + (lane >> 3);
             const int chunk = (lane & 7) ^ swz_a(r);
             gsrc[j] = A + (int64_t)min(m0 + r, M - 1) * lda + chunk * 16;
-            ldst[j] = A_BASE + p * 1024;
+            ldst[j] = R::A_BASE + p * 1024;
             kstep[j] = BK;
         } else {
-            const int q = p - PIECES_A;
+            const int q = p - R::PIECES_A;
             const int r = 16 * q + (lane >> 2);
             const int chunk = (lane & 3) ^ swz_b(r);
             gsrc[j] = reinterpret_cast<const int8_t *>(B) + (int64_t)min(n0 + r, N - 1) * ldb + chunk * 16;
-            ldst[j] = B_BASE + q * 1024;
+            ldst[j] = R::B_BASE + q * 1024;
             kstep[j] = BK / 2;
         }
     }
     auto issue = [&](int s, int kt) {
 #pragma unroll
-        for (int j = 0; j < PPW; j++) {
-            const int stage_off = ldst[j] < B_BASE ? s * SA : s * SB;
+        for (int j = 0; j < R::PPW; j++) {
+            const int stage_off = ldst[j] < R::B_BASE ? s * R::SA : s * SB;
             __builtin_amdgcn_global_load_lds(gsrc[j] + (int64_t)kt * kstep[j], pool + ldst[j] + stage_off, 16, 0, 0);
         }
     };
@@ -128,15 +155,20 @@ void gemm_s8s4_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__
 #pragma unroll
         for (int i = 0; i < F_M; i++) {
             const int r = wm * T_M + i * 32 + frow;
-            adrA[ks][i] = (uint32_t)(uintptr_t)pool + A_BASE + r * ROW_A + (((2 * ks + fhalf) ^ swz_a(r)) << 4);
-            adrA2[ks][i] = adrA[ks][i] + 2 * SA;
+            if constexpr (A4) {
+                // packed rows: chunk 2 p + (lane >> 5) of slice pair p (entries ks >= 2 unused)
+                adrA[ks][i] = (uint32_t)(uintptr_t)pool + R::A_BASE + r * R::ROW_A + (((2 * (ks & 1) + fhalf) ^ swz_b(r)) << 4);
+            } else {
+                adrA[ks][i] = (uint32_t)(uintptr_t)pool + R::A_BASE + r * R::ROW_A + (((2 * ks + fhalf) ^ swz_a(r)) << 4);
+                adrA2[ks][i] = adrA[ks][i] + 2 * R::SA;
+            }
         }
 #pragma unroll
     for (int pp = 0; pp < KS / 2; pp++)
 #pragma unroll
         for (int j = 0; j < F_N; j++) {
             const int r = wn * T_N + j * 32 + frow;
-            adrB[pp][j] = (uint32_t)(uintptr_t)pool + B_BASE + r * ROW_B + (((2 * pp + fhalf) ^ swz_b(r)) << 4);
+            adrB[pp][j] = (uint32_t)(uintptr_t)pool + R::B_BASE + r * ROW_B + (((2 * pp + fhalf) ^ swz_b(r)) << 4);
         }
 
     v16i acc[F_M][F_N];
@@ -149,13 +181,14 @@ void gemm_s8s4_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__
 
     v4i fa[2][F_M], fb[2][F_N];      // fragments of even (0) and odd (1) slices
     v4i braw[F_N];                    // weight fragment reads of one slice pair
+    v4i araw[F_M];                    // packed activation reads of one slice pair (W4A4)
     // LDS reads of stage s (a compile-time constant at every call, so the stage offset is
     // the instruction's immediate)
     auto lds = [](uint32_t a) { return reinterpret_cast<const __attribute__((address_space(3))) v4i *>(a); };
     auto read_a = [&](int s, int ks, int slot) {
 #pragma unroll
         for (int i = 0; i < F_M; i++)
-            fa[slot][i] = s == 2 ? *lds(adrA2[ks][i]) : *lds(adrA[ks][i] + s * SA);
+            fa[slot][i] = s == 2 ? *lds(adrA2[ks][i]) : *lds(adrA[ks][i] + s * R::SA);
     };
     auto read_b = [&](int s, int pp) {
 #pragma unroll
@@ -166,6 +199,18 @@ void gemm_s8s4_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__
         for (int j = 0; j < F_N; j++) {
             fb[0][j] = widen((uint32_t)braw[j][0], (uint32_t)braw[j][1]);
             fb[1][j] = widen((uint32_t)braw[j][2], (uint32_t)braw[j][3]);
+        }
+    };
+    // W4A4: packed activation fragments of slice pair pp, and their widening
+    auto read_a4 = [&](int s, int pp) {
+#pragma unroll
+        for (int i = 0; i < F_M; i++) araw[i] = *lds(adrA[pp][i] + s * R::SA);
+    };
+    auto widen_a = [&]() {
+#pragma unroll
+        for (int i = 0; i < F_M; i++) {
+            fa[0][i] = widen((uint32_t)araw[i][0], (uint32_t)araw[i][1]);
+            fa[1][i] = widen((uint32_t)araw[i][2], (uint32_t)araw[i][3]);
         }
     };
     // MFMAs number t0 .. t1-1 of a slice (t = i*F_N + j); weight fragment first, so lane l
@@ -184,9 +229,10 @@ void gemm_s8s4_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__
     const int nk = K_pad / BK;                   // even, >= 2 (K_pad is a multiple of 256)
 #pragma unroll
     for (int s = 0; s < NSTAGE; s++) issue(s, min(s, nk - 1));
-    __builtin_amdgcn_s_waitcnt(gemm::waitcnt_vm((NSTAGE - 1) * PPW));
+    __builtin_amdgcn_s_waitcnt(gemm::waitcnt_vm((NSTAGE - 1) * R::PPW));
     gemm::barrier();
-    read_a(0, 0, 0);
+    if constexpr (A4) read_a4(0, 0);
+    else read_a(0, 0, 0);
     read_b(0, 0);
 
     // One step k on stage S (= k % 3).  Before its last slice every wave waits for its own
@@ -202,9 +248,16 @@ void gemm_s8s4_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__
         constexpr int NX = (S + 1) % NSTAGE;
 #pragma unroll
         for (int ks = 0; ks < KS; ks++) {
-            if (ks % 2 == 0) widen_b();          // slices ks and ks+1 from the pair's read
+            if (ks % 2 == 0) {                   // slices ks and ks+1 from the pair's reads
+                if constexpr (A4) widen_a();
+                widen_b();
+            }
             if (ks < KS - 1) {
-                read_a(S, ks + 1, (ks + 1) & 1);
+                if constexpr (A4) {
+                    if (ks == 1) read_a4(S, 1);
+                } else {
+                    read_a(S, ks + 1, (ks + 1) & 1);
+                }
                 if (ks == 1) read_b(S, 1);
                 mfmas(ks & 1, 0, NMF);
                 __builtin_amdgcn_sched_barrier(0);
@@ -213,9 +266,10 @@ void gemm_s8s4_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__
                 // has completed before the barrier; it also covers part of the wait
                 mfmas(ks & 1, 0, 1);
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                __builtin_amdgcn_s_waitcnt(gemm::waitcnt_vm(PPW));
+                __builtin_amdgcn_s_waitcnt(gemm::waitcnt_vm(R::PPW));
                 gemm::barrier();
-                read_a(NX, 0, 0);
+                if constexpr (A4) read_a4(NX, 0);
+                else read_a(NX, 0, 0);
                 read_b(NX, 0);
                 mfmas(ks & 1, 1, NMF);
                 if (k + 1 < nk) issue(S, min(k + NSTAGE, nk - 1));
@@ -237,7 +291,7 @@ void gemm_s8s4_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__
     __builtin_amdgcn_s_waitcnt(gemm::waitcnt_vm(0));   // the clamped re-reads have landed
 
     // ---- epilogue (gemm::store_tile) on the idle ring: wave w's tile at w * EPI_BYTES, the
-    //      bias values after the eight tiles; the sums are 16 times too large ----
+    //      bias values after the eight tiles; the sums are 16 (W4A4: 256) times too large ----
     const int nbase = n0 + wn * T_N;
     gemm::EpiScales<F_M, F_N> esc;
     gemm::load_scales<OUT, F_M, F_N>(esc, sa, sb, m0 + wm * T_M, nbase, frow, fhalf, M, N);
@@ -251,17 +305,47 @@ void gemm_s8s4_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__
     constexpr int ES = (OUT == 0 || OUT == 1) ? 2 : 4;
     const bool vec_ok = (((uintptr_t)C) % 16 == 0) && ((ldc * ES) % 16 == 0);
     const bool interior = vec_ok && m0 + BM <= M && n0 + BN <= N;
-    gemm::store_tile<OUT, BIAS, F_M, F_N, T_N, 4>(acc, esc, pool + wave * EPI_BYTES, bias_lds + wn * T_N, C, ldc,
+    gemm::store_tile<OUT, BIAS, F_M, F_N, T_N, A4 ? 8 : 4>(acc, esc, pool + wave * EPI_BYTES, bias_lds + wn * T_N, C, ldc,
                                                   m0 + wm * T_M, nbase, M, N, interior, vec_ok, lane);
 }
 
-template <int OUT, bool BIAS>
+template <int OUT, bool BIAS, bool A4>
 void launch_one(const dim3 &grid, hipStream_t st, const int8_t *A, int64_t lda, const float *sa, const uint8_t *B,
                 int64_t ldb, const float *sb, const float *bias, int64_t M, int64_t N, int64_t K_pad, void *C,
                 int64_t ldc, int tiles_m, int tiles_n)
 {
-    hipLaunchKernelGGL((gemm_s8s4_kernel<OUT, BIAS>), grid, dim3(NTHREAD), 0, st, A, lda, sa, B, ldb, sb, bias,
+    hipLaunchKernelGGL((gemm_s8s4_kernel<OUT, BIAS, A4>), grid, dim3(NTHREAD), 0, st, A, lda, sa, B, ldb, sb, bias,
                        (int)M, (int)N, (int)K_pad, C, ldc, tiles_m, tiles_n);
+}
+
+using LaunchFn = void (*)(const dim3 &, hipStream_t, const int8_t *, int64_t, const float *, const uint8_t *,
+                         int64_t, const float *, const float *, int64_t, int64_t, int64_t, void *, int64_t, int, int);
+
+// the instantiation for one output dtype, bias and form (nullptr: no int32 output with bias)
+LaunchFn pick(int out_dtype, bool bias, bool a4)
+{
+    switch (out_dtype) {
+    case 0: return bias ? (a4 ? launch_one<0, true, true> : launch_one<0, true, false>)
+                        : (a4 ? launch_one<0, false, true> : launch_one<0, false, false>);
+    case 1: return bias ? (a4 ? launch_one<1, true, true> : launch_one<1, true, false>)
+                        : (a4 ? launch_one<1, false, true> : launch_one<1, false, false>);
+    case 2: return bias ? (a4 ? launch_one<2, true, true> : launch_one<2, true, false>)
+                        : (a4 ? launch_one<2, false, true> : launch_one<2, false, false>);
+    case 3: return bias ? nullptr : (a4 ? launch_one<3, false, true> : launch_one<3, false, false>);
+    default: return nullptr;
+    }
+}
+
+hipError_t launch_form(bool a4, const int8_t *A, int64_t lda, const float *sa, const uint8_t *B, int64_t ldb,
+                       const float *sb, const float *bias, int64_t M, int64_t N, int64_t K_pad, void *C,
+                       int out_dtype, int64_t ldc, hipStream_t st)
+{
+    const LaunchFn fn = pick(out_dtype, bias != nullptr, a4);
+    if (!fn) return hipErrorInvalidValue;
+    const int tiles_m = (int)((M + BM - 1) / BM);
+    const int tiles_n = (int)((N + BN - 1) / BN);
+    fn(dim3((unsigned)(tiles_m * tiles_n)), st, A, lda, sa, B, ldb, sb, bias, M, N, K_pad, C, ldc, tiles_m, tiles_n);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -270,21 +354,15 @@ hipError_t launch_gemm_s8s4(const int8_t *A, int64_t lda, const float *sa, const
                             const float *sb, const float *bias, int64_t M, int64_t N, int64_t K_pad, void *C,
                             int out_dtype, int64_t ldc, hipStream_t st)
 {
-    const int tiles_m = (int)((M + BM - 1) / BM);
-    const int tiles_n = (int)((N + BN - 1) / BN);
-    const dim3 grid((unsigned)(tiles_m * tiles_n));
-    const bool b = bias != nullptr;
-    switch (out_dtype) {
-    case 0: (b ? launch_one<0, true> : launch_one<0, false>)(grid, st, A, lda, sa, B, ldb, sb, bias, M, N, K_pad, C, ldc, tiles_m, tiles_n); break;
-    case 1: (b ? launch_one<1, true> : launch_one<1, false>)(grid, st, A, lda, sa, B, ldb, sb, bias, M, N, K_pad, C, ldc, tiles_m, tiles_n); break;
-    case 2: (b ? launch_one<2, true> : launch_one<2, false>)(grid, st, A, lda, sa, B, ldb, sb, bias, M, N, K_pad, C, ldc, tiles_m, tiles_n); break;
-    case 3:
-        if (b) return hipErrorInvalidValue;
-        launch_one<3, false>(grid, st, A, lda, sa, B, ldb, sb, bias, M, N, K_pad, C, ldc, tiles_m, tiles_n);
-        break;
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    return launch_form(false, A, lda, sa, B, ldb, sb, bias, M, N, K_pad, C, out_dtype, ldc, st);
+}
+
+hipError_t launch_gemm_s4s4(const uint8_t *A, int64_t lda, const float *sa, const uint8_t *B, int64_t ldb,
+                            const float *sb, const float *bias, int64_t M, int64_t N, int64_t K_pad, void *C,
+                            int out_dtype, int64_t ldc, hipStream_t st)
+{
+    return launch_form(true, reinterpret_cast<const int8_t *>(A), lda, sa, B, ldb, sb, bias, M, N, K_pad, C,
+                             out_dtype, ldc, st);
 }
 
 }  // namespace convrot

@@ -477,6 +477,41 @@ hipError_t launch_quant_weight_w4(const void *w, int dtype, int64_t ld_w, int64_
     }
 }
 
+// W4A4 activation preparation: the activation (or SwiGLU) loader, no pre-scale, ConvRot256,
+// 4-bit row quantization, packed codes (ComfyUI Turing Utils README: W4A4 dispatch; the packed
+// format is the weight's)
+template <int DT>
+static hipError_t launch_act_w4(const void *x, int64_t ld_x, bool swiglu, int64_t M, int64_t K, uint8_t *x_s4,
+                                int64_t ld_s4, float *x_scale, bool two_pass, bool transposed, hipStream_t st)
+{
+    using T = typename Elem<DT>::T;
+    const int64_t es = (int64_t)sizeof(T);
+    const auto *xp = static_cast<const T *>(x);
+    const int64_t nb = (K + 255) / 256;
+    int8_t *out = reinterpret_cast<int8_t *>(x_s4);
+    const bool row_ok = ((uintptr_t)x % 16 == 0) && ((ld_x * es) % 16 == 0);
+    if (swiglu) {
+        const bool val_ok = row_ok && ((K * es) % 16 == 0);
+        return launch_rows<SwigluLoader<DT, false>, 4>(SwigluLoader<DT, false>{xp, ld_x, K, row_ok, val_ok, nullptr},
+                                                       M, nb, out, ld_s4, x_scale, two_pass, transposed, st,
+                                                       kMaxGroupsWide);
+    }
+    return launch_rows<ActLoader<DT, false>, 4>(ActLoader<DT, false>{xp, ld_x, K, row_ok, nullptr}, M, nb, out,
+                                                ld_s4, x_scale, two_pass, transposed, st);
+}
+
+hipError_t launch_quant_act_w4(const void *x, int dtype, int64_t ld_x, bool swiglu, int64_t M, int64_t K,
+                               uint8_t *x_s4, int64_t ld_s4, float *x_scale, bool two_pass, bool transposed,
+                               hipStream_t st)
+{
+    switch (dtype) {
+    case 0: return launch_act_w4<0>(x, ld_x, swiglu, M, K, x_s4, ld_s4, x_scale, two_pass, transposed, st);
+    case 1: return launch_act_w4<1>(x, ld_x, swiglu, M, K, x_s4, ld_s4, x_scale, two_pass, transposed, st);
+    case 2: return launch_act_w4<2>(x, ld_x, swiglu, M, K, x_s4, ld_s4, x_scale, two_pass, transposed, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_swiglu(const void *h, int dtype, int64_t ld_h, int64_t M, int64_t F, float *out,
                          int64_t ld_out, hipStream_t st)
 {

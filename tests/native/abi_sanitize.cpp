@@ -156,6 +156,32 @@ int main()
                                           P(), CR_I32, 8, P(), 1 << 20, 0, nullptr), CR_ERR_UNSUPPORTED_DTYPE);
     expect("w4a8 empty", cr_linear_w4a8(nullptr, CR_BF16, 512, 0, 0, 512, Q<uint8_t>(), 256, Q<float>(), 8, nullptr,
                                         nullptr, CR_BF16, 8, nullptr, 0, 0, nullptr), CR_OK);
+    // W4A4
+    expect("aw4 ld_s4 < K_pad/2", cr_quant_act_w4(P(), CR_BF16, 512, 0, 8, 512, Q<uint8_t>(), 240, Q<float>(), 0,
+                                                  nullptr), CR_ERR_INVALID_ARG);
+    expect("aw4 swiglu ld_x < 2K", cr_quant_act_w4(P(), CR_BF16, 1000, 1, 8, 512, Q<uint8_t>(), 256, Q<float>(), 0,
+                                                   nullptr), CR_ERR_INVALID_ARG);
+    expect("aw4 dtype", cr_quant_act_w4(P(), CR_I32, 512, 0, 8, 512, Q<uint8_t>(), 256, Q<float>(), 0, nullptr),
+           CR_ERR_UNSUPPORTED_DTYPE);
+    expect("aw4 empty", cr_quant_act_w4(nullptr, CR_BF16, 512, 0, 0, 512, nullptr, 256, nullptr, 0, nullptr), CR_OK);
+    expect("s4s4 lda < K_pad/2", cr_gemm_s4s4_rowscale(Q<uint8_t>(), 240, Q<float>(), Q<uint8_t>(), 256, Q<float>(),
+                                                       nullptr, 8, 8, 512, P(), CR_BF16, 8, nullptr),
+           CR_ERR_INVALID_ARG);
+    expect("s4s4 misaligned lda", cr_gemm_s4s4_rowscale(Q<uint8_t>(), 264, Q<float>(), Q<uint8_t>(), 256,
+                                                        Q<float>(), nullptr, 8, 8, 512, P(), CR_BF16, 8, nullptr),
+           CR_ERR_MISALIGNED);
+    expect("s4s4 bias on i32", cr_gemm_s4s4_rowscale(Q<uint8_t>(), 256, Q<float>(), Q<uint8_t>(), 256, Q<float>(),
+                                                     Q<float>(), 8, 8, 512, P(), CR_I32, 8, nullptr),
+           CR_ERR_INVALID_ARG);
+    expect("s4s4 empty", cr_gemm_s4s4_rowscale(Q<uint8_t>(), 256, Q<float>(), Q<uint8_t>(), 256, Q<float>(), nullptr,
+                                               8, 0, 512, P(), CR_BF16, 8, nullptr), CR_OK);
+    expect("w4a4 small workspace", cr_linear_w4a4(P(), CR_BF16, 512, 0, 300, 512, Q<uint8_t>(), 256, Q<float>(), 8,
+                                                  nullptr, P(), CR_BF16, 8, P(), cr_linear_w4a4_workspace_bytes(300, 512) - 1,
+                                                  0, nullptr), CR_ERR_TOO_LARGE);
+    expect("w4a4 i32 out", cr_linear_w4a4(P(), CR_BF16, 512, 0, 300, 512, Q<uint8_t>(), 256, Q<float>(), 8, nullptr,
+                                          P(), CR_I32, 8, P(), 1 << 20, 0, nullptr), CR_ERR_UNSUPPORTED_DTYPE);
+    expect("w4a4 empty", cr_linear_w4a4(nullptr, CR_BF16, 512, 0, 0, 512, Q<uint8_t>(), 256, Q<float>(), 8, nullptr,
+                                        nullptr, CR_BF16, 8, nullptr, 0, 0, nullptr), CR_OK);
     auto na = [&](int64_t M, int64_t N, int64_t K, size_t mt) {
         return cr_linear_nvfp4_noalloc(P(), CR_BF16, 5376, 0, M, K, nullptr, Q<uint8_t>(), 2688, Q<uint8_t>(), 336,
                                        Q<float>(), N, nullptr, P(), CR_BF16, 21504, mt, 0, nullptr);
@@ -169,6 +195,11 @@ int main()
         expect("w4a8 without a device", cr_linear_w4a8(P(), CR_BF16, 512, 0, 300, 512, Q<uint8_t>(), 256, Q<float>(),
                                                        8, nullptr, P(), CR_BF16, 8, P(), 1 << 20, 0, nullptr),
                CR_ERR_NO_DEVICE);
+        expect("w4a4 without a device", cr_linear_w4a4(P(), CR_BF16, 512, 0, 300, 512, Q<uint8_t>(), 256, Q<float>(),
+                                                       8, nullptr, P(), CR_BF16, 8, P(), 1 << 20, 0, nullptr),
+               CR_ERR_NO_DEVICE);
+        expect("aw4 without a device", cr_quant_act_w4(P(), CR_BF16, 512, 0, 8, 512, Q<uint8_t>(), 256, Q<float>(), 0,
+                                                       nullptr), CR_ERR_NO_DEVICE);
         expect("layer without a device", lin(300, 1000, 5376, CR_BF16, need, P()), CR_ERR_NO_DEVICE);
         expect("qa without a device", qa(P(), 0, 512, 4, 512, P(), 512, P(), 0), CR_ERR_NO_DEVICE);
     }
