@@ -62,6 +62,10 @@ def lib():
             "or_gemm_s8s4": (C.c_int, [vp, i64, vp, i64, i64, i64, i64, vp, i64]),
             "or_linear_w4a8": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, i64, vp, i64, vp, vp,
                                          C.c_int, i64]),
+            "or_e2m3": (C.c_float, [C.c_uint8]),
+            "or_pack_e2m3": (C.c_int, [vp, i64, i64, i64, vp, i64]),
+            "or_unpack_e2m3": (C.c_int, [vp, i64, i64, i64, vp, i64]),
+            "or_gemm_e2m3": (C.c_int, [vp, i64, vp, i64, i64, i64, i64, vp, i64]),
             "or_quant_act_w4": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, i64, vp]),
             "or_gemm_s4s4": (C.c_int, [vp, i64, vp, i64, i64, i64, i64, vp, i64]),
             "or_linear_w4a4": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, i64, vp, i64, vp, vp,
@@ -389,3 +393,36 @@ def linear_w4a4(x: np.ndarray, x_dtype: int, K: int, swiglu: bool, w_s4: np.ndar
                               _p(w_scale), N, bp, _p(out), out_dtype, N)
     assert rc == 0
     return out
+
+
+# ------------------------------------------- 4-bit codes in E2M3 fields ----
+
+def e2m3(code: int) -> float:
+    return float(lib().or_e2m3(code))
+
+
+def pack_e2m3(q: np.ndarray) -> np.ndarray:
+    """Codes [rows, K_pad] (-7..7, K_pad % 128 == 0) -> E2M3 fields [rows, 3 K_pad / 4] uint8."""
+    q = np.ascontiguousarray(q, np.int8)
+    n, kp = q.shape
+    assert kp % 128 == 0
+    p = np.empty((n, 3 * kp // 4), np.uint8)
+    assert lib().or_pack_e2m3(_p(q), n, kp, kp, _p(p), 3 * kp // 4) == 0
+    return p
+
+
+def unpack_e2m3(p: np.ndarray, K_pad: int) -> np.ndarray:
+    p = np.ascontiguousarray(p, np.uint8)
+    n = p.shape[0]
+    q = np.empty((n, K_pad), np.int8)
+    assert lib().or_unpack_e2m3(_p(p), n, K_pad, p.shape[1], _p(q), K_pad) == 0
+    return q
+
+
+def gemm_e2m3(a: np.ndarray, b: np.ndarray, K_pad: int) -> np.ndarray:
+    a = np.ascontiguousarray(a, np.uint8)
+    b = np.ascontiguousarray(b, np.uint8)
+    M, N = a.shape[0], b.shape[0]
+    acc = np.empty((M, N), np.int32)
+    assert lib().or_gemm_e2m3(_p(a), a.shape[1], _p(b), b.shape[1], M, N, K_pad, _p(acc), N) == 0
+    return acc

@@ -98,6 +98,16 @@ float or_e4m3(uint8_t b)
     return s ? -mag : mag;
 }
 
+/* E2M3 (6-bit float: 1 sign, 2 exponent bits with bias 1, 3 mantissa bits, no inf/NaN).
+ * Exponent field 0 is subnormal: value = m / 8.  Otherwise (1 + m/8) * 2^(e-1); the
+ * integers 0..7 are all exact (largest magnitude 7.5). */
+float or_e2m3(uint8_t code)
+{
+    int s = (code >> 5) & 1, e = (code >> 3) & 3, m = code & 7;
+    float mag = (e == 0) ? (float)m / 8.0f : ldexpf(1.0f + (float)m / 8.0f, e - 1);
+    return s ? -mag : mag;
+}
+
 /* bfloat16 is the top half of a binary32: widening is exact. */
 float or_bf16_to_f32(uint16_t h) { return bits_to_f32((uint32_t)h << 16); }
 
@@ -627,6 +637,87 @@ int or_linear_w4a8(const void *x, int x_dtype, int64_t ld_x, int swiglu, int64_t
         rc = 0;
     }
     free(xq); free(xs); free(acc);
+    return rc;
+}
+
+/* --------------------------------------- 4-bit codes in E2M3 fields (execution form) ---- */
+
+/* This library's second storage form of 4-bit code rows (the pages describe none): every
+ * code -7..7 is stored as the E2M3 number of the same value, so that matrix cores with
+ * 6-bit floating-point inputs multiply the codes directly and exactly.  A row of K_pad
+ * codes takes 3 K_pad / 4 bytes in units of 96 bytes per 128 codes; a unit's quarters of
+ * 32 codes Q0 (codes 0..31), Q1, Q2, Q3 are stored in the order Q0, Q2, Q1, Q3, 24 bytes
+ * each, code e of a quarter in bits 6e .. 6e+5 of its 24 bytes read as one little-endian
+ * number.  The codes follow the column order of the flags, as in the nibble form. */
+
+/* the code whose E2M3 value is q (+0 for 0), found by search over the 64 codes */
+static uint8_t e2m3_code_of(int q)
+{
+    for (int c = 0; c < 64; c++)
+        if (or_e2m3((uint8_t)c) == (float)q && !(q == 0 && c != 0)) return (uint8_t)c;
+    return 0xFF;
+}
+
+static int64_t e2m3_quarter_offset(int64_t g)   /* byte offset of quarter g (32 codes) in a row */
+{
+    static const int slot[4] = {0, 2, 1, 3};
+    return 96 * (g / 4) + 24 * slot[g % 4];
+}
+
+/* Codes q [n_rows, ld_q] (each -7..7) -> E2M3 fields p [n_rows, ld_p bytes]; returns 0, or
+ * -1 if a code is out of range. */
+int or_pack_e2m3(const int8_t *q, int64_t n_rows, int64_t K_pad, int64_t ld_q, uint8_t *p, int64_t ld_p)
+{
+    uint8_t table[15];
+    for (int v = -7; v <= 7; v++) table[v + 7] = e2m3_code_of(v);
+    for (int64_t n = 0; n < n_rows; n++)
+        for (int64_t g = 0; g < K_pad / 32; g++) {
+            uint8_t *f = p + n * ld_p + e2m3_quarter_offset(g);
+            memset(f, 0, 24);
+            for (int e = 0; e < 32; e++) {
+                const int v = q[n * ld_q + 32 * g + e];
+                if (v < -7 || v > 7) return -1;
+                const uint32_t c = table[v + 7];
+                for (int bit = 0; bit < 6; bit++)
+                    if ((c >> bit) & 1) f[(6 * e + bit) / 8] |= (uint8_t)(1u << ((6 * e + bit) % 8));
+            }
+        }
+    return 0;
+}
+
+/* The inverse: every field decoded as E2M3; returns 0, or -1 if a value is not an integer
+ * in -7..7. */
+int or_unpack_e2m3(const uint8_t *p, int64_t n_rows, int64_t K_pad, int64_t ld_p, int8_t *q, int64_t ld_q)
+{
+    for (int64_t n = 0; n < n_rows; n++)
+        for (int64_t g = 0; g < K_pad / 32; g++) {
+            const uint8_t *f = p + n * ld_p + e2m3_quarter_offset(g);
+            for (int e = 0; e < 32; e++) {
+                uint8_t c = 0;
+                for (int bit = 0; bit < 6; bit++)
+                    if ((f[(6 * e + bit) / 8] >> ((6 * e + bit) % 8)) & 1) c |= (uint8_t)(1u << bit);
+                const float v = or_e2m3(c);
+                if (v != floorf(v) || v < -7.0f || v > 7.0f) return -1;
+                q[n * ld_q + 32 * g + e] = (int8_t)v;
+            }
+        }
+    return 0;
+}
+
+/* acc[m, n] = sum_k A[m, k] B[n, k] over the codes of two E2M3-field rows. */
+int or_gemm_e2m3(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb, int64_t M, int64_t N,
+                 int64_t K_pad, int32_t *acc, int64_t ldc)
+{
+    int8_t *aq = (int8_t *)malloc((size_t)(M > 0 ? M : 1) * (size_t)K_pad);
+    int8_t *bq = (int8_t *)malloc((size_t)(N > 0 ? N : 1) * (size_t)K_pad);
+    int rc = -1;
+    if (aq && bq && or_unpack_e2m3(A, M, K_pad, lda, aq, K_pad) == 0 &&
+        or_unpack_e2m3(B, N, K_pad, ldb, bq, K_pad) == 0) {
+        or_gemm_s8(aq, K_pad, bq, K_pad, M, N, K_pad, acc, ldc);
+        rc = 0;
+    }
+    free(aq);
+    free(bq);
     return rc;
 }
 

@@ -53,6 +53,11 @@ int or_gemm_s8s4(const int8_t *A, int64_t lda, const uint8_t *B, int64_t ldb, in
 int or_linear_w4a8(const void *x, int x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K, const uint8_t *w_s4,
                    int64_t ld_s4, const float *w_scale, int64_t N, const float *bias, void *out, int out_dtype,
                    int64_t ldc);
+float or_e2m3(uint8_t code);
+int or_pack_e2m3(const int8_t *q, int64_t n_rows, int64_t K_pad, int64_t ld_q, uint8_t *p, int64_t ld_p);
+int or_unpack_e2m3(const uint8_t *p, int64_t n_rows, int64_t K_pad, int64_t ld_p, int8_t *q, int64_t ld_q);
+int or_gemm_e2m3(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb, int64_t M, int64_t N, int64_t K_pad,
+                 int32_t *acc, int64_t ldc);
 int or_quant_act_w4(const void *x, int dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K, uint8_t *x_s4,
                     int64_t ld_s4, float *x_scale);
 int or_gemm_s4s4(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb, int64_t M, int64_t N, int64_t K_pad,
@@ -273,6 +278,18 @@ static void w4a8_case(int64_t M, int64_t N, int64_t K)
         free(hp);
     }
     for (int dt = 0; dt < 3; dt++) CHECK(or_linear_w4a4(x, 0, K, 0, M, K, p, lp, s, N, s, y, dt, N) == 0, "w4a4");
+    /* the E2M3 field form of the same codes: exactly 3 K_pad / 4 bytes per row */
+    {
+        const int64_t l6 = 3 * kp / 4;
+        uint8_t *f = xmalloc((size_t)(N * l6));
+        int8_t *q2 = xmalloc((size_t)(N * kp));
+        CHECK(or_pack_e2m3(q, N, kp, kp, f, l6) == 0, "pack_e2m3");
+        CHECK(or_unpack_e2m3(f, N, kp, l6, q2, kp) == 0 && memcmp(q, q2, (size_t)(N * kp)) == 0, "unpack_e2m3");
+        int32_t *acc2 = xmalloc(sizeof(int32_t) * (size_t)(N * N));
+        CHECK(or_gemm_e2m3(f, l6, f, l6, N, N, kp, acc2, N) == 0, "gemm_e2m3");
+        for (int c = 0; c < 64; c++) (void)or_e2m3((uint8_t)c);
+        free(f); free(q2); free(acc2);
+    }
     free(xp); free(xs);
     float y4[256];
     for (int i = 0; i < 256; i++) y4[i] = (float)(int)(next_u32() % 15) - 7.0f;

@@ -1,0 +1,63 @@
+"""Pins of the oracle's second storage form of 4-bit code rows: each code -7..7 stored as
+the E2M3 (6-bit float) number of the same value, in 96-byte units of 128 codes (quarters
+Q0, Q2, Q1, Q3 of 24 bytes, code e of a quarter in bits 6e..6e+5).  The pages describe no
+W4A4 format (ComfyUI Turing Utils README names W4A4 dispatch only); this form exists so that
+6-bit floating-point matrix cores multiply the codes exactly."""
+import numpy as np
+import pytest
+
+import oracle
+from test_oracle_formats import minifloat
+
+
+@pytest.fixture(scope="module")
+def orc():
+    oracle.build.build()
+    return oracle
+
+
+def test_e2m3_decoder_matches_the_generic_minifloat(orc):
+    """All 64 codes against the minifloat decoder validated on torch's FP8 formats (2
+    exponent bits, bias 1, 3 mantissa bits, no inf/NaN)."""
+    for c in range(64):
+        assert orc.e2m3(c) == minifloat(c, 2, 3, 1), c
+    assert orc.e2m3(0b011110) == 7.0 and orc.e2m3(0b011111) == 7.5 and orc.e2m3(0b000001) == 0.125
+
+
+def test_hand_worked_unit(orc):
+    """Codes 1 at k = 0 and 1, 3 at 32, -7 at 64, -1 at 127 of a 128-code row.  E2M3: 1 =
+    0b001000, 3 = 1.5 * 2 = 0b010100, 7 = 1.75 * 4 = 0b011110, sign bit 0b100000.  k = 0 ->
+    byte 0 = 0x08; k = 1 -> bits 6..11: byte 0 bits 6, 7 = 0, byte 1 = 0x08 >> 2 = 0x02;
+    k = 32 (Q1, stored third) -> byte 48 = 0x14; k = 64 (Q2, stored second) -> byte 24 =
+    0x3E; k = 127 (Q3, e = 31, bits 186..191) -> byte 72 + 23 = 95, bits 2..7: 0x28 << 2 =
+    0xA0."""
+    q = np.zeros((1, 128), np.int8)
+    q[0, [0, 1, 32, 64, 127]] = [1, 1, 3, -7, -1]
+    p = orc.pack_e2m3(q)
+    assert p.shape == (1, 96)
+    want = np.zeros(96, np.uint8)
+    want[[0, 1, 24, 48, 95]] = [0x08, 0x02, 0x3E, 0x14, 0xA0]
+    assert np.array_equal(p[0], want)
+
+
+def test_round_trip_and_agreement_with_the_nibble_form(orc):
+    rng = np.random.default_rng(3)
+    q = rng.integers(-7, 8, (9, 768), dtype=np.int8)
+    p = orc.pack_e2m3(q)
+    assert p.shape == (9, 576)
+    assert np.array_equal(orc.unpack_e2m3(p, 768), q)
+    assert np.array_equal(orc.unpack_s4(orc.pack_s4(q), 768), q)
+    # every value occurs, in every quarter position of a unit
+    for v in range(-7, 8):
+        qq = np.full((1, 128), v, np.int8)
+        assert np.array_equal(orc.unpack_e2m3(orc.pack_e2m3(qq), 128), qq)
+
+
+def test_gemm_e2m3_int64_brute_force(orc):
+    rng = np.random.default_rng(4)
+    for (M, N, K_pad) in [(1, 1, 256), (7, 13, 512)]:
+        qa = rng.integers(-7, 8, (M, K_pad), dtype=np.int8)
+        qb = rng.integers(-7, 8, (N, K_pad), dtype=np.int8)
+        ref = qa.astype(np.int64) @ qb.astype(np.int64).T
+        got = orc.gemm_e2m3(orc.pack_e2m3(qa), orc.pack_e2m3(qb), K_pad)
+        assert np.array_equal(got.astype(np.int64), ref)
