@@ -1,6 +1,7 @@
 """Pins of the oracle's second storage form of 4-bit code rows: each code -7..7 stored as
 the E2M3 (6-bit float) number of the same value, in 96-byte units of 128 codes (quarters
-Q0, Q2, Q1, Q3 of 24 bytes, code e of a quarter in bits 6e..6e+5).  The pages describe no
+of 32 codes as 192-bit fields, code e in bits 6e..6e+5; the fields' first 16 bytes in the
+order Q0, Q2, Q1, Q3, then their last 8 bytes in the same order).  The pages describe no
 W4A4 format (ComfyUI Turing Utils README names W4A4 dispatch only); this form exists so that
 6-bit floating-point matrix cores multiply the codes exactly."""
 import numpy as np
@@ -25,19 +26,22 @@ def test_e2m3_decoder_matches_the_generic_minifloat(orc):
 
 
 def test_hand_worked_unit(orc):
-    """Codes 1 at k = 0 and 1, 3 at 32, -7 at 64, -1 at 127 of a 128-code row.  E2M3: 1 =
-    0b001000, 3 = 1.5 * 2 = 0b010100, 7 = 1.75 * 4 = 0b011110, sign bit 0b100000.  k = 0 ->
-    byte 0 = 0x08; k = 1 -> bits 6..11: byte 0 bits 6, 7 = 0, byte 1 = 0x08 >> 2 = 0x02;
-    k = 32 (Q1, stored third) -> byte 48 = 0x14; k = 64 (Q2, stored second) -> byte 24 =
-    0x3E; k = 127 (Q3, e = 31, bits 186..191) -> byte 72 + 23 = 95, bits 2..7: 0x28 << 2 =
-    0xA0."""
+    """Codes 1 at k = 0 and 1, 3 at 32, -7 at 64, 5 at 85, -1 at 127 of a 128-code row.
+    E2M3: 1 = 0b001000, 3 = 1.5 * 2 = 0b010100, 5 = 1.25 * 4 = 0b011010, 7 = 1.75 * 4 =
+    0b011110, sign bit 0b100000.  Heads (bits 0..127) of Q0 Q2 Q1 Q3 at bytes 0, 16, 32, 48,
+    tails (bits 128..191) at 64, 72, 80, 88.  k = 0 -> byte 0 = 0x08; k = 1 -> bits 6..11:
+    byte 0 bits 6, 7 = 0, byte 1 = 0x08 >> 2 = 0x02; k = 32 (Q1 head) -> byte 32 = 0x14;
+    k = 64 (Q2 head) -> byte 16 = 0x3E; k = 85 (Q2, e = 21, bits 126..131: the last two bits
+    of the head, the first four of the tail) -> 0b011010: bits 0, 1 = 0b10 into byte 16 + 15
+    bits 6, 7 (0x80), bits 2..5 = 0b0110 into byte 72 bits 0..3 (0x06); k = 127 (Q3, e = 31,
+    bits 186..191, the tail's byte 7 bits 2..7) -> byte 88 + 7 = 95 = 0x28 << 2 = 0xA0."""
     q = np.zeros((1, 128), np.int8)
-    q[0, [0, 1, 32, 64, 127]] = [1, 1, 3, -7, -1]
+    q[0, [0, 1, 32, 64, 85, 127]] = [1, 1, 3, -7, 5, -1]
     p = orc.pack_e2m3(q)
     assert p.shape == (1, 96)
     want = np.zeros(96, np.uint8)
-    want[[0, 1, 24, 48, 95]] = [0x08, 0x02, 0x3E, 0x14, 0xA0]
-    assert np.array_equal(p[0], want)
+    want[[0, 1, 32, 16, 31, 72, 95]] = [0x08, 0x02, 0x14, 0x3E, 0x80, 0x06, 0xA0]
+    assert np.array_equal(p[0], want), np.nonzero(p[0])
 
 
 def test_round_trip_and_agreement_with_the_nibble_form(orc):
