@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "ms/layer and INT8 TOPS (fraction of peak), QKV and FFN-down at M=19989"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 MFMA, TOP/s
+PEAK_FP6_TOPS = 10100.0      # MI355X dense FP6 / FP4 MFMA, TFLOP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 BT = 2                       # CR_FLAG_BLOCK_TRANSPOSED: the order cr_linear_nvfp4 uses inside
 # Decode-inside-GEMM: vector instructions per weight element at the minimum (decode: one
@@ -518,9 +519,32 @@ def w4a4_layers(torch, rbl, synth, dev, names, s_main, n=20):
         torch.cuda.synchronize()
         if not torch.equal(out, out2):
             raise SystemExit(f"bench: cr_linear_w4a4 differs from activation prep + W4A4 GEMM on {name}")
+        del qx, ws
+        # the same layer on the 6-bit matrix cores (codes as E2M3 fields): identical outputs
+        wf = synth.make_weight_f32(w).to(dev)
+        lf = w.K_pad // 4 * 3
+        p6 = torch.empty(w.N, lf, dtype=torch.uint8, device=dev)
+        sw6 = torch.empty(w.N, dtype=torch.float32, device=dev)
+        rbl.cr_quant_weight_w4_e2m3(wf, w.K, p6, sw6, BT, stream=s_main)
+        torch.cuda.synchronize()
+        del wf
+        out6 = torch.empty_like(out)
+        ws6 = torch.empty(rbl.cr_linear_w4a4_e2m3_workspace_bytes(w.M, w.K), dtype=torch.uint8, device=dev)
+        qx6 = torch.empty(w.M, lf, dtype=torch.uint8, device=dev)
+        act6 = lambda: rbl.cr_quant_act_w4_e2m3(x, w.K, w.swiglu, qx6, sx, BT, stream=s_main)  # noqa: E731
+        layer6 = lambda: rbl.cr_linear_w4a4_e2m3(x, w.K, w.swiglu, p6, sw6, out6, ws6, flags=BT,  # noqa: E731
+                                                 stream=s_main)
+        gemm6 = lambda: rbl.cr_gemm_e2m3_rowscale(qx6, sx, p6, sw6, out2, stream=s_main)  # noqa: E731
+        t_layer6 = time_loop(torch, layer6, s_main, n=n)
+        t_act6 = time_loop(torch, act6, s_main, n=n)
+        t_gemm6 = time_loop(torch, gemm6, s_main, n=n)
+        torch.cuda.synchronize()
+        if not (torch.equal(out6, out) and torch.equal(out2, out)):
+            raise SystemExit(f"bench: the E2M3 W4A4 layer differs from the nibble-form layer on {name}")
         ops = 2 * w.M * w.N * w.K_pad
         in_cols = 2 * w.K if w.swiglu else w.K
         act_bytes = w.M * (in_cols * x.element_size() + w.K_pad // 2 + 4)
+        act6_bytes = w.M * (in_cols * x.element_size() + lf + 4)
         info[name] = {
             "M": w.M, "N": w.N, "K": w.K, "K_pad": w.K_pad, "swiglu": w.swiglu,
             "layer_ms": round(t_layer, 4),
@@ -529,8 +553,16 @@ def w4a4_layers(torch, rbl, synth, dev, names, s_main, n=20):
             "gemm_ms": round(t_gemm, 4),
             "gemm_tops": round(ops / (t_gemm * 1e-3) / 1e12, 1),
             "gemm_frac_peak": round(ops / (t_gemm * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+            "e2m3": {
+                "layer_ms": round(t_layer6, 4),
+                "act_prep_ms": round(t_act6, 4),
+                "act_prep_gbs": round(act6_bytes / (t_act6 * 1e-3) / 1e9, 1),
+                "gemm_ms": round(t_gemm6, 4),
+                "gemm_tops": round(ops / (t_gemm6 * 1e-3) / 1e12, 1),
+                "gemm_frac_fp6_peak": round(ops / (t_gemm6 * 1e-3) / 1e12 / PEAK_FP6_TOPS, 4),
+            },
         }
-        del x, p, sw, out, out2, ws, qx, sx
+        del x, p, sw, out, out2, sx, p6, sw6, out6, ws6, qx6
     return info
 
 
@@ -719,6 +751,8 @@ def main():
         print(f"bench: W4A4 variant on {w44_names}", file=sys.stderr, flush=True)
         w44_info = w4a4_layers(torch, rbl, synth, dev, w44_names, s_main, n=max(5, K // 2))
         w44_info["value_ms_per_layer"] = round(sum(v["layer_ms"] for v in w44_info.values()) / len(w44_names), 4)
+        w44_info["e2m3_value_ms_per_layer"] = round(
+            sum(w44_info[k]["e2m3"]["layer_ms"] for k in w44_names) / len(w44_names), 4)
 
     short_info = None
     rows_list = [int(v) for v in args.short_batches.split(",") if v.strip()]

@@ -360,6 +360,37 @@ cr_status cr_linear_w4a4(const void *x, cr_dtype x_dtype, int64_t ld_x, int swig
                          uint32_t flags, hipStream_t stream);
 
 /*
+ * W4A4 on the 6-bit matrix cores.  The same 4-bit codes in a second storage form (this
+ * library's; the pages describe none): each code -7..7 stored as the E2M3 number of equal
+ * value (1 sign, 2 exponent bits with bias 1, 3 mantissa bits), so that gfx950's 6-bit
+ * floating-point matrix instructions multiply the codes exactly; the sums are those of the
+ * nibble form, bit for bit.  A row of K_pad codes takes 3 K_pad / 4 bytes in units of 96
+ * bytes per 128 codes: each quarter of 32 codes is a 192-bit field with code e in bits
+ * 6e .. 6e+5 (little-endian); a unit holds the first 16 bytes of the fields of quarters
+ * Q0, Q2, Q1, Q3, then their last 8 bytes in the same order.  Column order as for the
+ * nibble form (flags).
+ *
+ * cr_quant_weight_w4_e2m3 and cr_quant_act_w4_e2m3 are cr_quant_weight_w4 and
+ * cr_quant_act_w4 with that output form: w_f6 / x_f6 [rows, ld_f6] bytes, ld_f6 >= 3 K_pad / 4,
+ * a multiple of 16.  cr_gemm_e2m3_rowscale is cr_gemm_s4s4_rowscale on two such operands
+ * (lda, ldb >= 3 K_pad / 4, multiples of 16).  cr_linear_w4a4_e2m3 is cr_linear_w4a4 with the
+ * weight in that form and cr_linear_w4a4_e2m3_workspace_bytes(M, K) bytes of workspace.
+ */
+cr_status cr_quant_weight_w4_e2m3(const void *w, cr_dtype w_dtype, int64_t ld_w, int64_t N, int64_t K,
+                                  uint8_t *w_f6, int64_t ld_f6, float *w_scale, uint32_t flags, hipStream_t stream);
+cr_status cr_quant_act_w4_e2m3(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
+                               uint8_t *x_f6, int64_t ld_f6, float *x_scale, uint32_t flags, hipStream_t stream);
+cr_status cr_gemm_e2m3_rowscale(const uint8_t *a_f6, int64_t lda, const float *a_scale,
+                                const uint8_t *b_f6, int64_t ldb, const float *b_scale, const float *bias,
+                                int64_t M, int64_t N, int64_t K_pad, void *c, cr_dtype c_dtype, int64_t ldc,
+                                hipStream_t stream);
+size_t cr_linear_w4a4_e2m3_workspace_bytes(int64_t M, int64_t K);
+cr_status cr_linear_w4a4_e2m3(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
+                              const uint8_t *w_f6, int64_t ld_f6, const float *w_scale, int64_t N,
+                              const float *bias, void *out, cr_dtype out_dtype, int64_t ldc, void *workspace,
+                              size_t ws_bytes, uint32_t flags, hipStream_t stream);
+
+/*
  * The layer for callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): cr_linear_nvfp4_ex with serial
  * staging on `stream` and, as its workspace, a device array of CR_NOALLOC_SCRATCH_BYTES

@@ -84,6 +84,12 @@ def lib() -> C.CDLL:
             "cr_linear_w4a4_workspace_bytes": (sz, [i64, i64]),
             "cr_linear_w4a4": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, i64, vp, i64, vp, vp, C.c_int,
                                          i64, vp, sz, u32, vp]),
+            "cr_quant_weight_w4_e2m3": (C.c_int, [vp, C.c_int, i64, i64, i64, vp, i64, vp, u32, vp]),
+            "cr_quant_act_w4_e2m3": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, i64, vp, u32, vp]),
+            "cr_gemm_e2m3_rowscale": (C.c_int, [vp, i64, vp, vp, i64, vp, vp, i64, i64, i64, vp, C.c_int, i64, vp]),
+            "cr_linear_w4a4_e2m3_workspace_bytes": (sz, [i64, i64]),
+            "cr_linear_w4a4_e2m3": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, i64, vp, i64, vp, vp,
+                                              C.c_int, i64, vp, sz, u32, vp]),
             "cr_gemm_nvfp4_fused": (C.c_int, [vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, i64, i64, i64, vp,
                                               C.c_int, i64, u32, vp]),
         }
@@ -323,6 +329,45 @@ def cr_linear_w4a4(x, K, swiglu, w_s4, w_scale, out, workspace, bias=None, flags
         0 if workspace is None else workspace.numel() * workspace.element_size(), flags, _stream(stream)))
 
 
+def cr_quant_weight_w4_e2m3(w, K, w_f6, w_scale, flags=0, stream=None):
+    N, ld_w = _rows_ld(w)
+    _, ld_f6 = _rows_ld(w_f6)
+    _check("cr_quant_weight_w4_e2m3", lib().cr_quant_weight_w4_e2m3(
+        _ptr(w), _TORCH_TO_CR[w.dtype], ld_w, N, K, _ptr(w_f6), ld_f6, _ptr(w_scale), flags, _stream(stream)))
+
+
+def cr_quant_act_w4_e2m3(x, K, swiglu, x_f6, x_scale, flags=0, stream=None):
+    M, ld_x = _rows_ld(x)
+    _, ld_f6 = _rows_ld(x_f6)
+    _check("cr_quant_act_w4_e2m3", lib().cr_quant_act_w4_e2m3(
+        _ptr(x), _TORCH_TO_CR[x.dtype], ld_x, int(bool(swiglu)), M, K, _ptr(x_f6), ld_f6, _ptr(x_scale), flags,
+        _stream(stream)))
+
+
+def cr_gemm_e2m3_rowscale(a_f6, a_scale, b_f6, b_scale, c, bias=None, K_pad=None, stream=None):
+    M, lda = _rows_ld(a_f6)
+    N, ldb = _rows_ld(b_f6)
+    _, ldc = _rows_ld(c)
+    kp = 4 * a_f6.shape[1] // 3 if K_pad is None else K_pad
+    _check("cr_gemm_e2m3_rowscale", lib().cr_gemm_e2m3_rowscale(
+        _ptr(a_f6), lda, _ptr(a_scale), _ptr(b_f6), ldb, _ptr(b_scale), _ptr(bias), M, N, kp,
+        _ptr(c), _TORCH_TO_CR[c.dtype], ldc, _stream(stream)))
+
+
+def cr_linear_w4a4_e2m3_workspace_bytes(M, K) -> int:
+    return int(lib().cr_linear_w4a4_e2m3_workspace_bytes(M, K))
+
+
+def cr_linear_w4a4_e2m3(x, K, swiglu, w_f6, w_scale, out, workspace, bias=None, flags=0, stream=None):
+    M, ld_x = _rows_ld(x)
+    N, ld_f6 = _rows_ld(w_f6)
+    _, ldc = _rows_ld(out)
+    _check("cr_linear_w4a4_e2m3", lib().cr_linear_w4a4_e2m3(
+        _ptr(x), _TORCH_TO_CR[x.dtype], ld_x, int(bool(swiglu)), M, K, _ptr(w_f6), ld_f6, _ptr(w_scale), N,
+        _ptr(bias), _ptr(out), _TORCH_TO_CR[out.dtype], ldc, _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), flags, _stream(stream)))
+
+
 # ---------------------------------------------------------------- conveniences ----
 
 def quant_act(x: torch.Tensor, K: int | None = None, swiglu: bool = False, flags: int = 0,
@@ -429,4 +474,36 @@ def linear_w4a4(x, w_s4, w_scale, K, out_dtype=torch.bfloat16, swiglu=False, bia
         out = torch.empty(M, N, dtype=out_dtype, device=x.device)
     ws = torch.empty(max(1, cr_linear_w4a4_workspace_bytes(M, K)), dtype=torch.uint8, device=x.device)
     cr_linear_w4a4(x, K, swiglu, w_s4, w_scale, out, ws, bias=bias, flags=flags)
+    return out
+
+
+def quant_weight_w4_e2m3(w: torch.Tensor, K: int | None = None, flags: int = 0):
+    """(4-bit codes as E2M3 fields [N, 3 K_pad / 4] uint8, scales [N] fp32) of a dense weight."""
+    if K is None:
+        K = w.shape[1]
+    kp = padded_k(K)
+    q = torch.empty(w.shape[0], kp // 4 * 3, dtype=torch.uint8, device=w.device)
+    s = torch.empty(w.shape[0], dtype=torch.float32, device=w.device)
+    cr_quant_weight_w4_e2m3(w, K, q, s, flags)
+    return q, s
+
+
+def quant_act_w4_e2m3(x: torch.Tensor, K: int | None = None, swiglu: bool = False, flags: int = 0):
+    """(4-bit codes as E2M3 fields [M, 3 K_pad / 4] uint8, scales [M] fp32) of X or SwiGLU(H)."""
+    if K is None:
+        K = x.shape[1] // 2 if swiglu else x.shape[1]
+    kp = padded_k(K)
+    q = torch.empty(x.shape[0], kp // 4 * 3, dtype=torch.uint8, device=x.device)
+    s = torch.empty(x.shape[0], dtype=torch.float32, device=x.device)
+    cr_quant_act_w4_e2m3(x, K, swiglu, q, s, flags)
+    return q, s
+
+
+def linear_w4a4_e2m3(x, w_f6, w_scale, K, out_dtype=torch.bfloat16, swiglu=False, bias=None, flags=0, out=None):
+    """y = x W^T (+ b) through the W4A4 route on the 6-bit matrix cores."""
+    M, N = x.shape[0], w_f6.shape[0]
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype, device=x.device)
+    ws = torch.empty(max(1, cr_linear_w4a4_e2m3_workspace_bytes(M, K)), dtype=torch.uint8, device=x.device)
+    cr_linear_w4a4_e2m3(x, K, swiglu, w_f6, w_scale, out, ws, bias=bias, flags=flags)
     return out

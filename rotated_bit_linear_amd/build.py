@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libconvrot.so")
-SOURCES = ["api.cpp", "quant_act.hip", "prep_weight.hip", "gemm_s8.hip", "gemm_fused.hip", "gemm_s8s4.hip"]
+SOURCES = ["api.cpp", "quant_act.hip", "prep_weight.hip", "gemm_s8.hip", "gemm_fused.hip", "gemm_s8s4.hip", "gemm_e2m3.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -780,6 +780,113 @@ cr_status cr_linear_w4a4(const void *x, cr_dtype x_dtype, int64_t ld_x, int swig
                                               (int)out_dtype, ldc, stream));
 }
 
+cr_status cr_quant_weight_w4_e2m3(const void *w, cr_dtype w_dtype, int64_t ld_w, int64_t N, int64_t K,
+                                  uint8_t *w_f6, int64_t ld_f6, float *w_scale, uint32_t flags, hipStream_t stream)
+{
+    if (N > 0 && (!w || !w_f6 || !w_scale)) return CR_ERR_INVALID_ARG;
+    if (w_dtype != CR_BF16 && w_dtype != CR_FP16 && w_dtype != CR_FP32) return CR_ERR_UNSUPPORTED_DTYPE;
+    if (N < 0 || K < 1 || N > kMaxRows) return CR_ERR_INVALID_ARG;
+    if (check_flags(flags) != CR_OK) return CR_ERR_INVALID_ARG;
+    const int64_t kp = pad256(K);
+    if (kp > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
+    if (ld_w < K || ld_f6 < kp / 4 * 3) return CR_ERR_INVALID_ARG;
+    if (!aligned(w, 16) || (ld_w * elem_size(w_dtype)) % 16 != 0) return CR_ERR_MISALIGNED;
+    if (!aligned(w_f6, 16) || ld_f6 % 16 != 0 || !aligned(w_scale, 4)) return CR_ERR_MISALIGNED;
+    if (N == 0) return CR_OK;
+    cr_status s = current_device_ok();
+    if (s != CR_OK) return s;
+    return from_hip(convrot::launch_quant_weight_e2m3(w, (int)w_dtype, ld_w, N, K, w_f6, ld_f6, w_scale,
+                                                      (flags & CR_FLAG_FORCE_TWO_PASS) != 0,
+                                                      (flags & CR_FLAG_BLOCK_TRANSPOSED) != 0, stream));
+}
+
+cr_status cr_quant_act_w4_e2m3(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
+                               uint8_t *x_f6, int64_t ld_f6, float *x_scale, uint32_t flags, hipStream_t stream)
+{
+    if (M > 0 && (!x || !x_f6 || !x_scale)) return CR_ERR_INVALID_ARG;
+    if (x_dtype != CR_BF16 && x_dtype != CR_FP16 && x_dtype != CR_FP32) return CR_ERR_UNSUPPORTED_DTYPE;
+    if (M < 0 || K < 1 || M > kMaxRows) return CR_ERR_INVALID_ARG;
+    if (check_flags(flags) != CR_OK) return CR_ERR_INVALID_ARG;
+    if (swiglu && K > (int64_t)1 << 40) return CR_ERR_TOO_LARGE;
+    const int64_t kp = pad256(K);
+    if (kp > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
+    if (ld_x < (swiglu ? 2 * K : K) || ld_f6 < kp / 4 * 3) return CR_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || (ld_x * elem_size(x_dtype)) % 16 != 0) return CR_ERR_MISALIGNED;
+    if (!aligned(x_f6, 16) || ld_f6 % 16 != 0 || !aligned(x_scale, 4)) return CR_ERR_MISALIGNED;
+    if (M == 0) return CR_OK;
+    cr_status s = current_device_ok();
+    if (s != CR_OK) return s;
+    return from_hip(convrot::launch_quant_act_e2m3(x, (int)x_dtype, ld_x, swiglu != 0, M, K, x_f6, ld_f6, x_scale,
+                                                   (flags & CR_FLAG_FORCE_TWO_PASS) != 0,
+                                                   (flags & CR_FLAG_BLOCK_TRANSPOSED) != 0, stream));
+}
+
+cr_status cr_gemm_e2m3_rowscale(const uint8_t *a_f6, int64_t lda, const float *a_scale,
+                                const uint8_t *b_f6, int64_t ldb, const float *b_scale, const float *bias,
+                                int64_t M, int64_t N, int64_t K_pad, void *c, cr_dtype c_dtype, int64_t ldc,
+                                hipStream_t stream)
+{
+    if ((M > 0 && !a_f6) || (N > 0 && !b_f6) || (M > 0 && N > 0 && !c)) return CR_ERR_INVALID_ARG;
+    if (c_dtype != CR_BF16 && c_dtype != CR_FP16 && c_dtype != CR_FP32 && c_dtype != CR_I32)
+        return CR_ERR_UNSUPPORTED_DTYPE;
+    if (c_dtype != CR_I32 && ((M > 0 && !a_scale) || (N > 0 && !b_scale))) return CR_ERR_INVALID_ARG;
+    if (bias && c_dtype == CR_I32) return CR_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K_pad < 1 || K_pad % 256 != 0 || M > kMaxRows || N > kMaxRows) return CR_ERR_INVALID_ARG;
+    if (((M + 255) / 256) * ((N + 255) / 256) > (int64_t)(UINT32_MAX / 512)) return CR_ERR_TOO_LARGE;
+    if (K_pad > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
+    if (lda < K_pad / 4 * 3 || ldb < K_pad / 4 * 3 || ldc < N) return CR_ERR_INVALID_ARG;   // lda, ldb in bytes
+    if (!aligned(a_f6, 16) || !aligned(b_f6, 16) || lda % 16 != 0 || ldb % 16 != 0) return CR_ERR_MISALIGNED;
+    if (!aligned(c, (size_t)elem_size(c_dtype))) return CR_ERR_MISALIGNED;
+    if ((a_scale && !aligned(a_scale, 4)) || (b_scale && !aligned(b_scale, 4)) || (bias && !aligned(bias, 4)))
+        return CR_ERR_MISALIGNED;
+    if (M == 0 || N == 0) return CR_OK;
+    cr_status s = current_device_ok();
+    if (s != CR_OK) return s;
+    return from_hip(convrot::launch_gemm_e2m3(a_f6, lda, a_scale, b_f6, ldb, b_scale, bias, M, N, K_pad, c,
+                                              (int)c_dtype, ldc, stream));
+}
+
+size_t cr_linear_w4a4_e2m3_workspace_bytes(int64_t M, int64_t K)
+{
+    if (M < 1 || K < 1 || pad256(K) > CR_MAX_K_PAD) return 0;
+    return up256(up256((size_t)M * (size_t)(pad256(K) / 4 * 3)) + (size_t)M * 4);
+}
+
+cr_status cr_linear_w4a4_e2m3(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
+                              const uint8_t *w_f6, int64_t ld_f6, const float *w_scale, int64_t N,
+                              const float *bias, void *out, cr_dtype out_dtype, int64_t ldc, void *workspace,
+                              size_t ws_bytes, uint32_t flags, hipStream_t stream)
+{
+    if (x_dtype != CR_BF16 && x_dtype != CR_FP16 && x_dtype != CR_FP32) return CR_ERR_UNSUPPORTED_DTYPE;
+    if (out_dtype != CR_BF16 && out_dtype != CR_FP16 && out_dtype != CR_FP32) return CR_ERR_UNSUPPORTED_DTYPE;
+    if (M < 0 || N < 0 || K < 1 || M > kMaxRows || N > kMaxRows) return CR_ERR_INVALID_ARG;
+    if (check_flags(flags) != CR_OK) return CR_ERR_INVALID_ARG;
+    if (swiglu && K > (int64_t)1 << 40) return CR_ERR_TOO_LARGE;
+    const int64_t kp = pad256(K);
+    if (kp > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
+    if (((M + 255) / 256) * ((N + 255) / 256) > (int64_t)(UINT32_MAX / 512)) return CR_ERR_TOO_LARGE;
+    if (ld_x < (swiglu ? 2 * K : K) || ld_f6 < kp / 4 * 3 || ldc < N) return CR_ERR_INVALID_ARG;
+    if ((M > 0 && !x) || (N > 0 && (!w_f6 || !w_scale)) || (M > 0 && N > 0 && !out)) return CR_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || (ld_x * elem_size(x_dtype)) % 16 != 0) return CR_ERR_MISALIGNED;
+    if (!aligned(w_f6, 16) || ld_f6 % 16 != 0 || !aligned(w_scale, 4)) return CR_ERR_MISALIGNED;
+    if ((bias && !aligned(bias, 4)) || !aligned(out, (size_t)elem_size(out_dtype))) return CR_ERR_MISALIGNED;
+    if (M == 0 || N == 0) return CR_OK;       // an empty layer: nothing to enqueue, no workspace
+    if (!workspace) return CR_ERR_INVALID_ARG;
+    if (!aligned(workspace, 256)) return CR_ERR_MISALIGNED;
+    if (ws_bytes < cr_linear_w4a4_e2m3_workspace_bytes(M, K)) return CR_ERR_TOO_LARGE;
+    cr_status s = current_device_ok();
+    if (s != CR_OK) return s;
+    const int64_t lf = kp / 4 * 3;
+    uint8_t *x_f6 = static_cast<uint8_t *>(workspace);
+    float *x_scale = reinterpret_cast<float *>(x_f6 + up256((size_t)M * (size_t)lf));
+    hipError_t e = convrot::launch_quant_act_e2m3(x, (int)x_dtype, ld_x, swiglu != 0, M, K, x_f6, lf, x_scale,
+                                                  (flags & CR_FLAG_FORCE_TWO_PASS) != 0,
+                                                  (flags & CR_FLAG_BLOCK_TRANSPOSED) != 0, stream);
+    if (e != hipSuccess) return CR_ERR_LAUNCH;
+    return from_hip(convrot::launch_gemm_e2m3(x_f6, lf, x_scale, w_f6, ld_f6, w_scale, bias, M, N, kp, out,
+                                              (int)out_dtype, ldc, stream));
+}
+
 cr_status cr_linear_nvfp4_noalloc(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu,
                                   int64_t M, int64_t K, const float *pre_scale,
                                   const uint8_t *w_fp4, int64_t ld_fp4,

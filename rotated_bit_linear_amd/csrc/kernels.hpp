@@ -28,11 +28,18 @@ hipError_t launch_swiglu(const void *h, int dtype, int64_t ld_h, int64_t M, int6
 hipError_t launch_quant_weight_w4(const void *w, int dtype, int64_t ld_w, int64_t N, int64_t K, uint8_t *w_s4,
                                   int64_t ld_s4, float *w_scale, bool two_pass, bool transposed, hipStream_t st);
 
+// The same 4-bit weight rows as E2M3 fields [N, ld_f6 bytes] (ld_f6 >= 3 K_pad / 4)
+hipError_t launch_quant_weight_e2m3(const void *w, int dtype, int64_t ld_w, int64_t N, int64_t K, uint8_t *w_f6,
+                                    int64_t ld_f6, float *w_scale, bool two_pass, bool transposed, hipStream_t st);
+
 // W4A4: activation rows (swiglu: H [M, 2K], SwiGLU first) -> ConvRot256 -> packed 4-bit
 // codes [M, ld_s4 bytes] + scales, the format of launch_quant_weight_w4
 hipError_t launch_quant_act_w4(const void *x, int dtype, int64_t ld_x, bool swiglu, int64_t M, int64_t K,
                                uint8_t *x_s4, int64_t ld_s4, float *x_scale, bool two_pass, bool transposed,
                                hipStream_t st);
+hipError_t launch_quant_act_e2m3(const void *x, int dtype, int64_t ld_x, bool swiglu, int64_t M, int64_t K,
+                                 uint8_t *x_f6, int64_t ld_f6, float *x_scale, bool two_pass, bool transposed,
+                                 hipStream_t st);
 
 hipError_t launch_prep_weight(const uint8_t *codes, int64_t ld_codes, const uint8_t *sf, int64_t ld_sf,
                               const float *g, int64_t n_rows, int64_t K, int8_t *w_s8, int64_t ld_s8,
@@ -51,6 +58,11 @@ hipError_t launch_gemm_s8s4(const int8_t *A, int64_t lda, const float *sa, const
 
 // W4A4: packed 4-bit activation x packed 4-bit weight, same epilogue; lda, ldb in bytes
 hipError_t launch_gemm_s4s4(const uint8_t *A, int64_t lda, const float *sa, const uint8_t *B, int64_t ldb,
+                            const float *sb, const float *bias, int64_t M, int64_t N, int64_t K_pad, void *C,
+                            int out_dtype, int64_t ldc, hipStream_t st);
+
+// W4A4 on the 6-bit matrix cores: two E2M3-field operands (lda, ldb in bytes), same epilogue
+hipError_t launch_gemm_e2m3(const uint8_t *A, int64_t lda, const float *sa, const uint8_t *B, int64_t ldb,
                             const float *sb, const float *bias, int64_t M, int64_t N, int64_t K_pad, void *C,
                             int out_dtype, int64_t ldc, hipStream_t st);
 

@@ -454,33 +454,46 @@ hipError_t launch_quant_act(const void *x, int dtype, int64_t ld_x, int64_t M, i
 // W4A8 weight preparation from dense rows (the activation loader, no pre-scale): ConvRot256,
 // 4-bit row quantization, packed codes (ComfyUI Turing Utils README: W4A8 dispatch; the
 // packed format is this library's, the pages describe none)
-template <int DT>
+template <int DT, int kBits>
 static hipError_t launch_w4(const void *w, int64_t ld_w, int64_t N, int64_t K, uint8_t *w_s4, int64_t ld_s4,
                             float *w_scale, bool two_pass, bool transposed, hipStream_t st)
 {
     const auto *wp = static_cast<const typename Elem<DT>::T *>(w);
     const bool aligned = ((uintptr_t)w % 16 == 0) && ((ld_w * (int64_t)sizeof(typename Elem<DT>::T)) % 16 == 0);
     const int64_t nb = (K + 255) / 256;
-    return launch_rows<ActLoader<DT, false>, 4>(ActLoader<DT, false>{wp, ld_w, K, aligned, nullptr}, N, nb,
-                                                reinterpret_cast<int8_t *>(w_s4), ld_s4, w_scale, two_pass,
-                                                transposed, st);
+    return launch_rows<ActLoader<DT, false>, kBits>(ActLoader<DT, false>{wp, ld_w, K, aligned, nullptr}, N, nb,
+                                                    reinterpret_cast<int8_t *>(w_s4), ld_s4, w_scale, two_pass,
+                                                    transposed, st);
+}
+
+template <int kBits>
+static hipError_t launch_weight_4bit(const void *w, int dtype, int64_t ld_w, int64_t N, int64_t K, uint8_t *out,
+                                     int64_t ld_out, float *w_scale, bool two_pass, bool transposed, hipStream_t st)
+{
+    switch (dtype) {
+    case 0: return launch_w4<0, kBits>(w, ld_w, N, K, out, ld_out, w_scale, two_pass, transposed, st);
+    case 1: return launch_w4<1, kBits>(w, ld_w, N, K, out, ld_out, w_scale, two_pass, transposed, st);
+    case 2: return launch_w4<2, kBits>(w, ld_w, N, K, out, ld_out, w_scale, two_pass, transposed, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_quant_weight_w4(const void *w, int dtype, int64_t ld_w, int64_t N, int64_t K, uint8_t *w_s4,
                                   int64_t ld_s4, float *w_scale, bool two_pass, bool transposed, hipStream_t st)
 {
-    switch (dtype) {
-    case 0: return launch_w4<0>(w, ld_w, N, K, w_s4, ld_s4, w_scale, two_pass, transposed, st);
-    case 1: return launch_w4<1>(w, ld_w, N, K, w_s4, ld_s4, w_scale, two_pass, transposed, st);
-    case 2: return launch_w4<2>(w, ld_w, N, K, w_s4, ld_s4, w_scale, two_pass, transposed, st);
-    default: return hipErrorInvalidValue;
-    }
+    return launch_weight_4bit<4>(w, dtype, ld_w, N, K, w_s4, ld_s4, w_scale, two_pass, transposed, st);
+}
+
+hipError_t launch_quant_weight_e2m3(const void *w, int dtype, int64_t ld_w, int64_t N, int64_t K, uint8_t *w_f6,
+                                    int64_t ld_f6, float *w_scale, bool two_pass, bool transposed, hipStream_t st)
+{
+    return launch_weight_4bit<6>(w, dtype, ld_w, N, K, w_f6, ld_f6, w_scale, two_pass, transposed, st);
 }
 
 // W4A4 activation preparation: the activation (or SwiGLU) loader, no pre-scale, ConvRot256,
-// 4-bit row quantization, packed codes (ComfyUI Turing Utils README: W4A4 dispatch; the packed
-// format is the weight's)
-template <int DT>
+// 4-bit row quantization, packed codes or E2M3 fields (ComfyUI Turing Utils README: W4A4
+// dispatch; both forms are the weight's)
+template <int DT, int kBits>
 static hipError_t launch_act_w4(const void *x, int64_t ld_x, bool swiglu, int64_t M, int64_t K, uint8_t *x_s4,
                                 int64_t ld_s4, float *x_scale, bool two_pass, bool transposed, hipStream_t st)
 {
@@ -492,24 +505,39 @@ static hipError_t launch_act_w4(const void *x, int64_t ld_x, bool swiglu, int64_
     const bool row_ok = ((uintptr_t)x % 16 == 0) && ((ld_x * es) % 16 == 0);
     if (swiglu) {
         const bool val_ok = row_ok && ((K * es) % 16 == 0);
-        return launch_rows<SwigluLoader<DT, false>, 4>(SwigluLoader<DT, false>{xp, ld_x, K, row_ok, val_ok, nullptr},
-                                                       M, nb, out, ld_s4, x_scale, two_pass, transposed, st,
-                                                       kMaxGroupsWide);
+        return launch_rows<SwigluLoader<DT, false>, kBits>(
+            SwigluLoader<DT, false>{xp, ld_x, K, row_ok, val_ok, nullptr}, M, nb, out, ld_s4, x_scale, two_pass,
+            transposed, st, kMaxGroupsWide);
     }
-    return launch_rows<ActLoader<DT, false>, 4>(ActLoader<DT, false>{xp, ld_x, K, row_ok, nullptr}, M, nb, out,
-                                                ld_s4, x_scale, two_pass, transposed, st);
+    return launch_rows<ActLoader<DT, false>, kBits>(ActLoader<DT, false>{xp, ld_x, K, row_ok, nullptr}, M, nb, out,
+                                                    ld_s4, x_scale, two_pass, transposed, st);
+}
+
+template <int kBits>
+static hipError_t launch_act_4bit(const void *x, int dtype, int64_t ld_x, bool swiglu, int64_t M, int64_t K,
+                                  uint8_t *out, int64_t ld_out, float *x_scale, bool two_pass, bool transposed,
+                                  hipStream_t st)
+{
+    switch (dtype) {
+    case 0: return launch_act_w4<0, kBits>(x, ld_x, swiglu, M, K, out, ld_out, x_scale, two_pass, transposed, st);
+    case 1: return launch_act_w4<1, kBits>(x, ld_x, swiglu, M, K, out, ld_out, x_scale, two_pass, transposed, st);
+    case 2: return launch_act_w4<2, kBits>(x, ld_x, swiglu, M, K, out, ld_out, x_scale, two_pass, transposed, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_quant_act_w4(const void *x, int dtype, int64_t ld_x, bool swiglu, int64_t M, int64_t K,
                                uint8_t *x_s4, int64_t ld_s4, float *x_scale, bool two_pass, bool transposed,
                                hipStream_t st)
 {
-    switch (dtype) {
-    case 0: return launch_act_w4<0>(x, ld_x, swiglu, M, K, x_s4, ld_s4, x_scale, two_pass, transposed, st);
-    case 1: return launch_act_w4<1>(x, ld_x, swiglu, M, K, x_s4, ld_s4, x_scale, two_pass, transposed, st);
-    case 2: return launch_act_w4<2>(x, ld_x, swiglu, M, K, x_s4, ld_s4, x_scale, two_pass, transposed, st);
-    default: return hipErrorInvalidValue;
-    }
+    return launch_act_4bit<4>(x, dtype, ld_x, swiglu, M, K, x_s4, ld_s4, x_scale, two_pass, transposed, st);
+}
+
+hipError_t launch_quant_act_e2m3(const void *x, int dtype, int64_t ld_x, bool swiglu, int64_t M, int64_t K,
+                                 uint8_t *x_f6, int64_t ld_f6, float *x_scale, bool two_pass, bool transposed,
+                                 hipStream_t st)
+{
+    return launch_act_4bit<6>(x, dtype, ld_x, swiglu, M, K, x_f6, ld_f6, x_scale, two_pass, transposed, st);
 }
 
 hipError_t launch_swiglu(const void *h, int dtype, int64_t ld_h, int64_t M, int64_t F, float *out,

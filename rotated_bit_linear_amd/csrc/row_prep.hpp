@@ -39,7 +39,7 @@
 // 4-bit codes (the W4A8 weight rows) follow the same rule with L = 7 levels in place of
 // 127 (s = a / 7, r = 7 / a, no clamp evaluated: |y * r| <= 7 (1 + 2^-24)); everything said
 // above holds with 127 replaced by 7.  They are packed two per byte (quantize_store16_s4,
-// code_offset).
+// code_offset), or stored as E2M3 fields of equal value (quantize_e2m3_16, store_codes).
 //
 // Rows whose K_pad exceeds 128 blocks (32768 columns; 64 blocks for the activation loaders,
 // whose two-pass form measured faster), or when forced, are streamed twice:
@@ -251,6 +251,33 @@ __device__ __forceinline__ void quantize_store16_s4(const float (&z)[16], float 
     *reinterpret_cast<uint2 *>(dst) = o;
 }
 
+// The same 4-bit codes as E2M3 numbers of equal value (kBits == 6, the execution form of the
+// W4A4 operands): 16 codes -> 16 six-bit fields = 12 bytes, code i in bits 6i..6i+5 of the
+// 96-bit result (w0 = bits 0..31).  q = rint(t) + 0 (round half to even, as code_bits; the
+// + 0 turns -0 into +0); for |q| in 0..7 the fp32 bits 20..30 of |q| are (127 + E) * 8 + the
+// top three mantissa bits, so (those bits - 1008), clamped at 0, is the E2M3 magnitude
+// code ((E + 1) * 8 + mantissa; 0 for q = 0), and bit 31 moves to the E2M3 sign bit 5.
+template <bool kScaleFirst>
+__device__ __forceinline__ void quantize_e2m3_16(const float (&z)[16], float m, uint32_t &w0, uint32_t &w1,
+                                                 uint32_t &w2)
+{
+    uint32_t w[3] = {0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const float y = kScaleFirst ? (z[i] * 0.0625f) * 0x1p64f : z[i];
+        const float q = __builtin_rintf(y * m) + 0.0f;
+        const uint32_t u = __float_as_uint(q);
+        const uint32_t mag = max((u >> 20) & 0x7FFu, 1008u) - 1008u;
+        const uint32_t code = mag | ((u >> 26) & 0x20u);
+        const int bit = 6 * i;
+        w[bit / 32] |= code << (bit % 32);
+        if (bit % 32 > 26) w[bit / 32 + 1] |= code >> (32 - bit % 32);
+    }
+    w0 = w[0];
+    w1 = w[1];
+    w2 = w[2];
+}
+
 // Row constants from a' = max |z|: the scale a / L and the code multiplier, for codes of
 // L = 127 (8-bit) or L = 7 (4-bit) levels on each side of zero.
 struct RowQuant {
@@ -285,15 +312,42 @@ __device__ __forceinline__ int64_t code_offset(int64_t b, int t)
     else return b * 128 + (t >> 2) * 32 + ((((t & 1) << 1) | ((t >> 1) & 1)) << 3);
 }
 
-template <int kBits = 8>
+// 8-bit codes of 16 butterfly outputs at dst (16 bytes)
 __device__ __forceinline__ void store_codes(const float (&z)[16], const RowQuant &q, int8_t *dst)
 {
+    if (q.folded) quantize_store16<false>(z, q.mult, dst);
+    else quantize_store16<true>(z, q.mult, dst);
+}
+
+// Codes of member t of block b stored in the row at `row`.  kBits == 6 (E2M3 fields): a
+// 128-code unit is 96 bytes, its quarters' first 16 bytes in the order Q0 Q2 Q1 Q3, then
+// their last 8 bytes in the same order; member t holds half t & 1 of quarter (t >> 1) & 3 of
+// unit t >> 3: bits 0..95 of the quarter's field (its head's bytes 0..11), or bits 96..191
+// (head bytes 12..15 and the 8-byte tail).
+template <int kBits = 8>
+__device__ __forceinline__ void store_codes(const float (&z)[16], const RowQuant &q, int8_t *row, int64_t b, int t)
+{
     if constexpr (kBits == 8) {
+        int8_t *dst = row + code_offset<8>(b, t);
         if (q.folded) quantize_store16<false>(z, q.mult, dst);
         else quantize_store16<true>(z, q.mult, dst);
-    } else {
+    } else if constexpr (kBits == 4) {
+        int8_t *dst = row + code_offset<4>(b, t);
         if (q.folded) quantize_store16_s4<false>(z, q.mult, dst);
         else quantize_store16_s4<true>(z, q.mult, dst);
+    } else {
+        uint32_t w0, w1, w2;
+        if (q.folded) quantize_e2m3_16<false>(z, q.mult, w0, w1, w2);
+        else quantize_e2m3_16<true>(z, q.mult, w0, w1, w2);
+        // one dword and one 8-byte store either way: half 0 writes head bytes 0..3 and
+        // 4..11, half 1 head bytes 12..15 and the tail (32-bit offsets from the row: fewer
+        // live registers than two 64-bit addresses)
+        const int g = (t >> 1) & 3, slot = ((g & 1) << 1) | (g >> 1), h = t & 1;
+        const int unit = (int)b * 192 + (t >> 3) * 96;
+        const int o0 = unit + 16 * slot + 12 * h;
+        const int o1 = h ? unit + 64 + 8 * slot : o0 + 4;
+        *reinterpret_cast<uint32_t *>(row + o0) = w0;
+        *reinterpret_cast<uint2 *>(row + o1) = make_uint2(w1, w2);
     }
 }
 
@@ -374,7 +428,7 @@ __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, 
 #pragma unroll
         for (int q = 0; q < RB; q++) {
             const int b = grp + q * G;
-            if (b < nb) store_codes<kBits>(v[q], rq, orow + code_offset<kBits>(b, t));
+            if (b < nb) store_codes<kBits>(v[q], rq, orow, b, t);
         }
         if (tid == 0) scale_out[row] = rq.scale;
     };
@@ -520,7 +574,7 @@ __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row,
             decode_slice(s, cur, v);
         }
         hadamard256(v, tile, t, natural);
-        if (b < nb) store_codes<kBits>(v, rq, orow + code_offset<kBits>(b, t));
+        if (b < nb) store_codes<kBits>(v, rq, orow, b, t);
     }
     if (tid == 0) scale_out[row] = rq.scale;
 }
@@ -588,7 +642,7 @@ __device__ __forceinline__ void row_prep_multi(const Loader &ld, int64_t n_rows,
             return;
         }
         const RowQuant rq = row_quant<kBits>(zrow);
-        if (live) store_codes<kBits>(v, rq, out + row * ld_out + code_offset<kBits>(b, t));
+        if (live) store_codes<kBits>(v, rq, out + row * ld_out, b, t);
         if (live && b == 0 && t == 0) scale_out[row] = rq.scale;
     };
 
@@ -657,7 +711,8 @@ __host__ __device__ constexpr size_t row_prep_multi_lds_bytes(int threads)
     return (size_t)(threads / kLanesPerBlock) * (kTileStrideF + 2) * sizeof(float);
 }
 
-// Kernel body shared by all loaders (kBits: 8-bit codes, or packed 4-bit codes).
+// Kernel body shared by all loaders (kBits: 8-bit codes, packed 4-bit codes, or 4-bit codes
+// as E2M3 fields).
 // mode: bit 0 two-pass, bit 1 block-transposed code order, bit 2 row maximum only (the
 // row's a = max |y| goes to scale_out; no codes are written and `out` is not used)
 template <class Loader, int RB, int kBits = 8>

@@ -187,3 +187,147 @@ def test_linear_w4a4_against_oracle(M, N, K, dt, swiglu, flags):
             torch.cuda.synchronize()
             ref = oracle.linear_w4a4(xb, dt, K, swiglu, rp, rs, odt, bias=bias.numpy() if with_bias else None)
             check_output(y, ref, odt, f"W4A4 layer out={odt} bias={with_bias}")
+
+
+# ------------------------------------------------ the E2M3 execution form ----
+# The same codes stored as E2M3 fields (6-bit floats of equal value) and multiplied on the
+# 6-bit matrix cores: codes, scales, int32 sums and outputs must equal the oracle's.
+
+def _e2m3(p_nibbles: np.ndarray) -> np.ndarray:
+    """The oracle's E2M3 form of the codes of nibble-packed rows."""
+    kp = p_nibbles.shape[1] * 2
+    return oracle.pack_e2m3(oracle.unpack_s4(p_nibbles, kp))
+
+
+@pytest.mark.parametrize("dt,swiglu,M,K", A_CASES,
+                         ids=[f"dt{c[0]}-sw{int(c[1])}-M{c[2]}-K{c[3]}" for c in A_CASES])
+def test_quant_act_w4_e2m3_bit_exact(dt, swiglu, M, K):
+    width = 2 * K if swiglu else K
+    x = _act(M, width, dt, M + K + int(swiglu))
+    rp, rs = oracle.quant_act_w4(_host(x, dt), dt, K, swiglu=swiglu)
+    rf, rf_bt = _e2m3(rp), _e2m3(_bt_packed(rp))
+    xd = x.to(dev())
+    for flags in (0, BT, rbl.CR_FLAG_FORCE_TWO_PASS, rbl.CR_FLAG_FORCE_TWO_PASS | BT):
+        say(f"cr_quant_act_w4_e2m3 dt={dt} swiglu={swiglu} M={M} K={K} flags={flags}")
+        p, s = rbl.quant_act_w4_e2m3(xd, K, swiglu=swiglu, flags=flags)
+        torch.cuda.synchronize()
+        assert_bits_equal(p.cpu().numpy(), rf_bt if flags & BT else rf, f"x_f6 flags={flags}")
+        assert_bits_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32), f"x_scale flags={flags}")
+
+
+W_CASES = [(synth.DT_BF16, 300, 1000), (synth.DT_FP16, 97, 5376), (synth.DT_FP32, 64, 20000),
+           (synth.DT_FP32, 21, 17), (synth.DT_BF16, 70, 14336)]
+
+
+@pytest.mark.parametrize("dt,N,K", W_CASES, ids=[f"dt{c[0]}-N{c[1]}-K{c[2]}" for c in W_CASES])
+def test_quant_weight_w4_e2m3_bit_exact(dt, N, K):
+    w = _act(N, K, dt, 3 * N + K)
+    rp, rs = oracle.quant_weight_w4(_host(w, dt), dt, K)
+    rf, rf_bt = _e2m3(rp), _e2m3(_bt_packed(rp))
+    wd = w.to(dev())
+    for flags in (0, BT, rbl.CR_FLAG_FORCE_TWO_PASS | BT):
+        say(f"cr_quant_weight_w4_e2m3 dt={dt} N={N} K={K} flags={flags}")
+        p, s = rbl.quant_weight_w4_e2m3(wd, K, flags=flags)
+        torch.cuda.synchronize()
+        assert_bits_equal(p.cpu().numpy(), rf_bt if flags & BT else rf, f"w_f6 flags={flags}")
+        assert_bits_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32), f"w_scale flags={flags}")
+
+
+@pytest.mark.parametrize("M,N,Kp", G_CASES, ids=[f"M{c[0]}-N{c[1]}-K{c[2]}" for c in G_CASES])
+def test_gemm_e2m3_int32_exact_and_epilogues(M, N, Kp):
+    g = torch.Generator().manual_seed(M * 13 + N + Kp)
+    qa = torch.randint(-7, 8, (M, Kp), generator=g, dtype=torch.int32).to(torch.int8)
+    qb = torch.randint(-7, 8, (N, Kp), generator=g, dtype=torch.int32).to(torch.int8)
+    a = torch.from_numpy(oracle.pack_e2m3(qa.numpy()))
+    b = torch.from_numpy(oracle.pack_e2m3(qb.numpy()))
+    sa = torch.rand(M, generator=g) * 1e-2
+    sb = torch.rand(N, generator=g) * 1e-2
+    sa[0] = 0.0
+    bias = torch.randn(N, generator=g)
+    acc = oracle.gemm_e2m3(a.numpy(), b.numpy(), Kp)
+    ad, bd, sad, sbd, biasd = a.to(dev()), b.to(dev()), sa.to(dev()), sb.to(dev()), bias.to(dev())
+    for ldc in (N + 9, (N + 7) // 8 * 8 + 8):
+        for odt in (synth.DT_I32, synth.DT_BF16, synth.DT_FP16, synth.DT_FP32):
+            for with_bias in ((False,) if odt == synth.DT_I32 else (False, True)):
+                tdt = synth.TORCH_DTYPE[odt]
+                full = torch.full((M, ldc), 7, dtype=tdt, device=dev())
+                c = full[:, :N]
+                say(f"cr_gemm_e2m3_rowscale M={M} N={N} K_pad={Kp} out={odt} ldc={ldc} bias={with_bias}")
+                rbl.cr_gemm_e2m3_rowscale(ad, sad, bd, sbd, c, bias=biasd if with_bias else None)
+                torch.cuda.synchronize()
+                fc = full.cpu()
+                assert (fc[:, N:] == 7).all(), "columns past N were written"
+                if odt == synth.DT_I32:
+                    assert_bits_equal(fc[:, :N].numpy(), acc, "int32 accumulator")
+                else:
+                    ref = oracle.epilogue(acc, sa.numpy(), sb.numpy(), odt,
+                                          bias=bias.numpy() if with_bias else None)
+                    check_output(fc[:, :N], ref, odt, f"E2M3 GEMM out={odt} bias={with_bias}")
+
+
+def test_gemm_e2m3_strided_operands_and_worst_case():
+    """Row strides beyond 3 K_pad / 4 on both operands; and the largest accepted K_pad with
+    codes +-7 (|sum| = 49 * 133120 < 2^23: the fp32 sums stay exact)."""
+    M, N, Kp = 300, 260, 1280
+    g = torch.Generator().manual_seed(6)
+    qa = torch.randint(-7, 8, (M, Kp), generator=g, dtype=torch.int32).to(torch.int8)
+    qb = torch.randint(-7, 8, (N, Kp), generator=g, dtype=torch.int32).to(torch.int8)
+    a = torch.from_numpy(oracle.pack_e2m3(qa.numpy()))
+    b = torch.from_numpy(oracle.pack_e2m3(qb.numpy()))
+    acc = oracle.gemm_e2m3(a.numpy(), b.numpy(), Kp)
+    lf = Kp // 4 * 3
+    af = torch.full((M, lf + 48), 0x3F, dtype=torch.uint8)
+    bf = torch.full((N, lf + 16), 0x3F, dtype=torch.uint8)
+    af[:, :lf] = a
+    bf[:, :lf] = b
+    c = torch.empty(M, N, dtype=torch.int32, device=dev())
+    say(f"cr_gemm_e2m3_rowscale strided lda={af.shape[1]} ldb={bf.shape[1]}")
+    rbl.cr_gemm_e2m3_rowscale(af.to(dev())[:, :lf], None, bf.to(dev())[:, :lf], None, c, K_pad=Kp)
+    torch.cuda.synchronize()
+    assert_bits_equal(c.cpu().numpy(), acc, "int32 accumulator with row strides")
+
+    Kp = rbl.CR_MAX_K_PAD
+    qa = torch.full((3, Kp), 7, dtype=torch.int8)
+    qa[1] = -7
+    qa[2, ::2] = -7
+    qb = torch.full((5, Kp), 7, dtype=torch.int8)
+    qb[1] = -7
+    qb[3, 1::2] = -7
+    qb[4] = 0
+    a = torch.from_numpy(oracle.pack_e2m3(qa.numpy()))
+    b = torch.from_numpy(oracle.pack_e2m3(qb.numpy()))
+    acc = oracle.gemm_e2m3(a.numpy(), b.numpy(), Kp)
+    assert int(np.abs(acc).max()) == 49 * Kp
+    say(f"cr_gemm_e2m3_rowscale worst-case accumulator K_pad={Kp}")
+    c = torch.empty(3, 5, dtype=torch.int32, device=dev())
+    rbl.cr_gemm_e2m3_rowscale(a.to(dev()), None, b.to(dev()), None, c)
+    torch.cuda.synchronize()
+    assert_bits_equal(c.cpu().numpy(), acc, "int32 accumulator at the K_pad limit")
+
+
+@pytest.mark.parametrize("M,N,K,dt,swiglu,flags", L_CASES,
+                         ids=[f"M{c[0]}-N{c[1]}-K{c[2]}-sw{int(c[4])}-f{c[5]}" for c in L_CASES])
+def test_linear_w4a4_e2m3_against_oracle(M, N, K, dt, swiglu, flags):
+    """The layer on the 6-bit matrix cores equals the oracle's W4A4 layer bit for bit (and
+    so the nibble-form layer)."""
+    wl = synth.Workload("w4a4", M, N, K, dt, (synth.DT_BF16,), M + N, swiglu=swiglu, outlier_frac=0.01)
+    x = synth.make_activation(wl)
+    g = torch.Generator().manual_seed(N * 5 + K)
+    w = (torch.randn(N, (K + 7) // 8 * 8, generator=g) * 0.02).float()
+    rp, rs = oracle.quant_weight_w4(w.numpy(), synth.DT_FP32, K)
+    say(f"cr_quant_weight_w4_e2m3 for the layer N={N} K={K} flags={flags}")
+    p, s = rbl.quant_weight_w4_e2m3(w.to(dev())[:, :K], K, flags=flags)
+    bias = torch.randn(N, generator=torch.Generator().manual_seed(N)).float()
+    xb = synth.bits_u16(x) if dt != synth.DT_FP32 else x.numpy()
+    cols = x.shape[1]
+    xpad = torch.zeros(M, (cols + 7) // 8 * 8 + 8, dtype=x.dtype)
+    xpad[:, :cols] = x
+    xd = xpad.to(dev())[:, :cols]
+    for odt in (synth.DT_BF16, synth.DT_FP32):
+        for with_bias in (False, True):
+            say(f"cr_linear_w4a4_e2m3 M={M} N={N} K={K} swiglu={swiglu} flags={flags} out={odt} bias={with_bias}")
+            y = rbl.linear_w4a4_e2m3(xd, p, s, K, out_dtype=synth.TORCH_DTYPE[odt], swiglu=swiglu,
+                                     bias=bias.to(dev()) if with_bias else None, flags=flags)
+            torch.cuda.synchronize()
+            ref = oracle.linear_w4a4(xb, dt, K, swiglu, rp, rs, odt, bias=bias.numpy() if with_bias else None)
+            check_output(y, ref, odt, f"W4A4 E2M3 layer out={odt} bias={with_bias}")
