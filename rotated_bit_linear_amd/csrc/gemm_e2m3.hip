@@ -15,8 +15,9 @@
 // operand for one slice is its row's quarter: 16 bytes of head (one aligned 16-byte LDS read)
 // and 8 bytes of tail (one 8-byte read).  A row's 96 bytes of a step are six 16-byte chunks
 // (heads of Q0 Q2 Q1 Q3, then the two tail chunks [Q0 Q2] and [Q1 Q3]); the chunks of row r
-// sit at LDS positions rotated by (r >> 2) & 1, which spreads eight consecutive rows over all
-// banks for the head reads.  Stages: 24 KB per operand, three stages (144 KB) in flight.
+// sit at LDS positions rotated by one bit of r (rot below), which spreads sixteen consecutive
+// rows over all banks for the head reads.  Stages: 24 KB per operand, three stages (144 KB)
+// in flight.
 // Waits, refills, tile order and the epilogue follow the packed 4-bit GEMM (gemm_s8s4.hip).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -59,8 +60,15 @@ static_assert(NWAVE * EPI_BYTES + BN * 4 <= POOL, "epilogue tiles and bias fit t
 static_assert(PPW * (NSTAGE - 1) <= 63, "vmcnt range");
 static_assert(KS == 2, "the step below has two slices");
 
-// rotation of row r's chunk positions
-__device__ __forceinline__ int rot(int r) { return (r >> 2) & 1; }
+// Rotation of row r's chunk positions: chunk c of row r sits at 16-byte slot
+// 6 r + (c + rot(r)) mod 6.  The LDS has 64 banks of 4 bytes and a 16-byte read serves 16
+// lanes (rows r0 .. r0+15, r0 % 16 == 0) per cycle.  6 r mod 16 is even and repeats after
+// 8 rows, so rows r and r + 8 need rotations of different parity; with rot = bit 2 xor bit 3
+// of r every aligned group of 16 rows (and of 8, for 32 banks) reads a chunk from 16 (8)
+// different bank groups.  The 8-byte tail reads (32 lanes per cycle) meet each bank twice:
+// a row's two tail halves share a chunk, so the 32 halves of one slice take only 16 bank
+// pairs.
+__device__ __forceinline__ int rot(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 
 template <int OUT, bool BIAS>
 __global__ __launch_bounds__(NTHREAD, 1)
@@ -134,18 +142,21 @@ void gemm_e2m3_kernel(const uint8_t *__restrict__ A, int64_t lda, const float *_
     v2i ta[2][F_M], tb[2][F_N];      // tails
     auto lds16 = [](uint32_t a) { return *reinterpret_cast<const __attribute__((address_space(3))) v4i_ *>(a); };
     auto lds8 = [](uint32_t a) { return *reinterpret_cast<const __attribute__((address_space(3))) v2i *>(a); };
-    // fragments of slice ks of stage s into slot ks (compile-time offsets: immediates)
+    // fragments of slice ks of stage s into slot ks (compile-time offsets: immediates), in
+    // the order the MFMAs below first need them: A0 B0 B1 .. B(F_N-1) A1 .. A(F_M-1)
+    auto read_a = [&](int s, int ks, int i) {
+        ha[ks][i] = lds16(adrHA[i] + s * SOP + ks * 16);
+        ta[ks][i] = lds8(adrTA[i] + s * SOP + ks * 8);
+    };
     auto read = [&](int s, int ks) {
-#pragma unroll
-        for (int i = 0; i < F_M; i++) {
-            ha[ks][i] = lds16(adrHA[i] + s * SOP + ks * 16);
-            ta[ks][i] = lds8(adrTA[i] + s * SOP + ks * 8);
-        }
+        read_a(s, ks, 0);
 #pragma unroll
         for (int j = 0; j < F_N; j++) {
             hb[ks][j] = lds16(adrHB[j] + s * SOP + ks * 16);
             tb[ks][j] = lds8(adrTB[j] + s * SOP + ks * 8);
         }
+#pragma unroll
+        for (int i = 1; i < F_M; i++) read_a(s, ks, i);
     };
     // MFMAs t0 .. t1-1 of slice `slot` (t = i*F_N + j); weight operand first, so lane l of
     // block (i, j) holds output row l % 32 (the layout gemm::store_tile expects).  The two
