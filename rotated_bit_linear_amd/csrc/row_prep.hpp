@@ -278,6 +278,38 @@ __device__ __forceinline__ void quantize_e2m3_16(const float (&z)[16], float m, 
     w2 = w[2];
 }
 
+// The same result from two 8-entry byte tables (fewer vector instructions, two more live
+// registers): per byte of four codes (rounded as code_bits), bit 3 of the nibble is set
+// exactly for q < 0, the low three bits index the table of the code's sign.
+template <bool kScaleFirst>
+__device__ __forceinline__ void quantize_e2m3_16_tables(const float (&z)[16], float m, uint32_t &w0, uint32_t &w1,
+                                                        uint32_t &w2)
+{
+    uint32_t f[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        uint32_t c[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float y = kScaleFirst ? (z[4 * k + i] * 0.0625f) * 0x1p64f : z[4 * k + i];
+            c[i] = code_bits(y * m);
+        }
+        const uint32_t p = pack_low_bytes(c[0], c[1], c[2], c[3]);
+        const uint32_t sel = p & 0x07070707u;
+        // E2M3 of 0..7: 0x00 0x08 0x10 0x14 0x18 0x1A 0x1C 0x1E; of -8..-1 (nibble 8..15):
+        // (unused) 0x3E 0x3C 0x3A 0x38 0x34 0x30 0x28
+        const uint32_t pos = __builtin_amdgcn_perm(0x1E1C1A18u, 0x14100800u, sel);
+        const uint32_t neg = __builtin_amdgcn_perm(0x28303438u, 0x3A3C3E00u, sel);
+        const uint32_t one = (p >> 3) & 0x01010101u;
+        const uint32_t mask = (one << 8) - one;                     // 0xFF in the bytes of negative codes
+        const uint32_t e = (neg & mask) | (pos & ~mask);
+        f[k] = (e & 0x3Fu) | ((e >> 2) & 0xFC0u) | ((e >> 4) & 0x3F000u) | ((e >> 6) & 0xFC0000u);
+    }
+    w0 = f[0] | (f[1] << 24);
+    w1 = (f[1] >> 8) | (f[2] << 16);
+    w2 = (f[2] >> 16) | (f[3] << 8);
+}
+
 // Row constants from a' = max |z|: the scale a / L and the code multiplier, for codes of
 // L = 127 (8-bit) or L = 7 (4-bit) levels on each side of zero.
 struct RowQuant {
@@ -324,7 +356,7 @@ __device__ __forceinline__ void store_codes(const float (&z)[16], const RowQuant
 // their last 8 bytes in the same order; member t holds half t & 1 of quarter (t >> 1) & 3 of
 // unit t >> 3: bits 0..95 of the quarter's field (its head's bytes 0..11), or bits 96..191
 // (head bytes 12..15 and the 8-byte tail).
-template <int kBits = 8>
+template <int kBits = 8, bool kTables = true>
 __device__ __forceinline__ void store_codes(const float (&z)[16], const RowQuant &q, int8_t *row, int64_t b, int t)
 {
     if constexpr (kBits == 8) {
@@ -337,8 +369,13 @@ __device__ __forceinline__ void store_codes(const float (&z)[16], const RowQuant
         else quantize_store16_s4<true>(z, q.mult, dst);
     } else {
         uint32_t w0, w1, w2;
-        if (q.folded) quantize_e2m3_16<false>(z, q.mult, w0, w1, w2);
-        else quantize_e2m3_16<true>(z, q.mult, w0, w1, w2);
+        if constexpr (kTables) {
+            if (q.folded) quantize_e2m3_16_tables<false>(z, q.mult, w0, w1, w2);
+            else quantize_e2m3_16_tables<true>(z, q.mult, w0, w1, w2);
+        } else {
+            if (q.folded) quantize_e2m3_16<false>(z, q.mult, w0, w1, w2);
+            else quantize_e2m3_16<true>(z, q.mult, w0, w1, w2);
+        }
         // one dword and one 8-byte store either way: half 0 writes head bytes 0..3 and
         // 4..11, half 1 head bytes 12..15 and the tail (32-bit offsets from the row: fewer
         // live registers than two 64-bit addresses)
@@ -361,6 +398,8 @@ __host__ __device__ constexpr size_t row_prep_lds_bytes(int threads)
 // Loader concept:
 //   static constexpr bool kFourBlocks;               rows of 65-128 blocks are held in one
 //                                                    pass, four blocks per lane group
+//   static constexpr bool kE2M3Tables;               E2M3 codes through byte tables (else
+//                                                    arithmetic: fewer live registers)
 //   static constexpr bool kFetchAfterDecode;         request the next row after decoding
 //                                                    this one (else before: two buffers)
 //   static constexpr bool kTwoPassPrefetch;          two-pass rows: request the next slice
@@ -428,7 +467,7 @@ __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, 
 #pragma unroll
         for (int q = 0; q < RB; q++) {
             const int b = grp + q * G;
-            if (b < nb) store_codes<kBits>(v[q], rq, orow, b, t);
+            if (b < nb) store_codes<kBits, Loader::kE2M3Tables>(v[q], rq, orow, b, t);
         }
         if (tid == 0) scale_out[row] = rq.scale;
     };
@@ -574,7 +613,7 @@ __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row,
             decode_slice(s, cur, v);
         }
         hadamard256(v, tile, t, natural);
-        if (b < nb) store_codes<kBits>(v, rq, orow, b, t);
+        if (b < nb) store_codes<kBits, Loader::kE2M3Tables>(v, rq, orow, b, t);
     }
     if (tid == 0) scale_out[row] = rq.scale;
 }
@@ -642,7 +681,7 @@ __device__ __forceinline__ void row_prep_multi(const Loader &ld, int64_t n_rows,
             return;
         }
         const RowQuant rq = row_quant<kBits>(zrow);
-        if (live) store_codes<kBits>(v, rq, out + row * ld_out, b, t);
+        if (live) store_codes<kBits, Loader::kE2M3Tables>(v, rq, out + row * ld_out, b, t);
         if (live && b == 0 && t == 0) scale_out[row] = rq.scale;
     };
 
