@@ -23,6 +23,7 @@ from helpers import assert_bits_equal, check_output, dev, say
 pytestmark = pytest.mark.gpu
 
 BT = rbl.CR_FLAG_BLOCK_TRANSPOSED
+DT_T = {synth.DT_BF16: torch.bfloat16, synth.DT_FP16: torch.float16, synth.DT_FP32: torch.float32}
 
 
 def _block_transposed(codes: np.ndarray) -> np.ndarray:
@@ -331,3 +332,88 @@ def test_linear_w4a4_e2m3_against_oracle(M, N, K, dt, swiglu, flags):
             torch.cuda.synchronize()
             ref = oracle.linear_w4a4(xb, dt, K, swiglu, rp, rs, odt, bias=bias.numpy() if with_bias else None)
             check_output(y, ref, odt, f"W4A4 E2M3 layer out={odt} bias={with_bias}")
+
+
+# ------------------------------------------------------ seeded random shapes ----
+# M, N, K, dtypes, SwiGLU, order and bias drawn per case; activations with padded strides and
+# garbage past the used columns; the nibble-form and E2M3-form layers, their activation codes
+# and the GEMMs' int32 sums against the oracle, bit for bit.
+
+def _rcase(i):
+    r = np.random.default_rng(2000 + i)
+    M = int(r.choice([1, 2, 7, 31, 33, 64, 65, 129, 257, 300]))
+    N = int(r.choice([1, 5, 32, 100, 255, 256, 257, 513]))
+    K = int(r.choice([1, 15, 17, 255, 256, 257, 1000, 5376, 16385, 20000]))
+    xdt = int(r.choice([synth.DT_BF16, synth.DT_FP16, synth.DT_FP32]))
+    odt = int(r.choice([synth.DT_BF16, synth.DT_FP16, synth.DT_FP32]))
+    swiglu = bool(r.random() < 0.3)
+    order = int(r.choice([0, BT]))
+    with_bias = bool(r.random() < 0.4)
+    return M, N, K, xdt, odt, swiglu, order, with_bias
+
+
+R_CASES = [_rcase(i) for i in range(40)]
+
+
+@pytest.mark.parametrize("case", R_CASES, ids=[f"M{c[0]}-N{c[1]}-K{c[2]}-x{c[3]}-o{c[4]}-sw{int(c[5])}-f{c[6]}-b{int(c[7])}"
+                                              for c in R_CASES])
+def test_random_shapes_both_forms(case):
+    M, N, K, xdt, odt, swiglu, flags, with_bias = case
+    seed = M * 7919 + N * 31 + K + 5
+    g = torch.Generator().manual_seed(seed)
+    cols = 2 * K if swiglu else K
+    ld = (cols + 7) // 8 * 8 + 8
+    x = torch.randn(M, ld, generator=g) * 1.5
+    x[:, cols:] = 3e3
+    x = x.to(DT_T[xdt])
+    w = (torch.randn(N, (K + 7) // 8 * 8, generator=g) * 0.02).float()
+    bias = torch.randn(N, generator=g).float() if with_bias else None
+    xh = _host(x, xdt)
+    rp, rs = oracle.quant_weight_w4(w.numpy(), synth.DT_FP32, K)
+    ap, as_ = oracle.quant_act_w4(xh, xdt, K, swiglu=swiglu)
+    ref = oracle.linear_w4a4(xh, xdt, K, swiglu, rp, rs, odt, bias=None if bias is None else bias.numpy())
+    acc = oracle.gemm_s4s4(ap, rp, rp.shape[1] * 2)
+    xd, wd = x.to(dev()), w.to(dev())[:, :K]
+    bd = None if bias is None else bias.to(dev())
+    say(f"W4A4 random case {case}")
+    # nibble form
+    p, s = rbl.quant_weight_w4(wd, K, flags=flags)
+    q, qs = rbl.quant_act_w4(xd, K, swiglu=swiglu, flags=flags)
+    y = rbl.linear_w4a4(xd, p, s, K, out_dtype=DT_T[odt], swiglu=swiglu, bias=bd, flags=flags)
+    c = torch.empty(M, N, dtype=torch.int32, device=dev())
+    rbl.cr_gemm_s4s4_rowscale(q, None, p, None, c)
+    # E2M3 form
+    p6, s6 = rbl.quant_weight_w4_e2m3(wd, K, flags=flags)
+    q6, qs6 = rbl.quant_act_w4_e2m3(xd, K, swiglu=swiglu, flags=flags)
+    y6 = rbl.linear_w4a4_e2m3(xd, p6, s6, K, out_dtype=DT_T[odt], swiglu=swiglu, bias=bd, flags=flags)
+    c6 = torch.empty(M, N, dtype=torch.int32, device=dev())
+    rbl.cr_gemm_e2m3_rowscale(q6, None, p6, None, c6)
+    torch.cuda.synchronize()
+    want_q = _bt_packed(ap) if flags & BT else ap
+    assert_bits_equal(q.cpu().numpy(), want_q, "activation nibbles")
+    assert_bits_equal(q6.cpu().numpy(), _e2m3(want_q), "activation E2M3 fields")
+    assert_bits_equal(qs.cpu().numpy().view(np.uint32), as_.view(np.uint32), "activation scales")
+    assert_bits_equal(qs6.cpu().numpy().view(np.uint32), as_.view(np.uint32), "activation scales (E2M3 call)")
+    assert_bits_equal(c.cpu().numpy(), acc, "int32 sums, nibble form")
+    assert_bits_equal(c6.cpu().numpy(), acc, "int32 sums, E2M3 form")
+    check_output(y, ref, odt, "W4A4 layer, nibble form")
+    check_output(y6, ref, odt, "W4A4 layer, E2M3 form")
+
+
+def test_empty_extents_are_no_ops():
+    """M = 0 or N = 0 through every W4A4 call: nothing written, no error."""
+    x = torch.randn(4, 512, device=dev()).to(torch.bfloat16)
+    w = torch.randn(8, 512, device=dev())
+    p, s = rbl.quant_weight_w4(w, 512)
+    p6, s6 = rbl.quant_weight_w4_e2m3(w, 512)
+    out = torch.full((4, 8), 7.0, device=dev())
+    say("W4A4 empty extents")
+    for fn, wp, ws in ((rbl.cr_linear_w4a4, p, s), (rbl.cr_linear_w4a4_e2m3, p6, s6)):
+        fn(x[:0], 512, False, wp, ws, out[:0], None)                  # no rows: no workspace needed
+        fn(x, 512, False, wp[:0], ws[:0], out[:, :0], None)            # no columns
+    q = torch.empty(0, 256, dtype=torch.uint8, device=dev())
+    rbl.cr_quant_act_w4(x[:0], 512, False, q, torch.empty(0, device=dev()))
+    rbl.cr_quant_act_w4_e2m3(x[:0], 512, False, torch.empty(0, 384, dtype=torch.uint8, device=dev()),
+                             torch.empty(0, device=dev()))
+    torch.cuda.synchronize()
+    assert (out == 7.0).all()
