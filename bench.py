@@ -522,15 +522,15 @@ def w4a4_layers(torch, rbl, synth, dev, names, s_main, n=20):
         del qx, ws
         # the same layer on the 6-bit matrix cores (codes as E2M3 fields): identical outputs
         wf = synth.make_weight_f32(w).to(dev)
-        lf = w.K_pad // 4 * 3
-        p6 = torch.empty(w.N, lf, dtype=torch.uint8, device=dev)
+        lf = 3 * w.K_pad                  # E2M3 fields: bytes per quad of rows
+        p6 = torch.empty((w.N + 3) // 4, lf, dtype=torch.uint8, device=dev)
         sw6 = torch.empty(w.N, dtype=torch.float32, device=dev)
         rbl.cr_quant_weight_w4_e2m3(wf, w.K, p6, sw6, BT, stream=s_main)
         torch.cuda.synchronize()
         del wf
         out6 = torch.empty_like(out)
         ws6 = torch.empty(rbl.cr_linear_w4a4_e2m3_workspace_bytes(w.M, w.K), dtype=torch.uint8, device=dev)
-        qx6 = torch.empty(w.M, lf, dtype=torch.uint8, device=dev)
+        qx6 = torch.empty((w.M + 3) // 4, lf, dtype=torch.uint8, device=dev)
         act6 = lambda: rbl.cr_quant_act_w4_e2m3(x, w.K, w.swiglu, qx6, sx, BT, stream=s_main)  # noqa: E731
         layer6 = lambda: rbl.cr_linear_w4a4_e2m3(x, w.K, w.swiglu, p6, sw6, out6, ws6, flags=BT,  # noqa: E731
                                                  stream=s_main)
@@ -544,7 +544,7 @@ def w4a4_layers(torch, rbl, synth, dev, names, s_main, n=20):
         ops = 2 * w.M * w.N * w.K_pad
         in_cols = 2 * w.K if w.swiglu else w.K
         act_bytes = w.M * (in_cols * x.element_size() + w.K_pad // 2 + 4)
-        act6_bytes = w.M * (in_cols * x.element_size() + lf + 4)
+        act6_bytes = w.M * (in_cols * x.element_size() + w.K_pad // 4 * 3 + 4)
         info[name] = {
             "M": w.M, "N": w.N, "K": w.K, "K_pad": w.K_pad, "swiglu": w.swiglu,
             "layer_ms": round(t_layer, 4),

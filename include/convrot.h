@@ -364,17 +364,20 @@ cr_status cr_linear_w4a4(const void *x, cr_dtype x_dtype, int64_t ld_x, int swig
  * library's; the pages describe none): each code -7..7 stored as the E2M3 number of equal
  * value (1 sign, 2 exponent bits with bias 1, 3 mantissa bits), so that gfx950's 6-bit
  * floating-point matrix instructions multiply the codes exactly; the sums are those of the
- * nibble form, bit for bit.  A row of K_pad codes takes 3 K_pad / 4 bytes in units of 96
- * bytes per 128 codes: each quarter of 32 codes is a 192-bit field with code e in bits
- * 6e .. 6e+5 (little-endian); a unit holds the first 16 bytes of the fields of quarters
- * Q0, Q2, Q1, Q3, then their last 8 bytes in the same order.  Column order as for the
- * nibble form (flags).
+ * nibble form, bit for bit.  A row's 128-code unit takes 96 bytes: each quarter of 32 codes
+ * is a 192-bit field with code e in bits 6e .. 6e+5 (little-endian); a unit holds the first
+ * 16 bytes of the fields of quarters Q0, Q2, Q1, Q3, then their last 8 bytes in the same
+ * order.  Rows are stored in quads: rows 4q .. 4q+3 occupy the ld_f6 bytes from q * ld_f6
+ * (ld_f6 >= 3 K_pad, a multiple of 16; a multiple of 128 keeps every step of the GEMM on
+ * whole cache lines), and unit u of row 4q + i starts at byte u * 384 + i * 96 of its quad.
+ * A buffer of `rows` rows holds ceil(rows / 4) quads; the bytes of rows past `rows` in the
+ * last quad are neither written nor read.  Column order as for the nibble form (flags).
  *
  * cr_quant_weight_w4_e2m3 and cr_quant_act_w4_e2m3 are cr_quant_weight_w4 and
- * cr_quant_act_w4 with that output form: w_f6 / x_f6 [rows, ld_f6] bytes, ld_f6 >= 3 K_pad / 4,
- * a multiple of 16.  cr_gemm_e2m3_rowscale is cr_gemm_s4s4_rowscale on two such operands
- * (lda, ldb >= 3 K_pad / 4, multiples of 16).  cr_linear_w4a4_e2m3 is cr_linear_w4a4 with the
- * weight in that form and cr_linear_w4a4_e2m3_workspace_bytes(M, K) bytes of workspace.
+ * cr_quant_act_w4 with that output form: w_f6 / x_f6 [ceil(rows / 4), ld_f6] bytes.
+ * cr_gemm_e2m3_rowscale is cr_gemm_s4s4_rowscale on two such operands (lda, ldb: bytes per
+ * quad, >= 3 K_pad, multiples of 16).  cr_linear_w4a4_e2m3 is cr_linear_w4a4 with the weight
+ * in that form and cr_linear_w4a4_e2m3_workspace_bytes(M, K) bytes of workspace.
  */
 cr_status cr_quant_weight_w4_e2m3(const void *w, cr_dtype w_dtype, int64_t ld_w, int64_t N, int64_t K,
                                   uint8_t *w_f6, int64_t ld_f6, float *w_scale, uint32_t flags, hipStream_t stream);

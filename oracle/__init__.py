@@ -402,27 +402,27 @@ def e2m3(code: int) -> float:
 
 
 def pack_e2m3(q: np.ndarray) -> np.ndarray:
-    """Codes [rows, K_pad] (-7..7, K_pad % 128 == 0) -> E2M3 fields [rows, 3 K_pad / 4] uint8."""
+    """Codes [rows, K_pad] (-7..7, K_pad % 128 == 0) -> E2M3 fields in quads of rows:
+    [ceil(rows / 4), 3 K_pad] uint8 (one array row per quad of four code rows)."""
     q = np.ascontiguousarray(q, np.int8)
     n, kp = q.shape
     assert kp % 128 == 0
-    p = np.empty((n, 3 * kp // 4), np.uint8)
-    assert lib().or_pack_e2m3(_p(q), n, kp, kp, _p(p), 3 * kp // 4) == 0
+    p = np.empty(((n + 3) // 4, 3 * kp), np.uint8)
+    assert lib().or_pack_e2m3(_p(q), n, kp, kp, _p(p), 3 * kp) == 0
     return p
 
 
-def unpack_e2m3(p: np.ndarray, K_pad: int) -> np.ndarray:
+def unpack_e2m3(p: np.ndarray, K_pad: int, n_rows: int) -> np.ndarray:
     p = np.ascontiguousarray(p, np.uint8)
-    n = p.shape[0]
-    q = np.empty((n, K_pad), np.int8)
-    assert lib().or_unpack_e2m3(_p(p), n, K_pad, p.shape[1], _p(q), K_pad) == 0
+    assert p.shape[0] == (n_rows + 3) // 4
+    q = np.empty((n_rows, K_pad), np.int8)
+    assert lib().or_unpack_e2m3(_p(p), n_rows, K_pad, p.shape[1], _p(q), K_pad) == 0
     return q
 
 
-def gemm_e2m3(a: np.ndarray, b: np.ndarray, K_pad: int) -> np.ndarray:
+def gemm_e2m3(a: np.ndarray, b: np.ndarray, K_pad: int, M: int, N: int) -> np.ndarray:
     a = np.ascontiguousarray(a, np.uint8)
     b = np.ascontiguousarray(b, np.uint8)
-    M, N = a.shape[0], b.shape[0]
     acc = np.empty((M, N), np.int32)
     assert lib().or_gemm_e2m3(_p(a), a.shape[1], _p(b), b.shape[1], M, N, K_pad, _p(acc), N) == 0
     return acc

@@ -644,12 +644,15 @@ int or_linear_w4a8(const void *x, int x_dtype, int64_t ld_x, int swiglu, int64_t
 
 /* This library's second storage form of 4-bit code rows (the pages describe none): every
  * code -7..7 is stored as the E2M3 number of the same value, so that matrix cores with
- * 6-bit floating-point inputs multiply the codes directly and exactly.  A row of K_pad
- * codes takes 3 K_pad / 4 bytes in units of 96 bytes per 128 codes.  A unit's quarters of
- * 32 codes Q0 (codes 0..31), Q1, Q2, Q3 each form a 192-bit field, code e in bits
- * 6e .. 6e+5; the unit holds the first 16 bytes of the fields of Q0, Q2, Q1, Q3 (bits
- * 0..127, little-endian), then their last 8 bytes (bits 128..191) in the same order.  The
- * codes follow the column order of the flags, as in the nibble form. */
+ * 6-bit floating-point inputs multiply the codes directly and exactly.  A row's 128-code
+ * unit takes 96 bytes: its quarters of 32 codes Q0 (codes 0..31), Q1, Q2, Q3 each form a
+ * 192-bit field, code e in bits 6e .. 6e+5; the unit holds the first 16 bytes of the fields
+ * of Q0, Q2, Q1, Q3 (bits 0..127, little-endian), then their last 8 bytes in the same order.
+ * Rows are stored in quads: rows 4q .. 4q+3 occupy the ld_p bytes from q * ld_p (ld_p >=
+ * 3 K_pad / 4 * 4), and unit u of row 4q + i sits at u * 384 + i * 96 inside them, so the four
+ * rows' units u are contiguous.  Bytes of rows past n_rows in the last quad are unused (the
+ * packing here writes zeros).  The codes follow the column order of the flags, as in the
+ * nibble form. */
 
 /* the code whose E2M3 value is q (+0 for 0), found by search over the 64 codes */
 static uint8_t e2m3_code_of(int q)
@@ -659,33 +662,31 @@ static uint8_t e2m3_code_of(int q)
     return 0xFF;
 }
 
-/* byte of bit `bit` (0..191) of quarter g's field in a row */
-static int64_t e2m3_field_byte(int64_t g, int bit)
+/* byte of bit `bit` (0..191) of quarter g's field of row n, from the start of the buffer */
+static int64_t e2m3_field_byte(int64_t n, int64_t ld_p, int64_t g, int bit)
 {
     static const int slot[4] = {0, 2, 1, 3};
-    const int64_t unit = 96 * (g / 4), k = slot[g % 4];
+    const int64_t unit = (n / 4) * ld_p + 384 * (g / 4) + 96 * (n % 4), k = slot[g % 4];
     const int byte = bit / 8;
     return byte < 16 ? unit + 16 * k + byte : unit + 64 + 8 * k + (byte - 16);
 }
 
-/* Codes q [n_rows, ld_q] (each -7..7) -> E2M3 fields p [n_rows, ld_p bytes]; returns 0, or
- * -1 if a code is out of range. */
+/* Codes q [n_rows, ld_q] (each -7..7) -> E2M3 fields p [ceil(n_rows / 4) quads of ld_p
+ * bytes]; returns 0, or -1 if a code is out of range. */
 int or_pack_e2m3(const int8_t *q, int64_t n_rows, int64_t K_pad, int64_t ld_q, uint8_t *p, int64_t ld_p)
 {
     uint8_t table[15];
     for (int v = -7; v <= 7; v++) table[v + 7] = e2m3_code_of(v);
-    for (int64_t n = 0; n < n_rows; n++) {
-        uint8_t *row = p + n * ld_p;
-        memset(row, 0, (size_t)(3 * K_pad / 4));
+    memset(p, 0, (size_t)(((n_rows + 3) / 4) * ld_p));
+    for (int64_t n = 0; n < n_rows; n++)
         for (int64_t g = 0; g < K_pad / 32; g++)
             for (int e = 0; e < 32; e++) {
                 const int v = q[n * ld_q + 32 * g + e];
                 if (v < -7 || v > 7) return -1;
                 const uint32_t c = table[v + 7];
                 for (int b = 0; b < 6; b++)
-                    if ((c >> b) & 1) row[e2m3_field_byte(g, 6 * e + b)] |= (uint8_t)(1u << ((6 * e + b) % 8));
+                    if ((c >> b) & 1) p[e2m3_field_byte(n, ld_p, g, 6 * e + b)] |= (uint8_t)(1u << ((6 * e + b) % 8));
             }
-    }
     return 0;
 }
 
@@ -693,22 +694,21 @@ int or_pack_e2m3(const int8_t *q, int64_t n_rows, int64_t K_pad, int64_t ld_q, u
  * in -7..7. */
 int or_unpack_e2m3(const uint8_t *p, int64_t n_rows, int64_t K_pad, int64_t ld_p, int8_t *q, int64_t ld_q)
 {
-    for (int64_t n = 0; n < n_rows; n++) {
-        const uint8_t *row = p + n * ld_p;
+    for (int64_t n = 0; n < n_rows; n++)
         for (int64_t g = 0; g < K_pad / 32; g++)
             for (int e = 0; e < 32; e++) {
                 uint8_t c = 0;
                 for (int b = 0; b < 6; b++)
-                    if ((row[e2m3_field_byte(g, 6 * e + b)] >> ((6 * e + b) % 8)) & 1) c |= (uint8_t)(1u << b);
+                    if ((p[e2m3_field_byte(n, ld_p, g, 6 * e + b)] >> ((6 * e + b) % 8)) & 1) c |= (uint8_t)(1u << b);
                 const float v = or_e2m3(c);
                 if (v != floorf(v) || v < -7.0f || v > 7.0f) return -1;
                 q[n * ld_q + 32 * g + e] = (int8_t)v;
             }
-    }
     return 0;
 }
 
-/* acc[m, n] = sum_k A[m, k] B[n, k] over the codes of two E2M3-field rows. */
+/* acc[m, n] = sum_k A[m, k] B[n, k] over the codes of two E2M3-field operands (quads of
+ * lda and ldb bytes). */
 int or_gemm_e2m3(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb, int64_t M, int64_t N,
                  int64_t K_pad, int32_t *acc, int64_t ldc)
 {

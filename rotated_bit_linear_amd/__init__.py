@@ -345,10 +345,13 @@ def cr_quant_act_w4_e2m3(x, K, swiglu, x_f6, x_scale, flags=0, stream=None):
 
 
 def cr_gemm_e2m3_rowscale(a_f6, a_scale, b_f6, b_scale, c, bias=None, K_pad=None, stream=None):
-    M, lda = _rows_ld(a_f6)
-    N, ldb = _rows_ld(b_f6)
-    _, ldc = _rows_ld(c)
-    kp = 4 * a_f6.shape[1] // 3 if K_pad is None else K_pad
+    """E2M3-field operands are [quads, >= 3 K_pad] uint8 (four code rows per tensor row); M and N
+    are the output's extents."""
+    _, lda = _rows_ld(a_f6)
+    _, ldb = _rows_ld(b_f6)
+    M, ldc = _rows_ld(c)
+    N = c.shape[1]
+    kp = a_f6.shape[1] // 3 if K_pad is None else K_pad
     _check("cr_gemm_e2m3_rowscale", lib().cr_gemm_e2m3_rowscale(
         _ptr(a_f6), lda, _ptr(a_scale), _ptr(b_f6), ldb, _ptr(b_scale), _ptr(bias), M, N, kp,
         _ptr(c), _TORCH_TO_CR[c.dtype], ldc, _stream(stream)))
@@ -360,8 +363,9 @@ def cr_linear_w4a4_e2m3_workspace_bytes(M, K) -> int:
 
 def cr_linear_w4a4_e2m3(x, K, swiglu, w_f6, w_scale, out, workspace, bias=None, flags=0, stream=None):
     M, ld_x = _rows_ld(x)
-    N, ld_f6 = _rows_ld(w_f6)
+    _, ld_f6 = _rows_ld(w_f6)
     _, ldc = _rows_ld(out)
+    N = out.shape[1]
     _check("cr_linear_w4a4_e2m3", lib().cr_linear_w4a4_e2m3(
         _ptr(x), _TORCH_TO_CR[x.dtype], ld_x, int(bool(swiglu)), M, K, _ptr(w_f6), ld_f6, _ptr(w_scale), N,
         _ptr(bias), _ptr(out), _TORCH_TO_CR[out.dtype], ldc, _ptr(workspace),
@@ -478,22 +482,24 @@ def linear_w4a4(x, w_s4, w_scale, K, out_dtype=torch.bfloat16, swiglu=False, bia
 
 
 def quant_weight_w4_e2m3(w: torch.Tensor, K: int | None = None, flags: int = 0):
-    """(4-bit codes as E2M3 fields [N, 3 K_pad / 4] uint8, scales [N] fp32) of a dense weight."""
+    """(4-bit codes as E2M3 fields in quads of rows [ceil(N / 4), 3 K_pad] uint8, scales [N]
+    fp32) of a dense weight; unused rows of the last quad are zero."""
     if K is None:
         K = w.shape[1]
     kp = padded_k(K)
-    q = torch.empty(w.shape[0], kp // 4 * 3, dtype=torch.uint8, device=w.device)
+    q = torch.zeros((w.shape[0] + 3) // 4, 3 * kp, dtype=torch.uint8, device=w.device)
     s = torch.empty(w.shape[0], dtype=torch.float32, device=w.device)
     cr_quant_weight_w4_e2m3(w, K, q, s, flags)
     return q, s
 
 
 def quant_act_w4_e2m3(x: torch.Tensor, K: int | None = None, swiglu: bool = False, flags: int = 0):
-    """(4-bit codes as E2M3 fields [M, 3 K_pad / 4] uint8, scales [M] fp32) of X or SwiGLU(H)."""
+    """(4-bit codes as E2M3 fields in quads of rows [ceil(M / 4), 3 K_pad] uint8, scales [M]
+    fp32) of X or SwiGLU(H); unused rows of the last quad are zero."""
     if K is None:
         K = x.shape[1] // 2 if swiglu else x.shape[1]
     kp = padded_k(K)
-    q = torch.empty(x.shape[0], kp // 4 * 3, dtype=torch.uint8, device=x.device)
+    q = torch.zeros((x.shape[0] + 3) // 4, 3 * kp, dtype=torch.uint8, device=x.device)
     s = torch.empty(x.shape[0], dtype=torch.float32, device=x.device)
     cr_quant_act_w4_e2m3(x, K, swiglu, q, s, flags)
     return q, s
@@ -501,7 +507,7 @@ def quant_act_w4_e2m3(x: torch.Tensor, K: int | None = None, swiglu: bool = Fals
 
 def linear_w4a4_e2m3(x, w_f6, w_scale, K, out_dtype=torch.bfloat16, swiglu=False, bias=None, flags=0, out=None):
     """y = x W^T (+ b) through the W4A4 route on the 6-bit matrix cores."""
-    M, N = x.shape[0], w_f6.shape[0]
+    M, N = x.shape[0], w_scale.shape[0]
     if out is None:
         out = torch.empty(M, N, dtype=out_dtype, device=x.device)
     ws = torch.empty(max(1, cr_linear_w4a4_e2m3_workspace_bytes(M, K)), dtype=torch.uint8, device=x.device)

@@ -789,7 +789,7 @@ cr_status cr_quant_weight_w4_e2m3(const void *w, cr_dtype w_dtype, int64_t ld_w,
     if (check_flags(flags) != CR_OK) return CR_ERR_INVALID_ARG;
     const int64_t kp = pad256(K);
     if (kp > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
-    if (ld_w < K || ld_f6 < kp / 4 * 3) return CR_ERR_INVALID_ARG;
+    if (ld_w < K || ld_f6 < 3 * kp) return CR_ERR_INVALID_ARG;
     if (!aligned(w, 16) || (ld_w * elem_size(w_dtype)) % 16 != 0) return CR_ERR_MISALIGNED;
     if (!aligned(w_f6, 16) || ld_f6 % 16 != 0 || !aligned(w_scale, 4)) return CR_ERR_MISALIGNED;
     if (N == 0) return CR_OK;
@@ -810,7 +810,7 @@ cr_status cr_quant_act_w4_e2m3(const void *x, cr_dtype x_dtype, int64_t ld_x, in
     if (swiglu && K > (int64_t)1 << 40) return CR_ERR_TOO_LARGE;
     const int64_t kp = pad256(K);
     if (kp > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
-    if (ld_x < (swiglu ? 2 * K : K) || ld_f6 < kp / 4 * 3) return CR_ERR_INVALID_ARG;
+    if (ld_x < (swiglu ? 2 * K : K) || ld_f6 < 3 * kp) return CR_ERR_INVALID_ARG;
     if (!aligned(x, 16) || (ld_x * elem_size(x_dtype)) % 16 != 0) return CR_ERR_MISALIGNED;
     if (!aligned(x_f6, 16) || ld_f6 % 16 != 0 || !aligned(x_scale, 4)) return CR_ERR_MISALIGNED;
     if (M == 0) return CR_OK;
@@ -834,7 +834,7 @@ cr_status cr_gemm_e2m3_rowscale(const uint8_t *a_f6, int64_t lda, const float *a
     if (M < 0 || N < 0 || K_pad < 1 || K_pad % 256 != 0 || M > kMaxRows || N > kMaxRows) return CR_ERR_INVALID_ARG;
     if (((M + 255) / 256) * ((N + 255) / 256) > (int64_t)(UINT32_MAX / 512)) return CR_ERR_TOO_LARGE;
     if (K_pad > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
-    if (lda < K_pad / 4 * 3 || ldb < K_pad / 4 * 3 || ldc < N) return CR_ERR_INVALID_ARG;   // lda, ldb in bytes
+    if (lda < 3 * K_pad || ldb < 3 * K_pad || ldc < N) return CR_ERR_INVALID_ARG;   // bytes per quad of rows
     if (!aligned(a_f6, 16) || !aligned(b_f6, 16) || lda % 16 != 0 || ldb % 16 != 0) return CR_ERR_MISALIGNED;
     if (!aligned(c, (size_t)elem_size(c_dtype))) return CR_ERR_MISALIGNED;
     if ((a_scale && !aligned(a_scale, 4)) || (b_scale && !aligned(b_scale, 4)) || (bias && !aligned(bias, 4)))
@@ -849,7 +849,7 @@ cr_status cr_gemm_e2m3_rowscale(const uint8_t *a_f6, int64_t lda, const float *a
 size_t cr_linear_w4a4_e2m3_workspace_bytes(int64_t M, int64_t K)
 {
     if (M < 1 || K < 1 || pad256(K) > CR_MAX_K_PAD) return 0;
-    return up256(up256((size_t)M * (size_t)(pad256(K) / 4 * 3)) + (size_t)M * 4);
+    return up256(up256((size_t)((M + 3) / 4) * (size_t)(3 * pad256(K))) + (size_t)M * 4);
 }
 
 cr_status cr_linear_w4a4_e2m3(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
@@ -865,7 +865,7 @@ cr_status cr_linear_w4a4_e2m3(const void *x, cr_dtype x_dtype, int64_t ld_x, int
     const int64_t kp = pad256(K);
     if (kp > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
     if (((M + 255) / 256) * ((N + 255) / 256) > (int64_t)(UINT32_MAX / 512)) return CR_ERR_TOO_LARGE;
-    if (ld_x < (swiglu ? 2 * K : K) || ld_f6 < kp / 4 * 3 || ldc < N) return CR_ERR_INVALID_ARG;
+    if (ld_x < (swiglu ? 2 * K : K) || ld_f6 < 3 * kp || ldc < N) return CR_ERR_INVALID_ARG;
     if ((M > 0 && !x) || (N > 0 && (!w_f6 || !w_scale)) || (M > 0 && N > 0 && !out)) return CR_ERR_INVALID_ARG;
     if (!aligned(x, 16) || (ld_x * elem_size(x_dtype)) % 16 != 0) return CR_ERR_MISALIGNED;
     if (!aligned(w_f6, 16) || ld_f6 % 16 != 0 || !aligned(w_scale, 4)) return CR_ERR_MISALIGNED;
@@ -876,9 +876,9 @@ cr_status cr_linear_w4a4_e2m3(const void *x, cr_dtype x_dtype, int64_t ld_x, int
     if (ws_bytes < cr_linear_w4a4_e2m3_workspace_bytes(M, K)) return CR_ERR_TOO_LARGE;
     cr_status s = current_device_ok();
     if (s != CR_OK) return s;
-    const int64_t lf = kp / 4 * 3;
+    const int64_t lf = 3 * kp;                  // one quad of rows
     uint8_t *x_f6 = static_cast<uint8_t *>(workspace);
-    float *x_scale = reinterpret_cast<float *>(x_f6 + up256((size_t)M * (size_t)lf));
+    float *x_scale = reinterpret_cast<float *>(x_f6 + up256((size_t)((M + 3) / 4) * (size_t)lf));
     hipError_t e = convrot::launch_quant_act_e2m3(x, (int)x_dtype, ld_x, swiglu != 0, M, K, x_f6, lf, x_scale,
                                                   (flags & CR_FLAG_FORCE_TWO_PASS) != 0,
                                                   (flags & CR_FLAG_BLOCK_TRANSPOSED) != 0, stream);

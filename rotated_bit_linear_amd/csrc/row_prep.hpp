@@ -351,11 +351,21 @@ __device__ __forceinline__ void store_codes(const float (&z)[16], const RowQuant
     else quantize_store16<true>(z, q.mult, dst);
 }
 
-// Codes of member t of block b stored in the row at `row`.  kBits == 6 (E2M3 fields): a
-// 128-code unit is 96 bytes, its quarters' first 16 bytes in the order Q0 Q2 Q1 Q3, then
-// their last 8 bytes in the same order; member t holds half t & 1 of quarter (t >> 1) & 3 of
-// unit t >> 3: bits 0..95 of the quarter's field (its head's bytes 0..11), or bits 96..191
-// (head bytes 12..15 and the 8-byte tail).
+// Start of row `row`'s codes in an output of row stride ld_out: for E2M3 fields (kBits == 6)
+// rows are stored in quads, ld_out bytes per quad, row 4q + i starting 96 i bytes into quad q
+// (its 128-code units then follow every 384 bytes, store_codes).
+template <int kBits>
+__device__ __forceinline__ int8_t *row_base(int8_t *out, int64_t row, int64_t ld_out)
+{
+    if constexpr (kBits == 6) return out + (row >> 2) * ld_out + (row & 3) * 96;
+    else return out + row * ld_out;
+}
+
+// Codes of member t of block b stored in the row at `row` (row_base).  kBits == 6 (E2M3
+// fields): a 128-code unit is 96 bytes, its quarters' first 16 bytes in the order Q0 Q2 Q1
+// Q3, then their last 8 bytes in the same order; member t holds half t & 1 of quarter
+// (t >> 1) & 3 of unit t >> 3 of the block: bits 0..95 of the quarter's field (its head's
+// bytes 0..11), or bits 96..191 (head bytes 12..15 and the 8-byte tail).
 template <int kBits = 8, bool kTables = true>
 __device__ __forceinline__ void store_codes(const float (&z)[16], const RowQuant &q, int8_t *row, int64_t b, int t)
 {
@@ -378,9 +388,9 @@ __device__ __forceinline__ void store_codes(const float (&z)[16], const RowQuant
         }
         // one dword and one 8-byte store either way: half 0 writes head bytes 0..3 and
         // 4..11, half 1 head bytes 12..15 and the tail (32-bit offsets from the row: fewer
-        // live registers than two 64-bit addresses)
+        // live registers than two 64-bit addresses); a row's units are 384 bytes apart (quads)
         const int g = (t >> 1) & 3, slot = ((g & 1) << 1) | (g >> 1), h = t & 1;
-        const int unit = (int)b * 192 + (t >> 3) * 96;
+        const int unit = (int)b * 768 + (t >> 3) * 384;
         const int o0 = unit + 16 * slot + 12 * h;
         const int o1 = h ? unit + 64 + 8 * slot : o0 + 4;
         *reinterpret_cast<uint32_t *>(row + o0) = w0;
@@ -463,7 +473,7 @@ __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, 
             return;
         }
         const RowQuant rq = row_quant<kBits>(zrow);
-        int8_t *orow = out + row * ld_out;
+        int8_t *orow = row_base<kBits>(out, row, ld_out);
 #pragma unroll
         for (int q = 0; q < RB; q++) {
             const int b = grp + q * G;
@@ -551,7 +561,7 @@ __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row,
     const int G = blockDim.x >> 4;
     float *tile = lds + grp * kTileStrideF;
     float *red = lds + G * kTileStrideF;
-    int8_t *orow = out + row * ld_out;
+    int8_t *orow = row_base<kBits>(out, row, ld_out);
 
     // Slices are visited twice, pass 1 then pass 2 (once with amax_only).  With
     // Loader::kTwoPassPrefetch the raw bytes of the next visit are requested before this one
@@ -681,7 +691,7 @@ __device__ __forceinline__ void row_prep_multi(const Loader &ld, int64_t n_rows,
             return;
         }
         const RowQuant rq = row_quant<kBits>(zrow);
-        if (live) store_codes<kBits, Loader::kE2M3Tables>(v, rq, out + row * ld_out, b, t);
+        if (live) store_codes<kBits, Loader::kE2M3Tables>(v, rq, row_base<kBits>(out, row, ld_out), b, t);
         if (live && b == 0 && t == 0) scale_out[row] = rq.scale;
     };
 

@@ -182,30 +182,31 @@ int main()
                                           P(), CR_I32, 8, P(), 1 << 20, 0, nullptr), CR_ERR_UNSUPPORTED_DTYPE);
     expect("w4a4 empty", cr_linear_w4a4(nullptr, CR_BF16, 512, 0, 0, 512, Q<uint8_t>(), 256, Q<float>(), 8, nullptr,
                                         nullptr, CR_BF16, 8, nullptr, 0, 0, nullptr), CR_OK);
-    // W4A4, E2M3 form: rows of 3 K_pad / 4 bytes
-    expect("f6w ld_f6 < 3K_pad/4", cr_quant_weight_w4_e2m3(P(), CR_FP32, 512, 8, 512, Q<uint8_t>(), 368, Q<float>(), 0,
-                                                          nullptr), CR_ERR_INVALID_ARG);
-    expect("f6w misaligned ld", cr_quant_weight_w4_e2m3(P(), CR_FP32, 512, 8, 512, Q<uint8_t>(), 392, Q<float>(), 0,
+    // W4A4, E2M3 form: quads of rows, 3 K_pad bytes each
+    expect("f6w ld_f6 < 3K_pad", cr_quant_weight_w4_e2m3(P(), CR_FP32, 512, 8, 512, Q<uint8_t>(), 1520, Q<float>(), 0,
+                                                        nullptr), CR_ERR_INVALID_ARG);
+    expect("f6w misaligned ld", cr_quant_weight_w4_e2m3(P(), CR_FP32, 512, 8, 512, Q<uint8_t>(), 1544, Q<float>(), 0,
                                                         nullptr), CR_ERR_MISALIGNED);
-    expect("f6w empty", cr_quant_weight_w4_e2m3(nullptr, CR_FP32, 512, 0, 512, nullptr, 384, nullptr, 0, nullptr), CR_OK);
-    expect("f6a swiglu ld_x < 2K", cr_quant_act_w4_e2m3(P(), CR_BF16, 1000, 1, 8, 512, Q<uint8_t>(), 384, Q<float>(),
+    expect("f6w empty", cr_quant_weight_w4_e2m3(nullptr, CR_FP32, 512, 0, 512, nullptr, 1536, nullptr, 0, nullptr),
+           CR_OK);
+    expect("f6a swiglu ld_x < 2K", cr_quant_act_w4_e2m3(P(), CR_BF16, 1000, 1, 8, 512, Q<uint8_t>(), 1536, Q<float>(),
                                                         0, nullptr), CR_ERR_INVALID_ARG);
-    expect("f6a dtype", cr_quant_act_w4_e2m3(P(), CR_I32, 512, 0, 8, 512, Q<uint8_t>(), 384, Q<float>(), 0, nullptr),
+    expect("f6a dtype", cr_quant_act_w4_e2m3(P(), CR_I32, 512, 0, 8, 512, Q<uint8_t>(), 1536, Q<float>(), 0, nullptr),
            CR_ERR_UNSUPPORTED_DTYPE);
-    expect("f6 gemm lda < 3K_pad/4", cr_gemm_e2m3_rowscale(Q<uint8_t>(), 368, Q<float>(), Q<uint8_t>(), 384,
-                                                           Q<float>(), nullptr, 8, 8, 512, P(), CR_BF16, 8, nullptr),
+    expect("f6 gemm lda < 3K_pad", cr_gemm_e2m3_rowscale(Q<uint8_t>(), 1520, Q<float>(), Q<uint8_t>(), 1536,
+                                                         Q<float>(), nullptr, 8, 8, 512, P(), CR_BF16, 8, nullptr),
            CR_ERR_INVALID_ARG);
-    expect("f6 gemm bias on i32", cr_gemm_e2m3_rowscale(Q<uint8_t>(), 384, Q<float>(), Q<uint8_t>(), 384, Q<float>(),
+    expect("f6 gemm bias on i32", cr_gemm_e2m3_rowscale(Q<uint8_t>(), 1536, Q<float>(), Q<uint8_t>(), 1536, Q<float>(),
                                                         Q<float>(), 8, 8, 512, P(), CR_I32, 8, nullptr),
            CR_ERR_INVALID_ARG);
-    expect("f6 gemm K_pad not a multiple of 256", cr_gemm_e2m3_rowscale(Q<uint8_t>(), 384, Q<float>(), Q<uint8_t>(),
-                                                                        384, Q<float>(), nullptr, 8, 8, 500, P(),
+    expect("f6 gemm K_pad not a multiple of 256", cr_gemm_e2m3_rowscale(Q<uint8_t>(), 1536, Q<float>(), Q<uint8_t>(),
+                                                                        1536, Q<float>(), nullptr, 8, 8, 500, P(),
                                                                         CR_BF16, 8, nullptr), CR_ERR_INVALID_ARG);
     expect("f6 layer small workspace",
-           cr_linear_w4a4_e2m3(P(), CR_BF16, 512, 0, 300, 512, Q<uint8_t>(), 384, Q<float>(), 8, nullptr, P(), CR_BF16,
+           cr_linear_w4a4_e2m3(P(), CR_BF16, 512, 0, 300, 512, Q<uint8_t>(), 1536, Q<float>(), 8, nullptr, P(), CR_BF16,
                                8, P(), cr_linear_w4a4_e2m3_workspace_bytes(300, 512) - 1, 0, nullptr),
            CR_ERR_TOO_LARGE);
-    expect("f6 layer empty", cr_linear_w4a4_e2m3(nullptr, CR_BF16, 512, 0, 0, 512, Q<uint8_t>(), 384, Q<float>(), 8,
+    expect("f6 layer empty", cr_linear_w4a4_e2m3(nullptr, CR_BF16, 512, 0, 0, 512, Q<uint8_t>(), 1536, Q<float>(), 8,
                                                  nullptr, nullptr, CR_BF16, 8, nullptr, 0, 0, nullptr), CR_OK);
     auto na = [&](int64_t M, int64_t N, int64_t K, size_t mt) {
         return cr_linear_nvfp4_noalloc(P(), CR_BF16, 5376, 0, M, K, nullptr, Q<uint8_t>(), 2688, Q<uint8_t>(), 336,
@@ -224,7 +225,7 @@ int main()
                                                        8, nullptr, P(), CR_BF16, 8, P(), 1 << 20, 0, nullptr),
                CR_ERR_NO_DEVICE);
         expect("f6 layer without a device",
-               cr_linear_w4a4_e2m3(P(), CR_BF16, 512, 0, 300, 512, Q<uint8_t>(), 384, Q<float>(), 8, nullptr, P(),
+               cr_linear_w4a4_e2m3(P(), CR_BF16, 512, 0, 300, 512, Q<uint8_t>(), 1536, Q<float>(), 8, nullptr, P(),
                                    CR_BF16, 8, P(), 1 << 20, 0, nullptr), CR_ERR_NO_DEVICE);
         expect("aw4 without a device", cr_quant_act_w4(P(), CR_BF16, 512, 0, 8, 512, Q<uint8_t>(), 256, Q<float>(), 0,
                                                        nullptr), CR_ERR_NO_DEVICE);

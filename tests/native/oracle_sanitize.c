@@ -278,10 +278,10 @@ static void w4a8_case(int64_t M, int64_t N, int64_t K)
         free(hp);
     }
     for (int dt = 0; dt < 3; dt++) CHECK(or_linear_w4a4(x, 0, K, 0, M, K, p, lp, s, N, s, y, dt, N) == 0, "w4a4");
-    /* the E2M3 field form of the same codes: exactly 3 K_pad / 4 bytes per row */
+    /* the E2M3 field form of the same codes: quads of rows, exactly 3 K_pad bytes each */
     {
-        const int64_t l6 = 3 * kp / 4;
-        uint8_t *f = xmalloc((size_t)(N * l6));
+        const int64_t l6 = 3 * kp;                              /* one quad of rows */
+        uint8_t *f = xmalloc((size_t)((N + 3) / 4 * l6));
         int8_t *q2 = xmalloc((size_t)(N * kp));
         CHECK(or_pack_e2m3(q, N, kp, kp, f, l6) == 0, "pack_e2m3");
         CHECK(or_unpack_e2m3(f, N, kp, l6, q2, kp) == 0 && memcmp(q, q2, (size_t)(N * kp)) == 0, "unpack_e2m3");

@@ -191,8 +191,10 @@ def test_linear_w4a4_against_oracle(M, N, K, dt, swiglu, flags):
 
 
 # ------------------------------------------------ the E2M3 execution form ----
-# The same codes stored as E2M3 fields (6-bit floats of equal value) and multiplied on the
-# 6-bit matrix cores: codes, scales, int32 sums and outputs must equal the oracle's.
+# The same codes stored as E2M3 fields (6-bit floats of equal value, rows in quads) and
+# multiplied on the 6-bit matrix cores: codes, scales, int32 sums and outputs must equal the
+# oracle's.  The conveniences zero their outputs first, so the unused rows of a last quad
+# compare equal to the oracle's zeros.
 
 def _e2m3(p_nibbles: np.ndarray) -> np.ndarray:
     """The oracle's E2M3 form of the codes of nibble-packed rows."""
@@ -245,7 +247,7 @@ def test_gemm_e2m3_int32_exact_and_epilogues(M, N, Kp):
     sb = torch.rand(N, generator=g) * 1e-2
     sa[0] = 0.0
     bias = torch.randn(N, generator=g)
-    acc = oracle.gemm_e2m3(a.numpy(), b.numpy(), Kp)
+    acc = oracle.gemm_e2m3(a.numpy(), b.numpy(), Kp, M, N)
     ad, bd, sad, sbd, biasd = a.to(dev()), b.to(dev()), sa.to(dev()), sb.to(dev()), bias.to(dev())
     for ldc in (N + 9, (N + 7) // 8 * 8 + 8):
         for odt in (synth.DT_I32, synth.DT_BF16, synth.DT_FP16, synth.DT_FP32):
@@ -267,18 +269,18 @@ def test_gemm_e2m3_int32_exact_and_epilogues(M, N, Kp):
 
 
 def test_gemm_e2m3_strided_operands_and_worst_case():
-    """Row strides beyond 3 K_pad / 4 on both operands; and the largest accepted K_pad with
-    codes +-7 (|sum| = 49 * 133120 < 2^23: the fp32 sums stay exact)."""
+    """Quad strides beyond 3 K_pad on both operands; and the largest accepted K_pad with codes
+    +-7 (|sum| = 49 * 133120 < 2^23: the fp32 sums stay exact)."""
     M, N, Kp = 300, 260, 1280
     g = torch.Generator().manual_seed(6)
     qa = torch.randint(-7, 8, (M, Kp), generator=g, dtype=torch.int32).to(torch.int8)
     qb = torch.randint(-7, 8, (N, Kp), generator=g, dtype=torch.int32).to(torch.int8)
     a = torch.from_numpy(oracle.pack_e2m3(qa.numpy()))
     b = torch.from_numpy(oracle.pack_e2m3(qb.numpy()))
-    acc = oracle.gemm_e2m3(a.numpy(), b.numpy(), Kp)
-    lf = Kp // 4 * 3
-    af = torch.full((M, lf + 48), 0x3F, dtype=torch.uint8)
-    bf = torch.full((N, lf + 16), 0x3F, dtype=torch.uint8)
+    acc = oracle.gemm_e2m3(a.numpy(), b.numpy(), Kp, M, N)
+    lf = 3 * Kp
+    af = torch.full(((M + 3) // 4, lf + 48), 0x3F, dtype=torch.uint8)
+    bf = torch.full(((N + 3) // 4, lf + 16), 0x3F, dtype=torch.uint8)
     af[:, :lf] = a
     bf[:, :lf] = b
     c = torch.empty(M, N, dtype=torch.int32, device=dev())
@@ -297,7 +299,7 @@ def test_gemm_e2m3_strided_operands_and_worst_case():
     qb[4] = 0
     a = torch.from_numpy(oracle.pack_e2m3(qa.numpy()))
     b = torch.from_numpy(oracle.pack_e2m3(qb.numpy()))
-    acc = oracle.gemm_e2m3(a.numpy(), b.numpy(), Kp)
+    acc = oracle.gemm_e2m3(a.numpy(), b.numpy(), Kp, 3, 5)
     assert int(np.abs(acc).max()) == 49 * Kp
     say(f"cr_gemm_e2m3_rowscale worst-case accumulator K_pad={Kp}")
     c = torch.empty(3, 5, dtype=torch.int32, device=dev())
@@ -413,7 +415,7 @@ def test_empty_extents_are_no_ops():
         fn(x, 512, False, wp[:0], ws[:0], out[:, :0], None)            # no columns
     q = torch.empty(0, 256, dtype=torch.uint8, device=dev())
     rbl.cr_quant_act_w4(x[:0], 512, False, q, torch.empty(0, device=dev()))
-    rbl.cr_quant_act_w4_e2m3(x[:0], 512, False, torch.empty(0, 384, dtype=torch.uint8, device=dev()),
+    rbl.cr_quant_act_w4_e2m3(x[:0], 512, False, torch.empty(0, 1536, dtype=torch.uint8, device=dev()),
                              torch.empty(0, device=dev()))
     torch.cuda.synchronize()
     assert (out == 7.0).all()
