@@ -218,7 +218,7 @@ struct ActLoader {
     // rows of 65-128 blocks stream twice: measured faster than four blocks per group here
     // (the second read is served from the cache, and a slice workgroup has 960 threads)
     static constexpr bool kFourBlocks = false;
-    static constexpr bool kE2M3Tables = true;
+    static constexpr bool kE2M3Fast = true;
     static constexpr bool kFetchAfterDecode = true;
     static constexpr bool kTwoPassPrefetch = true;
     static constexpr bool kSigTable = false;
@@ -250,7 +250,7 @@ struct SwigluLoader {
     // as for ActLoader (and fp16/fp32 gates with a pre-scale would spill at four blocks)
     static constexpr bool kFourBlocks = false;
     // fp16/fp32 gates (the refined reciprocal, no sigma table) leave no room for the tables
-    static constexpr bool kE2M3Tables = DT == 0;
+    static constexpr bool kE2M3Fast = DT == 0;
     static constexpr bool kFetchAfterDecode = true;
     // fp32 segments (128 bytes a lane) leave no registers for a second buffer
     static constexpr bool kTwoPassPrefetch = DT != 2;

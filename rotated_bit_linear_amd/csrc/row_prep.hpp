@@ -366,7 +366,7 @@ __device__ __forceinline__ int8_t *row_base(int8_t *out, int64_t row, int64_t ld
 // Q3, then their last 8 bytes in the same order; member t holds half t & 1 of quarter
 // (t >> 1) & 3 of unit t >> 3 of the block: bits 0..95 of the quarter's field (its head's
 // bytes 0..11), or bits 96..191 (head bytes 12..15 and the 8-byte tail).
-template <int kBits = 8, bool kTables = true>
+template <int kBits = 8, bool kFast = true>
 __device__ __forceinline__ void store_codes(const float (&z)[16], const RowQuant &q, int8_t *row, int64_t b, int t)
 {
     if constexpr (kBits == 8) {
@@ -379,22 +379,32 @@ __device__ __forceinline__ void store_codes(const float (&z)[16], const RowQuant
         else quantize_store16_s4<true>(z, q.mult, dst);
     } else {
         uint32_t w0, w1, w2;
-        if constexpr (kTables) {
+        if constexpr (kFast) {
             if (q.folded) quantize_e2m3_16_tables<false>(z, q.mult, w0, w1, w2);
             else quantize_e2m3_16_tables<true>(z, q.mult, w0, w1, w2);
         } else {
             if (q.folded) quantize_e2m3_16<false>(z, q.mult, w0, w1, w2);
             else quantize_e2m3_16<true>(z, q.mult, w0, w1, w2);
         }
-        // one dword and one 8-byte store either way: half 0 writes head bytes 0..3 and
-        // 4..11, half 1 head bytes 12..15 and the tail (32-bit offsets from the row: fewer
-        // live registers than two 64-bit addresses); a row's units are 384 bytes apart (quads)
+        // A row's units are 384 bytes apart (quads); 32-bit offsets from the row keep fewer
+        // registers live.  Members t and t ^ 1 (adjacent lanes, the same block of the same
+        // row: both store or neither) hold the two halves of one quarter.
         const int g = (t >> 1) & 3, slot = ((g & 1) << 1) | (g >> 1), h = t & 1;
         const int unit = (int)b * 768 + (t >> 3) * 384;
-        const int o0 = unit + 16 * slot + 12 * h;
-        const int o1 = h ? unit + 64 + 8 * slot : o0 + 4;
-        *reinterpret_cast<uint32_t *>(row + o0) = w0;
-        *reinterpret_cast<uint2 *>(row + o1) = make_uint2(w1, w2);
+        if constexpr (kFast) {
+            // half 1's first word (head bytes 12..15) moves to half 0 by DPP: half 0 stores
+            // the whole 16-byte head, half 1 the 8-byte tail (aligned, contiguous in a unit)
+            const uint32_t w0_partner = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w0, 0xB1, 0xF, 0xF, true);  // quad_perm 1,0,3,2
+            if (h == 0) *reinterpret_cast<uint4 *>(row + unit + 16 * slot) = make_uint4(w0, w1, w2, w0_partner);
+            else *reinterpret_cast<uint2 *>(row + unit + 64 + 8 * slot) = make_uint2(w1, w2);
+        } else {
+            // one dword and one 8-byte store per lane: half 0 writes head bytes 0..3 and 4..11,
+            // half 1 head bytes 12..15 and the tail
+            const int o0 = unit + 16 * slot + 12 * h;
+            const int o1 = h ? unit + 64 + 8 * slot : o0 + 4;
+            *reinterpret_cast<uint32_t *>(row + o0) = w0;
+            *reinterpret_cast<uint2 *>(row + o1) = make_uint2(w1, w2);
+        }
     }
 }
 
@@ -408,8 +418,9 @@ __host__ __device__ constexpr size_t row_prep_lds_bytes(int threads)
 // Loader concept:
 //   static constexpr bool kFourBlocks;               rows of 65-128 blocks are held in one
 //                                                    pass, four blocks per lane group
-//   static constexpr bool kE2M3Tables;               E2M3 codes through byte tables (else
-//                                                    arithmetic: fewer live registers)
+//   static constexpr bool kE2M3Fast;                 E2M3 codes through byte tables and
+//                                                    paired stores (else arithmetic codes and
+//                                                    per-lane stores: fewer live registers)
 //   static constexpr bool kFetchAfterDecode;         request the next row after decoding
 //                                                    this one (else before: two buffers)
 //   static constexpr bool kTwoPassPrefetch;          two-pass rows: request the next slice
@@ -477,7 +488,7 @@ __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, 
 #pragma unroll
         for (int q = 0; q < RB; q++) {
             const int b = grp + q * G;
-            if (b < nb) store_codes<kBits, Loader::kE2M3Tables>(v[q], rq, orow, b, t);
+            if (b < nb) store_codes<kBits, Loader::kE2M3Fast>(v[q], rq, orow, b, t);
         }
         if (tid == 0) scale_out[row] = rq.scale;
     };
@@ -623,7 +634,7 @@ __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row,
             decode_slice(s, cur, v);
         }
         hadamard256(v, tile, t, natural);
-        if (b < nb) store_codes<kBits, Loader::kE2M3Tables>(v, rq, orow, b, t);
+        if (b < nb) store_codes<kBits, Loader::kE2M3Fast>(v, rq, orow, b, t);
     }
     if (tid == 0) scale_out[row] = rq.scale;
 }
@@ -691,7 +702,7 @@ __device__ __forceinline__ void row_prep_multi(const Loader &ld, int64_t n_rows,
             return;
         }
         const RowQuant rq = row_quant<kBits>(zrow);
-        if (live) store_codes<kBits, Loader::kE2M3Tables>(v, rq, row_base<kBits>(out, row, ld_out), b, t);
+        if (live) store_codes<kBits, Loader::kE2M3Fast>(v, rq, row_base<kBits>(out, row, ld_out), b, t);
         if (live && b == 0 && t == 0) scale_out[row] = rq.scale;
     };
 
