@@ -381,6 +381,17 @@ cr_status cr_linear_w4a4(const void *x, cr_dtype x_dtype, int64_t ld_x, int swig
  */
 cr_status cr_quant_weight_w4_e2m3(const void *w, cr_dtype w_dtype, int64_t ld_w, int64_t N, int64_t K,
                                   uint8_t *w_f6, int64_t ld_f6, float *w_scale, uint32_t flags, hipStream_t stream);
+/*
+ * The same weight codes moved from the nibble form (w_s4 [N, ld_s4 bytes], as written by
+ * cr_quant_weight_w4; ld_s4 >= K_pad / 2, a multiple of 16) to the E2M3 form (w_f6
+ * [ceil(N / 4), ld_f6 bytes], ld_f6 >= 3 K_pad, a multiple of 16), for a 4-bit weight kept in
+ * the compact form; the row scales stay as they are.  The codes must be -7..7 (nibble 8 is
+ * not a code of the form and gives an unspecified field).  The codes are copied, so the result
+ * equals cr_quant_weight_w4_e2m3 of the same dense weight bit for bit.  K_pad a multiple of
+ * 256, at most CR_MAX_K_PAD.
+ */
+cr_status cr_repack_w4_e2m3(const uint8_t *w_s4, int64_t ld_s4, int64_t N, int64_t K_pad, uint8_t *w_f6,
+                            int64_t ld_f6, hipStream_t stream);
 cr_status cr_quant_act_w4_e2m3(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
                                uint8_t *x_f6, int64_t ld_f6, float *x_scale, uint32_t flags, hipStream_t stream);
 cr_status cr_gemm_e2m3_rowscale(const uint8_t *a_f6, int64_t lda, const float *a_scale,

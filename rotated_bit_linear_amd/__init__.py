@@ -85,6 +85,7 @@ def lib() -> C.CDLL:
             "cr_linear_w4a4": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, i64, vp, i64, vp, vp, C.c_int,
                                          i64, vp, sz, u32, vp]),
             "cr_quant_weight_w4_e2m3": (C.c_int, [vp, C.c_int, i64, i64, i64, vp, i64, vp, u32, vp]),
+            "cr_repack_w4_e2m3": (C.c_int, [vp, i64, i64, i64, vp, i64, vp]),
             "cr_quant_act_w4_e2m3": (C.c_int, [vp, C.c_int, i64, C.c_int, i64, i64, vp, i64, vp, u32, vp]),
             "cr_gemm_e2m3_rowscale": (C.c_int, [vp, i64, vp, vp, i64, vp, vp, i64, i64, i64, vp, C.c_int, i64, vp]),
             "cr_linear_w4a4_e2m3_workspace_bytes": (sz, [i64, i64]),
@@ -336,6 +337,14 @@ def cr_quant_weight_w4_e2m3(w, K, w_f6, w_scale, flags=0, stream=None):
         _ptr(w), _TORCH_TO_CR[w.dtype], ld_w, N, K, _ptr(w_f6), ld_f6, _ptr(w_scale), flags, _stream(stream)))
 
 
+def cr_repack_w4_e2m3(w_s4, w_f6, K_pad=None, stream=None):
+    N, ld_s4 = _rows_ld(w_s4)
+    _, ld_f6 = _rows_ld(w_f6)
+    kp = 2 * w_s4.shape[1] if K_pad is None else K_pad
+    _check("cr_repack_w4_e2m3", lib().cr_repack_w4_e2m3(_ptr(w_s4), ld_s4, N, kp, _ptr(w_f6), ld_f6,
+                                                          _stream(stream)))
+
+
 def cr_quant_act_w4_e2m3(x, K, swiglu, x_f6, x_scale, flags=0, stream=None):
     M, ld_x = _rows_ld(x)
     _, ld_f6 = _rows_ld(x_f6)
@@ -512,4 +521,13 @@ def linear_w4a4_e2m3(x, w_f6, w_scale, K, out_dtype=torch.bfloat16, swiglu=False
         out = torch.empty(M, N, dtype=out_dtype, device=x.device)
     ws = torch.empty(max(1, cr_linear_w4a4_e2m3_workspace_bytes(M, K)), dtype=torch.uint8, device=x.device)
     cr_linear_w4a4_e2m3(x, K, swiglu, w_f6, w_scale, out, ws, bias=bias, flags=flags)
+    return out
+
+
+def repack_w4_e2m3(w_s4: torch.Tensor, K_pad: int | None = None):
+    """The E2M3 form [ceil(N / 4), 3 K_pad] uint8 of nibble-form 4-bit rows [N, K_pad / 2] (the
+    row scales are unchanged); unused rows of the last quad are zero."""
+    kp = 2 * w_s4.shape[1] if K_pad is None else K_pad
+    out = torch.zeros((w_s4.shape[0] + 3) // 4, 3 * kp, dtype=torch.uint8, device=w_s4.device)
+    cr_repack_w4_e2m3(w_s4, out, K_pad=kp)
     return out

@@ -800,6 +800,20 @@ cr_status cr_quant_weight_w4_e2m3(const void *w, cr_dtype w_dtype, int64_t ld_w,
                                                       (flags & CR_FLAG_BLOCK_TRANSPOSED) != 0, stream));
 }
 
+cr_status cr_repack_w4_e2m3(const uint8_t *w_s4, int64_t ld_s4, int64_t N, int64_t K_pad, uint8_t *w_f6,
+                            int64_t ld_f6, hipStream_t stream)
+{
+    if (N > 0 && (!w_s4 || !w_f6)) return CR_ERR_INVALID_ARG;
+    if (N < 0 || N > kMaxRows || K_pad < 1 || K_pad % 256 != 0) return CR_ERR_INVALID_ARG;
+    if (K_pad > CR_MAX_K_PAD) return CR_ERR_TOO_LARGE;
+    if (ld_s4 < K_pad / 2 || ld_f6 < 3 * K_pad) return CR_ERR_INVALID_ARG;
+    if (!aligned(w_s4, 16) || ld_s4 % 16 != 0 || !aligned(w_f6, 16) || ld_f6 % 16 != 0) return CR_ERR_MISALIGNED;
+    if (N == 0) return CR_OK;
+    cr_status s = current_device_ok();
+    if (s != CR_OK) return s;
+    return from_hip(convrot::launch_repack_w4_e2m3(w_s4, ld_s4, N, K_pad, w_f6, ld_f6, stream));
+}
+
 cr_status cr_quant_act_w4_e2m3(const void *x, cr_dtype x_dtype, int64_t ld_x, int swiglu, int64_t M, int64_t K,
                                uint8_t *x_f6, int64_t ld_f6, float *x_scale, uint32_t flags, hipStream_t stream)
 {

@@ -32,6 +32,10 @@ hipError_t launch_quant_weight_w4(const void *w, int dtype, int64_t ld_w, int64_
 hipError_t launch_quant_weight_e2m3(const void *w, int dtype, int64_t ld_w, int64_t N, int64_t K, uint8_t *w_f6,
                                     int64_t ld_f6, float *w_scale, bool two_pass, bool transposed, hipStream_t st);
 
+// nibble-form 4-bit rows [N, ld_s4] -> the same codes as E2M3 fields (quads of ld_f6 bytes)
+hipError_t launch_repack_w4_e2m3(const uint8_t *w_s4, int64_t ld_s4, int64_t N, int64_t K_pad, uint8_t *w_f6,
+                                 int64_t ld_f6, hipStream_t st);
+
 // W4A4: activation rows (swiglu: H [M, 2K], SwiGLU first) -> ConvRot256 -> packed 4-bit
 // codes [M, ld_s4 bytes] + scales, the format of launch_quant_weight_w4
 hipError_t launch_quant_act_w4(const void *x, int dtype, int64_t ld_x, bool swiglu, int64_t M, int64_t K,

@@ -543,6 +543,58 @@ hipError_t launch_quant_act_e2m3(const void *x, int dtype, int64_t ld_x, bool sw
     return launch_act_4bit<6>(x, dtype, ld_x, swiglu, M, K, x_f6, ld_f6, x_scale, two_pass, transposed, st);
 }
 
+// Nibble form -> E2M3 fields (W4A4 weights prepared once in the packed form): one thread per
+// 16-code group of a row.  The group's 8 bytes (byte j: codes j and 4 + j, byte 4 + j: codes
+// 8 + j and 12 + j, low nibble first) become 16 six-bit fields, stored where the E2M3 form
+// keeps that half of that quarter (rows in quads, store_codes' layout).  Codes are copied, not
+// recomputed: the results equal the E2M3 preparation of the same rows bit for bit.
+__global__ __launch_bounds__(256) void repack_w4_e2m3_kernel(const uint8_t *__restrict__ src, int64_t ld_s4,
+                                                             int64_t n_rows, int groups, uint8_t *__restrict__ dst,
+                                                             int64_t ld_f6)
+{
+    const int64_t total = n_rows * groups;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = i / groups;
+        const int G = (int)(i - row * groups);
+        // the group's bytes: 64-code unit G / 4, groups stored in the order G0 G2 G1 G3
+        const int p = G & 3, pslot = ((p & 1) << 1) | (p >> 1);
+        const uint2 d = *reinterpret_cast<const uint2 *>(src + row * ld_s4 + (G >> 2) * 32 + pslot * 8);
+        uint32_t w[3] = {0u, 0u, 0u};
+#pragma unroll
+        for (int c = 0; c < 16; c++) {
+            // code c: byte (c & 3) of the low (c < 8) or high word, high nibble when (c >> 2) is odd
+            const uint32_t word = (c < 8) ? d.x : d.y;
+            const uint32_t nib = (word >> (8 * (c & 3) + 4 * ((c >> 2) & 1))) & 15u;
+            const int q = (int)nib - (nib >= 8u ? 16 : 0);
+            const int m = (q < 0 ? -q : q) & 7;          // codes are -7..7 (nibble 8 is no code)
+            // E2M3 magnitude codes of 0..7 and the sign bit
+            const uint32_t mag = (uint32_t)((0x1E1C1A1814100800ull >> (8 * m)) & 0xFFu);
+            const uint32_t code = mag | (q < 0 ? 0x20u : 0u);
+            const int bit = 6 * c;
+            w[bit / 32] |= code << (bit % 32);
+            if (bit % 32 > 26) w[bit / 32 + 1] |= code >> (32 - bit % 32);
+        }
+        // quarter (G >> 1) & 3 of 128-code unit G >> 3, half G & 1
+        const int g = (G >> 1) & 3, slot = ((g & 1) << 1) | (g >> 1), h = G & 1;
+        uint8_t *base = dst + (row >> 2) * ld_f6 + (row & 3) * 96 + (int64_t)(G >> 3) * 384;
+        const int o0 = 16 * slot + 12 * h;
+        const int o1 = h ? 64 + 8 * slot : o0 + 4;
+        *reinterpret_cast<uint32_t *>(base + o0) = w[0];
+        *reinterpret_cast<uint2 *>(base + o1) = make_uint2(w[1], w[2]);
+    }
+}
+
+hipError_t launch_repack_w4_e2m3(const uint8_t *w_s4, int64_t ld_s4, int64_t N, int64_t K_pad, uint8_t *w_f6,
+                                 int64_t ld_f6, hipStream_t st)
+{
+    const int groups = (int)(K_pad / 16);
+    const int64_t total = N * groups;
+    const int64_t blocks = (total + 255) / 256;
+    const dim3 grid((unsigned)(blocks < 65536 ? blocks : 65536));
+    hipLaunchKernelGGL(repack_w4_e2m3_kernel, grid, dim3(256), 0, st, w_s4, ld_s4, N, groups, w_f6, ld_f6);
+    return hipGetLastError();
+}
+
 hipError_t launch_swiglu(const void *h, int dtype, int64_t ld_h, int64_t M, int64_t F, float *out,
                          int64_t ld_out, hipStream_t st)
 {

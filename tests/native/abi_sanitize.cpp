@@ -206,6 +206,11 @@ int main()
            cr_linear_w4a4_e2m3(P(), CR_BF16, 512, 0, 300, 512, Q<uint8_t>(), 1536, Q<float>(), 8, nullptr, P(), CR_BF16,
                                8, P(), cr_linear_w4a4_e2m3_workspace_bytes(300, 512) - 1, 0, nullptr),
            CR_ERR_TOO_LARGE);
+    expect("repack ld_f6 < 3K_pad", cr_repack_w4_e2m3(Q<uint8_t>(), 256, 8, 512, Q<uint8_t>(), 1520, nullptr),
+           CR_ERR_INVALID_ARG);
+    expect("repack K_pad not a multiple of 256", cr_repack_w4_e2m3(Q<uint8_t>(), 256, 8, 500, Q<uint8_t>(), 1536,
+                                                                   nullptr), CR_ERR_INVALID_ARG);
+    expect("repack empty", cr_repack_w4_e2m3(nullptr, 256, 0, 512, nullptr, 1536, nullptr), CR_OK);
     expect("f6 layer empty", cr_linear_w4a4_e2m3(nullptr, CR_BF16, 512, 0, 0, 512, Q<uint8_t>(), 1536, Q<float>(), 8,
                                                  nullptr, nullptr, CR_BF16, 8, nullptr, 0, 0, nullptr), CR_OK);
     auto na = [&](int64_t M, int64_t N, int64_t K, size_t mt) {

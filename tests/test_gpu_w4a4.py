@@ -236,6 +236,28 @@ def test_quant_weight_w4_e2m3_bit_exact(dt, N, K):
         assert_bits_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32), f"w_scale flags={flags}")
 
 
+@pytest.mark.parametrize("dt,N,K", W_CASES, ids=[f"dt{c[0]}-N{c[1]}-K{c[2]}" for c in W_CASES])
+def test_repack_w4_e2m3_equals_direct_preparation(dt, N, K):
+    """cr_repack_w4_e2m3 of the nibble-form weight equals cr_quant_weight_w4_e2m3 of the same
+    dense weight and the oracle's E2M3 packing of the oracle's codes, bit for bit (both
+    column orders); a nibble row stride beyond K_pad / 2 is honoured."""
+    w = _act(N, K, dt, 5 * N + K)
+    rp, _ = oracle.quant_weight_w4(_host(w, dt), dt, K)
+    wd = w.to(dev())
+    for flags in (0, BT):
+        say(f"cr_repack_w4_e2m3 dt={dt} N={N} K={K} flags={flags}")
+        p4, _ = rbl.quant_weight_w4(wd, K, flags=flags)
+        kp = p4.shape[1] * 2
+        wide = torch.full((N, kp // 2 + 32), 0x88, dtype=torch.uint8, device=dev())
+        wide[:, :kp // 2] = p4
+        f6 = rbl.repack_w4_e2m3(wide[:, :kp // 2], K_pad=kp)
+        d6, _ = rbl.quant_weight_w4_e2m3(wd, K, flags=flags)
+        torch.cuda.synchronize()
+        want = _e2m3(_bt_packed(rp) if flags & BT else rp)
+        assert_bits_equal(f6.cpu().numpy(), want, f"repacked fields flags={flags}")
+        assert_bits_equal(d6.cpu().numpy(), want, f"directly prepared fields flags={flags}")
+
+
 @pytest.mark.parametrize("M,N,Kp", G_CASES, ids=[f"M{c[0]}-N{c[1]}-K{c[2]}" for c in G_CASES])
 def test_gemm_e2m3_int32_exact_and_epilogues(M, N, Kp):
     g = torch.Generator().manual_seed(M * 13 + N + Kp)
