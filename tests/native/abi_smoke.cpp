@@ -1,7 +1,8 @@
 // Native consumer of the C ABI: no Python, no torch.  Device memory from hipMalloc, inputs
 // from a fixed-seed generator on the host.  Runs the layer through the component calls and
-// through cr_linear_nvfp4 (staged and short-batch paths, one and two streams) and checks
-// that every route gives the same bits; also checks argument errors come back as statuses.
+// through cr_linear_nvfp4 (staged and short-batch paths, one and two streams), and the
+// W4A8 / W4A4 variants through theirs, and checks that every route gives the same bits;
+// also checks argument errors come back as statuses.
 // Exit status 0 on success.
 #include <hip/hip_runtime.h>
 
@@ -118,6 +119,114 @@ int run_case(int64_t M, int64_t N, int64_t K, hipStream_t s_main, hipStream_t s_
     return 0;
 }
 
+// The 4-bit variants through their C calls: W4A8 and W4A4 (nibble and E2M3 forms) each as
+// components and as the layer call, the E2M3 weight both prepared directly and repacked
+// from the nibble form; all routes of one variant give the same bits, and the two W4A4
+// forms give the same bits.
+int run_w4_case(int64_t M, int64_t N, int64_t K, hipStream_t s)
+{
+    const int64_t kp = cr_padded_k(K), ldx = (K + 7) / 8 * 8, l4 = kp / 2, l6 = 3 * kp;
+    const int64_t q_m = (M + 3) / 4, q_n = (N + 3) / 4;
+    uint64_t seed = (uint64_t)(M * 7919 + N * 31 + K);
+    std::vector<uint16_t> hx((size_t)(M * ldx)), hw((size_t)(N * ldx));
+    for (auto &v : hx) v = bf16_of(((float)(lcg(seed) % 2001) - 1000.0f) / 400.0f);
+    for (auto &v : hw) v = bf16_of(((float)(lcg(seed) % 2001) - 1000.0f) / 50000.0f);
+
+    void *x, *w, *out_a, *out_b, *ws;
+    int8_t *qx8;
+    uint8_t *p4, *p6, *p6r, *qx4, *qx6;
+    float *sx8, *sx4, *sx6, *sw4, *sw6;
+    const size_t ob = (size_t)(M * N * 2);
+    const size_t wsb = cr_linear_w4a8_workspace_bytes(M, K) > cr_linear_w4a4_e2m3_workspace_bytes(M, K)
+                           ? cr_linear_w4a8_workspace_bytes(M, K) : cr_linear_w4a4_e2m3_workspace_bytes(M, K);
+    HIP_OK(hipMalloc(&x, hx.size() * 2));
+    HIP_OK(hipMalloc(&w, hw.size() * 2));
+    HIP_OK(hipMalloc((void **)&qx8, (size_t)(M * kp)));
+    HIP_OK(hipMalloc((void **)&qx4, (size_t)(M * l4)));
+    HIP_OK(hipMalloc((void **)&qx6, (size_t)(q_m * l6)));
+    HIP_OK(hipMalloc((void **)&p4, (size_t)(N * l4)));
+    HIP_OK(hipMalloc((void **)&p6, (size_t)(q_n * l6)));
+    HIP_OK(hipMalloc((void **)&p6r, (size_t)(q_n * l6)));
+    for (float **f : {&sx8, &sx4, &sx6}) HIP_OK(hipMalloc((void **)f, (size_t)M * 4));
+    for (float **f : {&sw4, &sw6}) HIP_OK(hipMalloc((void **)f, (size_t)N * 4));
+    HIP_OK(hipMalloc(&out_a, ob));
+    HIP_OK(hipMalloc(&out_b, ob));
+    HIP_OK(hipMalloc(&ws, wsb));
+    HIP_OK(hipMemcpy(x, hx.data(), hx.size() * 2, hipMemcpyHostToDevice));
+    HIP_OK(hipMemcpy(w, hw.data(), hw.size() * 2, hipMemcpyHostToDevice));
+    HIP_OK(hipMemset(p6, 0, (size_t)(q_n * l6)));       // rows past N in the last quad
+    HIP_OK(hipMemset(p6r, 0, (size_t)(q_n * l6)));
+
+    const uint32_t bt = CR_FLAG_BLOCK_TRANSPOSED;
+    CR_OK_(cr_quant_weight_w4(w, CR_BF16, ldx, N, K, p4, l4, sw4, bt, s));
+    CR_OK_(cr_quant_weight_w4_e2m3(w, CR_BF16, ldx, N, K, p6, l6, sw6, bt, s));
+    CR_OK_(cr_repack_w4_e2m3(p4, l4, N, kp, p6r, l6, s));
+    HIP_OK(hipStreamSynchronize(s));
+    std::vector<uint8_t> f6a((size_t)(q_n * l6)), f6b((size_t)(q_n * l6));
+    std::vector<float> sa((size_t)N), sb((size_t)N);
+    HIP_OK(hipMemcpy(f6a.data(), p6, f6a.size(), hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(f6b.data(), p6r, f6b.size(), hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(sa.data(), sw4, (size_t)N * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(sb.data(), sw6, (size_t)N * 4, hipMemcpyDeviceToHost));
+    if (f6a != f6b || std::memcmp(sa.data(), sb.data(), sa.size() * 4) != 0) {
+        std::fprintf(stderr, "M=%lld N=%lld K=%lld: repacked E2M3 weight differs from the direct one\n",
+                     (long long)M, (long long)N, (long long)K);
+        return 1;
+    }
+
+    std::vector<uint16_t> ra((size_t)(M * N)), rb((size_t)(M * N)), r4((size_t)(M * N));
+    auto same = [&](const char *what, const std::vector<uint16_t> &want) -> bool {
+        if (hipStreamSynchronize(s) != hipSuccess || hipMemcpy(rb.data(), out_b, ob, hipMemcpyDeviceToHost) != hipSuccess)
+            return false;
+        if (std::memcmp(want.data(), rb.data(), ob) != 0) {
+            std::fprintf(stderr, "M=%lld N=%lld K=%lld: %s differs\n", (long long)M, (long long)N, (long long)K, what);
+            return false;
+        }
+        return true;
+    };
+    // W4A8: components == layer
+    CR_OK_(cr_quant_act(x, CR_BF16, ldx, M, K, qx8, kp, sx8, bt, s));
+    CR_OK_(cr_gemm_s8s4_rowscale(qx8, kp, sx8, p4, l4, sw4, nullptr, M, N, kp, out_a, CR_BF16, N, s));
+    HIP_OK(hipStreamSynchronize(s));
+    HIP_OK(hipMemcpy(ra.data(), out_a, ob, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemset(out_b, 0xFF, ob));
+    CR_OK_(cr_linear_w4a8(x, CR_BF16, ldx, 0, M, K, p4, l4, sw4, N, nullptr, out_b, CR_BF16, N, ws, wsb, bt, s));
+    if (!same("cr_linear_w4a8 vs its components", ra)) return 1;
+    // W4A4, nibble form: components == layer
+    CR_OK_(cr_quant_act_w4(x, CR_BF16, ldx, 0, M, K, qx4, l4, sx4, bt, s));
+    CR_OK_(cr_gemm_s4s4_rowscale(qx4, l4, sx4, p4, l4, sw4, nullptr, M, N, kp, out_a, CR_BF16, N, s));
+    HIP_OK(hipStreamSynchronize(s));
+    HIP_OK(hipMemcpy(r4.data(), out_a, ob, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemset(out_b, 0xFF, ob));
+    CR_OK_(cr_linear_w4a4(x, CR_BF16, ldx, 0, M, K, p4, l4, sw4, N, nullptr, out_b, CR_BF16, N, ws, wsb, bt, s));
+    if (!same("cr_linear_w4a4 vs its components", r4)) return 1;
+    // W4A4, E2M3 form: components and layer == the nibble form
+    CR_OK_(cr_quant_act_w4_e2m3(x, CR_BF16, ldx, 0, M, K, qx6, l6, sx6, bt, s));
+    HIP_OK(hipMemset(out_b, 0xFF, ob));
+    CR_OK_(cr_gemm_e2m3_rowscale(qx6, l6, sx6, p6r, l6, sw6, nullptr, M, N, kp, out_b, CR_BF16, N, s));
+    if (!same("E2M3 GEMM vs the nibble-form layer", r4)) return 1;
+    HIP_OK(hipMemset(out_b, 0xFF, ob));
+    CR_OK_(cr_linear_w4a4_e2m3(x, CR_BF16, ldx, 0, M, K, p6, l6, sw6, N, nullptr, out_b, CR_BF16, N, ws, wsb, bt, s));
+    if (!same("cr_linear_w4a4_e2m3 vs the nibble-form layer", r4)) return 1;
+    std::printf("M=%lld N=%lld K=%lld: W4A8 and W4A4 (both forms) components == layers, repack == direct, ok\n",
+                (long long)M, (long long)N, (long long)K);
+
+    // argument errors come back as statuses
+    if (cr_gemm_e2m3_rowscale(qx6, l6 - 16, sx6, p6, l6, sw6, nullptr, M, N, kp, out_b, CR_BF16, N, s) != CR_ERR_INVALID_ARG ||
+        cr_repack_w4_e2m3(p4, l4, N, kp + 128, p6r, l6 + 384, s) != CR_ERR_INVALID_ARG ||
+        cr_quant_act_w4(x, CR_BF16, ldx, 0, M, K, qx4 + 1, l4, sx4, bt, s) != CR_ERR_MISALIGNED ||
+        cr_linear_w4a4_e2m3(x, CR_BF16, ldx, 0, M, K, p6, l6, sw6, N, nullptr, out_b, CR_BF16, N, ws,
+                            cr_linear_w4a4_e2m3_workspace_bytes(M, K) - 1, bt, s) != CR_ERR_TOO_LARGE ||
+        cr_linear_w4a8(x, CR_BF16, ldx, 0, 0, K, p4, l4, sw4, N, nullptr, nullptr, CR_BF16, N, nullptr, 0, bt, s) != CR_OK) {
+        std::fprintf(stderr, "4-bit argument checks did not return the documented statuses\n");
+        return 1;
+    }
+    for (void *p : {(void *)x, (void *)w, (void *)qx8, (void *)qx4, (void *)qx6, (void *)p4, (void *)p6, (void *)p6r,
+                    (void *)sx8, (void *)sx4, (void *)sx6, (void *)sw4, (void *)sw6, out_a, out_b, ws})
+        HIP_OK(hipFree(p));
+    return 0;
+}
+
 }  // namespace
 
 int main()
@@ -132,6 +241,9 @@ int main()
     const int64_t cases[][3] = {{300, 520, 1000}, {8, 300, 5376}, {70, 1000, 20000}};
     for (const auto &c : cases)
         if (run_case(c[0], c[1], c[2], s_main, s_aux) != 0) return 1;
+    const int64_t w4_cases[][3] = {{300, 517, 1000}, {33, 256, 5376}, {70, 90, 20000}};
+    for (const auto &c : w4_cases)
+        if (run_w4_case(c[0], c[1], c[2], s_main) != 0) return 1;
     HIP_OK(hipStreamDestroy(s_main));
     HIP_OK(hipStreamDestroy(s_aux));
     std::printf("abi_smoke: all cases ok\n");

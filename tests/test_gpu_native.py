@@ -1,7 +1,9 @@
 """The C ABI from a native program (tests/native/abi_smoke.cpp, built by the build step):
 no Python binding, no torch; device memory from hipMalloc.  The program runs in a child
 process and checks that the component calls and cr_linear_nvfp4 (staged, two-stream and
-short-batch paths) give the same bits and that argument errors come back as statuses."""
+short-batch paths) give the same bits, that the W4A8 / W4A4 layer calls equal their
+components (the E2M3 form equal to the nibble form, a repacked E2M3 weight equal to a
+directly prepared one), and that argument errors come back as statuses."""
 import os
 import subprocess
 
