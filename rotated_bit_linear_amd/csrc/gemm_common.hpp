@@ -98,6 +98,13 @@ __device__ __forceinline__ void tile_of(int pid, int tiles_m, int tiles_n, int &
     }
 }
 
+// Whether workgroup pid walks K from the end.  The 32 workgroups an XCD runs at once (one
+// per CU, consecutive in tile_of's order) form a generation, and consecutive generations
+// share their activation bands.  Odd generations run K backwards, so each generation starts
+// on the operand slices that the previous one read last, while they are still in the XCD's
+// L2.  The int32 sums are exact in any order.
+__device__ __forceinline__ bool k_reversed(int pid) { return ((pid / NUM_XCD) >> 5) & 1; }
+
 // Row and column scales one lane needs in the epilogue: sav[i] for its row of 32-row block
 // i, sbv[j][g] for the 4-column run n = 8g + 4(l/32) .. +3 of 32-column block j (16-byte
 // loads when aligned).  Requested before the last barrier so their latency overlaps the

@@ -114,10 +114,15 @@ void gemm_e2m3_kernel(const uint8_t *__restrict__ A, int64_t lda, const float *_
         gsrc[j] = (wave_a ? A : B) + (rr >> 2) * (wave_a ? lda : ldb) + (rr & 3) * ROW + chunk * 16;
         ldst[j] = (wave_a ? A_BASE : B_BASE) + q * 1024;
     }
+    // step kt of the K loop reads the operands' step kt, or step last_step - kt when this
+    // workgroup walks K backwards (gemm::k_reversed)
+    const bool k_rev = gemm::k_reversed(blockIdx.x);
+    const int last_step = K_pad / BK - 1;
     auto issue = [&](int s, int kt) {
+        const int64_t ks = k_rev ? last_step - kt : kt;
 #pragma unroll
         for (int j = 0; j < PPW; j++)
-            __builtin_amdgcn_global_load_lds(gsrc[j] + (int64_t)kt * QUAD_STEP, pool + ldst[j] + s * SOP, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(gsrc[j] + ks * QUAD_STEP, pool + ldst[j] + s * SOP, 16, 0, 0);
     };
 
     // ---- fragment addresses: row = base + (lane & 31), lane half h = lane >> 5 reads the

@@ -21,7 +21,8 @@
 // Tiles are assigned so that all XCDs (workgroup id mod 8 on this part) work on one chip
 // block at a time, each on a compact sub-block: L2 reuse inside an XCD, and one MALL-resident
 // working set for the whole chip (the XCDs form a 2 x 4 grid over a square chip block, so a
-// round of workgroups touches as few distinct operand bands as possible).
+// round of workgroups touches as few distinct operand bands as possible).  Every other
+// generation of an XCD's workgroups walks K backwards (gemm::k_reversed).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -139,9 +140,13 @@ void gemm_s8_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__re
     }
     const int dma_off = (dma_a ? piece0 : piece0 - STAGE_A / 1024) * 1024;
 
+    // step kt of the K loop reads the operands' step kt, or step last_step - kt when this
+    // workgroup walks K backwards (gemm::k_reversed)
+    const bool k_rev = gemm::k_reversed(blockIdx.x);
+    const int last_step = K_pad / GBK - 1;
     auto issue = [&](int s, int kt) {
         int8_t *dst = (dma_a ? stA[s] : stB[s]) + dma_off;
-        const int64_t ko = (int64_t)kt * GBK;
+        const int64_t ko = (int64_t)(k_rev ? last_step - kt : kt) * GBK;
 #pragma unroll
         for (int j = 0; j < PPW; j++)
             __builtin_amdgcn_global_load_lds(gsrc[j] + ko, dst + j * 1024, 16, 0, 0);

@@ -138,11 +138,16 @@ void gemm_s8s4_kernel(const int8_t *__restrict__ A, int64_t lda, const float *__
             kstep[j] = BK / 2;
         }
     }
+    // step kt of the K loop reads the operands' step kt, or step last_step - kt when this
+    // workgroup walks K backwards (gemm::k_reversed)
+    const bool k_rev = gemm::k_reversed(blockIdx.x);
+    const int last_step = K_pad / BK - 1;
     auto issue = [&](int s, int kt) {
+        const int64_t ks = k_rev ? last_step - kt : kt;
 #pragma unroll
         for (int j = 0; j < R::PPW; j++) {
             const int stage_off = ldst[j] < R::B_BASE ? s * R::SA : s * SB;
-            __builtin_amdgcn_global_load_lds(gsrc[j] + (int64_t)kt * kstep[j], pool + ldst[j] + stage_off, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(gsrc[j] + ks * kstep[j], pool + ldst[j] + stage_off, 16, 0, 0);
         }
     };
 
