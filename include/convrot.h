@@ -69,8 +69,10 @@ extern "C" {
 
 #define CR_ABI_VERSION 3
 #define CR_MAX_K_PAD 133120       /* largest multiple of 256 with 127*127*K_pad < 2^31 */
-#define CR_TWO_PASS_K_PAD 16384   /* activation rows with K_pad above this stream twice */
-#define CR_W_TWO_PASS_K_PAD 32768 /* NVFP4 weight rows with K_pad above this stream twice */
+#define CR_TWO_PASS_K_PAD 16384   /* SwiGLU and fp32 activation rows (and dense fp32 4-bit weight
+                                     rows) with K_pad above this stream twice */
+#define CR_W_TWO_PASS_K_PAD 32768 /* NVFP4 weight rows, and bf16/fp16 plain activation rows and
+                                     dense 4-bit weight rows, with K_pad above this stream twice */
 #define CR_DEFAULT_MAX_TILE_BYTES ((size_t)128 << 20)
 
 typedef enum {

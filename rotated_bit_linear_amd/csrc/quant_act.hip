@@ -215,9 +215,11 @@ __device__ __forceinline__ float sigma_lookup(uint32_t off, uint32_t p)
 // unfused pre-scale (ComfyUI Turing Utils README, "Load ConvRot DiT ..." bullet).
 template <int DT, bool kPre>
 struct ActLoader {
-    // rows of 65-128 blocks stream twice: measured faster than four blocks per group here
-    // (the second read is served from the cache, and a slice workgroup has 960 threads)
+    // bf16/fp16 rows of 65-128 blocks are held in one pass at two blocks per group, up to 64
+    // groups (kWideTwo); four blocks per group measured slower than two passes here (fewer
+    // rows in flight per CU), and fp32 rows (64 raw bytes a segment) would spill at two
     static constexpr bool kFourBlocks = false;
+    static constexpr bool kWideTwo = DT != 2;
     static constexpr bool kE2M3Fast = true;
     static constexpr bool kFetchAfterDecode = true;
     static constexpr bool kTwoPassPrefetch = true;
@@ -247,8 +249,10 @@ struct ActLoader {
 
 template <int DT, bool kPre>
 struct SwigluLoader {
-    // as for ActLoader (and fp16/fp32 gates with a pre-scale would spill at four blocks)
+    // rows of 65-128 blocks stream twice (fp16/fp32 gates with a pre-scale would spill at
+    // four blocks, and at two blocks per group under a 1024-thread bound)
     static constexpr bool kFourBlocks = false;
+    static constexpr bool kWideTwo = false;
     // fp16/fp32 gates (the refined reciprocal, no sigma table) leave no room for the tables
     static constexpr bool kE2M3Fast = DT == 0;
     static constexpr bool kFetchAfterDecode = true;
@@ -349,6 +353,16 @@ __global__ __launch_bounds__(row_prep_max_threads<RB>()) void quant_act_kernel(L
     row_prep_kernel_body<Loader, RB, kBits>(ld, n_rows, nb, out, ld_out, scale, mode);
 }
 
+// Rows of 65-128 blocks in one pass for loaders with kWideTwo: two blocks per lane group and
+// up to 64 groups (1024 threads), so each block is loaded and rotated once.  With at most
+// 128 registers a lane, two such rows fit on a CU at once.
+template <class Loader, int kBits = 8>
+__global__ __launch_bounds__(1024) void quant_act_wide_kernel(Loader ld, int64_t n_rows, int nb, int8_t *__restrict__ out,
+                                                              int64_t ld_out, float *__restrict__ scale, int mode)
+{
+    row_prep_kernel_body<Loader, 2, kBits>(ld, n_rows, nb, out, ld_out, scale, mode);
+}
+
 // Several short rows per workgroup (see row_prep_multi).
 template <class Loader, int kBits = 8>
 __global__ __launch_bounds__(1024) void quant_act_multi_kernel(Loader ld, int64_t n_rows, int nb, int rpw,
@@ -389,6 +403,18 @@ static hipError_t launch_rows(const Loader &L, int64_t rows, int64_t nb, int8_t 
         hipLaunchKernelGGL((quant_act_multi_kernel<Loader, kBits>), grid, dim3(threads), mlds, st, L, rows, (int)nb,
                            rpw, out, ld_out, scale, mode);
         return hipGetLastError();
+    }
+    if constexpr (Loader::kWideTwo) {
+        if (s.two_pass && !force_two_pass && nb > 2 * kMaxGroups2 && nb <= 4 * kMaxGroups2) {
+            const int64_t groups = (nb + 1) / 2;
+            const RowPrepShape ws{(int)((groups + 3) / 4 * 64), 2, false};
+            const size_t wlds = row_prep_lds_bytes(ws.threads);
+            const void *k = reinterpret_cast<const void *>(&quant_act_wide_kernel<Loader, kBits>);
+            const dim3 grid((unsigned)row_prep_grid(rows, ws, k, wlds));
+            hipLaunchKernelGGL((quant_act_wide_kernel<Loader, kBits>), grid, dim3(ws.threads), wlds, st,
+                               L, rows, (int)nb, out, ld_out, scale, transposed ? 2 : 0);
+            return hipGetLastError();
+        }
     }
     if constexpr (Loader::kFourBlocks) {
         if (s.rb == 4) {

@@ -41,8 +41,8 @@
 // above holds with 127 replaced by 7.  They are packed two per byte (quantize_store16_s4,
 // code_offset), or stored as E2M3 fields of equal value (quantize_e2m3_16, store_codes).
 //
-// Rows whose K_pad exceeds 128 blocks (32768 columns; 64 blocks for the activation loaders,
-// whose two-pass form measured faster), or when forced, are streamed twice:
+// Rows whose K_pad exceeds 128 blocks (32768 columns; 64 blocks for the SwiGLU loaders,
+// which have no one-pass form for longer rows), or when forced, are streamed twice:
 // pass 1 rotates every block to find the row maximum, pass 2 reloads, rotates again and
 // quantizes (same operations, so the same bits).
 #pragma once
@@ -418,6 +418,9 @@ __host__ __device__ constexpr size_t row_prep_lds_bytes(int threads)
 // Loader concept:
 //   static constexpr bool kFourBlocks;               rows of 65-128 blocks are held in one
 //                                                    pass, four blocks per lane group
+//   static constexpr bool kWideTwo;                  (activation loaders) rows of 65-128
+//                                                    blocks are held in one pass, two blocks
+//                                                    per group, up to 64 groups
 //   static constexpr bool kE2M3Fast;                 E2M3 codes through byte tables and
 //                                                    paired stores (else arithmetic codes and
 //                                                    per-lane stores: fewer live registers)

@@ -111,10 +111,12 @@ ACT_CASES = [
     (synth.DT_FP16, 33, 1000, 1016, True, False),
     (synth.DT_FP32, 17, 777, 780, True, False),
     (synth.DT_BF16, 5, 16384, 16384, False, False),
-    (synth.DT_BF16, 5, 16385, 16392, True, False),    # 65 blocks: two-pass by size
-    (synth.DT_FP16, 3, 20000, 20000, True, False),
-    (synth.DT_FP32, 4, 32768, 32768, True, False),
-    (synth.DT_BF16, 4, 32769, 32776, True, False),
+    (synth.DT_BF16, 5, 16385, 16392, True, False),    # 65 blocks: one pass, two blocks a group
+    (synth.DT_FP16, 3, 20000, 20000, True, False),    # 79 blocks: one pass
+    (synth.DT_FP16, 6, 32768, 32768, True, False),    # 128 blocks: one pass, 1024 threads
+    (synth.DT_FP32, 4, 32768, 32768, True, False),    # fp32 rows above 64 blocks: two-pass
+    (synth.DT_BF16, 4, 32769, 32776, True, False),    # 129 blocks: two-pass by size
+    (synth.DT_BF16, 7, 20000, 20000, True, True),     # forced two-pass at 79 blocks
     (synth.DT_BF16, 11, 5376, 5376, True, True),      # forced two-pass
     (synth.DT_FP32, 1, 1, 4, False, False),           # one element
 ]
@@ -133,12 +135,14 @@ def test_quant_act_bit_exact(dt, M, K, ld, special, forced):
 
 
 def test_two_pass_equals_one_pass_activation():
-    x = make_x(50, 4000, synth.DT_BF16, seed=3, special=True).to(dev())
-    say("cr_quant_act one-pass vs forced two-pass M=50 K=4000")
-    q1, s1 = rbl.quant_act(x, 4000)
-    q2, s2 = rbl.quant_act(x, 4000, flags=rbl.CR_FLAG_FORCE_TWO_PASS)
-    torch.cuda.synchronize()
-    assert torch.equal(q1, q2) and torch.equal(s1, s2)
+    for K in (4000, 25000):      # one block a group; two blocks a group over 49 groups
+        x = make_x(50, K, synth.DT_BF16, seed=3, special=True).to(dev())
+        for flags in (0, rbl.CR_FLAG_BLOCK_TRANSPOSED):
+            say(f"cr_quant_act one-pass vs forced two-pass M=50 K={K} flags={flags}")
+            q1, s1 = rbl.quant_act(x, K, flags=flags)
+            q2, s2 = rbl.quant_act(x, K, flags=flags | rbl.CR_FLAG_FORCE_TWO_PASS)
+            torch.cuda.synchronize()
+            assert torch.equal(q1, q2) and torch.equal(s1, s2), (K, flags)
 
 
 SWI_CASES = [
