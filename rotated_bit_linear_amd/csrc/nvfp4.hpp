@@ -39,8 +39,7 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b)
 }
 
 struct NVFP4Loader {
-    static constexpr bool kFourBlocks = true;
-    static constexpr bool kWideTwo = false;
+    static constexpr bool kLongOnePass = true;
     static constexpr bool kE2M3Fast = true;       // (no E2M3 output from NVFP4 rows)
     static constexpr bool kFetchAfterDecode = false;   // little raw data, cheap decode
     // two-pass rows: loads then decode in place (prefetching the next slice measured 6 %

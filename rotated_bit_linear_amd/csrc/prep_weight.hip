@@ -23,6 +23,15 @@ __global__ __launch_bounds__(row_prep_max_threads<RB>()) void prep_weight_kernel
     row_prep_kernel_body<NVFP4Loader, RB>(ld, n_rows, nb, out, ld_out, scale, mode);
 }
 
+// Rows of 65-128 blocks in one pass (the wide form): two blocks per lane group in up to 64
+// groups, 1024 threads at most.
+__global__ __launch_bounds__(1024) void prep_weight_wide_kernel(NVFP4Loader ld, int64_t n_rows, int nb, int8_t *__restrict__ out,
+                                                                int64_t ld_out, float *__restrict__ scale, int mode)
+{
+    ld.gs = *ld.g;
+    row_prep_kernel_body<NVFP4Loader, 2>(ld, n_rows, nb, out, ld_out, scale, mode);
+}
+
 // Several short rows per workgroup (see row_prep_multi): rows of up to 32 blocks whose
 // lane groups would not fill the workgroup's last wave.
 __global__ __launch_bounds__(1024) void prep_weight_multi_kernel(NVFP4Loader ld, int64_t n_rows, int nb, int rpw,
@@ -60,10 +69,10 @@ hipError_t launch_prep_weight(const uint8_t *codes, int64_t ld_codes, const uint
     const int mode = (s.two_pass ? 1 : 0) | (transposed ? 2 : 0);
     NVFP4Loader L{codes, ld_codes, sf, ld_sf, g, K, 0.0f};
     if (launch_multi(L, n_rows, nb, s.two_pass, w_s8, ld_s8, w_scale, mode, st)) return hipGetLastError();
-    if (s.rb == 4) {
-        const void *k = reinterpret_cast<const void *>(&prep_weight_kernel<4>);
+    if (s.wide) {
+        const void *k = reinterpret_cast<const void *>(&prep_weight_wide_kernel);
         const dim3 grid((unsigned)row_prep_grid(n_rows, s, k, lds));
-        hipLaunchKernelGGL(prep_weight_kernel<4>, grid, dim3(s.threads), lds, st,
+        hipLaunchKernelGGL(prep_weight_wide_kernel, grid, dim3(s.threads), lds, st,
                            L, n_rows, (int)nb, w_s8, ld_s8, w_scale, mode);
     } else if (s.rb == 2) {
         const void *k = reinterpret_cast<const void *>(&prep_weight_kernel<2>);
@@ -89,10 +98,10 @@ hipError_t launch_weight_amax(const uint8_t *codes, int64_t ld_codes, const uint
     const int mode = (s.two_pass ? 1 : 0) | 2 | 4;     // the order of z does not matter for the maximum
     NVFP4Loader L{codes, ld_codes, sf, ld_sf, g, K, 0.0f};
     if (launch_multi(L, n_rows, nb, s.two_pass, nullptr, 0, amax, mode, st)) return hipGetLastError();
-    if (s.rb == 4) {
-        const void *k = reinterpret_cast<const void *>(&prep_weight_kernel<4>);
+    if (s.wide) {
+        const void *k = reinterpret_cast<const void *>(&prep_weight_wide_kernel);
         const dim3 grid((unsigned)row_prep_grid(n_rows, s, k, lds));
-        hipLaunchKernelGGL(prep_weight_kernel<4>, grid, dim3(s.threads), lds, st,
+        hipLaunchKernelGGL(prep_weight_wide_kernel, grid, dim3(s.threads), lds, st,
                            L, n_rows, (int)nb, nullptr, (int64_t)0, amax, mode);
     } else if (s.rb == 2) {
         const void *k = reinterpret_cast<const void *>(&prep_weight_kernel<2>);

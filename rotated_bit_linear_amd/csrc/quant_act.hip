@@ -215,11 +215,9 @@ __device__ __forceinline__ float sigma_lookup(uint32_t off, uint32_t p)
 // unfused pre-scale (ComfyUI Turing Utils README, "Load ConvRot DiT ..." bullet).
 template <int DT, bool kPre>
 struct ActLoader {
-    // bf16/fp16 rows of 65-128 blocks are held in one pass at two blocks per group, up to 64
-    // groups (kWideTwo); four blocks per group measured slower than two passes here (fewer
-    // rows in flight per CU), and fp32 rows (64 raw bytes a segment) would spill at two
-    static constexpr bool kFourBlocks = false;
-    static constexpr bool kWideTwo = DT != 2;
+    // bf16/fp16 rows of 65-128 blocks are held in one pass (the wide form); fp32 rows (64
+    // raw bytes a segment) would spill under its 1024-thread bound and stream twice
+    static constexpr bool kLongOnePass = DT != 2;
     static constexpr bool kE2M3Fast = true;
     static constexpr bool kFetchAfterDecode = true;
     static constexpr bool kTwoPassPrefetch = true;
@@ -249,10 +247,8 @@ struct ActLoader {
 
 template <int DT, bool kPre>
 struct SwigluLoader {
-    // rows of 65-128 blocks stream twice (fp16/fp32 gates with a pre-scale would spill at
-    // four blocks, and at two blocks per group under a 1024-thread bound)
-    static constexpr bool kFourBlocks = false;
-    static constexpr bool kWideTwo = false;
+    // rows of 65-128 blocks stream twice (fp16/fp32 gates would spill in the wide form)
+    static constexpr bool kLongOnePass = false;
     // fp16/fp32 gates (the refined reciprocal, no sigma table) leave no room for the tables
     static constexpr bool kE2M3Fast = DT == 0;
     static constexpr bool kFetchAfterDecode = true;
@@ -353,9 +349,9 @@ __global__ __launch_bounds__(row_prep_max_threads<RB>()) void quant_act_kernel(L
     row_prep_kernel_body<Loader, RB, kBits>(ld, n_rows, nb, out, ld_out, scale, mode);
 }
 
-// Rows of 65-128 blocks in one pass for loaders with kWideTwo: two blocks per lane group and
-// up to 64 groups (1024 threads), so each block is loaded and rotated once.  With at most
-// 128 registers a lane, two such rows fit on a CU at once.
+// Rows of 65-128 blocks in one pass (the wide form, loaders with kLongOnePass): two blocks
+// per lane group in up to 64 groups (1024 threads), so each block is loaded and rotated
+// once.  With at most 128 registers a lane, two such rows fit on a CU at once.
 template <class Loader, int kBits = 8>
 __global__ __launch_bounds__(1024) void quant_act_wide_kernel(Loader ld, int64_t n_rows, int nb, int8_t *__restrict__ out,
                                                               int64_t ld_out, float *__restrict__ scale, int mode)
@@ -383,7 +379,7 @@ static hipError_t launch_rows(const Loader &L, int64_t rows, int64_t nb, int8_t 
                               float *scale, bool force_two_pass, bool transposed, hipStream_t st,
                               int one_pass_groups = kMaxGroups2)
 {
-    const RowPrepShape s = row_prep_shape(nb, force_two_pass, one_pass_groups, Loader::kFourBlocks);
+    const RowPrepShape s = row_prep_shape(nb, force_two_pass, one_pass_groups, Loader::kLongOnePass);
     // the sigma table sits past the engine's LDS, at a 16-byte boundary
     constexpr size_t extra = Loader::kSigTable ? kSigTableBytes + 16 : 0;
     const size_t lds = row_prep_lds_bytes(s.threads) + extra;
@@ -404,23 +400,11 @@ static hipError_t launch_rows(const Loader &L, int64_t rows, int64_t nb, int8_t 
                            rpw, out, ld_out, scale, mode);
         return hipGetLastError();
     }
-    if constexpr (Loader::kWideTwo) {
-        if (s.two_pass && !force_two_pass && nb > 2 * kMaxGroups2 && nb <= 4 * kMaxGroups2) {
-            const int64_t groups = (nb + 1) / 2;
-            const RowPrepShape ws{(int)((groups + 3) / 4 * 64), 2, false};
-            const size_t wlds = row_prep_lds_bytes(ws.threads);
+    if constexpr (Loader::kLongOnePass) {
+        if (s.wide) {
             const void *k = reinterpret_cast<const void *>(&quant_act_wide_kernel<Loader, kBits>);
-            const dim3 grid((unsigned)row_prep_grid(rows, ws, k, wlds));
-            hipLaunchKernelGGL((quant_act_wide_kernel<Loader, kBits>), grid, dim3(ws.threads), wlds, st,
-                               L, rows, (int)nb, out, ld_out, scale, transposed ? 2 : 0);
-            return hipGetLastError();
-        }
-    }
-    if constexpr (Loader::kFourBlocks) {
-        if (s.rb == 4) {
-            const void *k = reinterpret_cast<const void *>(&quant_act_kernel<Loader, 4, kBits>);
             const dim3 grid((unsigned)row_prep_grid(rows, s, k, lds));
-            hipLaunchKernelGGL((quant_act_kernel<Loader, 4, kBits>), grid, dim3(s.threads), lds, st,
+            hipLaunchKernelGGL((quant_act_wide_kernel<Loader, kBits>), grid, dim3(s.threads), lds, st,
                                L, rows, (int)nb, out, ld_out, scale, mode);
             return hipGetLastError();
         }

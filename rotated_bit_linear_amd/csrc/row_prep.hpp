@@ -58,7 +58,7 @@ namespace convrot {
 constexpr int kLanesPerBlock = 16;          // lanes sharing one 256-column block
 constexpr int kTileStrideF = 272;           // floats per 16x16 transpose tile (256 + 16 pad)
 constexpr int kMaxGroups1 = 60;             // two-pass rows: 960 threads
-constexpr int kMaxGroups2 = 32;             // one-pass rows: 512 threads (two or four blocks per group)
+constexpr int kMaxGroups2 = 32;             // one-pass rows of two blocks per group: 512 threads
 constexpr int kMaxGroupsWide = 64;          // one-pass SwiGLU rows, one block per group
 constexpr int64_t kTwoPassMaxGrid = 65536;  // workgroups of a two-pass launch (they loop)
 
@@ -416,11 +416,9 @@ __host__ __device__ constexpr size_t row_prep_lds_bytes(int threads)
 }
 
 // Loader concept:
-//   static constexpr bool kFourBlocks;               rows of 65-128 blocks are held in one
-//                                                    pass, four blocks per lane group
-//   static constexpr bool kWideTwo;                  (activation loaders) rows of 65-128
-//                                                    blocks are held in one pass, two blocks
-//                                                    per group, up to 64 groups
+//   static constexpr bool kLongOnePass;              rows of 65-128 blocks are held in one
+//                                                    pass, two blocks per lane group in up to
+//                                                    64 groups (the 1024-thread kernels)
 //   static constexpr bool kE2M3Fast;                 E2M3 codes through byte tables and
 //                                                    paired stores (else arithmetic codes and
 //                                                    per-lane stores: fewer live registers)
@@ -796,32 +794,40 @@ __device__ __forceinline__ void row_prep_kernel_body(const Loader &ld, int64_t n
     }
 }
 
-// Launch shape of a row of nb blocks.  Up to one_pass_groups blocks (32, or 64 for the
-// SwiGLU activation kernel), one block per 16-lane group; up to 64 blocks, two per group,
-// and, for loaders that opt in, up to 128 blocks four per group (at most 512 threads: the
-// whole row stays in registers, so it is loaded, decoded and rotated once); beyond that, two
-// passes over slices of at most 60 groups (960 threads), the blocks spread evenly over the
-// slices.  One block per group keeps fewer values per
-// lane, so a SwiGLU row of 56 blocks runs 14 waves of at most 128 registers instead of 7
-// waves of 144 (1-3 % faster); rows with a short decode (plain activations, NVFP4 weights)
-// are 2-3 % faster at two blocks per group.
+// Launch shape of a row of nb blocks.
+// * Up to one_pass_groups blocks (32, or 64 for the SwiGLU activation kernel): one block per
+//   16-lane group.
+// * Up to 64 blocks: two per group (at most 512 threads).
+// * For loaders that opt in (kLongOnePass), up to 128 blocks: two per group in up to 64
+//   groups.  This is the "wide" form, a kernel bound to 1024 threads and at most 128
+//   registers a lane.  The whole row stays in registers, so it is loaded, decoded and
+//   rotated once.
+// * Beyond that: two passes over slices of at most 60 groups (960 threads), the blocks
+//   spread evenly over the slices.
+// One block per group keeps fewer values per lane, so a SwiGLU row of 56 blocks runs 14 waves
+// of at most 128 registers instead of 7 waves of 144 (1-3 % faster).  Rows with a short
+// decode (plain activations, NVFP4 weights) are 2-3 % faster at two blocks per group.  For
+// 65-128 blocks, two blocks per group in up to 64 groups (79-91 registers) beat four blocks
+// per group in up to 32 (129 registers): twice the lanes per row at the same rows per CU.
+// On long-K weights [5000, 20000] the time fell from 0.091 to 0.056 ms.
 struct RowPrepShape {
     int threads;   // workgroup size, a multiple of 64
-    int rb;        // blocks held per 16-lane group in one-pass mode (1, 2 or 4)
+    int rb;        // blocks held per 16-lane group in one-pass mode (1 or 2)
     bool two_pass;
+    bool wide;     // two blocks per group beyond 32 groups: the 1024-thread kernel
 };
 
-// Launch bound of the kernel instantiation that runs RB blocks per group.
+// Launch bound of the kernel instantiation that runs RB blocks per group (the wide form has
+// kernels of its own, bound to 1024 threads).
 template <int RB>
 constexpr int row_prep_max_threads() { return RB == 1 ? 1024 : 512; }
 
-// Longest row (in 256-column blocks) prepared in one pass: four blocks per group.
+// Longest row (in 256-column blocks) prepared in one pass: two blocks in each of 64 groups.
 constexpr int64_t kOnePassMaxBlocks = 4 * kMaxGroups2;
 
-// four_per_group: the loader takes rows of 65-128 blocks in one pass, four blocks per group
-// (the NVFP4 weight loader: it then decodes and rotates each block once instead of twice)
+// long_one_pass: the loader takes rows of 65-128 blocks in one pass (the wide form)
 inline RowPrepShape row_prep_shape(int64_t nb, bool force_two_pass, int one_pass_groups = kMaxGroups2,
-                                   bool four_per_group = true)
+                                   bool long_one_pass = true)
 {
     RowPrepShape s{};
     int64_t groups;
@@ -831,9 +837,10 @@ inline RowPrepShape row_prep_shape(int64_t nb, bool force_two_pass, int one_pass
     } else if (!force_two_pass && nb <= 2 * kMaxGroups2) {
         s.rb = 2;
         groups = (nb + 1) / 2;
-    } else if (!force_two_pass && four_per_group && nb <= kOnePassMaxBlocks) {
-        s.rb = 4;
-        groups = (nb + 3) / 4;
+    } else if (!force_two_pass && long_one_pass && nb <= kOnePassMaxBlocks) {
+        s.rb = 2;
+        s.wide = true;
+        groups = (nb + 1) / 2;
     } else {
         // as few slices as 60 groups allow, with the blocks spread evenly over them
         s.rb = 1;

@@ -172,8 +172,8 @@ def test_quant_act_swiglu_bit_exact(dt, M, F):
 # ---------------------------------------------------------------- weight prep ----
 
 # row shapes: one block per lane group (K <= 8192), two (8192 < K <= 16384: 14336 and a
-# 33-block row with a tail), four (16384 < K <= 32768: 20000, 32768), two-pass (K > 32768:
-# 40000), and tiny rows
+# 33-block row with a tail), two in up to 64 groups (16384 < K <= 32768: 20000, 32768),
+# two-pass (K > 32768: 40000), and tiny rows
 W_CASES = [(256, 512, None, None), (300, 1000, 512, 80), (97, 20000, None, None), (64, 5376, None, None),
            (1, 17, 16, 5), (40, 14336, None, None), (21, 8200, 4112, 520), (33, 32768, None, None),
            (19, 40000, None, None)]
