@@ -310,6 +310,33 @@ __device__ __forceinline__ void quantize_e2m3_16_tables(const float (&z)[16], fl
     w2 = (f[2] >> 16) | (f[3] << 8);
 }
 
+// The same result from gfx950's conversion of fp32 to packed 6-bit fields (E2M3, scale
+// 1): each code is rounded to an integral fp32 value exactly as code_bits rounds it (adding
+// and subtracting 1.5 * 2^23, which also turns -0 into +0, the field 0x00), and one
+// instruction packs the lane's 16 codes.  Its output interleaves its two sources (field
+// 2i from source 0, field 2i + 1 from source 1), so the even codes go to source 0 and the
+// odd codes to source 1, with zeros above element 7; fields 0..15, the first three words,
+// are the lane's codes in order.  Fewer vector instructions than the tables, but 32
+// operand registers: used where the registers allow it (store_codes' kCvt).
+template <bool kScaleFirst>
+__device__ __forceinline__ void quantize_e2m3_16_cvt(const float (&z)[16], float m, uint32_t &w0, uint32_t &w1,
+                                                     uint32_t &w2)
+{
+    typedef float f32x16 __attribute__((ext_vector_type(16)));
+    f32x16 even = {}, odd = {};
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const float y0 = kScaleFirst ? (z[2 * i] * 0.0625f) * 0x1p64f : z[2 * i];
+        const float y1 = kScaleFirst ? (z[2 * i + 1] * 0.0625f) * 0x1p64f : z[2 * i + 1];
+        even[i] = (y0 * m + 12582912.0f) - 12582912.0f;
+        odd[i] = (y1 * m + 12582912.0f) - 12582912.0f;
+    }
+    const auto f = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(even, odd, 1.0f);
+    w0 = f[0];
+    w1 = f[1];
+    w2 = f[2];
+}
+
 // Row constants from a' = max |z|: the scale a / L and the code multiplier, for codes of
 // L = 127 (8-bit) or L = 7 (4-bit) levels on each side of zero.
 struct RowQuant {
@@ -365,8 +392,10 @@ __device__ __forceinline__ int8_t *row_base(int8_t *out, int64_t row, int64_t ld
 // fields): a 128-code unit is 96 bytes, its quarters' first 16 bytes in the order Q0 Q2 Q1
 // Q3, then their last 8 bytes in the same order; member t holds half t & 1 of quarter
 // (t >> 1) & 3 of unit t >> 3 of the block: bits 0..95 of the quarter's field (its head's
-// bytes 0..11), or bits 96..191 (head bytes 12..15 and the 8-byte tail).
-template <int kBits = 8, bool kFast = true>
+// bytes 0..11), or bits 96..191 (head bytes 12..15 and the 8-byte tail).  kFast: byte
+// tables (or, with kCvt, the conversion instruction) and paired stores; else the arithmetic
+// encoding and per-lane stores (fewer registers).
+template <int kBits = 8, bool kFast = true, bool kCvt = false>
 __device__ __forceinline__ void store_codes(const float (&z)[16], const RowQuant &q, int8_t *row, int64_t b, int t)
 {
     if constexpr (kBits == 8) {
@@ -379,7 +408,10 @@ __device__ __forceinline__ void store_codes(const float (&z)[16], const RowQuant
         else quantize_store16_s4<true>(z, q.mult, dst);
     } else {
         uint32_t w0, w1, w2;
-        if constexpr (kFast) {
+        if constexpr (kFast && kCvt) {
+            if (q.folded) quantize_e2m3_16_cvt<false>(z, q.mult, w0, w1, w2);
+            else quantize_e2m3_16_cvt<true>(z, q.mult, w0, w1, w2);
+        } else if constexpr (kFast) {
             if (q.folded) quantize_e2m3_16_tables<false>(z, q.mult, w0, w1, w2);
             else quantize_e2m3_16_tables<true>(z, q.mult, w0, w1, w2);
         } else {
@@ -489,7 +521,7 @@ __device__ __forceinline__ void row_prep_rows(const Loader &ld, int64_t n_rows, 
 #pragma unroll
         for (int q = 0; q < RB; q++) {
             const int b = grp + q * G;
-            if (b < nb) store_codes<kBits, Loader::kE2M3Fast>(v[q], rq, orow, b, t);
+            if (b < nb) store_codes<kBits, Loader::kE2M3Fast, true>(v[q], rq, orow, b, t);
         }
         if (tid == 0) scale_out[row] = rq.scale;
     };
@@ -635,7 +667,7 @@ __device__ __forceinline__ void row_prep_two_pass(const Loader &ld, int64_t row,
             decode_slice(s, cur, v);
         }
         hadamard256(v, tile, t, natural);
-        if (b < nb) store_codes<kBits, Loader::kE2M3Fast>(v, rq, orow, b, t);
+        if (b < nb) store_codes<kBits, Loader::kE2M3Fast, true>(v, rq, orow, b, t);
     }
     if (tid == 0) scale_out[row] = rq.scale;
 }
@@ -703,7 +735,9 @@ __device__ __forceinline__ void row_prep_multi(const Loader &ld, int64_t n_rows,
             return;
         }
         const RowQuant rq = row_quant<kBits>(zrow);
-        if (live) store_codes<kBits, Loader::kE2M3Fast>(v, rq, row_base<kBits>(out, row, ld_out), b, t);
+        // the multi-row kernel keeps the byte tables: the conversion's operand registers
+        // would halve its workgroups per CU
+        if (live) store_codes<kBits, Loader::kE2M3Fast, false>(v, rq, row_base<kBits>(out, row, ld_out), b, t);
         if (live && b == 0 && t == 0) scale_out[row] = rq.scale;
     };
 
