@@ -341,6 +341,8 @@ PRE_CASES = [
     (synth.DT_BF16, 7, 700, True, False),
     (synth.DT_BF16, 4, 14336, True, False),         # 56-block SwiGLU rows: one block per lane group
     (synth.DT_BF16, 4, 14336, False, False),        # 56-block plain rows: two blocks per lane group
+    (synth.DT_BF16, 5, 20000, False, False),        # 79-block plain rows: two blocks a group, 40 groups
+    (synth.DT_FP16, 3, 32768, False, False),        # 128 blocks: 64 groups, 1024 threads
     (synth.DT_BF16, 6, 1000, False, True),          # forced two-pass
 ]
 

@@ -56,6 +56,7 @@ def _host(x, dt):
 
 
 A_CASES = [(synth.DT_BF16, False, 300, 1000), (synth.DT_FP16, False, 97, 5376), (synth.DT_FP32, False, 64, 20000),
+           (synth.DT_FP16, False, 30, 20000), (synth.DT_BF16, False, 9, 32768),
            (synth.DT_BF16, False, 40, 16384), (synth.DT_FP32, False, 21, 17), (synth.DT_BF16, True, 70, 14336),
            (synth.DT_FP16, True, 33, 3000), (synth.DT_FP32, True, 9, 20000), (synth.DT_BF16, True, 50, 255)]
 
@@ -218,7 +219,7 @@ def test_quant_act_w4_e2m3_bit_exact(dt, swiglu, M, K):
         assert_bits_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32), f"x_scale flags={flags}")
 
 
-W_CASES = [(synth.DT_BF16, 300, 1000), (synth.DT_FP16, 97, 5376), (synth.DT_FP32, 64, 20000),
+W_CASES = [(synth.DT_BF16, 300, 1000), (synth.DT_FP16, 97, 5376), (synth.DT_FP32, 64, 20000), (synth.DT_BF16, 37, 20000),
            (synth.DT_FP32, 21, 17), (synth.DT_BF16, 70, 14336)]
 
 

@@ -49,7 +49,8 @@ def _host(w, dt):
 
 
 W_CASES = [(synth.DT_BF16, 300, 1000), (synth.DT_FP16, 97, 5376), (synth.DT_FP32, 64, 20000),
-           (synth.DT_BF16, 40, 16384), (synth.DT_FP32, 21, 17), (synth.DT_BF16, 70, 14336)]
+           (synth.DT_BF16, 40, 16384), (synth.DT_FP32, 21, 17), (synth.DT_BF16, 70, 14336),
+           (synth.DT_FP16, 33, 25000)]
 
 
 @pytest.mark.parametrize("dt,N,K", W_CASES, ids=[f"dt{c[0]}-N{c[1]}-K{c[2]}" for c in W_CASES])
