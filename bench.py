@@ -471,7 +471,8 @@ def w4a8_layers(torch, rbl, synth, dev, names, s_main, n=20):
                (lambda: rbl.cr_quant_act(x, w.K, qx, sx, BT, stream=s_main)))
         layer = lambda: rbl.cr_linear_w4a8(x, w.K, w.swiglu, p, sw, out, ws, flags=BT, stream=s_main)  # noqa: E731
         gemm = lambda: rbl.cr_gemm_s8s4_rowscale(qx, sx, p, sw, out2, stream=s_main)  # noqa: E731
-        t_layer = time_loop(torch, layer, s_main, n=n)
+        # the weight was just made on the host (the GPU idled): warm as long as the timed loop
+        t_layer = time_loop(torch, layer, s_main, n=n, warm=n)
         act()
         t_gemm = time_loop(torch, gemm, s_main, n=n)
         torch.cuda.synchronize()
@@ -513,7 +514,8 @@ def w4a4_layers(torch, rbl, synth, dev, names, s_main, n=20):
         act = lambda: rbl.cr_quant_act_w4(x, w.K, w.swiglu, qx, sx, BT, stream=s_main)  # noqa: E731
         layer = lambda: rbl.cr_linear_w4a4(x, w.K, w.swiglu, p, sw, out, ws, flags=BT, stream=s_main)  # noqa: E731
         gemm = lambda: rbl.cr_gemm_s4s4_rowscale(qx, sx, p, sw, out2, stream=s_main)  # noqa: E731
-        t_layer = time_loop(torch, layer, s_main, n=n)
+        # the weight was just made on the host (the GPU idled): warm as long as the timed loop
+        t_layer = time_loop(torch, layer, s_main, n=n, warm=n)
         t_act = time_loop(torch, act, s_main, n=n)
         t_gemm = time_loop(torch, gemm, s_main, n=n)
         torch.cuda.synchronize()
@@ -535,7 +537,7 @@ def w4a4_layers(torch, rbl, synth, dev, names, s_main, n=20):
         layer6 = lambda: rbl.cr_linear_w4a4_e2m3(x, w.K, w.swiglu, p6, sw6, out6, ws6, flags=BT,  # noqa: E731
                                                  stream=s_main)
         gemm6 = lambda: rbl.cr_gemm_e2m3_rowscale(qx6, sx, p6, sw6, out2, stream=s_main)  # noqa: E731
-        t_layer6 = time_loop(torch, layer6, s_main, n=n)
+        t_layer6 = time_loop(torch, layer6, s_main, n=n, warm=n)
         t_act6 = time_loop(torch, act6, s_main, n=n)
         t_gemm6 = time_loop(torch, gemm6, s_main, n=n)
         torch.cuda.synchronize()
