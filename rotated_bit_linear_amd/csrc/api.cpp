@@ -172,21 +172,35 @@ int current_cus()
     return cus;
 }
 
-// Rows per weight chunk.  The tile bound gives the largest chunk (a multiple of the GEMM
-// tile height).  When the whole weight fits one chunk it is still split in two whenever
-// the two GEMMs together need no more rounds of workgroups over the CUs than one GEMM
-// would: then the second chunk's preparation can overlap the first chunk's GEMM and the
-// split costs nothing.
+// Rows per weight chunk, a multiple of the GEMM tile height.  The chunks' GEMMs run one
+// after another, so each pays for whole rounds of workgroups over the CUs: a GEMM of
+// t tiles takes ceil(t / cus) rounds.
+// * When the tile bound forces several chunks, the chunk height within the bound is the
+//   one whose GEMMs need the fewest rounds in total (the tallest of those on a tie).  With
+//   M = 19989 (79 tile rows) and a 16 MiB bound on K_pad = 14336, 1024-row chunks would be
+//   316-tile GEMMs of two rounds each (11 rounds for 5376 rows); 768-row chunks are
+//   237-tile GEMMs of one round (7 rounds, as many as one unchunked GEMM).
+// * When the whole weight fits one chunk it is still split in two whenever the two GEMMs
+//   together need no more rounds than one GEMM would: then the second chunk's preparation
+//   can overlap the first chunk's GEMM and the split costs nothing.
 int64_t plan_rows(int64_t M, int64_t N, int64_t K_pad, size_t max_tile_bytes, int cus)
 {
     const int64_t T = convrot::kGemmTileRows;
-    int64_t R = (int64_t)(max_tile_bytes / (size_t)K_pad) / T * T;
-    if (R < T) R = T;
+    int64_t kmax = (int64_t)(max_tile_bytes / (size_t)K_pad) / T;   // tile rows per chunk
+    if (kmax < 1) kmax = 1;
     const int64_t tiles_n = (N + T - 1) / T;
-    if (R < tiles_n * T) return R;                      // chunked by the bound already
-    if (tiles_n < 2) return tiles_n * T;
     const int64_t tiles_m = (M + convrot::kGemmTileCols - 1) / convrot::kGemmTileCols;
     auto rounds = [&](int64_t tiles) { return (tiles + cus - 1) / cus; };
+    if (kmax < tiles_n) {                               // chunked by the bound
+        int64_t best_k = kmax, best = -1;
+        for (int64_t k = kmax; k >= 1 && kmax - k < 4096; k--) {   // host time stays bounded
+            const int64_t rem = tiles_n % k;
+            const int64_t r = (tiles_n / k) * rounds(tiles_m * k) + (rem ? rounds(tiles_m * rem) : 0);
+            if (best < 0 || r < best) { best = r; best_k = k; }
+        }
+        return best_k * T;
+    }
+    if (tiles_n < 2) return tiles_n * T;
     const int64_t t0 = (tiles_n + 1) / 2, t1 = tiles_n - t0;
     if (rounds(tiles_m * t0) + rounds(tiles_m * t1) <= rounds(tiles_m * tiles_n)) return t0 * T;
     return tiles_n * T;

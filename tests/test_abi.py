@@ -7,6 +7,7 @@ visible.
 """
 import ctypes as C
 
+import numpy as np
 import pytest
 import torch
 
@@ -176,8 +177,12 @@ def test_layer_chunk_plan():
     assert rbl.cr_linear_nvfp4_plan(1, 21504, 5376) == (0, 0)
     assert rbl.cr_linear_nvfp4_workspace_bytes(64, 512, 256) == 64 * 256 + 256
     assert rbl.cr_linear_nvfp4_workspace_bytes(1, 1, 1) == 256 + 256
-    # the tile bound chunks first: 16 MiB / 5376 B per row -> 3072 rows
+    # the tile bound chunks first: 16 MiB / 5376 B per row -> at most 3072 rows; 12 tile
+    # columns per chunk take 7 x 4 = 28 rounds, which no lower height beats (3 columns tie)
     assert rbl.cr_linear_nvfp4_plan(19989, 21504, 5376, 16 << 20) == (3072, 7)
+    # FFN down under 16 MiB (at most 1170 rows of 14336 bytes): 1024-row chunks take 2
+    # rounds each (79 x 4 = 316 tiles), 11 in all; 768-row chunks take 1 each, 7 in all
+    assert rbl.cr_linear_nvfp4_plan(19989, 5376, 14336, 16 << 20) == (768, 7)
     # a bound below one tile height still gives one 256-row chunk
     assert rbl.cr_linear_nvfp4_plan(300, 1000, 5376, 1) == (256, 4)
     # an empty layer: no chunks, no workspace
@@ -191,6 +196,34 @@ def test_layer_chunk_plan():
         rbl.cr_linear_nvfp4_plan(1, 256, 0)
     with pytest.raises(rbl.CrError):
         rbl.cr_linear_nvfp4_plan(1, 256, rbl.CR_MAX_K_PAD + 1)
+
+
+def test_bounded_chunk_plan_takes_fewest_rounds():
+    """Under a tile bound, the chunk height is the tallest of those (multiples of 256 rows,
+    within the bound) whose GEMMs take the fewest rounds of workgroups over 256 CUs in all,
+    checked by enumerating every height on random shapes."""
+    rng = np.random.default_rng(7)
+
+    def rounds(tiles):
+        return -(-tiles // 256)
+
+    for _ in range(400):
+        M = int(rng.integers(65, 40000))
+        N = int(rng.integers(1, 30000))
+        kp = 256 * int(rng.integers(1, 80))
+        bound = int(rng.integers(1, 256 * kp * 40))
+        R, nch = rbl.cr_linear_nvfp4_plan(M, N, kp, bound)
+        tm, tn = -(-M // 256), -(-N // 256)
+        kmax = max(1, bound // kp // 256)
+        if kmax >= tn:
+            continue                                    # the whole weight fits the bound
+        total = {k: (tn // k) * rounds(tm * k) + (rounds(tm * (tn % k)) if tn % k else 0)
+                 for k in range(1, kmax + 1)}
+        best = min(total.values())
+        assert R % 256 == 0 and R // 256 <= kmax, (M, N, kp, bound, R)
+        assert total[R // 256] == best, (M, N, kp, bound, R, best)
+        assert all(total[k] > best for k in range(R // 256 + 1, kmax + 1)), (M, N, kp, bound, R)
+        assert nch == -(-N // R)
 
 
 def wa(codes=A16, ld=256, sf=A16, ld_sf=32, g=A16, n=8, K=512, a=A16, flags=0):

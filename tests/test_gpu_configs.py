@@ -166,3 +166,35 @@ def test_qkv_at_the_pages_16mib_tile_bound():
     ref = oracle.epilogue(acc, rsx[rows_m], rsw_all, synth.DT_BF16)
     err = check_output(out[torch.from_numpy(rows_m).to(dev())].cpu(), ref, synth.DT_BF16, "qkv at 16 MiB")
     print(f"qkv at the 16 MiB bound: rows checked={len(rows_m)} rel_l2={err:.3e}, bit-identical")
+
+
+def test_ffn_down_at_the_pages_16mib_tile_bound():
+    """FFN-down with its SwiGLU at M = 19989 with S8 weight tiles bounded by 16 MiB: the plan
+    takes 7 chunks of 768 rows (237-tile GEMMs, one round of workgroups each) instead of
+    1024-row chunks.  The output equals the default bound's bit for bit, and the oracle's on
+    sampled rows (their SwiGLU, rotation and quantization computed row by row)."""
+    w = synth.WORKLOADS["ffn_down"]
+    bound = 16 << 20
+    R, nch = rbl.cr_linear_nvfp4_plan(w.M, w.N, w.K, bound)
+    assert (R, nch) == (768, 7)
+    x = synth.make_activation(w)
+    p = synth.make_weight_nvfp4(w)
+    gs = torch.tensor([p.g], dtype=torch.float32, device=dev())
+    xd, cd, sd = x.to(dev()), p.codes.to(dev()), p.sf.to(dev())
+    aux = torch.cuda.Stream()
+    ws = torch.empty(rbl.cr_linear_nvfp4_workspace_bytes(w.M, w.N, w.K, bound), dtype=torch.uint8, device=dev())
+    out = torch.empty(w.M, w.N, dtype=torch.bfloat16, device=dev())
+    say(f"ffn_down: cr_linear_nvfp4 swiglu M={w.M} N={w.N} K={w.K} max_tile_bytes=16 MiB, aux stream")
+    rbl.cr_linear_nvfp4(xd, w.K, True, cd, sd, gs, out, ws, bound, aux_stream=aux)
+    say("ffn_down: cr_linear_nvfp4 default tile bound")
+    ref_default = rbl.linear_nvfp4(xd, cd, sd, gs, w.K, swiglu=True, aux_stream=aux)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_default), "16 MiB and default tile bounds differ"
+
+    rows_m = synth.sample_rows(w.M, SAMPLE_ROWS, w.seed, torch.empty(0, dtype=torch.long)).numpy()
+    xs = np.ascontiguousarray(synth.bits_u16(x)[rows_m])
+    rqx, rsx = oracle.quant_act(xs, w.x_dtype, w.K, swiglu=True)
+    rqw, rsw = oracle.prep_weight_nvfp4(p.codes.numpy(), p.sf.numpy(), p.g, w.K)
+    ref = oracle.epilogue(oracle.gemm_s8(rqx, rqw), rsx, rsw, synth.DT_BF16)
+    err = check_output(out[torch.from_numpy(rows_m).to(dev())].cpu(), ref, synth.DT_BF16, "ffn_down at 16 MiB")
+    print(f"ffn_down at the 16 MiB bound: rows checked={len(rows_m)} rel_l2={err:.3e}, bit-identical")
