@@ -43,7 +43,7 @@ def test_c_abi_host_side_under_asan_ubsan(tmp_path):
     kernel_objs = hip_build.kernel_objects()
     inc = os.path.join(ROOT, "include")
     # every -fsanitize= applies to the host side only (-Xarch_host); api.cpp keeps its device
-    # part (the allocation-free entry point's scratch array), the driver has none
+    # part (the allocation-free entry point's scratch array), the test program has none
     san = ["-O1", "-g", "-std=c++17", "-fPIC", "-Xarch_host", f"-fsanitize={SAN}", "-Xarch_host",
            "-fno-sanitize-recover=all", "-I", inc]
     api_o, drv_o, exe = (str(tmp_path / n) for n in ("api.o", "drv.o", "abi_sanitize"))
