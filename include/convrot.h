@@ -241,10 +241,11 @@ cr_status cr_gemm_s8_rowscale_bias(const int8_t *a_s8, int64_t lda, const float 
 size_t cr_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes);
 
 /* The chunking cr_linear_nvfp4 uses on the current device: rows per weight chunk (a
- * multiple of 256) and the number of chunks.  The bound max_tile_bytes caps a chunk; a
- * weight that fits one chunk is still split in two when the two GEMMs need no more
- * workgroup rounds over the device's compute units than one (the second chunk is then
- * prepared while the first multiplies).  Both are 0 for short batches (M <= 64), which
+ * multiple of 256) and the number of chunks.  The bound max_tile_bytes caps a chunk.  A
+ * weight the bound splits gets the chunk height, within the bound, whose GEMMs need the
+ * fewest workgroup rounds over the device's compute units in total (the tallest such
+ * height).  A weight that fits one chunk is still split in two when the two GEMMs need no
+ * more rounds than one (the second chunk is then prepared while the first multiplies).  Both are 0 for short batches (M <= 64), which
  * decode the weight inside the GEMM, and for an empty layer (M or N = 0, which needs no
  * workspace and launches nothing).  Host pointers; CR_OK or an argument status. */
 cr_status cr_linear_nvfp4_plan(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes,
