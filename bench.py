@@ -4,8 +4,10 @@
 One step = the QKV projection layer (qkv_proj [21504, 5376]) and the FFN-down layer with
 fused SwiGLU (fc2 [5376, 14336], H [19989, 28672]) at M = 19989 tokens, each one call of the
 product entry point cr_linear_nvfp4 (activation preparation, NVFP4 weight preparation of each
-chunk on a second stream, INT8 MFMA GEMM with the row-scale epilogue).  Inputs are seeded
-synthetic data resident in HBM before timing starts.
+chunk, INT8 MFMA GEMM with the row-scale epilogue, all on the calling stream).  Inputs are
+seeded synthetic data resident in HBM before timing starts.  Staging the weight chunks on a
+second stream (the pages' overlap) measures slower on this chip; --two-stream times that
+schedule for value instead, and the JSON reports the other schedule apart from value.
 
 Prints one JSON line: ms/layer (mean over the two layers of the product call, HIP events on
 the calling stream), the per-kernel split of the same layers from a mirror of the call made
@@ -68,7 +70,11 @@ def parse_args():
                     help="layers timed through the W4A4 variant, apart from value ('' = none)")
     ap.add_argument("--configs", default="tiny,qkv_m4096,longk",
                     help="the other configurations, reported apart from value ('' = none)")
-    ap.add_argument("--serial", action="store_true", help="prepare weights on the main stream")
+    ap.add_argument("--two-stream", action="store_true",
+                    help="stage weight tiles on a second stream (the pages' overlap) for value; by default "
+                         "they are staged on the calling stream, which is faster on this chip")
+    ap.add_argument("--no-stream-compare", action="store_true",
+                    help="skip the line that times the other staging schedule")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=8192)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -189,10 +195,11 @@ def product_stats(times):
 
 
 def run_layer(L, rbl, s_main, s_aux, ev):
-    """The component mirror of the layer, as cr_linear_nvfp4 runs it: activation prep (main stream) while chunk 0 of
-    the weight is prepared (second stream); GEMM of chunk c on the main stream while chunk
-    c+1 is prepared; a weight tile is refilled only after the GEMM that read it.  A weight
-    of one chunk is staged on the main stream.
+    """The component mirror of the layer, as cr_linear_nvfp4 runs it.  Without s_aux every
+    launch goes in order on the main stream.  With s_aux: activation prep (main stream) while
+    chunk 0 of the weight is prepared (second stream); GEMM of chunk c on the main stream
+    while chunk c+1 is prepared; a weight tile is refilled only after the GEMM that read it;
+    a weight of one chunk is staged on the main stream.
     ev: 3 + 4 * nchunks events: start, act begin/end, then per chunk prep begin/end and
     GEMM begin/end."""
     w = L.w
@@ -670,7 +677,7 @@ def main():
     torch.cuda.synchronize()
 
     s_main = torch.cuda.current_stream()
-    s_aux = None if args.serial else torch.cuda.Stream()
+    s_aux = torch.cuda.Stream() if args.two_stream else None
     K, W = args.steps, args.warmup
     layer_info, ms_per_step, wall_ms, mirror_step = measure_layers(torch, rbl, layers, K, W, s_main, s_aux)
 
@@ -679,7 +686,26 @@ def main():
     for L in layers:
         layer_info[L.name]["alone"] = alone_stats(torch, rbl, L, s_main, copy_gbs)
 
-    # the pages' bound on one S8 weight tile (16 MiB), same layers, product call, two streams
+    # the other staging schedule (the pages' second stream, or serial staging when value
+    # uses the second stream), product call, same layers, reported apart from value
+    other_staging = None
+    if not args.no_stream_compare:
+        alt = None if args.two_stream else torch.cuda.Stream()
+        print(f"bench: the layers with weight tiles staged {'serially' if alt is None else 'on a second stream'}",
+              file=sys.stderr, flush=True)
+        k2 = max(5, K // 2)
+        prod, _, _ = time_product(torch, rbl, layers, k2, W, s_main, alt)
+        other_staging = {"weight_prep_stream": "second stream" if alt is not None else "calling stream (serial staging)",
+                         "layers": {}}
+        for li, L in enumerate(layers):
+            check_product_equals_mirror(torch, L)
+            st = product_stats(prod[li])
+            st["vs_value_ms"] = round(st["ms"] - layer_info[L.name]["ms"], 4)
+            other_staging["layers"][L.name] = st
+        other_staging["value_ms_per_layer"] = round(
+            sum(v["ms"] for v in other_staging["layers"].values()) / len(layers), 4)
+
+    # the pages' bound on one S8 weight tile (16 MiB), same layers, product call, same staging as value
     staging = None
     if args.bounded_tile_mib > 0:
         mt = args.bounded_tile_mib << 20
@@ -811,13 +837,14 @@ def main():
             "layers": names,
             "timed_call": "cr_linear_nvfp4 (one call per layer, events on the calling stream)",
             "inputs": "bf16 activations ~N(0,1) (QKV: 1% channels x20), NVFP4 weights from 0.02*N(0,1)",
-            "weight_prep_stream": "serial" if args.serial else "second stream",
+            "weight_prep_stream": "second stream" if args.two_stream else "calling stream (serial staging)",
             "max_tile_bytes": args.max_tile_bytes or rbl.DEFAULT_MAX_TILE_BYTES,
         },
         "roofline": roofline,
         "layers": layer_info,
         "component_mirror_ms_per_step": round(mirror_step, 4),
         "bounded_staging": staging,
+        "other_staging": other_staging,
         "configs": cfg_info,
         "next_shapes": next_info,
         "short_batches": short_info,

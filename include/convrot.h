@@ -231,6 +231,8 @@ cr_status cr_gemm_s8_rowscale_bias(const int8_t *a_s8, int64_t lda, const float 
  *   s_aux      NULL: weight tiles are prepared on s_main (serial staging); otherwise,
  *              when the weight takes more than one chunk, they are prepared on s_aux,
  *              ordered against s_main by events (a single chunk is staged on s_main).
+ *              On MI355X serial staging measured faster (1-3.5 % per layer at 19989
+ *              rows): a preparation kernel beside a running GEMM competes for its CUs.
  *              On return all work is ordered before any later work on s_main.
  * Short batches (M <= 64) take the decode-inside-GEMM path instead: the activation
  * preparation, then cr_gemm_nvfp4_fused with w_amax NULL (the row maxima from its own
