@@ -1,9 +1,12 @@
 """GPU parity at the five workload sizes (tiny, QKV M=4096, QKV M=19989, FFN-down with
 SwiGLU M=19989, long-K fp16) and at the block's other linear shapes (out_proj, fc1), in the
-launch configuration the benchmark times (cr_linear_nvfp4, default tile bound, weight
-preparation on a second stream); and the block's MLP as a chain (fc1 -> SwiGLU -> fc2).
+launch configurations of the benchmark (cr_linear_nvfp4, default tile bound, weight
+preparation serial and on a second stream); and the block's MLP as a chain (fc1 -> SwiGLU ->
+fc2).
 
-Full checks: every S8 code and row scale of the activation and of the weight, bit-exact.
+Full checks: every S8 code and row scale of the activation and of the weight, bit-exact;
+every output element of the layer call equal to the same call with serial staging and to
+the component GEMM on those operands.
 Sampled checks: the layer output on a seeded sample of rows that always holds the M tail
 and every zero/tiny row, against the oracle's int32 GEMM and epilogue on those rows.
 """
@@ -44,6 +47,17 @@ def test_workload_parity(name):
         say(f"{name}: cr_linear_nvfp4 M={w.M} N={w.N} K={w.K} out={odt} (default tiles, aux stream)")
         outs[odt] = rbl.linear_nvfp4(xd, cd, sd, gs, w.K, out_dtype=synth.TORCH_DTYPE[odt], swiglu=w.swiglu,
                                      aux_stream=aux)
+    # every output element: the layer call (weight chunks on the second stream) equals the
+    # same call with serial staging, and the component GEMM on the separately prepared
+    # operands, which are checked in full against the oracle below
+    say(f"{name}: cr_linear_nvfp4 serial staging, cr_gemm_s8_rowscale on the components")
+    for odt, out in outs.items():
+        serial = rbl.linear_nvfp4(xd, cd, sd, gs, w.K, out_dtype=synth.TORCH_DTYPE[odt], swiglu=w.swiglu)
+        assert torch.equal(serial, out), f"{name} out={odt}: serial and two-stream staging differ"
+        del serial
+        comp = rbl.gemm_s8_rowscale(qx, sx, qw, sw, out_dtype=synth.TORCH_DTYPE[odt])
+        assert torch.equal(comp, out), f"{name} out={odt}: layer call and component GEMM differ"
+        del comp
     torch.cuda.synchronize()
 
     rqx, rsx = oracle.quant_act(xb, w.x_dtype, w.K, swiglu=w.swiglu)
