@@ -13,7 +13,8 @@ Sampled checks, on a seeded sample of rows that always holds the M tail:
 * the bf16 outputs of cr_linear_w4a8, cr_linear_w4a4 and cr_linear_w4a4_e2m3 against the
   oracle's epilogue.
 
-The two W4A4 layers must also agree over every output element.
+Every output element: the two W4A4 layers agree, and each layer call equals its component
+GEMM on the operands checked in full above.
 """
 import numpy as np
 import pytest
@@ -100,6 +101,11 @@ def test_w4_variants_at_config_size(name):
         run()
         torch.cuda.synchronize()
         assert_bits_equal(acc[rd].cpu().numpy(), want[what], f"{name} {what} int32 sums")
+    # the layer calls' outputs, compared in full below: the component GEMMs on these operands
+    comp8 = torch.empty(w.M, w.N, dtype=torch.bfloat16, device=dev())
+    comp4 = torch.empty_like(comp8)
+    rbl.cr_gemm_s8s4_rowscale(qx8, sx8, p4, s4, comp8)
+    rbl.cr_gemm_s4s4_rowscale(qa4, sa4, p4, s4, comp4)
     del acc, qx8, qa4, qa6
 
     # ---- the three layers (bf16 out), sampled against the oracle; W4A4 forms equal ----
@@ -107,6 +113,8 @@ def test_w4_variants_at_config_size(name):
     y8 = rbl.linear_w4a8(xd, p4, s4, w.K, swiglu=w.swiglu, flags=BT)
     torch.cuda.synchronize()
     ref8 = oracle.epilogue(want["s8 x s4"], rsx8[r], rsw, synth.DT_BF16)
+    assert torch.equal(y8, comp8), f"{name}: cr_linear_w4a8 and its component GEMM differ"
+    del comp8
     err = check_output(y8[rd].cpu(), ref8, synth.DT_BF16, f"{name} W4A8 out")
     print(f"{name} W4A8: rows checked={len(r)} rel_l2={err:.3e}, bit-identical")
     del y8
@@ -116,6 +124,7 @@ def test_w4_variants_at_config_size(name):
     y6 = rbl.linear_w4a4_e2m3(xd, p6, s6, w.K, swiglu=w.swiglu, flags=BT)
     torch.cuda.synchronize()
     assert torch.equal(y4, y6), f"{name}: the two W4A4 forms differ"
+    assert torch.equal(y4, comp4), f"{name}: cr_linear_w4a4 and its component GEMM differ"
     ref4 = oracle.epilogue(want["s4 x s4"], rsx4[r], rsw, synth.DT_BF16)
     err = check_output(y4[rd].cpu(), ref4, synth.DT_BF16, f"{name} W4A4 out")
     print(f"{name} W4A4 (both forms): rows checked={len(r)} rel_l2={err:.3e}, bit-identical")
