@@ -147,8 +147,12 @@ def test_qkv_at_the_pages_16mib_tile_bound():
     rbl.cr_linear_nvfp4(xd, w.K, False, cd, sd, gs, out, ws, bound, aux_stream=aux)
     say("qkv: cr_linear_nvfp4 default tile bound")
     ref_default = rbl.linear_nvfp4(xd, cd, sd, gs, w.K, aux_stream=aux)
+    say("qkv: cr_linear_nvfp4 max_tile_bytes=16 MiB, serial staging (separate workspace)")
+    serial = rbl.linear_nvfp4(xd, cd, sd, gs, w.K, max_tile_bytes=bound)
     torch.cuda.synchronize()
     assert torch.equal(out, ref_default), "16 MiB and default tile bounds differ"
+    assert torch.equal(serial, out), "16 MiB bound: serial and two-stream staging differ"
+    del serial
 
     kp = w.K_pad
     up = lambda v: (v + 255) // 256 * 256   # noqa: E731  (the workspace's 256-byte regions)
@@ -185,8 +189,9 @@ def test_qkv_at_the_pages_16mib_tile_bound():
 def test_ffn_down_at_the_pages_16mib_tile_bound():
     """FFN-down with its SwiGLU at M = 19989 with S8 weight tiles bounded by 16 MiB: the plan
     takes 7 chunks of 768 rows (237-tile GEMMs, one round of workgroups each) instead of
-    1024-row chunks.  The output equals the default bound's bit for bit, and the oracle's on
-    sampled rows (their SwiGLU, rotation and quantization computed row by row)."""
+    1024-row chunks.  The output equals the default bound's and serial staging's bit for bit,
+    and the oracle's on sampled rows (their SwiGLU, rotation and quantization computed row
+    by row)."""
     w = synth.WORKLOADS["ffn_down"]
     bound = 16 << 20
     R, nch = rbl.cr_linear_nvfp4_plan(w.M, w.N, w.K, bound)
@@ -202,8 +207,12 @@ def test_ffn_down_at_the_pages_16mib_tile_bound():
     rbl.cr_linear_nvfp4(xd, w.K, True, cd, sd, gs, out, ws, bound, aux_stream=aux)
     say("ffn_down: cr_linear_nvfp4 default tile bound")
     ref_default = rbl.linear_nvfp4(xd, cd, sd, gs, w.K, swiglu=True, aux_stream=aux)
+    say("ffn_down: cr_linear_nvfp4 max_tile_bytes=16 MiB, serial staging")
+    serial = rbl.linear_nvfp4(xd, cd, sd, gs, w.K, swiglu=True, max_tile_bytes=bound)
     torch.cuda.synchronize()
     assert torch.equal(out, ref_default), "16 MiB and default tile bounds differ"
+    assert torch.equal(serial, out), "16 MiB bound: serial and two-stream staging differ"
+    del serial
 
     rows_m = synth.sample_rows(w.M, SAMPLE_ROWS, w.seed, torch.empty(0, dtype=torch.long)).numpy()
     xs = np.ascontiguousarray(synth.bits_u16(x)[rows_m])
