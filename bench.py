@@ -54,7 +54,7 @@ def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workloads", default="qkv,ffn_down")
     ap.add_argument("--next-shapes", default="out_proj,ffn_up,qkv+pre_bias",
                     help="other linear shapes of the block, reported apart from value ('' = none); "
