@@ -3,7 +3,9 @@
 Each case draws M, N, K (ragged, with K sometimes past the two-pass threshold), input and
 output dtypes, padded row strides with garbage in the padding, a column order, and an
 optional pre-scale and bias, then checks the S8 codes and scales bit for bit, the int32
-accumulator bit for bit, and the outputs within the output tolerance."""
+accumulator bit for bit, and the outputs within the output tolerance.  The layer call is
+repeated under a small tile bound (1-3 tile heights), serially or with a second stream, and
+must give the same bits."""
 import numpy as np
 import pytest
 import torch
@@ -92,7 +94,17 @@ def test_random_shape_all_entry_points(case):
     y = rbl.gemm_s8_rowscale(qx, sx, qw, sw, out_dtype=tdt, bias=bd)
     yl = rbl.linear_nvfp4(x.to(dev()), cd, sd, gs, K, out_dtype=tdt, swiglu=swiglu,
                           pre_scale=None if pre is None else pre.to(dev()), bias=bd)
+    # the same layer under a small tile bound (weight chunks of 1-3 tile heights, chosen
+    # by the chunk planner), staged serially or on a second stream: the same bits
+    rr = np.random.default_rng(seed + 99)
+    bound = int(rr.integers(1, 4)) * 256 * kp
+    aux = torch.cuda.Stream() if rr.random() < 0.5 else None
+    yb = rbl.linear_nvfp4(x.to(dev()), cd, sd, gs, K, out_dtype=tdt, swiglu=swiglu, max_tile_bytes=bound,
+                          aux_stream=aux, pre_scale=None if pre is None else pre.to(dev()), bias=bd)
     torch.cuda.synchronize()
+    assert torch.equal(yb, yl), f"layer output under a {bound}-byte tile bound differs"
+    if aux is not None:
+        del aux
     assert_bits_equal(ci.cpu().numpy(), acc, "int32 accumulator")
     assert_bits_equal(cf.cpu().numpy(), acc, "int32 accumulator (decode inside the GEMM)")
     ref = oracle.epilogue(acc, rs, rsw, odt, bias=None if bias is None else bias.numpy())
