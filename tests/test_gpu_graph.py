@@ -16,8 +16,9 @@ from helpers import dev, say
 pytestmark = pytest.mark.gpu
 
 # short batch (decode inside the GEMM, main stream only), one staged chunk, and a chunked
-# weight on two streams with events
-CASES = [(16, 300, 1000, 0, False), (300, 520, 768, 0, True), (300, 1000, 1000, 256 * 1024, True)]
+# weight on two streams with events and staged serially
+CASES = [(16, 300, 1000, 0, False), (300, 520, 768, 0, True), (300, 1000, 1000, 256 * 1024, True),
+         (300, 1000, 1000, 256 * 1024, False)]
 
 
 @pytest.mark.parametrize("M,N,K,mt,use_aux", CASES, ids=[f"M{c[0]}-N{c[1]}-K{c[2]}-mt{c[3]}-aux{int(c[4])}"
