@@ -247,9 +247,11 @@ size_t cr_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t m
  * weight the bound splits gets the chunk height, within the bound, whose GEMMs need the
  * fewest workgroup rounds over the device's compute units in total (the tallest such
  * height).  A weight that fits one chunk is still split in two when the two GEMMs need no
- * more rounds than one (the second chunk is then prepared while the first multiplies).  Both are 0 for short batches (M <= 64), which
- * decode the weight inside the GEMM, and for an empty layer (M or N = 0, which needs no
- * workspace and launches nothing).  Host pointers; CR_OK or an argument status. */
+ * more rounds than one: with a second stream the second chunk is then prepared while the
+ * first multiplies, and staged serially the split costs nothing.  Both are 0 for short
+ * batches (M <= 64), which decode the weight inside the GEMM, and for an empty layer (M or
+ * N = 0, which needs no workspace and launches nothing).  Host pointers; CR_OK or an
+ * argument status. */
 cr_status cr_linear_nvfp4_plan(int64_t M, int64_t N, int64_t K, size_t max_tile_bytes,
                                int64_t *rows_per_chunk, int64_t *nchunks);
 
